@@ -1,0 +1,305 @@
+"""ctypes binding of libfpr.so (C interface in include/fpr.h).
+
+Argument marshalling only: torch supplies device memory and the current HIP
+stream; every step of the computation runs in the library's kernels.  There
+is no fallback: if the library is not built, ``load()`` raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import re
+
+import torch
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libfpr.so")
+HEADER = os.path.join(os.path.dirname(HERE), "include", "fpr.h")
+
+FPR_CALL_PACK, FPR_CALL_FORWARD, FPR_CALL_BACKWARD = 0, 1, 2
+STATUS_W_NONFINITE, STATUS_X_NONFINITE, STATUS_G_NONFINITE = 1, 2, 4
+
+
+class FprError(RuntimeError):
+    def __init__(self, code: int, what: str):
+        super().__init__(f"{what}: {status_string(code)} (code {code})")
+        self.code = code
+
+
+class Dims(ctypes.Structure):
+    _fields_ = [("d_model", ctypes.c_int32), ("n_heads", ctypes.c_int32),
+                ("d_qk", ctypes.c_int32), ("d_v", ctypes.c_int32),
+                ("eps", ctypes.c_float), ("rope_base", ctypes.c_float)]
+
+    @property
+    def n_packed(self) -> int:
+        return self.n_heads * (2 * self.d_qk + self.d_v)
+
+    @property
+    def n_q(self) -> int:
+        return self.n_heads * self.d_qk
+
+
+class _CacheC(ctypes.Structure):
+    _fields_ = [("w_packed", ctypes.c_void_p), ("w_packed_t", ctypes.c_void_p),
+                ("scales", ctypes.c_void_p), ("status", ctypes.c_void_p)]
+
+
+TRACE_MAX = 4096
+
+
+class _TraceC(ctypes.Structure):
+    _fields_ = [("events", ctypes.POINTER(ctypes.c_void_p)), ("capacity", ctypes.c_int),
+                ("count", ctypes.c_int), ("only", ctypes.c_char_p),
+                ("names", ctypes.c_char_p * TRACE_MAX)]
+
+
+class Layout(ctypes.Structure):
+    _fields_ = [("tokens", ctypes.c_int64), ("tokens_padded", ctypes.c_int64),
+                ("saved_x8t", ctypes.c_size_t), ("saved_qk_pre", ctypes.c_size_t),
+                ("saved_x_scales", ctypes.c_size_t), ("fwd_x8", ctypes.c_size_t),
+                ("bwd_dqkv", ctypes.c_size_t), ("bwd_g_scales", ctypes.c_size_t),
+                ("bwd_g8", ctypes.c_size_t), ("bwd_g8t", ctypes.c_size_t)]
+
+
+_lib = None
+_V, _I64, _I32, _SZ = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32, ctypes.c_size_t
+
+
+def load():
+    """Load libfpr.so (built in-tree by fp8_packed_reduced_amd.build)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise RuntimeError(f"{LIB_PATH} is not built; run `python -m fp8_packed_reduced_amd.build`")
+    L = ctypes.CDLL(LIB_PATH)  # torch is imported first, so HIP resolves to torch's runtime
+    P = ctypes.POINTER
+    L.fpr_workspace_bytes.restype = _SZ
+    L.fpr_workspace_bytes.argtypes = [P(Dims), _I64, ctypes.c_int]
+    L.fpr_saved_bytes.restype = _SZ
+    L.fpr_saved_bytes.argtypes = [P(Dims), _I64]
+    L.fpr_get_layout.restype = ctypes.c_int
+    L.fpr_get_layout.argtypes = [P(Dims), _I64, P(Layout)]
+    L.fpr_status_string.restype = ctypes.c_char_p
+    L.fpr_status_string.argtypes = [ctypes.c_int]
+    L.pack_quantize_weights.restype = ctypes.c_int
+    L.pack_quantize_weights.argtypes = [P(Dims), _V, _I64, _V, _I64, _V, _I64, P(_CacheC),
+                                        _V, _SZ, _V]
+    L.qkv_forward.restype = ctypes.c_int
+    L.qkv_forward.argtypes = [P(Dims), _I32, _I32, _V, P(_CacheC), _V, _V, _V, _V, _SZ, _V,
+                              _SZ, _V]
+    L.qkv_backward.restype = ctypes.c_int
+    L.qkv_backward.argtypes = [P(Dims), _I32, _I32, _V, _V, _V, _V, _SZ, P(_CacheC), _V,
+                               _V, _I64, _V, _I64, _V, _I64, _V, _SZ, _V]
+    L.fpr_trace_set.restype = None
+    L.fpr_trace_set.argtypes = [ctypes.POINTER(_TraceC)]
+    L.fpr_e4m3_encode.restype = ctypes.c_int
+    L.fpr_e4m3_encode.argtypes = [_V, _I64, ctypes.c_float, _V, _V]
+    _lib = L
+    return L
+
+
+def declared_functions() -> list[str]:
+    """Names the public header declares with FPR_API."""
+    text = open(HEADER).read()
+    return re.findall(r"^FPR_API\s+[\w\s\*]*?\b(\w+)\s*\(", text, flags=re.M)
+
+
+def status_string(code: int) -> str:
+    return load().fpr_status_string(code).decode()
+
+
+def make_dims(d_model: int, n_heads: int, d_qk: int = 96, d_v: int = 128,
+              eps: float = 1e-6, rope_base: float = 10000.0) -> Dims:
+    return Dims(d_model, n_heads, d_qk, d_v, eps, rope_base)
+
+
+def workspace_bytes(dims: Dims, tokens: int, which: int) -> int:
+    return int(load().fpr_workspace_bytes(ctypes.byref(dims), tokens, which))
+
+
+def saved_bytes(dims: Dims, tokens: int) -> int:
+    return int(load().fpr_saved_bytes(ctypes.byref(dims), tokens))
+
+
+def layout(dims: Dims, tokens: int) -> Layout:
+    out = Layout()
+    rc = load().fpr_get_layout(ctypes.byref(dims), tokens, ctypes.byref(out))
+    if rc:
+        raise FprError(rc, "fpr_get_layout")
+    return out
+
+
+def _stream(device) -> int:
+    return torch.cuda.current_stream(device).cuda_stream
+
+
+def _ptr(t: torch.Tensor | None) -> int | None:
+    return None if t is None else t.data_ptr()
+
+
+def _need(t: torch.Tensor, dtype, shape, what: str):
+    if t.dtype != dtype or tuple(t.shape) != tuple(shape) or not t.is_cuda:
+        raise ValueError(f"{what}: want {dtype} {tuple(shape)} on the GPU, "
+                         f"got {t.dtype} {tuple(t.shape)} on {t.device}")
+    if not t.is_contiguous():
+        raise ValueError(f"{what} must be contiguous")
+
+
+def _need_rows(t: torch.Tensor, rows: int, cols: int, what: str) -> int:
+    """2-D fp32 with unit column stride; returns its row stride."""
+    if t.dtype != torch.float32 or t.dim() != 2 or tuple(t.shape) != (rows, cols) or not t.is_cuda:
+        raise ValueError(f"{what}: want float32 ({rows}, {cols}) on the GPU")
+    if t.stride(1) != 1:
+        raise ValueError(f"{what} needs unit column stride")
+    return t.stride(0)
+
+
+class WeightCache:
+    """Device buffers of the cached FP8 weight views (rebuilt per update)."""
+
+    def __init__(self, dims: Dims, device="cuda"):
+        D, N = dims.d_model, dims.n_packed
+        self.dims = dims
+        self.w_packed = torch.empty((D, N), dtype=torch.uint8, device=device)
+        self.w_packed_t = torch.empty((N, D), dtype=torch.uint8, device=device)
+        self.scales = torch.zeros(2, dtype=torch.float32, device=device)
+        self.status = torch.zeros(1, dtype=torch.int32, device=device)
+
+    def c(self) -> _CacheC:
+        return _CacheC(self.w_packed.data_ptr(), self.w_packed_t.data_ptr(),
+                       self.scales.data_ptr(), self.status.data_ptr())
+
+
+def pack_quantize_weights(dims: Dims, wq, wk, wv, cache: WeightCache, workspace=None):
+    D, nq, nv = dims.d_model, dims.n_q, dims.n_heads * dims.d_v
+    ldq = _need_rows(wq, D, nq, "wq")
+    ldk = _need_rows(wk, D, nq, "wk")
+    ldv = _need_rows(wv, D, nv, "wv")
+    dev = wq.device
+    nbytes = workspace_bytes(dims, 0, FPR_CALL_PACK)
+    if workspace is None:
+        workspace = torch.empty(nbytes, dtype=torch.uint8, device=dev)
+    cc = cache.c()
+    rc = load().pack_quantize_weights(ctypes.byref(dims), wq.data_ptr(), ldq, wk.data_ptr(), ldk,
+                                      wv.data_ptr(), ldv, ctypes.byref(cc), workspace.data_ptr(),
+                                      workspace.numel(), _stream(dev))
+    if rc:
+        raise FprError(rc, "pack_quantize_weights")
+    return cache
+
+
+def qkv_forward(dims: Dims, n_seq: int, seq_len: int, x, cache: WeightCache, q=None, k=None,
+                v=None, saved=None, workspace=None):
+    """Returns (q, k, v, saved)."""
+    T = n_seq * seq_len
+    H, dqk, dv = dims.n_heads, dims.d_qk, dims.d_v
+    dev = x.device
+    _need(x, torch.bfloat16, (T, dims.d_model), "x")
+    if q is None:
+        q = torch.empty((n_seq, H, seq_len, dqk), dtype=torch.bfloat16, device=dev)
+    if k is None:
+        k = torch.empty((n_seq, H, seq_len, dqk), dtype=torch.bfloat16, device=dev)
+    if v is None:
+        v = torch.empty((n_seq, H, seq_len, dv), dtype=torch.bfloat16, device=dev)
+    _need(q, torch.bfloat16, (n_seq, H, seq_len, dqk), "q")
+    _need(k, torch.bfloat16, (n_seq, H, seq_len, dqk), "k")
+    _need(v, torch.bfloat16, (n_seq, H, seq_len, dv), "v")
+    if saved is None:
+        saved = torch.empty(saved_bytes(dims, T), dtype=torch.uint8, device=dev)
+    if workspace is None:
+        workspace = torch.empty(workspace_bytes(dims, T, FPR_CALL_FORWARD), dtype=torch.uint8,
+                                device=dev)
+    cc = cache.c()
+    rc = load().qkv_forward(ctypes.byref(dims), n_seq, seq_len, x.data_ptr(), ctypes.byref(cc),
+                            q.data_ptr(), k.data_ptr(), v.data_ptr(), saved.data_ptr(),
+                            saved.numel(), workspace.data_ptr(), workspace.numel(), _stream(dev))
+    if rc:
+        raise FprError(rc, "qkv_forward")
+    return q, k, v, saved
+
+
+def qkv_backward(dims: Dims, n_seq: int, seq_len: int, dq, dk, dv, saved, cache: WeightCache,
+                 dx=None, dw=None, workspace=None):
+    """Returns (dx, dw) with dw the [D][N] packed fp32 gradient whose column
+    blocks [:nq], [nq:2nq], [2nq:] are dW_q, dW_k, dW_v."""
+    T = n_seq * seq_len
+    H, dqk, dvw, D, N, nq = dims.n_heads, dims.d_qk, dims.d_v, dims.d_model, dims.n_packed, dims.n_q
+    dev = dq.device
+    _need(dq, torch.bfloat16, (n_seq, H, seq_len, dqk), "dq")
+    _need(dk, torch.bfloat16, (n_seq, H, seq_len, dqk), "dk")
+    _need(dv, torch.bfloat16, (n_seq, H, seq_len, dvw), "dv")
+    if dx is None:
+        dx = torch.empty((T, D), dtype=torch.bfloat16, device=dev)
+    _need(dx, torch.bfloat16, (T, D), "dx")
+    if dw is None:
+        dw = torch.empty((D, N), dtype=torch.float32, device=dev)
+    _need(dw, torch.float32, (D, N), "dw")
+    if workspace is None:
+        workspace = torch.empty(workspace_bytes(dims, T, FPR_CALL_BACKWARD), dtype=torch.uint8,
+                                device=dev)
+    dwq, dwk, dwv = dw[:, :nq], dw[:, nq:2 * nq], dw[:, 2 * nq:]
+    cc = cache.c()
+    rc = load().qkv_backward(ctypes.byref(dims), n_seq, seq_len, dq.data_ptr(), dk.data_ptr(),
+                             dv.data_ptr(), saved.data_ptr(), saved.numel(), ctypes.byref(cc),
+                             dx.data_ptr(), dwq.data_ptr(), N, dwk.data_ptr(), N, dwv.data_ptr(),
+                             N, workspace.data_ptr(), workspace.numel(), _stream(dev))
+    if rc:
+        raise FprError(rc, "qkv_backward")
+    return dx, dw
+
+
+def e4m3_encode(values: torch.Tensor, inv_scale: float = 1.0) -> torch.Tensor:
+    """Device encoder hook: e4m3(values * inv_scale), no amax."""
+    if values.dtype != torch.float32 or not values.is_cuda or not values.is_contiguous():
+        raise ValueError("values must be a contiguous float32 GPU tensor")
+    out = torch.empty(values.shape, dtype=torch.uint8, device=values.device)
+    rc = load().fpr_e4m3_encode(values.data_ptr(), values.numel(), inv_scale, out.data_ptr(),
+                                _stream(values.device))
+    if rc:
+        raise FprError(rc, "fpr_e4m3_encode")
+    return out
+
+
+def view_bytes(buf: torch.Tensor, offset: int, shape, dtype) -> torch.Tensor:
+    """A typed view into a byte buffer (for reading intermediates in tests)."""
+    n = 1
+    for s in shape:
+        n *= s
+    nbytes = n * torch.empty((), dtype=dtype).element_size()
+    return buf[offset:offset + nbytes].view(dtype).view(*shape)
+
+
+class KernelTrace:
+    """Brackets the library's kernels with torch (HIP) timing events on the
+    launch stream.  Use as a context manager around calls made on this
+    thread; ``only`` restricts it to one stage name."""
+
+    def __init__(self, capacity: int, only: str | None = None, device=None):
+        capacity = min(capacity, TRACE_MAX)
+        stream = torch.cuda.current_stream(device)
+        self.events = [torch.cuda.Event(enable_timing=True) for _ in range(2 * capacity)]
+        for e in self.events:       # materialise the underlying hipEvent_t
+            e.record(stream)
+        torch.cuda.synchronize(device)
+        self._handles = (ctypes.c_void_p * (2 * capacity))(*[e.cuda_event for e in self.events])
+        self._only = only.encode() if only else None
+        self._c = _TraceC(ctypes.cast(self._handles, ctypes.POINTER(ctypes.c_void_p)), capacity,
+                          0, self._only)
+
+    def __enter__(self):
+        load().fpr_trace_set(ctypes.byref(self._c))
+        return self
+
+    def __exit__(self, *exc):
+        load().fpr_trace_set(None)
+        return False
+
+    def records(self):
+        """[(stage name, milliseconds)] in launch order (call after a sync)."""
+        out = []
+        for i in range(self._c.count):
+            name = self._c.names[i].decode()
+            out.append((name, self.events[2 * i].elapsed_time(self.events[2 * i + 1])))
+        return out

@@ -1,0 +1,329 @@
+// C interface of libfpr.so (declared in include/fpr.h): argument checks,
+// the memory plan of the caller-provided buffers, and the launch sequence of
+// each call on the caller's stream.  No allocation, no synchronisation.
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cstdint>
+
+#include "../../include/fpr.h"
+#include "common.hpp"
+#include "launch.hpp"
+
+namespace {
+
+using fpr::ceil_div;
+using fpr::round_up;
+
+constexpr size_t kAlign = 256;
+constexpr int kPartsW = 256;     // amax blocks for W_packed
+constexpr int kPartsAct = 1024;  // amax blocks for x
+constexpr int64_t kMaxTokens = int64_t(1) << 30;
+constexpr size_t kMaxDynLds = 64 * 1024;  // dynamic LDS of one epilogue block
+
+struct Plan {
+  int D, H, dqk, dv, nq, nqk2, N;
+  int64_t T, Tp;
+  size_t s_x8t, s_qk, s_xsc, saved_total;
+  size_t f_part, f_x8, fwd_total;
+  int f_parts;
+  size_t b_part, b_gsc, b_dqkv, b_g8, b_g8t, b_dwpart, bwd_total;
+  int b_parts;
+  size_t p_part, pack_total;
+};
+
+bool dims_ok(const fpr_dims* d) {
+  if (!d) return false;
+  if (d->d_model <= 0 || d->n_heads <= 0 || d->d_qk <= 0 || d->d_v <= 0) return false;
+  if (!(d->eps >= 0.0f) || !(d->rope_base > 0.0f)) return false;
+  return true;
+}
+
+int shape_check(const fpr_dims* d) {
+  if (!dims_ok(d)) return FPR_ERR_ARG;
+  const int64_t N = (int64_t)d->n_heads * (2 * d->d_qk + d->d_v);
+  if (d->d_model % 64 || d->d_qk % 16 || d->d_v % 16 || N % 64) return FPR_ERR_SHAPE;
+  if (d->n_heads > 64 || d->d_qk > 512 || d->d_v > 4096 || N > (1 << 20) ||
+      d->d_model > (1 << 16))
+    return FPR_ERR_SHAPE;
+  if (fpr::norm_rope_fwd_lds(d->n_heads, d->d_qk) > kMaxDynLds ||
+      fpr::norm_rope_bwd_lds(d->n_heads, d->d_qk) > kMaxDynLds)
+    return FPR_ERR_SHAPE;
+  return FPR_OK;
+}
+
+size_t take(size_t& cursor, size_t bytes) {
+  const size_t at = cursor;
+  cursor = (size_t)round_up((int64_t)(cursor + bytes), kAlign);
+  return at;
+}
+
+Plan make_plan(const fpr_dims* d, int64_t T) {
+  Plan p{};
+  p.D = d->d_model;
+  p.H = d->n_heads;
+  p.dqk = d->d_qk;
+  p.dv = d->d_v;
+  p.nq = p.H * p.dqk;
+  p.nqk2 = 2 * p.nq;
+  p.N = p.nqk2 + p.H * p.dv;
+  p.T = T;
+  p.Tp = round_up(T > 0 ? T : 1, 128);
+  size_t c = 0;
+  p.s_x8t = take(c, (size_t)p.D * p.Tp);
+  p.s_qk = take(c, (size_t)T * p.nqk2 * 2);
+  p.s_xsc = take(c, 4 * sizeof(float));
+  p.saved_total = c;
+  c = 0;
+  // one amax block per 256 x 16-byte vectors of x, at most kPartsAct
+  p.f_parts = (int)std::max<int64_t>(1, std::min<int64_t>(kPartsAct, ceil_div(T * p.D / 8, fpr::kThreads)));
+  p.f_part = take(c, (size_t)p.f_parts * 4);
+  p.f_x8 = take(c, (size_t)T * p.D);
+  p.fwd_total = c;
+  c = 0;
+  p.b_parts = fpr::norm_rope_bwd_blocks(T > 0 ? T : 1);
+  p.b_part = take(c, (size_t)p.b_parts * 4);
+  p.b_gsc = take(c, 4 * sizeof(float));
+  p.b_dqkv = take(c, (size_t)T * p.N * 2);
+  p.b_g8 = take(c, (size_t)T * p.N);
+  p.b_g8t = take(c, (size_t)p.N * p.Tp);
+  p.b_dwpart = take(c, fpr::dw_partial_bytes(p.D, p.N, p.Tp));
+  p.bwd_total = c;
+  c = 0;
+  p.p_part = take(c, (size_t)kPartsW * 4);
+  p.pack_total = c;
+  return p;
+}
+
+thread_local fpr_trace* t_trace = nullptr;
+
+bool same_name(const char* a, const char* b) {
+  while (*a && *a == *b) ++a, ++b;
+  return *a == *b;
+}
+
+// Launch one stage, bracketed by the caller's events when a trace is set.
+template <class F>
+void stage(const char* name, hipStream_t s, F&& launch) {
+  fpr_trace* t = t_trace;
+  if (t && t->count < t->capacity && t->count < FPR_TRACE_MAX &&
+      (!t->only || same_name(t->only, name))) {
+    const int i = t->count;
+    (void)hipEventRecord(static_cast<hipEvent_t>(t->events[2 * i]), s);
+    launch();
+    (void)hipEventRecord(static_cast<hipEvent_t>(t->events[2 * i + 1]), s);
+    t->names[i] = name;
+    t->count = i + 1;
+  } else {
+    launch();
+  }
+}
+
+bool al16(const void* p) { return p && ((uintptr_t)p % 16 == 0); }
+
+int finish() { return hipGetLastError() == hipSuccess ? FPR_OK : FPR_ERR_LAUNCH; }
+
+template <class T>
+T* at(void* base, size_t off) {
+  return reinterpret_cast<T*>(static_cast<uint8_t*>(base) + off);
+}
+template <class T>
+const T* at(const void* base, size_t off) {
+  return reinterpret_cast<const T*>(static_cast<const uint8_t*>(base) + off);
+}
+
+int cache_check(const fpr_weight_cache* c) {
+  if (!c || !c->w_packed || !c->w_packed_t || !c->scales || !c->status) return FPR_ERR_ARG;
+  if (!al16(c->w_packed) || !al16(c->w_packed_t) || (uintptr_t)c->scales % 4 ||
+      (uintptr_t)c->status % 4)
+    return FPR_ERR_ALIGN;
+  return FPR_OK;
+}
+
+int tokens_check(int32_t n_seq, int32_t seq_len, int64_t* T) {
+  if (n_seq <= 0 || seq_len <= 0) return FPR_ERR_ARG;
+  *T = (int64_t)n_seq * seq_len;
+  if (*T > kMaxTokens) return FPR_ERR_SHAPE;
+  return FPR_OK;
+}
+
+int ld_check(int64_t ld, int64_t cols, const void* p) {
+  if (!p || ld < cols) return FPR_ERR_ARG;
+  if (!al16(p) || ld % 4) return FPR_ERR_ALIGN;
+  return FPR_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t fpr_workspace_bytes(const fpr_dims* dims, int64_t tokens, int which) {
+  if (shape_check(dims) != FPR_OK) return 0;
+  if (which == FPR_CALL_PACK) return make_plan(dims, 1).pack_total;
+  if (tokens <= 0 || tokens > kMaxTokens) return 0;
+  const Plan p = make_plan(dims, tokens);
+  if (which == FPR_CALL_FORWARD) return p.fwd_total;
+  if (which == FPR_CALL_BACKWARD) return p.bwd_total;
+  return 0;
+}
+
+size_t fpr_saved_bytes(const fpr_dims* dims, int64_t tokens) {
+  if (shape_check(dims) != FPR_OK || tokens <= 0 || tokens > kMaxTokens) return 0;
+  return make_plan(dims, tokens).saved_total;
+}
+
+int fpr_get_layout(const fpr_dims* dims, int64_t tokens, fpr_layout* out) {
+  int rc = shape_check(dims);
+  if (rc) return rc;
+  if (!out || tokens <= 0) return FPR_ERR_ARG;
+  if (tokens > kMaxTokens) return FPR_ERR_SHAPE;
+  const Plan p = make_plan(dims, tokens);
+  out->tokens = p.T;
+  out->tokens_padded = p.Tp;
+  out->saved_x8t = p.s_x8t;
+  out->saved_qk_pre = p.s_qk;
+  out->saved_x_scales = p.s_xsc;
+  out->fwd_x8 = p.f_x8;
+  out->bwd_dqkv = p.b_dqkv;
+  out->bwd_g_scales = p.b_gsc;
+  out->bwd_g8 = p.b_g8;
+  out->bwd_g8t = p.b_g8t;
+  return FPR_OK;
+}
+
+int pack_quantize_weights(const fpr_dims* dims, const float* wq, int64_t ldq, const float* wk,
+                          int64_t ldk, const float* wv, int64_t ldv,
+                          const fpr_weight_cache* cache, void* workspace,
+                          size_t workspace_bytes, void* stream) {
+  int rc = shape_check(dims);
+  if (rc) return rc;
+  const Plan p = make_plan(dims, 1);
+  if ((rc = ld_check(ldq, p.nq, wq)) || (rc = ld_check(ldk, p.nq, wk)) ||
+      (rc = ld_check(ldv, (int64_t)p.H * p.dv, wv)) || (rc = cache_check(cache)))
+    return rc;
+  if (!workspace) return FPR_ERR_ARG;
+  if (!al16(workspace)) return FPR_ERR_ALIGN;
+  if (workspace_bytes < p.pack_total) return FPR_ERR_WORKSPACE;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  (void)hipGetLastError();
+  uint32_t* parts = at<uint32_t>(workspace, p.p_part);
+  stage("amax_w", s, [&] {
+    fpr::launch_amax_w(wq, ldq, wk, ldk, wv, ldv, p.D, p.nq, p.N, parts, kPartsW, s);
+  });
+  stage("finalize_w", s, [&] {
+    fpr::launch_finalize_scales(parts, kPartsW, cache->scales, cache->status,
+                                FPR_STATUS_W_NONFINITE, true, s);
+  });
+  stage("quantize_w", s, [&] {
+    fpr::launch_quantize_w(wq, ldq, wk, ldk, wv, ldv, p.D, p.nq, p.N, cache->scales,
+                           cache->w_packed, cache->w_packed_t, s);
+  });
+  return finish();
+}
+
+int qkv_forward(const fpr_dims* dims, int32_t n_seq, int32_t seq_len, const uint16_t* x,
+                const fpr_weight_cache* cache, uint16_t* q, uint16_t* k, uint16_t* v,
+                void* saved, size_t saved_bytes, void* workspace, size_t workspace_bytes,
+                void* stream) {
+  int rc = shape_check(dims);
+  if (rc) return rc;
+  int64_t T;
+  if ((rc = tokens_check(n_seq, seq_len, &T)) || (rc = cache_check(cache))) return rc;
+  if (!x || !q || !k || !v || !saved || !workspace) return FPR_ERR_ARG;
+  if (!al16(x) || !al16(q) || !al16(k) || !al16(v) || !al16(saved) || !al16(workspace))
+    return FPR_ERR_ALIGN;
+  const Plan p = make_plan(dims, T);
+  if (saved_bytes < p.saved_total || workspace_bytes < p.fwd_total) return FPR_ERR_WORKSPACE;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  (void)hipGetLastError();
+  uint32_t* parts = at<uint32_t>(workspace, p.f_part);
+  float* xsc = at<float>(saved, p.s_xsc);
+  uint8_t* x8 = at<uint8_t>(workspace, p.f_x8);
+  uint8_t* x8t = at<uint8_t>(saved, p.s_x8t);
+  uint16_t* qk = at<uint16_t>(saved, p.s_qk);
+  stage("amax_x", s, [&] { fpr::launch_amax_bf16(x, T * p.D, parts, p.f_parts, s); });
+  stage("finalize_x", s, [&] {
+    fpr::launch_finalize_scales(parts, p.f_parts, xsc, cache->status, FPR_STATUS_X_NONFINITE,
+                                false, s);
+  });
+  stage("quantize_x", s, [&] { fpr::launch_quantize_rows(x, T, p.D, xsc, x8, x8t, p.Tp, s); });
+  stage("gemm_fwd", s, [&] {
+    fpr::launch_gemm_fwd(x8, cache->w_packed_t, (int)T, p.N, p.D, xsc, cache->scales, qk,
+                         p.nqk2, v, p.H, p.dv, seq_len, s);
+  });
+  stage("norm_rope_fwd", s, [&] {
+    fpr::launch_norm_rope_fwd(qk, T, seq_len, p.H, p.dqk, dims->eps, dims->rope_base, q, k, s);
+  });
+  return finish();
+}
+
+int qkv_backward(const fpr_dims* dims, int32_t n_seq, int32_t seq_len, const uint16_t* dq,
+                 const uint16_t* dk, const uint16_t* dv, const void* saved, size_t saved_bytes,
+                 const fpr_weight_cache* cache, uint16_t* dx, float* dwq, int64_t ldq,
+                 float* dwk, int64_t ldk, float* dwv, int64_t ldv, void* workspace,
+                 size_t workspace_bytes, void* stream) {
+  int rc = shape_check(dims);
+  if (rc) return rc;
+  int64_t T;
+  if ((rc = tokens_check(n_seq, seq_len, &T)) || (rc = cache_check(cache))) return rc;
+  const Plan p = make_plan(dims, T);
+  if ((rc = ld_check(ldq, p.nq, dwq)) || (rc = ld_check(ldk, p.nq, dwk)) ||
+      (rc = ld_check(ldv, (int64_t)p.H * p.dv, dwv)))
+    return rc;
+  if (!dq || !dk || !dv || !saved || !dx || !workspace) return FPR_ERR_ARG;
+  if (!al16(dq) || !al16(dk) || !al16(dv) || !al16(saved) || !al16(dx) || !al16(workspace))
+    return FPR_ERR_ALIGN;
+  if (saved_bytes < p.saved_total || workspace_bytes < p.bwd_total) return FPR_ERR_WORKSPACE;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  (void)hipGetLastError();
+  const float* xsc = at<float>(saved, p.s_xsc);
+  const uint8_t* x8t = at<uint8_t>(saved, p.s_x8t);
+  const uint16_t* qk = at<uint16_t>(saved, p.s_qk);
+  uint32_t* parts = at<uint32_t>(workspace, p.b_part);
+  float* gsc = at<float>(workspace, p.b_gsc);
+  uint16_t* dqkv = at<uint16_t>(workspace, p.b_dqkv);
+  uint8_t* g8 = at<uint8_t>(workspace, p.b_g8);
+  uint8_t* g8t = at<uint8_t>(workspace, p.b_g8t);
+  float* dwpart = at<float>(workspace, p.b_dwpart);
+  stage("norm_rope_bwd", s, [&] {
+    fpr::launch_norm_rope_bwd(dq, dk, dv, qk, T, seq_len, p.H, p.dqk, p.dv, dims->eps,
+                              dims->rope_base, dqkv, parts, s);
+  });
+  stage("finalize_g", s, [&] {
+    fpr::launch_finalize_scales(parts, p.b_parts, gsc, cache->status, FPR_STATUS_G_NONFINITE,
+                                false, s);
+  });
+  stage("quantize_g", s, [&] { fpr::launch_quantize_rows(dqkv, T, p.N, gsc, g8, g8t, p.Tp, s); });
+  stage("gemm_dx", s, [&] {
+    fpr::launch_gemm_dx(g8, cache->w_packed, (int)T, p.D, p.N, gsc, cache->scales, dx, s);
+  });
+  stage("gemm_dw", s, [&] { fpr::launch_gemm_dw(x8t, g8t, p.D, p.N, p.Tp, dwpart, s); });
+  stage("dw_reduce", s, [&] {
+    fpr::launch_dw_reduce(dwpart, p.D, p.N, p.Tp, xsc, gsc, dwq, ldq, dwk, ldk, dwv, ldv, p.nq, s);
+  });
+  return finish();
+}
+
+void fpr_trace_set(fpr_trace* trace) { t_trace = trace; }
+
+const char* fpr_status_string(int code) {
+  switch (code) {
+    case FPR_OK: return "ok";
+    case FPR_ERR_ARG: return "invalid argument (null pointer, non-positive size or ld < columns)";
+    case FPR_ERR_SHAPE: return "unsupported shape";
+    case FPR_ERR_ALIGN: return "misaligned pointer or leading dimension";
+    case FPR_ERR_WORKSPACE: return "workspace or saved buffer too small";
+    case FPR_ERR_LAUNCH: return "kernel launch failed";
+    default: return "unknown status code";
+  }
+}
+
+int fpr_e4m3_encode(const float* in, int64_t n, float inv_scale, uint8_t* out, void* stream) {
+  if (!in || !out || n <= 0) return FPR_ERR_ARG;
+  if (!al16(in) || !al16(out) || n % 16) return FPR_ERR_ALIGN;
+  (void)hipGetLastError();
+  fpr::launch_encode(in, n, inv_scale, out, static_cast<hipStream_t>(stream));
+  return finish();
+}
+
+}  // extern "C"

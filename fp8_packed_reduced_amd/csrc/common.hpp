@@ -1,0 +1,69 @@
+// Device helpers shared by the gfx950 kernels of libfpr.so.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace fpr {
+
+typedef int v8i __attribute__((ext_vector_type(8)));
+typedef float v4f __attribute__((ext_vector_type(4)));
+
+constexpr int kThreads = 256;        // every kernel runs 256-thread blocks (4 waves)
+constexpr int kMaxPartials = 4096;   // upper bound on per-block amax partials
+
+__host__ __device__ inline int64_t round_up(int64_t a, int64_t b) { return (a + b - 1) / b * b; }
+__host__ __device__ inline int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+// ------------------------------------------------------------------ bf16
+
+__device__ inline float bf16_to_f32(uint32_t bits16) { return __uint_as_float(bits16 << 16); }
+
+// fp32 -> bf16, round to nearest even; NaN stays a quiet NaN.
+__device__ inline uint32_t f32_to_bf16(float f) {
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0x7fffffffu) > 0x7f800000u) return 0x7fc0u;
+  u += 0x7fffu + ((u >> 16) & 1u);
+  return u >> 16;
+}
+
+__device__ inline uint32_t pack_bf16x2(float a, float b) {
+  return f32_to_bf16(a) | (f32_to_bf16(b) << 16);
+}
+
+// ------------------------------------------------------------------ e4m3
+//
+// OCP E4M3 through the gfx950 converter (round to nearest even).  The
+// explicit clamp to +-448 makes the conversion saturating for any input; a
+// per-tensor amax scale never produces more than 448 * (1 + 2^-24) anyway.
+__device__ inline float sat448(float v) { return __builtin_amdgcn_fmed3f(v, -448.0f, 448.0f); }
+
+// Four fp32 values -> four e4m3 bytes, a in the lowest byte.
+__device__ inline uint32_t e4m3x4(float a, float b, float c, float d) {
+  int lo = __builtin_amdgcn_cvt_pk_fp8_f32(sat448(a), sat448(b), 0, false);
+  return (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(sat448(c), sat448(d), lo, true);
+}
+
+// ------------------------------------------------------------ reductions
+
+__device__ inline uint32_t wave_max_u32(uint32_t v) {
+  for (int off = 32; off >= 1; off >>= 1) {
+    uint32_t o = __shfl_xor(v, off, 64);
+    v = v > o ? v : o;
+  }
+  return v;
+}
+
+// Max over the 256 threads of a block; every thread gets the result.
+__device__ inline uint32_t block_max_u32(uint32_t v, uint32_t* lds4) {
+  v = wave_max_u32(v);
+  const int wave = threadIdx.x >> 6;
+  if ((threadIdx.x & 63) == 0) lds4[wave] = v;
+  __syncthreads();
+  uint32_t r = lds4[0];
+  for (int i = 1; i < kThreads / 64; ++i) r = r > lds4[i] ? r : lds4[i];
+  __syncthreads();
+  return r;
+}
+
+}  // namespace fpr

@@ -1,0 +1,88 @@
+// Host-side launchers of the gfx950 kernels (internal to libfpr.so).
+// Every launcher enqueues on `s` and returns; errors surface through
+// hipGetLastError() in the caller.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace fpr {
+
+// ---- quantize.hip --------------------------------------------------------
+
+// Per-block max |w| over the logical W_packed [D][N] read from its three
+// pieces; writes `parts` fp32 bit patterns (as uint32) to `partials`.
+void launch_amax_w(const float* wq, int64_t ldq, const float* wk, int64_t ldk,
+                   const float* wv, int64_t ldv, int D, int nq, int N,
+                   uint32_t* partials, int parts, hipStream_t s);
+
+// Per-block max |x| of n bf16 values (n % 8 == 0).
+void launch_amax_bf16(const uint16_t* x, int64_t n, uint32_t* partials, int parts,
+                      hipStream_t s);
+
+// Reduce `parts` partials into scales[0] = s, scales[1] = inv.  A non-finite
+// amax sets `status_bit` in *status (overwriting *status when `reset`).
+void launch_finalize_scales(const uint32_t* partials, int parts, float* scales,
+                            int32_t* status, int status_bit, bool reset, hipStream_t s);
+
+// Quantise W_packed and write both layouts: w_packed [D][N], w_packed_t [N][D].
+void launch_quantize_w(const float* wq, int64_t ldq, const float* wk, int64_t ldk,
+                       const float* wv, int64_t ldv, int D, int nq, int N,
+                       const float* scales, uint8_t* w_packed, uint8_t* w_packed_t,
+                       hipStream_t s);
+
+// Quantise a [rows][cols] bf16 matrix with the per-tensor scale in `scales`:
+// dst [rows][cols] e4m3 (row-major) and dst_t [cols][ld_t] e4m3 (transposed;
+// columns rows..ld_t-1 are written as zero).  cols % 64 == 0, ld_t % 128 == 0.
+void launch_quantize_rows(const uint16_t* src, int64_t rows, int cols, const float* scales,
+                          uint8_t* dst, uint8_t* dst_t, int64_t ld_t, hipStream_t s);
+
+void launch_encode(const float* in, int64_t n, float inv, uint8_t* out, hipStream_t s);
+
+// ---- gemm.hip --------------------------------------------------------------
+
+// Forward: Y = s_x s_w x8 @ W_packed, M = T rows, N packed columns, K = D.
+// Q|K columns go to qk_pre [T][nqk2] bf16; V columns to v head-major.
+void launch_gemm_fwd(const uint8_t* x8, const uint8_t* w_packed_t, int T, int N, int D,
+                     const float* x_scales, const float* w_scales, uint16_t* qk_pre, int nqk2,
+                     uint16_t* v, int H, int d_v, int seq_len, hipStream_t s);
+
+// dX = s_g s_w g8 @ W_packed^T: M = T, N = D, K = N_packed; dx [T][D] bf16.
+void launch_gemm_dx(const uint8_t* g8, const uint8_t* w_packed, int T, int D, int Np,
+                    const float* g_scales, const float* w_scales, uint16_t* dx, hipStream_t s);
+
+// Number of K splits the dW GEMM uses, and its partial-buffer size.
+int dw_splits(int64_t tokens_padded);
+size_t dw_partial_bytes(int D, int Np, int64_t tokens_padded);
+
+// dW = s_x s_g x^T g: M = D, N = N_packed, K = tokens (padded, zero tail).
+// x8t [D][Tp], g8t [Np][Tp]; unscaled split-K partial sums go to `part`
+// [dw_splits][D][Np] fp32 ...
+void launch_gemm_dw(const uint8_t* x8t, const uint8_t* g8t, int D, int Np, int64_t Tp,
+                    float* part, hipStream_t s);
+// ... and are summed in split order, scaled by s_x s_g and written into the
+// three column blocks dwq [D][nq] (ldq), dwk, dwv [D][N - 2nq] (ldv).
+void launch_dw_reduce(const float* part, int D, int Np, int64_t Tp, const float* x_scales,
+                      const float* g_scales, float* dwq, int64_t ldq, float* dwk, int64_t ldk,
+                      float* dwv, int64_t ldv, int nq, hipStream_t s);
+
+// ---- epilogue.hip ----------------------------------------------------------
+
+// Dynamic LDS bytes of the two epilogue kernels (callers keep them <= 64 KiB).
+size_t norm_rope_fwd_lds(int H, int d_qk);
+size_t norm_rope_bwd_lds(int H, int d_qk);
+
+// Forward epilogue: pre-norm Q|K rows (qk_pre [T][2*H*d_qk] bf16) ->
+// RMSNorm -> RoPE -> head-major q, k.
+void launch_norm_rope_fwd(const uint16_t* qk_pre, int64_t T, int seq_len, int H, int d_qk,
+                          float eps, float base, uint16_t* q, uint16_t* k, hipStream_t s);
+
+// Backward epilogue: dq, dk, dv (head-major) + qk_pre -> packed dQKV [T][N]
+// bf16, plus one amax partial per block (returned count via blocks_out).
+int norm_rope_bwd_blocks(int64_t T);
+void launch_norm_rope_bwd(const uint16_t* dq, const uint16_t* dk, const uint16_t* dv,
+                          const uint16_t* qk_pre, int64_t T, int seq_len, int H, int d_qk,
+                          int d_v, float eps, float base, uint16_t* dqkv,
+                          uint32_t* partials, hipStream_t s);
+
+}  // namespace fpr

@@ -1,0 +1,251 @@
+// Per-tensor e4m3 quantisers for gfx950: the packed weight (both cached
+// layouts from one read of W, PR #344 page, "Changes"), and bf16 activations
+// / gradients (row-major plus the transposed copy the dW GEMM streams).
+//
+// The scale needs the whole tensor's amax before any code can be written,
+// so each quantiser is: per-block partial amax -> one-block finalize ->
+// quantize.  Partials are fp32 bit patterns of |v| held as uint32: for
+// non-negative floats the integer order is the float order, and any NaN or
+// Inf pattern compares above every finite value.
+#include "common.hpp"
+#include "launch.hpp"
+
+namespace fpr {
+
+// ------------------------------------------------------------- amax of W
+
+__device__ inline float4 load_w4(const float* wq, int64_t ldq, const float* wk, int64_t ldk,
+                                 const float* wv, int64_t ldv, int nq, int d, int n) {
+  const float* p = n < nq       ? wq + d * ldq + n
+                   : n < 2 * nq ? wk + d * ldk + (n - nq)
+                                : wv + d * ldv + (n - 2 * nq);
+  return *reinterpret_cast<const float4*>(p);
+}
+
+__global__ __launch_bounds__(kThreads) void amax_w_kernel(
+    const float* __restrict__ wq, int64_t ldq, const float* __restrict__ wk, int64_t ldk,
+    const float* __restrict__ wv, int64_t ldv, int D, int nq, int N,
+    uint32_t* __restrict__ partials) {
+  __shared__ uint32_t red[4];
+  const int64_t quads = (int64_t)D * (N / 4);
+  uint32_t m = 0;
+  for (int64_t i = blockIdx.x * (int64_t)kThreads + threadIdx.x; i < quads;
+       i += (int64_t)gridDim.x * kThreads) {
+    const int d = (int)(i / (N / 4));
+    const int n = (int)(i % (N / 4)) * 4;
+    float4 w = load_w4(wq, ldq, wk, ldk, wv, ldv, nq, d, n);
+    uint32_t a = __float_as_uint(w.x) & 0x7fffffffu;
+    uint32_t b = __float_as_uint(w.y) & 0x7fffffffu;
+    uint32_t c = __float_as_uint(w.z) & 0x7fffffffu;
+    uint32_t e = __float_as_uint(w.w) & 0x7fffffffu;
+    a = a > b ? a : b;
+    c = c > e ? c : e;
+    a = a > c ? a : c;
+    m = m > a ? m : a;
+  }
+  m = block_max_u32(m, red);
+  if (threadIdx.x == 0) partials[blockIdx.x] = m;
+}
+
+// --------------------------------------------------------- amax of bf16
+
+__global__ __launch_bounds__(kThreads) void amax_bf16_kernel(const uint16_t* __restrict__ x,
+                                                             int64_t n,
+                                                             uint32_t* __restrict__ partials) {
+  __shared__ uint32_t red[4];
+  const int64_t vecs = n / 8;
+  uint32_t m = 0;
+  for (int64_t i = blockIdx.x * (int64_t)kThreads + threadIdx.x; i < vecs;
+       i += (int64_t)gridDim.x * kThreads) {
+    uint4 v = reinterpret_cast<const uint4*>(x)[i];
+    uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      uint32_t lo = w[j] & 0x7fffu, hi = (w[j] >> 16) & 0x7fffu;
+      uint32_t a = lo > hi ? lo : hi;
+      m = m > a ? m : a;
+    }
+  }
+  m = block_max_u32(m << 16, red);
+  if (threadIdx.x == 0) partials[blockIdx.x] = m;
+}
+
+// ------------------------------------------------------------- finalize
+
+__global__ __launch_bounds__(kThreads) void finalize_scales_kernel(
+    const uint32_t* __restrict__ partials, int parts, float* __restrict__ scales,
+    int32_t* __restrict__ status, int status_bit, int reset) {
+  __shared__ uint32_t red[4];
+  uint32_t m = 0;
+  for (int i = threadIdx.x; i < parts; i += kThreads) m = m > partials[i] ? m : partials[i];
+  m = block_max_u32(m, red);
+  if (threadIdx.x == 0) {
+    float s = 1.0f, inv = 1.0f;
+    const bool finite = m < 0x7f800000u;
+    if (finite) {
+      const float amax = __uint_as_float(m);
+      const float i = 448.0f / amax;          // IEEE-correct fp32 division
+      if (amax != 0.0f && i <= 3.40282347e38f) {
+        s = amax / 448.0f;
+        inv = i;
+      }
+    }
+    scales[0] = s;
+    scales[1] = inv;
+    if (reset)
+      *status = finite ? 0 : status_bit;
+    else if (!finite)
+      atomicOr(status, status_bit);
+  }
+}
+
+// ----------------------------------------------- W_packed, both layouts
+
+// One 64 (d) x 64 (n) tile per block.  Each fp32 weight is read once; its
+// code goes straight to w_packed[d][n] and, through an LDS transpose, to
+// w_packed_t[n][d].
+__global__ __launch_bounds__(kThreads) void quantize_w_kernel(
+    const float* __restrict__ wq, int64_t ldq, const float* __restrict__ wk, int64_t ldk,
+    const float* __restrict__ wv, int64_t ldv, int D, int nq, int N,
+    const float* __restrict__ scales, uint8_t* __restrict__ w_packed,
+    uint8_t* __restrict__ w_packed_t) {
+  __shared__ uint8_t tile_t[64][64 + 4];
+  const int n0 = blockIdx.x * 64, d0 = blockIdx.y * 64;
+  const float inv = scales[1];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int idx = threadIdx.x + kThreads * i;
+    const int r = idx >> 4, c = (idx & 15) * 4;
+    const int d = d0 + r, n = n0 + c;
+    uint32_t code = 0;
+    if (d < D && n < N) {
+      float4 w = load_w4(wq, ldq, wk, ldk, wv, ldv, nq, d, n);
+      code = e4m3x4(w.x * inv, w.y * inv, w.z * inv, w.w * inv);
+      *reinterpret_cast<uint32_t*>(w_packed + (int64_t)d * N + n) = code;
+    }
+    tile_t[c + 0][r] = (uint8_t)(code);
+    tile_t[c + 1][r] = (uint8_t)(code >> 8);
+    tile_t[c + 2][r] = (uint8_t)(code >> 16);
+    tile_t[c + 3][r] = (uint8_t)(code >> 24);
+  }
+  __syncthreads();
+  {
+    const int r = threadIdx.x >> 2, c = (threadIdx.x & 3) * 16;  // r: n_local, c: d_local
+    const int n = n0 + r, d = d0 + c;
+    if (n < N && d < D) {
+      uint32_t w[4];
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        w[j] = (uint32_t)tile_t[r][c + 4 * j] | ((uint32_t)tile_t[r][c + 4 * j + 1] << 8) |
+               ((uint32_t)tile_t[r][c + 4 * j + 2] << 16) |
+               ((uint32_t)tile_t[r][c + 4 * j + 3] << 24);
+      *reinterpret_cast<uint4*>(w_packed_t + (int64_t)n * D + d) = make_uint4(w[0], w[1], w[2], w[3]);
+    }
+  }
+}
+
+// ---------------------------------------- bf16 rows -> e4m3, two layouts
+
+// Tile of 128 rows x 64 columns per block.  Thread (rg, cc) owns rows
+// 4rg..4rg+3 and columns 8cc..8cc+7: it reads 4 x 16 B of bf16, writes 4 x 8 B
+// of codes to the row-major output, and for each of its 8 columns one dword
+// (4 consecutive rows) into the transposed LDS tile, from which full 16 B row
+// segments of the transposed output are written.
+__global__ __launch_bounds__(kThreads) void quantize_rows_kernel(
+    const uint16_t* __restrict__ src, int64_t rows, int cols, const float* __restrict__ scales,
+    uint8_t* __restrict__ dst, uint8_t* __restrict__ dst_t, int64_t ld_t) {
+  __shared__ uint32_t tile_t[64][32 + 1];  // [col][row/4], one dword = 4 rows
+  const int64_t r0 = (int64_t)blockIdx.x * 128;
+  const int c0 = blockIdx.y * 64;
+  const int cc = threadIdx.x & 7, rg = threadIdx.x >> 3;
+  const float inv = scales[1];
+  uint32_t codes[4][2];
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    const int64_t row = r0 + 4 * rg + r;
+    uint4 v = make_uint4(0, 0, 0, 0);
+    if (row < rows)
+      v = *reinterpret_cast<const uint4*>(src + row * cols + c0 + 8 * cc);
+    codes[r][0] = e4m3x4(bf16_to_f32(v.x & 0xffffu) * inv, bf16_to_f32(v.x >> 16) * inv,
+                         bf16_to_f32(v.y & 0xffffu) * inv, bf16_to_f32(v.y >> 16) * inv);
+    codes[r][1] = e4m3x4(bf16_to_f32(v.z & 0xffffu) * inv, bf16_to_f32(v.z >> 16) * inv,
+                         bf16_to_f32(v.w & 0xffffu) * inv, bf16_to_f32(v.w >> 16) * inv);
+    if (row < rows)
+      *reinterpret_cast<uint2*>(dst + row * cols + c0 + 8 * cc) =
+          make_uint2(codes[r][0], codes[r][1]);
+  }
+  // byte j of column group: column 8cc + j; gather the 4 rows into a dword
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    const int w = j >> 2, sh = (j & 3) * 8;
+    uint32_t d = ((codes[0][w] >> sh) & 0xffu) | (((codes[1][w] >> sh) & 0xffu) << 8) |
+                 (((codes[2][w] >> sh) & 0xffu) << 16) | (((codes[3][w] >> sh) & 0xffu) << 24);
+    tile_t[8 * cc + j][rg] = d;
+  }
+  __syncthreads();
+  // 64 columns x 128 rows = 64 x 8 chunks of 16 B; two per thread
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    const int q = threadIdx.x + kThreads * i;
+    const int col = q >> 3, ch = q & 7;
+    uint4 o = make_uint4(tile_t[col][4 * ch], tile_t[col][4 * ch + 1], tile_t[col][4 * ch + 2],
+                         tile_t[col][4 * ch + 3]);
+    const int64_t row = r0 + 16 * ch;
+    if (row < ld_t)
+      *reinterpret_cast<uint4*>(dst_t + (int64_t)(c0 + col) * ld_t + row) = o;
+  }
+}
+
+__global__ __launch_bounds__(kThreads) void encode_kernel(const float* __restrict__ in, int64_t n,
+                                                          float inv, uint8_t* __restrict__ out) {
+  const int64_t i = (blockIdx.x * (int64_t)kThreads + threadIdx.x) * 16;
+  if (i >= n) return;
+  const float4* p = reinterpret_cast<const float4*>(in + i);
+  uint32_t w[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    float4 f = p[j];
+    w[j] = e4m3x4(f.x * inv, f.y * inv, f.z * inv, f.w * inv);
+  }
+  *reinterpret_cast<uint4*>(out + i) = make_uint4(w[0], w[1], w[2], w[3]);
+}
+
+// --------------------------------------------------------------- launchers
+
+void launch_amax_w(const float* wq, int64_t ldq, const float* wk, int64_t ldk, const float* wv,
+                   int64_t ldv, int D, int nq, int N, uint32_t* partials, int parts,
+                   hipStream_t s) {
+  amax_w_kernel<<<parts, kThreads, 0, s>>>(wq, ldq, wk, ldk, wv, ldv, D, nq, N, partials);
+}
+
+void launch_amax_bf16(const uint16_t* x, int64_t n, uint32_t* partials, int parts,
+                      hipStream_t s) {
+  amax_bf16_kernel<<<parts, kThreads, 0, s>>>(x, n, partials);
+}
+
+void launch_finalize_scales(const uint32_t* partials, int parts, float* scales, int32_t* status,
+                            int status_bit, bool reset, hipStream_t s) {
+  finalize_scales_kernel<<<1, kThreads, 0, s>>>(partials, parts, scales, status, status_bit,
+                                                reset ? 1 : 0);
+}
+
+void launch_quantize_w(const float* wq, int64_t ldq, const float* wk, int64_t ldk,
+                       const float* wv, int64_t ldv, int D, int nq, int N, const float* scales,
+                       uint8_t* w_packed, uint8_t* w_packed_t, hipStream_t s) {
+  dim3 grid((unsigned)ceil_div(N, 64), (unsigned)ceil_div(D, 64));
+  quantize_w_kernel<<<grid, kThreads, 0, s>>>(wq, ldq, wk, ldk, wv, ldv, D, nq, N, scales,
+                                              w_packed, w_packed_t);
+}
+
+void launch_quantize_rows(const uint16_t* src, int64_t rows, int cols, const float* scales,
+                          uint8_t* dst, uint8_t* dst_t, int64_t ld_t, hipStream_t s) {
+  dim3 grid((unsigned)(ld_t / 128), (unsigned)(cols / 64));
+  quantize_rows_kernel<<<grid, kThreads, 0, s>>>(src, rows, cols, scales, dst, dst_t, ld_t);
+}
+
+void launch_encode(const float* in, int64_t n, float inv, uint8_t* out, hipStream_t s) {
+  const int64_t blocks = ceil_div(n / 16, kThreads);
+  encode_kernel<<<(unsigned)blocks, kThreads, 0, s>>>(in, n, inv, out);
+}
+
+}  // namespace fpr

@@ -1,0 +1,215 @@
+/*
+ * fpr.h -- C interface of libfpr.so: the packed FP8 QKV projection with
+ * reduced-width Q/K heads, forward and backward, on one MI355X (gfx950).
+ *
+ * The method ("96 is enough: shrinking attention's routing vectors",
+ * section "The change"): Q and K heads are d_qk = 96 wide while V stays
+ * d_v = 128 wide; the three projections are packed into one weight
+ * W_packed = [W_q | W_k | W_v] (320 columns per head instead of 384) and
+ * computed by a single FP8 matmul qkv = x @ W_packed; q, k, v are split off,
+ * q and k are RMS-normalised and rotated with RoPE.  The PR #344 page,
+ * section "Changes", adds: both FP8 layouts of W_packed (row-major and
+ * transposed) are cached per optimizer update and come from one weight
+ * read; the logical Q/K and V packs are quantised without materialising the
+ * concatenation; norm, RoPE and layout conversion are fused; the backward
+ * pass runs in FP8 too.  "Where the eight seconds were hiding", section
+ * "The inventory": the transposed view is reused, not rebuilt, by backward.
+ *
+ * Conventions shared by every call
+ * --------------------------------
+ *  - All tensor pointers are DEVICE pointers owned by the caller.  The
+ *    library never allocates, frees or synchronises, and keeps no mutable
+ *    global state (apart from the optional per-thread profiling trace).  Every call only enqueues kernels on `stream` (a
+ *    hipStream_t; NULL means the default stream) and returns.
+ *  - Inputs are read-only.  Outputs are fully overwritten (dW is written,
+ *    not accumulated).
+ *  - bf16 tensors are passed as uint16_t bit patterns.  FP8 is OCP E4M3
+ *    ("e4m3fn": max 448, no infinities), round to nearest even, saturating.
+ *  - Per-tensor scales: s = amax/448 and inv = 448/amax in fp32 (IEEE
+ *    division); codes are e4m3(v * inv).  amax == 0 (or 448/amax overflowing)
+ *    gives s = inv = 1.  One scale covers the whole W_packed, one covers x,
+ *    one covers the packed gradient dQKV (over its bf16 values).
+ *  - T = n_seq * seq_len tokens; token t = b*seq_len + s has RoPE position s.
+ *  - Packed column order: [Q heads | K heads | V heads],
+ *    N = n_heads * (2*d_qk + d_v).
+ *  - RMSNorm has no gain: u = a / sqrt(mean(a^2) + eps).  RoPE rotates the
+ *    pairs (i, i + d_qk/2) by p * rope_base^(-2i/d_qk).
+ *  - Return value: FPR_OK or an FPR_ERR_* code.  Argument errors are found
+ *    before anything is launched.  A non-finite amax is reported on the
+ *    device, in cache->status (see fpr_weight_cache), readable after the
+ *    caller synchronises.
+ *
+ * Supported shapes: d_model % 64 == 0, d_qk % 16 == 0, d_v % 16 == 0,
+ * N % 64 == 0, and the norm/RoPE tiles of 16 tokens must fit 64 KiB of LDS
+ * (36 * 2*n_heads*d_qk + 64*d_qk bytes; the pages' 6 heads of 96 use 47 KiB);
+ * any 1 <= T <= 2^30 (ragged tails are masked).
+ * Alignment: every pointer 16-byte aligned; ldq/ldk/ldv multiples of 4.
+ */
+#ifndef FPR_H
+#define FPR_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* The library is built with hidden visibility; only these calls are exported. */
+#define FPR_API __attribute__((visibility("default")))
+
+enum {
+    FPR_OK = 0,
+    FPR_ERR_ARG = 1,        /* null pointer, non-positive size, ld < columns */
+    FPR_ERR_SHAPE = 2,      /* dimensions outside the supported set */
+    FPR_ERR_ALIGN = 3,      /* pointer or leading dimension misaligned */
+    FPR_ERR_WORKSPACE = 4,  /* workspace or saved buffer too small */
+    FPR_ERR_LAUNCH = 5      /* a kernel launch failed */
+};
+
+/* Bits of *cache->status (device int32). */
+enum {
+    FPR_STATUS_W_NONFINITE = 1,   /* W_packed had a NaN/Inf (set by pack) */
+    FPR_STATUS_X_NONFINITE = 2,   /* x had a NaN/Inf (set by forward) */
+    FPR_STATUS_G_NONFINITE = 4    /* dQKV had a NaN/Inf (set by backward) */
+};
+
+/* Model dimensions.  The pages' setting: d_qk = 96, d_v = 128. */
+typedef struct fpr_dims {
+    int32_t d_model;   /* D, width of x */
+    int32_t n_heads;   /* H */
+    int32_t d_qk;      /* width of each q and k head */
+    int32_t d_v;       /* width of each v head */
+    float eps;         /* RMSNorm epsilon (inside the square root) */
+    float rope_base;   /* RoPE base, e.g. 10000 */
+} fpr_dims;
+
+/* The cached FP8 views of W_packed, rebuilt by pack_quantize_weights after
+ * every update of the fp32 weights ("invalidate on update").  All four
+ * pointers are caller-owned device buffers. */
+typedef struct fpr_weight_cache {
+    uint8_t* w_packed;    /* [D][N] e4m3: W_packed row-major (read by dX)      */
+    uint8_t* w_packed_t;  /* [N][D] e4m3: its transpose (read by the forward)  */
+    float* scales;        /* [2] fp32: s_w, inv_w                              */
+    int32_t* status;      /* [1] FPR_STATUS_* bits; pack resets it             */
+} fpr_weight_cache;
+
+enum { FPR_CALL_PACK = 0, FPR_CALL_FORWARD = 1, FPR_CALL_BACKWARD = 2 };
+
+/* Bytes of workspace each call needs for `tokens` = T tokens (ignored for
+ * FPR_CALL_PACK).  0 for invalid dims. */
+FPR_API size_t fpr_workspace_bytes(const fpr_dims* dims, int64_t tokens, int which);
+
+/* Bytes of the buffer qkv_forward fills for qkv_backward: the FP8 x (in the
+ * layout the dW GEMM reads), its scales, and the pre-norm Q|K values in bf16.
+ * It must stay alive and unmodified from forward to backward. */
+FPR_API size_t fpr_saved_bytes(const fpr_dims* dims, int64_t tokens);
+
+/* Step 1 ("Changes": cache row-major and transposed FP8 weights once per
+ * optimizer update, both from one weight read; no materialised
+ * concatenation).  Computes amax over the logical W_packed whose pieces are
+ *   wq: [D][H*d_qk] fp32, row stride ldq elements
+ *   wk: [D][H*d_qk] fp32, row stride ldk
+ *   wv: [D][H*d_v]  fp32, row stride ldv
+ * then writes cache->w_packed, cache->w_packed_t, cache->scales and resets
+ * cache->status.  Workspace: fpr_workspace_bytes(dims, 0, FPR_CALL_PACK). */
+FPR_API int pack_quantize_weights(const fpr_dims* dims,
+                          const float* wq, int64_t ldq,
+                          const float* wk, int64_t ldk,
+                          const float* wv, int64_t ldv,
+                          const fpr_weight_cache* cache,
+                          void* workspace, size_t workspace_bytes,
+                          void* stream);
+
+/* Step 2 ("The change": qkv = fp8_matmul(x, W_packed); split; rms_norm and
+ * rope on q and k).
+ *   x:  [T][D] bf16 input activations
+ *   q:  [n_seq][H][seq_len][d_qk] bf16 out (normalised, rotated)
+ *   k:  [n_seq][H][seq_len][d_qk] bf16 out (normalised, rotated)
+ *   v:  [n_seq][H][seq_len][d_v]  bf16 out
+ *   saved: fpr_saved_bytes(dims, T) bytes, filled for qkv_backward.
+ * The weight cache must have been filled by pack_quantize_weights. */
+FPR_API int qkv_forward(const fpr_dims* dims, int32_t n_seq, int32_t seq_len,
+                const uint16_t* x, const fpr_weight_cache* cache,
+                uint16_t* q, uint16_t* k, uint16_t* v,
+                void* saved, size_t saved_bytes,
+                void* workspace, size_t workspace_bytes,
+                void* stream);
+
+/* Step 3 (FP8 backward: norm/RoPE backward, then dX through the cached
+ * W_packed codes and dW = x^T dQKV, quantisers treated as identity).
+ *   dq, dk: [n_seq][H][seq_len][d_qk] bf16 upstream gradients
+ *   dv:     [n_seq][H][seq_len][d_v]  bf16
+ *   saved:  the buffer filled by the matching qkv_forward
+ *   dx:     [T][D] bf16 out
+ *   dwq: [D][H*d_qk] fp32 out (row stride ldq), dwk likewise, dwv [D][H*d_v]. */
+FPR_API int qkv_backward(const fpr_dims* dims, int32_t n_seq, int32_t seq_len,
+                 const uint16_t* dq, const uint16_t* dk, const uint16_t* dv,
+                 const void* saved, size_t saved_bytes,
+                 const fpr_weight_cache* cache,
+                 uint16_t* dx,
+                 float* dwq, int64_t ldq,
+                 float* dwk, int64_t ldk,
+                 float* dwv, int64_t ldv,
+                 void* workspace, size_t workspace_bytes,
+                 void* stream);
+
+/* Human-readable text of an FPR_* return code (static storage). */
+FPR_API const char* fpr_status_string(int code);
+
+/* ---------------------------------------------------------------------
+ * Verification hooks.  Byte offsets of the intermediates inside `saved`
+ * and the forward/backward workspaces, so that tests can check each stage
+ * on its own.  The layout is private and may change between versions.
+ * Offsets of (size_t)-1 mean "not present".
+ * ------------------------------------------------------------------- */
+typedef struct fpr_layout {
+    int64_t tokens;          /* T */
+    int64_t tokens_padded;   /* row stride of the transposed FP8 tensors */
+    /* in `saved` */
+    size_t saved_x8t;        /* [D][tokens_padded] e4m3, x transposed      */
+    size_t saved_qk_pre;     /* [T][2*H*d_qk] bf16, pre-norm Q|K            */
+    size_t saved_x_scales;   /* [2] fp32: s_x, inv_x                        */
+    /* in the forward workspace */
+    size_t fwd_x8;           /* [T][D] e4m3                                 */
+    /* in the backward workspace */
+    size_t bwd_dqkv;         /* [T][N] bf16 packed gradient                  */
+    size_t bwd_g_scales;     /* [2] fp32: s_g, inv_g                         */
+    size_t bwd_g8;           /* [T][N] e4m3                                  */
+    size_t bwd_g8t;          /* [N][tokens_padded] e4m3                      */
+} fpr_layout;
+
+FPR_API int fpr_get_layout(const fpr_dims* dims, int64_t tokens, fpr_layout* out);
+
+/* Profiling: while a trace is set on the calling thread, every kernel the
+ * calls above launch from that thread whose stage name matches `only` (all
+ * kernels when `only` is NULL) is bracketed by hipEventRecord(events[2i]) and
+ * hipEventRecord(events[2i+1]) on the call's stream, and its stage name is
+ * stored in names[i], for i = count, count+1, ... while count < capacity
+ * (and count < FPR_TRACE_MAX).  events are caller-created hipEvent_t handles.
+ * Stage names: amax_w, finalize_w, quantize_w, amax_x, finalize_x,
+ * quantize_x, gemm_fwd, norm_rope_fwd, norm_rope_bwd, finalize_g, quantize_g,
+ * gemm_dx, gemm_dw, dw_reduce.  fpr_trace_set(NULL) stops tracing.  This is
+ * the only per-thread state the library keeps. */
+#define FPR_TRACE_MAX 4096
+typedef struct fpr_trace {
+    void** events;
+    int capacity;
+    int count;
+    const char* only;
+    const char* names[FPR_TRACE_MAX];
+} fpr_trace;
+
+FPR_API void fpr_trace_set(fpr_trace* trace);
+
+/* Encode n fp32 values as e4m3(in[i] * inv_scale) with the library's device
+ * encoder (no amax; the caller supplies the scale).  For exhaustive tests of
+ * the encoder.  in/out are device pointers, 16-byte aligned, n % 16 == 0. */
+FPR_API int fpr_e4m3_encode(const float* in, int64_t n, float inv_scale, uint8_t* out,
+                    void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* FPR_H */

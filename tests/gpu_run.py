@@ -1,0 +1,120 @@
+"""Helpers for the GPU parity tests: run the HIP path through the C interface
+on seeded inputs and return every stage's output as numpy arrays (bf16 as
+uint16 bit patterns), plus tolerance helpers.  Imports no oracle code."""
+from __future__ import annotations
+
+import sys
+
+import numpy as np
+import torch
+
+from fp8_packed_reduced_amd import binding as B
+from fp8_packed_reduced_amd import inputs
+
+EPS = inputs.EPS
+BASE = inputs.ROPE_BASE
+
+
+def say(msg: str):
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+def bits_to_dev(bits: np.ndarray) -> torch.Tensor:
+    return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16).cuda()
+
+
+def dev_to_bits(t: torch.Tensor) -> np.ndarray:
+    return t.contiguous().view(torch.int16).cpu().numpy().view(np.uint16)
+
+
+def dims_for(w: dict):
+    return B.make_dims(w["d_model"], w["n_heads"], w["d_qk"], w["d_v"], EPS, BASE)
+
+
+def run(w: dict, seed: int = 42, x_bits=None, W=None, dy=None, backward: bool = True):
+    """Pack, forward (and backward) on the GPU; returns a dict of numpy arrays."""
+    n_seq, S = w["n_seq"], w["seq_len"]
+    T = n_seq * S
+    D, H, dqk, dv = w["d_model"], w["n_heads"], w["d_qk"], w["d_v"]
+    N = inputs.packed_width(w)
+    dims = dims_for(w)
+    say(f"[gpu] run n_seq={n_seq} S={S} D={D} H={H} d_qk={dqk} d_v={dv} seed={seed}")
+    if x_bits is None:
+        x_bits = inputs.make_x(w, seed)
+    if W is None:
+        W = inputs.make_w(w, seed + 1)
+    Wd = torch.from_numpy(np.ascontiguousarray(W)).cuda()
+    nq = H * dqk
+    wq, wk, wv = Wd[:, :nq], Wd[:, nq:2 * nq], Wd[:, 2 * nq:]
+    cache = B.WeightCache(dims)
+    B.pack_quantize_weights(dims, wq, wk, wv, cache)
+    x = bits_to_dev(x_bits)
+    ws_f = torch.empty(B.workspace_bytes(dims, T, B.FPR_CALL_FORWARD), dtype=torch.uint8,
+                       device="cuda")
+    q, k, v, saved = B.qkv_forward(dims, n_seq, S, x, cache, workspace=ws_f)
+    lay = B.layout(dims, T)
+    Tp = lay.tokens_padded
+    out = dict(T=T, N=N, Tp=Tp, x_bits=x_bits, W=W)
+    torch.cuda.synchronize()
+    out["w_packed"] = cache.w_packed.cpu().numpy()
+    out["w_packed_t"] = cache.w_packed_t.cpu().numpy()
+    out["w_scales"] = cache.scales.cpu().numpy()
+    out["x8"] = B.view_bytes(ws_f, lay.fwd_x8, (T, D), torch.uint8).cpu().numpy()
+    out["x8t"] = B.view_bytes(saved, lay.saved_x8t, (D, Tp), torch.uint8).cpu().numpy()
+    out["x_scales"] = B.view_bytes(saved, lay.saved_x_scales, (2,), torch.float32).cpu().numpy()
+    out["qk_pre"] = dev_to_bits(B.view_bytes(saved, lay.saved_qk_pre, (T, 2 * nq), torch.bfloat16))
+    out["q"], out["k"], out["v"] = dev_to_bits(q), dev_to_bits(k), dev_to_bits(v)
+    if backward:
+        if dy is None:
+            dy = inputs.make_dy(w, seed + 2)
+        dqd, dkd, dvd = (bits_to_dev(a) for a in dy)
+        ws_b = torch.empty(B.workspace_bytes(dims, T, B.FPR_CALL_BACKWARD), dtype=torch.uint8,
+                           device="cuda")
+        dx, dw = B.qkv_backward(dims, n_seq, S, dqd, dkd, dvd, saved, cache, workspace=ws_b)
+        torch.cuda.synchronize()
+        out["dy"] = dy
+        out["dqkv"] = dev_to_bits(B.view_bytes(ws_b, lay.bwd_dqkv, (T, N), torch.bfloat16))
+        out["g_scales"] = B.view_bytes(ws_b, lay.bwd_g_scales, (2,), torch.float32).cpu().numpy()
+        out["g8"] = B.view_bytes(ws_b, lay.bwd_g8, (T, N), torch.uint8).cpu().numpy()
+        out["g8t"] = B.view_bytes(ws_b, lay.bwd_g8t, (N, Tp), torch.uint8).cpu().numpy()
+        out["dx"] = dev_to_bits(dx)
+        out["dw"] = dw.cpu().numpy()
+    out["status"] = int(cache.status.cpu().item())
+    say("[gpu] done")
+    return out
+
+
+def bf16_to_f64(bits: np.ndarray) -> np.ndarray:
+    bits = np.asarray(bits, dtype=np.uint16)
+    with np.errstate(invalid="ignore"):
+        return (bits.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+
+
+def row_rel_err(got: np.ndarray, want: np.ndarray) -> float:
+    """max over rows of ||got - want|| / ||want|| (rows = all but the last axis)."""
+    g = np.asarray(got, dtype=np.float64).reshape(-1, got.shape[-1])
+    o = np.asarray(want, dtype=np.float64).reshape(-1, want.shape[-1])
+    num = np.linalg.norm(g - o, axis=1)
+    den = np.linalg.norm(o, axis=1)
+    den = np.where(den == 0, 1.0, den)
+    return float(np.max(num / den)) if num.size else 0.0
+
+
+def row_errors(got: np.ndarray, want: np.ndarray) -> np.ndarray:
+    """Per-row ||got - want|| / ||want|| (rows = all but the last axis)."""
+    g = np.asarray(got, dtype=np.float64).reshape(-1, got.shape[-1])
+    o = np.asarray(want, dtype=np.float64).reshape(-1, want.shape[-1])
+    den = np.linalg.norm(o, axis=1)
+    return np.linalg.norm(g - o, axis=1) / np.where(den == 0, 1.0, den)
+
+
+def bf16_gemm_excess(gpu_bits: np.ndarray, exact: np.ndarray, round_bf16) -> tuple[float, float]:
+    """For a GEMM whose output is bf16: per row, the GPU's distance to the
+    exact float64 product against the distance that rounding the exact
+    product to bf16 costs by itself.  Returns (worst gpu / rounding ratio
+    excess, worst gpu - 1.1 * rounding) so a test can require
+    e_gpu <= 1.1 * e_round + 1e-3 on every row."""
+    e_gpu = row_errors(bf16_to_f64(gpu_bits), exact)
+    e_rnd = row_errors(bf16_to_f64(round_bf16(exact)), exact)
+    return float(np.max(e_gpu - e_rnd)), float(np.max(e_gpu - 1.1 * e_rnd))

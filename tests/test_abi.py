@@ -1,0 +1,106 @@
+"""Host-side checks of the C interface (no GPU needed, nothing is launched):
+the library loads, exports every call the header declares, sizes and the
+private layout are consistent, and every argument error is reported before
+any kernel launch."""
+import ctypes
+
+import pytest
+import torch  # noqa: F401  (loads the HIP runtime the library binds to)
+
+from fp8_packed_reduced_amd import binding as B
+
+pytestmark = pytest.mark.skipif(not __import__("os").path.exists(B.LIB_PATH),
+                                reason="libfpr.so not built")
+
+
+def test_library_exports_every_declared_call():
+    names = B.declared_functions()
+    assert set(names) == {"fpr_workspace_bytes", "fpr_saved_bytes", "pack_quantize_weights",
+                          "qkv_forward", "qkv_backward", "fpr_status_string", "fpr_get_layout",
+                          "fpr_e4m3_encode", "fpr_trace_set"}
+    lib = B.load()
+    for n in names:
+        assert hasattr(lib, n), n
+
+
+def test_status_strings():
+    for code in range(6):
+        assert B.status_string(code)
+    assert "unknown" in B.status_string(99)
+
+
+def test_sizes_and_layout_at_the_64k_step_shape():
+    d = B.make_dims(768, 6)
+    T = 65536
+    lay = B.layout(d, T)
+    assert lay.tokens == T and lay.tokens_padded == T
+    saved = B.saved_bytes(d, T)
+    # x8t [768][T] + pre-norm Q|K [T][1152] bf16 + scales
+    assert saved >= 768 * T + T * 1152 * 2 + 8
+    assert lay.saved_x8t + 768 * T <= lay.saved_qk_pre
+    assert lay.saved_qk_pre + T * 1152 * 2 <= lay.saved_x_scales < saved
+    assert B.workspace_bytes(d, T, B.FPR_CALL_FORWARD) >= lay.fwd_x8 + T * 768
+    bw = B.workspace_bytes(d, T, B.FPR_CALL_BACKWARD)
+    assert bw >= lay.bwd_g8t + 1920 * T
+    for off in (lay.saved_x8t, lay.saved_qk_pre, lay.saved_x_scales, lay.fwd_x8,
+                lay.bwd_dqkv, lay.bwd_g8, lay.bwd_g8t, lay.bwd_g_scales):
+        assert off % 256 == 0
+
+
+def test_ragged_tokens_pad_the_transposed_stride():
+    d = B.make_dims(128, 1)
+    assert B.layout(d, 300).tokens_padded == 384
+    assert B.layout(d, 1).tokens_padded == 128
+
+
+@pytest.mark.parametrize("dims,ok", [
+    ((768, 6, 96, 128), True), ((128, 1, 96, 128), True), ((768, 6, 64, 128), True),
+    ((768, 6, 128, 128), True), ((100, 6, 96, 128), False), ((768, 6, 40, 128), False),
+    ((768, 6, 96, 120), False), ((768, 1, 32, 32), False), ((768, 0, 96, 128), False),
+    ((768, 16, 96, 128), False)])
+def test_shape_support(dims, ok):
+    d = B.make_dims(*dims)
+    assert (B.saved_bytes(d, 256) > 0) == ok
+    assert (B.workspace_bytes(d, 256, B.FPR_CALL_FORWARD) > 0) == ok
+
+
+def _cache_c(ptr=0x1000):
+    return B._CacheC(ptr, ptr, ptr, ptr)
+
+
+def test_argument_errors_are_reported_before_any_launch():
+    L = B.load()
+    d = B.make_dims(128, 1)
+    cc = _cache_c()
+    ws = 0x10000
+    by = ctypes.byref
+    # null weight piece
+    assert L.pack_quantize_weights(by(d), None, 96, ws, 96, ws, 128, by(cc), ws, 1 << 20, None) == 1
+    # ld smaller than the piece width
+    assert L.pack_quantize_weights(by(d), ws, 95, ws, 96, ws, 128, by(cc), ws, 1 << 20, None) == 1
+    # misaligned piece and ld
+    assert L.pack_quantize_weights(by(d), ws + 4, 96, ws, 96, ws, 128, by(cc), ws, 1 << 20, None) == 3
+    assert L.pack_quantize_weights(by(d), ws, 98, ws, 96, ws, 128, by(cc), ws, 1 << 20, None) == 3
+    # workspace too small
+    assert L.pack_quantize_weights(by(d), ws, 96, ws, 96, ws, 128, by(cc), ws, 16, None) == 4
+    # bad shapes
+    bad = B.make_dims(100, 1)
+    assert L.pack_quantize_weights(by(bad), ws, 96, ws, 96, ws, 128, by(cc), ws, 1 << 20, None) == 2
+    # forward: non-positive sizes, null outputs, small saved buffer
+    assert L.qkv_forward(by(d), 0, 256, ws, by(cc), ws, ws, ws, ws, 1 << 30, ws, 1 << 30, None) == 1
+    assert L.qkv_forward(by(d), 1, 256, ws, by(cc), None, ws, ws, ws, 1 << 30, ws, 1 << 30, None) == 1
+    assert L.qkv_forward(by(d), 1, 256, ws + 2, by(cc), ws, ws, ws, ws, 1 << 30, ws, 1 << 30, None) == 3
+    assert L.qkv_forward(by(d), 1, 256, ws, by(cc), ws, ws, ws, ws, 10, ws, 1 << 30, None) == 4
+    assert L.qkv_forward(by(d), 1 << 16, 1 << 15, ws, by(cc), ws, ws, ws, ws, 1 << 40, ws, 1 << 40,
+                         None) == 2
+    # forward with an incomplete weight cache
+    half = B._CacheC(ws, None, ws, ws)
+    assert L.qkv_forward(by(d), 1, 256, ws, by(half), ws, ws, ws, ws, 1 << 30, ws, 1 << 30, None) == 1
+    # backward: ld errors on the dW outputs, small workspace
+    assert L.qkv_backward(by(d), 1, 256, ws, ws, ws, ws, 1 << 30, by(cc), ws, ws, 90, ws, 96, ws,
+                          128, ws, 1 << 30, None) == 1
+    assert L.qkv_backward(by(d), 1, 256, ws, ws, ws, ws, 1 << 30, by(cc), ws, ws, 96, ws, 96, ws,
+                          128, ws, 100, None) == 4
+    # encoder hook
+    assert L.fpr_e4m3_encode(ws, 15, 1.0, ws, None) == 3
+    assert L.fpr_e4m3_encode(None, 16, 1.0, ws, None) == 1

@@ -1,0 +1,327 @@
+"""Parity of the HIP path (through the C interface) with the CPU oracle.
+
+Stage-wise: every GPU stage is compared with the oracle's stage fed the
+GPU's own inputs to that stage.  Bars:
+  * FP8 codes and scales, the transposed copies, the V relayout: bit-exact;
+  * GEMM outputs: the accumulated product must be within 1e-3 per row norm.
+    dW is fp32 and is compared directly: ||gpu - oracle|| / ||oracle|| <= 1e-3
+    per row.  The projection Y and dX are rounded to bf16, whose own rounding
+    costs ~2e-3 per row, so per row their distance to the exact float64
+    product may exceed what rounding the exact product costs by at most
+    1.1x + 1e-3 (the protocol the end-to-end check uses too).  The matrix
+    cores' FP8 dot products carry ~14-15 significant bits in their partial
+    sums, which flips a few bf16 roundings; compared directly with the
+    bf16-rounded oracle the worst row of a K=128 product reaches ~1.2e-3;
+  * normalised / rotated q, k and the packed gradient dQKV: <= 1e-2 per
+    (token, head) row.
+End to end (from x, W and the upstream gradients alone): q, k, v <= 1e-2;
+dX and dW, whose FP8 gradient codes can flip where the bf16 dQKV differs
+by one ulp, must be no further from the unquantised float64 result than
+1.1 x the oracle's own distance + 1e-3.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from fp8_packed_reduced_amd import inputs
+
+from gpu_run import BASE, EPS, bf16_gemm_excess, bf16_to_f64, row_rel_err, run, say
+
+pytestmark = pytest.mark.gpu
+
+GEMM_TOL = 1e-3
+NORM_TOL = 1e-2
+
+RAGGED = dict(n_seq=3, seq_len=100, d_model=128, n_heads=2, d_qk=96, d_v=128)
+SMALL_16K_DIMS = dict(n_seq=2, seq_len=384, d_model=768, n_heads=6, d_qk=96, d_v=128)
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.fail("no GPU visible")
+    oracle.build(force=False)
+
+
+def _dims(w):
+    return inputs.dims_of(w)
+
+
+# ------------------------------------------------------------------ encoder
+
+def test_encoder_matches_oracle_on_every_rounding_class():
+    from fp8_packed_reduced_amd import binding as B
+    hi = np.arange(1 << 16, dtype=np.uint32) << 16
+    tails = np.array([0x0000, 0x0001, 0x7FFF, 0x8000, 0x8001, 0xFFFF], dtype=np.uint32)
+    v = (hi[:, None] | tails[None, :]).ravel().view(np.float32)
+    v = v[np.isfinite(v)]
+    v = v[: (v.size // 16) * 16]
+    say(f"[gpu] encoder sweep over {v.size} fp32 patterns")
+    got = B.e4m3_encode(torch.from_numpy(v).cuda(), 1.0).cpu().numpy()
+    assert np.array_equal(got, oracle.e4m3_encode(v))
+    # with a scale: codes of fl32(v * inv)
+    rng = np.random.default_rng(1)
+    r = rng.standard_normal(1 << 20).astype(np.float32)
+    inv = np.float32(448.0) / np.float32(np.abs(r).max())
+    got = B.e4m3_encode(torch.from_numpy(r).cuda(), float(inv)).cpu().numpy()
+    assert np.array_equal(got, oracle.e4m3_encode(r * inv))
+
+
+# ------------------------------------------------------------ weight quant
+
+@pytest.mark.parametrize("wl", ["tiny", "fwd_16k", "sweep_64", "sweep_128"])
+def test_pack_quantize_bit_exact(wl):
+    w = dict(inputs.WORKLOADS[wl], n_seq=1, seq_len=128)
+    r = run(w, seed=5, backward=False)
+    wp, wpt, s, inv, rc = oracle.pack_quantize_weights(_dims(w), r["W"])
+    assert np.array_equal(r["w_packed"], wp)
+    assert np.array_equal(r["w_packed_t"], wpt)
+    assert r["w_scales"][0] == s and r["w_scales"][1] == inv
+    assert r["status"] == 0
+
+
+def test_pack_flags_nonfinite_weights():
+    w = dict(inputs.WORKLOADS["tiny"], seq_len=128)
+    W = inputs.make_w(w, 3)
+    W[5, 7] = np.inf
+    r = run(w, seed=3, W=W, backward=False)
+    assert r["status"] & 1
+
+
+# ------------------------------------------------------------ forward
+
+def _check_forward(w, r):
+    dims = _dims(w)
+    n_seq, S = w["n_seq"], w["seq_len"]
+    T, H, dqk, dv = r["T"], w["n_heads"], w["d_qk"], w["d_v"]
+    nqk2 = 2 * H * dqk
+    # a2: activation quantiser, both layouts, bit-exact
+    x8, s_x, inv_x, _ = oracle.quantize_bf16(r["x_bits"])
+    assert np.array_equal(r["x8"], x8)
+    assert r["x_scales"][0] == s_x and r["x_scales"][1] == inv_x
+    assert np.array_equal(r["x8t"][:, :T], x8.T) and not r["x8t"][:, T:].any()
+    # a3: packed GEMM from the GPU's own codes
+    y = oracle.gemm_e4m3(r["x8"], r["w_packed"], r["x_scales"][0], r["w_scales"][0])
+    y_bits = oracle.round_bf16(y)
+    gpu_y = np.empty((T, r["N"]), dtype=np.uint16)
+    gpu_y[:, :nqk2] = r["qk_pre"]
+    gpu_y[:, nqk2:] = oracle.from_head_major(r["v"]).reshape(T, H * dv)
+    e_gemm = row_rel_err(bf16_to_f64(gpu_y), bf16_to_f64(y_bits))
+    x_gemm, over_gemm = bf16_gemm_excess(gpu_y, y, oracle.round_bf16)
+    # a4: epilogue fed the GPU's own pre-norm rows
+    o = oracle.qkv_forward(dims, n_seq, S, r["x_bits"], r["w_packed"], r["w_scales"][0],
+                           y_bits=gpu_y)
+    e_q = row_rel_err(bf16_to_f64(r["q"]), o["q64"])
+    e_k = row_rel_err(bf16_to_f64(r["k"]), o["k64"])
+    say(f"[gpu] forward errors: gemm {e_gemm:.2e} (excess over bf16 rounding {x_gemm:.2e}) "
+        f"q {e_q:.2e} k {e_k:.2e}")
+    assert over_gemm <= GEMM_TOL
+    assert e_q <= NORM_TOL and e_k <= NORM_TOL
+    assert np.array_equal(r["v"], o["v_bits"])  # v is a pure relayout of Y's V columns
+
+
+def _check_backward(w, r):
+    dims = _dims(w)
+    n_seq, S = w["n_seq"], w["seq_len"]
+    T, H, dqk = r["T"], w["n_heads"], w["d_qk"]
+    nqk2 = 2 * H * dqk
+    dq, dk, dv = r["dy"]
+    # a5: norm/RoPE backward fed the GPU's saved pre-norm rows
+    ob = oracle.qkv_backward(dims, n_seq, S, dq, dk, dv, r["x8"], r["x_scales"][0], r["qk_pre"],
+                             r["w_packed"], r["w_scales"][0])
+    g = r["dqkv"]
+    e_dqk = row_rel_err(bf16_to_f64(g[:, :nqk2]).reshape(T, 2 * H, dqk),
+                        ob["dqkv64"][:, :nqk2].reshape(T, 2 * H, dqk))
+    assert np.array_equal(g[:, nqk2:], ob["dqkv_bits"][:, nqk2:])  # dv relayout
+    # a6: gradient quantiser, bit-exact on the GPU's own dQKV
+    g8, s_g, inv_g, _ = oracle.quantize_bf16(g)
+    assert np.array_equal(r["g8"], g8)
+    assert r["g_scales"][0] == s_g and r["g_scales"][1] == inv_g
+    assert np.array_equal(r["g8t"][:, :T], g8.T) and not r["g8t"][:, T:].any()
+    # a7, a8: GEMMs from the GPU's own codes
+    dx64 = oracle.gemm_e4m3(r["g8"], np.ascontiguousarray(r["w_packed"].T), s_g, r["w_scales"][0])
+    e_dx = row_rel_err(bf16_to_f64(r["dx"]), bf16_to_f64(oracle.round_bf16(dx64)))
+    x_dx, over_dx = bf16_gemm_excess(r["dx"], dx64, oracle.round_bf16)
+    dw = oracle.round_f32(oracle.gemm_e4m3(np.ascontiguousarray(r["x8"].T), r["g8"],
+                                           r["x_scales"][0], s_g))
+    e_dw = row_rel_err(r["dw"], dw)
+    say(f"[gpu] backward errors: dqkv {e_dqk:.2e} dx {e_dx:.2e} (excess {x_dx:.2e}) "
+        f"dw {e_dw:.2e}")
+    assert e_dqk <= NORM_TOL
+    assert over_dx <= GEMM_TOL and e_dw <= GEMM_TOL
+
+
+@pytest.mark.parametrize("name,w", [("tiny", inputs.WORKLOADS["tiny"]), ("ragged", RAGGED),
+                                    ("d768", SMALL_16K_DIMS)])
+def test_forward_backward_stagewise(name, w):
+    r = run(w, seed=42)
+    assert r["status"] == 0
+    _check_forward(w, r)
+    _check_backward(w, r)
+
+
+@pytest.mark.parametrize("dqk", [64, 128])
+def test_width_sweep_stagewise(dqk):
+    w = dict(n_seq=1, seq_len=512, d_model=768, n_heads=6, d_qk=dqk, d_v=128)
+    r = run(w, seed=7)
+    _check_forward(w, r)
+    _check_backward(w, r)
+
+
+def test_forward_only_16k_shape_full():
+    w = inputs.WORKLOADS["fwd_16k"]
+    r = run(w, seed=42, backward=False)
+    _check_forward(w, r)
+
+
+# ---------------------------------------------------------- end to end
+
+def _unquantised(w, x_bits, W, dy):
+    """float64 result with no FP8 anywhere (reference for the e2e protocol)."""
+    n_seq, S = w["n_seq"], w["seq_len"]
+    T, H, dqk = n_seq * S, w["n_heads"], w["d_qk"]
+    nq = H * dqk
+    x = bf16_to_f64(x_bits)
+    Wd = W.astype(np.float64)
+    y = x @ Wd
+    pos = oracle.positions_of(n_seq, S)
+    dq, dk, dv = (bf16_to_f64(a) for a in dy)
+    dqp = oracle.qk_norm_rope_bwd(y[:, :nq].reshape(T, H, dqk), oracle.from_head_major(dq), pos,
+                                  EPS, BASE)
+    dkp = oracle.qk_norm_rope_bwd(y[:, nq:2 * nq].reshape(T, H, dqk),
+                                  oracle.from_head_major(dk), pos, EPS, BASE)
+    g = np.concatenate([dqp.reshape(T, nq), dkp.reshape(T, nq),
+                        oracle.from_head_major(dv).reshape(T, -1)], axis=1)
+    return g @ Wd.T, x.T @ g
+
+
+def test_end_to_end_against_oracle_chain():
+    w = inputs.WORKLOADS["tiny"]
+    dims = _dims(w)
+    r = run(w, seed=42)
+    wp, _, s_w, _, _ = oracle.pack_quantize_weights(dims, r["W"])
+    of = oracle.qkv_forward(dims, 1, w["seq_len"], r["x_bits"], wp, s_w)
+    e_q = row_rel_err(bf16_to_f64(r["q"]), of["q64"])
+    e_k = row_rel_err(bf16_to_f64(r["k"]), of["k64"])
+    e_v = row_rel_err(bf16_to_f64(r["v"]), of["v64"])
+    assert max(e_q, e_k, e_v) <= NORM_TOL
+    dq, dk, dv = r["dy"]
+    ob = oracle.qkv_backward(dims, 1, w["seq_len"], dq, dk, dv, of["x8"], of["s_x"],
+                             of["y_bits"][:, :2 * w["n_heads"] * w["d_qk"]], wp, s_w)
+    dx_ref, dw_ref = _unquantised(w, r["x_bits"], r["W"], r["dy"])
+    e_gpu_dx = row_rel_err(bf16_to_f64(r["dx"]), dx_ref)
+    e_orc_dx = row_rel_err(bf16_to_f64(ob["dx_bits"]), dx_ref)
+    e_gpu_dw = row_rel_err(r["dw"], dw_ref)
+    e_orc_dw = row_rel_err(ob["dw_f32"], dw_ref)
+    say(f"[gpu] e2e: q {e_q:.2e} k {e_k:.2e} v {e_v:.2e}; vs unquantised: dx gpu {e_gpu_dx:.3e} "
+        f"oracle {e_orc_dx:.3e}; dw gpu {e_gpu_dw:.3e} oracle {e_orc_dw:.3e}")
+    assert e_gpu_dx <= 1.1 * e_orc_dx + 1e-3
+    assert e_gpu_dw <= 1.1 * e_orc_dw + 1e-3
+
+
+# ------------------------------------------------------------ properties
+
+def test_deterministic_rerun():
+    w = RAGGED
+    a = run(w, seed=9)
+    b = run(w, seed=9)
+    for key in ("q", "k", "v", "x8", "qk_pre", "dqkv", "g8", "dx", "dw"):
+        assert np.array_equal(a[key], b[key]), key
+
+
+def test_scores_depend_only_on_position_difference():
+    # every token has the same x row: pre-RoPE q and k are the same for all
+    # positions, so q_m . k_n may only depend on m - n
+    w = inputs.WORKLOADS["tiny"]
+    row = inputs.make_x(dict(w, seq_len=1), 4)
+    x_bits = np.repeat(row, w["seq_len"], axis=0)
+    r = run(w, seed=4, x_bits=x_bits, backward=False)
+    q = bf16_to_f64(r["q"][0, 0])
+    k = bf16_to_f64(r["k"][0, 0])
+    Sc = q @ k.T
+    worst = max(np.ptp(np.diagonal(Sc, off)) for off in range(-255, 256))
+    say(f"[gpu] max spread along a diagonal: {worst:.3e} (scores up to {np.abs(Sc).max():.1f})")
+    assert worst <= 0.02 * np.abs(Sc).max()
+
+
+def test_zero_inputs_give_zero_outputs():
+    w = RAGGED
+    T = w["n_seq"] * w["seq_len"]
+    x_bits = np.zeros((T, w["d_model"]), dtype=np.uint16)
+    dq, dk, dv = inputs.make_dy(w, 1)
+    dy = (np.zeros_like(dq), np.zeros_like(dk), np.zeros_like(dv))
+    r = run(w, seed=1, x_bits=x_bits, dy=dy)
+    assert r["x_scales"][0] == 1.0 and r["g_scales"][0] == 1.0
+    for key in ("q", "k", "v", "dx"):
+        assert not (bf16_to_f64(r[key]) != 0).any(), key
+    assert not (r["dw"] != 0).any()
+    assert r["status"] == 0
+
+
+def test_nonfinite_activation_sets_status():
+    w = RAGGED
+    x_bits = inputs.make_x(w, 2)
+    x_bits[17, 3] = 0x7FC0  # NaN
+    r = run(w, seed=2, x_bits=x_bits, backward=False)
+    assert r["status"] & 2
+
+
+# ------------------------------------------- the 64k-token step, sampled
+
+def test_step_64k_sampled_rows():
+    """Full-size forward + backward (the benchmark's launch configuration);
+    codes checked in full, float outputs on sampled rows."""
+    w = inputs.WORKLOADS["step_64k"]
+    dims = _dims(w)
+    r = run(w, seed=42)
+    T, H, dqk, dv, S = r["T"], w["n_heads"], w["d_qk"], w["d_v"], w["seq_len"]
+    nq = H * dqk
+    assert r["status"] == 0
+    wp, wpt, s_w, inv_w, _ = oracle.pack_quantize_weights(dims, r["W"])
+    assert np.array_equal(r["w_packed"], wp) and np.array_equal(r["w_packed_t"], wpt)
+    x8, s_x, inv_x, _ = oracle.quantize_bf16(r["x_bits"])
+    assert np.array_equal(r["x8"], x8) and r["x_scales"][0] == s_x
+    assert np.array_equal(r["x8t"], x8.T)
+    rng = np.random.default_rng(0)
+    rows = np.unique(np.concatenate([[0, 1, T - 1], rng.choice(T, 253, replace=False)]))
+    pos = rows % S
+    # GEMM rows
+    y64 = oracle.gemm_e4m3(x8[rows], wp, s_x, s_w)
+    gpu_y = np.concatenate([r["qk_pre"][rows],
+                            r["v"][0][:, rows, :].transpose(1, 0, 2).reshape(len(rows), -1)], axis=1)
+    e_gemm = row_rel_err(bf16_to_f64(gpu_y), bf16_to_f64(oracle.round_bf16(y64)))
+    _, over_gemm = bf16_gemm_excess(gpu_y, y64, oracle.round_bf16)
+    # epilogue rows, fed the GPU's pre-norm values
+    a = bf16_to_f64(r["qk_pre"][rows])
+    qo = oracle.qk_norm_rope_fwd(a[:, :nq].reshape(-1, H, dqk), pos, EPS, BASE)
+    ko = oracle.qk_norm_rope_fwd(a[:, nq:].reshape(-1, H, dqk), pos, EPS, BASE)
+    e_q = row_rel_err(bf16_to_f64(r["q"][0][:, rows, :].transpose(1, 0, 2)), qo)
+    e_k = row_rel_err(bf16_to_f64(r["k"][0][:, rows, :].transpose(1, 0, 2)), ko)
+    # backward epilogue rows
+    dq, dk, dvg = r["dy"]
+    dqo = oracle.qk_norm_rope_bwd(a[:, :nq].reshape(-1, H, dqk),
+                                  bf16_to_f64(dq[0][:, rows, :].transpose(1, 0, 2)), pos, EPS, BASE)
+    dko = oracle.qk_norm_rope_bwd(a[:, nq:].reshape(-1, H, dqk),
+                                  bf16_to_f64(dk[0][:, rows, :].transpose(1, 0, 2)), pos, EPS, BASE)
+    gq = bf16_to_f64(r["dqkv"][rows, :nq]).reshape(-1, H, dqk)
+    gk = bf16_to_f64(r["dqkv"][rows, nq:2 * nq]).reshape(-1, H, dqk)
+    e_dq = row_rel_err(gq, dqo)
+    e_dk = row_rel_err(gk, dko)
+    assert np.array_equal(r["dqkv"][rows, 2 * nq:],
+                          dvg[0][:, rows, :].transpose(1, 0, 2).reshape(len(rows), -1))
+    # gradient codes in full
+    g8, s_g, inv_g, _ = oracle.quantize_bf16(r["dqkv"])
+    assert np.array_equal(r["g8"], g8) and r["g_scales"][0] == s_g
+    assert np.array_equal(r["g8t"], g8.T)
+    # dX rows and dW rows
+    dx64 = oracle.gemm_e4m3(g8[rows], np.ascontiguousarray(wp.T), s_g, s_w)
+    e_dx = row_rel_err(bf16_to_f64(r["dx"][rows]), bf16_to_f64(oracle.round_bf16(dx64)))
+    _, over_dx = bf16_gemm_excess(r["dx"][rows], dx64, oracle.round_bf16)
+    jrows = np.unique(np.concatenate([[0, w["d_model"] - 1], rng.choice(w["d_model"], 30)]))
+    dw = oracle.round_f32(oracle.gemm_e4m3(np.ascontiguousarray(x8[:, jrows].T), g8, s_x, s_g))
+    e_dw = row_rel_err(r["dw"][jrows], dw)
+    say(f"[gpu] 64k: gemm {e_gemm:.2e} q {e_q:.2e} k {e_k:.2e} dq {e_dq:.2e} dk {e_dk:.2e} "
+        f"dx {e_dx:.2e} dw {e_dw:.2e}")
+    assert over_gemm <= GEMM_TOL and over_dx <= GEMM_TOL and e_dw <= GEMM_TOL
+    assert max(e_q, e_k, e_dq, e_dk) <= NORM_TOL
