@@ -194,7 +194,7 @@ def main():
     per_stage = {}
     for name, ms in tr.records():
         per_stage[name] = per_stage.get(name, 0.0) + ms
-    dw_splits = min(8, (-(-T // 128)))
+    dw_splits = B.layout(dims, T).dw_splits
     work = stage_work(w, dw_splits)
     dominant = max(per_stage, key=per_stage.get)
 

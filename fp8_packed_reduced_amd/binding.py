@@ -59,7 +59,8 @@ class Layout(ctypes.Structure):
                 ("saved_x8t", ctypes.c_size_t), ("saved_qk_pre", ctypes.c_size_t),
                 ("saved_x_scales", ctypes.c_size_t), ("fwd_x8", ctypes.c_size_t),
                 ("bwd_dqkv", ctypes.c_size_t), ("bwd_g_scales", ctypes.c_size_t),
-                ("bwd_g8", ctypes.c_size_t), ("bwd_g8t", ctypes.c_size_t)]
+                ("bwd_g8", ctypes.c_size_t), ("bwd_g8t", ctypes.c_size_t),
+                ("bwd_dw_part", ctypes.c_size_t), ("dw_splits", ctypes.c_int32)]
 
 
 _lib = None

@@ -18,7 +18,7 @@ using fpr::round_up;
 constexpr size_t kAlign = 256;
 constexpr int kPartsW = 256;     // amax blocks for W_packed
 constexpr int kPartsAct = 1024;  // amax blocks for x
-constexpr int64_t kMaxTokens = int64_t(1) << 30;
+using fpr::kMaxTokens;
 constexpr size_t kMaxDynLds = 64 * 1024;  // dynamic LDS of one epilogue block
 
 struct Plan {
@@ -188,6 +188,8 @@ int fpr_get_layout(const fpr_dims* dims, int64_t tokens, fpr_layout* out) {
   out->bwd_g_scales = p.b_gsc;
   out->bwd_g8 = p.b_g8;
   out->bwd_g8t = p.b_g8t;
+  out->bwd_dw_part = p.b_dwpart;
+  out->dw_splits = fpr::dw_splits(p.D, p.N, p.Tp);
   return FPR_OK;
 }
 

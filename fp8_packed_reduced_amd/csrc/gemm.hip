@@ -6,45 +6,77 @@
 // transposed view serves the backward pass).
 //
 // All three are C[m][n] = sum_k A[m][k] * B[n][k] with both operands
-// K-contiguous in memory.  A block of 4 waves computes a BM x BN tile; each
-// wave a (BM/2) x (BN/2) sub-tile from 16x16x128 MFMAs.  K advances 128 bytes
-// per step through a double-buffered LDS stage; the 16-byte chunks of each
-// 128-byte LDS row are XOR-swizzled by the row index so that the 16 rows a
-// fragment read touches fall on distinct banks.
+// K-contiguous in memory, built from v_mfma_scale_f32_32x32x64_f8f6f4 with
+// neutral E8M0 scales (it sustains ~4.3 PFLOP/s here, against ~3.2-3.9 for
+// the 16x16x128 form).
 //
-// The MFMA's first operand is fed from B (n rows) and its second from A (m
-// rows).  Its 16x16 result then lands with lane l holding four consecutive n
-// (4*(l/16) .. +3) of one m (l % 16): each lane stores 8 contiguous bytes of
-// a row-major bf16 output (or 16 bytes of fp32).  Which k each byte of a
-// lane's 32-byte operand stands for does not matter, as long as both
-// operands use the same assignment, which they do.
+// A block is 8 waves with two roles.  Waves 0-3 (one per SIMD) are the
+// matrix waves: 2 x 2 of them compute a BM x BN tile and never load from
+// global memory.  Waves 4-7 are the copy waves: they fill a ring of three
+// LDS stages, K advancing 128 bytes per stage, with direct global-to-LDS
+// loads and wait only on their own vector-memory counter.  As that counter
+// is per wave, the matrix waves' output stores never hold up the operand
+// stream, and the copy waves keep two stages in flight while the matrix
+// waves work on the third.  One workgroup barrier per step hands a stage
+// over; it carries no memory fence, so no wave waits for stores there.
+//
+// One load instruction of a copy wave fills 1 KiB = 8 consecutive 128-byte
+// LDS rows; lane i lands at physical 16-byte chunk i % 8 of row i / 8 and
+// therefore fetches logical chunk (i % 8) ^ (row % 8): the XOR swizzle that
+// spreads the 8 rows of one LDS access phase over all banks.
+//
+// The MFMA's first operand is fed from B (n rows), its second from A (m
+// rows).  The 32x32 result then lands with lane l holding, for each group
+// g of four accumulator registers, four consecutive n (8g + 4(l/32) + 0..3)
+// of one m (l % 32).  Which k each byte of a lane's 32-byte operand stands
+// for does not matter, as both operands use the same assignment.
+//
+// bf16 outputs (forward, dX) come from a persistent kernel, one block per
+// CU walking its tiles; a finished 32-row slice of a matrix wave's tile is
+// transposed through that wave's own 4 KiB of LDS so that every lane
+// stores a 16-byte run of one row.  dW (K = tokens) splits K over blocks
+// and writes fp32 partial sums that a second kernel adds in split order.
 #include "common.hpp"
 #include "launch.hpp"
 
 namespace fpr {
 
+typedef float v16f __attribute__((ext_vector_type(16)));
+
 constexpr int kBK = 128;  // bytes (= e4m3 elements) of K per step
+constexpr int kMmaWaves = 4, kCopyWaves = 4;
+constexpr int kGemmThreads = 64 * (kMmaWaves + kCopyWaves);
+constexpr int kStages = 3;
 
 template <int BM, int BN>
 struct TileCfg {
-  static constexpr int WM = BM / 2, WN = BN / 2;        // 2 x 2 waves
-  static constexpr int FM = WM / 16, FN = WN / 16;      // 16x16 fragments per wave
-  static constexpr int A_CH = BM * (kBK / 16) / kThreads;  // 16 B chunks per thread
-  static constexpr int B_CH = BN * (kBK / 16) / kThreads;
-  static constexpr int STAGE = (BM + BN) * kBK;
-  static_assert(A_CH * kThreads == BM * 8 && B_CH * kThreads == BN * 8, "tile/threads");
+  static constexpr int BM_ = BM, BN_ = BN;
+  static constexpr int WM = BM / 2, WN = BN / 2;       // 2 x 2 matrix waves
+  static constexpr int FM = WM / 32, FN = WN / 32;     // 32x32 fragments per wave
+  static constexpr int STAGE_BYTES = (BM + BN) * kBK;  // one K step of A and B rows
+  static constexpr int BLOCKS = (BM + BN) / 8;         // 1 KiB DMA blocks per stage
+  static constexpr int PER_WAVE = BLOCKS / kCopyWaves;
+  static constexpr int A_PER_WAVE = BM / 8 / kCopyWaves;  // a wave's first blocks hold A rows
+  static_assert(FM * 64 == BM && FN * 64 == BN, "tile/waves");
+  static_assert(BLOCKS % kCopyWaves == 0 && (BM / 8) % kCopyWaves == 0, "DMA blocks per wave");
+  static_assert(PER_WAVE < 64, "vmcnt range");
 };
 
-__device__ inline int swz(int row, int chunk) { return row * kBK + ((chunk ^ (row & 7)) << 4); }
-
-// Workgroups are dispatched round-robin over the 8 XCDs (block b -> XCD b % 8).
-// Give each XCD a contiguous run of tiles so that the N tiles of one M tile,
-// which share their A rows, run on the same XCD and share its L2.
-__device__ inline int xcd_contiguous(int b, int nblocks) {
-  const int per = nblocks / 8, rem = nblocks % 8;
-  const int xcd = b % 8, local = b / 8;
-  return xcd < rem ? xcd * (per + 1) + local : rem * (per + 1) + (xcd - rem) * per + local;
+// Workgroup barrier without a memory fence, after this wave's LDS
+// operations are done (the matrix waves' fragment reads, the copy waves'
+// tail blanking).  Global stores stay in flight.  The clobber keeps the
+// compiler from moving memory accesses across it.
+__device__ __forceinline__ void barrier_lds() {
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
 }
+
+// Wait until at most N vector-memory operations of this wave are in flight.
+template <int N>
+__device__ __forceinline__ void wait_vm() {
+  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
+
+__device__ inline int swz(int row, int chunk) { return row * kBK + ((chunk ^ (row & 7)) << 4); }
 
 __device__ inline v8i as_v8i(uint4 lo, uint4 hi) {
   v8i r;
@@ -53,166 +85,415 @@ __device__ inline v8i as_v8i(uint4 lo, uint4 hi) {
   return r;
 }
 
-// splits == 1: tiles mapped XCD-contiguously.  splits > 1 (split-K): block b
-// takes split b % splits of tile b / splits, so with 8 splits every XCD
-// streams one K range for all tiles and the A/B rows are shared in its L2.
-template <int BM, int BN, class Epi>
-__global__ __launch_bounds__(kThreads) void gemm_e4m3_kernel(
-    const uint8_t* __restrict__ A, int64_t lda, const uint8_t* __restrict__ B, int64_t ldb,
-    int M, int N, int K, int n_tiles, int splits, int ksteps_per_split, Epi epi) {
-  using C = TileCfg<BM, BN>;
-  __shared__ __attribute__((aligned(16))) uint8_t lds[2 * C::STAGE];
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int wm = wave >> 1, wn = wave & 1;
-
-  int split = 0, tile;
-  if (splits > 1) {
-    split = blockIdx.x % splits;
-    tile = blockIdx.x / splits;
-  } else {
-    tile = xcd_contiguous(blockIdx.x, gridDim.x);
-  }
-  const int m0 = (tile / n_tiles) * BM, n0 = (tile % n_tiles) * BN;
-  const int nk = (K + kBK - 1) / kBK;
-  const int ks0 = split * ksteps_per_split;
-  const int ks1 = min(nk, ks0 + ksteps_per_split);
-
-  v4f acc[C::FM][C::FN];
-#pragma unroll
-  for (int i = 0; i < C::FM; ++i)
-#pragma unroll
-    for (int j = 0; j < C::FN; ++j) acc[i][j] = v4f{0.f, 0.f, 0.f, 0.f};
-
-  uint4 ra[C::A_CH], rb[C::B_CH];
-  // Rows past M / N are clamped to the last valid row (their results are
-  // never stored); K chunks past K are zero.
-  auto gload = [&](int ks) {
-    const int k0 = ks * kBK;
-#pragma unroll
-    for (int i = 0; i < C::A_CH; ++i) {
-      const int q = tid + kThreads * i, row = q >> 3, ch = q & 7;
-      const int64_t grow = min(m0 + row, M - 1);
-      const int kc = k0 + ch * 16;
-      ra[i] = kc < K ? *reinterpret_cast<const uint4*>(A + grow * lda + kc) : make_uint4(0, 0, 0, 0);
-    }
-#pragma unroll
-    for (int i = 0; i < C::B_CH; ++i) {
-      const int q = tid + kThreads * i, row = q >> 3, ch = q & 7;
-      const int64_t grow = min(n0 + row, N - 1);
-      const int kc = k0 + ch * 16;
-      rb[i] = kc < K ? *reinterpret_cast<const uint4*>(B + grow * ldb + kc) : make_uint4(0, 0, 0, 0);
-    }
-  };
-  auto sstore = [&](int buf) {
-    uint8_t* As = lds + buf * C::STAGE;
-    uint8_t* Bs = As + BM * kBK;
-#pragma unroll
-    for (int i = 0; i < C::A_CH; ++i) {
-      const int q = tid + kThreads * i;
-      *reinterpret_cast<uint4*>(As + swz(q >> 3, q & 7)) = ra[i];
-    }
-#pragma unroll
-    for (int i = 0; i < C::B_CH; ++i) {
-      const int q = tid + kThreads * i;
-      *reinterpret_cast<uint4*>(Bs + swz(q >> 3, q & 7)) = rb[i];
-    }
-  };
-
-  if (ks0 < ks1) {
-    gload(ks0);
-    sstore(0);
-    __syncthreads();
-    const int g = lane >> 4, r16 = lane & 15;
-    for (int ks = ks0; ks < ks1; ++ks) {
-      const int buf = (ks - ks0) & 1;
-      if (ks + 1 < ks1) gload(ks + 1);
-      const uint8_t* As = lds + buf * C::STAGE;
-      const uint8_t* Bs = As + BM * kBK;
-      v8i fb[C::FN];
-#pragma unroll
-      for (int j = 0; j < C::FN; ++j) {
-        const int row = wn * C::WN + j * 16 + r16;
-        fb[j] = as_v8i(*reinterpret_cast<const uint4*>(Bs + swz(row, 2 * g)),
-                       *reinterpret_cast<const uint4*>(Bs + swz(row, 2 * g + 1)));
-      }
-#pragma unroll
-      for (int i = 0; i < C::FM; ++i) {
-        const int row = wm * C::WM + i * 16 + r16;
-        const v8i fa = as_v8i(*reinterpret_cast<const uint4*>(As + swz(row, 2 * g)),
-                              *reinterpret_cast<const uint4*>(As + swz(row, 2 * g + 1)));
-#pragma unroll
-        for (int j = 0; j < C::FN; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
-              fb[j], fa, acc[i][j], 0, 0, 0, 127, 0, 127);  // e4m3 x e4m3, unit E8M0 scales
-      }
-      if (ks + 1 < ks1) sstore(buf ^ 1);
-      __syncthreads();
-    }
-  }
-
-  Epi e = epi;
-  e.prepare();
-#pragma unroll
-  for (int i = 0; i < C::FM; ++i)
-#pragma unroll
-    for (int j = 0; j < C::FN; ++j) {
-      const int m = m0 + wm * C::WM + i * 16 + (lane & 15);
-      const int n = n0 + wn * C::WN + j * 16 + 4 * (lane >> 4);
-      e(split, m, n, acc[i][j]);
-    }
+// One 32-row MFMA operand for K substep h (64 bytes): lane l takes row
+// `row` (= base + l % 32) and the 32 bytes [64h + 32(l/32), +32).
+__device__ __forceinline__ v8i lds_frag(const uint8_t* base, int row, int kg, int h) {
+  const int c = 4 * h + 2 * kg;
+  return as_v8i(*reinterpret_cast<const uint4*>(base + swz(row, c)),
+                *reinterpret_cast<const uint4*>(base + swz(row, c + 1)));
 }
 
-// ------------------------------------------------------------- epilogues
+__device__ __forceinline__ v16f mfma32(v8i b, v8i a, v16f c) {
+  return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(b, a, c, 0, 0, 0, 127, 0, 127);
+}
 
-// Forward: scale, round to bf16; Q|K columns to the saved pre-norm rows,
-// V columns straight into the head-major v output.
+// ------------------------------------------------------------ schedule
+
+// The operands and the (tile, K step) pairs a block walks, in order.  Step
+// g belongs to the block's tile number ord = g / nk, which is tile
+// first_tile + ord * tile_stride, at K step ks0 + g % nk.  A persistent
+// block has several tiles (stride = grid size) and all K steps; a split-K
+// block has one tile and a K range.
+struct Gemm {
+  const uint8_t* A;
+  int64_t lda;
+  const uint8_t* B;
+  int64_t ldb;
+  int M, N, K, n_tiles;
+};
+
+struct Sched {
+  int nk, ks0, first_tile, tile_stride, steps;
+  __device__ int ord(int g) const { return g / nk; }
+  __device__ int tile(int g) const { return first_tile + ord(g) * tile_stride; }
+  __device__ int ks(int g) const { return ks0 + g - ord(g) * nk; }
+};
+
+// ------------------------------------------------------------ copy waves
+
+// Per-lane DMA offsets of one tile: block t of copy wave w covers stage
+// rows [8(w + 4t), +8).  Offsets are relative to the tile's first A (resp.
+// B) row, with rows past M (resp. N) clamped to the last valid one.
+template <class C>
+struct CopyState {
+  uint32_t off[C::PER_WAVE];
+  const uint8_t* Atile;
+  const uint8_t* Btile;
+  int tile;    // tile the offsets belong to
+  int issued;  // steps issued so far
+};
+
+template <class C>
+__device__ __forceinline__ void dma_plan(CopyState<C>& st, const Gemm& gm, int tile, int cw,
+                                         int lane) {
+  const int m0 = (tile / gm.n_tiles) * C::BM_, n0 = (tile % gm.n_tiles) * C::BN_;
+  const int rl = lane >> 3, p = lane & 7;
+#pragma unroll
+  for (int t = 0; t < C::PER_WAVE; ++t) {
+    const int row = (cw + kCopyWaves * t) * 8 + rl;
+    const uint32_t chunk = (uint32_t)((p ^ (row & 7)) << 4);
+    if (t < C::A_PER_WAVE)
+      st.off[t] = (uint32_t)((min(m0 + row, gm.M - 1) - m0) * gm.lda) + chunk;
+    else
+      st.off[t] = (uint32_t)((min(n0 + row - C::BM_, gm.N - 1) - n0) * gm.ldb) + chunk;
+  }
+  st.Atile = gm.A + (int64_t)m0 * gm.lda;
+  st.Btile = gm.B + (int64_t)n0 * gm.ldb;
+  st.tile = tile;
+}
+
+// Issue the DMA of the block's next step into its stage.  With KTAIL,
+// chunks past K are fetched from inside the row instead and blanked by
+// zero_tail() once they have landed.
+template <class C, bool KTAIL>
+__device__ __forceinline__ void issue_next(CopyState<C>& st, uint8_t* lds, const Gemm& gm,
+                                           const Sched& sc, int cw, int lane) {
+  const int g = st.issued++;
+  const int tile = sc.tile(g);
+  if (tile != st.tile) dma_plan<C>(st, gm, tile, cw, lane);
+  const int k0 = sc.ks(g) * kBK;
+  const uint8_t* Ak = st.Atile + k0;
+  const uint8_t* Bk = st.Btile + k0;
+  uint8_t* stage = lds + (g % kStages) * C::STAGE_BYTES;
+#pragma unroll
+  for (int t = 0; t < C::PER_WAVE; ++t) {
+    uint32_t off = st.off[t];
+    if (KTAIL) {
+      const int row = (cw + kCopyWaves * t) * 8 + (lane >> 3);
+      const int kc = k0 + (((lane & 7) ^ (row & 7)) << 4);
+      if (kc >= gm.K) off -= (uint32_t)(kc - (gm.K - 16));
+    }
+#if defined(__HIP_DEVICE_COMPILE__)  // an AMDGPU builtin: the host pass never runs this
+    __builtin_amdgcn_global_load_lds((t < C::A_PER_WAVE ? Ak : Bk) + off,
+                                     stage + (cw + kCopyWaves * t) * 1024, 16, 0, 0);
+#endif
+  }
+}
+
+template <class C>
+__device__ __forceinline__ void zero_tail(uint8_t* stage, int K, int ks, int cw, int lane) {
+  const int k0 = ks * kBK;
+  if (k0 + kBK <= K) return;
+#pragma unroll
+  for (int t = 0; t < C::PER_WAVE; ++t) {
+    const int blk = cw + kCopyWaves * t;
+    const int row = blk * 8 + (lane >> 3);
+    const int kc = k0 + (((lane & 7) ^ (row & 7)) << 4);
+    if (kc >= K) *reinterpret_cast<uint4*>(stage + blk * 1024 + lane * 16) = make_uint4(0, 0, 0, 0);
+  }
+}
+
+// Wait until step g has landed in its stage (every step after it that is
+// already issued may stay in flight: at most one, of PER_WAVE loads).
+template <class C, bool KTAIL>
+__device__ __forceinline__ void land(const CopyState<C>& st, uint8_t* lds, const Gemm& gm,
+                                     const Sched& sc, int g, int cw, int lane) {
+  if (st.issued > g + 1)
+    wait_vm<C::PER_WAVE>();
+  else
+    wait_vm<0>();
+  if (KTAIL) zero_tail<C>(lds + (g % kStages) * C::STAGE_BYTES, gm.K, sc.ks(g), cw, lane);
+}
+
+// The copy waves' side of the pipeline.  Before barrier -1 steps 0 and 1
+// are issued and step 0 has landed; in iteration g step g + 2 is issued
+// into the stage step g - 1 used (read before barrier g - 1) and step g + 1
+// has landed before barrier g.
+template <class C, bool KTAIL>
+__device__ __forceinline__ void copy_role(uint8_t* lds, const Gemm& gm, const Sched& sc, int cw,
+                                          int lane) {
+  CopyState<C> st;
+  st.tile = -1;
+  st.issued = 0;
+  if (sc.steps > 0) issue_next<C, KTAIL>(st, lds, gm, sc, cw, lane);
+  if (sc.steps > 1) issue_next<C, KTAIL>(st, lds, gm, sc, cw, lane);
+  if (sc.steps > 0) land<C, KTAIL>(st, lds, gm, sc, 0, cw, lane);
+  barrier_lds();
+  for (int g = 0; g < sc.steps; ++g) {
+    if (g + 2 < sc.steps) issue_next<C, KTAIL>(st, lds, gm, sc, cw, lane);
+    if (g + 1 < sc.steps) land<C, KTAIL>(st, lds, gm, sc, g + 1, cw, lane);
+    barrier_lds();
+  }
+}
+
+// ------------------------------------------------------------ matrix waves
+
+// Operand fragments of one K half-step (64 bytes of K) of a matrix wave.
+template <class C>
+struct Half {
+  v8i a[C::FM];
+  v8i b[C::FN];
+};
+
+template <class C>
+__device__ __forceinline__ void load_half(const uint8_t* stage, int arow0, int brow0, int kg,
+                                          int h, Half<C>& f) {
+#pragma unroll
+  for (int j = 0; j < C::FN; ++j) f.b[j] = lds_frag(stage + C::BM_ * kBK, brow0 + j * 32, kg, h);
+#pragma unroll
+  for (int i = 0; i < C::FM; ++i) f.a[i] = lds_frag(stage, arow0 + i * 32, kg, h);
+}
+
+// The FM x FN MFMAs of one half-step on the operands in f, while the
+// operands of the half-step after it (K half h of stage `src`) stream into
+// f: its B fragments first, then A fragment i as soon as the current A
+// fragment i has had its last use.  A fragment is thus loaded a whole
+// half-step (FM x FN MFMAs) before it is needed.
+template <class C>
+__device__ __forceinline__ void mma_half(v16f (&acc)[C::FM][C::FN], Half<C>& f, const uint8_t* src,
+                                         int arow0, int brow0, int kg, int h) {
+  v8i nb[C::FN];
+#pragma unroll
+  for (int j = 0; j < C::FN; ++j) nb[j] = lds_frag(src + C::BM_ * kBK, brow0 + j * 32, kg, h);
+#pragma unroll
+  for (int i = 0; i < C::FM; ++i) {
+#pragma unroll
+    for (int j = 0; j < C::FN; ++j) acc[i][j] = mfma32(f.b[j], f.a[i], acc[i][j]);
+    f.a[i] = lds_frag(src, arow0 + i * 32, kg, h);
+#pragma unroll
+    for (int j = 0; j < C::FN; ++j) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // 1 MFMA
+      __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);  // then up to 2 LDS reads
+    }
+  }
+#pragma unroll
+  for (int j = 0; j < C::FN; ++j) f.b[j] = nb[j];
+}
+
+template <class C>
+__device__ __forceinline__ void zero_acc(v16f (&acc)[C::FM][C::FN]) {
+#pragma unroll
+  for (int i = 0; i < C::FM; ++i)
+#pragma unroll
+    for (int j = 0; j < C::FN; ++j)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
+}
+
+// The matrix waves' pipeline over the block's steps.  Half 0 of step g
+// was loaded after barrier g - 1; half 1 streams in during half 0's MFMAs;
+// then barrier g (all of this wave's reads of step g are done, step g + 1
+// has landed), and half 0 of step g + 1 streams in during half 1's MFMAs.
+// `tile_done(acc)` runs after the last K step of each tile (every nk
+// steps) and must leave acc zeroed.  After the block's last step the
+// stream reads a stage whose contents are not used.
+template <class C, class TileDone>
+__device__ __forceinline__ void mma_role(const uint8_t* lds, const Sched& sc, int wm, int wn,
+                                         int lane, v16f (&acc)[C::FM][C::FN],
+                                         const TileDone& tile_done) {
+  const int kg = lane >> 5;
+  const int arow0 = wm * C::WM + (lane & 31), brow0 = wn * C::WN + (lane & 31);
+  zero_acc<C>(acc);
+  barrier_lds();
+  Half<C> f;
+  load_half<C>(lds, arow0, brow0, kg, 0, f);
+  int ks_in_tile = 0;
+  for (int g = 0; g < sc.steps; ++g) {
+    const uint8_t* cur = lds + (g % kStages) * C::STAGE_BYTES;
+    const uint8_t* nxt = lds + ((g + 1) % kStages) * C::STAGE_BYTES;
+    mma_half<C>(acc, f, cur, arow0, brow0, kg, 1);
+    barrier_lds();
+    mma_half<C>(acc, f, nxt, arow0, brow0, kg, 0);
+    if (++ks_in_tile == sc.nk) {
+      tile_done(acc);
+      ks_in_tile = 0;
+    }
+  }
+}
+
+// ------------------------------------------------------------ epilogues
+
+// bf16 tile store through the matrix wave's own LDS slice: 32 rows x WN
+// columns (WN * 2 bytes per row, 16-byte chunks XOR-swizzled by row).  Each
+// lane writes its 4-column groups, then reads back whole 16-byte chunks:
+// lane l takes chunk l % 8 of rows l / 8 + 8q.  LDS operations of one wave
+// complete in order, so no wait is needed between the two.
+template <class C>
+struct WaveSlice {
+  static constexpr int BYTES = 32 * C::WN * 2;
+  static_assert(C::WN == 64, "8 chunks of 16 bytes per row");
+  __device__ static int at(int row, int chunk) {
+    return row * (C::WN * 2) + ((chunk ^ (row & 7)) << 4);
+  }
+};
+
+// Forward: Q|K columns to the saved pre-norm rows, V columns straight into
+// the head-major v output.  A chunk of 8 columns never straddles a V head
+// (d_v % 16 == 0) nor the Q|K / V boundary.
 struct EpiFwd {
-  const float* sx;
-  const float* sw;
   uint16_t* qk_pre;
   uint16_t* v;
-  int M, N, nqk2, H, dv, S;
-  float alpha;
-  __device__ void prepare() { alpha = sx[0] * sw[0]; }
-  __device__ void operator()(int, int m, int n, v4f a) const {
-    if (m >= M || n >= N) return;
-    const uint2 p = make_uint2(pack_bf16x2(a[0] * alpha, a[1] * alpha),
-                               pack_bf16x2(a[2] * alpha, a[3] * alpha));
-    if (n < nqk2) {
-      *reinterpret_cast<uint2*>(qk_pre + (int64_t)m * nqk2 + n) = p;
-    } else {
+  int N, nqk2, H, dv, S;
+  struct Col { int n; int64_t voff; bool qk; bool live; };
+  struct Row { int m; int b; int s; };
+  __device__ Col column(int n) const {
+    Col c{n, 0, n < nqk2, n < N};
+    if (!c.qk && c.live) {
       const int nn = n - nqk2, h = nn / dv, j = nn - h * dv;
-      const int b = m / S, s = m - b * S;
-      *reinterpret_cast<uint2*>(v + (((int64_t)b * H + h) * S + s) * dv + j) = p;
+      c.voff = (int64_t)h * S * dv + j;
     }
+    return c;
+  }
+  __device__ Row row(int m) const { return Row{m, m / S, m % S}; }
+  __device__ void advance(Row& r, int step) const {
+    r.m += step;
+    r.s += step;
+    while (r.s >= S) { r.s -= S; ++r.b; }
+  }
+  __device__ void chunk(const Row& r, const Col& c, uint4 val) const {
+    if (!c.live) return;
+    if (c.qk)
+      *reinterpret_cast<uint4*>(qk_pre + (int64_t)r.m * nqk2 + c.n) = val;
+    else
+      *reinterpret_cast<uint4*>(v + (int64_t)r.b * H * S * dv + (int64_t)r.s * dv + c.voff) = val;
   }
 };
 
 struct EpiDx {
-  const float* sg;
-  const float* sw;
   uint16_t* dx;
-  int M, N;
-  float alpha;
-  __device__ void prepare() { alpha = sg[0] * sw[0]; }
-  __device__ void operator()(int, int m, int n, v4f a) const {
-    if (m >= M || n >= N) return;
-    *reinterpret_cast<uint2*>(dx + (int64_t)m * N + n) =
-        make_uint2(pack_bf16x2(a[0] * alpha, a[1] * alpha), pack_bf16x2(a[2] * alpha, a[3] * alpha));
+  int N;
+  struct Col { int n; };
+  struct Row { int m; };
+  __device__ Col column(int n) const { return Col{n}; }
+  __device__ Row row(int m) const { return Row{m}; }
+  __device__ void advance(Row& r, int step) const { r.m += step; }
+  __device__ void chunk(const Row& r, const Col& c, uint4 val) const {
+    if (c.n < N) *reinterpret_cast<uint4*>(dx + (int64_t)r.m * N + c.n) = val;
   }
 };
 
-// dW split-K: unscaled fp32 partial sums, part[split][m][n].
-struct EpiDwPart {
-  float* part;
-  int M, N;
-  __device__ void prepare() {}
-  __device__ void operator()(int split, int m, int n, v4f a) const {
-    if (m >= M || n >= N) return;
-    *reinterpret_cast<float4*>(part + ((int64_t)split * M + m) * N + n) =
-        make_float4(a[0], a[1], a[2], a[3]);
+template <class C, class Epi>
+__device__ __forceinline__ void store_bf16_tile(const v16f (&acc)[C::FM][C::FN], float alpha,
+                                                uint8_t* slice, const Epi& epi, int M, int m0,
+                                                int n0, int wm, int wn, int lane) {
+  using W = WaveSlice<C>;
+  const int p = lane & 7, rq = lane >> 3;
+  const typename Epi::Col col = epi.column(n0 + wn * C::WN + 8 * p);
+  typename Epi::Row row = epi.row(m0 + wm * C::WM + rq);
+#pragma unroll
+  for (int i = 0; i < C::FM; ++i) {
+#pragma unroll
+    for (int j = 0; j < C::FN; ++j)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const v16f& a = acc[i][j];
+        *reinterpret_cast<uint2*>(slice + W::at(lane & 31, 4 * j + g) + 8 * (lane >> 5)) =
+            make_uint2(pack_bf16x2(a[4 * g] * alpha, a[4 * g + 1] * alpha),
+                       pack_bf16x2(a[4 * g + 2] * alpha, a[4 * g + 3] * alpha));
+      }
+    uint4 val[4];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) val[q] = *reinterpret_cast<const uint4*>(slice + W::at(rq + 8 * q, p));
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      if (row.m < M) epi.chunk(row, col, val[q]);
+      epi.advance(row, 8);
+    }
   }
-};
+}
+
+// fp32 split-K partials: lane l holds four consecutive n of one m.
+template <class C>
+__device__ __forceinline__ void store_partial_tile(const v16f (&acc)[C::FM][C::FN], float* part,
+                                                   int M, int N, int m0, int n0, int wm, int wn,
+                                                   int lane) {
+#pragma unroll
+  for (int i = 0; i < C::FM; ++i)
+#pragma unroll
+    for (int j = 0; j < C::FN; ++j)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const int m = m0 + wm * C::WM + i * 32 + (lane & 31);
+        const int n = n0 + wn * C::WN + j * 32 + 8 * g + 4 * (lane >> 5);
+        if (m < M && n < N)
+          *reinterpret_cast<float4*>(part + (int64_t)m * N + n) =
+              make_float4(acc[i][j][4 * g], acc[i][j][4 * g + 1], acc[i][j][4 * g + 2],
+                          acc[i][j][4 * g + 3]);
+      }
+}
+
+// -------------------------------------------------- persistent bf16 GEMM
+
+// The first tile of block b: within a round of gridDim.x tiles the 8 XCDs
+// (blocks are dispatched round-robin over them) each take a contiguous run,
+// so concurrent tiles of one XCD share A rows in its L2.
+__device__ __forceinline__ int first_tile_of(int b, int G) {
+  return (G % 8 == 0) ? (b % 8) * (G / 8) + b / 8 : b;
+}
+
+template <int BM, int BN, bool KTAIL, class Epi>
+__global__ __launch_bounds__(kGemmThreads, 1) void gemm_bf16out_kernel(
+    Gemm gm, int ntiles, const float* __restrict__ sa, const float* __restrict__ sb, Epi epi) {
+  using C = TileCfg<BM, BN>;
+  __shared__ __attribute__((aligned(16))) uint8_t lds[kStages * C::STAGE_BYTES];
+  __shared__ __attribute__((aligned(16))) uint8_t slices[kMmaWaves * WaveSlice<C>::BYTES];
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int G = gridDim.x;
+  Sched sc;
+  sc.nk = (gm.K + kBK - 1) / kBK;
+  sc.ks0 = 0;
+  sc.first_tile = first_tile_of(blockIdx.x, G);
+  sc.tile_stride = G;
+  const int my_tiles = sc.first_tile < ntiles ? (ntiles - sc.first_tile + G - 1) / G : 0;
+  sc.steps = my_tiles * sc.nk;
+  if (wave >= kMmaWaves) {
+    copy_role<C, KTAIL>(lds, gm, sc, wave - kMmaWaves, lane);
+    return;
+  }
+  const int wm = wave >> 1, wn = wave & 1;
+  const float alpha = sa[0] * sb[0];
+  uint8_t* slice = slices + wave * WaveSlice<C>::BYTES;
+  int tile = sc.first_tile;
+  v16f acc[C::FM][C::FN];
+  mma_role<C>(lds, sc, wm, wn, lane, acc, [&](v16f (&a)[C::FM][C::FN]) {
+    store_bf16_tile<C, Epi>(a, alpha, slice, epi, gm.M, (tile / gm.n_tiles) * BM,
+                            (tile % gm.n_tiles) * BN, wm, wn, lane);
+    zero_acc<C>(a);
+    tile += sc.tile_stride;
+  });
+}
+
+// ------------------------------------------------------------ dW split-K
+
+// Block b takes K split b % splits of tile b / splits.  Unscaled fp32
+// partial sums go to part[split][m][n]; a split with no K steps writes
+// zeros.
+template <int BM, int BN>
+__global__ __launch_bounds__(kGemmThreads, 1) void gemm_dw_part_kernel(
+    Gemm gm, int splits, int ksteps_per_split, float* __restrict__ part) {
+  using C = TileCfg<BM, BN>;
+  __shared__ __attribute__((aligned(16))) uint8_t lds[kStages * C::STAGE_BYTES];
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int split = blockIdx.x % splits, tile = blockIdx.x / splits;
+  const int nk_all = (gm.K + kBK - 1) / kBK;
+  Sched sc;
+  sc.ks0 = split * ksteps_per_split;
+  sc.steps = max(0, min(nk_all, sc.ks0 + ksteps_per_split) - sc.ks0);
+  sc.nk = sc.steps > 0 ? sc.steps : 1;
+  sc.first_tile = tile;
+  sc.tile_stride = 0;
+  if (wave >= kMmaWaves) {
+    copy_role<C, false>(lds, gm, sc, wave - kMmaWaves, lane);
+    return;
+  }
+  const int wm = wave >> 1, wn = wave & 1;
+  v16f acc[C::FM][C::FN];
+  mma_role<C>(lds, sc, wm, wn, lane, acc, [](v16f (&)[C::FM][C::FN]) {});
+  store_partial_tile<C>(acc, part + (int64_t)split * gm.M * gm.N, gm.M, gm.N,
+                        (tile / gm.n_tiles) * BM, (tile % gm.n_tiles) * BN, wm, wn, lane);
+}
 
 // Sum the split-K partials in split order (deterministic), scale, and write
 // the three column blocks of dW.
@@ -238,49 +519,77 @@ __global__ __launch_bounds__(kThreads) void dw_reduce_kernel(
 
 // ------------------------------------------------------------- launchers
 
-constexpr int kBM = 256, kBN = 192;
+constexpr int kBMo = 256, kBNo = 128;  // bf16-output tile (persistent)
+constexpr int kBMw = 192, kBNw = 192;  // dW split-K tile
+// Split-K counts are chosen for a 256-CU part; the choice must not depend on
+// the device present, since workspace sizes are queried without one.
+constexpr int kSplitCUs = 256, kMaxSplits = 8;
+static_assert((kBMw - 1) * kMaxTokens + kBK <= 0xFFFFFFFFll &&
+                  (kBNw - 1) * kMaxTokens + kBK <= 0xFFFFFFFFll,
+              "dW row offsets must fit 32 bits");
+
+static int cu_count() {
+  int dev = 0, n = 0;
+  if (hipGetDevice(&dev) != hipSuccess ||
+      hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
+    n = 256;
+  return n;
+}
 
 template <class Epi>
-static void launch_gemm(const uint8_t* A, int64_t lda, const uint8_t* B, int64_t ldb, int M,
-                        int N, int K, int splits, int ksteps_per_split, const Epi& epi,
-                        hipStream_t s) {
-  const int m_tiles = (int)ceil_div(M, kBM), n_tiles = (int)ceil_div(N, kBN);
-  const int blocks = m_tiles * n_tiles * splits;
-  gemm_e4m3_kernel<kBM, kBN, Epi><<<blocks, kThreads, 0, s>>>(A, lda, B, ldb, M, N, K, n_tiles,
-                                                              splits, ksteps_per_split, epi);
+static void launch_bf16out(const Gemm& gm, const float* sa, const float* sb, const Epi& epi,
+                           hipStream_t s) {
+  const int ntiles = (int)ceil_div(gm.M, kBMo) * gm.n_tiles;
+  const int cus = cu_count();
+  const int blocks = ntiles < cus ? ntiles : cus;
+  if (gm.K % kBK)
+    gemm_bf16out_kernel<kBMo, kBNo, true, Epi><<<blocks, kGemmThreads, 0, s>>>(gm, ntiles, sa,
+                                                                              sb, epi);
+  else
+    gemm_bf16out_kernel<kBMo, kBNo, false, Epi><<<blocks, kGemmThreads, 0, s>>>(gm, ntiles, sa,
+                                                                               sb, epi);
 }
 
 void launch_gemm_fwd(const uint8_t* x8, const uint8_t* w_packed_t, int T, int N, int D,
                      const float* x_scales, const float* w_scales, uint16_t* qk_pre, int nqk2,
                      uint16_t* v, int H, int d_v, int seq_len, hipStream_t s) {
-  EpiFwd e{x_scales, w_scales, qk_pre, v, T, N, nqk2, H, d_v, seq_len, 0.f};
-  const int nk = (int)ceil_div(D, kBK);
-  launch_gemm(x8, D, w_packed_t, D, T, N, D, 1, nk, e, s);
+  const Gemm gm{x8, D, w_packed_t, D, T, N, D, (int)ceil_div(N, kBNo)};
+  launch_bf16out(gm, x_scales, w_scales, EpiFwd{qk_pre, v, N, nqk2, H, d_v, seq_len}, s);
 }
 
 void launch_gemm_dx(const uint8_t* g8, const uint8_t* w_packed, int T, int D, int Np,
                     const float* g_scales, const float* w_scales, uint16_t* dx, hipStream_t s) {
-  EpiDx e{g_scales, w_scales, dx, T, D, 0.f};
-  const int nk = (int)ceil_div(Np, kBK);
-  launch_gemm(g8, Np, w_packed, Np, T, D, Np, 1, nk, e, s);
+  const Gemm gm{g8, Np, w_packed, Np, T, D, Np, (int)ceil_div(D, kBNo)};
+  launch_bf16out(gm, g_scales, w_scales, EpiDx{dx, D}, s);
 }
 
-int dw_splits(int64_t tokens_padded) {
+// The split count s <= kMaxSplits (and <= the K steps) whose tiles x s
+// blocks fill the last round of kSplitCUs best; ties go to fewer splits.
+int dw_splits(int D, int Np, int64_t tokens_padded) {
   const int64_t nk = ceil_div(tokens_padded, kBK);
-  return (int)(nk < 8 ? nk : 8);
+  const int64_t tiles = ceil_div(D, kBMw) * ceil_div(Np, kBNw);
+  int best = 1;
+  double best_fill = 0.0;
+  for (int sp = 1; sp <= kMaxSplits && sp <= nk; ++sp) {
+    const int64_t blocks = tiles * sp;
+    const double fill = (double)blocks / (double)(ceil_div(blocks, kSplitCUs) * kSplitCUs);
+    if (fill > best_fill + 1e-9) { best_fill = fill; best = sp; }
+  }
+  return best;
 }
 
 size_t dw_partial_bytes(int D, int Np, int64_t tokens_padded) {
-  return (size_t)dw_splits(tokens_padded) * D * Np * sizeof(float);
+  return (size_t)dw_splits(D, Np, tokens_padded) * D * Np * sizeof(float);
 }
 
 void launch_gemm_dw(const uint8_t* x8t, const uint8_t* g8t, int D, int Np, int64_t Tp,
                     float* part, hipStream_t s) {
-  const int splits = dw_splits(Tp);
+  const int splits = dw_splits(D, Np, Tp);
   const int nk = (int)ceil_div(Tp, kBK);
   const int per = (int)ceil_div(nk, splits);
-  EpiDwPart e{part, D, Np};
-  launch_gemm(x8t, Tp, g8t, Tp, D, Np, (int)Tp, splits, per, e, s);
+  const Gemm gm{x8t, Tp, g8t, Tp, D, Np, (int)Tp, (int)ceil_div(Np, kBNw)};
+  const int blocks = (int)ceil_div(D, kBMw) * gm.n_tiles * splits;
+  gemm_dw_part_kernel<kBMw, kBNw><<<blocks, kGemmThreads, 0, s>>>(gm, splits, per, part);
 }
 
 void launch_dw_reduce(const float* part, int D, int Np, int64_t Tp, const float* x_scales,
@@ -288,7 +597,7 @@ void launch_dw_reduce(const float* part, int D, int Np, int64_t Tp, const float*
                       float* dwv, int64_t ldv, int nq, hipStream_t s) {
   const int64_t quads = (int64_t)D * Np / 4;
   dw_reduce_kernel<<<(unsigned)ceil_div(quads, kThreads), kThreads, 0, s>>>(
-      part, dw_splits(Tp), D, Np, x_scales, g_scales, nq, dwq, ldq, dwk, ldk, dwv, ldv);
+      part, dw_splits(D, Np, Tp), D, Np, x_scales, g_scales, nq, dwq, ldq, dwk, ldk, dwv, ldv);
 }
 
 }  // namespace fpr

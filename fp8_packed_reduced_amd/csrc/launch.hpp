@@ -8,6 +8,11 @@
 
 namespace fpr {
 
+// Largest token count a call accepts.  The GEMMs address a tile's rows by
+// 32-bit offsets from its first row, (tile rows - 1) * stride + 128 bytes,
+// and the dW stride is the padded token count.
+constexpr int64_t kMaxTokens = int64_t(1) << 24;
+
 // ---- quantize.hip --------------------------------------------------------
 
 // Per-block max |w| over the logical W_packed [D][N] read from its three
@@ -52,7 +57,7 @@ void launch_gemm_dx(const uint8_t* g8, const uint8_t* w_packed, int T, int D, in
                     const float* g_scales, const float* w_scales, uint16_t* dx, hipStream_t s);
 
 // Number of K splits the dW GEMM uses, and its partial-buffer size.
-int dw_splits(int64_t tokens_padded);
+int dw_splits(int D, int Np, int64_t tokens_padded);
 size_t dw_partial_bytes(int D, int Np, int64_t tokens_padded);
 
 // dW = s_x s_g x^T g: M = D, N = N_packed, K = tokens (padded, zero tail).

@@ -42,7 +42,7 @@
  * Supported shapes: d_model % 64 == 0, d_qk % 16 == 0, d_v % 16 == 0,
  * N % 64 == 0, and the norm/RoPE tiles of 16 tokens must fit 64 KiB of LDS
  * (36 * 2*n_heads*d_qk + 64*d_qk bytes; the pages' 6 heads of 96 use 47 KiB);
- * any 1 <= T <= 2^30 (ragged tails are masked).
+ * any 1 <= T <= 2^24 (ragged tails are masked).
  * Alignment: every pointer 16-byte aligned; ldq/ldk/ldv multiples of 4.
  */
 #ifndef FPR_H
@@ -177,6 +177,8 @@ typedef struct fpr_layout {
     size_t bwd_g_scales;     /* [2] fp32: s_g, inv_g                         */
     size_t bwd_g8;           /* [T][N] e4m3                                  */
     size_t bwd_g8t;          /* [N][tokens_padded] e4m3                      */
+    size_t bwd_dw_part;      /* [dw_splits][D][N] fp32 split-K dW partials   */
+    int32_t dw_splits;       /* K splits of the dW GEMM at this token count  */
 } fpr_layout;
 
 FPR_API int fpr_get_layout(const fpr_dims* dims, int64_t tokens, fpr_layout* out);

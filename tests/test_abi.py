@@ -43,8 +43,29 @@ def test_sizes_and_layout_at_the_64k_step_shape():
     bw = B.workspace_bytes(d, T, B.FPR_CALL_BACKWARD)
     assert bw >= lay.bwd_g8t + 1920 * T
     for off in (lay.saved_x8t, lay.saved_qk_pre, lay.saved_x_scales, lay.fwd_x8,
-                lay.bwd_dqkv, lay.bwd_g8, lay.bwd_g8t, lay.bwd_g_scales):
+                lay.bwd_dqkv, lay.bwd_g8, lay.bwd_g8t, lay.bwd_g_scales, lay.bwd_dw_part):
         assert off % 256 == 0
+    # split-K partials of dW fit after the transposed gradient codes
+    assert 1 <= lay.dw_splits <= 8
+    assert lay.bwd_dw_part >= lay.bwd_g8t + 1920 * T
+    assert lay.bwd_dw_part + lay.dw_splits * 768 * 1920 * 4 <= bw
+
+
+def test_dw_split_count_depends_only_on_shapes():
+    d = B.make_dims(768, 6)
+    # 768 x 1920 in 192 x 192 tiles is 40 tiles; 6 splits make 240 blocks,
+    # the fullest single round of 256 compute units with at most 8 splits
+    assert B.layout(d, 65536).dw_splits == 6
+    assert B.layout(d, 16384).dw_splits == 6
+    # never more splits than 128-token K steps
+    assert B.layout(B.make_dims(128, 1), 100).dw_splits == 1
+
+
+def test_token_limit():
+    d = B.make_dims(768, 6)
+    assert B.workspace_bytes(d, 1 << 24, B.FPR_CALL_BACKWARD) > 0
+    assert B.workspace_bytes(d, (1 << 24) + 1, B.FPR_CALL_BACKWARD) == 0
+    assert B.saved_bytes(d, (1 << 24) + 1) == 0
 
 
 def test_ragged_tokens_pad_the_transposed_stride():
