@@ -81,7 +81,7 @@ Plan make_plan(const fpr_dims* d, int64_t T) {
   p.f_x8 = take(c, (size_t)T * p.D);
   p.fwd_total = c;
   c = 0;
-  p.b_parts = fpr::norm_rope_bwd_blocks(T > 0 ? T : 1);
+  p.b_parts = fpr::norm_rope_bwd_blocks(T > 0 ? T : 1, p.H, p.dqk);
   p.b_part = take(c, (size_t)p.b_parts * 4);
   p.b_gsc = take(c, 4 * sizeof(float));
   p.b_dqkv = take(c, (size_t)T * p.N * 2);

@@ -11,10 +11,19 @@
 // the V gradient is re-laid out; everything is packed into dQKV [T][N] bf16
 // with one amax partial per block for the gradient quantiser.
 //
-// Work item = (token, head row, chunk c): a thread owns the 8 elements
-// [8c, 8c+8) of a row together with their rotation partners [h+8c, h+8c+8),
-// h = d/2, so a RoPE pair never leaves the thread's registers.  The row sums
-// are combined through per-item partials in LDS, summed in a fixed order.
+// Main kernels (d = 64, 96, 128): four consecutive lanes own one head row,
+// lane q the P = d/8 pairs (i, i + d/2) for i in [qP, qP + P), so a RoPE
+// pair never leaves a thread and the row sums take two cross-lane steps
+// (DPP quad permutes) with no LDS.  Rotation angles are formed in
+// revolutions: position * theta_j / (2 pi) in double, reduced to its
+// fractional part, then the hardware sin/cos of that fraction.
+//
+// Fallback kernels (other head widths): work item = (token, head row,
+// chunk c), a thread owns the 8 elements [8c, 8c+8) of a row and their
+// rotation partners; row sums go through per-item partials in LDS, summed
+// in a fixed order.
+#include <algorithm>
+
 #include "common.hpp"
 #include "launch.hpp"
 
@@ -61,6 +70,169 @@ __device__ inline uint32_t absmax8(uint4 v) {
     m = m > hi ? m : hi;
   }
   return m;
+}
+
+// ------------------------------------------------- quad-lane kernels
+
+constexpr int kQuadBlocks = 2048;  // grid of the grid-stride quad kernels
+
+// theta_j / (2 pi) = base^(-2j/d) / (2 pi), j < h, for the block.
+__device__ inline void build_rev_table(double* rev, int h, int d, float base) {
+  const double lg = log2((double)base);
+  for (int j = threadIdx.x; j < h; j += kThreads)
+    rev[j] = exp2(-(2.0 * j / d) * lg) * 0.15915494309189533576888376337251;
+  __syncthreads();
+}
+
+// cos / sin of the angle pos * theta_j, from its fractional revolution.
+__device__ inline void rope_cs(double rev_j, int64_t pos, float& c, float& s) {
+  double r = (double)pos * rev_j;
+  r -= rint(r);
+  const float f = (float)r;
+  s = __builtin_amdgcn_sinf(f);  // sin(2 pi f)
+  c = __builtin_amdgcn_cosf(f);
+}
+
+__device__ inline float quad_sum(float v) {
+  v += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0xB1, 0xF, 0xF, true));  // lane ^ 1
+  v += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x4E, 0xF, 0xF, true));  // lane ^ 2
+  return v;
+}
+
+template <int P>
+__device__ inline void load_bf16(const uint16_t* p, float (&f)[P]) {
+#pragma unroll
+  for (int i = 0; i < P / 4; ++i) {
+    const uint2 w = *reinterpret_cast<const uint2*>(p + 4 * i);
+    f[4 * i] = bf16_to_f32(w.x & 0xffffu);
+    f[4 * i + 1] = bf16_to_f32(w.x >> 16);
+    f[4 * i + 2] = bf16_to_f32(w.y & 0xffffu);
+    f[4 * i + 3] = bf16_to_f32(w.y >> 16);
+  }
+}
+
+// Stores P values as bf16 and returns the largest |bf16| bit pattern.
+template <int P>
+__device__ inline uint32_t store_bf16(uint16_t* p, const float (&f)[P]) {
+  uint32_t m = 0;
+#pragma unroll
+  for (int i = 0; i < P / 4; ++i) {
+    const uint2 w = make_uint2(pack_bf16x2(f[4 * i], f[4 * i + 1]),
+                               pack_bf16x2(f[4 * i + 2], f[4 * i + 3]));
+    *reinterpret_cast<uint2*>(p + 4 * i) = w;
+    m = max(m, max(max(w.x & 0x7fffu, (w.x >> 16) & 0x7fffu),
+                   max(w.y & 0x7fffu, (w.y >> 16) & 0x7fffu)));
+  }
+  return m;
+}
+
+template <int P>
+__global__ __launch_bounds__(kThreads) void norm_rope_fwd_quad(
+    const uint16_t* __restrict__ qk_pre, int64_t T, int seq_len, int H, float eps, float base,
+    uint16_t* __restrict__ q, uint16_t* __restrict__ k) {
+  constexpr int h = 4 * P, d = 2 * h;
+  __shared__ double rev[h];
+  build_rev_table(rev, h, d, base);
+  const int R = 2 * H, lq = threadIdx.x & 3;
+  const int64_t units = T * R * 4;
+  for (int64_t u = blockIdx.x * (int64_t)kThreads + threadIdx.x; u < units;
+       u += (int64_t)gridDim.x * kThreads) {
+    const int64_t row = u >> 2, t = row / R;
+    const int rr = (int)(row - t * R);
+    const uint16_t* src = qk_pre + row * d + lq * P;  // row t, head row rr
+    float a[P], b[P];
+    load_bf16<P>(src, a);
+    load_bf16<P>(src + h, b);
+    float ss = 0.f;
+#pragma unroll
+    for (int i = 0; i < P; ++i) ss += a[i] * a[i] + b[i] * b[i];
+    ss = quad_sum(ss);
+    const float rho = 1.0f / sqrtf(ss / (float)d + eps);
+    const int64_t bseq = t / seq_len, s = t - bseq * seq_len;
+#pragma unroll
+    for (int i = 0; i < P; ++i) {
+      float cn, sn;
+      rope_cs(rev[lq * P + i], s, cn, sn);
+      const float ua = a[i] * rho, ub = b[i] * rho;
+      a[i] = ua * cn - ub * sn;
+      b[i] = ub * cn + ua * sn;
+    }
+    uint16_t* dst = (rr < H ? q + ((bseq * H + rr) * seq_len + s) * d
+                            : k + ((bseq * H + (rr - H)) * seq_len + s) * d) + lq * P;
+    store_bf16<P>(dst, a);
+    store_bf16<P>(dst + h, b);
+  }
+}
+
+// Backward, then the V gradient re-laid out into the packed rows; one amax
+// partial per block.
+template <int P>
+__global__ __launch_bounds__(kThreads) void norm_rope_bwd_quad(
+    const uint16_t* __restrict__ dq, const uint16_t* __restrict__ dk,
+    const uint16_t* __restrict__ dv, const uint16_t* __restrict__ qk_pre, int64_t T,
+    int seq_len, int H, int dvw, float eps, float base, uint16_t* __restrict__ dqkv,
+    uint32_t* __restrict__ partials) {
+  constexpr int h = 4 * P, d = 2 * h;
+  __shared__ double rev[h];
+  __shared__ uint32_t red[4];
+  build_rev_table(rev, h, d, base);
+  const int R = 2 * H, qkw = R * d, N = qkw + H * dvw, lq = threadIdx.x & 3;
+  const int64_t stride = (int64_t)gridDim.x * kThreads;
+  uint32_t amax = 0;
+  const int64_t units = T * R * 4;
+  for (int64_t u = blockIdx.x * (int64_t)kThreads + threadIdx.x; u < units; u += stride) {
+    const int64_t row = u >> 2, t = row / R;
+    const int rr = (int)(row - t * R);
+    const int64_t bseq = t / seq_len, s = t - bseq * seq_len;
+    const uint16_t* asrc = qk_pre + row * d + lq * P;
+    const uint16_t* gsrc = (rr < H ? dq + ((bseq * H + rr) * seq_len + s) * d
+                                   : dk + ((bseq * H + (rr - H)) * seq_len + s) * d) + lq * P;
+    float a[P], b[P], ga[P], gb[P];
+    load_bf16<P>(asrc, a);
+    load_bf16<P>(asrc + h, b);
+    load_bf16<P>(gsrc, ga);
+    load_bf16<P>(gsrc + h, gb);
+    float ss = 0.f, sd = 0.f;
+#pragma unroll
+    for (int i = 0; i < P; ++i) {
+      float cn, sn;
+      rope_cs(rev[lq * P + i], s, cn, sn);
+      const float dua = ga[i] * cn + gb[i] * sn;  // R_{-p}
+      const float dub = gb[i] * cn - ga[i] * sn;
+      ga[i] = dua;
+      gb[i] = dub;
+      ss += a[i] * a[i] + b[i] * b[i];
+      sd += a[i] * dua + b[i] * dub;
+    }
+    ss = quad_sum(ss);
+    sd = quad_sum(sd);
+    const float rho = 1.0f / sqrtf(ss / (float)d + eps);
+    // rho^2 <u,du> / d, where <u,du> = rho * sum(a du)
+    const float coef = rho * rho * rho * sd / (float)d;
+#pragma unroll
+    for (int i = 0; i < P; ++i) {
+      ga[i] = rho * ga[i] - coef * a[i];
+      gb[i] = rho * gb[i] - coef * b[i];
+    }
+    uint16_t* dst = dqkv + t * N + rr * d + lq * P;
+    amax = max(amax, store_bf16<P>(dst, ga));
+    amax = max(amax, store_bf16<P>(dst + h, gb));
+  }
+  const int cv = dvw / 8;
+  const int64_t vunits = T * H * cv;
+  for (int64_t u = blockIdx.x * (int64_t)kThreads + threadIdx.x; u < vunits; u += stride) {
+    const int64_t th = u / cv;
+    const int c = (int)(u - th * cv);
+    const int64_t t = th / H;
+    const int hh = (int)(th - t * H);
+    const int64_t bseq = t / seq_len, s = t - bseq * seq_len;
+    const uint4 g =
+        *reinterpret_cast<const uint4*>(dv + ((bseq * H + hh) * seq_len + s) * dvw + 8 * c);
+    amax = max(amax, absmax8(g));
+    *reinterpret_cast<uint4*>(dqkv + t * N + qkw + hh * dvw + 8 * c) = g;
+  }
+  amax = block_max_u32(amax << 16, red);
+  if (threadIdx.x == 0) partials[blockIdx.x] = amax;
 }
 
 // ------------------------------------------------------------- forward
@@ -234,6 +406,12 @@ __global__ __launch_bounds__(kThreads) void norm_rope_bwd_kernel(
 
 constexpr int kFwdTT = 16, kBwdTT = 8;
 
+static bool quad_width(int d) { return d == 64 || d == 96 || d == 128; }
+
+static unsigned quad_grid(int64_t units) {
+  return (unsigned)std::min<int64_t>(kQuadBlocks, std::max<int64_t>(1, ceil_div(units, kThreads)));
+}
+
 size_t norm_rope_fwd_lds(int H, int d) {
   const size_t items = (size_t)kFwdTT * 2 * H * (d / 16);
   return items * (32 + 4) + (size_t)kFwdTT * (d / 2) * 8;
@@ -246,20 +424,53 @@ size_t norm_rope_bwd_lds(int H, int d) {
 
 void launch_norm_rope_fwd(const uint16_t* qk_pre, int64_t T, int seq_len, int H, int d, float eps,
                           float base, uint16_t* q, uint16_t* k, hipStream_t s) {
+  const unsigned grid = quad_grid(T * 2 * H * 4);
+  switch (d) {
+    case 64:
+      norm_rope_fwd_quad<8><<<grid, kThreads, 0, s>>>(qk_pre, T, seq_len, H, eps, base, q, k);
+      return;
+    case 96:
+      norm_rope_fwd_quad<12><<<grid, kThreads, 0, s>>>(qk_pre, T, seq_len, H, eps, base, q, k);
+      return;
+    case 128:
+      norm_rope_fwd_quad<16><<<grid, kThreads, 0, s>>>(qk_pre, T, seq_len, H, eps, base, q, k);
+      return;
+    default:
+      break;
+  }
   const size_t lds = norm_rope_fwd_lds(H, d);
   norm_rope_fwd_kernel<kFwdTT><<<(unsigned)ceil_div(T, kFwdTT), kThreads, lds, s>>>(
       qk_pre, T, seq_len, H, d, eps, base, q, k);
 }
 
-int norm_rope_bwd_blocks(int64_t T) { return (int)ceil_div(T, kBwdTT); }
+int norm_rope_bwd_blocks(int64_t T, int H, int d) {
+  return quad_width(d) ? (int)quad_grid(T * 2 * H * 4) : (int)ceil_div(T, kBwdTT);
+}
 
 void launch_norm_rope_bwd(const uint16_t* dq, const uint16_t* dk, const uint16_t* dv,
                           const uint16_t* qk_pre, int64_t T, int seq_len, int H, int d, int d_v,
                           float eps, float base, uint16_t* dqkv, uint32_t* partials,
                           hipStream_t s) {
+  const unsigned grid = (unsigned)norm_rope_bwd_blocks(T, H, d);
+  switch (d) {
+    case 64:
+      norm_rope_bwd_quad<8><<<grid, kThreads, 0, s>>>(dq, dk, dv, qk_pre, T, seq_len, H, d_v, eps,
+                                                      base, dqkv, partials);
+      return;
+    case 96:
+      norm_rope_bwd_quad<12><<<grid, kThreads, 0, s>>>(dq, dk, dv, qk_pre, T, seq_len, H, d_v,
+                                                       eps, base, dqkv, partials);
+      return;
+    case 128:
+      norm_rope_bwd_quad<16><<<grid, kThreads, 0, s>>>(dq, dk, dv, qk_pre, T, seq_len, H, d_v,
+                                                       eps, base, dqkv, partials);
+      return;
+    default:
+      break;
+  }
   const size_t lds = norm_rope_bwd_lds(H, d);
-  norm_rope_bwd_kernel<kBwdTT><<<(unsigned)norm_rope_bwd_blocks(T), kThreads, lds, s>>>(
-      dq, dk, dv, qk_pre, T, seq_len, H, d, d_v, eps, base, dqkv, partials);
+  norm_rope_bwd_kernel<kBwdTT><<<grid, kThreads, lds, s>>>(dq, dk, dv, qk_pre, T, seq_len, H, d,
+                                                          d_v, eps, base, dqkv, partials);
 }
 
 }  // namespace fpr

@@ -83,8 +83,9 @@ void launch_norm_rope_fwd(const uint16_t* qk_pre, int64_t T, int seq_len, int H,
                           float eps, float base, uint16_t* q, uint16_t* k, hipStream_t s);
 
 // Backward epilogue: dq, dk, dv (head-major) + qk_pre -> packed dQKV [T][N]
-// bf16, plus one amax partial per block (returned count via blocks_out).
-int norm_rope_bwd_blocks(int64_t T);
+// bf16, plus one amax partial per block; norm_rope_bwd_blocks() is that
+// block count.
+int norm_rope_bwd_blocks(int64_t T, int H, int d_qk);
 void launch_norm_rope_bwd(const uint16_t* dq, const uint16_t* dk, const uint16_t* dv,
                           const uint16_t* qk_pre, int64_t T, int seq_len, int H, int d_qk,
                           int d_v, float eps, float base, uint16_t* dqkv,

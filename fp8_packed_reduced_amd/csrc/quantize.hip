@@ -55,6 +55,7 @@ __global__ __launch_bounds__(kThreads) void amax_bf16_kernel(const uint16_t* __r
   __shared__ uint32_t red[4];
   const int64_t vecs = n / 8;
   uint32_t m = 0;
+#pragma unroll 4
   for (int64_t i = blockIdx.x * (int64_t)kThreads + threadIdx.x; i < vecs;
        i += (int64_t)gridDim.x * kThreads) {
     uint4 v = reinterpret_cast<const uint4*>(x)[i];
@@ -77,6 +78,7 @@ __global__ __launch_bounds__(kThreads) void finalize_scales_kernel(
     int32_t* __restrict__ status, int status_bit, int reset) {
   __shared__ uint32_t red[4];
   uint32_t m = 0;
+#pragma unroll 8
   for (int i = threadIdx.x; i < parts; i += kThreads) m = m > partials[i] ? m : partials[i];
   m = block_max_u32(m, red);
   if (threadIdx.x == 0) {

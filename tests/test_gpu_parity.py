@@ -35,6 +35,9 @@ NORM_TOL = 1e-2
 
 RAGGED = dict(n_seq=3, seq_len=100, d_model=128, n_heads=2, d_qk=96, d_v=128)
 SMALL_16K_DIMS = dict(n_seq=2, seq_len=384, d_model=768, n_heads=6, d_qk=96, d_v=128)
+# K tails in both bf16-output GEMMs (d_model 192 and N = 320 are not multiples
+# of 128) and a head width outside the quad-lane norm/RoPE kernels (48)
+TAILS = dict(n_seq=2, seq_len=77, d_model=192, n_heads=2, d_qk=48, d_v=64)
 
 
 @pytest.fixture(scope="module", autouse=True)
@@ -153,7 +156,7 @@ def _check_backward(w, r):
 
 
 @pytest.mark.parametrize("name,w", [("tiny", inputs.WORKLOADS["tiny"]), ("ragged", RAGGED),
-                                    ("d768", SMALL_16K_DIMS)])
+                                    ("d768", SMALL_16K_DIMS), ("tails", TAILS)])
 def test_forward_backward_stagewise(name, w):
     r = run(w, seed=42)
     assert r["status"] == 0
