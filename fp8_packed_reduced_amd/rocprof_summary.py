@@ -1,0 +1,104 @@
+"""Turn rocprofv3 output of ``bench.py`` into the short text summaries kept
+under ``profiles/``.
+
+    python -m fp8_packed_reduced_amd.rocprof_summary stats KERNEL_STATS_CSV TITLE CMD
+        -> markdown table of per-kernel durations (``--kernel-trace --stats``)
+
+    python -m fp8_packed_reduced_amd.rocprof_summary traffic FETCH_CSV WRITE_CSV WORKLOAD CMD...
+        -> per-launch HBM bytes of every stage of the step, from two ``--pmc``
+           runs (FETCH_SIZE, then WRITE_SIZE, in KiB per dispatch)
+
+Byte counters are calibrated against the encoder launches bench.py makes
+before its first step (known traffic: 4 bytes read and 1 byte written per
+element): factor = known bytes / counter reading, per counter.  A stage's
+line carries the hash of its kernel source, and bench.py ignores the line
+once that source has changed.
+"""
+from __future__ import annotations
+
+import csv
+import statistics
+import sys
+
+STEP_ORDER = ["amax_w", "finalize_w", "quantize_w", "amax_x", "finalize_x", "quantize_x",
+              "gemm_fwd", "norm_rope_fwd", "norm_rope_bwd", "finalize_g", "quantize_g",
+              "gemm_dx", "gemm_dw", "dw_reduce"]
+KERNEL_OF_STAGE = {
+    "amax_w": "amax_w_kernel", "finalize_w": "finalize_scales_kernel",
+    "quantize_w": "quantize_w_kernel", "amax_x": "amax_bf16_kernel",
+    "finalize_x": "finalize_scales_kernel", "quantize_x": "quantize_rows_kernel",
+    "gemm_fwd": "gemm_bf16out_kernel", "norm_rope_fwd": "norm_rope_fwd",
+    "norm_rope_bwd": "norm_rope_bwd", "finalize_g": "finalize_scales_kernel",
+    "quantize_g": "quantize_rows_kernel", "gemm_dx": "gemm_bf16out_kernel",
+    "gemm_dw": "gemm_dw_part_kernel", "dw_reduce": "dw_reduce_kernel",
+}
+CALIB_KERNEL = "encode_kernel"
+
+
+def short(name: str) -> str:
+    return name.split("(")[0].replace("void ", "")
+
+
+def stats(path: str, title: str, cmd: str) -> str:
+    rows = list(csv.DictReader(open(path)))
+    out = [f"# {title}\n", "Command (run from /tmp with TMPDIR=/tmp, repository at $R):\n",
+           "```\n" + cmd + "\n```\n",
+           "| kernel | calls | avg µs | min µs | max µs | % of GPU time |",
+           "|---|---:|---:|---:|---:|---:|"]
+    for r in rows:
+        out.append(f"| `{short(r['Name'])}` | {r['Calls']} | {float(r['AverageNs']) / 1e3:.2f} | "
+                   f"{float(r['MinNs']) / 1e3:.2f} | {float(r['MaxNs']) / 1e3:.2f} | "
+                   f"{float(r['Percentage']):.2f} |")
+    return "\n".join(out) + "\n"
+
+
+def _dispatches(path: str, counter: str):
+    """(dispatch id, kernel name, value) in dispatch order."""
+    rows = [r for r in csv.DictReader(open(path)) if r["Counter_Name"] == counter]
+    rows.sort(key=lambda r: int(r["Dispatch_Id"]))
+    return [(int(r["Dispatch_Id"]), short(r["Kernel_Name"]), float(r["Counter_Value"]))
+            for r in rows]
+
+
+def _per_stage(path: str, counter: str, known_bytes: float):
+    ds = _dispatches(path, counter)
+    calib = [v for _, n, v in ds if CALIB_KERNEL in n]
+    if not calib:
+        raise SystemExit(f"{path}: no calibration launch ({CALIB_KERNEL}) found")
+    factor = known_bytes / (statistics.median(calib) * 1024.0)
+    step_kernels = [(n, v) for _, n, v in ds if "fpr::" in n and CALIB_KERNEL not in n]
+    if len(step_kernels) % len(STEP_ORDER):
+        raise SystemExit(f"{path}: {len(step_kernels)} library dispatches is not a whole "
+                         f"number of {len(STEP_ORDER)}-kernel steps")
+    per = {s: [] for s in STEP_ORDER}
+    for i, (n, v) in enumerate(step_kernels):
+        stage = STEP_ORDER[i % len(STEP_ORDER)]
+        if KERNEL_OF_STAGE[stage] not in n:
+            raise SystemExit(f"{path}: dispatch {i} is {n}, expected {stage}")
+        per[stage].append(v * 1024.0 * factor)
+    return {s: statistics.mean(v) for s, v in per.items()}, factor
+
+
+def traffic(fetch_csv: str, write_csv: str, workload: str, cmd: str) -> str:
+    sys.path.insert(0, ".")
+    import bench  # the stage -> source mapping and the calibration size
+    n = bench.CALIB_FLOATS
+    fetch, ff = _per_stage(fetch_csv, "FETCH_SIZE", 4.0 * n)
+    write, wf = _per_stage(write_csv, "WRITE_SIZE", 1.0 * n)
+    out = [f"# HBM traffic per launch, {workload}: stage fetch_bytes write_bytes source_sha12",
+           f"# from rocprofv3 --pmc FETCH_SIZE and --pmc WRITE_SIZE runs of: {cmd}",
+           f"# calibration (encoder, {4 * n} B read / {n} B written): fetch x{ff:.4f}, "
+           f"write x{wf:.4f}"]
+    for s in STEP_ORDER:
+        out.append(f"{s} {fetch[s]:.0f} {write[s]:.0f} {bench.source_hash(s)}")
+    return "\n".join(out) + "\n"
+
+
+if __name__ == "__main__":
+    mode = sys.argv[1]
+    if mode == "stats":
+        sys.stdout.write(stats(sys.argv[2], sys.argv[3], sys.argv[4]))
+    elif mode == "traffic":
+        sys.stdout.write(traffic(sys.argv[2], sys.argv[3], sys.argv[4], " ".join(sys.argv[5:])))
+    else:
+        raise SystemExit(__doc__)
