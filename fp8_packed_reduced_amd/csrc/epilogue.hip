@@ -76,6 +76,31 @@ __device__ inline uint32_t absmax8(uint4 v) {
 
 constexpr int kQuadBlocks = 2048;  // grid of the grid-stride quad kernels
 
+// Work of the forward quad kernel: a wave's 16 quads (one head row each)
+// cover TG consecutive tokens x HG consecutive head rows (4 x 4, or 8 x 2
+// when the 2H head rows are not a multiple of 4), so each token's rows that
+// a wave reads, and each head's rows it writes head-major, are runs of HG
+// (resp. TG) whole rows: 768 contiguous bytes for 96-wide heads, whole
+// cache lines, where rows of 192 bytes alone would leave lines half
+// written.  The backward kernel, whose large streams (pre-norm rows in,
+// dQKV out) are both token-major, takes head rows in plain row order.
+__host__ __device__ inline int quad_heads(int R) { return R % 4 == 0 ? 4 : 2; }
+__host__ __device__ inline int64_t quad_units(int64_t T, int R) {
+  const int HG = quad_heads(R);
+  return ceil_div(T, 16 / HG) * (R / HG) * 64;
+}
+
+// Token and head row of quad-kernel unit u (lane u % 4 of its quad).
+__device__ inline void quad_row(int64_t u, int R, int64_t& t, int& rr) {
+  const int HG = quad_heads(R), TG = 16 / HG, n_hg = R / HG;
+  const int64_t w = u >> 6;
+  const int qd = (int)((u >> 2) & 15);
+  const int64_t tg = w / n_hg;
+  const int hg = (int)(w - tg * n_hg);
+  t = tg * TG + qd % TG;
+  rr = hg * HG + qd / TG;
+}
+
 // theta_j / (2 pi) = base^(-2j/d) / (2 pi), j < h, for the block.
 __device__ inline void build_rev_table(double* rev, int h, int d, float base) {
   const double lg = log2((double)base);
@@ -134,12 +159,14 @@ __global__ __launch_bounds__(kThreads) void norm_rope_fwd_quad(
   __shared__ double rev[h];
   build_rev_table(rev, h, d, base);
   const int R = 2 * H, lq = threadIdx.x & 3;
-  const int64_t units = T * R * 4;
+  const int64_t units = quad_units(T, R);
   for (int64_t u = blockIdx.x * (int64_t)kThreads + threadIdx.x; u < units;
        u += (int64_t)gridDim.x * kThreads) {
-    const int64_t row = u >> 2, t = row / R;
-    const int rr = (int)(row - t * R);
-    const uint16_t* src = qk_pre + row * d + lq * P;  // row t, head row rr
+    int64_t t;
+    int rr;
+    quad_row(u, R, t, rr);
+    if (t >= T) continue;  // the whole quad
+    const uint16_t* src = qk_pre + (t * R + rr) * d + lq * P;  // row t, head row rr
     float a[P], b[P];
     load_bf16<P>(src, a);
     load_bf16<P>(src + h, b);
@@ -424,7 +451,7 @@ size_t norm_rope_bwd_lds(int H, int d) {
 
 void launch_norm_rope_fwd(const uint16_t* qk_pre, int64_t T, int seq_len, int H, int d, float eps,
                           float base, uint16_t* q, uint16_t* k, hipStream_t s) {
-  const unsigned grid = quad_grid(T * 2 * H * 4);
+  const unsigned grid = quad_grid(quad_units(T, 2 * H));
   switch (d) {
     case 64:
       norm_rope_fwd_quad<8><<<grid, kThreads, 0, s>>>(qk_pre, T, seq_len, H, eps, base, q, k);

@@ -100,10 +100,14 @@ __device__ __forceinline__ v16f mfma32(v8i b, v8i a, v16f c) {
 // ------------------------------------------------------------ schedule
 
 // The operands and the (tile, K step) pairs a block walks, in order.  Step
-// g belongs to the block's tile number ord = g / nk, which is tile
-// first_tile + ord * tile_stride, at K step ks0 + g % nk.  A persistent
-// block has several tiles (stride = grid size) and all K steps; a split-K
-// block has one tile and a K range.
+// g belongs to the block's tile number ord = g / nk, at K step ks0 + g % nk.
+// A split-K block has one tile and a K range.  A persistent block has
+// several tiles and all K steps: its group x of P takes the row panels
+// m = x, x + P, ... and their tiles in (m, n) order, of which the block
+// takes every c-th from the i-th.  With P = 8 and blocks dispatched
+// round-robin over the 8 XCDs, group x is one XCD: its blocks work on a
+// few row panels at a time that no other XCD touches, so the A rows come
+// from memory once and are shared in that XCD's L2.
 struct Gemm {
   const uint8_t* A;
   int64_t lda;
@@ -113,9 +117,16 @@ struct Gemm {
 };
 
 struct Sched {
-  int nk, ks0, first_tile, tile_stride, steps;
+  int nk, ks0, steps;
+  int single;                 // >= 0: the block's only tile
+  int x, P, i, c, n_tiles;    // otherwise: panel group, groups, rank, stride
   __device__ int ord(int g) const { return g / nk; }
-  __device__ int tile(int g) const { return first_tile + ord(g) * tile_stride; }
+  __device__ int tile_of(int o) const {
+    if (single >= 0) return single;
+    const int k = i + c * o, q = k / n_tiles;
+    return (x + P * q) * n_tiles + (k - q * n_tiles);
+  }
+  __device__ int tile(int g) const { return tile_of(ord(g)); }
   __device__ int ks(int g) const { return ks0 + g - ord(g) * nk; }
 };
 
@@ -424,11 +435,21 @@ __device__ __forceinline__ void store_partial_tile(const v16f (&acc)[C::FM][C::F
 
 // -------------------------------------------------- persistent bf16 GEMM
 
-// The first tile of block b: within a round of gridDim.x tiles the 8 XCDs
-// (blocks are dispatched round-robin over them) each take a contiguous run,
-// so concurrent tiles of one XCD share A rows in its L2.
-__device__ __forceinline__ int first_tile_of(int b, int G) {
-  return (G % 8 == 0) ? (b % 8) * (G / 8) + b / 8 : b;
+// Block b's tiles: per-XCD row panels when every XCD gets the same number
+// of them, else simply tiles b, b + G, b + 2G, ...
+__device__ __forceinline__ void persistent_tiles(Sched& sc, int b, int G, int ntiles,
+                                                 int n_tiles) {
+  const int m_tiles = ntiles / n_tiles;
+  sc.single = -1;
+  sc.n_tiles = n_tiles;
+  if (G % 8 == 0 && m_tiles % 8 == 0) {
+    sc.P = 8; sc.x = b % 8; sc.i = b / 8; sc.c = G / 8;
+  } else {
+    sc.P = 1; sc.x = 0; sc.i = b; sc.c = G;
+  }
+  const int total = (m_tiles - sc.x + sc.P - 1) / sc.P * n_tiles;
+  const int mine = sc.i < total ? (total - sc.i + sc.c - 1) / sc.c : 0;
+  sc.steps = mine * sc.nk;
 }
 
 template <int BM, int BN, bool KTAIL, class Epi>
@@ -443,10 +464,7 @@ __global__ __launch_bounds__(kGemmThreads, 1) void gemm_bf16out_kernel(
   Sched sc;
   sc.nk = (gm.K + kBK - 1) / kBK;
   sc.ks0 = 0;
-  sc.first_tile = first_tile_of(blockIdx.x, G);
-  sc.tile_stride = G;
-  const int my_tiles = sc.first_tile < ntiles ? (ntiles - sc.first_tile + G - 1) / G : 0;
-  sc.steps = my_tiles * sc.nk;
+  persistent_tiles(sc, blockIdx.x, G, ntiles, gm.n_tiles);
   if (wave >= kMmaWaves) {
     copy_role<C, KTAIL>(lds, gm, sc, wave - kMmaWaves, lane);
     return;
@@ -454,21 +472,23 @@ __global__ __launch_bounds__(kGemmThreads, 1) void gemm_bf16out_kernel(
   const int wm = wave >> 1, wn = wave & 1;
   const float alpha = sa[0] * sb[0];
   uint8_t* slice = slices + wave * WaveSlice<C>::BYTES;
-  int tile = sc.first_tile;
+  int ord = 0;
   v16f acc[C::FM][C::FN];
   mma_role<C>(lds, sc, wm, wn, lane, acc, [&](v16f (&a)[C::FM][C::FN]) {
+    const int tile = sc.tile_of(ord++);
     store_bf16_tile<C, Epi>(a, alpha, slice, epi, gm.M, (tile / gm.n_tiles) * BM,
                             (tile % gm.n_tiles) * BN, wm, wn, lane);
     zero_acc<C>(a);
-    tile += sc.tile_stride;
   });
 }
 
 // ------------------------------------------------------------ dW split-K
 
-// Block b takes K split b % splits of tile b / splits.  Unscaled fp32
-// partial sums go to part[split][m][n]; a split with no K steps writes
-// zeros.
+// The (split, tile) items in that order, tile = m * n_tiles + n, are dealt
+// to the XCDs in contiguous runs (blocks go round-robin over the 8 XCDs),
+// so the blocks of one XCD share K ranges and rows of both operands in its
+// L2.  Unscaled fp32 partial sums go to part[split][m][n]; a split with no
+// K steps writes zeros.
 template <int BM, int BN>
 __global__ __launch_bounds__(kGemmThreads, 1) void gemm_dw_part_kernel(
     Gemm gm, int splits, int ksteps_per_split, float* __restrict__ part) {
@@ -476,14 +496,15 @@ __global__ __launch_bounds__(kGemmThreads, 1) void gemm_dw_part_kernel(
   __shared__ __attribute__((aligned(16))) uint8_t lds[kStages * C::STAGE_BYTES];
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int split = blockIdx.x % splits, tile = blockIdx.x / splits;
+  const int G = gridDim.x, b = blockIdx.x, tiles = G / splits;
+  const int item = G % 8 == 0 ? (b % 8) * (G / 8) + b / 8 : b;
+  const int split = item / tiles, tile = item - split * tiles;
   const int nk_all = (gm.K + kBK - 1) / kBK;
   Sched sc;
   sc.ks0 = split * ksteps_per_split;
   sc.steps = max(0, min(nk_all, sc.ks0 + ksteps_per_split) - sc.ks0);
   sc.nk = sc.steps > 0 ? sc.steps : 1;
-  sc.first_tile = tile;
-  sc.tile_stride = 0;
+  sc.single = tile;
   if (wave >= kMmaWaves) {
     copy_role<C, false>(lds, gm, sc, wave - kMmaWaves, lane);
     return;
