@@ -151,6 +151,57 @@ __device__ inline uint32_t store_bf16(uint16_t* p, const float (&f)[P]) {
   return m;
 }
 
+// One head row of the forward quad kernel: loaded first, finished later,
+// so a thread can have several rows' loads in flight.
+template <int P>
+struct FwdRow {
+  float a[P], b[P];
+  int64_t t;
+  int rr;
+  bool ok;
+};
+
+template <int P>
+__device__ __forceinline__ void fwd_load(FwdRow<P>& r, int64_t u, int64_t units, int64_t T, int R,
+                                         const uint16_t* __restrict__ qk_pre, int lq) {
+  constexpr int h = 4 * P, d = 2 * h;
+  r.ok = false;
+  if (u >= units) return;
+  quad_row(u, R, r.t, r.rr);
+  if (r.t >= T) return;  // the whole quad
+  r.ok = true;
+  const uint16_t* src = qk_pre + (r.t * R + r.rr) * d + lq * P;  // row t, head row rr
+  load_bf16<P>(src, r.a);
+  load_bf16<P>(src + h, r.b);
+}
+
+template <int P>
+__device__ __forceinline__ void fwd_finish(FwdRow<P>& r, const double* rev, int seq_len, int H,
+                                           float eps, uint16_t* __restrict__ q,
+                                           uint16_t* __restrict__ k, int lq) {
+  constexpr int h = 4 * P, d = 2 * h;
+  if (!r.ok) return;
+  float ss = 0.f;
+#pragma unroll
+  for (int i = 0; i < P; ++i) ss += r.a[i] * r.a[i] + r.b[i] * r.b[i];
+  ss = quad_sum(ss);
+  const float rho = 1.0f / sqrtf(ss / (float)d + eps);
+  const int64_t bseq = r.t / seq_len, s = r.t - bseq * seq_len;
+#pragma unroll
+  for (int i = 0; i < P; ++i) {
+    float cn, sn;
+    rope_cs(rev[lq * P + i], s, cn, sn);
+    const float ua = r.a[i] * rho, ub = r.b[i] * rho;
+    r.a[i] = ua * cn - ub * sn;
+    r.b[i] = ub * cn + ua * sn;
+  }
+  const int rr = r.rr;
+  uint16_t* dst = (rr < H ? q + ((bseq * H + rr) * seq_len + s) * d
+                          : k + ((bseq * H + (rr - H)) * seq_len + s) * d) + lq * P;
+  store_bf16<P>(dst, r.a);
+  store_bf16<P>(dst + h, r.b);
+}
+
 template <int P>
 __global__ __launch_bounds__(kThreads) void norm_rope_fwd_quad(
     const uint16_t* __restrict__ qk_pre, int64_t T, int seq_len, int H, float eps, float base,
@@ -159,36 +210,80 @@ __global__ __launch_bounds__(kThreads) void norm_rope_fwd_quad(
   __shared__ double rev[h];
   build_rev_table(rev, h, d, base);
   const int R = 2 * H, lq = threadIdx.x & 3;
-  const int64_t units = quad_units(T, R);
-  for (int64_t u = blockIdx.x * (int64_t)kThreads + threadIdx.x; u < units;
-       u += (int64_t)gridDim.x * kThreads) {
-    int64_t t;
-    int rr;
-    quad_row(u, R, t, rr);
-    if (t >= T) continue;  // the whole quad
-    const uint16_t* src = qk_pre + (t * R + rr) * d + lq * P;  // row t, head row rr
-    float a[P], b[P];
-    load_bf16<P>(src, a);
-    load_bf16<P>(src + h, b);
-    float ss = 0.f;
-#pragma unroll
-    for (int i = 0; i < P; ++i) ss += a[i] * a[i] + b[i] * b[i];
-    ss = quad_sum(ss);
-    const float rho = 1.0f / sqrtf(ss / (float)d + eps);
-    const int64_t bseq = t / seq_len, s = t - bseq * seq_len;
-#pragma unroll
-    for (int i = 0; i < P; ++i) {
-      float cn, sn;
-      rope_cs(rev[lq * P + i], s, cn, sn);
-      const float ua = a[i] * rho, ub = b[i] * rho;
-      a[i] = ua * cn - ub * sn;
-      b[i] = ub * cn + ua * sn;
-    }
-    uint16_t* dst = (rr < H ? q + ((bseq * H + rr) * seq_len + s) * d
-                            : k + ((bseq * H + (rr - H)) * seq_len + s) * d) + lq * P;
-    store_bf16<P>(dst, a);
-    store_bf16<P>(dst + h, b);
+  const int64_t units = quad_units(T, R), stride = (int64_t)gridDim.x * kThreads;
+  for (int64_t u = blockIdx.x * (int64_t)kThreads + threadIdx.x; u < units; u += 2 * stride) {
+    FwdRow<P> r0, r1;  // two rows' loads in flight per thread
+    fwd_load<P>(r0, u, units, T, R, qk_pre, lq);
+    fwd_load<P>(r1, u + stride, units, T, R, qk_pre, lq);
+    fwd_finish<P>(r0, rev, seq_len, H, eps, q, k, lq);
+    fwd_finish<P>(r1, rev, seq_len, H, eps, q, k, lq);
   }
+}
+
+// One head row of the backward quad kernel, loaded first and finished
+// later (as FwdRow).
+template <int P>
+struct BwdRow {
+  float a[P], b[P], ga[P], gb[P];
+  int64_t t, s;
+  int rr;
+  bool ok;
+};
+
+template <int P>
+__device__ __forceinline__ void bwd_load(BwdRow<P>& r, int64_t u, int64_t units, int R, int H,
+                                         int seq_len, const uint16_t* __restrict__ dq,
+                                         const uint16_t* __restrict__ dk,
+                                         const uint16_t* __restrict__ qk_pre, int lq) {
+  constexpr int h = 4 * P, d = 2 * h;
+  r.ok = u < units;
+  if (!r.ok) return;
+  const int64_t row = u >> 2;
+  r.t = row / R;
+  r.rr = (int)(row - r.t * R);
+  const int64_t bseq = r.t / seq_len;
+  r.s = r.t - bseq * seq_len;
+  const int rr = r.rr;
+  const uint16_t* asrc = qk_pre + row * d + lq * P;
+  const uint16_t* gsrc = (rr < H ? dq + ((bseq * H + rr) * seq_len + r.s) * d
+                                 : dk + ((bseq * H + (rr - H)) * seq_len + r.s) * d) + lq * P;
+  load_bf16<P>(asrc, r.a);
+  load_bf16<P>(asrc + h, r.b);
+  load_bf16<P>(gsrc, r.ga);
+  load_bf16<P>(gsrc + h, r.gb);
+}
+
+// Finishes the row and returns the largest |bf16| bit pattern it wrote.
+template <int P>
+__device__ __forceinline__ uint32_t bwd_finish(BwdRow<P>& r, const double* rev, int N,
+                                               float eps, uint16_t* __restrict__ dqkv, int lq) {
+  constexpr int h = 4 * P, d = 2 * h;
+  if (!r.ok) return 0;
+  float ss = 0.f, sd = 0.f;
+#pragma unroll
+  for (int i = 0; i < P; ++i) {
+    float cn, sn;
+    rope_cs(rev[lq * P + i], r.s, cn, sn);
+    const float dua = r.ga[i] * cn + r.gb[i] * sn;  // R_{-p}
+    const float dub = r.gb[i] * cn - r.ga[i] * sn;
+    r.ga[i] = dua;
+    r.gb[i] = dub;
+    ss += r.a[i] * r.a[i] + r.b[i] * r.b[i];
+    sd += r.a[i] * dua + r.b[i] * dub;
+  }
+  ss = quad_sum(ss);
+  sd = quad_sum(sd);
+  const float rho = 1.0f / sqrtf(ss / (float)d + eps);
+  // rho^2 <u,du> / d, where <u,du> = rho * sum(a du)
+  const float coef = rho * rho * rho * sd / (float)d;
+#pragma unroll
+  for (int i = 0; i < P; ++i) {
+    r.ga[i] = rho * r.ga[i] - coef * r.a[i];
+    r.gb[i] = rho * r.gb[i] - coef * r.b[i];
+  }
+  uint16_t* dst = dqkv + r.t * N + r.rr * d + lq * P;
+  const uint32_t m = store_bf16<P>(dst, r.ga);
+  return max(m, store_bf16<P>(dst + h, r.gb));
 }
 
 // Backward, then the V gradient re-laid out into the packed rows; one amax
@@ -207,43 +302,12 @@ __global__ __launch_bounds__(kThreads) void norm_rope_bwd_quad(
   const int64_t stride = (int64_t)gridDim.x * kThreads;
   uint32_t amax = 0;
   const int64_t units = T * R * 4;
-  for (int64_t u = blockIdx.x * (int64_t)kThreads + threadIdx.x; u < units; u += stride) {
-    const int64_t row = u >> 2, t = row / R;
-    const int rr = (int)(row - t * R);
-    const int64_t bseq = t / seq_len, s = t - bseq * seq_len;
-    const uint16_t* asrc = qk_pre + row * d + lq * P;
-    const uint16_t* gsrc = (rr < H ? dq + ((bseq * H + rr) * seq_len + s) * d
-                                   : dk + ((bseq * H + (rr - H)) * seq_len + s) * d) + lq * P;
-    float a[P], b[P], ga[P], gb[P];
-    load_bf16<P>(asrc, a);
-    load_bf16<P>(asrc + h, b);
-    load_bf16<P>(gsrc, ga);
-    load_bf16<P>(gsrc + h, gb);
-    float ss = 0.f, sd = 0.f;
-#pragma unroll
-    for (int i = 0; i < P; ++i) {
-      float cn, sn;
-      rope_cs(rev[lq * P + i], s, cn, sn);
-      const float dua = ga[i] * cn + gb[i] * sn;  // R_{-p}
-      const float dub = gb[i] * cn - ga[i] * sn;
-      ga[i] = dua;
-      gb[i] = dub;
-      ss += a[i] * a[i] + b[i] * b[i];
-      sd += a[i] * dua + b[i] * dub;
-    }
-    ss = quad_sum(ss);
-    sd = quad_sum(sd);
-    const float rho = 1.0f / sqrtf(ss / (float)d + eps);
-    // rho^2 <u,du> / d, where <u,du> = rho * sum(a du)
-    const float coef = rho * rho * rho * sd / (float)d;
-#pragma unroll
-    for (int i = 0; i < P; ++i) {
-      ga[i] = rho * ga[i] - coef * a[i];
-      gb[i] = rho * gb[i] - coef * b[i];
-    }
-    uint16_t* dst = dqkv + t * N + rr * d + lq * P;
-    amax = max(amax, store_bf16<P>(dst, ga));
-    amax = max(amax, store_bf16<P>(dst + h, gb));
+  for (int64_t u = blockIdx.x * (int64_t)kThreads + threadIdx.x; u < units; u += 2 * stride) {
+    BwdRow<P> r0, r1;  // two rows' loads in flight per thread
+    bwd_load<P>(r0, u, units, R, H, seq_len, dq, dk, qk_pre, lq);
+    bwd_load<P>(r1, u + stride, units, R, H, seq_len, dq, dk, qk_pre, lq);
+    amax = max(amax, bwd_finish<P>(r0, rev, N, eps, dqkv, lq));
+    amax = max(amax, bwd_finish<P>(r1, rev, N, eps, dqkv, lq));
   }
   const int cv = dvw / 8;
   const int64_t vunits = T * H * cv;
