@@ -70,7 +70,7 @@ Plan make_plan(const fpr_dims* d, int64_t T) {
   p.T = T;
   p.Tp = round_up(T > 0 ? T : 1, 128);
   size_t c = 0;
-  p.s_x8t = take(c, (size_t)p.D * p.Tp);
+  p.s_x8t = take(c, fpr::t_blocked_bytes(p.D, p.Tp));
   p.s_qk = take(c, (size_t)T * p.nqk2 * 2);
   p.s_xsc = take(c, 4 * sizeof(float));
   p.saved_total = c;
@@ -78,15 +78,15 @@ Plan make_plan(const fpr_dims* d, int64_t T) {
   // one amax block per 256 x 16-byte vectors of x, at most kPartsAct
   p.f_parts = (int)std::max<int64_t>(1, std::min<int64_t>(kPartsAct, ceil_div(T * p.D / 8, fpr::kThreads)));
   p.f_part = take(c, (size_t)p.f_parts * 4);
-  p.f_x8 = take(c, (size_t)T * p.D);
+  p.f_x8 = take(c, fpr::act_blocked_bytes(T, p.D));
   p.fwd_total = c;
   c = 0;
   p.b_parts = fpr::norm_rope_bwd_blocks(T > 0 ? T : 1, p.H, p.dqk);
   p.b_part = take(c, (size_t)p.b_parts * 4);
   p.b_gsc = take(c, 4 * sizeof(float));
   p.b_dqkv = take(c, (size_t)T * p.N * 2);
-  p.b_g8 = take(c, (size_t)T * p.N);
-  p.b_g8t = take(c, (size_t)p.N * p.Tp);
+  p.b_g8 = take(c, fpr::act_blocked_bytes(T, p.N));
+  p.b_g8t = take(c, fpr::t_blocked_bytes(p.N, p.Tp));
   p.b_dwpart = take(c, fpr::dw_partial_bytes(p.D, p.N, p.Tp));
   p.bwd_total = c;
   c = 0;
@@ -190,6 +190,9 @@ int fpr_get_layout(const fpr_dims* dims, int64_t tokens, fpr_layout* out) {
   out->bwd_g8t = p.b_g8t;
   out->bwd_dw_part = p.b_dwpart;
   out->dw_splits = fpr::dw_splits(p.D, p.N, p.Tp);
+  out->k_block = fpr::kKBlock;
+  out->act_block_rows = fpr::kActRows;
+  out->t_block_rows = fpr::kTRows;
   return FPR_OK;
 }
 
@@ -248,7 +251,7 @@ int qkv_forward(const fpr_dims* dims, int32_t n_seq, int32_t seq_len, const uint
     fpr::launch_finalize_scales(parts, p.f_parts, xsc, cache->status, FPR_STATUS_X_NONFINITE,
                                 false, s);
   });
-  stage("quantize_x", s, [&] { fpr::launch_quantize_rows(x, T, p.D, xsc, x8, x8t, p.Tp, s); });
+  stage("quantize_x", s, [&] { fpr::launch_quantize_act(x, T, p.D, xsc, x8, x8t, p.Tp, s); });
   stage("gemm_fwd", s, [&] {
     fpr::launch_gemm_fwd(x8, cache->w_packed_t, (int)T, p.N, p.D, xsc, cache->scales, qk,
                          p.nqk2, v, p.H, p.dv, seq_len, s);
@@ -295,7 +298,7 @@ int qkv_backward(const fpr_dims* dims, int32_t n_seq, int32_t seq_len, const uin
     fpr::launch_finalize_scales(parts, p.b_parts, gsc, cache->status, FPR_STATUS_G_NONFINITE,
                                 false, s);
   });
-  stage("quantize_g", s, [&] { fpr::launch_quantize_rows(dqkv, T, p.N, gsc, g8, g8t, p.Tp, s); });
+  stage("quantize_g", s, [&] { fpr::launch_quantize_act(dqkv, T, p.N, gsc, g8, g8t, p.Tp, s); });
   stage("gemm_dx", s, [&] {
     fpr::launch_gemm_dx(g8, cache->w_packed, (int)T, p.D, p.N, gsc, cache->scales, dx, s);
   });

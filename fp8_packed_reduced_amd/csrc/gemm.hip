@@ -108,12 +108,16 @@ __device__ __forceinline__ v16f mfma32(v8i b, v8i a, v16f c) {
 // round-robin over the 8 XCDs, group x is one XCD: its blocks work on a
 // few row panels at a time that no other XCD touches, so the A rows come
 // from memory once and are shared in that XCD's L2.
+// An operand is either row-major with leading dimension ld, or blocked
+// (blk > 0): blocks of blk rows x 128 bytes of K, as the activation
+// quantiser writes them (blk equals the tile's rows for that operand).
 struct Gemm {
   const uint8_t* A;
   int64_t lda;
   const uint8_t* B;
   int64_t ldb;
   int M, N, K, n_tiles;
+  int a_blk, b_blk;  // 0: row-major; else block rows
 };
 
 struct Sched {
@@ -149,17 +153,21 @@ __device__ __forceinline__ void dma_plan(CopyState<C>& st, const Gemm& gm, int t
                                          int lane) {
   const int m0 = (tile / gm.n_tiles) * C::BM_, n0 = (tile % gm.n_tiles) * C::BN_;
   const int rl = lane >> 3, p = lane & 7;
+  const int64_t ra = gm.a_blk ? kBK : gm.lda, rb = gm.b_blk ? kBK : gm.ldb;
 #pragma unroll
   for (int t = 0; t < C::PER_WAVE; ++t) {
     const int row = (cw + kCopyWaves * t) * 8 + rl;
     const uint32_t chunk = (uint32_t)((p ^ (row & 7)) << 4);
     if (t < C::A_PER_WAVE)
-      st.off[t] = (uint32_t)((min(m0 + row, gm.M - 1) - m0) * gm.lda) + chunk;
+      st.off[t] = (uint32_t)((min(m0 + row, gm.M - 1) - m0) * ra) + chunk;
     else
-      st.off[t] = (uint32_t)((min(n0 + row - C::BM_, gm.N - 1) - n0) * gm.ldb) + chunk;
+      st.off[t] = (uint32_t)((min(n0 + row - C::BM_, gm.N - 1) - n0) * rb) + chunk;
   }
-  st.Atile = gm.A + (int64_t)m0 * gm.lda;
-  st.Btile = gm.B + (int64_t)n0 * gm.ldb;
+  const int64_t kblocks = (gm.K + kBK - 1) / kBK;
+  st.Atile = gm.a_blk ? gm.A + (int64_t)(m0 / C::BM_) * kblocks * C::BM_ * kBK
+                      : gm.A + (int64_t)m0 * gm.lda;
+  st.Btile = gm.b_blk ? gm.B + (int64_t)(n0 / C::BN_) * kblocks * C::BN_ * kBK
+                      : gm.B + (int64_t)n0 * gm.ldb;
   st.tile = tile;
 }
 
@@ -172,9 +180,9 @@ __device__ __forceinline__ void issue_next(CopyState<C>& st, uint8_t* lds, const
   const int g = st.issued++;
   const int tile = sc.tile(g);
   if (tile != st.tile) dma_plan<C>(st, gm, tile, cw, lane);
-  const int k0 = sc.ks(g) * kBK;
-  const uint8_t* Ak = st.Atile + k0;
-  const uint8_t* Bk = st.Btile + k0;
+  const int ks = sc.ks(g), k0 = ks * kBK;
+  const uint8_t* Ak = st.Atile + (gm.a_blk ? (int64_t)ks * C::BM_ * kBK : k0);
+  const uint8_t* Bk = st.Btile + (gm.b_blk ? (int64_t)ks * C::BN_ * kBK : k0);
   uint8_t* stage = lds + (g % kStages) * C::STAGE_BYTES;
 #pragma unroll
   for (int t = 0; t < C::PER_WAVE; ++t) {
@@ -571,16 +579,19 @@ static void launch_bf16out(const Gemm& gm, const float* sa, const float* sb, con
                                                                                sb, epi);
 }
 
+static_assert(kBMo == kActRows && kBMw == kTRows && kBNw == kTRows && kBK == kKBlock,
+              "GEMM tiles and the blocked activation layouts");
+
 void launch_gemm_fwd(const uint8_t* x8, const uint8_t* w_packed_t, int T, int N, int D,
                      const float* x_scales, const float* w_scales, uint16_t* qk_pre, int nqk2,
                      uint16_t* v, int H, int d_v, int seq_len, hipStream_t s) {
-  const Gemm gm{x8, D, w_packed_t, D, T, N, D, (int)ceil_div(N, kBNo)};
+  const Gemm gm{x8, 0, w_packed_t, D, T, N, D, (int)ceil_div(N, kBNo), kActRows, 0};
   launch_bf16out(gm, x_scales, w_scales, EpiFwd{qk_pre, v, N, nqk2, H, d_v, seq_len}, s);
 }
 
 void launch_gemm_dx(const uint8_t* g8, const uint8_t* w_packed, int T, int D, int Np,
                     const float* g_scales, const float* w_scales, uint16_t* dx, hipStream_t s) {
-  const Gemm gm{g8, Np, w_packed, Np, T, D, Np, (int)ceil_div(D, kBNo)};
+  const Gemm gm{g8, 0, w_packed, Np, T, D, Np, (int)ceil_div(D, kBNo), kActRows, 0};
   launch_bf16out(gm, g_scales, w_scales, EpiDx{dx, D}, s);
 }
 
@@ -608,7 +619,7 @@ void launch_gemm_dw(const uint8_t* x8t, const uint8_t* g8t, int D, int Np, int64
   const int splits = dw_splits(D, Np, Tp);
   const int nk = (int)ceil_div(Tp, kBK);
   const int per = (int)ceil_div(nk, splits);
-  const Gemm gm{x8t, Tp, g8t, Tp, D, Np, (int)Tp, (int)ceil_div(Np, kBNw)};
+  const Gemm gm{x8t, 0, g8t, 0, D, Np, (int)Tp, (int)ceil_div(Np, kBNw), kTRows, kTRows};
   const int blocks = (int)ceil_div(D, kBMw) * gm.n_tiles * splits;
   gemm_dw_part_kernel<kBMw, kBNw><<<blocks, kGemmThreads, 0, s>>>(gm, splits, per, part);
 }

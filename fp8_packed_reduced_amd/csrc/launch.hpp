@@ -6,6 +6,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "common.hpp"
+
 namespace fpr {
 
 // Largest token count a call accepts.  The GEMMs address a tile's rows by
@@ -36,11 +38,30 @@ void launch_quantize_w(const float* wq, int64_t ldq, const float* wk, int64_t ld
                        const float* scales, uint8_t* w_packed, uint8_t* w_packed_t,
                        hipStream_t s);
 
-// Quantise a [rows][cols] bf16 matrix with the per-tensor scale in `scales`:
-// dst [rows][cols] e4m3 (row-major) and dst_t [cols][ld_t] e4m3 (transposed;
-// columns rows..ld_t-1 are written as zero).  cols % 64 == 0, ld_t % 128 == 0.
-void launch_quantize_rows(const uint16_t* src, int64_t rows, int cols, const float* scales,
-                          uint8_t* dst, uint8_t* dst_t, int64_t ld_t, hipStream_t s);
+// Blocked layouts of the FP8 activation copies, which only the GEMMs read.
+// A matrix of R rows and K columns (K contiguous) is stored as blocks of
+// `block rows` x kKBlock bytes: block (R / block rows, K / kKBlock) at
+// ((r_blk * ceil(K / kKBlock) + k_blk) * block rows) * kKBlock, rows kKBlock
+// bytes apart inside.  One K step of a GEMM tile is then one contiguous
+// block, which keeps a CU's loads on few pages and whole cache lines.
+//   row layout (x8, g8; the A operand of forward / dX):   kActRows rows
+//   transposed layout (x8t, g8t; both operands of dW):     kTRows rows
+constexpr int kKBlock = 128, kActRows = 256, kTRows = 192;
+inline size_t act_blocked_bytes(int64_t rows, int64_t cols) {
+  return (size_t)round_up(rows, kActRows) * (size_t)round_up(cols, kKBlock);
+}
+inline size_t t_blocked_bytes(int64_t cols, int64_t tokens_padded) {
+  return (size_t)round_up(cols, kTRows) * (size_t)tokens_padded;
+}
+
+// Quantise a [rows][cols] bf16 matrix with the per-tensor scale in `scales`
+// into dst (row layout, rows x cols; columns cols .. multiple of kKBlock
+// written as zero) and dst_t (transposed layout, cols x tokens_padded;
+// tokens rows .. tokens_padded written as zero).  cols % 16 == 0,
+// tokens_padded % kKBlock == 0.  Rows past `rows` (resp. `cols`) inside
+// the last block of rows are left unwritten: the GEMMs never read them.
+void launch_quantize_act(const uint16_t* src, int64_t rows, int cols, const float* scales,
+                         uint8_t* dst, uint8_t* dst_t, int64_t tokens_padded, hipStream_t s);
 
 void launch_encode(const float* in, int64_t n, float inv, uint8_t* out, hipStream_t s);
 

@@ -1,6 +1,7 @@
 // Per-tensor e4m3 quantisers for gfx950: the packed weight (both cached
 // layouts from one read of W, PR #344 page, "Changes"), and bf16 activations
-// / gradients (row-major plus the transposed copy the dW GEMM streams).
+// / gradients (the GEMMs' blocked row layout plus the transposed copy the dW
+// GEMM streams, both from one read).
 //
 // The scale needs the whole tensor's amax before any code can be written,
 // so each quantiser is: per-block partial amax -> one-block finalize ->
@@ -146,55 +147,67 @@ __global__ __launch_bounds__(kThreads) void quantize_w_kernel(
   }
 }
 
-// ---------------------------------------- bf16 rows -> e4m3, two layouts
+// ------------------------------ bf16 rows -> e4m3, two blocked layouts
 
-// Tile of 128 rows x 64 columns per block.  Thread (rg, cc) owns rows
-// 4rg..4rg+3 and columns 8cc..8cc+7: it reads 4 x 16 B of bf16, writes 4 x 8 B
-// of codes to the row-major output, and for each of its 8 columns one dword
-// (4 consecutive rows) into the transposed LDS tile, from which full 16 B row
-// segments of the transposed output are written.
-__global__ __launch_bounds__(kThreads) void quantize_rows_kernel(
+// One block per 128 tokens x 128 columns (one K block of the row layout,
+// and one K block of the transposed layout).  Thread (rg, cc) owns tokens
+// 8rg..8rg+7 and columns 8cc..8cc+7: it reads 8 x 16 bytes of bf16 and
+// writes 8 x 8 bytes of codes into the row layout (16 threads cover a
+// block row's 128 bytes), and its 8 x 8 codes go, four tokens to a dword,
+// into an LDS tile from which the transposed layout's 128-byte token runs
+// are written as 16-byte chunks.
+__global__ __launch_bounds__(kThreads) void quantize_act_kernel(
     const uint16_t* __restrict__ src, int64_t rows, int cols, const float* __restrict__ scales,
-    uint8_t* __restrict__ dst, uint8_t* __restrict__ dst_t, int64_t ld_t) {
-  __shared__ uint32_t tile_t[64][32 + 1];  // [col][row/4], one dword = 4 rows
-  const int64_t r0 = (int64_t)blockIdx.x * 128;
-  const int c0 = blockIdx.y * 64;
-  const int cc = threadIdx.x & 7, rg = threadIdx.x >> 3;
+    uint8_t* __restrict__ dst, uint8_t* __restrict__ dst_t, int64_t tokens_padded) {
+  __shared__ uint32_t tile_t[kKBlock][kKBlock / 4 + 1];  // [column][token / 4]
+  const int64_t t0 = (int64_t)blockIdx.x * kKBlock;        // first token
+  const int kb = blockIdx.y, c0 = kb * kKBlock;            // K block of the row layout
+  const int cc = threadIdx.x & 15, rg = threadIdx.x >> 4;
   const float inv = scales[1];
-  uint32_t codes[4][2];
+  const int kblocks = (int)ceil_div(cols, kKBlock);
+  const int c = c0 + 8 * cc;
+  uint32_t codes[8][2];
 #pragma unroll
-  for (int r = 0; r < 4; ++r) {
-    const int64_t row = r0 + 4 * rg + r;
+  for (int i = 0; i < 8; ++i) {
+    const int64_t t = t0 + 8 * rg + i;
     uint4 v = make_uint4(0, 0, 0, 0);
-    if (row < rows)
-      v = *reinterpret_cast<const uint4*>(src + row * cols + c0 + 8 * cc);
-    codes[r][0] = e4m3x4(bf16_to_f32(v.x & 0xffffu) * inv, bf16_to_f32(v.x >> 16) * inv,
+    if (t < rows && c < cols) v = *reinterpret_cast<const uint4*>(src + t * cols + c);
+    codes[i][0] = e4m3x4(bf16_to_f32(v.x & 0xffffu) * inv, bf16_to_f32(v.x >> 16) * inv,
                          bf16_to_f32(v.y & 0xffffu) * inv, bf16_to_f32(v.y >> 16) * inv);
-    codes[r][1] = e4m3x4(bf16_to_f32(v.z & 0xffffu) * inv, bf16_to_f32(v.z >> 16) * inv,
+    codes[i][1] = e4m3x4(bf16_to_f32(v.z & 0xffffu) * inv, bf16_to_f32(v.z >> 16) * inv,
                          bf16_to_f32(v.w & 0xffffu) * inv, bf16_to_f32(v.w >> 16) * inv);
-    if (row < rows)
-      *reinterpret_cast<uint2*>(dst + row * cols + c0 + 8 * cc) =
-          make_uint2(codes[r][0], codes[r][1]);
+    if (t < rows) {
+      const int64_t blk = (t / kActRows) * kblocks + kb;
+      *reinterpret_cast<uint2*>(dst + (blk * kActRows + t % kActRows) * kKBlock + 8 * cc) =
+          make_uint2(codes[i][0], codes[i][1]);
+    }
   }
-  // byte j of column group: column 8cc + j; gather the 4 rows into a dword
+  // column 8cc + j: tokens 8rg..8rg+3 and 8rg+4..8rg+7 as two dwords
 #pragma unroll
   for (int j = 0; j < 8; ++j) {
     const int w = j >> 2, sh = (j & 3) * 8;
-    uint32_t d = ((codes[0][w] >> sh) & 0xffu) | (((codes[1][w] >> sh) & 0xffu) << 8) |
-                 (((codes[2][w] >> sh) & 0xffu) << 16) | (((codes[3][w] >> sh) & 0xffu) << 24);
-    tile_t[8 * cc + j][rg] = d;
+    uint32_t lo = 0, hi = 0;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      lo |= ((codes[i][w] >> sh) & 0xffu) << (8 * i);
+      hi |= ((codes[4 + i][w] >> sh) & 0xffu) << (8 * i);
+    }
+    tile_t[8 * cc + j][2 * rg] = lo;
+    tile_t[8 * cc + j][2 * rg + 1] = hi;
   }
   __syncthreads();
-  // 64 columns x 128 rows = 64 x 8 chunks of 16 B; two per thread
+  // 128 columns x 128 tokens = 128 x 8 chunks of 16 bytes; four per thread
+  const int64_t kt_blocks = tokens_padded / kKBlock, tk = t0 / kKBlock;
 #pragma unroll
-  for (int i = 0; i < 2; ++i) {
+  for (int i = 0; i < 4; ++i) {
     const int q = threadIdx.x + kThreads * i;
     const int col = q >> 3, ch = q & 7;
-    uint4 o = make_uint4(tile_t[col][4 * ch], tile_t[col][4 * ch + 1], tile_t[col][4 * ch + 2],
-                         tile_t[col][4 * ch + 3]);
-    const int64_t row = r0 + 16 * ch;
-    if (row < ld_t)
-      *reinterpret_cast<uint4*>(dst_t + (int64_t)(c0 + col) * ld_t + row) = o;
+    const int cg = c0 + col;
+    if (cg >= cols) continue;
+    const uint4 o = make_uint4(tile_t[col][4 * ch], tile_t[col][4 * ch + 1],
+                               tile_t[col][4 * ch + 2], tile_t[col][4 * ch + 3]);
+    const int64_t blk = (cg / kTRows) * kt_blocks + tk;
+    *reinterpret_cast<uint4*>(dst_t + (blk * kTRows + cg % kTRows) * kKBlock + 16 * ch) = o;
   }
 }
 
@@ -239,10 +252,11 @@ void launch_quantize_w(const float* wq, int64_t ldq, const float* wk, int64_t ld
                                               w_packed, w_packed_t);
 }
 
-void launch_quantize_rows(const uint16_t* src, int64_t rows, int cols, const float* scales,
-                          uint8_t* dst, uint8_t* dst_t, int64_t ld_t, hipStream_t s) {
-  dim3 grid((unsigned)(ld_t / 128), (unsigned)(cols / 64));
-  quantize_rows_kernel<<<grid, kThreads, 0, s>>>(src, rows, cols, scales, dst, dst_t, ld_t);
+void launch_quantize_act(const uint16_t* src, int64_t rows, int cols, const float* scales,
+                         uint8_t* dst, uint8_t* dst_t, int64_t tokens_padded, hipStream_t s) {
+  dim3 grid((unsigned)(tokens_padded / kKBlock), (unsigned)ceil_div(cols, kKBlock));
+  quantize_act_kernel<<<grid, kThreads, 0, s>>>(src, rows, cols, scales, dst, dst_t,
+                                                tokens_padded);
 }
 
 void launch_encode(const float* in, int64_t n, float inv, uint8_t* out, hipStream_t s) {

@@ -32,6 +32,28 @@ def dims_for(w: dict):
     return B.make_dims(w["d_model"], w["n_heads"], w["d_qk"], w["d_v"], EPS, BASE)
 
 
+def _ceil(a: int, b: int) -> int:
+    return -(-a // b)
+
+
+def unblock_rows(buf, off: int, rows: int, cols: int, lay) -> np.ndarray:
+    """[rows_pad][cols_pad] bytes from the row-blocked FP8 layout: blocks of
+    act_block_rows x k_block bytes, ceil(cols / k_block) blocks per block row."""
+    R, KB = lay.act_block_rows, lay.k_block
+    nb, kc = _ceil(rows, R), _ceil(cols, KB)
+    a = B.view_bytes(buf, off, (nb, kc, R, KB), torch.uint8).cpu().numpy()
+    return a.transpose(0, 2, 1, 3).reshape(nb * R, kc * KB)
+
+
+def unblock_t(buf, off: int, cols: int, lay) -> np.ndarray:
+    """[cols_pad][tokens_padded] bytes from the transposed-blocked FP8 layout:
+    blocks of t_block_rows x k_block tokens, tokens_padded / k_block per block row."""
+    R, KB, Tp = lay.t_block_rows, lay.k_block, lay.tokens_padded
+    nb, kt = _ceil(cols, R), Tp // KB
+    a = B.view_bytes(buf, off, (nb, kt, R, KB), torch.uint8).cpu().numpy()
+    return a.transpose(0, 2, 1, 3).reshape(nb * R, kt * KB)
+
+
 def run(w: dict, seed: int = 42, x_bits=None, W=None, dy=None, backward: bool = True):
     """Pack, forward (and backward) on the GPU; returns a dict of numpy arrays."""
     n_seq, S = w["n_seq"], w["seq_len"]
@@ -60,8 +82,9 @@ def run(w: dict, seed: int = 42, x_bits=None, W=None, dy=None, backward: bool = 
     out["w_packed"] = cache.w_packed.cpu().numpy()
     out["w_packed_t"] = cache.w_packed_t.cpu().numpy()
     out["w_scales"] = cache.scales.cpu().numpy()
-    out["x8"] = B.view_bytes(ws_f, lay.fwd_x8, (T, D), torch.uint8).cpu().numpy()
-    out["x8t"] = B.view_bytes(saved, lay.saved_x8t, (D, Tp), torch.uint8).cpu().numpy()
+    x8 = unblock_rows(ws_f, lay.fwd_x8, T, D, lay)
+    out["x8"], out["x8_kpad"] = x8[:T, :D], x8[:T, D:]
+    out["x8t"] = unblock_t(saved, lay.saved_x8t, D, lay)[:D]
     out["x_scales"] = B.view_bytes(saved, lay.saved_x_scales, (2,), torch.float32).cpu().numpy()
     out["qk_pre"] = dev_to_bits(B.view_bytes(saved, lay.saved_qk_pre, (T, 2 * nq), torch.bfloat16))
     out["q"], out["k"], out["v"] = dev_to_bits(q), dev_to_bits(k), dev_to_bits(v)
@@ -76,8 +99,9 @@ def run(w: dict, seed: int = 42, x_bits=None, W=None, dy=None, backward: bool = 
         out["dy"] = dy
         out["dqkv"] = dev_to_bits(B.view_bytes(ws_b, lay.bwd_dqkv, (T, N), torch.bfloat16))
         out["g_scales"] = B.view_bytes(ws_b, lay.bwd_g_scales, (2,), torch.float32).cpu().numpy()
-        out["g8"] = B.view_bytes(ws_b, lay.bwd_g8, (T, N), torch.uint8).cpu().numpy()
-        out["g8t"] = B.view_bytes(ws_b, lay.bwd_g8t, (N, Tp), torch.uint8).cpu().numpy()
+        g8 = unblock_rows(ws_b, lay.bwd_g8, T, N, lay)
+        out["g8"], out["g8_kpad"] = g8[:T, :N], g8[:T, N:]
+        out["g8t"] = unblock_t(ws_b, lay.bwd_g8t, N, lay)[:N]
         out["dx"] = dev_to_bits(dx)
         out["dw"] = dw.cpu().numpy()
     out["status"] = int(cache.status.cpu().item())

@@ -51,6 +51,22 @@ def test_sizes_and_layout_at_the_64k_step_shape():
     assert lay.bwd_dw_part + lay.dw_splits * 768 * 1920 * 4 <= bw
 
 
+def test_blocked_fp8_layouts_cover_their_padding():
+    # ragged everywhere: 154 tokens, D = 192, N = 2 * 2 * 48 + 2 * 64 = 320
+    d = B.make_dims(192, 2, 48, 64)
+    T = 154
+    lay = B.layout(d, T)
+    assert (lay.k_block, lay.act_block_rows, lay.t_block_rows) == (128, 256, 192)
+    assert lay.tokens_padded == 256
+    # row-blocked x8: 256 rows x 2 K blocks of 128 bytes
+    assert B.workspace_bytes(d, T, B.FPR_CALL_FORWARD) >= lay.fwd_x8 + 256 * 256
+    # transposed-blocked x8t: one block of 192 features x 256 tokens
+    assert lay.saved_x8t + 192 * 256 <= lay.saved_qk_pre
+    # g8 256 x 384 bytes before g8t; g8t 2 blocks of 192 rows x 256 tokens
+    assert lay.bwd_g8 + 256 * 384 <= lay.bwd_g8t
+    assert lay.bwd_g8t + 384 * 256 <= lay.bwd_dw_part
+
+
 def test_dw_split_count_depends_only_on_shapes():
     d = B.make_dims(768, 6)
     # 768 x 1920 in 192 x 192 tiles is 40 tiles; 6 splits make 240 blocks,
