@@ -27,6 +27,16 @@ __device__ inline uint32_t f32_to_bf16(float f) {
   return u >> 16;
 }
 
+typedef float v2f_t __attribute__((ext_vector_type(2)));
+typedef __bf16 v2bf_t __attribute__((ext_vector_type(2)));
+
+// fp32 pair -> packed bf16 pair with the gfx950 converter: round to nearest
+// even (the same bits as f32_to_bf16 for every non-NaN input).
+__device__ inline uint32_t cvt_bf16x2_rn(float a, float b) {
+  const v2f_t x = {a, b};
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(x, v2bf_t));
+}
+
 __device__ inline uint32_t pack_bf16x2(float a, float b) {
   return f32_to_bf16(a) | (f32_to_bf16(b) << 16);
 }

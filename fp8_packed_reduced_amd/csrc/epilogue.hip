@@ -11,12 +11,12 @@
 // the V gradient is re-laid out; everything is packed into dQKV [T][N] bf16
 // with one amax partial per block for the gradient quantiser.
 //
-// Main kernels (d = 64, 96, 128): four consecutive lanes own one head row,
-// lane q the P = d/8 pairs (i, i + d/2) for i in [qP, qP + P), so a RoPE
-// pair never leaves a thread and the row sums take two cross-lane steps
-// (DPP quad permutes) with no LDS.  Rotation angles are formed in
+// Main kernels (d = 64, 96, 128): four consecutive lanes own one head row
+// and every access is a whole 16-byte chunk (below); the row sums take two
+// cross-lane steps (DPP quad permutes).  Rotation angles are formed in
 // revolutions: position * theta_j / (2 pi) in double, reduced to its
-// fractional part, then the hardware sin/cos of that fraction.
+// fractional part, then the hardware sin/cos of that fraction, once per
+// token and pair into an LDS table that all heads share.
 //
 // Fallback kernels (other head widths): work item = (token, head row,
 // chunk c), a thread owns the 8 elements [8c, 8c+8) of a row and their
@@ -72,34 +72,7 @@ __device__ inline uint32_t absmax8(uint4 v) {
   return m;
 }
 
-// ------------------------------------------------- quad-lane kernels
-
-constexpr int kQuadBlocks = 2048;  // grid of the grid-stride quad kernels
-
-// Work of the forward quad kernel: a wave's 16 quads (one head row each)
-// cover TG consecutive tokens x HG consecutive head rows (4 x 4, or 8 x 2
-// when the 2H head rows are not a multiple of 4), so each token's rows that
-// a wave reads, and each head's rows it writes head-major, are runs of HG
-// (resp. TG) whole rows: 768 contiguous bytes for 96-wide heads, whole
-// cache lines, where rows of 192 bytes alone would leave lines half
-// written.  The backward kernel, whose large streams (pre-norm rows in,
-// dQKV out) are both token-major, takes head rows in plain row order.
-__host__ __device__ inline int quad_heads(int R) { return R % 4 == 0 ? 4 : 2; }
-__host__ __device__ inline int64_t quad_units(int64_t T, int R) {
-  const int HG = quad_heads(R);
-  return ceil_div(T, 16 / HG) * (R / HG) * 64;
-}
-
-// Token and head row of quad-kernel unit u (lane u % 4 of its quad).
-__device__ inline void quad_row(int64_t u, int R, int64_t& t, int& rr) {
-  const int HG = quad_heads(R), TG = 16 / HG, n_hg = R / HG;
-  const int64_t w = u >> 6;
-  const int qd = (int)((u >> 2) & 15);
-  const int64_t tg = w / n_hg;
-  const int hg = (int)(w - tg * n_hg);
-  t = tg * TG + qd % TG;
-  rr = hg * HG + qd / TG;
-}
+// ------------------------------------------------------- shared helpers
 
 // theta_j / (2 pi) = base^(-2j/d) / (2 pi), j < h, for the block.
 __device__ inline void build_rev_table(double* rev, int h, int d, float base) {
@@ -124,203 +97,286 @@ __device__ inline float quad_sum(float v) {
   return v;
 }
 
-template <int P>
-__device__ inline void load_bf16(const uint16_t* p, float (&f)[P]) {
+// ------------------------------------------------- quad-chunk kernels
+//
+// Four lanes per head row, every access a whole 16-byte chunk (8-byte
+// lane accesses split each memory instruction over many partial lines and
+// ran ~25% slower here): of the CH = d / 8 chunks of a row, lane l owns
+// chunks l, l + 4, l + 8, ... (M = CH / 4 of them), so each load or store
+// instruction covers 64 consecutive bytes of every row in the wave.  The
+// RoPE partner of chunk c (elements i + d/2 of its elements i) is chunk
+// c +- CH/2: for d = 64 and 128 that is another chunk of the same lane;
+// for d = 96 it is a chunk of lane l ^ 2, which one DPP quad permute per
+// word brings over.  A block takes TT tokens at a time and first builds the
+// cos/sin table of their positions (shared by all heads) in LDS.
+
+constexpr int kQuadTT = 16;         // tokens per block iteration
+constexpr int kQuadTileBlocks = 2048;
+
+template <int D>
+struct QuadChunks {
+  static constexpr int CH = D / 8, HC = CH / 2, M = CH / 4, h = D / 2;
+  static_assert(CH % 4 == 0, "four lanes per row");
+  // chunk of lane l, own slot m
+  __device__ static int chunk(int l, int m) { return l + 4 * m; }
+  // the slot (in lane l ^ 2 for d = 96, else in lane l) holding the partner of slot m
+  __device__ static int partner_slot(int l, int m) {
+    if (CH == 12) return (m + (l < 2 ? 1 : 2)) % 3;
+    return (m + M / 2) % M;
+  }
+};
+
+__device__ __forceinline__ uint32_t dpp_quad_xor2(uint32_t v) {
+  return (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0x4E, 0xF, 0xF, true);  // [2,3,0,1]
+}
+
+// Partner chunks of the lane's M chunks.
+template <int D>
+__device__ __forceinline__ void quad_partners(const uint4 (&own)[QuadChunks<D>::M],
+                                              uint4 (&par)[QuadChunks<D>::M], int l) {
+  using Q = QuadChunks<D>;
+  if constexpr (Q::CH == 12) {
+    uint4 x[3];
 #pragma unroll
-  for (int i = 0; i < P / 4; ++i) {
-    const uint2 w = *reinterpret_cast<const uint2*>(p + 4 * i);
-    f[4 * i] = bf16_to_f32(w.x & 0xffffu);
-    f[4 * i + 1] = bf16_to_f32(w.x >> 16);
-    f[4 * i + 2] = bf16_to_f32(w.y & 0xffffu);
-    f[4 * i + 3] = bf16_to_f32(w.y >> 16);
+    for (int m = 0; m < 3; ++m)
+      x[m] = make_uint4(dpp_quad_xor2(own[m].x), dpp_quad_xor2(own[m].y), dpp_quad_xor2(own[m].z),
+                        dpp_quad_xor2(own[m].w));
+    // lanes 0, 1 take slot (m + 1) % 3 of lane l ^ 2, lanes 2, 3 slot (m + 2) % 3
+#pragma unroll
+    for (int m = 0; m < 3; ++m) par[m] = l < 2 ? x[(m + 1) % 3] : x[(m + 2) % 3];
+  } else {
+#pragma unroll
+    for (int m = 0; m < Q::M; ++m) par[m] = own[(m + Q::M / 2) % Q::M];
   }
 }
 
-// Stores P values as bf16 and returns the largest |bf16| bit pattern.
-template <int P>
-__device__ inline uint32_t store_bf16(uint16_t* p, const float (&f)[P]) {
-  uint32_t m = 0;
-#pragma unroll
-  for (int i = 0; i < P / 4; ++i) {
-    const uint2 w = make_uint2(pack_bf16x2(f[4 * i], f[4 * i + 1]),
-                               pack_bf16x2(f[4 * i + 2], f[4 * i + 3]));
-    *reinterpret_cast<uint2*>(p + 4 * i) = w;
-    m = max(m, max(max(w.x & 0x7fffu, (w.x >> 16) & 0x7fffu),
-                   max(w.y & 0x7fffu, (w.y >> 16) & 0x7fffu)));
-  }
-  return m;
+__device__ __forceinline__ uint4 pack8_rn(const float* f) {
+  return make_uint4(cvt_bf16x2_rn(f[0], f[1]), cvt_bf16x2_rn(f[2], f[3]),
+                    cvt_bf16x2_rn(f[4], f[5]), cvt_bf16x2_rn(f[6], f[7]));
 }
 
-// One head row of the forward quad kernel: loaded first, finished later,
-// so a thread can have several rows' loads in flight.
-template <int P>
-struct FwdRow {
-  float a[P], b[P];
-  int64_t t;
-  int rr;
+// cos/sin of pairs j < h at the positions of tokens t0 .. t0 + nt - 1, and
+// the tokens' sequence indices and positions.
+__device__ inline void quad_table(float2* cs, int64_t* bq, int* sp, const double* rev, int64_t t0,
+                                  int nt, int h, int seq_len) {
+  for (int i = threadIdx.x; i < nt * h; i += kThreads) {
+    const int tt = i / h, j = i - tt * h;
+    const int64_t t = t0 + tt;
+    float cn, sn;
+    rope_cs(rev[j], t - (t / seq_len) * seq_len, cn, sn);
+    cs[i] = make_float2(cn, sn);
+  }
+  if (threadIdx.x < nt) {
+    const int64_t t = t0 + threadIdx.x;
+    bq[threadIdx.x] = t / seq_len;
+    sp[threadIdx.x] = (int)(t - (t / seq_len) * seq_len);
+  }
+}
+
+template <int D>
+struct QcFwdRow {
+  uint4 own[QuadChunks<D>::M];
+  int tt, rr;
   bool ok;
 };
 
-template <int P>
-__device__ __forceinline__ void fwd_load(FwdRow<P>& r, int64_t u, int64_t units, int64_t T, int R,
-                                         const uint16_t* __restrict__ qk_pre, int lq) {
-  constexpr int h = 4 * P, d = 2 * h;
-  r.ok = false;
-  if (u >= units) return;
-  quad_row(u, R, r.t, r.rr);
-  if (r.t >= T) return;  // the whole quad
-  r.ok = true;
-  const uint16_t* src = qk_pre + (r.t * R + r.rr) * d + lq * P;  // row t, head row rr
-  load_bf16<P>(src, r.a);
-  load_bf16<P>(src + h, r.b);
+template <int D>
+__device__ __forceinline__ void qc_fwd_load(QcFwdRow<D>& r, int row, int rows, int R, int64_t t0,
+                                            const uint16_t* __restrict__ qk_pre, int l) {
+  using Q = QuadChunks<D>;
+  r.ok = row < rows;
+  if (!r.ok) return;
+  r.tt = row / R;
+  r.rr = row - r.tt * R;
+  const uint16_t* src = qk_pre + ((t0 + r.tt) * R + r.rr) * D;
+#pragma unroll
+  for (int m = 0; m < Q::M; ++m) r.own[m] = *reinterpret_cast<const uint4*>(src + 8 * Q::chunk(l, m));
 }
 
-template <int P>
-__device__ __forceinline__ void fwd_finish(FwdRow<P>& r, const double* rev, int seq_len, int H,
-                                           float eps, uint16_t* __restrict__ q,
-                                           uint16_t* __restrict__ k, int lq) {
-  constexpr int h = 4 * P, d = 2 * h;
+template <int D>
+__device__ __forceinline__ void qc_fwd_finish(const QcFwdRow<D>& r, const float2* cs,
+                                              const int64_t* bq, const int* sp, int H,
+                                              int seq_len, float eps, uint16_t* __restrict__ q,
+                                              uint16_t* __restrict__ k, int l) {
+  using Q = QuadChunks<D>;
+  constexpr int h = Q::h, M = Q::M, HC = Q::HC;
   if (!r.ok) return;
   float ss = 0.f;
 #pragma unroll
-  for (int i = 0; i < P; ++i) ss += r.a[i] * r.a[i] + r.b[i] * r.b[i];
-  ss = quad_sum(ss);
-  const float rho = 1.0f / sqrtf(ss / (float)d + eps);
-  const int64_t bseq = r.t / seq_len, s = r.t - bseq * seq_len;
+  for (int m = 0; m < M; ++m) {
+    float x[8];
+    unpack8(r.own[m], x);
 #pragma unroll
-  for (int i = 0; i < P; ++i) {
-    float cn, sn;
-    rope_cs(rev[lq * P + i], s, cn, sn);
-    const float ua = r.a[i] * rho, ub = r.b[i] * rho;
-    r.a[i] = ua * cn - ub * sn;
-    r.b[i] = ub * cn + ua * sn;
+    for (int e = 0; e < 8; ++e) ss += x[e] * x[e];
   }
-  const int rr = r.rr;
-  uint16_t* dst = (rr < H ? q + ((bseq * H + rr) * seq_len + s) * d
-                          : k + ((bseq * H + (rr - H)) * seq_len + s) * d) + lq * P;
-  store_bf16<P>(dst, r.a);
-  store_bf16<P>(dst + h, r.b);
+  ss = quad_sum(ss);
+  const float rho = 1.0f / sqrtf(ss / (float)D + eps);
+  uint4 par[M];
+  quad_partners<D>(r.own, par, l);
+  const int tt = r.tt, rr = r.rr, hh = rr < H ? rr : rr - H;
+  uint16_t* dst = (rr < H ? q : k) + ((bq[tt] * H + hh) * seq_len + sp[tt]) * D;
+#pragma unroll
+  for (int m = 0; m < M; ++m) {
+    const int c = Q::chunk(l, m);
+    const bool lower = c < HC;
+    const float2* tab = cs + tt * h + 8 * (lower ? c : c - HC);
+    float x[8], y[8], o[8];
+    unpack8(r.own[m], x);
+    unpack8(par[m], y);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const float u = x[e] * rho, w = y[e] * rho, cn = tab[e].x, sn = tab[e].y;
+      o[e] = lower ? u * cn - w * sn : u * cn + w * sn;
+    }
+    *reinterpret_cast<uint4*>(dst + 8 * c) = pack8_rn(o);
+  }
 }
 
-template <int P>
-__global__ __launch_bounds__(kThreads) void norm_rope_fwd_quad(
+template <int D>
+__global__ __launch_bounds__(kThreads) void norm_rope_fwd_qc(
     const uint16_t* __restrict__ qk_pre, int64_t T, int seq_len, int H, float eps, float base,
     uint16_t* __restrict__ q, uint16_t* __restrict__ k) {
-  constexpr int h = 4 * P, d = 2 * h;
+  using Q = QuadChunks<D>;
+  constexpr int h = Q::h, QUADS = kThreads / 4;
   __shared__ double rev[h];
-  build_rev_table(rev, h, d, base);
-  const int R = 2 * H, lq = threadIdx.x & 3;
-  const int64_t units = quad_units(T, R), stride = (int64_t)gridDim.x * kThreads;
-  for (int64_t u = blockIdx.x * (int64_t)kThreads + threadIdx.x; u < units; u += 2 * stride) {
-    FwdRow<P> r0, r1;  // two rows' loads in flight per thread
-    fwd_load<P>(r0, u, units, T, R, qk_pre, lq);
-    fwd_load<P>(r1, u + stride, units, T, R, qk_pre, lq);
-    fwd_finish<P>(r0, rev, seq_len, H, eps, q, k, lq);
-    fwd_finish<P>(r1, rev, seq_len, H, eps, q, k, lq);
+  __shared__ float2 cs[kQuadTT * h];
+  __shared__ int64_t bq[kQuadTT];
+  __shared__ int sp[kQuadTT];
+  build_rev_table(rev, h, D, base);
+  const int R = 2 * H, l = threadIdx.x & 3;
+  const int64_t groups = ceil_div(T, kQuadTT);
+  for (int64_t gi = blockIdx.x; gi < groups; gi += gridDim.x) {
+    const int64_t t0 = gi * kQuadTT;
+    const int nt = (int)min<int64_t>(kQuadTT, T - t0), rows = nt * R;
+    quad_table(cs, bq, sp, rev, t0, nt, h, seq_len);
+    __syncthreads();
+    for (int row = threadIdx.x >> 2; row < rows; row += 2 * QUADS) {
+      QcFwdRow<D> r0, r1;  // two rows' loads in flight per thread
+      qc_fwd_load<D>(r0, row, rows, R, t0, qk_pre, l);
+      qc_fwd_load<D>(r1, row + QUADS, rows, R, t0, qk_pre, l);
+      qc_fwd_finish<D>(r0, cs, bq, sp, H, seq_len, eps, q, k, l);
+      qc_fwd_finish<D>(r1, cs, bq, sp, H, seq_len, eps, q, k, l);
+    }
+    __syncthreads();
   }
 }
 
-// One head row of the backward quad kernel, loaded first and finished
-// later (as FwdRow).
-template <int P>
-struct BwdRow {
-  float a[P], b[P], ga[P], gb[P];
-  int64_t t, s;
-  int rr;
+template <int D>
+struct QcBwdRow {
+  uint4 a[QuadChunks<D>::M], g[QuadChunks<D>::M];
+  int tt, rr;
   bool ok;
 };
 
-template <int P>
-__device__ __forceinline__ void bwd_load(BwdRow<P>& r, int64_t u, int64_t units, int R, int H,
-                                         int seq_len, const uint16_t* __restrict__ dq,
-                                         const uint16_t* __restrict__ dk,
-                                         const uint16_t* __restrict__ qk_pre, int lq) {
-  constexpr int h = 4 * P, d = 2 * h;
-  r.ok = u < units;
+template <int D>
+__device__ __forceinline__ void qc_bwd_load(QcBwdRow<D>& r, int row, int rows, int R, int H,
+                                            int seq_len, int64_t t0, const int64_t* bq,
+                                            const int* sp, const uint16_t* __restrict__ dq,
+                                            const uint16_t* __restrict__ dk,
+                                            const uint16_t* __restrict__ qk_pre, int l) {
+  using Q = QuadChunks<D>;
+  r.ok = row < rows;
   if (!r.ok) return;
-  const int64_t row = u >> 2;
-  r.t = row / R;
-  r.rr = (int)(row - r.t * R);
-  const int64_t bseq = r.t / seq_len;
-  r.s = r.t - bseq * seq_len;
-  const int rr = r.rr;
-  const uint16_t* asrc = qk_pre + row * d + lq * P;
-  const uint16_t* gsrc = (rr < H ? dq + ((bseq * H + rr) * seq_len + r.s) * d
-                                 : dk + ((bseq * H + (rr - H)) * seq_len + r.s) * d) + lq * P;
-  load_bf16<P>(asrc, r.a);
-  load_bf16<P>(asrc + h, r.b);
-  load_bf16<P>(gsrc, r.ga);
-  load_bf16<P>(gsrc + h, r.gb);
+  const int tt = row / R, rr = row - tt * R, hh = rr < H ? rr : rr - H;
+  r.tt = tt;
+  r.rr = rr;
+  const uint16_t* asrc = qk_pre + ((t0 + tt) * R + rr) * D;
+  const uint16_t* gsrc = (rr < H ? dq : dk) + ((bq[tt] * H + hh) * seq_len + sp[tt]) * D;
+#pragma unroll
+  for (int m = 0; m < Q::M; ++m) {
+    r.a[m] = *reinterpret_cast<const uint4*>(asrc + 8 * Q::chunk(l, m));
+    r.g[m] = *reinterpret_cast<const uint4*>(gsrc + 8 * Q::chunk(l, m));
+  }
 }
 
-// Finishes the row and returns the largest |bf16| bit pattern it wrote.
-template <int P>
-__device__ __forceinline__ uint32_t bwd_finish(BwdRow<P>& r, const double* rev, int N,
-                                               float eps, uint16_t* __restrict__ dqkv, int lq) {
-  constexpr int h = 4 * P, d = 2 * h;
+// Finishes the row into dQKV and returns the largest |bf16| bit pattern.
+template <int D>
+__device__ __forceinline__ uint32_t qc_bwd_finish(const QcBwdRow<D>& r, const float2* cs,
+                                                  int64_t t0, int N, float eps,
+                                                  uint16_t* __restrict__ dqkv, int l) {
+  using Q = QuadChunks<D>;
+  constexpr int h = Q::h, M = Q::M, HC = Q::HC;
   if (!r.ok) return 0;
-  float ss = 0.f, sd = 0.f;
+  uint4 pg[M];
+  quad_partners<D>(r.g, pg, l);
+  // own element e of slot m is a_i (lower chunks) or b_i, i = 8 (c mod HC) + e;
+  // du = R_{-p} dq
+  float du[M][8], ss = 0.f, sd = 0.f;
 #pragma unroll
-  for (int i = 0; i < P; ++i) {
-    float cn, sn;
-    rope_cs(rev[lq * P + i], r.s, cn, sn);
-    const float dua = r.ga[i] * cn + r.gb[i] * sn;  // R_{-p}
-    const float dub = r.gb[i] * cn - r.ga[i] * sn;
-    r.ga[i] = dua;
-    r.gb[i] = dub;
-    ss += r.a[i] * r.a[i] + r.b[i] * r.b[i];
-    sd += r.a[i] * dua + r.b[i] * dub;
+  for (int m = 0; m < M; ++m) {
+    const int c = Q::chunk(l, m);
+    const bool lower = c < HC;
+    const float2* tab = cs + r.tt * h + 8 * (lower ? c : c - HC);
+    float x[8], gx[8], gp[8];
+    unpack8(r.a[m], x);
+    unpack8(r.g[m], gx);
+    unpack8(pg[m], gp);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const float cn = tab[e].x, sn = tab[e].y;
+      du[m][e] = lower ? gx[e] * cn + gp[e] * sn : gx[e] * cn - gp[e] * sn;
+      ss += x[e] * x[e];
+      sd += x[e] * du[m][e];
+    }
   }
   ss = quad_sum(ss);
   sd = quad_sum(sd);
-  const float rho = 1.0f / sqrtf(ss / (float)d + eps);
+  const float rho = 1.0f / sqrtf(ss / (float)D + eps);
   // rho^2 <u,du> / d, where <u,du> = rho * sum(a du)
-  const float coef = rho * rho * rho * sd / (float)d;
+  const float coef = rho * rho * rho * sd / (float)D;
+  uint16_t* dst = dqkv + (t0 + r.tt) * N + r.rr * D;
+  uint32_t amax = 0;
 #pragma unroll
-  for (int i = 0; i < P; ++i) {
-    r.ga[i] = rho * r.ga[i] - coef * r.a[i];
-    r.gb[i] = rho * r.gb[i] - coef * r.b[i];
+  for (int m = 0; m < M; ++m) {
+    float x[8], o[8];
+    unpack8(r.a[m], x);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) o[e] = rho * du[m][e] - coef * x[e];
+    const uint4 pk = pack8_rn(o);
+    amax = max(amax, absmax8(pk));
+    *reinterpret_cast<uint4*>(dst + 8 * Q::chunk(l, m)) = pk;
   }
-  uint16_t* dst = dqkv + r.t * N + r.rr * d + lq * P;
-  const uint32_t m = store_bf16<P>(dst, r.ga);
-  return max(m, store_bf16<P>(dst + h, r.gb));
+  return amax;
 }
 
-// Backward, then the V gradient re-laid out into the packed rows; one amax
-// partial per block.
-template <int P>
-__global__ __launch_bounds__(kThreads) void norm_rope_bwd_quad(
+template <int D>
+__global__ __launch_bounds__(kThreads) void norm_rope_bwd_qc(
     const uint16_t* __restrict__ dq, const uint16_t* __restrict__ dk,
     const uint16_t* __restrict__ dv, const uint16_t* __restrict__ qk_pre, int64_t T,
     int seq_len, int H, int dvw, float eps, float base, uint16_t* __restrict__ dqkv,
     uint32_t* __restrict__ partials) {
-  constexpr int h = 4 * P, d = 2 * h;
+  using Q = QuadChunks<D>;
+  constexpr int h = Q::h, QUADS = kThreads / 4;
   __shared__ double rev[h];
+  __shared__ float2 cs[kQuadTT * h];
+  __shared__ int64_t bq[kQuadTT];
+  __shared__ int sp[kQuadTT];
   __shared__ uint32_t red[4];
-  build_rev_table(rev, h, d, base);
-  const int R = 2 * H, qkw = R * d, N = qkw + H * dvw, lq = threadIdx.x & 3;
-  const int64_t stride = (int64_t)gridDim.x * kThreads;
+  build_rev_table(rev, h, D, base);
+  const int R = 2 * H, qkw = R * D, N = qkw + H * dvw, CV = dvw / 8, l = threadIdx.x & 3;
   uint32_t amax = 0;
-  const int64_t units = T * R * 4;
-  for (int64_t u = blockIdx.x * (int64_t)kThreads + threadIdx.x; u < units; u += 2 * stride) {
-    BwdRow<P> r0, r1;  // two rows' loads in flight per thread
-    bwd_load<P>(r0, u, units, R, H, seq_len, dq, dk, qk_pre, lq);
-    bwd_load<P>(r1, u + stride, units, R, H, seq_len, dq, dk, qk_pre, lq);
-    amax = max(amax, bwd_finish<P>(r0, rev, N, eps, dqkv, lq));
-    amax = max(amax, bwd_finish<P>(r1, rev, N, eps, dqkv, lq));
-  }
-  const int cv = dvw / 8;
-  const int64_t vunits = T * H * cv;
-  for (int64_t u = blockIdx.x * (int64_t)kThreads + threadIdx.x; u < vunits; u += stride) {
-    const int64_t th = u / cv;
-    const int c = (int)(u - th * cv);
-    const int64_t t = th / H;
-    const int hh = (int)(th - t * H);
-    const int64_t bseq = t / seq_len, s = t - bseq * seq_len;
-    const uint4 g =
-        *reinterpret_cast<const uint4*>(dv + ((bseq * H + hh) * seq_len + s) * dvw + 8 * c);
-    amax = max(amax, absmax8(g));
-    *reinterpret_cast<uint4*>(dqkv + t * N + qkw + hh * dvw + 8 * c) = g;
+  const int64_t groups = ceil_div(T, kQuadTT);
+  for (int64_t gi = blockIdx.x; gi < groups; gi += gridDim.x) {
+    const int64_t t0 = gi * kQuadTT;
+    const int nt = (int)min<int64_t>(kQuadTT, T - t0), rows = nt * R;
+    quad_table(cs, bq, sp, rev, t0, nt, h, seq_len);
+    __syncthreads();
+    for (int row = threadIdx.x >> 2; row < rows; row += 2 * QUADS) {
+      QcBwdRow<D> r0, r1;  // two rows' loads in flight per thread
+      qc_bwd_load<D>(r0, row, rows, R, H, seq_len, t0, bq, sp, dq, dk, qk_pre, l);
+      qc_bwd_load<D>(r1, row + QUADS, rows, R, H, seq_len, t0, bq, sp, dq, dk, qk_pre, l);
+      amax = max(amax, qc_bwd_finish<D>(r0, cs, t0, N, eps, dqkv, l));
+      amax = max(amax, qc_bwd_finish<D>(r1, cs, t0, N, eps, dqkv, l));
+    }
+    // V gradient: head hh, tokens consecutive (contiguous reads)
+    for (int i = threadIdx.x; i < nt * H * CV; i += kThreads) {
+      const int cc = i % CV, rest = i / CV, tt = rest % nt, hh = rest / nt;
+      const uint4 g = *reinterpret_cast<const uint4*>(
+          dv + ((bq[tt] * H + hh) * seq_len + sp[tt]) * dvw + 8 * cc);
+      amax = max(amax, absmax8(g));
+      *reinterpret_cast<uint4*>(dqkv + (t0 + tt) * N + qkw + hh * dvw + 8 * cc) = g;
+    }
+    __syncthreads();
   }
   amax = block_max_u32(amax << 16, red);
   if (threadIdx.x == 0) partials[blockIdx.x] = amax;
@@ -499,9 +555,6 @@ constexpr int kFwdTT = 16, kBwdTT = 8;
 
 static bool quad_width(int d) { return d == 64 || d == 96 || d == 128; }
 
-static unsigned quad_grid(int64_t units) {
-  return (unsigned)std::min<int64_t>(kQuadBlocks, std::max<int64_t>(1, ceil_div(units, kThreads)));
-}
 
 size_t norm_rope_fwd_lds(int H, int d) {
   const size_t items = (size_t)kFwdTT * 2 * H * (d / 16);
@@ -515,16 +568,17 @@ size_t norm_rope_bwd_lds(int H, int d) {
 
 void launch_norm_rope_fwd(const uint16_t* qk_pre, int64_t T, int seq_len, int H, int d, float eps,
                           float base, uint16_t* q, uint16_t* k, hipStream_t s) {
-  const unsigned grid = quad_grid(quad_units(T, 2 * H));
+  const unsigned grid =
+      (unsigned)std::min<int64_t>(kQuadTileBlocks, std::max<int64_t>(1, ceil_div(T, kQuadTT)));
   switch (d) {
     case 64:
-      norm_rope_fwd_quad<8><<<grid, kThreads, 0, s>>>(qk_pre, T, seq_len, H, eps, base, q, k);
+      norm_rope_fwd_qc<64><<<grid, kThreads, 0, s>>>(qk_pre, T, seq_len, H, eps, base, q, k);
       return;
     case 96:
-      norm_rope_fwd_quad<12><<<grid, kThreads, 0, s>>>(qk_pre, T, seq_len, H, eps, base, q, k);
+      norm_rope_fwd_qc<96><<<grid, kThreads, 0, s>>>(qk_pre, T, seq_len, H, eps, base, q, k);
       return;
     case 128:
-      norm_rope_fwd_quad<16><<<grid, kThreads, 0, s>>>(qk_pre, T, seq_len, H, eps, base, q, k);
+      norm_rope_fwd_qc<128><<<grid, kThreads, 0, s>>>(qk_pre, T, seq_len, H, eps, base, q, k);
       return;
     default:
       break;
@@ -535,7 +589,10 @@ void launch_norm_rope_fwd(const uint16_t* qk_pre, int64_t T, int seq_len, int H,
 }
 
 int norm_rope_bwd_blocks(int64_t T, int H, int d) {
-  return quad_width(d) ? (int)quad_grid(T * 2 * H * 4) : (int)ceil_div(T, kBwdTT);
+  (void)H;
+  return quad_width(d)
+             ? (int)std::min<int64_t>(kQuadTileBlocks, std::max<int64_t>(1, ceil_div(T, kQuadTT)))
+             : (int)ceil_div(T, kBwdTT);
 }
 
 void launch_norm_rope_bwd(const uint16_t* dq, const uint16_t* dk, const uint16_t* dv,
@@ -545,16 +602,16 @@ void launch_norm_rope_bwd(const uint16_t* dq, const uint16_t* dk, const uint16_t
   const unsigned grid = (unsigned)norm_rope_bwd_blocks(T, H, d);
   switch (d) {
     case 64:
-      norm_rope_bwd_quad<8><<<grid, kThreads, 0, s>>>(dq, dk, dv, qk_pre, T, seq_len, H, d_v, eps,
-                                                      base, dqkv, partials);
+      norm_rope_bwd_qc<64><<<grid, kThreads, 0, s>>>(dq, dk, dv, qk_pre, T, seq_len, H, d_v, eps,
+                                                        base, dqkv, partials);
       return;
     case 96:
-      norm_rope_bwd_quad<12><<<grid, kThreads, 0, s>>>(dq, dk, dv, qk_pre, T, seq_len, H, d_v,
-                                                       eps, base, dqkv, partials);
+      norm_rope_bwd_qc<96><<<grid, kThreads, 0, s>>>(dq, dk, dv, qk_pre, T, seq_len, H, d_v, eps,
+                                                        base, dqkv, partials);
       return;
     case 128:
-      norm_rope_bwd_quad<16><<<grid, kThreads, 0, s>>>(dq, dk, dv, qk_pre, T, seq_len, H, d_v,
-                                                       eps, base, dqkv, partials);
+      norm_rope_bwd_qc<128><<<grid, kThreads, 0, s>>>(dq, dk, dv, qk_pre, T, seq_len, H, d_v,
+                                                         eps, base, dqkv, partials);
       return;
     default:
       break;
