@@ -31,9 +31,8 @@ PEAK_FP8_FLOPS = 5.0e15   # MI355X dense FP8 MFMA
 PEAK_HBM_BYTES = 8.0e12   # MI355X HBM3E
 CALIB_FLOATS = 64 << 20   # counter calibration: encoder over 256 MiB of fp32
 STAGE_SOURCES = {
-    "amax_w": "quantize.hip", "finalize_w": "quantize.hip", "quantize_w": "quantize.hip",
-    "amax_x": "quantize.hip", "finalize_x": "quantize.hip", "quantize_x": "quantize.hip",
-    "finalize_g": "quantize.hip", "quantize_g": "quantize.hip",
+    "amax_w": "quantize.hip", "quantize_w": "quantize.hip",
+    "amax_x": "quantize.hip", "quantize_x": "quantize.hip", "quantize_g": "quantize.hip",
     "gemm_fwd": "gemm.hip", "gemm_dx": "gemm.hip", "gemm_dw": "gemm.hip",
     "dw_reduce": "gemm.hip", "norm_rope_fwd": "epilogue.hip", "norm_rope_bwd": "epilogue.hip",
 }
@@ -58,7 +57,6 @@ def stage_work(w: dict, dw_splits: int) -> dict:
         "gemm_dx": ("mfma", gemm),
         "gemm_dw": ("mfma", gemm),
         "dw_reduce": ("hbm", dw_splits * 4 * D * N + 4 * D * N),
-        "finalize_w": ("hbm", 0), "finalize_x": ("hbm", 0), "finalize_g": ("hbm", 0),
     }
 
 

@@ -215,13 +215,10 @@ int pack_quantize_weights(const fpr_dims* dims, const float* wq, int64_t ldq, co
   stage("amax_w", s, [&] {
     fpr::launch_amax_w(wq, ldq, wk, ldk, wv, ldv, p.D, p.nq, p.N, parts, kPartsW, s);
   });
-  stage("finalize_w", s, [&] {
-    fpr::launch_finalize_scales(parts, kPartsW, cache->scales, cache->status,
-                                FPR_STATUS_W_NONFINITE, true, s);
-  });
   stage("quantize_w", s, [&] {
-    fpr::launch_quantize_w(wq, ldq, wk, ldk, wv, ldv, p.D, p.nq, p.N, cache->scales,
-                           cache->w_packed, cache->w_packed_t, s);
+    fpr::launch_quantize_w(wq, ldq, wk, ldk, wv, ldv, p.D, p.nq, p.N, parts, kPartsW,
+                           cache->scales, cache->status, FPR_STATUS_W_NONFINITE, cache->w_packed,
+                           cache->w_packed_t, s);
   });
   return finish();
 }
@@ -247,11 +244,10 @@ int qkv_forward(const fpr_dims* dims, int32_t n_seq, int32_t seq_len, const uint
   uint8_t* x8t = at<uint8_t>(saved, p.s_x8t);
   uint16_t* qk = at<uint16_t>(saved, p.s_qk);
   stage("amax_x", s, [&] { fpr::launch_amax_bf16(x, T * p.D, parts, p.f_parts, s); });
-  stage("finalize_x", s, [&] {
-    fpr::launch_finalize_scales(parts, p.f_parts, xsc, cache->status, FPR_STATUS_X_NONFINITE,
-                                false, s);
+  stage("quantize_x", s, [&] {
+    fpr::launch_quantize_act(x, T, p.D, parts, p.f_parts, xsc, cache->status,
+                             FPR_STATUS_X_NONFINITE, x8, x8t, p.Tp, s);
   });
-  stage("quantize_x", s, [&] { fpr::launch_quantize_act(x, T, p.D, xsc, x8, x8t, p.Tp, s); });
   stage("gemm_fwd", s, [&] {
     fpr::launch_gemm_fwd(x8, cache->w_packed_t, (int)T, p.N, p.D, xsc, cache->scales, qk,
                          p.nqk2, v, p.H, p.dv, seq_len, s);
@@ -294,11 +290,10 @@ int qkv_backward(const fpr_dims* dims, int32_t n_seq, int32_t seq_len, const uin
     fpr::launch_norm_rope_bwd(dq, dk, dv, qk, T, seq_len, p.H, p.dqk, p.dv, dims->eps,
                               dims->rope_base, dqkv, parts, s);
   });
-  stage("finalize_g", s, [&] {
-    fpr::launch_finalize_scales(parts, p.b_parts, gsc, cache->status, FPR_STATUS_G_NONFINITE,
-                                false, s);
+  stage("quantize_g", s, [&] {
+    fpr::launch_quantize_act(dqkv, T, p.N, parts, p.b_parts, gsc, cache->status,
+                             FPR_STATUS_G_NONFINITE, g8, g8t, p.Tp, s);
   });
-  stage("quantize_g", s, [&] { fpr::launch_quantize_act(dqkv, T, p.N, gsc, g8, g8t, p.Tp, s); });
   stage("gemm_dx", s, [&] {
     fpr::launch_gemm_dx(g8, cache->w_packed, (int)T, p.D, p.N, gsc, cache->scales, dx, s);
   });

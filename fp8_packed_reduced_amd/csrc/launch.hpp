@@ -27,16 +27,16 @@ void launch_amax_w(const float* wq, int64_t ldq, const float* wk, int64_t ldk,
 void launch_amax_bf16(const uint16_t* x, int64_t n, uint32_t* partials, int parts,
                       hipStream_t s);
 
-// Reduce `parts` partials into scales[0] = s, scales[1] = inv.  A non-finite
-// amax sets `status_bit` in *status (overwriting *status when `reset`).
-void launch_finalize_scales(const uint32_t* partials, int parts, float* scales,
-                            int32_t* status, int status_bit, bool reset, hipStream_t s);
+// The quantisers below take the `parts` amax partials of their tensor and
+// reduce them to the scales (scales[0] = s, scales[1] = inv, which they also
+// write); a non-finite amax sets `status_bit` in *status (the weight
+// quantiser overwrites *status, the activation one ORs into it).
 
 // Quantise W_packed and write both layouts: w_packed [D][N], w_packed_t [N][D].
 void launch_quantize_w(const float* wq, int64_t ldq, const float* wk, int64_t ldk,
                        const float* wv, int64_t ldv, int D, int nq, int N,
-                       const float* scales, uint8_t* w_packed, uint8_t* w_packed_t,
-                       hipStream_t s);
+                       const uint32_t* partials, int parts, float* scales, int32_t* status,
+                       int status_bit, uint8_t* w_packed, uint8_t* w_packed_t, hipStream_t s);
 
 // Blocked layouts of the FP8 activation copies, which only the GEMMs read.
 // A matrix of R rows and K columns (K contiguous) is stored as blocks of
@@ -54,14 +54,16 @@ inline size_t t_blocked_bytes(int64_t cols, int64_t tokens_padded) {
   return (size_t)round_up(cols, kTRows) * (size_t)tokens_padded;
 }
 
-// Quantise a [rows][cols] bf16 matrix with the per-tensor scale in `scales`
-// into dst (row layout, rows x cols; columns cols .. multiple of kKBlock
-// written as zero) and dst_t (transposed layout, cols x tokens_padded;
-// tokens rows .. tokens_padded written as zero).  cols % 16 == 0,
-// tokens_padded % kKBlock == 0.  Rows past `rows` (resp. `cols`) inside
-// the last block of rows are left unwritten: the GEMMs never read them.
-void launch_quantize_act(const uint16_t* src, int64_t rows, int cols, const float* scales,
-                         uint8_t* dst, uint8_t* dst_t, int64_t tokens_padded, hipStream_t s);
+// Quantise a [rows][cols] bf16 matrix with its per-tensor scale (from the
+// partials, as above) into dst (row layout, rows x cols; columns cols ..
+// multiple of kKBlock written as zero) and dst_t (transposed layout, cols x
+// tokens_padded; tokens rows .. tokens_padded written as zero).  cols % 16
+// == 0, tokens_padded % kKBlock == 0.  Rows past `rows` (resp. `cols`)
+// inside the last block of rows are left unwritten: the GEMMs never read
+// them.
+void launch_quantize_act(const uint16_t* src, int64_t rows, int cols, const uint32_t* partials,
+                         int parts, float* scales, int32_t* status, int status_bit, uint8_t* dst,
+                         uint8_t* dst_t, int64_t tokens_padded, hipStream_t s);
 
 void launch_encode(const float* in, int64_t n, float inv, uint8_t* out, hipStream_t s);
 

@@ -4,10 +4,12 @@
 // GEMM streams, both from one read).
 //
 // The scale needs the whole tensor's amax before any code can be written,
-// so each quantiser is: per-block partial amax -> one-block finalize ->
-// quantize.  Partials are fp32 bit patterns of |v| held as uint32: for
-// non-negative floats the integer order is the float order, and any NaN or
-// Inf pattern compares above every finite value.
+// so each quantiser is two kernels: per-block partial amax, then quantize,
+// whose every block first reduces the (few KB of, L2-resident) partials to
+// the scales itself; its first block also publishes them.  Partials are
+// fp32 bit patterns of |v| held as uint32: for non-negative floats the
+// integer order is the float order, and any NaN or Inf pattern compares
+// above every finite value.
 #include "common.hpp"
 #include "launch.hpp"
 
@@ -72,34 +74,40 @@ __global__ __launch_bounds__(kThreads) void amax_bf16_kernel(const uint16_t* __r
   if (threadIdx.x == 0) partials[blockIdx.x] = m;
 }
 
-// ------------------------------------------------------------- finalize
+// ---------------------------------------------------------------- scales
 
-__global__ __launch_bounds__(kThreads) void finalize_scales_kernel(
-    const uint32_t* __restrict__ partials, int parts, float* __restrict__ scales,
-    int32_t* __restrict__ status, int status_bit, int reset) {
-  __shared__ uint32_t red[4];
+// The per-tensor scales from the amax partials (block-wide; every thread
+// gets them): s = fl(amax / 448), inv = fl(448 / amax) with IEEE-correct
+// fp32 divisions; (1, 1) for amax = 0, an inverse that overflows, or a
+// non-finite amax.  The block that `publishes` writes scales[0..1] and, for
+// a non-finite amax, sets `status_bit` in *status (overwriting *status
+// when `reset`).
+__device__ inline float2 tensor_scales(const uint32_t* __restrict__ partials, int parts,
+                                       uint32_t* red, bool publish, float* __restrict__ scales,
+                                       int32_t* __restrict__ status, int status_bit, bool reset) {
   uint32_t m = 0;
 #pragma unroll 8
   for (int i = threadIdx.x; i < parts; i += kThreads) m = m > partials[i] ? m : partials[i];
   m = block_max_u32(m, red);
-  if (threadIdx.x == 0) {
-    float s = 1.0f, inv = 1.0f;
-    const bool finite = m < 0x7f800000u;
-    if (finite) {
-      const float amax = __uint_as_float(m);
-      const float i = 448.0f / amax;          // IEEE-correct fp32 division
-      if (amax != 0.0f && i <= 3.40282347e38f) {
-        s = amax / 448.0f;
-        inv = i;
-      }
+  float sc = 1.0f, inv = 1.0f;
+  const bool finite = m < 0x7f800000u;
+  if (finite) {
+    const float amax = __uint_as_float(m);
+    const float i = 448.0f / amax;
+    if (amax != 0.0f && i <= 3.40282347e38f) {
+      sc = amax / 448.0f;
+      inv = i;
     }
-    scales[0] = s;
+  }
+  if (publish && threadIdx.x == 0) {
+    scales[0] = sc;
     scales[1] = inv;
     if (reset)
       *status = finite ? 0 : status_bit;
     else if (!finite)
       atomicOr(status, status_bit);
   }
+  return make_float2(sc, inv);
 }
 
 // ----------------------------------------------- W_packed, both layouts
@@ -110,11 +118,14 @@ __global__ __launch_bounds__(kThreads) void finalize_scales_kernel(
 __global__ __launch_bounds__(kThreads) void quantize_w_kernel(
     const float* __restrict__ wq, int64_t ldq, const float* __restrict__ wk, int64_t ldk,
     const float* __restrict__ wv, int64_t ldv, int D, int nq, int N,
-    const float* __restrict__ scales, uint8_t* __restrict__ w_packed,
+    const uint32_t* __restrict__ partials, int parts, float* __restrict__ scales,
+    int32_t* __restrict__ status, int status_bit, uint8_t* __restrict__ w_packed,
     uint8_t* __restrict__ w_packed_t) {
   __shared__ uint8_t tile_t[64][64 + 4];
+  __shared__ uint32_t red[4];
   const int n0 = blockIdx.x * 64, d0 = blockIdx.y * 64;
-  const float inv = scales[1];
+  const float inv = tensor_scales(partials, parts, red, blockIdx.x == 0 && blockIdx.y == 0,
+                                  scales, status, status_bit, true).y;
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     const int idx = threadIdx.x + kThreads * i;
@@ -157,21 +168,31 @@ __global__ __launch_bounds__(kThreads) void quantize_w_kernel(
 // into an LDS tile from which the transposed layout's 128-byte token runs
 // are written as 16-byte chunks.
 __global__ __launch_bounds__(kThreads) void quantize_act_kernel(
-    const uint16_t* __restrict__ src, int64_t rows, int cols, const float* __restrict__ scales,
-    uint8_t* __restrict__ dst, uint8_t* __restrict__ dst_t, int64_t tokens_padded) {
+    const uint16_t* __restrict__ src, int64_t rows, int cols,
+    const uint32_t* __restrict__ partials, int parts, float* __restrict__ scales,
+    int32_t* __restrict__ status, int status_bit, uint8_t* __restrict__ dst,
+    uint8_t* __restrict__ dst_t, int64_t tokens_padded) {
   __shared__ uint32_t tile_t[kKBlock][kKBlock / 4 + 1];  // [column][token / 4]
+  __shared__ uint32_t red[4];
   const int64_t t0 = (int64_t)blockIdx.x * kKBlock;        // first token
   const int kb = blockIdx.y, c0 = kb * kKBlock;            // K block of the row layout
   const int cc = threadIdx.x & 15, rg = threadIdx.x >> 4;
-  const float inv = scales[1];
   const int kblocks = (int)ceil_div(cols, kKBlock);
   const int c = c0 + 8 * cc;
+  uint4 in[8];  // the tile's loads go out before the scale reduction
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const int64_t t = t0 + 8 * rg + i;
+    in[i] = make_uint4(0, 0, 0, 0);
+    if (t < rows && c < cols) in[i] = *reinterpret_cast<const uint4*>(src + t * cols + c);
+  }
+  const float inv = tensor_scales(partials, parts, red, blockIdx.x == 0 && blockIdx.y == 0,
+                                  scales, status, status_bit, false).y;
   uint32_t codes[8][2];
 #pragma unroll
   for (int i = 0; i < 8; ++i) {
     const int64_t t = t0 + 8 * rg + i;
-    uint4 v = make_uint4(0, 0, 0, 0);
-    if (t < rows && c < cols) v = *reinterpret_cast<const uint4*>(src + t * cols + c);
+    const uint4 v = in[i];
     codes[i][0] = e4m3x4(bf16_to_f32(v.x & 0xffffu) * inv, bf16_to_f32(v.x >> 16) * inv,
                          bf16_to_f32(v.y & 0xffffu) * inv, bf16_to_f32(v.y >> 16) * inv);
     codes[i][1] = e4m3x4(bf16_to_f32(v.z & 0xffffu) * inv, bf16_to_f32(v.z >> 16) * inv,
@@ -238,25 +259,22 @@ void launch_amax_bf16(const uint16_t* x, int64_t n, uint32_t* partials, int part
   amax_bf16_kernel<<<parts, kThreads, 0, s>>>(x, n, partials);
 }
 
-void launch_finalize_scales(const uint32_t* partials, int parts, float* scales, int32_t* status,
-                            int status_bit, bool reset, hipStream_t s) {
-  finalize_scales_kernel<<<1, kThreads, 0, s>>>(partials, parts, scales, status, status_bit,
-                                                reset ? 1 : 0);
-}
-
 void launch_quantize_w(const float* wq, int64_t ldq, const float* wk, int64_t ldk,
-                       const float* wv, int64_t ldv, int D, int nq, int N, const float* scales,
-                       uint8_t* w_packed, uint8_t* w_packed_t, hipStream_t s) {
+                       const float* wv, int64_t ldv, int D, int nq, int N,
+                       const uint32_t* partials, int parts, float* scales, int32_t* status,
+                       int status_bit, uint8_t* w_packed, uint8_t* w_packed_t, hipStream_t s) {
   dim3 grid((unsigned)ceil_div(N, 64), (unsigned)ceil_div(D, 64));
-  quantize_w_kernel<<<grid, kThreads, 0, s>>>(wq, ldq, wk, ldk, wv, ldv, D, nq, N, scales,
-                                              w_packed, w_packed_t);
+  quantize_w_kernel<<<grid, kThreads, 0, s>>>(wq, ldq, wk, ldk, wv, ldv, D, nq, N, partials,
+                                              parts, scales, status, status_bit, w_packed,
+                                              w_packed_t);
 }
 
-void launch_quantize_act(const uint16_t* src, int64_t rows, int cols, const float* scales,
-                         uint8_t* dst, uint8_t* dst_t, int64_t tokens_padded, hipStream_t s) {
+void launch_quantize_act(const uint16_t* src, int64_t rows, int cols, const uint32_t* partials,
+                         int parts, float* scales, int32_t* status, int status_bit, uint8_t* dst,
+                         uint8_t* dst_t, int64_t tokens_padded, hipStream_t s) {
   dim3 grid((unsigned)(tokens_padded / kKBlock), (unsigned)ceil_div(cols, kKBlock));
-  quantize_act_kernel<<<grid, kThreads, 0, s>>>(src, rows, cols, scales, dst, dst_t,
-                                                tokens_padded);
+  quantize_act_kernel<<<grid, kThreads, 0, s>>>(src, rows, cols, partials, parts, scales, status,
+                                                status_bit, dst, dst_t, tokens_padded);
 }
 
 void launch_encode(const float* in, int64_t n, float inv, uint8_t* out, hipStream_t s) {

@@ -20,17 +20,15 @@ import csv
 import statistics
 import sys
 
-STEP_ORDER = ["amax_w", "finalize_w", "quantize_w", "amax_x", "finalize_x", "quantize_x",
-              "gemm_fwd", "norm_rope_fwd", "norm_rope_bwd", "finalize_g", "quantize_g",
-              "gemm_dx", "gemm_dw", "dw_reduce"]
+STEP_ORDER = ["amax_w", "quantize_w", "amax_x", "quantize_x", "gemm_fwd", "norm_rope_fwd",
+              "norm_rope_bwd", "quantize_g", "gemm_dx", "gemm_dw", "dw_reduce"]
 KERNEL_OF_STAGE = {
-    "amax_w": "amax_w_kernel", "finalize_w": "finalize_scales_kernel",
-    "quantize_w": "quantize_w_kernel", "amax_x": "amax_bf16_kernel",
-    "finalize_x": "finalize_scales_kernel", "quantize_x": "quantize_rows_kernel",
+    "amax_w": "amax_w_kernel", "quantize_w": "quantize_w_kernel",
+    "amax_x": "amax_bf16_kernel", "quantize_x": "quantize_act_kernel",
     "gemm_fwd": "gemm_bf16out_kernel", "norm_rope_fwd": "norm_rope_fwd",
-    "norm_rope_bwd": "norm_rope_bwd", "finalize_g": "finalize_scales_kernel",
-    "quantize_g": "quantize_rows_kernel", "gemm_dx": "gemm_bf16out_kernel",
-    "gemm_dw": "gemm_dw_part_kernel", "dw_reduce": "dw_reduce_kernel",
+    "norm_rope_bwd": "norm_rope_bwd", "quantize_g": "quantize_act_kernel",
+    "gemm_dx": "gemm_bf16out_kernel", "gemm_dw": "gemm_dw_part_kernel",
+    "dw_reduce": "dw_reduce_kernel",
 }
 CALIB_KERNEL = "encode_kernel"
 

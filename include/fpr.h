@@ -203,9 +203,8 @@ FPR_API int fpr_get_layout(const fpr_dims* dims, int64_t tokens, fpr_layout* out
  * hipEventRecord(events[2i+1]) on the call's stream, and its stage name is
  * stored in names[i], for i = count, count+1, ... while count < capacity
  * (and count < FPR_TRACE_MAX).  events are caller-created hipEvent_t handles.
- * Stage names: amax_w, finalize_w, quantize_w, amax_x, finalize_x,
- * quantize_x, gemm_fwd, norm_rope_fwd, norm_rope_bwd, finalize_g, quantize_g,
- * gemm_dx, gemm_dw, dw_reduce.  fpr_trace_set(NULL) stops tracing.  This is
+ * Stage names: amax_w, quantize_w, amax_x, quantize_x, gemm_fwd,
+ * norm_rope_fwd, norm_rope_bwd, quantize_g, gemm_dx, gemm_dw, dw_reduce.  fpr_trace_set(NULL) stops tracing.  This is
  * the only per-thread state the library keeps. */
 #define FPR_TRACE_MAX 4096
 typedef struct fpr_trace {
