@@ -407,8 +407,8 @@ __device__ __forceinline__ void store_bf16_tile(const v16f (&acc)[C::FM][C::FN],
       for (int g = 0; g < 4; ++g) {
         const v16f& a = acc[i][j];
         *reinterpret_cast<uint2*>(slice + W::at(lane & 31, 4 * j + g) + 8 * (lane >> 5)) =
-            make_uint2(pack_bf16x2(a[4 * g] * alpha, a[4 * g + 1] * alpha),
-                       pack_bf16x2(a[4 * g + 2] * alpha, a[4 * g + 3] * alpha));
+            make_uint2(cvt_bf16x2_rn(a[4 * g] * alpha, a[4 * g + 1] * alpha),
+                       cvt_bf16x2_rn(a[4 * g + 2] * alpha, a[4 * g + 3] * alpha));
       }
     uint4 val[4];
 #pragma unroll
