@@ -17,7 +17,7 @@ using fpr::round_up;
 
 constexpr size_t kAlign = 256;
 constexpr int kPartsW = 256;     // amax blocks for W_packed
-constexpr int kPartsAct = 1024;  // amax blocks for x
+constexpr int kPartsAct = 256;   // amax blocks for x
 using fpr::kMaxTokens;
 constexpr size_t kMaxDynLds = 64 * 1024;  // dynamic LDS of one epilogue block
 
@@ -84,7 +84,7 @@ Plan make_plan(const fpr_dims* d, int64_t T) {
   p.b_parts = fpr::norm_rope_bwd_blocks(T > 0 ? T : 1, p.H, p.dqk);
   p.b_part = take(c, (size_t)p.b_parts * 4);
   p.b_gsc = take(c, 4 * sizeof(float));
-  p.b_dqkv = take(c, (size_t)T * p.N * 2);
+  p.b_dqkv = take(c, (size_t)T * p.nqk2 * 2);
   p.b_g8 = take(c, fpr::act_blocked_bytes(T, p.N));
   p.b_g8t = take(c, fpr::t_blocked_bytes(p.N, p.Tp));
   p.b_dwpart = take(c, fpr::dw_partial_bytes(p.D, p.N, p.Tp));
@@ -291,8 +291,9 @@ int qkv_backward(const fpr_dims* dims, int32_t n_seq, int32_t seq_len, const uin
                               dims->rope_base, dqkv, parts, s);
   });
   stage("quantize_g", s, [&] {
-    fpr::launch_quantize_act(dqkv, T, p.N, parts, p.b_parts, gsc, cache->status,
-                             FPR_STATUS_G_NONFINITE, g8, g8t, p.Tp, s);
+    fpr::launch_quantize_act_split(dqkv, p.nqk2, dv, p.dv, p.H, seq_len, T, p.N, parts,
+                                   p.b_parts, gsc, cache->status, FPR_STATUS_G_NONFINITE, g8,
+                                   g8t, p.Tp, s);
   });
   stage("gemm_dx", s, [&] {
     fpr::launch_gemm_dx(g8, cache->w_packed, (int)T, p.D, p.N, gsc, cache->scales, dx, s);

@@ -7,9 +7,10 @@
 // p * base^(-2i/d) -> head-major q, k.
 //
 // Backward ("Where the eight seconds were hiding", "The inventory": the norm,
-// RoPE and backward shuffles): du = R_{-p} dq; da = rho * (du - u <u,du>/d);
-// the V gradient is re-laid out; everything is packed into dQKV [T][N] bf16
-// with one amax partial per block for the gradient quantiser.
+// RoPE and backward shuffles): du = R_{-p} dq; da = rho * (du - u <u,du>/d)
+// into the Q|K part of the packed gradient, dQK [T][2H d] bf16, with one
+// amax partial per block over dQK and dv together for the gradient
+// quantiser, which reads the V columns straight from dv.
 //
 // Main kernels (d = 64, 96, 128): four consecutive lanes own one head row
 // and every access is a whole 16-byte chunk (below); the row sums take two
@@ -111,7 +112,7 @@ __device__ inline float quad_sum(float v) {
 // cos/sin table of their positions (shared by all heads) in LDS.
 
 constexpr int kQuadTT = 16;         // tokens per block iteration
-constexpr int kQuadTileBlocks = 2048;
+constexpr int kQuadTileBlocks = 1024;
 
 template <int D>
 struct QuadChunks {
@@ -289,7 +290,8 @@ __device__ __forceinline__ void qc_bwd_load(QcBwdRow<D>& r, int row, int rows, i
   }
 }
 
-// Finishes the row into dQKV and returns the largest |bf16| bit pattern.
+// Finishes the row into dQK (rows of N elements) and returns the largest
+// |bf16| bit pattern.
 template <int D>
 __device__ __forceinline__ uint32_t qc_bwd_finish(const QcBwdRow<D>& r, const float2* cs,
                                                   int64_t t0, int N, float eps,
@@ -353,7 +355,7 @@ __global__ __launch_bounds__(kThreads) void norm_rope_bwd_qc(
   __shared__ int sp[kQuadTT];
   __shared__ uint32_t red[4];
   build_rev_table(rev, h, D, base);
-  const int R = 2 * H, qkw = R * D, N = qkw + H * dvw, CV = dvw / 8, l = threadIdx.x & 3;
+  const int R = 2 * H, qkw = R * D, CV = dvw / 8, l = threadIdx.x & 3;
   uint32_t amax = 0;
   const int64_t groups = ceil_div(T, kQuadTT);
   for (int64_t gi = blockIdx.x; gi < groups; gi += gridDim.x) {
@@ -365,16 +367,14 @@ __global__ __launch_bounds__(kThreads) void norm_rope_bwd_qc(
       QcBwdRow<D> r0, r1;  // two rows' loads in flight per thread
       qc_bwd_load<D>(r0, row, rows, R, H, seq_len, t0, bq, sp, dq, dk, qk_pre, l);
       qc_bwd_load<D>(r1, row + QUADS, rows, R, H, seq_len, t0, bq, sp, dq, dk, qk_pre, l);
-      amax = max(amax, qc_bwd_finish<D>(r0, cs, t0, N, eps, dqkv, l));
-      amax = max(amax, qc_bwd_finish<D>(r1, cs, t0, N, eps, dqkv, l));
+      amax = max(amax, qc_bwd_finish<D>(r0, cs, t0, qkw, eps, dqkv, l));
+      amax = max(amax, qc_bwd_finish<D>(r1, cs, t0, qkw, eps, dqkv, l));
     }
-    // V gradient: head hh, tokens consecutive (contiguous reads)
+    // amax of the V gradient: head hh, tokens consecutive (contiguous reads)
     for (int i = threadIdx.x; i < nt * H * CV; i += kThreads) {
       const int cc = i % CV, rest = i / CV, tt = rest % nt, hh = rest / nt;
-      const uint4 g = *reinterpret_cast<const uint4*>(
-          dv + ((bq[tt] * H + hh) * seq_len + sp[tt]) * dvw + 8 * cc);
-      amax = max(amax, absmax8(g));
-      *reinterpret_cast<uint4*>(dqkv + (t0 + tt) * N + qkw + hh * dvw + 8 * cc) = g;
+      amax = max(amax, absmax8(*reinterpret_cast<const uint4*>(
+                           dv + ((bq[tt] * H + hh) * seq_len + sp[tt]) * dvw + 8 * cc)));
     }
     __syncthreads();
   }
@@ -454,7 +454,7 @@ __global__ __launch_bounds__(kThreads) void norm_rope_bwd_kernel(
     uint32_t* __restrict__ partials) {
   extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
   __shared__ uint32_t red[4];
-  const int h = d / 2, C = h / 8, R = 2 * H, qkw = R * d, N = qkw + H * dvw;
+  const int h = d / 2, C = h / 8, R = 2 * H, qkw = R * d;
   const int items = TT * R * C;
   uint4* data = reinterpret_cast<uint4*>(smem);                  // [items][4]: a lo/hi, g lo/hi
   float* part = reinterpret_cast<float*>(data + 4 * items);      // [items][2]: sum a^2, sum a.du
@@ -530,20 +530,19 @@ __global__ __launch_bounds__(kThreads) void norm_rope_bwd_kernel(
     }
     const uint4 plo = pack8(oa), phi = pack8(ob);
     amax = max(amax, max(absmax8(plo), absmax8(phi)));
-    uint16_t* dst = dqkv + t * N + rr * d;
+    uint16_t* dst = dqkv + t * qkw + rr * d;
     *reinterpret_cast<uint4*>(dst + 8 * c) = plo;
     *reinterpret_cast<uint4*>(dst + h + 8 * c) = phi;
   }
-  // V gradient: re-lay out head-major dv into the packed rows
+  // amax of the V gradient
   const int cv = dvw / 8, vitems = TT * H * cv;
   for (int it = threadIdx.x; it < vitems; it += kThreads) {
     const int c = it % cv, hh = (it / cv) % H, tt = it / (cv * H);
     const int64_t t = t0 + tt;
     if (t >= T) continue;
     const int64_t bseq = t / seq_len, s = t - bseq * seq_len;
-    const uint4 g = *reinterpret_cast<const uint4*>(dv + ((bseq * H + hh) * seq_len + s) * dvw + 8 * c);
-    amax = max(amax, absmax8(g));
-    *reinterpret_cast<uint4*>(dqkv + t * N + qkw + hh * dvw + 8 * c) = g;
+    amax = max(amax, absmax8(*reinterpret_cast<const uint4*>(
+                         dv + ((bseq * H + hh) * seq_len + s) * dvw + 8 * c)));
   }
   amax = block_max_u32(amax << 16, red);
   if (threadIdx.x == 0) partials[blockIdx.x] = amax;

@@ -65,6 +65,15 @@ void launch_quantize_act(const uint16_t* src, int64_t rows, int cols, const uint
                          int parts, float* scales, int32_t* status, int status_bit, uint8_t* dst,
                          uint8_t* dst_t, int64_t tokens_padded, hipStream_t s);
 
+// The same for rows whose first `split` columns come from src [rows][split]
+// and the rest from head-major rows: column split + h * vw + j of token t is
+// element j of row (t / vs * vh + h) * vs + t % vs of vsrc (the packed
+// gradient: dQK, then dv [n_seq][H][S][d_v]).  split % 16 == 0, vw % 16 == 0.
+void launch_quantize_act_split(const uint16_t* src, int split, const uint16_t* vsrc, int vw,
+                               int vh, int vs, int64_t rows, int cols, const uint32_t* partials,
+                               int parts, float* scales, int32_t* status, int status_bit,
+                               uint8_t* dst, uint8_t* dst_t, int64_t tokens_padded, hipStream_t s);
+
 void launch_encode(const float* in, int64_t n, float inv, uint8_t* out, hipStream_t s);
 
 // ---- gemm.hip --------------------------------------------------------------
@@ -105,9 +114,9 @@ size_t norm_rope_bwd_lds(int H, int d_qk);
 void launch_norm_rope_fwd(const uint16_t* qk_pre, int64_t T, int seq_len, int H, int d_qk,
                           float eps, float base, uint16_t* q, uint16_t* k, hipStream_t s);
 
-// Backward epilogue: dq, dk, dv (head-major) + qk_pre -> packed dQKV [T][N]
-// bf16, plus one amax partial per block; norm_rope_bwd_blocks() is that
-// block count.
+// Backward epilogue: dq, dk (head-major) + qk_pre -> the Q|K part of the
+// packed gradient, dQK [T][2 H d_qk] bf16, plus one amax partial per block
+// over dQK and dv; norm_rope_bwd_blocks() is that block count.
 int norm_rope_bwd_blocks(int64_t T, int H, int d_qk);
 void launch_norm_rope_bwd(const uint16_t* dq, const uint16_t* dk, const uint16_t* dv,
                           const uint16_t* qk_pre, int64_t T, int seq_len, int H, int d_qk,

@@ -52,24 +52,32 @@ __global__ __launch_bounds__(kThreads) void amax_w_kernel(
 
 // --------------------------------------------------------- amax of bf16
 
+__device__ inline uint32_t absmax_bits8(uint4 v) {
+  const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+  uint32_t m = 0;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const uint32_t lo = w[j] & 0x7fffu, hi = (w[j] >> 16) & 0x7fffu;
+    const uint32_t a = lo > hi ? lo : hi;
+    m = m > a ? m : a;
+  }
+  return m;
+}
+
+// Four independent 16-byte loads in flight per thread.
 __global__ __launch_bounds__(kThreads) void amax_bf16_kernel(const uint16_t* __restrict__ x,
                                                              int64_t n,
                                                              uint32_t* __restrict__ partials) {
   __shared__ uint32_t red[4];
-  const int64_t vecs = n / 8;
+  const int64_t vecs = n / 8, stride = (int64_t)gridDim.x * kThreads;
+  const uint4* v = reinterpret_cast<const uint4*>(x);
   uint32_t m = 0;
-#pragma unroll 4
-  for (int64_t i = blockIdx.x * (int64_t)kThreads + threadIdx.x; i < vecs;
-       i += (int64_t)gridDim.x * kThreads) {
-    uint4 v = reinterpret_cast<const uint4*>(x)[i];
-    uint32_t w[4] = {v.x, v.y, v.z, v.w};
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      uint32_t lo = w[j] & 0x7fffu, hi = (w[j] >> 16) & 0x7fffu;
-      uint32_t a = lo > hi ? lo : hi;
-      m = m > a ? m : a;
-    }
+  int64_t i = blockIdx.x * (int64_t)kThreads + threadIdx.x;
+  for (; i + 3 * stride < vecs; i += 4 * stride) {
+    const uint4 a = v[i], b = v[i + stride], c = v[i + 2 * stride], d = v[i + 3 * stride];
+    m = max(m, max(max(absmax_bits8(a), absmax_bits8(b)), max(absmax_bits8(c), absmax_bits8(d))));
   }
+  for (; i < vecs; i += stride) m = max(m, absmax_bits8(v[i]));
   m = block_max_u32(m << 16, red);
   if (threadIdx.x == 0) partials[blockIdx.x] = m;
 }
@@ -161,17 +169,27 @@ __global__ __launch_bounds__(kThreads) void quantize_w_kernel(
 // ------------------------------ bf16 rows -> e4m3, two blocked layouts
 
 // One block per 128 tokens x 128 columns (one K block of the row layout,
-// and one K block of the transposed layout).  Thread (rg, cc) owns tokens
-// 8rg..8rg+7 and columns 8cc..8cc+7: it reads 8 x 16 bytes of bf16 and
+// and one K block of the transposed layout).  The source rows are the
+// tokens' first `split` columns, `split` elements apart, followed by the
+// columns of V-like head-major rows: column split + h * vw + j of token t
+// is element j of row (t / vs * vh + h) * vs + t % vs of `vsrc` (vw
+// elements per row, vh heads, sequences of vs tokens).  Thread (rg, cc)
+// owns tokens 8rg..8rg+7 and columns 8cc..8cc+7: it reads 8 x 16 bytes of bf16 and
 // writes 8 x 8 bytes of codes into the row layout (16 threads cover a
 // block row's 128 bytes), and its 8 x 8 codes go, four tokens to a dword,
 // into an LDS tile from which the transposed layout's 128-byte token runs
 // are written as 16-byte chunks.
+struct ActSrc {
+  const uint16_t* src;   // [rows][split]
+  int split;
+  const uint16_t* vsrc;  // head-major rows of the remaining columns
+  int vw, vh, vs;
+};
+
 __global__ __launch_bounds__(kThreads) void quantize_act_kernel(
-    const uint16_t* __restrict__ src, int64_t rows, int cols,
-    const uint32_t* __restrict__ partials, int parts, float* __restrict__ scales,
-    int32_t* __restrict__ status, int status_bit, uint8_t* __restrict__ dst,
-    uint8_t* __restrict__ dst_t, int64_t tokens_padded) {
+    ActSrc as, int64_t rows, int cols, const uint32_t* __restrict__ partials, int parts,
+    float* __restrict__ scales, int32_t* __restrict__ status, int status_bit,
+    uint8_t* __restrict__ dst, uint8_t* __restrict__ dst_t, int64_t tokens_padded) {
   __shared__ uint32_t tile_t[kKBlock][kKBlock / 4 + 1];  // [column][token / 4]
   __shared__ uint32_t red[4];
   const int64_t t0 = (int64_t)blockIdx.x * kKBlock;        // first token
@@ -180,11 +198,23 @@ __global__ __launch_bounds__(kThreads) void quantize_act_kernel(
   const int kblocks = (int)ceil_div(cols, kKBlock);
   const int c = c0 + 8 * cc;
   uint4 in[8];  // the tile's loads go out before the scale reduction
+  const bool head_major = c >= as.split;
+  const int hv = head_major ? (c - as.split) / as.vw : 0;
+  const int jv = head_major ? c - as.split - hv * as.vw : 0;
 #pragma unroll
   for (int i = 0; i < 8; ++i) {
     const int64_t t = t0 + 8 * rg + i;
     in[i] = make_uint4(0, 0, 0, 0);
-    if (t < rows && c < cols) in[i] = *reinterpret_cast<const uint4*>(src + t * cols + c);
+    if (t < rows && c < cols) {
+      const uint16_t* p;
+      if (head_major) {  // tokens < 2^24: 32-bit division
+        const int b = (int)t / as.vs;
+        p = as.vsrc + (((int64_t)b * as.vh + hv) * as.vs + ((int)t - b * as.vs)) * as.vw + jv;
+      } else {
+        p = as.src + t * as.split + c;
+      }
+      in[i] = *reinterpret_cast<const uint4*>(p);
+    }
   }
   const float inv = tensor_scales(partials, parts, red, blockIdx.x == 0 && blockIdx.y == 0,
                                   scales, status, status_bit, false).y;
@@ -272,9 +302,18 @@ void launch_quantize_w(const float* wq, int64_t ldq, const float* wk, int64_t ld
 void launch_quantize_act(const uint16_t* src, int64_t rows, int cols, const uint32_t* partials,
                          int parts, float* scales, int32_t* status, int status_bit, uint8_t* dst,
                          uint8_t* dst_t, int64_t tokens_padded, hipStream_t s) {
+  launch_quantize_act_split(src, cols, nullptr, 1, 1, 1, rows, cols, partials, parts, scales,
+                            status, status_bit, dst, dst_t, tokens_padded, s);
+}
+
+void launch_quantize_act_split(const uint16_t* src, int split, const uint16_t* vsrc, int vw,
+                               int vh, int vs, int64_t rows, int cols, const uint32_t* partials,
+                               int parts, float* scales, int32_t* status, int status_bit,
+                               uint8_t* dst, uint8_t* dst_t, int64_t tokens_padded, hipStream_t s) {
   dim3 grid((unsigned)(tokens_padded / kKBlock), (unsigned)ceil_div(cols, kKBlock));
-  quantize_act_kernel<<<grid, kThreads, 0, s>>>(src, rows, cols, partials, parts, scales, status,
-                                                status_bit, dst, dst_t, tokens_padded);
+  quantize_act_kernel<<<grid, kThreads, 0, s>>>(ActSrc{src, split, vsrc, vw, vh, vs}, rows, cols,
+                                                partials, parts, scales, status, status_bit, dst,
+                                                dst_t, tokens_padded);
 }
 
 void launch_encode(const float* in, int64_t n, float inv, uint8_t* out, hipStream_t s) {

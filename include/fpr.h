@@ -184,7 +184,8 @@ typedef struct fpr_layout {
     /* in the forward workspace */
     size_t fwd_x8;           /* [T][D] e4m3 row-blocked                     */
     /* in the backward workspace */
-    size_t bwd_dqkv;         /* [T][N] bf16 packed gradient                  */
+    size_t bwd_dqkv;         /* [T][2*H*d_qk] bf16, Q|K part of the packed
+                                gradient (its V part is dv itself)           */
     size_t bwd_g_scales;     /* [2] fp32: s_g, inv_g                         */
     size_t bwd_g8;           /* [T][N] e4m3 row-blocked                      */
     size_t bwd_g8t;          /* [N][tokens_padded] e4m3 transposed-blocked   */

@@ -97,7 +97,11 @@ def run(w: dict, seed: int = 42, x_bits=None, W=None, dy=None, backward: bool = 
         dx, dw = B.qkv_backward(dims, n_seq, S, dqd, dkd, dvd, saved, cache, workspace=ws_b)
         torch.cuda.synchronize()
         out["dy"] = dy
-        out["dqkv"] = dev_to_bits(B.view_bytes(ws_b, lay.bwd_dqkv, (T, N), torch.bfloat16))
+        # the packed gradient: its Q|K part from the workspace, its V part is
+        # dv itself (the gradient quantiser reads it head-major)
+        dqk = dev_to_bits(B.view_bytes(ws_b, lay.bwd_dqkv, (T, 2 * nq), torch.bfloat16))
+        dvt = np.ascontiguousarray(np.asarray(dy[2]).transpose(0, 2, 1, 3)).reshape(T, H * dv)
+        out["dqkv"] = np.concatenate([dqk, dvt], axis=1)
         out["g_scales"] = B.view_bytes(ws_b, lay.bwd_g_scales, (2,), torch.float32).cpu().numpy()
         g8 = unblock_rows(ws_b, lay.bwd_g8, T, N, lay)
         out["g8"], out["g8_kpad"] = g8[:T, :N], g8[:T, N:]

@@ -136,7 +136,9 @@ def _check_backward(w, r):
     g = r["dqkv"]
     e_dqk = row_rel_err(bf16_to_f64(g[:, :nqk2]).reshape(T, 2 * H, dqk),
                         ob["dqkv64"][:, :nqk2].reshape(T, 2 * H, dqk))
-    assert np.array_equal(g[:, nqk2:], ob["dqkv_bits"][:, nqk2:])  # dv relayout
+    # the packed V part is dv itself, which the gradient quantiser reads
+    # head-major: its codes below are what checks that read
+    assert np.array_equal(g[:, nqk2:], ob["dqkv_bits"][:, nqk2:])
     # a6: gradient quantiser, bit-exact on the GPU's own dQKV
     g8, s_g, inv_g, _ = oracle.quantize_bf16(g)
     assert np.array_equal(r["g8"], g8) and not r["g8_kpad"].any()
