@@ -52,7 +52,7 @@ def stage_work(w: dict, dw_splits: int) -> dict:
         "quantize_x": ("hbm", 2 * T * D + T * D),                # bf16 in, e4m3 out
         "gemm_fwd": ("mfma", gemm),
         "norm_rope_fwd": ("hbm", 2 * T * qk + 2 * T * qk),       # pre-norm Q|K in, q|k out
-        "norm_rope_bwd": ("hbm", 2 * T * qk * 2 + 2 * T * vv + 2 * T * N),  # dq,dk,pre, dv in; dQKV out
+        "norm_rope_bwd": ("hbm", 2 * T * qk * 2 + 2 * T * vv + 2 * T * qk),  # dq,dk,pre, dv in; dQK out
         "quantize_g": ("hbm", 2 * T * N + T * N),
         "gemm_dx": ("mfma", gemm),
         "gemm_dw": ("mfma", gemm),
