@@ -332,6 +332,15 @@ __device__ __forceinline__ void mma_role(const uint8_t* lds, const Sched& sc, in
 
 // ------------------------------------------------------------ epilogues
 
+// bf16 output chunks go out as streaming (non-temporal) stores: no wave of
+// the kernel reads them back, and they would otherwise push the operand
+// rows the other blocks are about to reuse out of L2.
+typedef unsigned v4u __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ void store_stream(uint16_t* p, uint4 v) {
+  const v4u x = {v.x, v.y, v.z, v.w};
+  __builtin_nontemporal_store(x, reinterpret_cast<v4u*>(p));
+}
+
 // bf16 tile store through the matrix wave's own LDS slice: 32 rows x WN
 // columns (WN * 2 bytes per row, 16-byte chunks XOR-swizzled by row).  Each
 // lane writes its 4-column groups, then reads back whole 16-byte chunks:
@@ -372,9 +381,9 @@ struct EpiFwd {
   __device__ void chunk(const Row& r, const Col& c, uint4 val) const {
     if (!c.live) return;
     if (c.qk)
-      *reinterpret_cast<uint4*>(qk_pre + (int64_t)r.m * nqk2 + c.n) = val;
+      store_stream(qk_pre + (int64_t)r.m * nqk2 + c.n, val);
     else
-      *reinterpret_cast<uint4*>(v + (int64_t)r.b * H * S * dv + (int64_t)r.s * dv + c.voff) = val;
+      store_stream(v + (int64_t)r.b * H * S * dv + (int64_t)r.s * dv + c.voff, val);
   }
 };
 
@@ -387,7 +396,7 @@ struct EpiDx {
   __device__ Row row(int m) const { return Row{m}; }
   __device__ void advance(Row& r, int step) const { r.m += step; }
   __device__ void chunk(const Row& r, const Col& c, uint4 val) const {
-    if (c.n < N) *reinterpret_cast<uint4*>(dx + (int64_t)r.m * N + c.n) = val;
+    if (c.n < N) store_stream(dx + (int64_t)r.m * N + c.n, val);
   }
 };
 
