@@ -38,6 +38,9 @@ STAGE_SOURCES = {
 }
 
 
+TRACE_STEPS = 10
+
+
 def stage_work(w: dict, dw_splits: int) -> dict:
     """Algorithmic work per launch: ("mfma", FLOP) or ("hbm", bytes)."""
     T = w["n_seq"] * w["seq_len"]
@@ -188,12 +191,15 @@ def main():
     for _ in range(max(args.warmup, 1)):
         step()
     torch.cuda.synchronize()
-    with B.KernelTrace(64, device=dev) as tr:
-        step()
+    # Per-stage times: the mean over TRACE_STEPS traced steps (one sample per
+    # stage and step; a single step is too noisy to rank the stages by).
+    with B.KernelTrace(16 * TRACE_STEPS, device=dev) as tr:
+        for _ in range(TRACE_STEPS):
+            step()
     torch.cuda.synchronize()
     per_stage = {}
     for name, ms in tr.records():
-        per_stage[name] = per_stage.get(name, 0.0) + ms
+        per_stage[name] = per_stage.get(name, 0.0) + ms / TRACE_STEPS
     dw_splits = B.layout(dims, T).dw_splits
     work = stage_work(w, dw_splits)
     dominant = max(per_stage, key=per_stage.get)

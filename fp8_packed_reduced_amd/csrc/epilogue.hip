@@ -269,10 +269,12 @@ struct QcBwdRow {
   bool ok;
 };
 
+// Token t (< 2^24, so 32-bit) of the packed rows is position t % seq_len of
+// sequence t / seq_len.
 template <int D>
 __device__ __forceinline__ void qc_bwd_load(QcBwdRow<D>& r, int row, int rows, int R, int H,
-                                            int seq_len, int64_t t0, const int64_t* bq,
-                                            const int* sp, const uint16_t* __restrict__ dq,
+                                            int seq_len, int64_t t0,
+                                            const uint16_t* __restrict__ dq,
                                             const uint16_t* __restrict__ dk,
                                             const uint16_t* __restrict__ qk_pre, int l) {
   using Q = QuadChunks<D>;
@@ -281,8 +283,9 @@ __device__ __forceinline__ void qc_bwd_load(QcBwdRow<D>& r, int row, int rows, i
   const int tt = row / R, rr = row - tt * R, hh = rr < H ? rr : rr - H;
   r.tt = tt;
   r.rr = rr;
+  const int t = (int)t0 + tt, b = t / seq_len, sp = t - b * seq_len;
   const uint16_t* asrc = qk_pre + ((t0 + tt) * R + rr) * D;
-  const uint16_t* gsrc = (rr < H ? dq : dk) + ((bq[tt] * H + hh) * seq_len + sp[tt]) * D;
+  const uint16_t* gsrc = (rr < H ? dq : dk) + (((int64_t)b * H + hh) * seq_len + sp) * D;
 #pragma unroll
   for (int m = 0; m < Q::M; ++m) {
     r.a[m] = *reinterpret_cast<const uint4*>(asrc + 8 * Q::chunk(l, m));
@@ -341,6 +344,26 @@ __device__ __forceinline__ uint32_t qc_bwd_finish(const QcBwdRow<D>& r, const fl
   return amax;
 }
 
+// Chunk i of the V gradient rows of tokens t0 .. t0 + nt - 1, head-major
+// (head, token, chunk of CV), so consecutive i are consecutive in memory.
+__device__ __forceinline__ uint4 dv_chunk(const uint16_t* __restrict__ dv, int i, int CV, int nt,
+                                          int H, int seq_len, int dvw, int64_t t0) {
+  const int cc = i % CV, rest = i / CV, tt = rest % nt, hh = rest / nt;
+  const int t = (int)t0 + tt, b = t / seq_len, sp = t - b * seq_len;
+  return *reinterpret_cast<const uint4*>(dv + (((int64_t)b * H + hh) * seq_len + sp) * dvw +
+                                         8 * cc);
+}
+
+// Per token group, every load is issued before anything waits on one: the
+// lane's bwd_rows<D>() head rows (for d = 96 and H = 6, the group's 192
+// rows are exactly 3 per quad) and its kBwdDv chunks of the V gradient
+// (only their amax is needed); the cos/sin table of the group is built
+// while they are in flight.  Three rows of d = 128 would not fit two waves
+// per SIMD in registers.
+template <int D>
+constexpr int bwd_rows() { return D == 128 ? 2 : 3; }
+constexpr int kBwdDv = 6;
+
 template <int D>
 __global__ __launch_bounds__(kThreads) void norm_rope_bwd_qc(
     const uint16_t* __restrict__ dq, const uint16_t* __restrict__ dk,
@@ -348,34 +371,42 @@ __global__ __launch_bounds__(kThreads) void norm_rope_bwd_qc(
     int seq_len, int H, int dvw, float eps, float base, uint16_t* __restrict__ dqkv,
     uint32_t* __restrict__ partials) {
   using Q = QuadChunks<D>;
-  constexpr int h = Q::h, QUADS = kThreads / 4;
+  constexpr int h = Q::h, QUADS = kThreads / 4, RB = bwd_rows<D>();
   __shared__ double rev[h];
   __shared__ float2 cs[kQuadTT * h];
   __shared__ int64_t bq[kQuadTT];
   __shared__ int sp[kQuadTT];
   __shared__ uint32_t red[4];
   build_rev_table(rev, h, D, base);
-  const int R = 2 * H, qkw = R * D, CV = dvw / 8, l = threadIdx.x & 3;
+  const int R = 2 * H, qkw = R * D, CV = dvw / 8, l = threadIdx.x & 3, quad = threadIdx.x >> 2;
   uint32_t amax = 0;
   const int64_t groups = ceil_div(T, kQuadTT);
   for (int64_t gi = blockIdx.x; gi < groups; gi += gridDim.x) {
     const int64_t t0 = gi * kQuadTT;
-    const int nt = (int)min<int64_t>(kQuadTT, T - t0), rows = nt * R;
-    quad_table(cs, bq, sp, rev, t0, nt, h, seq_len);
-    __syncthreads();
-    for (int row = threadIdx.x >> 2; row < rows; row += 2 * QUADS) {
-      QcBwdRow<D> r0, r1;  // two rows' loads in flight per thread
-      qc_bwd_load<D>(r0, row, rows, R, H, seq_len, t0, bq, sp, dq, dk, qk_pre, l);
-      qc_bwd_load<D>(r1, row + QUADS, rows, R, H, seq_len, t0, bq, sp, dq, dk, qk_pre, l);
-      amax = max(amax, qc_bwd_finish<D>(r0, cs, t0, qkw, eps, dqkv, l));
-      amax = max(amax, qc_bwd_finish<D>(r1, cs, t0, qkw, eps, dqkv, l));
+    const int nt = (int)min<int64_t>(kQuadTT, T - t0), rows = nt * R, nv = nt * H * CV;
+    uint4 vv[kBwdDv];
+#pragma unroll
+    for (int j = 0; j < kBwdDv; ++j) {
+      const int i = threadIdx.x + j * kThreads;
+      vv[j] = i < nv ? dv_chunk(dv, i, CV, nt, H, seq_len, dvw, t0) : make_uint4(0, 0, 0, 0);
     }
-    // amax of the V gradient: head hh, tokens consecutive (contiguous reads)
-    for (int i = threadIdx.x; i < nt * H * CV; i += kThreads) {
-      const int cc = i % CV, rest = i / CV, tt = rest % nt, hh = rest / nt;
-      amax = max(amax, absmax8(*reinterpret_cast<const uint4*>(
-                           dv + ((bq[tt] * H + hh) * seq_len + sp[tt]) * dvw + 8 * cc)));
+    for (int rb = 0; rb < rows; rb += RB * QUADS) {
+      QcBwdRow<D> r[RB];
+#pragma unroll
+      for (int j = 0; j < RB; ++j)
+        qc_bwd_load<D>(r[j], rb + quad + j * QUADS, rows, R, H, seq_len, t0, dq, dk, qk_pre, l);
+      if (rb == 0) {  // the same for every thread: rows > 0
+        quad_table(cs, bq, sp, rev, t0, nt, h, seq_len);
+        __syncthreads();
+      }
+#pragma unroll
+      for (int j = 0; j < RB; ++j)
+        amax = max(amax, qc_bwd_finish<D>(r[j], cs, t0, qkw, eps, dqkv, l));
     }
+#pragma unroll
+    for (int j = 0; j < kBwdDv; ++j) amax = max(amax, absmax8(vv[j]));
+    for (int i = threadIdx.x + kBwdDv * kThreads; i < nv; i += kThreads)
+      amax = max(amax, absmax8(dv_chunk(dv, i, CV, nt, H, seq_len, dvw, t0)));
     __syncthreads();
   }
   amax = block_max_u32(amax << 16, red);

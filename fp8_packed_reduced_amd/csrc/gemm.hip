@@ -22,8 +22,8 @@
 //
 // One load instruction of a copy wave fills 1 KiB = 8 consecutive 128-byte
 // LDS rows; lane i lands at physical 16-byte chunk i % 8 of row i / 8 and
-// therefore fetches logical chunk (i % 8) ^ (row % 8): the XOR swizzle that
-// spreads the 8 rows of one LDS access phase over all banks.
+// therefore fetches logical chunk (i % 8) ^ (row / 2 % 8): the XOR swizzle
+// that spreads the 16 rows of one LDS read phase over all banks.
 //
 // The MFMA's first operand is fed from B (n rows), its second from A (m
 // rows).  The 32x32 result then lands with lane l holding, for each group
@@ -58,6 +58,7 @@ struct TileCfg {
   static constexpr int PER_WAVE = BLOCKS / kCopyWaves;
   static constexpr int A_PER_WAVE = BM / 8 / kCopyWaves;  // a wave's first blocks hold A rows
   static_assert(FM * 64 == BM && FN * 64 == BN, "tile/waves");
+  static_assert(BM % 16 == 0, "B rows keep their swizzle key at stage row BM + r");
   static_assert(BLOCKS % kCopyWaves == 0 && (BM / 8) % kCopyWaves == 0, "DMA blocks per wave");
   static_assert(PER_WAVE < 64, "vmcnt range");
 };
@@ -76,7 +77,14 @@ __device__ __forceinline__ void wait_vm() {
   asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
 }
 
-__device__ inline int swz(int row, int chunk) { return row * kBK + ((chunk ^ (row & 7)) << 4); }
+// Stage rows are 128 bytes, half of the 64 four-byte LDS banks, so rows r
+// and r + 1 sit on opposite halves.  A ds_read_b128 phase of 16 lanes reads
+// one chunk of 16 consecutive rows; keying the XOR on row / 2 gives those 16
+// rows 16 distinct (bank half, chunk) slots, i.e. every bank once.  (Keying
+// it on row % 8 repeats each slot for rows r and r + 8: two-way conflicts
+// on every fragment read.)
+__device__ inline int swz_key(int row) { return (row >> 1) & 7; }
+__device__ inline int swz(int row, int chunk) { return row * kBK + ((chunk ^ swz_key(row)) << 4); }
 
 __device__ inline v8i as_v8i(uint4 lo, uint4 hi) {
   v8i r;
@@ -157,7 +165,7 @@ __device__ __forceinline__ void dma_plan(CopyState<C>& st, const Gemm& gm, int t
 #pragma unroll
   for (int t = 0; t < C::PER_WAVE; ++t) {
     const int row = (cw + kCopyWaves * t) * 8 + rl;
-    const uint32_t chunk = (uint32_t)((p ^ (row & 7)) << 4);
+    const uint32_t chunk = (uint32_t)((p ^ swz_key(row)) << 4);
     if (t < C::A_PER_WAVE)
       st.off[t] = (uint32_t)((min(m0 + row, gm.M - 1) - m0) * ra) + chunk;
     else
@@ -189,7 +197,7 @@ __device__ __forceinline__ void issue_next(CopyState<C>& st, uint8_t* lds, const
     uint32_t off = st.off[t];
     if (KTAIL) {
       const int row = (cw + kCopyWaves * t) * 8 + (lane >> 3);
-      const int kc = k0 + (((lane & 7) ^ (row & 7)) << 4);
+      const int kc = k0 + (((lane & 7) ^ swz_key(row)) << 4);
       if (kc >= gm.K) off -= (uint32_t)(kc - (gm.K - 16));
     }
 #if defined(__HIP_DEVICE_COMPILE__)  // an AMDGPU builtin: the host pass never runs this
@@ -207,7 +215,7 @@ __device__ __forceinline__ void zero_tail(uint8_t* stage, int K, int ks, int cw,
   for (int t = 0; t < C::PER_WAVE; ++t) {
     const int blk = cw + kCopyWaves * t;
     const int row = blk * 8 + (lane >> 3);
-    const int kc = k0 + (((lane & 7) ^ (row & 7)) << 4);
+    const int kc = k0 + (((lane & 7) ^ swz_key(row)) << 4);
     if (kc >= K) *reinterpret_cast<uint4*>(stage + blk * 1024 + lane * 16) = make_uint4(0, 0, 0, 0);
   }
 }
