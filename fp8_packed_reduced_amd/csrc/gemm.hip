@@ -276,7 +276,9 @@ __device__ __forceinline__ void load_half(const uint8_t* stage, int arow0, int b
 // f: its B fragments first, then A fragment i as soon as the current A
 // fragment i has had its last use.  A fragment is thus loaded a whole
 // half-step (FM x FN MFMAs) before it is needed.
-template <class C>
+// FIRST: the tile's first half-step, whose MFMAs start from zero rather
+// than from acc.
+template <class C, bool FIRST = false>
 __device__ __forceinline__ void mma_half(v16f (&acc)[C::FM][C::FN], Half<C>& f, const uint8_t* src,
                                          int arow0, int brow0, int kg, int h) {
   v8i nb[C::FN];
@@ -285,7 +287,7 @@ __device__ __forceinline__ void mma_half(v16f (&acc)[C::FM][C::FN], Half<C>& f, 
 #pragma unroll
   for (int i = 0; i < C::FM; ++i) {
 #pragma unroll
-    for (int j = 0; j < C::FN; ++j) acc[i][j] = mfma32(f.b[j], f.a[i], acc[i][j]);
+    for (int j = 0; j < C::FN; ++j) acc[i][j] = mfma32(f.b[j], f.a[i], FIRST ? v16f{} : acc[i][j]);
     f.a[i] = lds_frag(src, arow0 + i * 32, kg, h);
 #pragma unroll
     for (int j = 0; j < C::FN; ++j) {
@@ -312,9 +314,11 @@ __device__ __forceinline__ void zero_acc(v16f (&acc)[C::FM][C::FN]) {
 // then barrier g (all of this wave's reads of step g are done, step g + 1
 // has landed), and half 0 of step g + 1 streams in during half 1's MFMAs.
 // `tile_done(acc)` runs after the last K step of each tile (every nk
-// steps) and must leave acc zeroed.  After the block's last step the
-// stream reads a stage whose contents are not used.
-template <class C, class TileDone>
+// steps).  With ZC the first half-step of every tile starts from zero
+// accumulators and tile_done may leave acc as it is; without it tile_done
+// must zero acc.  After the block's last step the stream reads a stage
+// whose contents are not used.
+template <class C, bool ZC, class TileDone>
 __device__ __forceinline__ void mma_role(const uint8_t* lds, const Sched& sc, int wm, int wn,
                                          int lane, v16f (&acc)[C::FM][C::FN],
                                          const TileDone& tile_done) {
@@ -328,7 +332,10 @@ __device__ __forceinline__ void mma_role(const uint8_t* lds, const Sched& sc, in
   for (int g = 0; g < sc.steps; ++g) {
     const uint8_t* cur = lds + (g % kStages) * C::STAGE_BYTES;
     const uint8_t* nxt = lds + ((g + 1) % kStages) * C::STAGE_BYTES;
-    mma_half<C>(acc, f, cur, arow0, brow0, kg, 1);
+    if (ZC && ks_in_tile == 0)
+      mma_half<C, true>(acc, f, cur, arow0, brow0, kg, 1);
+    else
+      mma_half<C>(acc, f, cur, arow0, brow0, kg, 1);
     barrier_lds();
     mma_half<C>(acc, f, nxt, arow0, brow0, kg, 0);
     if (++ks_in_tile == sc.nk) {
@@ -393,19 +400,31 @@ struct EpiFwd {
     else
       store_stream(v + (int64_t)r.b * H * S * dv + (int64_t)r.s * dv + c.voff, val);
   }
+  // Rows m0 .. m1 are rows of one sequence: each column's rows are then
+  // evenly spaced in both outputs.
+  __device__ bool one_run(int m0, int m1) const { return m0 / S == m1 / S; }
+  __device__ uint16_t* at(int m, const Col& c) const {
+    if (c.qk) return qk_pre + (int64_t)m * nqk2 + c.n;
+    const int b = m / S, s = m - b * S;
+    return v + (int64_t)b * H * S * dv + (int64_t)s * dv + c.voff;
+  }
+  __device__ int64_t step8(const Col& c) const { return 8 * (int64_t)(c.qk ? nqk2 : dv); }
 };
 
 struct EpiDx {
   uint16_t* dx;
   int N;
-  struct Col { int n; };
+  struct Col { int n; bool live; };
   struct Row { int m; };
-  __device__ Col column(int n) const { return Col{n}; }
+  __device__ Col column(int n) const { return Col{n, n < N}; }
   __device__ Row row(int m) const { return Row{m}; }
   __device__ void advance(Row& r, int step) const { r.m += step; }
   __device__ void chunk(const Row& r, const Col& c, uint4 val) const {
-    if (c.n < N) store_stream(dx + (int64_t)r.m * N + c.n, val);
+    if (c.live) store_stream(dx + (int64_t)r.m * N + c.n, val);
   }
+  __device__ bool one_run(int, int) const { return true; }
+  __device__ uint16_t* at(int m, const Col& c) const { return dx + (int64_t)m * N + c.n; }
+  __device__ int64_t step8(const Col&) const { return 8 * (int64_t)N; }
 };
 
 template <class C, class Epi>
@@ -415,7 +434,14 @@ __device__ __forceinline__ void store_bf16_tile(const v16f (&acc)[C::FM][C::FN],
   using W = WaveSlice<C>;
   const int p = lane & 7, rq = lane >> 3;
   const typename Epi::Col col = epi.column(n0 + wn * C::WN + 8 * p);
-  typename Epi::Row row = epi.row(m0 + wm * C::WM + rq);
+  // Lane rows are mp + rq + 8k, k < 16.  When the part lies inside M and
+  // inside one sequence each lane walks one pointer by a fixed stride;
+  // otherwise every row is placed on its own.
+  const int mp = m0 + wm * C::WM;
+  const bool fast = mp + C::WM <= M && epi.one_run(mp, mp + C::WM - 1);
+  typename Epi::Row row = epi.row(mp + rq);
+  uint16_t* ptr = fast && col.live ? epi.at(mp + rq, col) : nullptr;
+  const int64_t step = epi.step8(col);
 #pragma unroll
   for (int i = 0; i < C::FM; ++i) {
 #pragma unroll
@@ -432,8 +458,13 @@ __device__ __forceinline__ void store_bf16_tile(const v16f (&acc)[C::FM][C::FN],
     for (int q = 0; q < 4; ++q) val[q] = *reinterpret_cast<const uint4*>(slice + W::at(rq + 8 * q, p));
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
-      if (row.m < M) epi.chunk(row, col, val[q]);
-      epi.advance(row, 8);
+      if (fast) {
+        if (col.live) store_stream(ptr, val[q]);
+        ptr += step;
+      } else {
+        if (row.m < M) epi.chunk(row, col, val[q]);
+        epi.advance(row, 8);
+      }
     }
   }
 }
@@ -499,11 +530,10 @@ __global__ __launch_bounds__(kGemmThreads, 1) void gemm_bf16out_kernel(
   uint8_t* slice = slices + wave * WaveSlice<C>::BYTES;
   int ord = 0;
   v16f acc[C::FM][C::FN];
-  mma_role<C>(lds, sc, wm, wn, lane, acc, [&](v16f (&a)[C::FM][C::FN]) {
+  mma_role<C, true>(lds, sc, wm, wn, lane, acc, [&](v16f (&a)[C::FM][C::FN]) {
     const int tile = sc.tile_of(ord++);
     store_bf16_tile<C, Epi>(a, alpha, slice, epi, gm.M, (tile / gm.n_tiles) * BM,
                             (tile % gm.n_tiles) * BN, wm, wn, lane);
-    zero_acc<C>(a);
   });
 }
 
@@ -536,7 +566,7 @@ __global__ __launch_bounds__(kGemmThreads, 1) void gemm_dw_part_kernel(
   }
   const int wm = wave >> 1, wn = wave & 1;
   v16f acc[C::FM][C::FN];
-  mma_role<C>(lds, sc, wm, wn, lane, acc, [](v16f (&)[C::FM][C::FN]) {});
+  mma_role<C, false>(lds, sc, wm, wn, lane, acc, [](v16f (&)[C::FM][C::FN]) {});
   store_partial_tile<C>(acc, part + (int64_t)split * gm.M * gm.N, gm.M, gm.N,
                         (tile / gm.n_tiles) * BM, (tile % gm.n_tiles) * BN, wm, wn, lane);
 }
