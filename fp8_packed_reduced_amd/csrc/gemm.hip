@@ -299,6 +299,47 @@ __device__ __forceinline__ void mma_half(v16f (&acc)[C::FM][C::FN], Half<C>& f, 
   for (int j = 0; j < C::FN; ++j) f.b[j] = nb[j];
 }
 
+// The second half-step of a step, around the step's barrier: its first
+// kEarlyRows rows of MFMAs (whose operands streamed in early in the first
+// half-step) go before the barrier, so that the barrier's wait for this
+// wave's last LDS reads overlaps matrix work; the operands of half h of
+// stage `src`, which the barrier releases, stream in behind the rest.
+constexpr int kEarlyRows = 2;
+
+template <class C>
+__device__ __forceinline__ void mma_half_barrier(v16f (&acc)[C::FM][C::FN], Half<C>& f,
+                                                 const uint8_t* src, int arow0, int brow0, int kg,
+                                                 int h) {
+  static_assert(kEarlyRows < C::FM, "rows after the barrier");
+#pragma unroll
+  for (int i = 0; i < kEarlyRows; ++i)
+#pragma unroll
+    for (int j = 0; j < C::FN; ++j) acc[i][j] = mfma32(f.b[j], f.a[i], acc[i][j]);
+  // scheduling fences: the barrier orders memory accesses only, and the
+  // compiler would otherwise sink the early MFMAs below it
+  __builtin_amdgcn_sched_barrier(0);
+  barrier_lds();
+  __builtin_amdgcn_sched_barrier(0);
+  v8i nb[C::FN];
+#pragma unroll
+  for (int j = 0; j < C::FN; ++j) nb[j] = lds_frag(src + C::BM_ * kBK, brow0 + j * 32, kg, h);
+#pragma unroll
+  for (int i = 0; i < kEarlyRows; ++i) f.a[i] = lds_frag(src, arow0 + i * 32, kg, h);
+#pragma unroll
+  for (int i = kEarlyRows; i < C::FM; ++i) {
+#pragma unroll
+    for (int j = 0; j < C::FN; ++j) acc[i][j] = mfma32(f.b[j], f.a[i], acc[i][j]);
+    f.a[i] = lds_frag(src, arow0 + i * 32, kg, h);
+#pragma unroll
+    for (int j = 0; j < C::FN; ++j) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // 1 MFMA
+      __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);  // then up to 2 LDS reads
+    }
+  }
+#pragma unroll
+  for (int j = 0; j < C::FN; ++j) f.b[j] = nb[j];
+}
+
 template <class C>
 __device__ __forceinline__ void zero_acc(v16f (&acc)[C::FM][C::FN]) {
 #pragma unroll
@@ -311,8 +352,9 @@ __device__ __forceinline__ void zero_acc(v16f (&acc)[C::FM][C::FN]) {
 
 // The matrix waves' pipeline over the block's steps.  Half 0 of step g
 // was loaded after barrier g - 1; half 1 streams in during half 0's MFMAs;
-// then barrier g (all of this wave's reads of step g are done, step g + 1
-// has landed), and half 0 of step g + 1 streams in during half 1's MFMAs.
+// then (after the first rows of half 1's MFMAs) barrier g: all of this
+// wave's reads of step g are done and step g + 1 has landed; half 0 of
+// step g + 1 streams in during the rest of half 1's MFMAs.
 // `tile_done(acc)` runs after the last K step of each tile (every nk
 // steps).  With ZC the first half-step of every tile starts from zero
 // accumulators and tile_done may leave acc as it is; without it tile_done
@@ -336,8 +378,7 @@ __device__ __forceinline__ void mma_role(const uint8_t* lds, const Sched& sc, in
       mma_half<C, true>(acc, f, cur, arow0, brow0, kg, 1);
     else
       mma_half<C>(acc, f, cur, arow0, brow0, kg, 1);
-    barrier_lds();
-    mma_half<C>(acc, f, nxt, arow0, brow0, kg, 0);
+    mma_half_barrier<C>(acc, f, nxt, arow0, brow0, kg, 0);
     if (++ks_in_tile == sc.nk) {
       tile_done(acc);
       ks_in_tile = 0;
