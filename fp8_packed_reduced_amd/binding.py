@@ -56,13 +56,12 @@ class _TraceC(ctypes.Structure):
 
 class Layout(ctypes.Structure):
     _fields_ = [("tokens", ctypes.c_int64), ("tokens_padded", ctypes.c_int64),
-                ("saved_x8t", ctypes.c_size_t), ("saved_qk_pre", ctypes.c_size_t),
-                ("saved_x_scales", ctypes.c_size_t), ("fwd_x8", ctypes.c_size_t),
+                ("saved_x8", ctypes.c_size_t), ("saved_qk_pre", ctypes.c_size_t),
+                ("saved_x_scales", ctypes.c_size_t),
                 ("bwd_dqkv", ctypes.c_size_t), ("bwd_g_scales", ctypes.c_size_t),
-                ("bwd_g8", ctypes.c_size_t), ("bwd_g8t", ctypes.c_size_t),
+                ("bwd_g8", ctypes.c_size_t),
                 ("bwd_dw_part", ctypes.c_size_t), ("dw_splits", ctypes.c_int32),
-                ("k_block", ctypes.c_int32), ("act_block_rows", ctypes.c_int32),
-                ("t_block_rows", ctypes.c_int32)]
+                ("k_block", ctypes.c_int32), ("act_block_rows", ctypes.c_int32)]
 
 
 _lib = None

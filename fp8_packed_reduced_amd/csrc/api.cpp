@@ -24,10 +24,10 @@ constexpr size_t kMaxDynLds = 64 * 1024;  // dynamic LDS of one epilogue block
 struct Plan {
   int D, H, dqk, dv, nq, nqk2, N;
   int64_t T, Tp;
-  size_t s_x8t, s_qk, s_xsc, saved_total;
-  size_t f_part, f_x8, fwd_total;
+  size_t s_x8, s_qk, s_xsc, saved_total;
+  size_t f_part, fwd_total;
   int f_parts;
-  size_t b_part, b_gsc, b_dqkv, b_g8, b_g8t, b_dwpart, bwd_total;
+  size_t b_part, b_gsc, b_dqkv, b_g8, b_dwpart, bwd_total;
   int b_parts;
   size_t p_part, pack_total;
 };
@@ -70,7 +70,7 @@ Plan make_plan(const fpr_dims* d, int64_t T) {
   p.T = T;
   p.Tp = round_up(T > 0 ? T : 1, 128);
   size_t c = 0;
-  p.s_x8t = take(c, fpr::t_blocked_bytes(p.D, p.Tp));
+  p.s_x8 = take(c, fpr::act_blocked_bytes(T, p.D));
   p.s_qk = take(c, (size_t)T * p.nqk2 * 2);
   p.s_xsc = take(c, 4 * sizeof(float));
   p.saved_total = c;
@@ -78,7 +78,6 @@ Plan make_plan(const fpr_dims* d, int64_t T) {
   // one amax block per 256 x 16-byte vectors of x, at most kPartsAct
   p.f_parts = (int)std::max<int64_t>(1, std::min<int64_t>(kPartsAct, ceil_div(T * p.D / 8, fpr::kThreads)));
   p.f_part = take(c, (size_t)p.f_parts * 4);
-  p.f_x8 = take(c, fpr::act_blocked_bytes(T, p.D));
   p.fwd_total = c;
   c = 0;
   p.b_parts = fpr::norm_rope_bwd_blocks(T > 0 ? T : 1, p.H, p.dqk);
@@ -86,7 +85,6 @@ Plan make_plan(const fpr_dims* d, int64_t T) {
   p.b_gsc = take(c, 4 * sizeof(float));
   p.b_dqkv = take(c, (size_t)T * p.nqk2 * 2);
   p.b_g8 = take(c, fpr::act_blocked_bytes(T, p.N));
-  p.b_g8t = take(c, fpr::t_blocked_bytes(p.N, p.Tp));
   p.b_dwpart = take(c, fpr::dw_partial_bytes(p.D, p.N, p.Tp));
   p.bwd_total = c;
   c = 0;
@@ -180,19 +178,16 @@ int fpr_get_layout(const fpr_dims* dims, int64_t tokens, fpr_layout* out) {
   const Plan p = make_plan(dims, tokens);
   out->tokens = p.T;
   out->tokens_padded = p.Tp;
-  out->saved_x8t = p.s_x8t;
+  out->saved_x8 = p.s_x8;
   out->saved_qk_pre = p.s_qk;
   out->saved_x_scales = p.s_xsc;
-  out->fwd_x8 = p.f_x8;
   out->bwd_dqkv = p.b_dqkv;
   out->bwd_g_scales = p.b_gsc;
   out->bwd_g8 = p.b_g8;
-  out->bwd_g8t = p.b_g8t;
   out->bwd_dw_part = p.b_dwpart;
   out->dw_splits = fpr::dw_splits(p.D, p.N, p.Tp);
   out->k_block = fpr::kKBlock;
   out->act_block_rows = fpr::kActRows;
-  out->t_block_rows = fpr::kTRows;
   return FPR_OK;
 }
 
@@ -240,13 +235,12 @@ int qkv_forward(const fpr_dims* dims, int32_t n_seq, int32_t seq_len, const uint
   (void)hipGetLastError();
   uint32_t* parts = at<uint32_t>(workspace, p.f_part);
   float* xsc = at<float>(saved, p.s_xsc);
-  uint8_t* x8 = at<uint8_t>(workspace, p.f_x8);
-  uint8_t* x8t = at<uint8_t>(saved, p.s_x8t);
+  uint8_t* x8 = at<uint8_t>(saved, p.s_x8);
   uint16_t* qk = at<uint16_t>(saved, p.s_qk);
   stage("amax_x", s, [&] { fpr::launch_amax_bf16(x, T * p.D, parts, p.f_parts, s); });
   stage("quantize_x", s, [&] {
     fpr::launch_quantize_act(x, T, p.D, parts, p.f_parts, xsc, cache->status,
-                             FPR_STATUS_X_NONFINITE, x8, x8t, p.Tp, s);
+                             FPR_STATUS_X_NONFINITE, x8, p.Tp, s);
   });
   stage("gemm_fwd", s, [&] {
     fpr::launch_gemm_fwd(x8, cache->w_packed_t, (int)T, p.N, p.D, xsc, cache->scales, qk,
@@ -278,13 +272,12 @@ int qkv_backward(const fpr_dims* dims, int32_t n_seq, int32_t seq_len, const uin
   hipStream_t s = static_cast<hipStream_t>(stream);
   (void)hipGetLastError();
   const float* xsc = at<float>(saved, p.s_xsc);
-  const uint8_t* x8t = at<uint8_t>(saved, p.s_x8t);
+  const uint8_t* x8 = at<uint8_t>(saved, p.s_x8);
   const uint16_t* qk = at<uint16_t>(saved, p.s_qk);
   uint32_t* parts = at<uint32_t>(workspace, p.b_part);
   float* gsc = at<float>(workspace, p.b_gsc);
   uint16_t* dqkv = at<uint16_t>(workspace, p.b_dqkv);
   uint8_t* g8 = at<uint8_t>(workspace, p.b_g8);
-  uint8_t* g8t = at<uint8_t>(workspace, p.b_g8t);
   float* dwpart = at<float>(workspace, p.b_dwpart);
   stage("norm_rope_bwd", s, [&] {
     fpr::launch_norm_rope_bwd(dq, dk, dv, qk, T, seq_len, p.H, p.dqk, p.dv, dims->eps,
@@ -293,12 +286,12 @@ int qkv_backward(const fpr_dims* dims, int32_t n_seq, int32_t seq_len, const uin
   stage("quantize_g", s, [&] {
     fpr::launch_quantize_act_split(dqkv, p.nqk2, dv, p.dv, p.H, seq_len, T, p.N, parts,
                                    p.b_parts, gsc, cache->status, FPR_STATUS_G_NONFINITE, g8,
-                                   g8t, p.Tp, s);
+                                   p.Tp, s);
   });
   stage("gemm_dx", s, [&] {
     fpr::launch_gemm_dx(g8, cache->w_packed, (int)T, p.D, p.N, gsc, cache->scales, dx, s);
   });
-  stage("gemm_dw", s, [&] { fpr::launch_gemm_dw(x8t, g8t, p.D, p.N, p.Tp, dwpart, s); });
+  stage("gemm_dw", s, [&] { fpr::launch_gemm_dw(x8, g8, p.D, p.N, p.Tp, dwpart, s); });
   stage("dw_reduce", s, [&] {
     fpr::launch_dw_reduce(dwpart, p.D, p.N, p.Tp, xsc, gsc, dwq, ldq, dwk, ldk, dwv, ldv, p.nq, s);
   });

@@ -34,8 +34,10 @@
 // bf16 outputs (forward, dX) come from a persistent kernel, one block per
 // CU walking its tiles; a finished 32-row slice of a matrix wave's tile is
 // transposed through that wave's own 4 KiB of LDS so that every lane
-// stores a 16-byte run of one row.  dW (K = tokens) splits K over blocks
-// and writes fp32 partial sums that a second kernel adds in split order.
+// stores a 16-byte run of one row.  dW (K = tokens) reads x8 and g8 as the
+// quantiser stores them, token by token, and turns them into MFMA operands
+// with transposing LDS reads; it splits K over blocks and writes fp32
+// partial sums that a second kernel adds in split order.
 #include "common.hpp"
 #include "launch.hpp"
 
@@ -101,6 +103,62 @@ __device__ __forceinline__ v8i lds_frag(const uint8_t* base, int row, int kg, in
                 *reinterpret_cast<const uint4*>(base + swz(row, c + 1)));
 }
 
+// ---- token-major operands (dW)
+//
+// dW = x^T g contracts over tokens, and x8, g8 are stored token by token
+// (features contiguous).  The dW stage therefore holds A as 128 token rows
+// of 256 feature bytes and B as 128 token rows of 128, and the operands
+// reach the MFMA layout through transposing LDS reads: in each 16-lane
+// group of ds_read_b64_tr_b8, byte k of lane i comes from byte i % 8 of the
+// 8 bytes addressed by lane 2k + i / 8.  Lane r = 2k + e of a group points
+// at token t0 + k, features f + 8e, so lane i receives features f + i of
+// tokens t0 .. t0 + 7; four such reads give a lane the 32 tokens of its
+// K half for one feature row, in the order the other operand uses too.
+// Rows are stored in 32-byte segments, segment s of token row t at
+// s ^ key(t): the 8 rows one 32-lane read phase touches then fall on 8
+// distinct bank octets (A rows span 256 bytes, key t % 8; B rows 128 bytes,
+// where rows t and t + 1 already sit on opposite bank halves, key t / 2 % 4).
+typedef int v2i_t __attribute__((ext_vector_type(2)));
+typedef __attribute__((address_space(3))) v2i_t lds_v2i;
+
+template <int PITCH>
+__device__ inline int tok_key(int t) { return PITCH == 256 ? (t & 7) : ((t >> 1) & 3); }
+template <int PITCH>
+__device__ inline int tok_at(int t, int f) {
+  return t * PITCH + (((f >> 5) ^ tok_key<PITCH>(t)) << 5) + (f & 31);
+}
+
+// One 32-row operand of K half h: lane l holds feature row f0 + l % 32 and
+// the 32 tokens 64h + 32(l / 32) + [0, 32) of the stage.
+template <int PITCH>
+__device__ __forceinline__ v8i tok_frag(const uint8_t* base, int f0, int lane, int h) {
+  const int r = lane & 15;
+  const int f = f0 + ((lane >> 4) & 1) * 16 + 8 * (r & 1);
+  const int t0 = 64 * h + 32 * (lane >> 5) + (r >> 1);
+  v8i out;
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const v2i_t x = __builtin_amdgcn_ds_read_tr8_b64_v2i32(
+        (lds_v2i*)(base + tok_at<PITCH>(t0 + 8 * q, f)));
+    out[2 * q] = x[0];
+    out[2 * q + 1] = x[1];
+  }
+  return out;
+}
+
+// The A (rows a0 + l % 32) and B (rows b0 + l % 32) operands of K half h of
+// a stage, in either storage.
+template <class C, bool TOK>
+__device__ __forceinline__ v8i frag_a(const uint8_t* stage, int a0, int lane, int h) {
+  if constexpr (TOK) return tok_frag<C::BM_>(stage, a0, lane, h);
+  else return lds_frag(stage, a0 + (lane & 31), lane >> 5, h);
+}
+template <class C, bool TOK>
+__device__ __forceinline__ v8i frag_b(const uint8_t* stage, int b0, int lane, int h) {
+  if constexpr (TOK) return tok_frag<C::BN_>(stage + C::BM_ * kBK, b0, lane, h);
+  else return lds_frag(stage + C::BM_ * kBK, b0 + (lane & 31), lane >> 5, h);
+}
+
 __device__ __forceinline__ v16f mfma32(v8i b, v8i a, v16f c) {
   return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(b, a, c, 0, 0, 0, 127, 0, 127);
 }
@@ -119,6 +177,9 @@ __device__ __forceinline__ v16f mfma32(v8i b, v8i a, v16f c) {
 // An operand is either row-major with leading dimension ld, or blocked
 // (blk > 0): blocks of blk rows x 128 bytes of K, as the activation
 // quantiser writes them (blk equals the tile's rows for that operand).
+// With tok, both operands are token-major instead (dW: K = tokens): the
+// row layouts of x8 and g8, blocks of kActRows tokens x kKBlock features,
+// lda / ldb = feature blocks per block row.
 struct Gemm {
   const uint8_t* A;
   int64_t lda;
@@ -126,6 +187,7 @@ struct Gemm {
   int64_t ldb;
   int M, N, K, n_tiles;
   int a_blk, b_blk;  // 0: row-major; else block rows
+  int tok;
 };
 
 struct Sched {
@@ -156,10 +218,38 @@ struct CopyState {
   int issued;  // steps issued so far
 };
 
+// Token-major stage (dW): A block u (< BM / 8) holds token rows 4u .. 4u + 3,
+// B block u rows 8u .. 8u + 7; lane j of a block lands at physical 16-byte
+// chunk j % (row chunks) of its row and fetches the chunk that tok_at()
+// puts there.  Features past the padded width read the last chunk (only
+// output rows and columns that are never stored see them).  Offsets are
+// from the first token row of the step's 128 within its 256-row block.
+template <class C>
+__device__ __forceinline__ uint32_t tok_off(int u, int lane, bool is_a, int f0, int fpad) {
+  const int pitch = is_a ? C::BM_ : C::BN_, per_row = pitch / 16;
+  const int t = u * (1024 / pitch) + lane / per_row, p = lane % per_row;
+  const int key = is_a ? tok_key<C::BM_>(t) : tok_key<C::BN_>(t);
+  const int f = min(f0 + ((((p >> 1) ^ key)) << 5) + ((p & 1) << 4), fpad - 16);
+  return (uint32_t)((((f >> 7) * kActRows + t) << 7) + (f & 127));
+}
+
 template <class C>
 __device__ __forceinline__ void dma_plan(CopyState<C>& st, const Gemm& gm, int tile, int cw,
                                          int lane) {
   const int m0 = (tile / gm.n_tiles) * C::BM_, n0 = (tile % gm.n_tiles) * C::BN_;
+  if (gm.tok) {
+#pragma unroll
+    for (int t = 0; t < C::PER_WAVE; ++t) {
+      const bool is_a = t < C::A_PER_WAVE;
+      const int u = cw + kCopyWaves * (is_a ? t : t - C::A_PER_WAVE);
+      st.off[t] = is_a ? tok_off<C>(u, lane, true, m0, (int)gm.lda * kBK)
+                       : tok_off<C>(u, lane, false, n0, (int)gm.ldb * kBK);
+    }
+    st.Atile = gm.A;
+    st.Btile = gm.B;
+    st.tile = tile;
+    return;
+  }
   const int rl = lane >> 3, p = lane & 7;
   const int64_t ra = gm.a_blk ? kBK : gm.lda, rb = gm.b_blk ? kBK : gm.ldb;
 #pragma unroll
@@ -189,8 +279,16 @@ __device__ __forceinline__ void issue_next(CopyState<C>& st, uint8_t* lds, const
   const int tile = sc.tile(g);
   if (tile != st.tile) dma_plan<C>(st, gm, tile, cw, lane);
   const int ks = sc.ks(g), k0 = ks * kBK;
-  const uint8_t* Ak = st.Atile + (gm.a_blk ? (int64_t)ks * C::BM_ * kBK : k0);
-  const uint8_t* Bk = st.Btile + (gm.b_blk ? (int64_t)ks * C::BN_ * kBK : k0);
+  const uint8_t* Ak;
+  const uint8_t* Bk;
+  if (gm.tok) {  // block row ks / 2, its first or second 128 tokens
+    const int64_t half = (int64_t)(ks & 1) * kBK * kBK;
+    Ak = st.Atile + (int64_t)(ks >> 1) * gm.lda * kActRows * kBK + half;
+    Bk = st.Btile + (int64_t)(ks >> 1) * gm.ldb * kActRows * kBK + half;
+  } else {
+    Ak = st.Atile + (gm.a_blk ? (int64_t)ks * C::BM_ * kBK : k0);
+    Bk = st.Btile + (gm.b_blk ? (int64_t)ks * C::BN_ * kBK : k0);
+  }
   uint8_t* stage = lds + (g % kStages) * C::STAGE_BYTES;
 #pragma unroll
   for (int t = 0; t < C::PER_WAVE; ++t) {
@@ -262,13 +360,13 @@ struct Half {
   v8i b[C::FN];
 };
 
-template <class C>
-__device__ __forceinline__ void load_half(const uint8_t* stage, int arow0, int brow0, int kg,
-                                          int h, Half<C>& f) {
+template <class C, bool TOK>
+__device__ __forceinline__ void load_half(const uint8_t* stage, int a0, int b0, int lane, int h,
+                                          Half<C>& f) {
 #pragma unroll
-  for (int j = 0; j < C::FN; ++j) f.b[j] = lds_frag(stage + C::BM_ * kBK, brow0 + j * 32, kg, h);
+  for (int j = 0; j < C::FN; ++j) f.b[j] = frag_b<C, TOK>(stage, b0 + j * 32, lane, h);
 #pragma unroll
-  for (int i = 0; i < C::FM; ++i) f.a[i] = lds_frag(stage, arow0 + i * 32, kg, h);
+  for (int i = 0; i < C::FM; ++i) f.a[i] = frag_a<C, TOK>(stage, a0 + i * 32, lane, h);
 }
 
 // The FM x FN MFMAs of one half-step on the operands in f, while the
@@ -278,17 +376,17 @@ __device__ __forceinline__ void load_half(const uint8_t* stage, int arow0, int b
 // half-step (FM x FN MFMAs) before it is needed.
 // FIRST: the tile's first half-step, whose MFMAs start from zero rather
 // than from acc.
-template <class C, bool FIRST = false>
+template <class C, bool TOK, bool FIRST = false>
 __device__ __forceinline__ void mma_half(v16f (&acc)[C::FM][C::FN], Half<C>& f, const uint8_t* src,
-                                         int arow0, int brow0, int kg, int h) {
+                                         int a0, int b0, int lane, int h) {
   v8i nb[C::FN];
 #pragma unroll
-  for (int j = 0; j < C::FN; ++j) nb[j] = lds_frag(src + C::BM_ * kBK, brow0 + j * 32, kg, h);
+  for (int j = 0; j < C::FN; ++j) nb[j] = frag_b<C, TOK>(src, b0 + j * 32, lane, h);
 #pragma unroll
   for (int i = 0; i < C::FM; ++i) {
 #pragma unroll
     for (int j = 0; j < C::FN; ++j) acc[i][j] = mfma32(f.b[j], f.a[i], FIRST ? v16f{} : acc[i][j]);
-    f.a[i] = lds_frag(src, arow0 + i * 32, kg, h);
+    f.a[i] = frag_a<C, TOK>(src, a0 + i * 32, lane, h);
 #pragma unroll
     for (int j = 0; j < C::FN; ++j) {
       __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // 1 MFMA
@@ -306,9 +404,9 @@ __device__ __forceinline__ void mma_half(v16f (&acc)[C::FM][C::FN], Half<C>& f, 
 // stage `src`, which the barrier releases, stream in behind the rest.
 constexpr int kEarlyRows = 2;
 
-template <class C>
+template <class C, bool TOK>
 __device__ __forceinline__ void mma_half_barrier(v16f (&acc)[C::FM][C::FN], Half<C>& f,
-                                                 const uint8_t* src, int arow0, int brow0, int kg,
+                                                 const uint8_t* src, int a0, int b0, int lane,
                                                  int h) {
   static_assert(kEarlyRows < C::FM, "rows after the barrier");
 #pragma unroll
@@ -322,14 +420,14 @@ __device__ __forceinline__ void mma_half_barrier(v16f (&acc)[C::FM][C::FN], Half
   __builtin_amdgcn_sched_barrier(0);
   v8i nb[C::FN];
 #pragma unroll
-  for (int j = 0; j < C::FN; ++j) nb[j] = lds_frag(src + C::BM_ * kBK, brow0 + j * 32, kg, h);
+  for (int j = 0; j < C::FN; ++j) nb[j] = frag_b<C, TOK>(src, b0 + j * 32, lane, h);
 #pragma unroll
-  for (int i = 0; i < kEarlyRows; ++i) f.a[i] = lds_frag(src, arow0 + i * 32, kg, h);
+  for (int i = 0; i < kEarlyRows; ++i) f.a[i] = frag_a<C, TOK>(src, a0 + i * 32, lane, h);
 #pragma unroll
   for (int i = kEarlyRows; i < C::FM; ++i) {
 #pragma unroll
     for (int j = 0; j < C::FN; ++j) acc[i][j] = mfma32(f.b[j], f.a[i], acc[i][j]);
-    f.a[i] = lds_frag(src, arow0 + i * 32, kg, h);
+    f.a[i] = frag_a<C, TOK>(src, a0 + i * 32, lane, h);
 #pragma unroll
     for (int j = 0; j < C::FN; ++j) {
       __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // 1 MFMA
@@ -360,25 +458,24 @@ __device__ __forceinline__ void zero_acc(v16f (&acc)[C::FM][C::FN]) {
 // accumulators and tile_done may leave acc as it is; without it tile_done
 // must zero acc.  After the block's last step the stream reads a stage
 // whose contents are not used.
-template <class C, bool ZC, class TileDone>
+template <class C, bool TOK, bool ZC, class TileDone>
 __device__ __forceinline__ void mma_role(const uint8_t* lds, const Sched& sc, int wm, int wn,
                                          int lane, v16f (&acc)[C::FM][C::FN],
                                          const TileDone& tile_done) {
-  const int kg = lane >> 5;
-  const int arow0 = wm * C::WM + (lane & 31), brow0 = wn * C::WN + (lane & 31);
+  const int a0 = wm * C::WM, b0 = wn * C::WN;
   zero_acc<C>(acc);
   barrier_lds();
   Half<C> f;
-  load_half<C>(lds, arow0, brow0, kg, 0, f);
+  load_half<C, TOK>(lds, a0, b0, lane, 0, f);
   int ks_in_tile = 0;
   for (int g = 0; g < sc.steps; ++g) {
     const uint8_t* cur = lds + (g % kStages) * C::STAGE_BYTES;
     const uint8_t* nxt = lds + ((g + 1) % kStages) * C::STAGE_BYTES;
     if (ZC && ks_in_tile == 0)
-      mma_half<C, true>(acc, f, cur, arow0, brow0, kg, 1);
+      mma_half<C, TOK, true>(acc, f, cur, a0, b0, lane, 1);
     else
-      mma_half<C>(acc, f, cur, arow0, brow0, kg, 1);
-    mma_half_barrier<C>(acc, f, nxt, arow0, brow0, kg, 0);
+      mma_half<C, TOK>(acc, f, cur, a0, b0, lane, 1);
+    mma_half_barrier<C, TOK>(acc, f, nxt, a0, b0, lane, 0);
     if (++ks_in_tile == sc.nk) {
       tile_done(acc);
       ks_in_tile = 0;
@@ -571,7 +668,7 @@ __global__ __launch_bounds__(kGemmThreads, 1) void gemm_bf16out_kernel(
   uint8_t* slice = slices + wave * WaveSlice<C>::BYTES;
   int ord = 0;
   v16f acc[C::FM][C::FN];
-  mma_role<C, true>(lds, sc, wm, wn, lane, acc, [&](v16f (&a)[C::FM][C::FN]) {
+  mma_role<C, false, true>(lds, sc, wm, wn, lane, acc, [&](v16f (&a)[C::FM][C::FN]) {
     const int tile = sc.tile_of(ord++);
     store_bf16_tile<C, Epi>(a, alpha, slice, epi, gm.M, (tile / gm.n_tiles) * BM,
                             (tile % gm.n_tiles) * BN, wm, wn, lane);
@@ -607,7 +704,7 @@ __global__ __launch_bounds__(kGemmThreads, 1) void gemm_dw_part_kernel(
   }
   const int wm = wave >> 1, wn = wave & 1;
   v16f acc[C::FM][C::FN];
-  mma_role<C, false>(lds, sc, wm, wn, lane, acc, [](v16f (&)[C::FM][C::FN]) {});
+  mma_role<C, true, false>(lds, sc, wm, wn, lane, acc, [](v16f (&)[C::FM][C::FN]) {});
   store_partial_tile<C>(acc, part + (int64_t)split * gm.M * gm.N, gm.M, gm.N,
                         (tile / gm.n_tiles) * BM, (tile % gm.n_tiles) * BN, wm, wn, lane);
 }
@@ -637,13 +734,11 @@ __global__ __launch_bounds__(kThreads) void dw_reduce_kernel(
 // ------------------------------------------------------------- launchers
 
 constexpr int kBMo = 256, kBNo = 128;  // bf16-output tile (persistent)
-constexpr int kBMw = 192, kBNw = 192;  // dW split-K tile
+constexpr int kBMw = 256, kBNw = 128;  // dW split-K tile (token-major operands)
 // Split-K counts are chosen for a 256-CU part; the choice must not depend on
 // the device present, since workspace sizes are queried without one.
 constexpr int kSplitCUs = 256, kMaxSplits = 8;
-static_assert((kBMw - 1) * kMaxTokens + kBK <= 0xFFFFFFFFll &&
-                  (kBNw - 1) * kMaxTokens + kBK <= 0xFFFFFFFFll,
-              "dW row offsets must fit 32 bits");
+static_assert(kActRows == 2 * kBK, "a dW step is one half of a token block");
 
 static int cu_count() {
   int dev = 0, n = 0;
@@ -667,19 +762,19 @@ static void launch_bf16out(const Gemm& gm, const float* sa, const float* sb, con
                                                                                sb, epi);
 }
 
-static_assert(kBMo == kActRows && kBMw == kTRows && kBNw == kTRows && kBK == kKBlock,
+static_assert(kBMo == kActRows && kBK == kKBlock,
               "GEMM tiles and the blocked activation layouts");
 
 void launch_gemm_fwd(const uint8_t* x8, const uint8_t* w_packed_t, int T, int N, int D,
                      const float* x_scales, const float* w_scales, uint16_t* qk_pre, int nqk2,
                      uint16_t* v, int H, int d_v, int seq_len, hipStream_t s) {
-  const Gemm gm{x8, 0, w_packed_t, D, T, N, D, (int)ceil_div(N, kBNo), kActRows, 0};
+  const Gemm gm{x8, 0, w_packed_t, D, T, N, D, (int)ceil_div(N, kBNo), kActRows, 0, 0};
   launch_bf16out(gm, x_scales, w_scales, EpiFwd{qk_pre, v, N, nqk2, H, d_v, seq_len}, s);
 }
 
 void launch_gemm_dx(const uint8_t* g8, const uint8_t* w_packed, int T, int D, int Np,
                     const float* g_scales, const float* w_scales, uint16_t* dx, hipStream_t s) {
-  const Gemm gm{g8, 0, w_packed, Np, T, D, Np, (int)ceil_div(D, kBNo), kActRows, 0};
+  const Gemm gm{g8, 0, w_packed, Np, T, D, Np, (int)ceil_div(D, kBNo), kActRows, 0, 0};
   launch_bf16out(gm, g_scales, w_scales, EpiDx{dx, D}, s);
 }
 
@@ -702,12 +797,13 @@ size_t dw_partial_bytes(int D, int Np, int64_t tokens_padded) {
   return (size_t)dw_splits(D, Np, tokens_padded) * D * Np * sizeof(float);
 }
 
-void launch_gemm_dw(const uint8_t* x8t, const uint8_t* g8t, int D, int Np, int64_t Tp,
+void launch_gemm_dw(const uint8_t* x8, const uint8_t* g8, int D, int Np, int64_t Tp,
                     float* part, hipStream_t s) {
   const int splits = dw_splits(D, Np, Tp);
   const int nk = (int)ceil_div(Tp, kBK);
   const int per = (int)ceil_div(nk, splits);
-  const Gemm gm{x8t, 0, g8t, 0, D, Np, (int)Tp, (int)ceil_div(Np, kBNw), kTRows, kTRows};
+  const Gemm gm{x8, ceil_div(D, kKBlock), g8, ceil_div(Np, kKBlock), D, Np, (int)Tp,
+                (int)ceil_div(Np, kBNw), 0, 0, 1};
   const int blocks = (int)ceil_div(D, kBMw) * gm.n_tiles * splits;
   gemm_dw_part_kernel<kBMw, kBNw><<<blocks, kGemmThreads, 0, s>>>(gm, splits, per, part);
 }

@@ -38,32 +38,27 @@ void launch_quantize_w(const float* wq, int64_t ldq, const float* wk, int64_t ld
                        const uint32_t* partials, int parts, float* scales, int32_t* status,
                        int status_bit, uint8_t* w_packed, uint8_t* w_packed_t, hipStream_t s);
 
-// Blocked layouts of the FP8 activation copies, which only the GEMMs read.
-// A matrix of R rows and K columns (K contiguous) is stored as blocks of
-// `block rows` x kKBlock bytes: block (R / block rows, K / kKBlock) at
-// ((r_blk * ceil(K / kKBlock) + k_blk) * block rows) * kKBlock, rows kKBlock
-// bytes apart inside.  One K step of a GEMM tile is then one contiguous
-// block, which keeps a CU's loads on few pages and whole cache lines.
-//   row layout (x8, g8; the A operand of forward / dX):   kActRows rows
-//   transposed layout (x8t, g8t; both operands of dW):     kTRows rows
-constexpr int kKBlock = 128, kActRows = 256, kTRows = 192;
+// Blocked layout of the FP8 activation copies x8 and g8, which only the
+// GEMMs read.  A matrix of R rows (tokens) and K columns (K contiguous) is
+// stored as blocks of kActRows rows x kKBlock bytes: block
+// (R / kActRows, K / kKBlock) at ((r_blk * ceil(K / kKBlock) + k_blk) *
+// kActRows) * kKBlock, rows kKBlock bytes apart inside.  One K step of a
+// forward / dX tile (the A operand) is one contiguous block, and one K step
+// of dW (128 tokens of x8 and g8) is half a block row.
+constexpr int kKBlock = 128, kActRows = 256;
 inline size_t act_blocked_bytes(int64_t rows, int64_t cols) {
   return (size_t)round_up(rows, kActRows) * (size_t)round_up(cols, kKBlock);
 }
-inline size_t t_blocked_bytes(int64_t cols, int64_t tokens_padded) {
-  return (size_t)round_up(cols, kTRows) * (size_t)tokens_padded;
-}
 
 // Quantise a [rows][cols] bf16 matrix with its per-tensor scale (from the
-// partials, as above) into dst (row layout, rows x cols; columns cols ..
-// multiple of kKBlock written as zero) and dst_t (transposed layout, cols x
-// tokens_padded; tokens rows .. tokens_padded written as zero).  cols % 16
-// == 0, tokens_padded % kKBlock == 0.  Rows past `rows` (resp. `cols`)
-// inside the last block of rows are left unwritten: the GEMMs never read
-// them.
+// partials, as above) into dst (blocked row layout; columns cols .. multiple
+// of kKBlock and rows rows .. tokens_padded written as zero, the latter
+// being the dW GEMM's K tail).  cols % 16 == 0, tokens_padded % kKBlock ==
+// 0.  Rows from tokens_padded to the end of the last block of rows are left
+// unwritten: no GEMM reads them.
 void launch_quantize_act(const uint16_t* src, int64_t rows, int cols, const uint32_t* partials,
                          int parts, float* scales, int32_t* status, int status_bit, uint8_t* dst,
-                         uint8_t* dst_t, int64_t tokens_padded, hipStream_t s);
+                         int64_t tokens_padded, hipStream_t s);
 
 // The same for rows whose first `split` columns come from src [rows][split]
 // and the rest from head-major rows: column split + h * vw + j of token t is
@@ -72,7 +67,7 @@ void launch_quantize_act(const uint16_t* src, int64_t rows, int cols, const uint
 void launch_quantize_act_split(const uint16_t* src, int split, const uint16_t* vsrc, int vw,
                                int vh, int vs, int64_t rows, int cols, const uint32_t* partials,
                                int parts, float* scales, int32_t* status, int status_bit,
-                               uint8_t* dst, uint8_t* dst_t, int64_t tokens_padded, hipStream_t s);
+                               uint8_t* dst, int64_t tokens_padded, hipStream_t s);
 
 void launch_encode(const float* in, int64_t n, float inv, uint8_t* out, hipStream_t s);
 
@@ -93,9 +88,9 @@ int dw_splits(int D, int Np, int64_t tokens_padded);
 size_t dw_partial_bytes(int D, int Np, int64_t tokens_padded);
 
 // dW = s_x s_g x^T g: M = D, N = N_packed, K = tokens (padded, zero tail).
-// x8t [D][Tp], g8t [Np][Tp]; unscaled split-K partial sums go to `part`
-// [dw_splits][D][Np] fp32 ...
-void launch_gemm_dw(const uint8_t* x8t, const uint8_t* g8t, int D, int Np, int64_t Tp,
+// x8 [T][D], g8 [T][Np] in the blocked row layout, rows T .. Tp - 1 zero;
+// unscaled split-K partial sums go to `part` [dw_splits][D][Np] fp32 ...
+void launch_gemm_dw(const uint8_t* x8, const uint8_t* g8, int D, int Np, int64_t Tp,
                     float* part, hipStream_t s);
 // ... and are summed in split order, scaled by s_x s_g and written into the
 // three column blocks dwq [D][nq] (ldq), dwk, dwv [D][N - 2nq] (ldv).

@@ -1,7 +1,7 @@
 // Per-tensor e4m3 quantisers for gfx950: the packed weight (both cached
 // layouts from one read of W, PR #344 page, "Changes"), and bf16 activations
-// / gradients (the GEMMs' blocked row layout plus the transposed copy the dW
-// GEMM streams, both from one read).
+// / gradients (the GEMMs' blocked row layout, which all three GEMMs read:
+// forward and dX as K-contiguous rows, dW token by token).
 //
 // The scale needs the whole tensor's amax before any code can be written,
 // so each quantiser is two kernels: per-block partial amax, then quantize,
@@ -166,19 +166,16 @@ __global__ __launch_bounds__(kThreads) void quantize_w_kernel(
   }
 }
 
-// ------------------------------ bf16 rows -> e4m3, two blocked layouts
+// ------------------------------ bf16 rows -> e4m3, blocked row layout
 
-// One block per 128 tokens x 128 columns (one K block of the row layout,
-// and one K block of the transposed layout).  The source rows are the
-// tokens' first `split` columns, `split` elements apart, followed by the
-// columns of V-like head-major rows: column split + h * vw + j of token t
-// is element j of row (t / vs * vh + h) * vs + t % vs of `vsrc` (vw
-// elements per row, vh heads, sequences of vs tokens).  Thread (rg, cc)
-// owns tokens 8rg..8rg+7 and columns 8cc..8cc+7: it reads 8 x 16 bytes of bf16 and
-// writes 8 x 8 bytes of codes into the row layout (16 threads cover a
-// block row's 128 bytes), and its 8 x 8 codes go, four tokens to a dword,
-// into an LDS tile from which the transposed layout's 128-byte token runs
-// are written as 16-byte chunks.
+// One block per 128 tokens x 128 columns (one K block of the row layout).
+// The source rows are the tokens' first `split` columns, `split` elements
+// apart, followed by the columns of V-like head-major rows: column
+// split + h * vw + j of token t is element j of row
+// (t / vs * vh + h) * vs + t % vs of `vsrc` (vw elements per row, vh heads,
+// sequences of vs tokens).  Thread (rg, cc) owns tokens 8rg..8rg+7 and
+// columns 8cc..8cc+7: it reads 8 x 16 bytes of bf16 and writes 8 x 8 bytes
+// of codes (16 threads cover a block row's 128 bytes).
 struct ActSrc {
   const uint16_t* src;   // [rows][split]
   int split;
@@ -189,8 +186,7 @@ struct ActSrc {
 __global__ __launch_bounds__(kThreads) void quantize_act_kernel(
     ActSrc as, int64_t rows, int cols, const uint32_t* __restrict__ partials, int parts,
     float* __restrict__ scales, int32_t* __restrict__ status, int status_bit,
-    uint8_t* __restrict__ dst, uint8_t* __restrict__ dst_t, int64_t tokens_padded) {
-  __shared__ uint32_t tile_t[kKBlock][kKBlock / 4 + 1];  // [column][token / 4]
+    uint8_t* __restrict__ dst, int64_t tokens_padded) {
   __shared__ uint32_t red[4];
   const int64_t t0 = (int64_t)blockIdx.x * kKBlock;        // first token
   const int kb = blockIdx.y, c0 = kb * kKBlock;            // K block of the row layout
@@ -218,47 +214,21 @@ __global__ __launch_bounds__(kThreads) void quantize_act_kernel(
   }
   const float inv = tensor_scales(partials, parts, red, blockIdx.x == 0 && blockIdx.y == 0,
                                   scales, status, status_bit, false).y;
-  uint32_t codes[8][2];
+  // rows rows .. tokens_padded - 1 (zero input) are written as zero codes:
+  // the dW GEMM reads them as its K tail
 #pragma unroll
   for (int i = 0; i < 8; ++i) {
     const int64_t t = t0 + 8 * rg + i;
     const uint4 v = in[i];
-    codes[i][0] = e4m3x4(bf16_to_f32(v.x & 0xffffu) * inv, bf16_to_f32(v.x >> 16) * inv,
-                         bf16_to_f32(v.y & 0xffffu) * inv, bf16_to_f32(v.y >> 16) * inv);
-    codes[i][1] = e4m3x4(bf16_to_f32(v.z & 0xffffu) * inv, bf16_to_f32(v.z >> 16) * inv,
-                         bf16_to_f32(v.w & 0xffffu) * inv, bf16_to_f32(v.w >> 16) * inv);
-    if (t < rows) {
+    const uint32_t lo = e4m3x4(bf16_to_f32(v.x & 0xffffu) * inv, bf16_to_f32(v.x >> 16) * inv,
+                               bf16_to_f32(v.y & 0xffffu) * inv, bf16_to_f32(v.y >> 16) * inv);
+    const uint32_t hi = e4m3x4(bf16_to_f32(v.z & 0xffffu) * inv, bf16_to_f32(v.z >> 16) * inv,
+                               bf16_to_f32(v.w & 0xffffu) * inv, bf16_to_f32(v.w >> 16) * inv);
+    if (t < tokens_padded) {
       const int64_t blk = (t / kActRows) * kblocks + kb;
       *reinterpret_cast<uint2*>(dst + (blk * kActRows + t % kActRows) * kKBlock + 8 * cc) =
-          make_uint2(codes[i][0], codes[i][1]);
+          make_uint2(lo, hi);
     }
-  }
-  // column 8cc + j: tokens 8rg..8rg+3 and 8rg+4..8rg+7 as two dwords
-#pragma unroll
-  for (int j = 0; j < 8; ++j) {
-    const int w = j >> 2, sh = (j & 3) * 8;
-    uint32_t lo = 0, hi = 0;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      lo |= ((codes[i][w] >> sh) & 0xffu) << (8 * i);
-      hi |= ((codes[4 + i][w] >> sh) & 0xffu) << (8 * i);
-    }
-    tile_t[8 * cc + j][2 * rg] = lo;
-    tile_t[8 * cc + j][2 * rg + 1] = hi;
-  }
-  __syncthreads();
-  // 128 columns x 128 tokens = 128 x 8 chunks of 16 bytes; four per thread
-  const int64_t kt_blocks = tokens_padded / kKBlock, tk = t0 / kKBlock;
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int q = threadIdx.x + kThreads * i;
-    const int col = q >> 3, ch = q & 7;
-    const int cg = c0 + col;
-    if (cg >= cols) continue;
-    const uint4 o = make_uint4(tile_t[col][4 * ch], tile_t[col][4 * ch + 1],
-                               tile_t[col][4 * ch + 2], tile_t[col][4 * ch + 3]);
-    const int64_t blk = (cg / kTRows) * kt_blocks + tk;
-    *reinterpret_cast<uint4*>(dst_t + (blk * kTRows + cg % kTRows) * kKBlock + 16 * ch) = o;
   }
 }
 
@@ -301,19 +271,19 @@ void launch_quantize_w(const float* wq, int64_t ldq, const float* wk, int64_t ld
 
 void launch_quantize_act(const uint16_t* src, int64_t rows, int cols, const uint32_t* partials,
                          int parts, float* scales, int32_t* status, int status_bit, uint8_t* dst,
-                         uint8_t* dst_t, int64_t tokens_padded, hipStream_t s) {
+                         int64_t tokens_padded, hipStream_t s) {
   launch_quantize_act_split(src, cols, nullptr, 1, 1, 1, rows, cols, partials, parts, scales,
-                            status, status_bit, dst, dst_t, tokens_padded, s);
+                            status, status_bit, dst, tokens_padded, s);
 }
 
 void launch_quantize_act_split(const uint16_t* src, int split, const uint16_t* vsrc, int vw,
                                int vh, int vs, int64_t rows, int cols, const uint32_t* partials,
                                int parts, float* scales, int32_t* status, int status_bit,
-                               uint8_t* dst, uint8_t* dst_t, int64_t tokens_padded, hipStream_t s) {
+                               uint8_t* dst, int64_t tokens_padded, hipStream_t s) {
   dim3 grid((unsigned)(tokens_padded / kKBlock), (unsigned)ceil_div(cols, kKBlock));
   quantize_act_kernel<<<grid, kThreads, 0, s>>>(ActSrc{src, split, vsrc, vw, vh, vs}, rows, cols,
                                                 partials, parts, scales, status, status_bit, dst,
-                                                dst_t, tokens_padded);
+                                                tokens_padded);
 }
 
 void launch_encode(const float* in, int64_t n, float inv, uint8_t* out, hipStream_t s) {

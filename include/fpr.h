@@ -163,37 +163,30 @@ FPR_API const char* fpr_status_string(int code);
  * on its own.  The layout is private and may change between versions.
  * Offsets of (size_t)-1 mean "not present".
  *
- * The FP8 copies are stored blocked, in the order the GEMMs stream them:
- *   row-blocked [R][C] (x8, g8): blocks of act_block_rows rows x k_block
- *     bytes, block (r / act_block_rows, c / k_block) at index
- *     (r / act_block_rows) * ceil(C / k_block) + c / k_block, each block
- *     row-major with a k_block-byte row; R padded to act_block_rows and C to
- *     k_block, the padding columns zero, the padding rows undefined.
- *   transposed-blocked [C][tokens_padded] (x8t, g8t): the same with
- *     t_block_rows rows (features) x k_block tokens per block and
- *     tokens_padded / k_block blocks per block row; C padded to
- *     t_block_rows (undefined), tokens T..tokens_padded-1 zero.
+ * The FP8 copies x8 and g8 are stored blocked, in the order the GEMMs
+ * stream them: blocks of act_block_rows rows (tokens) x k_block bytes,
+ * block (r / act_block_rows, c / k_block) at index
+ * (r / act_block_rows) * ceil(C / k_block) + c / k_block, each block
+ * row-major with a k_block-byte row; C is padded to k_block with zero
+ * columns, tokens T..tokens_padded-1 are zero rows (the dW GEMM's K tail),
+ * and rows from tokens_padded to the end of the last block are undefined.
  * ------------------------------------------------------------------- */
 typedef struct fpr_layout {
     int64_t tokens;          /* T */
     int64_t tokens_padded;   /* T rounded up to k_block                     */
     /* in `saved` */
-    size_t saved_x8t;        /* [D][tokens_padded] e4m3 transposed-blocked  */
+    size_t saved_x8;         /* [T][D] e4m3 blocked                         */
     size_t saved_qk_pre;     /* [T][2*H*d_qk] bf16, pre-norm Q|K            */
     size_t saved_x_scales;   /* [2] fp32: s_x, inv_x                        */
-    /* in the forward workspace */
-    size_t fwd_x8;           /* [T][D] e4m3 row-blocked                     */
-    /* in the backward workspace */
+    /* in the backward workspace (the forward one holds only amax partials) */
     size_t bwd_dqkv;         /* [T][2*H*d_qk] bf16, Q|K part of the packed
                                 gradient (its V part is dv itself)           */
     size_t bwd_g_scales;     /* [2] fp32: s_g, inv_g                         */
-    size_t bwd_g8;           /* [T][N] e4m3 row-blocked                      */
-    size_t bwd_g8t;          /* [N][tokens_padded] e4m3 transposed-blocked   */
+    size_t bwd_g8;           /* [T][N] e4m3 blocked                          */
     size_t bwd_dw_part;      /* [dw_splits][D][N] fp32 split-K dW partials   */
     int32_t dw_splits;       /* K splits of the dW GEMM at this token count  */
     int32_t k_block;         /* bytes of K per block (128)                   */
     int32_t act_block_rows;  /* rows per block of x8 and g8 (256)            */
-    int32_t t_block_rows;    /* rows per block of x8t and g8t (192)          */
 } fpr_layout;
 
 FPR_API int fpr_get_layout(const fpr_dims* dims, int64_t tokens, fpr_layout* out);

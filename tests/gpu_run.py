@@ -45,15 +45,6 @@ def unblock_rows(buf, off: int, rows: int, cols: int, lay) -> np.ndarray:
     return a.transpose(0, 2, 1, 3).reshape(nb * R, kc * KB)
 
 
-def unblock_t(buf, off: int, cols: int, lay) -> np.ndarray:
-    """[cols_pad][tokens_padded] bytes from the transposed-blocked FP8 layout:
-    blocks of t_block_rows x k_block tokens, tokens_padded / k_block per block row."""
-    R, KB, Tp = lay.t_block_rows, lay.k_block, lay.tokens_padded
-    nb, kt = _ceil(cols, R), Tp // KB
-    a = B.view_bytes(buf, off, (nb, kt, R, KB), torch.uint8).cpu().numpy()
-    return a.transpose(0, 2, 1, 3).reshape(nb * R, kt * KB)
-
-
 def run(w: dict, seed: int = 42, x_bits=None, W=None, dy=None, backward: bool = True):
     """Pack, forward (and backward) on the GPU; returns a dict of numpy arrays."""
     n_seq, S = w["n_seq"], w["seq_len"]
@@ -82,9 +73,9 @@ def run(w: dict, seed: int = 42, x_bits=None, W=None, dy=None, backward: bool = 
     out["w_packed"] = cache.w_packed.cpu().numpy()
     out["w_packed_t"] = cache.w_packed_t.cpu().numpy()
     out["w_scales"] = cache.scales.cpu().numpy()
-    x8 = unblock_rows(ws_f, lay.fwd_x8, T, D, lay)
-    out["x8"], out["x8_kpad"] = x8[:T, :D], x8[:T, D:]
-    out["x8t"] = unblock_t(saved, lay.saved_x8t, D, lay)[:D]
+    x8 = unblock_rows(saved, lay.saved_x8, T, D, lay)
+    # x8_tail: the zero token rows T .. Tp - 1 that the dW GEMM reads as its K tail
+    out["x8"], out["x8_kpad"], out["x8_tail"] = x8[:T, :D], x8[:T, D:], x8[T:Tp]
     out["x_scales"] = B.view_bytes(saved, lay.saved_x_scales, (2,), torch.float32).cpu().numpy()
     out["qk_pre"] = dev_to_bits(B.view_bytes(saved, lay.saved_qk_pre, (T, 2 * nq), torch.bfloat16))
     out["q"], out["k"], out["v"] = dev_to_bits(q), dev_to_bits(k), dev_to_bits(v)
@@ -104,8 +95,7 @@ def run(w: dict, seed: int = 42, x_bits=None, W=None, dy=None, backward: bool = 
         out["dqkv"] = np.concatenate([dqk, dvt], axis=1)
         out["g_scales"] = B.view_bytes(ws_b, lay.bwd_g_scales, (2,), torch.float32).cpu().numpy()
         g8 = unblock_rows(ws_b, lay.bwd_g8, T, N, lay)
-        out["g8"], out["g8_kpad"] = g8[:T, :N], g8[:T, N:]
-        out["g8t"] = unblock_t(ws_b, lay.bwd_g8t, N, lay)[:N]
+        out["g8"], out["g8_kpad"], out["g8_tail"] = g8[:T, :N], g8[:T, N:], g8[T:Tp]
         out["dx"] = dev_to_bits(dx)
         out["dw"] = dw.cpu().numpy()
     out["status"] = int(cache.status.cpu().item())

@@ -99,11 +99,12 @@ def _check_forward(w, r):
     n_seq, S = w["n_seq"], w["seq_len"]
     T, H, dqk, dv = r["T"], w["n_heads"], w["d_qk"], w["d_v"]
     nqk2 = 2 * H * dqk
-    # a2: activation quantiser, both layouts, bit-exact
+    # a2: activation quantiser, bit-exact; padding columns and the token
+    # rows up to the padded count (the dW GEMM's K tail) zero
     x8, s_x, inv_x, _ = oracle.quantize_bf16(r["x_bits"])
     assert np.array_equal(r["x8"], x8) and not r["x8_kpad"].any()
     assert r["x_scales"][0] == s_x and r["x_scales"][1] == inv_x
-    assert np.array_equal(r["x8t"][:, :T], x8.T) and not r["x8t"][:, T:].any()
+    assert not r["x8_tail"].any()
     # a3: packed GEMM from the GPU's own codes
     y = oracle.gemm_e4m3(r["x8"], r["w_packed"], r["x_scales"][0], r["w_scales"][0])
     y_bits = oracle.round_bf16(y)
@@ -143,7 +144,7 @@ def _check_backward(w, r):
     g8, s_g, inv_g, _ = oracle.quantize_bf16(g)
     assert np.array_equal(r["g8"], g8) and not r["g8_kpad"].any()
     assert r["g_scales"][0] == s_g and r["g_scales"][1] == inv_g
-    assert np.array_equal(r["g8t"][:, :T], g8.T) and not r["g8t"][:, T:].any()
+    assert not r["g8_tail"].any()
     # a7, a8: GEMMs from the GPU's own codes
     dx64 = oracle.gemm_e4m3(r["g8"], np.ascontiguousarray(r["w_packed"].T), s_g, r["w_scales"][0])
     e_dx = row_rel_err(bf16_to_f64(r["dx"]), bf16_to_f64(oracle.round_bf16(dx64)))
@@ -287,7 +288,6 @@ def test_step_64k_sampled_rows():
     assert np.array_equal(r["w_packed"], wp) and np.array_equal(r["w_packed_t"], wpt)
     x8, s_x, inv_x, _ = oracle.quantize_bf16(r["x_bits"])
     assert np.array_equal(r["x8"], x8) and r["x_scales"][0] == s_x
-    assert np.array_equal(r["x8t"], x8.T)
     rng = np.random.default_rng(0)
     rows = np.unique(np.concatenate([[0, 1, T - 1], rng.choice(T, 253, replace=False)]))
     pos = rows % S
@@ -318,7 +318,6 @@ def test_step_64k_sampled_rows():
     # gradient codes in full
     g8, s_g, inv_g, _ = oracle.quantize_bf16(r["dqkv"])
     assert np.array_equal(r["g8"], g8) and r["g_scales"][0] == s_g
-    assert np.array_equal(r["g8t"], g8.T)
     # dX rows and dW rows
     dx64 = oracle.gemm_e4m3(g8[rows], np.ascontiguousarray(wp.T), s_g, s_w)
     e_dx = row_rel_err(bf16_to_f64(r["dx"][rows]), bf16_to_f64(oracle.round_bf16(dx64)))
