@@ -46,20 +46,23 @@ namespace fpr {
 typedef float v16f __attribute__((ext_vector_type(16)));
 
 constexpr int kBK = 128;  // bytes (= e4m3 elements) of K per step
-constexpr int kMmaWaves = 4, kCopyWaves = 4;
-constexpr int kGemmThreads = 64 * (kMmaWaves + kCopyWaves);
+constexpr int kCopyWaves = 4;
 constexpr int kStages = 3;
 
-template <int BM, int BN>
+// A BM x BN tile computed by MW x NW matrix waves (wave w: rows w / NW,
+// columns w % NW) and filled by kCopyWaves copy waves.
+template <int BM, int BN, int MW = 2, int NW = 2>
 struct TileCfg {
   static constexpr int BM_ = BM, BN_ = BN;
-  static constexpr int WM = BM / 2, WN = BN / 2;       // 2 x 2 matrix waves
+  static constexpr int MMA = MW * NW, NW_ = NW;
+  static constexpr int THREADS = 64 * (MMA + kCopyWaves);
+  static constexpr int WM = BM / MW, WN = BN / NW;     // one matrix wave's part
   static constexpr int FM = WM / 32, FN = WN / 32;     // 32x32 fragments per wave
   static constexpr int STAGE_BYTES = (BM + BN) * kBK;  // one K step of A and B rows
   static constexpr int BLOCKS = (BM + BN) / 8;         // 1 KiB DMA blocks per stage
   static constexpr int PER_WAVE = BLOCKS / kCopyWaves;
   static constexpr int A_PER_WAVE = BM / 8 / kCopyWaves;  // a wave's first blocks hold A rows
-  static_assert(FM * 64 == BM && FN * 64 == BN, "tile/waves");
+  static_assert(FM * 32 * MW == BM && FN * 32 * NW == BN, "tile/waves");
   static_assert(BM % 16 == 0, "B rows keep their swizzle key at stage row BM + r");
   static_assert(BLOCKS % kCopyWaves == 0 && (BM / 8) % kCopyWaves == 0, "DMA blocks per wave");
   static_assert(PER_WAVE < 64, "vmcnt range");
@@ -390,7 +393,7 @@ __device__ __forceinline__ void mma_half(v16f (&acc)[C::FM][C::FN], Half<C>& f, 
 #pragma unroll
     for (int j = 0; j < C::FN; ++j) {
       __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // 1 MFMA
-      __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);  // then up to 2 LDS reads
+      __builtin_amdgcn_sched_group_barrier(0x100, TOK ? 4 : 2, 0);  // then LDS reads
     }
   }
 #pragma unroll
@@ -408,9 +411,10 @@ template <class C, bool TOK>
 __device__ __forceinline__ void mma_half_barrier(v16f (&acc)[C::FM][C::FN], Half<C>& f,
                                                  const uint8_t* src, int a0, int b0, int lane,
                                                  int h) {
-  static_assert(kEarlyRows < C::FM, "rows after the barrier");
+  constexpr int ER = kEarlyRows < C::FM ? kEarlyRows : C::FM - 1;  // rows before the barrier
+  static_assert(ER >= 1, "rows on both sides of the barrier");
 #pragma unroll
-  for (int i = 0; i < kEarlyRows; ++i)
+  for (int i = 0; i < ER; ++i)
 #pragma unroll
     for (int j = 0; j < C::FN; ++j) acc[i][j] = mfma32(f.b[j], f.a[i], acc[i][j]);
   // scheduling fences: the barrier orders memory accesses only, and the
@@ -422,16 +426,16 @@ __device__ __forceinline__ void mma_half_barrier(v16f (&acc)[C::FM][C::FN], Half
 #pragma unroll
   for (int j = 0; j < C::FN; ++j) nb[j] = frag_b<C, TOK>(src, b0 + j * 32, lane, h);
 #pragma unroll
-  for (int i = 0; i < kEarlyRows; ++i) f.a[i] = frag_a<C, TOK>(src, a0 + i * 32, lane, h);
+  for (int i = 0; i < ER; ++i) f.a[i] = frag_a<C, TOK>(src, a0 + i * 32, lane, h);
 #pragma unroll
-  for (int i = kEarlyRows; i < C::FM; ++i) {
+  for (int i = ER; i < C::FM; ++i) {
 #pragma unroll
     for (int j = 0; j < C::FN; ++j) acc[i][j] = mfma32(f.b[j], f.a[i], acc[i][j]);
     f.a[i] = frag_a<C, TOK>(src, a0 + i * 32, lane, h);
 #pragma unroll
     for (int j = 0; j < C::FN; ++j) {
       __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // 1 MFMA
-      __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);  // then up to 2 LDS reads
+      __builtin_amdgcn_sched_group_barrier(0x100, TOK ? 4 : 2, 0);  // then LDS reads
     }
   }
 #pragma unroll
@@ -647,11 +651,11 @@ __device__ __forceinline__ void persistent_tiles(Sched& sc, int b, int G, int nt
 }
 
 template <int BM, int BN, bool KTAIL, class Epi>
-__global__ __launch_bounds__(kGemmThreads, 1) void gemm_bf16out_kernel(
+__global__ __launch_bounds__((TileCfg<BM, BN>::THREADS), 1) void gemm_bf16out_kernel(
     Gemm gm, int ntiles, const float* __restrict__ sa, const float* __restrict__ sb, Epi epi) {
   using C = TileCfg<BM, BN>;
   __shared__ __attribute__((aligned(16))) uint8_t lds[kStages * C::STAGE_BYTES];
-  __shared__ __attribute__((aligned(16))) uint8_t slices[kMmaWaves * WaveSlice<C>::BYTES];
+  __shared__ __attribute__((aligned(16))) uint8_t slices[C::MMA * WaveSlice<C>::BYTES];
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int G = gridDim.x;
@@ -659,11 +663,11 @@ __global__ __launch_bounds__(kGemmThreads, 1) void gemm_bf16out_kernel(
   sc.nk = (gm.K + kBK - 1) / kBK;
   sc.ks0 = 0;
   persistent_tiles(sc, blockIdx.x, G, ntiles, gm.n_tiles);
-  if (wave >= kMmaWaves) {
-    copy_role<C, KTAIL>(lds, gm, sc, wave - kMmaWaves, lane);
+  if (wave >= C::MMA) {
+    copy_role<C, KTAIL>(lds, gm, sc, wave - C::MMA, lane);
     return;
   }
-  const int wm = wave >> 1, wn = wave & 1;
+  const int wm = wave / C::NW_, wn = wave % C::NW_;
   const float alpha = sa[0] * sb[0];
   uint8_t* slice = slices + wave * WaveSlice<C>::BYTES;
   int ord = 0;
@@ -682,15 +686,17 @@ __global__ __launch_bounds__(kGemmThreads, 1) void gemm_bf16out_kernel(
 // so the blocks of one XCD share K ranges and rows of both operands in its
 // L2.  Unscaled fp32 partial sums go to part[split][m][n]; a split with no
 // K steps writes zeros.
-template <int BM, int BN>
-__global__ __launch_bounds__(kGemmThreads, 1) void gemm_dw_part_kernel(
+template <int BM, int BN, int MW, int NW>
+__global__ __launch_bounds__((TileCfg<BM, BN, MW, NW>::THREADS), 1) void gemm_dw_part_kernel(
     Gemm gm, int splits, int ksteps_per_split, float* __restrict__ part) {
-  using C = TileCfg<BM, BN>;
+  using C = TileCfg<BM, BN, MW, NW>;
   __shared__ __attribute__((aligned(16))) uint8_t lds[kStages * C::STAGE_BYTES];
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int G = gridDim.x, b = blockIdx.x, tiles = G / splits;
-  const int item = G % 8 == 0 ? (b % 8) * (G / 8) + b / 8 : b;
+  // blocks go round-robin over the 8 XCDs: XCD x holds blocks x, x + 8, ...
+  // and takes the items from x * (G / 8) + min(x, G % 8) on, in order
+  const int x = b % 8, item = x * (G / 8) + min(x, G % 8) + b / 8;
   const int split = item / tiles, tile = item - split * tiles;
   const int nk_all = (gm.K + kBK - 1) / kBK;
   Sched sc;
@@ -698,11 +704,11 @@ __global__ __launch_bounds__(kGemmThreads, 1) void gemm_dw_part_kernel(
   sc.steps = max(0, min(nk_all, sc.ks0 + ksteps_per_split) - sc.ks0);
   sc.nk = sc.steps > 0 ? sc.steps : 1;
   sc.single = tile;
-  if (wave >= kMmaWaves) {
-    copy_role<C, false>(lds, gm, sc, wave - kMmaWaves, lane);
+  if (wave >= C::MMA) {
+    copy_role<C, false>(lds, gm, sc, wave - C::MMA, lane);
     return;
   }
-  const int wm = wave >> 1, wn = wave & 1;
+  const int wm = wave / C::NW_, wn = wave % C::NW_;
   v16f acc[C::FM][C::FN];
   mma_role<C, true, false>(lds, sc, wm, wn, lane, acc, [](v16f (&)[C::FM][C::FN]) {});
   store_partial_tile<C>(acc, part + (int64_t)split * gm.M * gm.N, gm.M, gm.N,
@@ -734,7 +740,9 @@ __global__ __launch_bounds__(kThreads) void dw_reduce_kernel(
 // ------------------------------------------------------------- launchers
 
 constexpr int kBMo = 256, kBNo = 128;  // bf16-output tile (persistent)
-constexpr int kBMw = 256, kBNw = 128;  // dW split-K tile (token-major operands)
+// dW split-K tile (token-major operands), 2 x 2 matrix waves of 128 x 64
+// (4 x 2 waves of 64 x 64, two per SIMD, measured the same)
+constexpr int kBMw = 256, kBNw = 128, kMWw = 2, kNWw = 2;
 // Split-K counts are chosen for a 256-CU part; the choice must not depend on
 // the device present, since workspace sizes are queried without one.
 constexpr int kSplitCUs = 256, kMaxSplits = 8;
@@ -755,10 +763,10 @@ static void launch_bf16out(const Gemm& gm, const float* sa, const float* sb, con
   const int cus = cu_count();
   const int blocks = ntiles < cus ? ntiles : cus;
   if (gm.K % kBK)
-    gemm_bf16out_kernel<kBMo, kBNo, true, Epi><<<blocks, kGemmThreads, 0, s>>>(gm, ntiles, sa,
+    gemm_bf16out_kernel<kBMo, kBNo, true, Epi><<<blocks, TileCfg<kBMo, kBNo>::THREADS, 0, s>>>(gm, ntiles, sa,
                                                                               sb, epi);
   else
-    gemm_bf16out_kernel<kBMo, kBNo, false, Epi><<<blocks, kGemmThreads, 0, s>>>(gm, ntiles, sa,
+    gemm_bf16out_kernel<kBMo, kBNo, false, Epi><<<blocks, TileCfg<kBMo, kBNo>::THREADS, 0, s>>>(gm, ntiles, sa,
                                                                                sb, epi);
 }
 
@@ -805,7 +813,8 @@ void launch_gemm_dw(const uint8_t* x8, const uint8_t* g8, int D, int Np, int64_t
   const Gemm gm{x8, ceil_div(D, kKBlock), g8, ceil_div(Np, kKBlock), D, Np, (int)Tp,
                 (int)ceil_div(Np, kBNw), 0, 0, 1};
   const int blocks = (int)ceil_div(D, kBMw) * gm.n_tiles * splits;
-  gemm_dw_part_kernel<kBMw, kBNw><<<blocks, kGemmThreads, 0, s>>>(gm, splits, per, part);
+  gemm_dw_part_kernel<kBMw, kBNw, kMWw, kNWw>
+      <<<blocks, TileCfg<kBMw, kBNw, kMWw, kNWw>::THREADS, 0, s>>>(gm, splits, per, part);
 }
 
 void launch_dw_reduce(const float* part, int D, int Np, int64_t Tp, const float* x_scales,
