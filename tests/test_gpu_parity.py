@@ -2,7 +2,8 @@
 
 Stage-wise: every GPU stage is compared with the oracle's stage fed the
 GPU's own inputs to that stage.  Bars:
-  * FP8 codes and scales, the transposed copies, the V relayout: bit-exact;
+  * FP8 codes and scales, the zero token rows padding the FP8 copies to a
+    whole K step, the V relayout: bit-exact;
   * GEMM outputs: the accumulated product must be within 1e-3 per row norm.
     dW is fp32 and is compared directly: ||gpu - oracle|| / ||oracle|| <= 1e-3
     per row.  The projection Y and dX are rounded to bf16, whose own rounding
@@ -329,3 +330,71 @@ def test_step_64k_sampled_rows():
         f"dx {e_dx:.2e} dw {e_dw:.2e}")
     assert over_gemm <= GEMM_TOL and over_dx <= GEMM_TOL and e_dw <= GEMM_TOL
     assert max(e_q, e_k, e_dq, e_dk) <= NORM_TOL
+
+
+# ------------------------------------------- exact GEMMs (integer inputs)
+
+def _int_values(rng, shape):
+    return rng.integers(-2, 3, size=shape).astype(np.float32)
+
+
+def test_gemms_bit_exact_on_integer_inputs():
+    """Small integers plus one 448 in each tensor make every scale exactly 1,
+    every code exact and every product sum an integer far below 2^14, so the
+    forward projection, dX and dW must equal the oracle's bit for bit
+    (integer brute force through the whole C interface)."""
+    w = dict(n_seq=2, seq_len=192, d_model=256, n_heads=2, d_qk=96, d_v=128)
+    dims = _dims(w)
+    n_seq, S, D, H = w["n_seq"], w["seq_len"], w["d_model"], w["n_heads"]
+    T, N, nq = n_seq * S, inputs.packed_width(w), H * w["d_qk"]
+    rng = np.random.default_rng(7)
+    x = _int_values(rng, (T, D))
+    x[0, 0] = 448.0
+    W = _int_values(rng, (D, N))
+    W[1, 0] = 448.0
+    dv = _int_values(rng, (n_seq, H, S, w["d_v"]))
+    dv[0, 0, 1, 0] = 448.0  # token 1: its x row holds no 448
+    zero = np.zeros((n_seq, H, S, w["d_qk"]), dtype=np.float32)
+    dy = tuple(inputs.f32_to_bf16_bits(a) for a in (zero, zero, dv))
+    r = run(w, seed=7, x_bits=inputs.f32_to_bf16_bits(x), W=W, dy=dy)
+    assert r["status"] == 0
+    assert r["x_scales"][0] == 1.0 and r["w_scales"][0] == 1.0 and r["g_scales"][0] == 1.0
+    wp, _, s_w, _, _ = oracle.pack_quantize_weights(dims, W)
+    x8, s_x, _, _ = oracle.quantize_bf16(r["x_bits"])
+    y = oracle.round_bf16(oracle.gemm_e4m3(x8, wp, s_x, s_w))
+    assert np.array_equal(r["qk_pre"], y[:, :2 * nq])
+    assert np.array_equal(r["v"], oracle.to_head_major(y[:, 2 * nq:].reshape(T, H, -1), n_seq, S))
+    # zero upstream q, k gradients: dQKV = [0 | dv]
+    assert not bf16_to_f64(r["dqkv"][:, :2 * nq]).any()  # zeros of either sign
+    g8, s_g, _, _ = oracle.quantize_bf16(r["dqkv"])
+    dx = oracle.round_bf16(oracle.gemm_e4m3(g8, np.ascontiguousarray(wp.T), s_g, s_w))
+    assert np.array_equal(r["dx"], dx)
+    dw = oracle.round_f32(oracle.gemm_e4m3(np.ascontiguousarray(x8.T), g8, s_x, s_g))
+    assert np.array_equal(r["dw"], dw)
+
+
+def test_all_codes_through_the_forward_gemm():
+    """x holds every finite e4m3 value (scale 1: 448 is among them) and W is
+    the identity plus one 448 that fixes its scale at 1: the projection's
+    first D columns are the decoded codes themselves, so the matrix cores'
+    reading of every code, subnormals included, is checked bit for bit."""
+    w = inputs.WORKLOADS["tiny"]
+    dims = _dims(w)
+    T, D, N = w["n_seq"] * w["seq_len"], w["d_model"], inputs.packed_width(w)
+    codes = np.array([c for c in range(256) if c not in (0x7F, 0xFF)], dtype=np.uint8)
+    vals = oracle.e4m3_decode(np.resize(codes, T * D)).reshape(T, D).astype(np.float32)
+    x_bits = inputs.f32_to_bf16_bits(vals)
+    assert np.array_equal(oracle.bf16_to_f64(x_bits), vals)  # every e4m3 value is a bf16 value
+    W = np.zeros((D, N), dtype=np.float32)
+    W[np.arange(D), np.arange(D)] = 1.0
+    W[0, N - 1] = 448.0
+    r = run(w, seed=7, x_bits=x_bits, W=W, backward=False)
+    assert r["x_scales"][0] == 1.0 and r["w_scales"][0] == 1.0
+    assert np.array_equal(r["x8"], np.resize(codes, T * D).reshape(T, D))
+    wp, _, s_w, _, _ = oracle.pack_quantize_weights(dims, W)
+    y = oracle.round_bf16(oracle.gemm_e4m3(r["x8"], wp, 1.0, s_w))
+    nqk2 = 2 * w["n_heads"] * w["d_qk"]
+    gpu_y = np.concatenate([r["qk_pre"], oracle.from_head_major(r["v"]).reshape(T, -1)], axis=1)
+    assert np.array_equal(gpu_y, y)
+    # the identity columns reproduce the decode table (signed zeros add to +0)
+    assert np.array_equal(oracle.bf16_to_f64(gpu_y[:, :D]), vals + 0.0)
