@@ -29,11 +29,17 @@ class FprError(RuntimeError):
 class Dims(ctypes.Structure):
     _fields_ = [("d_model", ctypes.c_int32), ("n_heads", ctypes.c_int32),
                 ("d_qk", ctypes.c_int32), ("d_v", ctypes.c_int32),
-                ("eps", ctypes.c_float), ("rope_base", ctypes.c_float)]
+                ("eps", ctypes.c_float), ("rope_base", ctypes.c_float),
+                ("qk_stride", ctypes.c_int32)]
 
     @property
     def n_packed(self) -> int:
         return self.n_heads * (2 * self.d_qk + self.d_v)
+
+    @property
+    def qk_row(self) -> int:
+        """Row stride of the q/k/dq/dk heads (d_qk unless padded)."""
+        return self.qk_stride or self.d_qk
 
     @property
     def n_q(self) -> int:
@@ -113,8 +119,9 @@ def status_string(code: int) -> str:
 
 
 def make_dims(d_model: int, n_heads: int, d_qk: int = 96, d_v: int = 128,
-              eps: float = 1e-6, rope_base: float = 10000.0) -> Dims:
-    return Dims(d_model, n_heads, d_qk, d_v, eps, rope_base)
+              eps: float = 1e-6, rope_base: float = 10000.0, qk_stride: int = 0) -> Dims:
+    """qk_stride > d_qk pads every q/k head row with zeros to that width."""
+    return Dims(d_model, n_heads, d_qk, d_v, eps, rope_base, qk_stride)
 
 
 def workspace_bytes(dims: Dims, tokens: int, which: int) -> int:
@@ -196,7 +203,7 @@ def qkv_forward(dims: Dims, n_seq: int, seq_len: int, x, cache: WeightCache, q=N
                 v=None, saved=None, workspace=None):
     """Returns (q, k, v, saved)."""
     T = n_seq * seq_len
-    H, dqk, dv = dims.n_heads, dims.d_qk, dims.d_v
+    H, dqk, dv = dims.n_heads, dims.qk_row, dims.d_v
     dev = x.device
     _need(x, torch.bfloat16, (T, dims.d_model), "x")
     if q is None:
@@ -227,7 +234,7 @@ def qkv_backward(dims: Dims, n_seq: int, seq_len: int, dq, dk, dv, saved, cache:
     """Returns (dx, dw) with dw the [D][N] packed fp32 gradient whose column
     blocks [:nq], [nq:2nq], [2nq:] are dW_q, dW_k, dW_v."""
     T = n_seq * seq_len
-    H, dqk, dvw, D, N, nq = dims.n_heads, dims.d_qk, dims.d_v, dims.d_model, dims.n_packed, dims.n_q
+    H, dqk, dvw, D, N, nq = dims.n_heads, dims.qk_row, dims.d_v, dims.d_model, dims.n_packed, dims.n_q
     dev = dq.device
     _need(dq, torch.bfloat16, (n_seq, H, seq_len, dqk), "dq")
     _need(dk, torch.bfloat16, (n_seq, H, seq_len, dqk), "dk")

@@ -22,7 +22,7 @@ using fpr::kMaxTokens;
 constexpr size_t kMaxDynLds = 64 * 1024;  // dynamic LDS of one epilogue block
 
 struct Plan {
-  int D, H, dqk, dv, nq, nqk2, N;
+  int D, H, dqk, dv, qs, nq, nqk2, N;
   int64_t T, Tp;
   size_t s_x8, s_qk, s_xsc, saved_total;
   size_t f_part, fwd_total;
@@ -36,6 +36,7 @@ bool dims_ok(const fpr_dims* d) {
   if (!d) return false;
   if (d->d_model <= 0 || d->n_heads <= 0 || d->d_qk <= 0 || d->d_v <= 0) return false;
   if (!(d->eps >= 0.0f) || !(d->rope_base > 0.0f)) return false;
+  if (d->qk_stride < 0) return false;
   return true;
 }
 
@@ -45,6 +46,8 @@ int shape_check(const fpr_dims* d) {
   if (d->d_model % 64 || d->d_qk % 16 || d->d_v % 16 || N % 64) return FPR_ERR_SHAPE;
   if (d->n_heads > 64 || d->d_qk > 512 || d->d_v > 4096 || N > (1 << 20) ||
       d->d_model > (1 << 16))
+    return FPR_ERR_SHAPE;
+  if (d->qk_stride && (d->qk_stride < d->d_qk || d->qk_stride % 8 || d->qk_stride > 1024))
     return FPR_ERR_SHAPE;
   if (fpr::norm_rope_fwd_lds(d->n_heads, d->d_qk) > kMaxDynLds ||
       fpr::norm_rope_bwd_lds(d->n_heads, d->d_qk) > kMaxDynLds)
@@ -64,6 +67,7 @@ Plan make_plan(const fpr_dims* d, int64_t T) {
   p.H = d->n_heads;
   p.dqk = d->d_qk;
   p.dv = d->d_v;
+  p.qs = d->qk_stride ? d->qk_stride : d->d_qk;
   p.nq = p.H * p.dqk;
   p.nqk2 = 2 * p.nq;
   p.N = p.nqk2 + p.H * p.dv;
@@ -247,7 +251,8 @@ int qkv_forward(const fpr_dims* dims, int32_t n_seq, int32_t seq_len, const uint
                          p.nqk2, v, p.H, p.dv, seq_len, s);
   });
   stage("norm_rope_fwd", s, [&] {
-    fpr::launch_norm_rope_fwd(qk, T, seq_len, p.H, p.dqk, dims->eps, dims->rope_base, q, k, s);
+    fpr::launch_norm_rope_fwd(qk, T, seq_len, p.H, p.dqk, p.qs, dims->eps, dims->rope_base, q, k,
+                              s);
   });
   return finish();
 }
@@ -280,7 +285,7 @@ int qkv_backward(const fpr_dims* dims, int32_t n_seq, int32_t seq_len, const uin
   uint8_t* g8 = at<uint8_t>(workspace, p.b_g8);
   float* dwpart = at<float>(workspace, p.b_dwpart);
   stage("norm_rope_bwd", s, [&] {
-    fpr::launch_norm_rope_bwd(dq, dk, dv, qk, T, seq_len, p.H, p.dqk, p.dv, dims->eps,
+    fpr::launch_norm_rope_bwd(dq, dk, dv, qk, T, seq_len, p.H, p.dqk, p.qs, p.dv, dims->eps,
                               dims->rope_base, dqkv, parts, s);
   });
   stage("quantize_g", s, [&] {

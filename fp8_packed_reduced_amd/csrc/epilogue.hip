@@ -4,7 +4,9 @@
 // rope(q), rope(k); PR #344 page, "Changes": norm, RoPE and layout
 // conversion fused, lane swaps kept in registers): pre-norm Q|K rows ->
 // u = a / sqrt(mean(a^2) + eps) -> rotate pairs (i, i + d/2) by
-// p * base^(-2i/d) -> head-major q, k.
+// p * base^(-2i/d) -> head-major q, k, whose rows may be padded with zeros
+// to a stride qs > d for an attention kernel that wants equal Q/K/V widths
+// (the FA3 padding of the PR #344 page, "Changes").
 //
 // Backward ("Where the eight seconds were hiding", "The inventory": the norm,
 // RoPE and backward shuffles): du = R_{-p} dq; da = rho * (du - u <u,du>/d)
@@ -197,7 +199,8 @@ __device__ __forceinline__ void qc_fwd_load(QcFwdRow<D>& r, int row, int rows, i
 template <int D>
 __device__ __forceinline__ void qc_fwd_finish(const QcFwdRow<D>& r, const float2* cs,
                                               const int64_t* bq, const int* sp, int H,
-                                              int seq_len, float eps, uint16_t* __restrict__ q,
+                                              int seq_len, int qs, float eps,
+                                              uint16_t* __restrict__ q,
                                               uint16_t* __restrict__ k, int l) {
   using Q = QuadChunks<D>;
   constexpr int h = Q::h, M = Q::M, HC = Q::HC;
@@ -215,7 +218,7 @@ __device__ __forceinline__ void qc_fwd_finish(const QcFwdRow<D>& r, const float2
   uint4 par[M];
   quad_partners<D>(r.own, par, l);
   const int tt = r.tt, rr = r.rr, hh = rr < H ? rr : rr - H;
-  uint16_t* dst = (rr < H ? q : k) + ((bq[tt] * H + hh) * seq_len + sp[tt]) * D;
+  uint16_t* dst = (rr < H ? q : k) + ((bq[tt] * H + hh) * seq_len + sp[tt]) * qs;
 #pragma unroll
   for (int m = 0; m < M; ++m) {
     const int c = Q::chunk(l, m);
@@ -231,12 +234,15 @@ __device__ __forceinline__ void qc_fwd_finish(const QcFwdRow<D>& r, const float2
     }
     *reinterpret_cast<uint4*>(dst + 8 * c) = pack8_rn(o);
   }
+  // zero padding chunks CH .. qs / 8 - 1, dealt round the quad like the row's
+  for (int c = Q::CH + l; c < qs / 8; c += 4)
+    *reinterpret_cast<uint4*>(dst + 8 * c) = make_uint4(0, 0, 0, 0);
 }
 
 template <int D>
 __global__ __launch_bounds__(kThreads) void norm_rope_fwd_qc(
-    const uint16_t* __restrict__ qk_pre, int64_t T, int seq_len, int H, float eps, float base,
-    uint16_t* __restrict__ q, uint16_t* __restrict__ k) {
+    const uint16_t* __restrict__ qk_pre, int64_t T, int seq_len, int H, int qs, float eps,
+    float base, uint16_t* __restrict__ q, uint16_t* __restrict__ k) {
   using Q = QuadChunks<D>;
   constexpr int h = Q::h, QUADS = kThreads / 4;
   __shared__ double rev[h];
@@ -255,8 +261,8 @@ __global__ __launch_bounds__(kThreads) void norm_rope_fwd_qc(
       QcFwdRow<D> r0, r1;  // two rows' loads in flight per thread
       qc_fwd_load<D>(r0, row, rows, R, t0, qk_pre, l);
       qc_fwd_load<D>(r1, row + QUADS, rows, R, t0, qk_pre, l);
-      qc_fwd_finish<D>(r0, cs, bq, sp, H, seq_len, eps, q, k, l);
-      qc_fwd_finish<D>(r1, cs, bq, sp, H, seq_len, eps, q, k, l);
+      qc_fwd_finish<D>(r0, cs, bq, sp, H, seq_len, qs, eps, q, k, l);
+      qc_fwd_finish<D>(r1, cs, bq, sp, H, seq_len, qs, eps, q, k, l);
     }
     __syncthreads();
   }
@@ -273,7 +279,7 @@ struct QcBwdRow {
 // sequence t / seq_len.
 template <int D>
 __device__ __forceinline__ void qc_bwd_load(QcBwdRow<D>& r, int row, int rows, int R, int H,
-                                            int seq_len, int64_t t0,
+                                            int seq_len, int qs, int64_t t0,
                                             const uint16_t* __restrict__ dq,
                                             const uint16_t* __restrict__ dk,
                                             const uint16_t* __restrict__ qk_pre, int l) {
@@ -285,7 +291,7 @@ __device__ __forceinline__ void qc_bwd_load(QcBwdRow<D>& r, int row, int rows, i
   r.rr = rr;
   const int t = (int)t0 + tt, b = t / seq_len, sp = t - b * seq_len;
   const uint16_t* asrc = qk_pre + ((t0 + tt) * R + rr) * D;
-  const uint16_t* gsrc = (rr < H ? dq : dk) + (((int64_t)b * H + hh) * seq_len + sp) * D;
+  const uint16_t* gsrc = (rr < H ? dq : dk) + (((int64_t)b * H + hh) * seq_len + sp) * qs;
 #pragma unroll
   for (int m = 0; m < Q::M; ++m) {
     r.a[m] = *reinterpret_cast<const uint4*>(asrc + 8 * Q::chunk(l, m));
@@ -368,7 +374,7 @@ template <int D>
 __global__ __launch_bounds__(kThreads) void norm_rope_bwd_qc(
     const uint16_t* __restrict__ dq, const uint16_t* __restrict__ dk,
     const uint16_t* __restrict__ dv, const uint16_t* __restrict__ qk_pre, int64_t T,
-    int seq_len, int H, int dvw, float eps, float base, uint16_t* __restrict__ dqkv,
+    int seq_len, int H, int qs, int dvw, float eps, float base, uint16_t* __restrict__ dqkv,
     uint32_t* __restrict__ partials) {
   using Q = QuadChunks<D>;
   constexpr int h = Q::h, QUADS = kThreads / 4, RB = bwd_rows<D>();
@@ -394,7 +400,8 @@ __global__ __launch_bounds__(kThreads) void norm_rope_bwd_qc(
       QcBwdRow<D> r[RB];
 #pragma unroll
       for (int j = 0; j < RB; ++j)
-        qc_bwd_load<D>(r[j], rb + quad + j * QUADS, rows, R, H, seq_len, t0, dq, dk, qk_pre, l);
+        qc_bwd_load<D>(r[j], rb + quad + j * QUADS, rows, R, H, seq_len, qs, t0, dq, dk, qk_pre,
+                       l);
       if (rb == 0) {  // the same for every thread: rows > 0
         quad_table(cs, bq, sp, rev, t0, nt, h, seq_len);
         __syncthreads();
@@ -417,8 +424,8 @@ __global__ __launch_bounds__(kThreads) void norm_rope_bwd_qc(
 
 template <int TT>
 __global__ __launch_bounds__(kThreads) void norm_rope_fwd_kernel(
-    const uint16_t* __restrict__ qk_pre, int64_t T, int seq_len, int H, int d, float eps,
-    float base, uint16_t* __restrict__ q, uint16_t* __restrict__ k) {
+    const uint16_t* __restrict__ qk_pre, int64_t T, int seq_len, int H, int d, int qs,
+    float eps, float base, uint16_t* __restrict__ q, uint16_t* __restrict__ k) {
   extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
   const int h = d / 2, C = h / 8, R = 2 * H, rowlen = R * d;
   const int items = TT * R * C;
@@ -468,10 +475,20 @@ __global__ __launch_bounds__(kThreads) void norm_rope_fwd_kernel(
       ob[j] = ub * cn + ua * sn;
     }
     const int64_t bseq = t / seq_len, s = t - bseq * seq_len;
-    uint16_t* dst = rr < H ? q + ((bseq * H + rr) * seq_len + s) * d
-                           : k + ((bseq * H + (rr - H)) * seq_len + s) * d;
+    uint16_t* dst = rr < H ? q + ((bseq * H + rr) * seq_len + s) * qs
+                           : k + ((bseq * H + (rr - H)) * seq_len + s) * qs;
     *reinterpret_cast<uint4*>(dst + 8 * c) = pack8(oa);
     *reinterpret_cast<uint4*>(dst + h + 8 * c) = pack8(ob);
+  }
+  // zero padding columns d .. qs - 1 of every row
+  const int pc = (qs - d) / 8, pitems = TT * R * pc;
+  for (int it = threadIdx.x; it < pitems; it += kThreads) {
+    const int c = it % pc, rr = (it / pc) % R, tt = it / (pc * R);
+    const int64_t t = t0 + tt;
+    if (t >= T) continue;
+    const int64_t bseq = t / seq_len, s = t - bseq * seq_len;
+    uint16_t* dst = (rr < H ? q : k) + ((bseq * H + (rr < H ? rr : rr - H)) * seq_len + s) * qs;
+    *reinterpret_cast<uint4*>(dst + d + 8 * c) = make_uint4(0, 0, 0, 0);
   }
 }
 
@@ -481,8 +498,8 @@ template <int TT>
 __global__ __launch_bounds__(kThreads) void norm_rope_bwd_kernel(
     const uint16_t* __restrict__ dq, const uint16_t* __restrict__ dk,
     const uint16_t* __restrict__ dv, const uint16_t* __restrict__ qk_pre, int64_t T,
-    int seq_len, int H, int d, int dvw, float eps, float base, uint16_t* __restrict__ dqkv,
-    uint32_t* __restrict__ partials) {
+    int seq_len, int H, int d, int qs, int dvw, float eps, float base,
+    uint16_t* __restrict__ dqkv, uint32_t* __restrict__ partials) {
   extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
   __shared__ uint32_t red[4];
   const int h = d / 2, C = h / 8, R = 2 * H, qkw = R * d;
@@ -504,8 +521,8 @@ __global__ __launch_bounds__(kThreads) void norm_rope_bwd_kernel(
       alo = *reinterpret_cast<const uint4*>(arow + 8 * c);
       ahi = *reinterpret_cast<const uint4*>(arow + h + 8 * c);
       const int64_t bseq = t / seq_len, s = t - bseq * seq_len;
-      const uint16_t* grow = rr < H ? dq + ((bseq * H + rr) * seq_len + s) * d
-                                    : dk + ((bseq * H + (rr - H)) * seq_len + s) * d;
+      const uint16_t* grow = rr < H ? dq + ((bseq * H + rr) * seq_len + s) * qs
+                                    : dk + ((bseq * H + (rr - H)) * seq_len + s) * qs;
       glo = *reinterpret_cast<const uint4*>(grow + 8 * c);
       ghi = *reinterpret_cast<const uint4*>(grow + h + 8 * c);
     }
@@ -596,26 +613,27 @@ size_t norm_rope_bwd_lds(int H, int d) {
   return items * (64 + 8) + (size_t)kBwdTT * (d / 2) * 8;
 }
 
-void launch_norm_rope_fwd(const uint16_t* qk_pre, int64_t T, int seq_len, int H, int d, float eps,
-                          float base, uint16_t* q, uint16_t* k, hipStream_t s) {
+void launch_norm_rope_fwd(const uint16_t* qk_pre, int64_t T, int seq_len, int H, int d, int qs,
+                          float eps, float base, uint16_t* q, uint16_t* k, hipStream_t s) {
   const unsigned grid =
       (unsigned)std::min<int64_t>(kQuadTileBlocks, std::max<int64_t>(1, ceil_div(T, kQuadTT)));
   switch (d) {
     case 64:
-      norm_rope_fwd_qc<64><<<grid, kThreads, 0, s>>>(qk_pre, T, seq_len, H, eps, base, q, k);
+      norm_rope_fwd_qc<64><<<grid, kThreads, 0, s>>>(qk_pre, T, seq_len, H, qs, eps, base, q, k);
       return;
     case 96:
-      norm_rope_fwd_qc<96><<<grid, kThreads, 0, s>>>(qk_pre, T, seq_len, H, eps, base, q, k);
+      norm_rope_fwd_qc<96><<<grid, kThreads, 0, s>>>(qk_pre, T, seq_len, H, qs, eps, base, q, k);
       return;
     case 128:
-      norm_rope_fwd_qc<128><<<grid, kThreads, 0, s>>>(qk_pre, T, seq_len, H, eps, base, q, k);
+      norm_rope_fwd_qc<128><<<grid, kThreads, 0, s>>>(qk_pre, T, seq_len, H, qs, eps, base, q,
+                                                       k);
       return;
     default:
       break;
   }
   const size_t lds = norm_rope_fwd_lds(H, d);
   norm_rope_fwd_kernel<kFwdTT><<<(unsigned)ceil_div(T, kFwdTT), kThreads, lds, s>>>(
-      qk_pre, T, seq_len, H, d, eps, base, q, k);
+      qk_pre, T, seq_len, H, d, qs, eps, base, q, k);
 }
 
 int norm_rope_bwd_blocks(int64_t T, int H, int d) {
@@ -626,29 +644,29 @@ int norm_rope_bwd_blocks(int64_t T, int H, int d) {
 }
 
 void launch_norm_rope_bwd(const uint16_t* dq, const uint16_t* dk, const uint16_t* dv,
-                          const uint16_t* qk_pre, int64_t T, int seq_len, int H, int d, int d_v,
-                          float eps, float base, uint16_t* dqkv, uint32_t* partials,
+                          const uint16_t* qk_pre, int64_t T, int seq_len, int H, int d, int qs,
+                          int d_v, float eps, float base, uint16_t* dqkv, uint32_t* partials,
                           hipStream_t s) {
   const unsigned grid = (unsigned)norm_rope_bwd_blocks(T, H, d);
   switch (d) {
     case 64:
-      norm_rope_bwd_qc<64><<<grid, kThreads, 0, s>>>(dq, dk, dv, qk_pre, T, seq_len, H, d_v, eps,
-                                                        base, dqkv, partials);
+      norm_rope_bwd_qc<64><<<grid, kThreads, 0, s>>>(dq, dk, dv, qk_pre, T, seq_len, H, qs, d_v,
+                                                        eps, base, dqkv, partials);
       return;
     case 96:
-      norm_rope_bwd_qc<96><<<grid, kThreads, 0, s>>>(dq, dk, dv, qk_pre, T, seq_len, H, d_v, eps,
-                                                        base, dqkv, partials);
+      norm_rope_bwd_qc<96><<<grid, kThreads, 0, s>>>(dq, dk, dv, qk_pre, T, seq_len, H, qs, d_v,
+                                                        eps, base, dqkv, partials);
       return;
     case 128:
-      norm_rope_bwd_qc<128><<<grid, kThreads, 0, s>>>(dq, dk, dv, qk_pre, T, seq_len, H, d_v,
-                                                         eps, base, dqkv, partials);
+      norm_rope_bwd_qc<128><<<grid, kThreads, 0, s>>>(dq, dk, dv, qk_pre, T, seq_len, H, qs,
+                                                         d_v, eps, base, dqkv, partials);
       return;
     default:
       break;
   }
   const size_t lds = norm_rope_bwd_lds(H, d);
   norm_rope_bwd_kernel<kBwdTT><<<grid, kThreads, lds, s>>>(dq, dk, dv, qk_pre, T, seq_len, H, d,
-                                                          d_v, eps, base, dqkv, partials);
+                                                          qs, d_v, eps, base, dqkv, partials);
 }
 
 }  // namespace fpr

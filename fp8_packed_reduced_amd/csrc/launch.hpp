@@ -105,17 +105,20 @@ size_t norm_rope_fwd_lds(int H, int d_qk);
 size_t norm_rope_bwd_lds(int H, int d_qk);
 
 // Forward epilogue: pre-norm Q|K rows (qk_pre [T][2*H*d_qk] bf16) ->
-// RMSNorm -> RoPE -> head-major q, k.
+// RMSNorm -> RoPE -> head-major q, k with rows of qs >= d_qk elements (a
+// multiple of 8), columns d_qk .. qs - 1 written as zero.
 void launch_norm_rope_fwd(const uint16_t* qk_pre, int64_t T, int seq_len, int H, int d_qk,
-                          float eps, float base, uint16_t* q, uint16_t* k, hipStream_t s);
+                          int qs, float eps, float base, uint16_t* q, uint16_t* k,
+                          hipStream_t s);
 
-// Backward epilogue: dq, dk (head-major) + qk_pre -> the Q|K part of the
+// Backward epilogue: dq, dk (head-major, rows of qs elements of which the
+// first d_qk are read) + qk_pre -> the Q|K part of the
 // packed gradient, dQK [T][2 H d_qk] bf16, plus one amax partial per block
 // over dQK and dv; norm_rope_bwd_blocks() is that block count.
 int norm_rope_bwd_blocks(int64_t T, int H, int d_qk);
 void launch_norm_rope_bwd(const uint16_t* dq, const uint16_t* dk, const uint16_t* dv,
                           const uint16_t* qk_pre, int64_t T, int seq_len, int H, int d_qk,
-                          int d_v, float eps, float base, uint16_t* dqkv,
+                          int qs, int d_v, float eps, float base, uint16_t* dqkv,
                           uint32_t* partials, hipStream_t s);
 
 }  // namespace fpr

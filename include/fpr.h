@@ -82,6 +82,16 @@ typedef struct fpr_dims {
     int32_t d_v;       /* width of each v head */
     float eps;         /* RMSNorm epsilon (inside the square root) */
     float rope_base;   /* RoPE base, e.g. 10000 */
+    int32_t qk_stride; /* row stride (elements) of the q/k/dq/dk heads; 0 means
+                          d_qk.  Otherwise a multiple of 8 in [d_qk, 1024]: a
+                          consumer that wants equal Q/K/V head widths (an
+                          attention kernel built for 128-wide heads) gets q and
+                          k with d_qk values and qk_stride - d_qk zeros per
+                          row, and hands dq/dk back in the same layout; their
+                          padding columns are never read.  The padding for
+                          FlashAttention-3 is one of the steps fused into the
+                          norm/RoPE kernel in "Reduced-width QK and packed FP8
+                          attention", Changes. */
 } fpr_dims;
 
 /* The cached FP8 views of W_packed, rebuilt by pack_quantize_weights after
@@ -124,8 +134,9 @@ FPR_API int pack_quantize_weights(const fpr_dims* dims,
 /* Step 2 ("The change": qkv = fp8_matmul(x, W_packed); split; rms_norm and
  * rope on q and k).
  *   x:  [T][D] bf16 input activations
- *   q:  [n_seq][H][seq_len][d_qk] bf16 out (normalised, rotated)
- *   k:  [n_seq][H][seq_len][d_qk] bf16 out (normalised, rotated)
+ *   q:  [n_seq][H][seq_len][qk_stride] bf16 out (normalised, rotated; the
+ *       columns past d_qk written as zero)
+ *   k:  [n_seq][H][seq_len][qk_stride] bf16 out, likewise
  *   v:  [n_seq][H][seq_len][d_v]  bf16 out
  *   saved: fpr_saved_bytes(dims, T) bytes, filled for qkv_backward.
  * The weight cache must have been filled by pack_quantize_weights. */
@@ -138,7 +149,8 @@ FPR_API int qkv_forward(const fpr_dims* dims, int32_t n_seq, int32_t seq_len,
 
 /* Step 3 (FP8 backward: norm/RoPE backward, then dX through the cached
  * W_packed codes and dW = x^T dQKV, quantisers treated as identity).
- *   dq, dk: [n_seq][H][seq_len][d_qk] bf16 upstream gradients
+ *   dq, dk: [n_seq][H][seq_len][qk_stride] bf16 upstream gradients (only
+ *           the first d_qk columns of each row are read)
  *   dv:     [n_seq][H][seq_len][d_v]  bf16
  *   saved:  the buffer filled by the matching qkv_forward
  *   dx:     [T][D] bf16 out

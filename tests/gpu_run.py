@@ -28,8 +28,15 @@ def dev_to_bits(t: torch.Tensor) -> np.ndarray:
     return t.contiguous().view(torch.int16).cpu().numpy().view(np.uint16)
 
 
-def dims_for(w: dict):
-    return B.make_dims(w["d_model"], w["n_heads"], w["d_qk"], w["d_v"], EPS, BASE)
+def dims_for(w: dict, qk_stride: int = 0):
+    return B.make_dims(w["d_model"], w["n_heads"], w["d_qk"], w["d_v"], EPS, BASE, qk_stride)
+
+
+def pad_rows(a: np.ndarray, width: int, fill: int) -> np.ndarray:
+    """bf16 bit rows widened to `width` columns of `fill` bits."""
+    out = np.full(a.shape[:-1] + (width,), fill, dtype=np.uint16)
+    out[..., :a.shape[-1]] = a
+    return out
 
 
 def _ceil(a: int, b: int) -> int:
@@ -45,14 +52,21 @@ def unblock_rows(buf, off: int, rows: int, cols: int, lay) -> np.ndarray:
     return a.transpose(0, 2, 1, 3).reshape(nb * R, kc * KB)
 
 
-def run(w: dict, seed: int = 42, x_bits=None, W=None, dy=None, backward: bool = True):
-    """Pack, forward (and backward) on the GPU; returns a dict of numpy arrays."""
+def run(w: dict, seed: int = 42, x_bits=None, W=None, dy=None, backward: bool = True,
+        qk_stride: int = 0):
+    """Pack, forward (and backward) on the GPU; returns a dict of numpy arrays.
+
+    With qk_stride > d_qk, q and k come back with their padded rows (the
+    output buffers start filled with NaN bits, so the padding seen is what
+    the kernels wrote) and dq, dk (given or drawn at d_qk) go in padded with
+    NaN bits, which the backward must never read."""
     n_seq, S = w["n_seq"], w["seq_len"]
     T = n_seq * S
     D, H, dqk, dv = w["d_model"], w["n_heads"], w["d_qk"], w["d_v"]
     N = inputs.packed_width(w)
-    dims = dims_for(w)
-    say(f"[gpu] run n_seq={n_seq} S={S} D={D} H={H} d_qk={dqk} d_v={dv} seed={seed}")
+    dims = dims_for(w, qk_stride)
+    qs = qk_stride or dqk
+    say(f"[gpu] run n_seq={n_seq} S={S} D={D} H={H} d_qk={dqk} d_v={dv} stride={qs} seed={seed}")
     if x_bits is None:
         x_bits = inputs.make_x(w, seed)
     if W is None:
@@ -65,7 +79,11 @@ def run(w: dict, seed: int = 42, x_bits=None, W=None, dy=None, backward: bool = 
     x = bits_to_dev(x_bits)
     ws_f = torch.empty(B.workspace_bytes(dims, T, B.FPR_CALL_FORWARD), dtype=torch.uint8,
                        device="cuda")
-    q, k, v, saved = B.qkv_forward(dims, n_seq, S, x, cache, workspace=ws_f)
+    qo = ko = None
+    if qs != dqk:
+        qo, ko = (torch.full((n_seq, H, S, qs), -1, dtype=torch.int16, device="cuda")
+                  .view(torch.bfloat16) for _ in range(2))
+    q, k, v, saved = B.qkv_forward(dims, n_seq, S, x, cache, q=qo, k=ko, workspace=ws_f)
     lay = B.layout(dims, T)
     Tp = lay.tokens_padded
     out = dict(T=T, N=N, Tp=Tp, x_bits=x_bits, W=W)
@@ -82,7 +100,8 @@ def run(w: dict, seed: int = 42, x_bits=None, W=None, dy=None, backward: bool = 
     if backward:
         if dy is None:
             dy = inputs.make_dy(w, seed + 2)
-        dqd, dkd, dvd = (bits_to_dev(a) for a in dy)
+        dqd, dkd, dvd = (bits_to_dev(pad_rows(a, qs, 0xFFFF) if i < 2 and qs != dqk else a)
+                         for i, a in enumerate(dy))
         ws_b = torch.empty(B.workspace_bytes(dims, T, B.FPR_CALL_BACKWARD), dtype=torch.uint8,
                            device="cuda")
         dx, dw = B.qkv_backward(dims, n_seq, S, dqd, dkd, dvd, saved, cache, workspace=ws_b)
@@ -90,9 +109,9 @@ def run(w: dict, seed: int = 42, x_bits=None, W=None, dy=None, backward: bool = 
         out["dy"] = dy
         # the packed gradient: its Q|K part from the workspace, its V part is
         # dv itself (the gradient quantiser reads it head-major)
-        dqk = dev_to_bits(B.view_bytes(ws_b, lay.bwd_dqkv, (T, 2 * nq), torch.bfloat16))
+        gqk = dev_to_bits(B.view_bytes(ws_b, lay.bwd_dqkv, (T, 2 * nq), torch.bfloat16))
         dvt = np.ascontiguousarray(np.asarray(dy[2]).transpose(0, 2, 1, 3)).reshape(T, H * dv)
-        out["dqkv"] = np.concatenate([dqk, dvt], axis=1)
+        out["dqkv"] = np.concatenate([gqk, dvt], axis=1)
         out["g_scales"] = B.view_bytes(ws_b, lay.bwd_g_scales, (2,), torch.float32).cpu().numpy()
         g8 = unblock_rows(ws_b, lay.bwd_g8, T, N, lay)
         out["g8"], out["g8_kpad"], out["g8_tail"] = g8[:T, :N], g8[:T, N:], g8[T:Tp]

@@ -99,6 +99,25 @@ def test_shape_support(dims, ok):
     assert (B.workspace_bytes(d, 256, B.FPR_CALL_FORWARD) > 0) == ok
 
 
+@pytest.mark.parametrize("stride,ok", [
+    (0, True), (96, True), (128, True), (104, True), (1024, True), (88, False), (100, False),
+    (1032, False), (-8, False)])
+def test_qk_stride_support(stride, ok):
+    d = B.make_dims(768, 6, 96, 128, qk_stride=stride)
+    assert (B.saved_bytes(d, 256) > 0) == ok
+    assert (B.workspace_bytes(d, 256, B.FPR_CALL_BACKWARD) > 0) == ok
+
+
+def test_qk_stride_leaves_buffers_alone():
+    """Padding only changes the caller's q/k/dq/dk rows, never the library's
+    saved or workspace buffers."""
+    a, b = B.make_dims(768, 6), B.make_dims(768, 6, qk_stride=128)
+    assert B.saved_bytes(a, 4096) == B.saved_bytes(b, 4096)
+    for which in (B.FPR_CALL_FORWARD, B.FPR_CALL_BACKWARD):
+        assert B.workspace_bytes(a, 4096, which) == B.workspace_bytes(b, 4096, which)
+    assert ctypes.sizeof(B.Dims) == 28 and B.Dims.qk_stride.offset == 24
+
+
 def _cache_c(ptr=0x1000):
     return B._CacheC(ptr, ptr, ptr, ptr)
 

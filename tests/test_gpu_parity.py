@@ -252,6 +252,26 @@ def test_scores_depend_only_on_position_difference():
     assert worst <= 0.02 * np.abs(Sc).max()
 
 
+@pytest.mark.parametrize("name,w,stride", [("tiny", inputs.WORKLOADS["tiny"], 128),
+                                           ("ragged", RAGGED, 104), ("tails", TAILS, 64)])
+def test_padded_qk_stride(name, w, stride):
+    """q/k rows padded to `stride` (the 96 -> 128 case an attention kernel with
+    equal head widths needs; 48 -> 64 goes through the other norm/RoPE
+    kernels): the first d_qk columns and every backward output are bit-equal
+    to the unpadded run's, the padding is written as zeros, and the NaN bits
+    in the padding of dq/dk are never read."""
+    d = w["d_qk"]
+    a = run(w, seed=13)
+    b = run(w, seed=13, dy=a["dy"], qk_stride=stride)
+    for key in ("q", "k"):
+        assert b[key].shape[-1] == stride
+        assert np.array_equal(b[key][..., :d], a[key]), key
+        assert not b[key][..., d:].any(), key  # +0.0 bits, not NaN
+    for key in ("v", "qk_pre", "dqkv", "g_scales", "g8", "dx", "dw"):
+        assert np.array_equal(a[key], b[key]), key
+    assert b["status"] == 0
+
+
 def test_zero_inputs_give_zero_outputs():
     w = RAGGED
     T = w["n_seq"] * w["seq_len"]
