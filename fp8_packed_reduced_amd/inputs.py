@@ -13,6 +13,12 @@ here; these shapes and distributions stand in for them):
 * ``step_64k`` : D=768, 6 heads, one sequence of 65536 tokens, forward+backward
 * ``sweep_64`` / ``sweep_128``: ``step_64k`` with d_qk = 64 or 128
 
+FP8 ReLU^2 MLP workloads (``MLP_WORKLOADS``): ``mlp_tiny`` (256 tokens,
+D=128, d_ff=512) and ``mlp_64k`` (65536 tokens, D=768, d_ff=3072, the MLP
+of the block whose attention projection is ``step_64k``).  W1 [D][d_ff] ~
+N(0, 1/D), W2 [d_ff][D] ~ N(0, 1/d_ff) (fan-in), both from seed base+1 in
+that order; dy [T][D] ~ N(0, 1e-2) as bf16.
+
 x ~ N(0, 1) as bf16; W ~ N(0, 1/D) as fp32 (one draw of the whole [D][N]
 packed matrix, handed over as three strided column blocks); the upstream
 gradients dq, dk, dv ~ N(0, 1e-2) (variance 1e-2, std 0.1) as bf16.
@@ -28,6 +34,11 @@ WORKLOADS = {
     "step_64k": dict(n_seq=1, seq_len=65536, d_model=768, n_heads=6, d_qk=96, d_v=128),
     "sweep_64": dict(n_seq=1, seq_len=65536, d_model=768, n_heads=6, d_qk=64, d_v=128),
     "sweep_128": dict(n_seq=1, seq_len=65536, d_model=768, n_heads=6, d_qk=128, d_v=128),
+}
+
+MLP_WORKLOADS = {
+    "mlp_tiny": dict(n_seq=1, seq_len=256, d_model=128, d_ff=512),
+    "mlp_64k": dict(n_seq=1, seq_len=65536, d_model=768, d_ff=3072),
 }
 
 EPS = 1e-6
@@ -84,3 +95,20 @@ def make_dy(w: dict, seed: int):
 
 def make_all(w: dict, seed: int = 42):
     return dict(x=make_x(w, seed), W=make_w(w, seed + 1), dy=make_dy(w, seed + 2))
+
+
+def make_mlp_w(w: dict, seed: int):
+    """W1 [D][d_ff] ~ N(0, 1/D) and W2 [d_ff][D] ~ N(0, 1/d_ff), fp32."""
+    D, F = w["d_model"], w["d_ff"]
+    rng = np.random.default_rng(seed)
+    w1 = rng.standard_normal((D, F), dtype=np.float32) * np.float32(1.0 / np.sqrt(D))
+    w2 = rng.standard_normal((F, D), dtype=np.float32) * np.float32(1.0 / np.sqrt(F))
+    return w1.astype(np.float32), w2.astype(np.float32)
+
+
+def make_mlp_dy(w: dict, seed: int, tokens: int | None = None) -> np.ndarray:
+    """Upstream gradient of the MLP output, [T][D] bf16 patterns, std 0.1."""
+    T = w["n_seq"] * w["seq_len"] if tokens is None else tokens
+    rng = np.random.default_rng(seed)
+    dy = rng.standard_normal((T, w["d_model"]), dtype=np.float32) * np.float32(0.1)
+    return f32_to_bf16_bits(dy)

@@ -17,6 +17,9 @@ What is computed, and where the pages say so:
   concatenation; norm, RoPE and layout conversion fused; FP8 backward.
 * "Where the eight seconds were hiding", section "The inventory": the
   transposed weight view is cached and reused by the backward pass.
+* PR #344 page, section "Changes": the FP8 ReLU-squared MLP, forward and
+  backward, with relu(pre) rebuilt from the stored squared activation
+  (``mlp_forward`` / ``mlp_backward``, readings at that section).
 
 Every floating-point step runs in float64.  FP8 codes, scales and bf16/fp32
 output roundings are the only reduced-precision steps, and they are the
@@ -372,4 +375,88 @@ def qkv_backward(dims, n_seq: int, S: int, dq_bits, dk_bits, dv_bits,
     dw64 = gemm_e4m3(np.ascontiguousarray(x8.T), g8, s_x, s_g)
     out["dw64"] = dw64
     out["dw_f32"] = round_f32(dw64)
+    return out
+
+
+# ------------------------------------------------------ FP8 ReLU^2 MLP
+#
+# PR #344 page, "Changes": FP8 covers the whole ReLU-squared MLP, forward
+# and backward, both projections and all four backward GEMMs; the backward
+# rebuilds relu(pre) from the stored squared activation instead of keeping
+# pre.  Readings where the page is silent: W1 is [D][F] and W2 is [F][D]
+# (y = relu(x W1)^2 W2), one per-tensor e4m3 scale per tensor exactly as for
+# the QKV path, and the stored squared activation is its e4m3 copy h8 with
+# scale s_h, which the second projection and dW2 read anyway, so
+# relu(pre) = sqrt(s_h dec(h8)).  The bf16 h that the quantiser reads is
+# relu(pre)^2 rounded once.
+
+def relu2(pre: np.ndarray) -> np.ndarray:
+    """h = relu(pre)^2."""
+    r = np.maximum(pre, 0.0)
+    return r * r
+
+
+def relu2_grad(dh: np.ndarray, h: np.ndarray) -> np.ndarray:
+    """d relu(pre)^2 / d pre = 2 relu(pre), with relu(pre) = sqrt(h):
+    dpre = 2 dh sqrt(h)."""
+    return 2.0 * dh * np.sqrt(h)
+
+
+def mlp_quantize_weights(w1: np.ndarray, w2: np.ndarray):
+    """Per-tensor e4m3 codes of W1 [D][F] and W2 [F][D] in both layouts."""
+    c1, s1, i1, rc1 = quantize_f32(w1)
+    c2, s2, i2, rc2 = quantize_f32(w2)
+    return dict(w1=c1, w1t=np.ascontiguousarray(c1.T), s_w1=s1, inv_w1=i1,
+                w2=c2, w2t=np.ascontiguousarray(c2.T), s_w2=s2, inv_w2=i2, rc=rc1 | rc2)
+
+
+def mlp_forward(x_bits: np.ndarray, wq: dict, h_bits: np.ndarray | None = None):
+    """x_bits [T][D] bf16 -> y = fp8(h) @ fp8(W2), h = relu(fp8(x) @ fp8(W1))^2.
+
+    If ``h_bits`` ([T][F] bf16) is given, the second projection is fed those
+    values instead of the oracle's own (stage-wise comparison)."""
+    x8, s_x, inv_x, rc_x = quantize_bf16(x_bits)
+    out = dict(x8=x8, s_x=s_x, inv_x=inv_x, rc_x=rc_x)
+    if h_bits is None:
+        pre64 = gemm_e4m3(x8, wq["w1"], s_x, wq["s_w1"])
+        out["pre64"] = pre64
+        out["h64"] = relu2(pre64)
+        h_bits = round_bf16(out["h64"])
+    out["h_bits"] = h_bits
+    h8, s_h, inv_h, rc_h = quantize_bf16(h_bits)
+    out.update(h8=h8, s_h=s_h, inv_h=inv_h, rc_h=rc_h)
+    y64 = gemm_e4m3(h8, wq["w2"], s_h, wq["s_w2"])
+    out["y64"] = y64
+    out["y_bits"] = round_bf16(y64)
+    return out
+
+
+def mlp_backward(dy_bits: np.ndarray, x8: np.ndarray, s_x, h8: np.ndarray, s_h, wq: dict,
+                 dpre_bits: np.ndarray | None = None):
+    """Backward of the FP8 ReLU^2 MLP from the saved x8, h8 and their scales;
+    quantisers treated as the identity.
+
+      dh   = dy @ W2^T            (through the cached [F][D] codes of W2)
+      dpre = 2 dh sqrt(s_h dec(h8))
+      dx   = dpre @ W1^T          (through the cached [D][F] codes of W1)
+      dW1  = x^T dpre,  dW2 = h^T dy
+
+    If ``dpre_bits`` is given, the stages after it are fed those values."""
+    dy8, s_dy, inv_dy, rc_dy = quantize_bf16(dy_bits)
+    out = dict(dy8=dy8, s_dy=s_dy, inv_dy=inv_dy, rc_dy=rc_dy)
+    if dpre_bits is None:
+        dh64 = gemm_e4m3(dy8, np.ascontiguousarray(wq["w2"].T), s_dy, wq["s_w2"])
+        h = float(s_h) * e4m3_decode(h8)
+        out["dh64"] = dh64
+        out["dpre64"] = relu2_grad(dh64, h)
+        dpre_bits = round_bf16(out["dpre64"])
+    out["dpre_bits"] = dpre_bits
+    dp8, s_dp, inv_dp, rc_dp = quantize_bf16(dpre_bits)
+    out.update(dp8=dp8, s_dp=s_dp, inv_dp=inv_dp, rc_dp=rc_dp)
+    dx64 = gemm_e4m3(dp8, np.ascontiguousarray(wq["w1"].T), s_dp, wq["s_w1"])
+    out["dx64"] = dx64
+    out["dx_bits"] = round_bf16(dx64)
+    dw1 = gemm_e4m3(np.ascontiguousarray(x8.T), dp8, s_x, s_dp)
+    dw2 = gemm_e4m3(np.ascontiguousarray(h8.T), dy8, s_h, s_dy)
+    out.update(dw1_64=dw1, dw2_64=dw2, dw1_f32=round_f32(dw1), dw2_f32=round_f32(dw2))
     return out
