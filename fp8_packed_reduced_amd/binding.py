@@ -17,7 +17,7 @@ LIB_PATH = os.path.join(HERE, "libfpr.so")
 HEADER = os.path.join(os.path.dirname(HERE), "include", "fpr.h")
 
 FPR_CALL_PACK, FPR_CALL_FORWARD, FPR_CALL_BACKWARD = 0, 1, 2
-STATUS_W_NONFINITE, STATUS_X_NONFINITE, STATUS_G_NONFINITE = 1, 2, 4
+STATUS_W_NONFINITE, STATUS_X_NONFINITE, STATUS_G_NONFINITE, STATUS_H_NONFINITE = 1, 2, 4, 8
 
 
 class FprError(RuntimeError):
@@ -70,6 +70,27 @@ class Layout(ctypes.Structure):
                 ("k_block", ctypes.c_int32), ("act_block_rows", ctypes.c_int32)]
 
 
+class MlpDims(ctypes.Structure):
+    _fields_ = [("d_model", ctypes.c_int32), ("d_ff", ctypes.c_int32)]
+
+
+class _MlpCacheC(ctypes.Structure):
+    _fields_ = [("w1", ctypes.c_void_p), ("w1_t", ctypes.c_void_p), ("w2", ctypes.c_void_p),
+                ("w2_t", ctypes.c_void_p), ("scales", ctypes.c_void_p),
+                ("status", ctypes.c_void_p)]
+
+
+class MlpLayout(ctypes.Structure):
+    _fields_ = [("tokens", ctypes.c_int64), ("tokens_padded", ctypes.c_int64),
+                ("saved_x8", ctypes.c_size_t), ("saved_h8", ctypes.c_size_t),
+                ("saved_x_scales", ctypes.c_size_t), ("saved_h_scales", ctypes.c_size_t),
+                ("fwd_h", ctypes.c_size_t), ("bwd_dy8", ctypes.c_size_t),
+                ("bwd_dy_scales", ctypes.c_size_t), ("bwd_dpre", ctypes.c_size_t),
+                ("bwd_dpre8", ctypes.c_size_t), ("bwd_dpre_scales", ctypes.c_size_t),
+                ("bwd_dw_part", ctypes.c_size_t), ("dw1_splits", ctypes.c_int32),
+                ("dw2_splits", ctypes.c_int32)]
+
+
 _lib = None
 _V, _I64, _I32, _SZ = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32, ctypes.c_size_t
 
@@ -104,6 +125,20 @@ def load():
     L.fpr_trace_set.argtypes = [ctypes.POINTER(_TraceC)]
     L.fpr_e4m3_encode.restype = ctypes.c_int
     L.fpr_e4m3_encode.argtypes = [_V, _I64, ctypes.c_float, _V, _V]
+    L.fpr_mlp_workspace_bytes.restype = _SZ
+    L.fpr_mlp_workspace_bytes.argtypes = [P(MlpDims), _I64, ctypes.c_int]
+    L.fpr_mlp_saved_bytes.restype = _SZ
+    L.fpr_mlp_saved_bytes.argtypes = [P(MlpDims), _I64]
+    L.fpr_mlp_get_layout.restype = ctypes.c_int
+    L.fpr_mlp_get_layout.argtypes = [P(MlpDims), _I64, P(MlpLayout)]
+    L.mlp_pack_quantize_weights.restype = ctypes.c_int
+    L.mlp_pack_quantize_weights.argtypes = [P(MlpDims), _V, _I64, _V, _I64, P(_MlpCacheC), _V,
+                                            _SZ, _V]
+    L.mlp_forward.restype = ctypes.c_int
+    L.mlp_forward.argtypes = [P(MlpDims), _I64, _V, P(_MlpCacheC), _V, _V, _SZ, _V, _SZ, _V]
+    L.mlp_backward.restype = ctypes.c_int
+    L.mlp_backward.argtypes = [P(MlpDims), _I64, _V, _V, _SZ, P(_MlpCacheC), _V, _V, _I64, _V,
+                               _I64, _V, _SZ, _V]
     _lib = L
     return L
 
@@ -312,3 +347,105 @@ class KernelTrace:
             name = self._c.names[i].decode()
             out.append((name, self.events[2 * i].elapsed_time(self.events[2 * i + 1])))
         return out
+
+
+# ------------------------------------------------------- FP8 ReLU^2 MLP
+
+def mlp_workspace_bytes(dims: MlpDims, tokens: int, which: int) -> int:
+    return int(load().fpr_mlp_workspace_bytes(ctypes.byref(dims), tokens, which))
+
+
+def mlp_saved_bytes(dims: MlpDims, tokens: int) -> int:
+    return int(load().fpr_mlp_saved_bytes(ctypes.byref(dims), tokens))
+
+
+def mlp_layout(dims: MlpDims, tokens: int) -> MlpLayout:
+    out = MlpLayout()
+    rc = load().fpr_mlp_get_layout(ctypes.byref(dims), tokens, ctypes.byref(out))
+    if rc:
+        raise FprError(rc, "fpr_mlp_get_layout")
+    return out
+
+
+class MlpCache:
+    """Device buffers of the cached FP8 views of W1 and W2."""
+
+    def __init__(self, dims: MlpDims, device="cuda"):
+        D, F = dims.d_model, dims.d_ff
+        self.dims = dims
+        self.w1 = torch.empty((D, F), dtype=torch.uint8, device=device)
+        self.w1_t = torch.empty((F, D), dtype=torch.uint8, device=device)
+        self.w2 = torch.empty((F, D), dtype=torch.uint8, device=device)
+        self.w2_t = torch.empty((D, F), dtype=torch.uint8, device=device)
+        self.scales = torch.zeros(4, dtype=torch.float32, device=device)
+        self.status = torch.zeros(1, dtype=torch.int32, device=device)
+
+    def c(self) -> _MlpCacheC:
+        return _MlpCacheC(self.w1.data_ptr(), self.w1_t.data_ptr(), self.w2.data_ptr(),
+                          self.w2_t.data_ptr(), self.scales.data_ptr(), self.status.data_ptr())
+
+
+def mlp_pack_quantize_weights(dims: MlpDims, w1, w2, cache: MlpCache, workspace=None):
+    D, F = dims.d_model, dims.d_ff
+    ld1 = _need_rows(w1, D, F, "w1")
+    ld2 = _need_rows(w2, F, D, "w2")
+    if workspace is None:
+        workspace = torch.empty(mlp_workspace_bytes(dims, 0, FPR_CALL_PACK), dtype=torch.uint8,
+                                device=w1.device)
+    cc = cache.c()
+    rc = load().mlp_pack_quantize_weights(ctypes.byref(dims), w1.data_ptr(), ld1, w2.data_ptr(),
+                                          ld2, ctypes.byref(cc), workspace.data_ptr(),
+                                          workspace.numel(), _stream(w1.device))
+    if rc:
+        raise FprError(rc, "mlp_pack_quantize_weights")
+    return cache
+
+
+def mlp_forward(dims: MlpDims, x, cache: MlpCache, y=None, saved=None, workspace=None):
+    """Returns (y, saved)."""
+    T, D = x.shape[0], dims.d_model
+    dev = x.device
+    _need(x, torch.bfloat16, (T, D), "x")
+    if y is None:
+        y = torch.empty((T, D), dtype=torch.bfloat16, device=dev)
+    _need(y, torch.bfloat16, (T, D), "y")
+    if saved is None:
+        saved = torch.empty(mlp_saved_bytes(dims, T), dtype=torch.uint8, device=dev)
+    if workspace is None:
+        workspace = torch.empty(mlp_workspace_bytes(dims, T, FPR_CALL_FORWARD),
+                                dtype=torch.uint8, device=dev)
+    cc = cache.c()
+    rc = load().mlp_forward(ctypes.byref(dims), T, x.data_ptr(), ctypes.byref(cc), y.data_ptr(),
+                            saved.data_ptr(), saved.numel(), workspace.data_ptr(),
+                            workspace.numel(), _stream(dev))
+    if rc:
+        raise FprError(rc, "mlp_forward")
+    return y, saved
+
+
+def mlp_backward(dims: MlpDims, dy, saved, cache: MlpCache, dx=None, dw1=None, dw2=None,
+                 workspace=None):
+    """Returns (dx, dw1, dw2)."""
+    T, D, F = dy.shape[0], dims.d_model, dims.d_ff
+    dev = dy.device
+    _need(dy, torch.bfloat16, (T, D), "dy")
+    if dx is None:
+        dx = torch.empty((T, D), dtype=torch.bfloat16, device=dev)
+    _need(dx, torch.bfloat16, (T, D), "dx")
+    if dw1 is None:
+        dw1 = torch.empty((D, F), dtype=torch.float32, device=dev)
+    if dw2 is None:
+        dw2 = torch.empty((F, D), dtype=torch.float32, device=dev)
+    ld1 = _need_rows(dw1, D, F, "dw1")
+    ld2 = _need_rows(dw2, F, D, "dw2")
+    if workspace is None:
+        workspace = torch.empty(mlp_workspace_bytes(dims, T, FPR_CALL_BACKWARD),
+                                dtype=torch.uint8, device=dev)
+    cc = cache.c()
+    rc = load().mlp_backward(ctypes.byref(dims), T, dy.data_ptr(), saved.data_ptr(),
+                             saved.numel(), ctypes.byref(cc), dx.data_ptr(), dw1.data_ptr(), ld1,
+                             dw2.data_ptr(), ld2, workspace.data_ptr(), workspace.numel(),
+                             _stream(dev))
+    if rc:
+        raise FprError(rc, "mlp_backward")
+    return dx, dw1, dw2

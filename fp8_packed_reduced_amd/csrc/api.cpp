@@ -97,6 +97,79 @@ Plan make_plan(const fpr_dims* d, int64_t T) {
   return p;
 }
 
+// ---- FP8 ReLU^2 MLP: shapes and memory plan
+
+bool al16(const void* p);
+
+struct MlpPlan {
+  int D, F;
+  int64_t T, Tp;
+  size_t s_x8, s_h8, s_xsc, s_hsc, saved_total;
+  int x_parts;
+  size_t f_xpart, f_h, f_hpart, fwd_total;
+  size_t b_dypart, b_dysc, b_dy8, b_dpre, b_dppart, b_dpsc, b_dp8, b_dwpart, bwd_total;
+  size_t p_part, pack_total;
+};
+
+int mlp_shape_check(const fpr_mlp_dims* d) {
+  if (!d || d->d_model <= 0 || d->d_ff <= 0) return FPR_ERR_ARG;
+  if (d->d_model % 64 || d->d_ff % 64 || d->d_model > (1 << 16) || d->d_ff > (1 << 16))
+    return FPR_ERR_SHAPE;
+  return FPR_OK;
+}
+
+MlpPlan make_mlp_plan(const fpr_mlp_dims* d, int64_t T) {
+  MlpPlan p{};
+  p.D = d->d_model;
+  p.F = d->d_ff;
+  p.T = T;
+  p.Tp = round_up(T > 0 ? T : 1, 128);
+  const size_t slots = (size_t)fpr::gemm_amax_slots_max() * 4;
+  size_t c = 0;
+  p.s_x8 = take(c, fpr::act_blocked_bytes(T, p.D));
+  p.s_h8 = take(c, fpr::act_blocked_bytes(T, p.F));
+  p.s_xsc = take(c, 4 * sizeof(float));
+  p.s_hsc = take(c, 4 * sizeof(float));
+  p.saved_total = c;
+  // one amax block per 256 x 16-byte vectors of x (or dy), at most kPartsAct
+  p.x_parts =
+      (int)std::max<int64_t>(1, std::min<int64_t>(kPartsAct, ceil_div(T * p.D / 8, fpr::kThreads)));
+  c = 0;
+  p.f_xpart = take(c, (size_t)p.x_parts * 4);
+  p.f_h = take(c, (size_t)T * p.F * 2);
+  p.f_hpart = take(c, slots);
+  p.fwd_total = c;
+  c = 0;
+  p.b_dypart = take(c, (size_t)p.x_parts * 4);
+  p.b_dysc = take(c, 4 * sizeof(float));
+  p.b_dy8 = take(c, fpr::act_blocked_bytes(T, p.D));
+  p.b_dpre = take(c, (size_t)T * p.F * 2);
+  p.b_dppart = take(c, slots);
+  p.b_dpsc = take(c, 4 * sizeof(float));
+  p.b_dp8 = take(c, fpr::act_blocked_bytes(T, p.F));
+  p.b_dwpart = take(c, std::max(fpr::dw_partial_bytes(p.D, p.F, p.Tp),
+                                fpr::dw_partial_bytes(p.F, p.D, p.Tp)));
+  p.bwd_total = c;
+  c = 0;
+  p.p_part = take(c, (size_t)kPartsW * 4);
+  p.pack_total = c;
+  return p;
+}
+
+int mlp_cache_check(const fpr_mlp_cache* c) {
+  if (!c || !c->w1 || !c->w1_t || !c->w2 || !c->w2_t || !c->scales || !c->status)
+    return FPR_ERR_ARG;
+  if (!al16(c->w1) || !al16(c->w1_t) || !al16(c->w2) || !al16(c->w2_t) ||
+      (uintptr_t)c->scales % 4 || (uintptr_t)c->status % 4)
+    return FPR_ERR_ALIGN;
+  return FPR_OK;
+}
+
+int mlp_tokens_check(int64_t T) {
+  if (T <= 0) return FPR_ERR_ARG;
+  return T > kMaxTokens ? FPR_ERR_SHAPE : FPR_OK;
+}
+
 thread_local fpr_trace* t_trace = nullptr;
 
 bool same_name(const char* a, const char* b) {
@@ -315,6 +388,177 @@ const char* fpr_status_string(int code) {
     case FPR_ERR_LAUNCH: return "kernel launch failed";
     default: return "unknown status code";
   }
+}
+
+// ---- FP8 ReLU^2 MLP
+
+size_t fpr_mlp_workspace_bytes(const fpr_mlp_dims* dims, int64_t tokens, int which) {
+  if (mlp_shape_check(dims) != FPR_OK) return 0;
+  if (which == FPR_CALL_PACK) return make_mlp_plan(dims, 1).pack_total;
+  if (mlp_tokens_check(tokens) != FPR_OK) return 0;
+  const MlpPlan p = make_mlp_plan(dims, tokens);
+  if (which == FPR_CALL_FORWARD) return p.fwd_total;
+  if (which == FPR_CALL_BACKWARD) return p.bwd_total;
+  return 0;
+}
+
+size_t fpr_mlp_saved_bytes(const fpr_mlp_dims* dims, int64_t tokens) {
+  if (mlp_shape_check(dims) != FPR_OK || mlp_tokens_check(tokens) != FPR_OK) return 0;
+  return make_mlp_plan(dims, tokens).saved_total;
+}
+
+int fpr_mlp_get_layout(const fpr_mlp_dims* dims, int64_t tokens, fpr_mlp_layout* out) {
+  int rc = mlp_shape_check(dims);
+  if (rc || (rc = mlp_tokens_check(tokens))) return rc;
+  if (!out) return FPR_ERR_ARG;
+  const MlpPlan p = make_mlp_plan(dims, tokens);
+  out->tokens = p.T;
+  out->tokens_padded = p.Tp;
+  out->saved_x8 = p.s_x8;
+  out->saved_h8 = p.s_h8;
+  out->saved_x_scales = p.s_xsc;
+  out->saved_h_scales = p.s_hsc;
+  out->fwd_h = p.f_h;
+  out->bwd_dy8 = p.b_dy8;
+  out->bwd_dy_scales = p.b_dysc;
+  out->bwd_dpre = p.b_dpre;
+  out->bwd_dpre8 = p.b_dp8;
+  out->bwd_dpre_scales = p.b_dpsc;
+  out->bwd_dw_part = p.b_dwpart;
+  out->dw1_splits = fpr::dw_splits(p.D, p.F, p.Tp);
+  out->dw2_splits = fpr::dw_splits(p.F, p.D, p.Tp);
+  return FPR_OK;
+}
+
+int mlp_pack_quantize_weights(const fpr_mlp_dims* dims, const float* w1, int64_t ld1,
+                              const float* w2, int64_t ld2, const fpr_mlp_cache* cache,
+                              void* workspace, size_t workspace_bytes, void* stream) {
+  int rc = mlp_shape_check(dims);
+  if (rc) return rc;
+  const MlpPlan p = make_mlp_plan(dims, 1);
+  if ((rc = ld_check(ld1, p.F, w1)) || (rc = ld_check(ld2, p.D, w2)) ||
+      (rc = mlp_cache_check(cache)))
+    return rc;
+  if (!workspace) return FPR_ERR_ARG;
+  if (!al16(workspace)) return FPR_ERR_ALIGN;
+  if (workspace_bytes < p.pack_total) return FPR_ERR_WORKSPACE;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  (void)hipGetLastError();
+  uint32_t* parts = at<uint32_t>(workspace, p.p_part);
+  // a single matrix is the packed-weight case with all columns in one piece
+  stage("mlp_amax_w", s, [&] {
+    fpr::launch_amax_w(w1, ld1, w1, ld1, w1, ld1, p.D, p.F, p.F, parts, kPartsW, s);
+  });
+  stage("mlp_quantize_w", s, [&] {
+    fpr::launch_quantize_w(w1, ld1, w1, ld1, w1, ld1, p.D, p.F, p.F, parts, kPartsW,
+                           cache->scales, cache->status, FPR_STATUS_W_NONFINITE, cache->w1,
+                           cache->w1_t, s, true);
+  });
+  stage("mlp_amax_w", s, [&] {
+    fpr::launch_amax_w(w2, ld2, w2, ld2, w2, ld2, p.F, p.D, p.D, parts, kPartsW, s);
+  });
+  stage("mlp_quantize_w", s, [&] {
+    fpr::launch_quantize_w(w2, ld2, w2, ld2, w2, ld2, p.F, p.D, p.D, parts, kPartsW,
+                           cache->scales + 2, cache->status, FPR_STATUS_W_NONFINITE, cache->w2,
+                           cache->w2_t, s, false);
+  });
+  return finish();
+}
+
+int mlp_forward(const fpr_mlp_dims* dims, int64_t tokens, const uint16_t* x,
+                const fpr_mlp_cache* cache, uint16_t* y, void* saved, size_t saved_bytes,
+                void* workspace, size_t workspace_bytes, void* stream) {
+  int rc = mlp_shape_check(dims);
+  if (rc || (rc = mlp_tokens_check(tokens)) || (rc = mlp_cache_check(cache))) return rc;
+  if (!x || !y || !saved || !workspace) return FPR_ERR_ARG;
+  if (!al16(x) || !al16(y) || !al16(saved) || !al16(workspace)) return FPR_ERR_ALIGN;
+  const MlpPlan p = make_mlp_plan(dims, tokens);
+  if (saved_bytes < p.saved_total || workspace_bytes < p.fwd_total) return FPR_ERR_WORKSPACE;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  (void)hipGetLastError();
+  const int64_t T = p.T;
+  uint32_t* xparts = at<uint32_t>(workspace, p.f_xpart);
+  uint32_t* hparts = at<uint32_t>(workspace, p.f_hpart);
+  uint16_t* h = at<uint16_t>(workspace, p.f_h);
+  uint8_t* x8 = at<uint8_t>(saved, p.s_x8);
+  uint8_t* h8 = at<uint8_t>(saved, p.s_h8);
+  float* xsc = at<float>(saved, p.s_xsc);
+  float* hsc = at<float>(saved, p.s_hsc);
+  int nh = 0;
+  stage("mlp_amax_x", s, [&] { fpr::launch_amax_bf16(x, T * p.D, xparts, p.x_parts, s); });
+  stage("mlp_quantize_x", s, [&] {
+    fpr::launch_quantize_act(x, T, p.D, xparts, p.x_parts, xsc, cache->status,
+                             FPR_STATUS_X_NONFINITE, x8, p.Tp, s);
+  });
+  stage("mlp_gemm_up", s, [&] {
+    nh = fpr::launch_gemm_relu2(x8, cache->w1_t, (int)T, p.F, p.D, xsc, cache->scales, h,
+                                hparts, s);
+  });
+  stage("mlp_quantize_h", s, [&] {
+    fpr::launch_quantize_act(h, T, p.F, hparts, nh, hsc, cache->status, FPR_STATUS_H_NONFINITE,
+                             h8, p.Tp, s);
+  });
+  stage("mlp_gemm_down", s, [&] {
+    fpr::launch_gemm_dx(h8, cache->w2_t, (int)T, p.D, p.F, hsc, cache->scales + 2, y, s);
+  });
+  return finish();
+}
+
+int mlp_backward(const fpr_mlp_dims* dims, int64_t tokens, const uint16_t* dy,
+                 const void* saved, size_t saved_bytes, const fpr_mlp_cache* cache,
+                 uint16_t* dx, float* dw1, int64_t ld1, float* dw2, int64_t ld2,
+                 void* workspace, size_t workspace_bytes, void* stream) {
+  int rc = mlp_shape_check(dims);
+  if (rc || (rc = mlp_tokens_check(tokens)) || (rc = mlp_cache_check(cache))) return rc;
+  const MlpPlan p = make_mlp_plan(dims, tokens);
+  if ((rc = ld_check(ld1, p.F, dw1)) || (rc = ld_check(ld2, p.D, dw2))) return rc;
+  if (!dy || !saved || !dx || !workspace) return FPR_ERR_ARG;
+  if (!al16(dy) || !al16(saved) || !al16(dx) || !al16(workspace)) return FPR_ERR_ALIGN;
+  if (saved_bytes < p.saved_total || workspace_bytes < p.bwd_total) return FPR_ERR_WORKSPACE;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  (void)hipGetLastError();
+  const int64_t T = p.T;
+  const uint8_t* x8 = at<uint8_t>(saved, p.s_x8);
+  const uint8_t* h8 = at<uint8_t>(saved, p.s_h8);
+  const float* xsc = at<float>(saved, p.s_xsc);
+  const float* hsc = at<float>(saved, p.s_hsc);
+  uint32_t* dyparts = at<uint32_t>(workspace, p.b_dypart);
+  float* dysc = at<float>(workspace, p.b_dysc);
+  uint8_t* dy8 = at<uint8_t>(workspace, p.b_dy8);
+  uint16_t* dpre = at<uint16_t>(workspace, p.b_dpre);
+  uint32_t* dpparts = at<uint32_t>(workspace, p.b_dppart);
+  float* dpsc = at<float>(workspace, p.b_dpsc);
+  uint8_t* dp8 = at<uint8_t>(workspace, p.b_dp8);
+  float* dwpart = at<float>(workspace, p.b_dwpart);
+  int np = 0;
+  stage("mlp_amax_dy", s, [&] { fpr::launch_amax_bf16(dy, T * p.D, dyparts, p.x_parts, s); });
+  stage("mlp_quantize_dy", s, [&] {
+    fpr::launch_quantize_act(dy, T, p.D, dyparts, p.x_parts, dysc, cache->status,
+                             FPR_STATUS_G_NONFINITE, dy8, p.Tp, s);
+  });
+  stage("mlp_gemm_dh", s, [&] {
+    np = fpr::launch_gemm_dpre(dy8, cache->w2, (int)T, p.F, p.D, dysc, cache->scales + 2, h8,
+                               hsc, dpre, dpparts, s);
+  });
+  stage("mlp_quantize_dpre", s, [&] {
+    fpr::launch_quantize_act(dpre, T, p.F, dpparts, np, dpsc, cache->status,
+                             FPR_STATUS_H_NONFINITE, dp8, p.Tp, s);
+  });
+  stage("mlp_gemm_dx", s, [&] {
+    fpr::launch_gemm_dx(dp8, cache->w1, (int)T, p.D, p.F, dpsc, cache->scales, dx, s);
+  });
+  // one column block covers the whole output (nq = its width)
+  stage("mlp_gemm_dw1", s, [&] { fpr::launch_gemm_dw(x8, dp8, p.D, p.F, p.Tp, dwpart, s); });
+  stage("mlp_dw1_reduce", s, [&] {
+    fpr::launch_dw_reduce(dwpart, p.D, p.F, p.Tp, xsc, dpsc, dw1, ld1, dw1, ld1, dw1, ld1, p.F,
+                          s);
+  });
+  stage("mlp_gemm_dw2", s, [&] { fpr::launch_gemm_dw(h8, dy8, p.F, p.D, p.Tp, dwpart, s); });
+  stage("mlp_dw2_reduce", s, [&] {
+    fpr::launch_dw_reduce(dwpart, p.F, p.D, p.Tp, hsc, dysc, dw2, ld2, dw2, ld2, dw2, ld2, p.D,
+                          s);
+  });
+  return finish();
 }
 
 int fpr_e4m3_encode(const float* in, int64_t n, float inv_scale, uint8_t* out, void* stream) {

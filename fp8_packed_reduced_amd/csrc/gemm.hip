@@ -38,6 +38,8 @@
 // quantiser stores them, token by token, and turns them into MFMA operands
 // with transposing LDS reads; it splits K over blocks and writes fp32
 // partial sums that a second kernel adds in split order.
+#include <algorithm>
+
 #include "common.hpp"
 #include "launch.hpp"
 
@@ -516,6 +518,7 @@ struct WaveSlice {
 // the head-major v output.  A chunk of 8 columns never straddles a V head
 // (d_v % 16 == 0) nor the Q|K / V boundary.
 struct EpiFwd {
+  static constexpr bool kMap = false, kAux = false, kAmax = false;
   uint16_t* qk_pre;
   uint16_t* v;
   int N, nqk2, H, dv, S;
@@ -553,7 +556,9 @@ struct EpiFwd {
   __device__ int64_t step8(const Col& c) const { return 8 * (int64_t)(c.qk ? nqk2 : dv); }
 };
 
+// Plain [M][N] rows: dX of the QKV projection, and the MLP's y and dX.
 struct EpiDx {
+  static constexpr bool kMap = false, kAux = false, kAmax = false;
   uint16_t* dx;
   int N;
   struct Col { int n; bool live; };
@@ -569,10 +574,75 @@ struct EpiDx {
   __device__ int64_t step8(const Col&) const { return 8 * (int64_t)N; }
 };
 
+// Epilogues that transform the product before it is rounded (map) also
+// keep the largest |bf16| of what they store, per matrix wave, for the
+// quantiser of their output: one partial per wave, slot block * 4 + wave,
+// as the fp32 bit pattern of that bf16 value.
+__device__ __forceinline__ void epi_partial(uint32_t* partials, uint32_t amax, int slot,
+                                            int lane) {
+  amax = wave_max_u32(amax);
+  if (lane == 0) partials[slot] = amax << 16;
+}
+
+// The MLP's first projection, PR #344 page, "Changes" (the FP8 ReLU^2 MLP):
+// h = relu(pre)^2 into [M][N] bf16 rows.  A NaN product stays NaN.
+struct EpiRelu2 : EpiDx {
+  static constexpr bool kMap = true, kAux = false, kAmax = true;
+  uint32_t* partials;
+  __device__ void prepare() {}
+  __device__ void map(float (&v)[4], uint32_t) const {
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const float r = v[e] <= 0.0f ? 0.0f : v[e];
+      v[e] = r * r;
+    }
+  }
+  __device__ void finish(uint32_t amax, int slot, int lane) const {
+    epi_partial(partials, amax, slot, lane);
+  }
+};
+
+// The MLP's dh = dy W2^T turned into dpre = 2 dh relu(pre), with relu(pre)
+// rebuilt from the stored squared activation as sqrt(s_h dec(h8)) (PR #344
+// page, "Changes"), computed as dh sqrt(4 s_h dec(h8)) with the hardware
+// square root (1 ulp; the result is rounded to bf16).  h8 is in the blocked
+// row layout (kc blocks of kKBlock columns per block row); aux_row() points
+// at the code of column n of row m, and the codes of a lane's columns n +
+// 32 j + 8 g, which share that 128-column block, follow at fixed offsets.
+struct EpiDpre : EpiDx {
+  static constexpr bool kMap = true, kAux = true, kAmax = true;
+  uint32_t* partials;
+  const uint8_t* h8;
+  const float* h_scales;
+  int kc;
+  float sh4;
+  __device__ void prepare() { sh4 = 4.0f * h_scales[0]; }
+  __device__ const uint8_t* aux_row(int m, int n) const {
+    const int64_t blk = (int64_t)(m / kActRows) * kc + n / kKBlock;
+    return h8 + (blk * kActRows + m % kActRows) * kKBlock + n % kKBlock;
+  }
+  __device__ void map(float (&v)[4], uint32_t codes) const {
+    const v2f_t lo = __builtin_amdgcn_cvt_pk_f32_fp8((int)codes, false);  // bytes 0, 1
+    const v2f_t hi = __builtin_amdgcn_cvt_pk_f32_fp8((int)codes, true);   // bytes 2, 3
+    const float h[4] = {lo.x, lo.y, hi.x, hi.y};
+#pragma unroll
+    for (int e = 0; e < 4; ++e) v[e] *= __builtin_amdgcn_sqrtf(sh4 * h[e]);
+  }
+  __device__ void finish(uint32_t amax, int slot, int lane) const {
+    epi_partial(partials, amax, slot, lane);
+  }
+};
+
+__device__ __forceinline__ uint32_t absmax_bf16x2(uint32_t w) {
+  const uint32_t lo = w & 0x7fffu, hi = (w >> 16) & 0x7fffu;
+  return lo > hi ? lo : hi;
+}
+
 template <class C, class Epi>
 __device__ __forceinline__ void store_bf16_tile(const v16f (&acc)[C::FM][C::FN], float alpha,
                                                 uint8_t* slice, const Epi& epi, int M, int m0,
-                                                int n0, int wm, int wn, int lane) {
+                                                int n0, int wm, int wn, int lane,
+                                                uint32_t& amax) {
   using W = WaveSlice<C>;
   const int p = lane & 7, rq = lane >> 3;
   const typename Epi::Col col = epi.column(n0 + wn * C::WN + 8 * p);
@@ -584,16 +654,38 @@ __device__ __forceinline__ void store_bf16_tile(const v16f (&acc)[C::FM][C::FN],
   typename Epi::Row row = epi.row(mp + rq);
   uint16_t* ptr = fast && col.live ? epi.at(mp + rq, col) : nullptr;
   const int64_t step = epi.step8(col);
+  // this lane's accumulator columns: nl + 32 j + 8 g + 0..3
+  const int nl = n0 + wn * C::WN + 4 * (lane >> 5);
 #pragma unroll
   for (int i = 0; i < C::FM; ++i) {
+    const int ml = mp + i * 32 + (lane & 31);  // this lane's accumulator row
+    uint32_t aux[C::FN][4];
+    if constexpr (Epi::kAux) {
+      static_assert(C::WN <= kKBlock, "a lane's columns share one block of h8");
+      const uint8_t* ar = epi.aux_row(ml, nl);
+#pragma unroll
+      for (int j = 0; j < C::FN; ++j)
+#pragma unroll
+        for (int g = 0; g < 4; ++g)
+          aux[j][g] = *reinterpret_cast<const uint32_t*>(ar + 32 * j + 8 * g);
+    }
 #pragma unroll
     for (int j = 0; j < C::FN; ++j)
 #pragma unroll
       for (int g = 0; g < 4; ++g) {
         const v16f& a = acc[i][j];
+        float v[4] = {a[4 * g] * alpha, a[4 * g + 1] * alpha, a[4 * g + 2] * alpha,
+                      a[4 * g + 3] * alpha};
+        if constexpr (Epi::kMap) epi.map(v, Epi::kAux ? aux[j][g] : 0u);
+        const uint32_t w0 = cvt_bf16x2_rn(v[0], v[1]), w1 = cvt_bf16x2_rn(v[2], v[3]);
+        if constexpr (Epi::kAmax) {
+          if (ml < M && nl + 32 * j + 8 * g < epi.N) {
+            const uint32_t a01 = absmax_bf16x2(w0), a23 = absmax_bf16x2(w1);
+            amax = max(amax, max(a01, a23));
+          }
+        }
         *reinterpret_cast<uint2*>(slice + W::at(lane & 31, 4 * j + g) + 8 * (lane >> 5)) =
-            make_uint2(cvt_bf16x2_rn(a[4 * g] * alpha, a[4 * g + 1] * alpha),
-                       cvt_bf16x2_rn(a[4 * g + 2] * alpha, a[4 * g + 3] * alpha));
+            make_uint2(w0, w1);
       }
     uint4 val[4];
 #pragma unroll
@@ -671,12 +763,16 @@ __global__ __launch_bounds__((TileCfg<BM, BN>::THREADS), 1) void gemm_bf16out_ke
   const float alpha = sa[0] * sb[0];
   uint8_t* slice = slices + wave * WaveSlice<C>::BYTES;
   int ord = 0;
+  uint32_t amax = 0;
+  Epi e = epi;
+  if constexpr (Epi::kMap) e.prepare();
   v16f acc[C::FM][C::FN];
   mma_role<C, false, true>(lds, sc, wm, wn, lane, acc, [&](v16f (&a)[C::FM][C::FN]) {
     const int tile = sc.tile_of(ord++);
-    store_bf16_tile<C, Epi>(a, alpha, slice, epi, gm.M, (tile / gm.n_tiles) * BM,
-                            (tile % gm.n_tiles) * BN, wm, wn, lane);
+    store_bf16_tile<C, Epi>(a, alpha, slice, e, gm.M, (tile / gm.n_tiles) * BM,
+                            (tile % gm.n_tiles) * BN, wm, wn, lane, amax);
   });
+  if constexpr (Epi::kAmax) e.finish(amax, blockIdx.x * C::MMA + wave, lane);
 }
 
 // ------------------------------------------------------------ dW split-K
@@ -756,11 +852,15 @@ static int cu_count() {
   return n;
 }
 
+// Returns the block count (the amax partial slots an epilogue with kAmax
+// fills are blocks * 4, at most kEpiAmaxBlocks * 4).
+constexpr int kEpiAmaxBlocks = 256;
+
 template <class Epi>
-static void launch_bf16out(const Gemm& gm, const float* sa, const float* sb, const Epi& epi,
-                           hipStream_t s) {
+static int launch_bf16out(const Gemm& gm, const float* sa, const float* sb, const Epi& epi,
+                          hipStream_t s) {
   const int ntiles = (int)ceil_div(gm.M, kBMo) * gm.n_tiles;
-  const int cus = cu_count();
+  const int cus = Epi::kAmax ? std::min(cu_count(), kEpiAmaxBlocks) : cu_count();
   const int blocks = ntiles < cus ? ntiles : cus;
   if (gm.K % kBK)
     gemm_bf16out_kernel<kBMo, kBNo, true, Epi><<<blocks, TileCfg<kBMo, kBNo>::THREADS, 0, s>>>(gm, ntiles, sa,
@@ -768,7 +868,10 @@ static void launch_bf16out(const Gemm& gm, const float* sa, const float* sb, con
   else
     gemm_bf16out_kernel<kBMo, kBNo, false, Epi><<<blocks, TileCfg<kBMo, kBNo>::THREADS, 0, s>>>(gm, ntiles, sa,
                                                                                sb, epi);
+  return blocks;
 }
+
+int gemm_amax_slots_max() { return kEpiAmaxBlocks * TileCfg<kBMo, kBNo>::MMA; }
 
 static_assert(kBMo == kActRows && kBK == kKBlock,
               "GEMM tiles and the blocked activation layouts");
@@ -784,6 +887,31 @@ void launch_gemm_dx(const uint8_t* g8, const uint8_t* w_packed, int T, int D, in
                     const float* g_scales, const float* w_scales, uint16_t* dx, hipStream_t s) {
   const Gemm gm{g8, 0, w_packed, Np, T, D, Np, (int)ceil_div(D, kBNo), kActRows, 0, 0};
   launch_bf16out(gm, g_scales, w_scales, EpiDx{dx, D}, s);
+}
+
+int launch_gemm_relu2(const uint8_t* x8, const uint8_t* w1_t, int T, int F, int D,
+                      const float* x_scales, const float* w_scales, uint16_t* h,
+                      uint32_t* partials, hipStream_t s) {
+  const Gemm gm{x8, 0, w1_t, D, T, F, D, (int)ceil_div(F, kBNo), kActRows, 0, 0};
+  EpiRelu2 epi{};
+  epi.dx = h;
+  epi.N = F;
+  epi.partials = partials;
+  return launch_bf16out(gm, x_scales, w_scales, epi, s) * TileCfg<kBMo, kBNo>::MMA;
+}
+
+int launch_gemm_dpre(const uint8_t* dy8, const uint8_t* w2, int T, int F, int D,
+                     const float* dy_scales, const float* w_scales, const uint8_t* h8,
+                     const float* h_scales, uint16_t* dpre, uint32_t* partials, hipStream_t s) {
+  const Gemm gm{dy8, 0, w2, D, T, F, D, (int)ceil_div(F, kBNo), kActRows, 0, 0};
+  EpiDpre epi{};
+  epi.dx = dpre;
+  epi.N = F;
+  epi.partials = partials;
+  epi.h8 = h8;
+  epi.h_scales = h_scales;
+  epi.kc = (int)ceil_div(F, kKBlock);
+  return launch_bf16out(gm, dy_scales, w_scales, epi, s) * TileCfg<kBMo, kBNo>::MMA;
 }
 
 // The split count s <= kMaxSplits (and <= the K steps) whose tiles x s

@@ -33,10 +33,14 @@ void launch_amax_bf16(const uint16_t* x, int64_t n, uint32_t* partials, int part
 // quantiser overwrites *status, the activation one ORs into it).
 
 // Quantise W_packed and write both layouts: w_packed [D][N], w_packed_t [N][D].
+// A single matrix is the case nq = N (all three pieces the same pointer).
+// With reset_status false the status bit is ORed in rather than *status
+// overwritten (the second of two weights quantised into one cache).
 void launch_quantize_w(const float* wq, int64_t ldq, const float* wk, int64_t ldk,
                        const float* wv, int64_t ldv, int D, int nq, int N,
                        const uint32_t* partials, int parts, float* scales, int32_t* status,
-                       int status_bit, uint8_t* w_packed, uint8_t* w_packed_t, hipStream_t s);
+                       int status_bit, uint8_t* w_packed, uint8_t* w_packed_t, hipStream_t s,
+                       bool reset_status = true);
 
 // Blocked layout of the FP8 activation copies x8 and g8, which only the
 // GEMMs read.  A matrix of R rows (tokens) and K columns (K contiguous) is
@@ -82,6 +86,22 @@ void launch_gemm_fwd(const uint8_t* x8, const uint8_t* w_packed_t, int T, int N,
 // dX = s_g s_w g8 @ W_packed^T: M = T, N = D, K = N_packed; dx [T][D] bf16.
 void launch_gemm_dx(const uint8_t* g8, const uint8_t* w_packed, int T, int D, int Np,
                     const float* g_scales, const float* w_scales, uint16_t* dx, hipStream_t s);
+
+// FP8 ReLU^2 MLP (W1 [D][F], W2 [F][D]; activations in the blocked row
+// layout).  h = relu(s_x s_w1 x8 @ W1)^2 into h [T][F] bf16, through the
+// cached W1^T codes w1_t [F][D]; and dpre = 2 (s_dy s_w2 dy8 @ W2^T)
+// sqrt(s_h dec(h8)) into dpre [T][F] bf16, through the cached W2 codes
+// w2 [F][D].  Both write one amax partial per matrix wave and return how
+// many (at most gemm_amax_slots_max()).  The MLP's y = h8 @ W2 and
+// dX = dpre8 @ W1^T are launch_gemm_dx with B = W2^T codes [D][F] and
+// W1 codes [D][F].
+int gemm_amax_slots_max();
+int launch_gemm_relu2(const uint8_t* x8, const uint8_t* w1_t, int T, int F, int D,
+                      const float* x_scales, const float* w_scales, uint16_t* h,
+                      uint32_t* partials, hipStream_t s);
+int launch_gemm_dpre(const uint8_t* dy8, const uint8_t* w2, int T, int F, int D,
+                     const float* dy_scales, const float* w_scales, const uint8_t* h8,
+                     const float* h_scales, uint16_t* dpre, uint32_t* partials, hipStream_t s);
 
 // Number of K splits the dW GEMM uses, and its partial-buffer size.
 int dw_splits(int D, int Np, int64_t tokens_padded);

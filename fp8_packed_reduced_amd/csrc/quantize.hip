@@ -128,12 +128,12 @@ __global__ __launch_bounds__(kThreads) void quantize_w_kernel(
     const float* __restrict__ wv, int64_t ldv, int D, int nq, int N,
     const uint32_t* __restrict__ partials, int parts, float* __restrict__ scales,
     int32_t* __restrict__ status, int status_bit, uint8_t* __restrict__ w_packed,
-    uint8_t* __restrict__ w_packed_t) {
+    uint8_t* __restrict__ w_packed_t, bool reset) {
   __shared__ uint8_t tile_t[64][64 + 4];
   __shared__ uint32_t red[4];
   const int n0 = blockIdx.x * 64, d0 = blockIdx.y * 64;
   const float inv = tensor_scales(partials, parts, red, blockIdx.x == 0 && blockIdx.y == 0,
-                                  scales, status, status_bit, true).y;
+                                  scales, status, status_bit, reset).y;
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     const int idx = threadIdx.x + kThreads * i;
@@ -262,11 +262,12 @@ void launch_amax_bf16(const uint16_t* x, int64_t n, uint32_t* partials, int part
 void launch_quantize_w(const float* wq, int64_t ldq, const float* wk, int64_t ldk,
                        const float* wv, int64_t ldv, int D, int nq, int N,
                        const uint32_t* partials, int parts, float* scales, int32_t* status,
-                       int status_bit, uint8_t* w_packed, uint8_t* w_packed_t, hipStream_t s) {
+                       int status_bit, uint8_t* w_packed, uint8_t* w_packed_t, hipStream_t s,
+                       bool reset_status) {
   dim3 grid((unsigned)ceil_div(N, 64), (unsigned)ceil_div(D, 64));
   quantize_w_kernel<<<grid, kThreads, 0, s>>>(wq, ldq, wk, ldk, wv, ldv, D, nq, N, partials,
                                               parts, scales, status, status_bit, w_packed,
-                                              w_packed_t);
+                                              w_packed_t, reset_status);
 }
 
 void launch_quantize_act(const uint16_t* src, int64_t rows, int cols, const uint32_t* partials,

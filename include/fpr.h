@@ -71,7 +71,8 @@ enum {
 enum {
     FPR_STATUS_W_NONFINITE = 1,   /* W_packed had a NaN/Inf (set by pack) */
     FPR_STATUS_X_NONFINITE = 2,   /* x had a NaN/Inf (set by forward) */
-    FPR_STATUS_G_NONFINITE = 4    /* dQKV had a NaN/Inf (set by backward) */
+    FPR_STATUS_G_NONFINITE = 4,   /* dQKV (or the MLP's dy) had a NaN/Inf */
+    FPR_STATUS_H_NONFINITE = 8    /* the MLP's h or dpre had a NaN/Inf */
 };
 
 /* Model dimensions.  The pages' setting: d_qk = 96, d_v = 128. */
@@ -210,8 +211,12 @@ FPR_API int fpr_get_layout(const fpr_dims* dims, int64_t tokens, fpr_layout* out
  * stored in names[i], for i = count, count+1, ... while count < capacity
  * (and count < FPR_TRACE_MAX).  events are caller-created hipEvent_t handles.
  * Stage names: amax_w, quantize_w, amax_x, quantize_x, gemm_fwd,
- * norm_rope_fwd, norm_rope_bwd, quantize_g, gemm_dx, gemm_dw, dw_reduce.  fpr_trace_set(NULL) stops tracing.  This is
- * the only per-thread state the library keeps. */
+ * norm_rope_fwd, norm_rope_bwd, quantize_g, gemm_dx, gemm_dw, dw_reduce;
+ * for the MLP: mlp_amax_w, mlp_quantize_w, mlp_amax_x, mlp_quantize_x,
+ * mlp_gemm_up, mlp_quantize_h, mlp_gemm_down, mlp_amax_dy, mlp_quantize_dy,
+ * mlp_gemm_dh, mlp_quantize_dpre, mlp_gemm_dx, mlp_gemm_dw1,
+ * mlp_dw1_reduce, mlp_gemm_dw2, mlp_dw2_reduce.  fpr_trace_set(NULL) stops
+ * tracing.  This is the only per-thread state the library keeps. */
 #define FPR_TRACE_MAX 4096
 typedef struct fpr_trace {
     void** events;
@@ -222,6 +227,101 @@ typedef struct fpr_trace {
 } fpr_trace;
 
 FPR_API void fpr_trace_set(fpr_trace* trace);
+
+/* ---------------------------------------------------------------------
+ * FP8 ReLU^2 MLP ("Reduced-width QK and packed FP8 attention", Changes:
+ * FP8 extended to the whole ReLU-squared MLP, forward and backward, both
+ * projections and all four backward GEMMs; relu(pre) rebuilt from the
+ * stored squared activation instead of keeping pre).
+ *
+ *   forward:  pre = x W1, h = relu(pre)^2, y = h W2
+ *             (W1 [D][F], W2 [F][D] fp32; x, y [T][D] bf16)
+ *   backward: dh = dy W2^T, dpre = 2 dh relu(pre), dx = dpre W1^T,
+ *             dW1 = x^T dpre, dW2 = h^T dy
+ *
+ * Every GEMM is FP8 e4m3 x e4m3 with fp32 accumulation and one per-tensor
+ * scale per operand (the convention of the QKV path): x, W1, h, W2, dy and
+ * dpre.  The stored squared activation is h's e4m3 copy h8 (and s_h),
+ * which the second projection and dW2 read anyway; the backward takes
+ * relu(pre) = sqrt(s_h * dec(h8)).  The h and dpre that are quantised are
+ * the fp32 results rounded once to bf16.  Quantisers are treated as the
+ * identity in the backward.  The conventions of the QKV calls above hold
+ * (caller-owned device memory, no allocation or synchronisation, outputs
+ * overwritten, argument errors before any launch, 16-byte alignment).
+ * Supported shapes: d_model % 64 == 0, d_ff % 64 == 0, both <= 65536, and
+ * 1 <= T <= 2^24.
+ * ------------------------------------------------------------------- */
+typedef struct fpr_mlp_dims {
+    int32_t d_model;   /* D */
+    int32_t d_ff;      /* F, the hidden width (3072 for D = 768) */
+} fpr_mlp_dims;
+
+/* The cached FP8 views of W1 and W2, rebuilt by mlp_pack_quantize_weights
+ * after every update of the fp32 weights.  Caller-owned device buffers. */
+typedef struct fpr_mlp_cache {
+    uint8_t* w1;       /* [D][F] e4m3 (read by dX = dpre W1^T)           */
+    uint8_t* w1_t;     /* [F][D] e4m3 (read by the first projection)     */
+    uint8_t* w2;       /* [F][D] e4m3 (read by dh = dy W2^T)             */
+    uint8_t* w2_t;     /* [D][F] e4m3 (read by the second projection)    */
+    float* scales;     /* [4] fp32: s_w1, inv_w1, s_w2, inv_w2            */
+    int32_t* status;   /* [1] FPR_STATUS_* bits; pack resets it           */
+} fpr_mlp_cache;
+
+/* Bytes of workspace (FPR_CALL_PACK / _FORWARD / _BACKWARD) and of the
+ * saved buffer (x8, h8 and their scales, which must stay alive and
+ * unmodified from mlp_forward to mlp_backward) for T = tokens; 0 for
+ * invalid dims or token counts. */
+FPR_API size_t fpr_mlp_workspace_bytes(const fpr_mlp_dims* dims, int64_t tokens, int which);
+FPR_API size_t fpr_mlp_saved_bytes(const fpr_mlp_dims* dims, int64_t tokens);
+
+/* Quantise W1 [D][F] (row stride ld1 elements) and W2 [F][D] (ld2) with one
+ * scale each, both layouts of each from one read of it; resets
+ * cache->status, then sets FPR_STATUS_W_NONFINITE if either had a NaN/Inf. */
+FPR_API int mlp_pack_quantize_weights(const fpr_mlp_dims* dims,
+                              const float* w1, int64_t ld1,
+                              const float* w2, int64_t ld2,
+                              const fpr_mlp_cache* cache,
+                              void* workspace, size_t workspace_bytes,
+                              void* stream);
+
+/* x [T][D] bf16 -> y [T][D] bf16; fills `saved` for mlp_backward.  Sets
+ * FPR_STATUS_X_NONFINITE for a NaN/Inf in x, FPR_STATUS_H_NONFINITE for one
+ * in h. */
+FPR_API int mlp_forward(const fpr_mlp_dims* dims, int64_t tokens,
+                const uint16_t* x, const fpr_mlp_cache* cache, uint16_t* y,
+                void* saved, size_t saved_bytes,
+                void* workspace, size_t workspace_bytes,
+                void* stream);
+
+/* dy [T][D] bf16 -> dx [T][D] bf16, dW1 [D][F] fp32 (row stride ld1),
+ * dW2 [F][D] fp32 (ld2).  Sets FPR_STATUS_G_NONFINITE for a NaN/Inf in dy,
+ * FPR_STATUS_H_NONFINITE for one in dpre. */
+FPR_API int mlp_backward(const fpr_mlp_dims* dims, int64_t tokens,
+                 const uint16_t* dy, const void* saved, size_t saved_bytes,
+                 const fpr_mlp_cache* cache, uint16_t* dx,
+                 float* dw1, int64_t ld1, float* dw2, int64_t ld2,
+                 void* workspace, size_t workspace_bytes,
+                 void* stream);
+
+/* Offsets of the MLP's intermediates, for stage-wise tests (blocked FP8
+ * layout as for fpr_layout). */
+typedef struct fpr_mlp_layout {
+    int64_t tokens, tokens_padded;
+    size_t saved_x8;          /* [T][D] e4m3 blocked                     */
+    size_t saved_h8;          /* [T][F] e4m3 blocked, the stored h       */
+    size_t saved_x_scales;    /* [2] fp32: s_x, inv_x                    */
+    size_t saved_h_scales;    /* [2] fp32: s_h, inv_h                    */
+    size_t fwd_h;             /* [T][F] bf16 relu(pre)^2                 */
+    size_t bwd_dy8;           /* [T][D] e4m3 blocked                     */
+    size_t bwd_dy_scales;     /* [2] fp32                                */
+    size_t bwd_dpre;          /* [T][F] bf16                             */
+    size_t bwd_dpre8;         /* [T][F] e4m3 blocked                     */
+    size_t bwd_dpre_scales;   /* [2] fp32                                */
+    size_t bwd_dw_part;       /* split-K dW partials                     */
+    int32_t dw1_splits, dw2_splits;
+} fpr_mlp_layout;
+
+FPR_API int fpr_mlp_get_layout(const fpr_mlp_dims* dims, int64_t tokens, fpr_mlp_layout* out);
 
 /* Encode n fp32 values as e4m3(in[i] * inv_scale) with the library's device
  * encoder (no amax; the caller supplies the scale).  For exhaustive tests of

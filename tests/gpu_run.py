@@ -155,3 +155,65 @@ def bf16_gemm_excess(gpu_bits: np.ndarray, exact: np.ndarray, round_bf16) -> tup
     e_gpu = row_errors(bf16_to_f64(gpu_bits), exact)
     e_rnd = row_errors(bf16_to_f64(round_bf16(exact)), exact)
     return float(np.max(e_gpu - e_rnd)), float(np.max(e_gpu - 1.1 * e_rnd))
+
+
+# ------------------------------------------------------- FP8 ReLU^2 MLP
+
+def run_mlp(w: dict, seed: int = 42, x_bits=None, w12=None, dy_bits=None,
+            backward: bool = True):
+    """Pack, forward (and backward) of the FP8 ReLU^2 MLP on the GPU; every
+    stage's output as numpy arrays (bf16 as uint16 patterns)."""
+    T = w["n_seq"] * w["seq_len"]
+    D, F = w["d_model"], w["d_ff"]
+    say(f"[gpu] mlp T={T} D={D} F={F} seed={seed}")
+    if x_bits is None:
+        x_bits = inputs.make_x(w, seed)
+    if w12 is None:
+        w12 = inputs.make_mlp_w(w, seed + 1)
+    dims = B.MlpDims(D, F)
+    cache = B.MlpCache(dims)
+    w1d, w2d = (torch.from_numpy(np.ascontiguousarray(a)).cuda() for a in w12)
+    B.mlp_pack_quantize_weights(dims, w1d, w2d, cache)
+    ws_f = torch.empty(B.mlp_workspace_bytes(dims, T, B.FPR_CALL_FORWARD), dtype=torch.uint8,
+                       device="cuda")
+    y, saved = B.mlp_forward(dims, bits_to_dev(x_bits), cache, workspace=ws_f)
+    torch.cuda.synchronize()
+    lay = B.mlp_layout(dims, T)
+    qlay = B.layout(B.make_dims(128, 1), 1)  # the blocked layout's parameters
+
+    class _L:
+        act_block_rows, k_block = qlay.act_block_rows, qlay.k_block
+
+    Tp = lay.tokens_padded
+    out = dict(T=T, Tp=Tp, x_bits=x_bits, w1=w12[0], w2=w12[1])
+    for k in ("w1", "w1_t", "w2", "w2_t"):
+        out["c_" + k] = getattr(cache, k).cpu().numpy()
+    out["w_scales"] = cache.scales.cpu().numpy()
+    x8 = unblock_rows(saved, lay.saved_x8, T, D, _L)
+    h8 = unblock_rows(saved, lay.saved_h8, T, F, _L)
+    out["x8"], out["x8_tail"] = x8[:T, :D], x8[T:Tp]
+    out["h8"], out["h8_tail"] = h8[:T, :F], h8[T:Tp]
+    out["x_scales"] = B.view_bytes(saved, lay.saved_x_scales, (2,), torch.float32).cpu().numpy()
+    out["h_scales"] = B.view_bytes(saved, lay.saved_h_scales, (2,), torch.float32).cpu().numpy()
+    out["h"] = dev_to_bits(B.view_bytes(ws_f, lay.fwd_h, (T, F), torch.bfloat16))
+    out["y"] = dev_to_bits(y)
+    if backward:
+        if dy_bits is None:
+            dy_bits = inputs.make_mlp_dy(w, seed + 2)
+        ws_b = torch.empty(B.mlp_workspace_bytes(dims, T, B.FPR_CALL_BACKWARD),
+                           dtype=torch.uint8, device="cuda")
+        dx, dw1, dw2 = B.mlp_backward(dims, bits_to_dev(dy_bits), saved, cache, workspace=ws_b)
+        torch.cuda.synchronize()
+        out["dy"] = dy_bits
+        dy8 = unblock_rows(ws_b, lay.bwd_dy8, T, D, _L)
+        dp8 = unblock_rows(ws_b, lay.bwd_dpre8, T, F, _L)
+        out["dy8"], out["dp8"], out["dp8_tail"] = dy8[:T, :D], dp8[:T, :F], dp8[T:Tp]
+        out["dy_scales"] = B.view_bytes(ws_b, lay.bwd_dy_scales, (2,), torch.float32).cpu().numpy()
+        out["dp_scales"] = B.view_bytes(ws_b, lay.bwd_dpre_scales, (2,),
+                                        torch.float32).cpu().numpy()
+        out["dpre"] = dev_to_bits(B.view_bytes(ws_b, lay.bwd_dpre, (T, F), torch.bfloat16))
+        out["dx"] = dev_to_bits(dx)
+        out["dw1"], out["dw2"] = dw1.cpu().numpy(), dw2.cpu().numpy()
+    out["status"] = int(cache.status.cpu().item())
+    say("[gpu] mlp done")
+    return out

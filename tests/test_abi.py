@@ -17,7 +17,9 @@ def test_library_exports_every_declared_call():
     names = B.declared_functions()
     assert set(names) == {"fpr_workspace_bytes", "fpr_saved_bytes", "pack_quantize_weights",
                           "qkv_forward", "qkv_backward", "fpr_status_string", "fpr_get_layout",
-                          "fpr_e4m3_encode", "fpr_trace_set"}
+                          "fpr_e4m3_encode", "fpr_trace_set", "fpr_mlp_workspace_bytes",
+                          "fpr_mlp_saved_bytes", "fpr_mlp_get_layout",
+                          "mlp_pack_quantize_weights", "mlp_forward", "mlp_backward"}
     lib = B.load()
     for n in names:
         assert hasattr(lib, n), n
@@ -158,3 +160,58 @@ def test_argument_errors_are_reported_before_any_launch():
     # encoder hook
     assert L.fpr_e4m3_encode(ws, 15, 1.0, ws, None) == 3
     assert L.fpr_e4m3_encode(None, 16, 1.0, ws, None) == 1
+
+
+# ------------------------------------------------------- FP8 ReLU^2 MLP
+
+@pytest.mark.parametrize("dims,ok", [((768, 3072), True), ((128, 512), True), ((192, 320), True),
+                                     ((100, 3072), False), ((768, 3000), False),
+                                     ((0, 3072), False), ((768, 1 << 17), False)])
+def test_mlp_shape_support(dims, ok):
+    d = B.MlpDims(*dims)
+    assert (B.mlp_saved_bytes(d, 256) > 0) == ok
+    assert (B.mlp_workspace_bytes(d, 256, B.FPR_CALL_BACKWARD) > 0) == ok
+
+
+def test_mlp_layout_is_disjoint_and_sized():
+    d = B.MlpDims(768, 3072)
+    T = 65536
+    lay = B.mlp_layout(d, T)
+    saved = [(lay.saved_x8, T * 768), (lay.saved_h8, T * 3072), (lay.saved_x_scales, 8),
+             (lay.saved_h_scales, 8)]
+    bwd = [(lay.bwd_dy8, T * 768), (lay.bwd_dy_scales, 8), (lay.bwd_dpre, 2 * T * 3072),
+           (lay.bwd_dpre8, T * 3072), (lay.bwd_dpre_scales, 8),
+           (lay.bwd_dw_part, lay.dw1_splits * 768 * 3072 * 4)]
+    for regions, total in ((saved, B.mlp_saved_bytes(d, T)),
+                           (bwd, B.mlp_workspace_bytes(d, T, B.FPR_CALL_BACKWARD))):
+        regions = sorted(regions)
+        for (a, n), (b, _) in zip(regions, regions[1:]):
+            assert a + n <= b
+        assert regions[-1][0] + regions[-1][1] <= total
+    assert lay.fwd_h + 2 * T * 3072 <= B.mlp_workspace_bytes(d, T, B.FPR_CALL_FORWARD)
+    assert lay.dw1_splits == lay.dw2_splits == 7
+
+
+def test_mlp_argument_errors_are_reported_before_any_launch():
+    L = B.load()
+    d = B.MlpDims(128, 512)
+    p = 0x10000
+    cc = B._MlpCacheC(p, p, p, p, p, p)
+    by = ctypes.byref
+    assert L.mlp_pack_quantize_weights(by(d), None, 512, p, 128, by(cc), p, 1 << 20, None) == 1
+    assert L.mlp_pack_quantize_weights(by(d), p, 500, p, 128, by(cc), p, 1 << 20, None) == 1
+    assert L.mlp_pack_quantize_weights(by(d), p, 514, p, 128, by(cc), p, 1 << 20, None) == 3
+    assert L.mlp_pack_quantize_weights(by(d), p, 512, p, 128, by(cc), p, 8, None) == 4
+    bad = B.MlpDims(100, 512)
+    assert L.mlp_forward(by(bad), 256, p, by(cc), p, p, 1 << 30, p, 1 << 30, None) == 2
+    assert L.mlp_forward(by(d), 0, p, by(cc), p, p, 1 << 30, p, 1 << 30, None) == 1
+    assert L.mlp_forward(by(d), (1 << 24) + 1, p, by(cc), p, p, 1 << 40, p, 1 << 40, None) == 2
+    assert L.mlp_forward(by(d), 256, p, by(cc), None, p, 1 << 30, p, 1 << 30, None) == 1
+    assert L.mlp_forward(by(d), 256, p + 2, by(cc), p, p, 1 << 30, p, 1 << 30, None) == 3
+    assert L.mlp_forward(by(d), 256, p, by(cc), p, p, 16, p, 1 << 30, None) == 4
+    half = B._MlpCacheC(p, p, None, p, p, p)
+    assert L.mlp_forward(by(d), 256, p, by(half), p, p, 1 << 30, p, 1 << 30, None) == 1
+    assert L.mlp_backward(by(d), 256, p, p, 1 << 30, by(cc), p, p, 500, p, 128, p, 1 << 30,
+                          None) == 1
+    assert L.mlp_backward(by(d), 256, p, p, 1 << 30, by(cc), p, p, 512, p, 128, p, 64,
+                          None) == 4

@@ -1,0 +1,135 @@
+"""Parity of the FP8 ReLU^2 MLP (through the C interface) with the CPU oracle.
+
+Stage-wise, each GPU stage against the oracle's stage fed the GPU's own
+inputs to it, with the bars of the QKV path:
+  * e4m3 codes and scales (W1, W2 in both layouts, x8, h8, dy8, dpre8) and
+    the zero token rows of the FP8 copies: bit-exact;
+  * the bf16 outputs of GEMMs (h = relu(pre)^2, y, dpre, dX): per row, the
+    distance to the exact float64 result may exceed what rounding that
+    result to bf16 costs by at most 1.1x + 1e-3;
+  * dW1, dW2 (fp32): <= 1e-3 relative per row.
+End to end from x, W1, W2 and dy alone: y, dX, dW1 and dW2 no further
+from the unquantised float64 results than 1.1x the oracle's own distance +
+1e-3.  (A one-ulp bf16 difference in h can move an h8 code by one e4m3
+step, 12.5%, so y is not compared with the oracle's chain row by row.)
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from fp8_packed_reduced_amd import inputs
+
+from gpu_run import bf16_gemm_excess, bf16_to_f64, row_rel_err, run_mlp, say
+
+pytestmark = pytest.mark.gpu
+
+GEMM_TOL = 1e-3
+
+# K tails in every GEMM (D = 192 and F = 320 are not multiples of 128) and a
+# ragged last token tile
+MLP_TAILS = dict(n_seq=1, seq_len=333, d_model=192, d_ff=320)
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.fail("no GPU visible")
+    oracle.build(force=False)
+
+
+def _check_bf16_gemm(name, gpu_bits, exact):
+    worst, excess = bf16_gemm_excess(gpu_bits, exact, oracle.round_bf16)
+    say(f"[gpu] {name}: worst e_gpu - e_round {worst:.2e}, vs bar {excess:.2e}")
+    assert excess <= GEMM_TOL, name
+
+
+def _check_stages(w, r):
+    T, D, F = r["T"], w["d_model"], w["d_ff"]
+    wq = oracle.mlp_quantize_weights(r["w1"], r["w2"])
+    for k in ("w1", "w1_t", "w2", "w2_t"):
+        assert np.array_equal(r["c_" + k], wq[k.replace("_", "")]), k
+    assert np.array_equal(r["w_scales"],
+                          np.array([wq["s_w1"], wq["inv_w1"], wq["s_w2"], wq["inv_w2"]],
+                                   np.float32))
+    # forward: x8 exact; h against the exact relu(pre)^2 of the GPU's x8
+    fw = oracle.mlp_forward(r["x_bits"], wq)
+    assert np.array_equal(r["x8"], fw["x8"])
+    assert r["x_scales"][0] == fw["s_x"] and r["x_scales"][1] == fw["inv_x"]
+    assert not r["x8_tail"].any()
+    _check_bf16_gemm("h", r["h"], fw["h64"])
+    # h8 from the GPU's h: exact; y against the exact product of the GPU's h8
+    fw2 = oracle.mlp_forward(r["x_bits"], wq, h_bits=r["h"])
+    assert np.array_equal(r["h8"], fw2["h8"])
+    assert r["h_scales"][0] == fw2["s_h"] and r["h_scales"][1] == fw2["inv_h"]
+    assert not r["h8_tail"].any()
+    _check_bf16_gemm("y", r["y"], fw2["y64"])
+    # backward from the GPU's saved x8, h8
+    s_x, s_h = np.float32(r["x_scales"][0]), np.float32(r["h_scales"][0])
+    bw = oracle.mlp_backward(r["dy"], r["x8"], s_x, r["h8"], s_h, wq)
+    assert np.array_equal(r["dy8"], bw["dy8"])
+    assert r["dy_scales"][0] == bw["s_dy"] and r["dy_scales"][1] == bw["inv_dy"]
+    _check_bf16_gemm("dpre", r["dpre"], bw["dpre64"])
+    bw2 = oracle.mlp_backward(r["dy"], r["x8"], s_x, r["h8"], s_h, wq, dpre_bits=r["dpre"])
+    assert np.array_equal(r["dp8"], bw2["dp8"])
+    assert r["dp_scales"][0] == bw2["s_dp"] and r["dp_scales"][1] == bw2["inv_dp"]
+    assert not r["dp8_tail"].any()
+    _check_bf16_gemm("dx", r["dx"], bw2["dx64"])
+    e1 = row_rel_err(r["dw1"], bw2["dw1_64"])
+    e2 = row_rel_err(r["dw2"], bw2["dw2_64"])
+    say(f"[gpu] dw1 {e1:.2e} dw2 {e2:.2e}")
+    assert e1 <= GEMM_TOL and e2 <= GEMM_TOL
+    assert r["status"] == 0
+
+
+@pytest.mark.parametrize("name,w", [("tiny", inputs.MLP_WORKLOADS["mlp_tiny"]),
+                                    ("tails", MLP_TAILS)])
+def test_mlp_stagewise(name, w):
+    _check_stages(w, run_mlp(w, seed=42))
+
+
+def test_mlp_end_to_end_against_oracle_chain():
+    w = inputs.MLP_WORKLOADS["mlp_tiny"]
+    r = run_mlp(w, seed=7)
+    wq = oracle.mlp_quantize_weights(r["w1"], r["w2"])
+    fw = oracle.mlp_forward(r["x_bits"], wq)
+    bw = oracle.mlp_backward(r["dy"], fw["x8"], fw["s_x"], fw["h8"], fw["s_h"], wq)
+    # unquantised float64 gradients
+    x = bf16_to_f64(r["x_bits"])
+    w1, w2 = r["w1"].astype(np.float64), r["w2"].astype(np.float64)
+    dy = bf16_to_f64(r["dy"])
+    pre = x @ w1
+    h = np.maximum(pre, 0.0) ** 2
+    dpre = 2.0 * (dy @ w2.T) * np.maximum(pre, 0.0)
+    ref = dict(y=h @ w2, dx=dpre @ w1.T, dw1=x.T @ dpre, dw2=h.T @ dy)
+    gpu = dict(y=bf16_to_f64(r["y"]), dx=bf16_to_f64(r["dx"]), dw1=r["dw1"], dw2=r["dw2"])
+    orc = dict(y=bf16_to_f64(fw["y_bits"]), dx=bf16_to_f64(bw["dx_bits"]), dw1=bw["dw1_64"],
+               dw2=bw["dw2_64"])
+    for k in ref:
+        eg = float(np.linalg.norm(gpu[k] - ref[k]) / np.linalg.norm(ref[k]))
+        eo = float(np.linalg.norm(orc[k] - ref[k]) / np.linalg.norm(ref[k]))
+        say(f"[gpu] mlp e2e {k}: gpu {eg:.3e} oracle {eo:.3e}")
+        assert eg <= 1.1 * eo + 1e-3, k
+
+
+def test_mlp_deterministic_and_zero_input():
+    w = MLP_TAILS
+    a = run_mlp(w, seed=5)
+    b = run_mlp(w, seed=5)
+    for k in ("h", "h8", "y", "dpre", "dp8", "dx", "dw1", "dw2"):
+        assert np.array_equal(a[k], b[k]), k
+    T = w["n_seq"] * w["seq_len"]
+    z = run_mlp(w, seed=5, x_bits=np.zeros((T, w["d_model"]), np.uint16))
+    for k in ("h", "y", "dpre", "dx"):  # values (a product of zeros may be -0)
+        assert not (bf16_to_f64(z[k]) != 0).any(), k
+    assert not (z["dw1"] != 0).any() and not (z["dw2"] != 0).any()
+    assert z["h_scales"][0] == 1.0 and z["status"] == 0
+
+
+def test_mlp_nonfinite_input_sets_status():
+    w = MLP_TAILS
+    T = w["n_seq"] * w["seq_len"]
+    x = inputs.make_x(w, 3)
+    x[5, 7] = 0x7FC0
+    r = run_mlp(w, seed=3, x_bits=x, backward=False)
+    assert r["status"] & 2
