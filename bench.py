@@ -7,12 +7,18 @@ N=1920), T=65536 tokens in one sequence, all through the C interface of
 libfpr.so.  Inputs are synthetic (seeded normals of the shapes the pages
 train on) and resident in HBM before timing starts.
 
-Prints one JSON line: whole-step tokens/s, TFLOP/s of the three FP8 GEMMs
+Prints one JSON line: whole-step tokens/s, TFLOP/s of the FP8 GEMMs
 against the FP8 dense peak, the live roofline of the dominant kernel (timed
 with HIP events on its launch stream inside the timed region), and the CPU
 oracle timed on a bounded sample on this host.
 
-    python bench.py [--steps K] [--warmup W] [--gpus 1] [--no-cpu-baseline]
+Other workloads (--workload): the QKV shapes of ``inputs.WORKLOADS``; the
+FP8 ReLU^2 MLP alone (``mlp_64k``: mlp_pack_quantize_weights + mlp_forward
++ mlp_backward at D=768, d_ff=3072, T=65536); and the block's projection set
+(``block_64k``: the QKV step of ``step_64k`` followed by the MLP step of
+``mlp_64k``).
+
+    python bench.py [--steps K] [--warmup W] [--gpus 1] [--workload W] [--no-cpu-baseline]
 """
 from __future__ import annotations
 
@@ -27,6 +33,11 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 METRIC = "packed FP8 QKV fwd+bwd tokens/s and TFLOP/s (% FP8 peak) at D=768,H=6,T=65536"
+METRIC_MLP = "FP8 ReLU^2 MLP fwd+bwd tokens/s and TFLOP/s (% FP8 peak) at D=768,d_ff=3072,T=65536"
+METRIC_BLOCK = ("packed FP8 QKV + FP8 ReLU^2 MLP fwd+bwd tokens/s and TFLOP/s (% FP8 peak) at "
+                "D=768,H=6,d_ff=3072,T=65536")
+# workload -> (QKV shapes or None, MLP shapes or None)
+BENCH_WORKLOADS = {"mlp_64k": (None, "mlp_64k"), "block_64k": ("step_64k", "mlp_64k")}
 PEAK_FP8_FLOPS = 5.0e15   # MI355X dense FP8 MFMA
 PEAK_HBM_BYTES = 8.0e12   # MI355X HBM3E
 CALIB_FLOATS = 64 << 20   # counter calibration: encoder over 256 MiB of fp32
@@ -35,6 +46,13 @@ STAGE_SOURCES = {
     "amax_x": "quantize.hip", "quantize_x": "quantize.hip", "quantize_g": "quantize.hip",
     "gemm_fwd": "gemm.hip", "gemm_dx": "gemm.hip", "gemm_dw": "gemm.hip",
     "dw_reduce": "gemm.hip", "norm_rope_fwd": "epilogue.hip", "norm_rope_bwd": "epilogue.hip",
+    "mlp_amax_w": "quantize.hip", "mlp_quantize_w": "quantize.hip",
+    "mlp_amax_x": "quantize.hip", "mlp_quantize_x": "quantize.hip",
+    "mlp_quantize_h": "quantize.hip", "mlp_amax_dy": "quantize.hip",
+    "mlp_quantize_dy": "quantize.hip", "mlp_quantize_dpre": "quantize.hip",
+    "mlp_gemm_up": "gemm.hip", "mlp_gemm_down": "gemm.hip", "mlp_gemm_dh": "gemm.hip",
+    "mlp_gemm_dx": "gemm.hip", "mlp_gemm_dw1": "gemm.hip", "mlp_gemm_dw2": "gemm.hip",
+    "mlp_dw1_reduce": "gemm.hip", "mlp_dw2_reduce": "gemm.hip",
 }
 
 
@@ -60,6 +78,31 @@ def stage_work(w: dict, dw_splits: int) -> dict:
         "gemm_dx": ("mfma", gemm),
         "gemm_dw": ("mfma", gemm),
         "dw_reduce": ("hbm", dw_splits * 4 * D * N + 4 * D * N),
+    }
+
+
+def mlp_stage_work(w: dict, dw_splits: tuple[int, int]) -> dict:
+    """Algorithmic work per launch of the MLP's stages."""
+    T = w["n_seq"] * w["seq_len"]
+    D, F = w["d_model"], w["d_ff"]
+    gemm = ("mfma", 2 * T * D * F)
+    return {
+        "mlp_amax_w": ("hbm", 4 * D * F),                  # one launch per weight
+        "mlp_quantize_w": ("hbm", 4 * D * F + 2 * D * F),
+        "mlp_amax_x": ("hbm", 2 * T * D),
+        "mlp_quantize_x": ("hbm", 3 * T * D),
+        "mlp_gemm_up": gemm,
+        "mlp_quantize_h": ("hbm", 3 * T * F),
+        "mlp_gemm_down": gemm,
+        "mlp_amax_dy": ("hbm", 2 * T * D),
+        "mlp_quantize_dy": ("hbm", 3 * T * D),
+        "mlp_gemm_dh": gemm,
+        "mlp_quantize_dpre": ("hbm", 3 * T * F),
+        "mlp_gemm_dx": gemm,
+        "mlp_gemm_dw1": gemm,
+        "mlp_dw1_reduce": ("hbm", dw_splits[0] * 4 * D * F + 4 * D * F),
+        "mlp_gemm_dw2": gemm,
+        "mlp_dw2_reduce": ("hbm", dw_splits[1] * 4 * D * F + 4 * D * F),
     }
 
 
@@ -105,19 +148,37 @@ def _oracle_step(w: dict, seed: int, tokens: int) -> float:
     return time.perf_counter() - t0
 
 
-def cpu_baseline(w: dict, seed: int, target_s: float) -> dict:
+def _oracle_mlp_step(w: dict, seed: int, tokens: int) -> float:
+    """Seconds the oracle takes for the MLP's pack + forward + backward of the
+    first `tokens` tokens of the workload."""
+    import oracle
+    from fp8_packed_reduced_amd import inputs
+    wl = dict(w, n_seq=1, seq_len=tokens)
+    x = inputs.make_x(wl, seed)
+    w1, w2 = inputs.make_mlp_w(wl, seed + 1)
+    dy = inputs.make_mlp_dy(wl, seed + 2)
+    oracle.lib()
+    t0 = time.perf_counter()
+    wq = oracle.mlp_quantize_weights(w1, w2)
+    fw = oracle.mlp_forward(x, wq)
+    oracle.mlp_backward(dy, fw["x8"], fw["s_x"], fw["h8"], fw["s_h"], wq)
+    return time.perf_counter() - t0
+
+
+def cpu_baseline(T: int, oracle_step, seed: int, target_s: float) -> dict:
     """The oracle, untouched, timed on a bounded prefix of the workload whose
     length is chosen (in multiples of 4096 tokens, at most the whole
     workload) from a 4096-token probe so that it takes about target_s; when
-    the whole workload takes less, it is run repeatedly for about target_s."""
-    T = w["n_seq"] * w["seq_len"]
+    the whole workload takes less, it is run repeatedly for about target_s.
+    oracle_step(seed, tokens) returns the seconds one step of that prefix
+    takes."""
     probe = min(4096, T)
-    t_probe = _oracle_step(w, seed, probe)
+    t_probe = oracle_step(seed, probe)
     tokens = int(min(T, max(probe, probe * round(target_s / max(t_probe, 1e-3)))))
-    dt = _oracle_step(w, seed, tokens)
+    dt = oracle_step(seed, tokens)
     reps = max(1, int(round(target_s / max(dt, 1e-3)))) if tokens == T else 1
     for _ in range(reps - 1):
-        dt += _oracle_step(w, seed, tokens)
+        dt += oracle_step(seed, tokens)
     try:
         from threadpoolctl import threadpool_info
         cores = max(int(i.get("num_threads", 1)) for i in threadpool_info())
@@ -156,35 +217,89 @@ def main():
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
-    w = inputs.WORKLOADS[args.workload]
-    n_seq, S = w["n_seq"], w["seq_len"]
-    T = n_seq * S
-    D, H, dqk, dvw = w["d_model"], w["n_heads"], w["d_qk"], w["d_v"]
-    N, nq = H * (2 * dqk + dvw), H * dqk
-    dims = B.make_dims(D, H, dqk, dvw, inputs.EPS, inputs.ROPE_BASE)
+    qkv_name, mlp_name = BENCH_WORKLOADS.get(args.workload, (args.workload, None))
+    w = inputs.WORKLOADS[qkv_name] if qkv_name else None
+    wm = inputs.MLP_WORKLOADS[mlp_name] if mlp_name else None
+    T = (w or wm)["n_seq"] * (w or wm)["seq_len"]
 
     def bf16(bits):
         return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16).to(dev)
 
-    x = bf16(inputs.make_x(w, args.seed))
-    W = torch.from_numpy(inputs.make_w(w, args.seed + 1)).to(dev)
-    dq, dk, dv = (bf16(a) for a in inputs.make_dy(w, args.seed + 2))
-    wq, wk, wv = W[:, :nq], W[:, nq:2 * nq], W[:, 2 * nq:]
-    cache = B.WeightCache(dims, dev)
-    ws_p = torch.empty(B.workspace_bytes(dims, 0, B.FPR_CALL_PACK), dtype=torch.uint8, device=dev)
-    ws_f = torch.empty(B.workspace_bytes(dims, T, B.FPR_CALL_FORWARD), dtype=torch.uint8, device=dev)
-    ws_b = torch.empty(B.workspace_bytes(dims, T, B.FPR_CALL_BACKWARD), dtype=torch.uint8, device=dev)
-    saved = torch.empty(B.saved_bytes(dims, T), dtype=torch.uint8, device=dev)
-    q = torch.empty((n_seq, H, S, dqk), dtype=torch.bfloat16, device=dev)
-    k = torch.empty_like(q)
-    v = torch.empty((n_seq, H, S, dvw), dtype=torch.bfloat16, device=dev)
-    dx = torch.empty((T, D), dtype=torch.bfloat16, device=dev)
-    dw = torch.empty((D, N), dtype=torch.float32, device=dev)
+    steps, work, gemm_flop, config, oracle_steps = [], {}, 0, {"workload": args.workload,
+                                                               "tokens": T}, []
+    if w is not None:
+        n_seq, S = w["n_seq"], w["seq_len"]
+        D, H, dqk, dvw = w["d_model"], w["n_heads"], w["d_qk"], w["d_v"]
+        N, nq = H * (2 * dqk + dvw), H * dqk
+        dims = B.make_dims(D, H, dqk, dvw, inputs.EPS, inputs.ROPE_BASE)
+        x = bf16(inputs.make_x(w, args.seed))
+        W = torch.from_numpy(inputs.make_w(w, args.seed + 1)).to(dev)
+        dq, dk, dv = (bf16(a) for a in inputs.make_dy(w, args.seed + 2))
+        wq, wk, wv = W[:, :nq], W[:, nq:2 * nq], W[:, 2 * nq:]
+        cache = B.WeightCache(dims, dev)
+        ws_p = torch.empty(B.workspace_bytes(dims, 0, B.FPR_CALL_PACK), dtype=torch.uint8,
+                           device=dev)
+        ws_f = torch.empty(B.workspace_bytes(dims, T, B.FPR_CALL_FORWARD), dtype=torch.uint8,
+                           device=dev)
+        ws_b = torch.empty(B.workspace_bytes(dims, T, B.FPR_CALL_BACKWARD), dtype=torch.uint8,
+                           device=dev)
+        saved = torch.empty(B.saved_bytes(dims, T), dtype=torch.uint8, device=dev)
+        q = torch.empty((n_seq, H, S, dqk), dtype=torch.bfloat16, device=dev)
+        k = torch.empty_like(q)
+        v = torch.empty((n_seq, H, S, dvw), dtype=torch.bfloat16, device=dev)
+        dx = torch.empty((T, D), dtype=torch.bfloat16, device=dev)
+        dw = torch.empty((D, N), dtype=torch.float32, device=dev)
+
+        def qkv_step():
+            B.pack_quantize_weights(dims, wq, wk, wv, cache, workspace=ws_p)
+            B.qkv_forward(dims, n_seq, S, x, cache, q, k, v, saved, ws_f)
+            B.qkv_backward(dims, n_seq, S, dq, dk, dv, saved, cache, dx, dw, ws_b)
+
+        steps.append(qkv_step)
+        work.update(stage_work(w, B.layout(dims, T).dw_splits))
+        gemm_flop += 3 * 2 * T * D * N
+        config.update(n_seq=n_seq, seq_len=S, d_model=D, n_heads=H, d_qk=dqk, d_v=dvw,
+                      packed_n=N)
+        oracle_steps.append(lambda seed, tokens: _oracle_step(w, seed, tokens))
+    if wm is not None:
+        Dm, F = wm["d_model"], wm["d_ff"]
+        mdims = B.MlpDims(Dm, F)
+        mx = bf16(inputs.make_x(wm, args.seed))
+        w1, w2 = (torch.from_numpy(a).to(dev) for a in inputs.make_mlp_w(wm, args.seed + 1))
+        mdy = bf16(inputs.make_mlp_dy(wm, args.seed + 2))
+        mcache = B.MlpCache(mdims, dev)
+        mws_p = torch.empty(B.mlp_workspace_bytes(mdims, 0, B.FPR_CALL_PACK), dtype=torch.uint8,
+                            device=dev)
+        mws_f = torch.empty(B.mlp_workspace_bytes(mdims, T, B.FPR_CALL_FORWARD),
+                            dtype=torch.uint8, device=dev)
+        mws_b = torch.empty(B.mlp_workspace_bytes(mdims, T, B.FPR_CALL_BACKWARD),
+                            dtype=torch.uint8, device=dev)
+        msaved = torch.empty(B.mlp_saved_bytes(mdims, T), dtype=torch.uint8, device=dev)
+        my = torch.empty((T, Dm), dtype=torch.bfloat16, device=dev)
+        mdx = torch.empty((T, Dm), dtype=torch.bfloat16, device=dev)
+        dw1 = torch.empty((Dm, F), dtype=torch.float32, device=dev)
+        dw2 = torch.empty((F, Dm), dtype=torch.float32, device=dev)
+
+        def mlp_step():
+            B.mlp_pack_quantize_weights(mdims, w1, w2, mcache, workspace=mws_p)
+            B.mlp_forward(mdims, mx, mcache, my, msaved, mws_f)
+            B.mlp_backward(mdims, mdy, msaved, mcache, mdx, dw1, dw2, mws_b)
+
+        steps.append(mlp_step)
+        ml = B.mlp_layout(mdims, T)
+        work.update(mlp_stage_work(wm, (ml.dw1_splits, ml.dw2_splits)))
+        gemm_flop += 6 * 2 * T * Dm * F
+        config.update(d_model=Dm, d_ff=F)
+        oracle_steps.append(lambda seed, tokens: _oracle_mlp_step(wm, seed, tokens))
+    config["step"] = " + ".join(
+        (["pack_quantize_weights + qkv_forward + qkv_backward"] if w is not None else []) +
+        (["mlp_pack_quantize_weights + mlp_forward + mlp_backward"] if wm is not None else []))
+    config["seed"] = args.seed
+    metric = METRIC if wm is None else METRIC_MLP if w is None else METRIC_BLOCK
 
     def step():
-        B.pack_quantize_weights(dims, wq, wk, wv, cache, workspace=ws_p)
-        B.qkv_forward(dims, n_seq, S, x, cache, q, k, v, saved, ws_f)
-        B.qkv_backward(dims, n_seq, S, dq, dk, dv, saved, cache, dx, dw, ws_b)
+        for f in steps:
+            f()
 
     # A streaming kernel of known traffic (the e4m3 encoder: 256 MiB of fp32
     # read, 64 MiB of codes written), so that rocprofv3 byte counters taken on
@@ -198,24 +313,23 @@ def main():
     for _ in range(max(args.warmup, 1)):
         step()
     torch.cuda.synchronize()
-    # Per-stage times: the mean over TRACE_STEPS traced steps (one sample per
-    # stage and step; a single step is too noisy to rank the stages by).
-    with B.KernelTrace(16 * TRACE_STEPS, device=dev) as tr:
+    # Per-stage times: the mean over TRACE_STEPS traced steps (the sum of a
+    # stage's launches in a step; a single step is too noisy to rank by).
+    with B.KernelTrace(32 * TRACE_STEPS, device=dev) as tr:
         for _ in range(TRACE_STEPS):
             step()
     torch.cuda.synchronize()
-    per_stage = {}
+    per_stage, launches = {}, {}
     for name, ms in tr.records():
         per_stage[name] = per_stage.get(name, 0.0) + ms / TRACE_STEPS
-    dw_splits = B.layout(dims, T).dw_splits
-    work = stage_work(w, dw_splits)
+        launches[name] = launches.get(name, 0) + 1
     dominant = max(per_stage, key=per_stage.get)
 
     K = args.steps
     stream = torch.cuda.current_stream(dev)
     e0 = torch.cuda.Event(enable_timing=True)
     e1 = torch.cuda.Event(enable_timing=True)
-    with B.KernelTrace(K, only=dominant, device=dev) as dom:
+    with B.KernelTrace(K * launches[dominant] // TRACE_STEPS, only=dominant, device=dev) as dom:
         torch.cuda.synchronize()
         t_wall = time.perf_counter()
         e0.record(stream)
@@ -235,20 +349,22 @@ def main():
         achieved, peak, unit = amount / dom_avg_s / 1e9, PEAK_HBM_BYTES / 1e9, "GB/s"
     traffic = read_traffic(args.workload, dominant)
 
-    gemm_flop = 3 * 2 * T * D * N
     tflops = gemm_flop / (ms_step / 1e3) / 1e12
     tokens_per_s = T / (ms_step / 1e3)
     kernels = {}
     for name, ms in per_stage.items():
         kd, amt = work[name]
-        rate = amt / (ms / 1e3)
+        n_launch = launches[name] // TRACE_STEPS
+        rate = n_launch * amt / (ms / 1e3)
         kernels[name] = {"us": round(ms * 1e3, 2),
                          ("TFLOP/s" if kd == "mfma" else "GB/s"):
                              round(rate / (1e12 if kd == "mfma" else 1e9), 1),
                          "frac": round(rate / (PEAK_FP8_FLOPS if kd == "mfma" else PEAK_HBM_BYTES), 4)}
+        if n_launch > 1:
+            kernels[name]["launches"] = n_launch
 
     out = {
-        "metric": METRIC,
+        "metric": metric,
         "value": round(tokens_per_s, 1),
         "unit": "tokens/s",
         "n_gpus": 1,
@@ -260,10 +376,7 @@ def main():
         "vs_baseline": None,
         "dtype": "e4m3",
         "data": "synthetic",
-        "config": {"workload": args.workload, "tokens": T, "n_seq": n_seq, "seq_len": S,
-                   "d_model": D, "n_heads": H, "d_qk": dqk, "d_v": dvw, "packed_n": N,
-                   "step": "pack_quantize_weights + qkv_forward + qkv_backward",
-                   "seed": args.seed},
+        "config": config,
         "tflops": round(tflops, 1),
         "pct_fp8_peak": round(100 * tflops * 1e12 / PEAK_FP8_FLOPS, 2),
         "wall_ms_per_step": round(t_wall * 1e3 / K, 4),
@@ -274,7 +387,9 @@ def main():
         "kernels": kernels,
     }
     if not args.no_cpu_baseline:
-        out["cpu_baseline"] = cpu_baseline(w, args.seed, args.cpu_seconds)
+        out["cpu_baseline"] = cpu_baseline(
+            T, lambda seed, tokens: sum(f(seed, tokens) for f in oracle_steps), args.seed,
+            args.cpu_seconds)
     print(json.dumps(out), flush=True)
 
 

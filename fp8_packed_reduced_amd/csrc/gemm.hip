@@ -656,18 +656,26 @@ __device__ __forceinline__ void store_bf16_tile(const v16f (&acc)[C::FM][C::FN],
   const int64_t step = epi.step8(col);
   // this lane's accumulator columns: nl + 32 j + 8 g + 0..3
   const int nl = n0 + wn * C::WN + 4 * (lane >> 5);
-#pragma unroll
-  for (int i = 0; i < C::FM; ++i) {
-    const int ml = mp + i * 32 + (lane & 31);  // this lane's accumulator row
-    uint32_t aux[C::FN][4];
+  // auxiliary inputs of the rows of slice i + 1 are fetched while slice i
+  // is worked on (two slices in flight)
+  uint32_t aux[2][C::FN][4];
+  auto fetch_aux = [&](int i, uint32_t (&dst)[C::FN][4]) {
     if constexpr (Epi::kAux) {
       static_assert(C::WN <= kKBlock, "a lane's columns share one block of h8");
-      const uint8_t* ar = epi.aux_row(ml, nl);
+      const uint8_t* ar = epi.aux_row(mp + i * 32 + (lane & 31), nl);
 #pragma unroll
       for (int j = 0; j < C::FN; ++j)
 #pragma unroll
         for (int g = 0; g < 4; ++g)
-          aux[j][g] = *reinterpret_cast<const uint32_t*>(ar + 32 * j + 8 * g);
+          dst[j][g] = *reinterpret_cast<const uint32_t*>(ar + 32 * j + 8 * g);
+    }
+  };
+  if constexpr (Epi::kAux) fetch_aux(0, aux[0]);
+#pragma unroll
+  for (int i = 0; i < C::FM; ++i) {
+    const int ml = mp + i * 32 + (lane & 31);  // this lane's accumulator row
+    if constexpr (Epi::kAux) {
+      if (i + 1 < C::FM) fetch_aux(i + 1, aux[(i + 1) & 1]);
     }
 #pragma unroll
     for (int j = 0; j < C::FN; ++j)
@@ -676,7 +684,7 @@ __device__ __forceinline__ void store_bf16_tile(const v16f (&acc)[C::FM][C::FN],
         const v16f& a = acc[i][j];
         float v[4] = {a[4 * g] * alpha, a[4 * g + 1] * alpha, a[4 * g + 2] * alpha,
                       a[4 * g + 3] * alpha};
-        if constexpr (Epi::kMap) epi.map(v, Epi::kAux ? aux[j][g] : 0u);
+        if constexpr (Epi::kMap) epi.map(v, Epi::kAux ? aux[i & 1][j][g] : 0u);
         const uint32_t w0 = cvt_bf16x2_rn(v[0], v[1]), w1 = cvt_bf16x2_rn(v[2], v[3]);
         if constexpr (Epi::kAmax) {
           if (ml < M && nl + 32 * j + 8 * g < epi.N) {

@@ -20,8 +20,13 @@ import csv
 import statistics
 import sys
 
-STEP_ORDER = ["amax_w", "quantize_w", "amax_x", "quantize_x", "gemm_fwd", "norm_rope_fwd",
-              "norm_rope_bwd", "quantize_g", "gemm_dx", "gemm_dw", "dw_reduce"]
+# Launch order of one step of each part (a stage may launch more than once)
+QKV_ORDER = ["amax_w", "quantize_w", "amax_x", "quantize_x", "gemm_fwd", "norm_rope_fwd",
+             "norm_rope_bwd", "quantize_g", "gemm_dx", "gemm_dw", "dw_reduce"]
+MLP_ORDER = ["mlp_amax_w", "mlp_quantize_w", "mlp_amax_w", "mlp_quantize_w", "mlp_amax_x",
+             "mlp_quantize_x", "mlp_gemm_up", "mlp_quantize_h", "mlp_gemm_down", "mlp_amax_dy",
+             "mlp_quantize_dy", "mlp_gemm_dh", "mlp_quantize_dpre", "mlp_gemm_dx",
+             "mlp_gemm_dw1", "mlp_dw1_reduce", "mlp_gemm_dw2", "mlp_dw2_reduce"]
 KERNEL_OF_STAGE = {
     "amax_w": "amax_w_kernel", "quantize_w": "quantize_w_kernel",
     "amax_x": "amax_bf16_kernel", "quantize_x": "quantize_act_kernel",
@@ -29,7 +34,21 @@ KERNEL_OF_STAGE = {
     "norm_rope_bwd": "norm_rope_bwd", "quantize_g": "quantize_act_kernel",
     "gemm_dx": "gemm_bf16out_kernel", "gemm_dw": "gemm_dw_part_kernel",
     "dw_reduce": "dw_reduce_kernel",
+    "mlp_amax_w": "amax_w_kernel", "mlp_quantize_w": "quantize_w_kernel",
+    "mlp_amax_x": "amax_bf16_kernel", "mlp_quantize_x": "quantize_act_kernel",
+    "mlp_gemm_up": "EpiRelu2", "mlp_quantize_h": "quantize_act_kernel",
+    "mlp_gemm_down": "EpiDx", "mlp_amax_dy": "amax_bf16_kernel",
+    "mlp_quantize_dy": "quantize_act_kernel", "mlp_gemm_dh": "EpiDpre",
+    "mlp_quantize_dpre": "quantize_act_kernel", "mlp_gemm_dx": "EpiDx",
+    "mlp_gemm_dw1": "gemm_dw_part_kernel", "mlp_dw1_reduce": "dw_reduce_kernel",
+    "mlp_gemm_dw2": "gemm_dw_part_kernel", "mlp_dw2_reduce": "dw_reduce_kernel",
 }
+
+
+def step_order(workload: str) -> list[str]:
+    import bench
+    qkv, mlp = bench.BENCH_WORKLOADS.get(workload, (workload, None))
+    return (QKV_ORDER if qkv else []) + (MLP_ORDER if mlp else [])
 CALIB_KERNEL = "encode_kernel"
 
 
@@ -58,19 +77,19 @@ def _dispatches(path: str, counter: str):
             for r in rows]
 
 
-def _per_stage(path: str, counter: str, known_bytes: float):
+def _per_stage(path: str, counter: str, known_bytes: float, order: list[str]):
     ds = _dispatches(path, counter)
     calib = [v for _, n, v in ds if CALIB_KERNEL in n]
     if not calib:
         raise SystemExit(f"{path}: no calibration launch ({CALIB_KERNEL}) found")
     factor = known_bytes / (statistics.median(calib) * 1024.0)
     step_kernels = [(n, v) for _, n, v in ds if "fpr::" in n and CALIB_KERNEL not in n]
-    if len(step_kernels) % len(STEP_ORDER):
+    if len(step_kernels) % len(order):
         raise SystemExit(f"{path}: {len(step_kernels)} library dispatches is not a whole "
-                         f"number of {len(STEP_ORDER)}-kernel steps")
-    per = {s: [] for s in STEP_ORDER}
+                         f"number of {len(order)}-kernel steps")
+    per = {s: [] for s in order}
     for i, (n, v) in enumerate(step_kernels):
-        stage = STEP_ORDER[i % len(STEP_ORDER)]
+        stage = order[i % len(order)]
         if KERNEL_OF_STAGE[stage] not in n:
             raise SystemExit(f"{path}: dispatch {i} is {n}, expected {stage}")
         per[stage].append(v * 1024.0 * factor)
@@ -81,13 +100,14 @@ def traffic(fetch_csv: str, write_csv: str, workload: str, cmd: str) -> str:
     sys.path.insert(0, ".")
     import bench  # the stage -> source mapping and the calibration size
     n = bench.CALIB_FLOATS
-    fetch, ff = _per_stage(fetch_csv, "FETCH_SIZE", 4.0 * n)
-    write, wf = _per_stage(write_csv, "WRITE_SIZE", 1.0 * n)
+    order = step_order(workload)
+    fetch, ff = _per_stage(fetch_csv, "FETCH_SIZE", 4.0 * n, order)
+    write, wf = _per_stage(write_csv, "WRITE_SIZE", 1.0 * n, order)
     out = [f"# HBM traffic per launch, {workload}: stage fetch_bytes write_bytes source_sha12",
            f"# from rocprofv3 --pmc FETCH_SIZE and --pmc WRITE_SIZE runs of: {cmd}",
            f"# calibration (encoder, {4 * n} B read / {n} B written): fetch x{ff:.4f}, "
            f"write x{wf:.4f}"]
-    for s in STEP_ORDER:
+    for s in dict.fromkeys(order):
         out.append(f"{s} {fetch[s]:.0f} {write[s]:.0f} {bench.source_hash(s)}")
     return "\n".join(out) + "\n"
 
