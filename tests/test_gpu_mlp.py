@@ -133,3 +133,51 @@ def test_mlp_nonfinite_input_sets_status():
     x[5, 7] = 0x7FC0
     r = run_mlp(w, seed=3, x_bits=x, backward=False)
     assert r["status"] & 2
+
+
+def test_mlp_64k_sampled():
+    """The benchmark's MLP workload (T = 65536, D = 768, d_ff = 3072) in its
+    launch configuration: every e4m3 code of x8, h8, dy8 and dpre8 bit-exact
+    against the oracle's quantiser of the GPU's own input to it; sampled
+    token rows of h, y, dpre and dX, and sampled rows of dW1 and dW2, against
+    the oracle computed row by row."""
+    w = inputs.MLP_WORKLOADS["mlp_64k"]
+    r = run_mlp(w, seed=42)
+    T, D, F = r["T"], w["d_model"], w["d_ff"]
+    wq = oracle.mlp_quantize_weights(r["w1"], r["w2"])
+    for k in ("w1", "w1_t", "w2", "w2_t"):
+        assert np.array_equal(r["c_" + k], wq[k.replace("_", "")]), k
+    x8, s_x, _, _ = oracle.quantize_bf16(r["x_bits"])
+    assert np.array_equal(r["x8"], x8) and r["x_scales"][0] == s_x
+    h8, s_h, _, _ = oracle.quantize_bf16(r["h"])
+    assert np.array_equal(r["h8"], h8) and r["h_scales"][0] == s_h
+    dy8, s_dy, _, _ = oracle.quantize_bf16(r["dy"])
+    assert np.array_equal(r["dy8"], dy8) and r["dy_scales"][0] == s_dy
+    dp8, s_dp, _, _ = oracle.quantize_bf16(r["dpre"])
+    assert np.array_equal(r["dp8"], dp8) and r["dp_scales"][0] == s_dp
+    assert not r["x8_tail"].any() and not r["h8_tail"].any() and not r["dp8_tail"].any()
+    rng = np.random.default_rng(1)
+    rows = np.unique(np.concatenate([[0, 1, T // 2, T - 2, T - 1], rng.integers(0, T, 27)]))
+    say(f"[gpu] mlp 64k: checking {rows.size} token rows")
+    w1c = wq["w1"]
+    h_exact = oracle.relu2(oracle.gemm_e4m3(x8[rows], w1c, s_x, wq["s_w1"]))
+    _check_bf16_gemm("h rows", r["h"][rows], h_exact)
+    _check_bf16_gemm("y rows", r["y"][rows], oracle.gemm_e4m3(h8[rows], wq["w2"], s_h, wq["s_w2"]))
+    dh = oracle.gemm_e4m3(dy8[rows], np.ascontiguousarray(wq["w2"].T), s_dy, wq["s_w2"])
+    dpre_exact = oracle.relu2_grad(dh, float(s_h) * oracle.e4m3_decode(h8[rows]))
+    _check_bf16_gemm("dpre rows", r["dpre"][rows], dpre_exact)
+    _check_bf16_gemm("dx rows", r["dx"][rows],
+                     oracle.gemm_e4m3(dp8[rows], np.ascontiguousarray(w1c.T), s_dp, wq["s_w1"]))
+    # dW1 rows i: x8[:, i]^T dpre8; dW2 rows f: h8[:, f]^T dy8
+    tab = oracle.e4m3_decode_table()
+    di, df = [0, 383, D - 1], [0, 1537, F - 1]
+    w1_rows, w2_rows = np.zeros((len(di), F)), np.zeros((len(df), D))
+    for t0 in range(0, T, 8192):  # float64 sums over token chunks
+        sl = slice(t0, t0 + 8192)
+        w1_rows += tab[x8[sl][:, di]].T @ tab[dp8[sl]]
+        w2_rows += tab[h8[sl][:, df]].T @ tab[dy8[sl]]
+    e1 = row_rel_err(r["dw1"][di], float(s_x) * float(s_dp) * w1_rows)
+    e2 = row_rel_err(r["dw2"][df], float(s_h) * float(s_dy) * w2_rows)
+    say(f"[gpu] mlp 64k dw1 rows {e1:.2e} dw2 rows {e2:.2e}")
+    assert e1 <= GEMM_TOL and e2 <= GEMM_TOL
+    assert r["status"] == 0
