@@ -97,6 +97,20 @@ def lib():
             ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p, ctypes.c_int64,
             ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p, ctypes.c_void_p,
             ctypes.c_void_p]
+        L.orc_e5m2_decode.restype = ctypes.c_double
+        L.orc_e5m2_decode.argtypes = [ctypes.c_uint8]
+        L.orc_e5m2_decode_table.argtypes = [ctypes.c_void_p]
+        L.orc_e5m2_encode.restype = ctypes.c_uint8
+        L.orc_e5m2_encode.argtypes = [ctypes.c_float]
+        L.orc_e5m2_encode_search.restype = ctypes.c_uint8
+        L.orc_e5m2_encode_search.argtypes = [ctypes.c_float]
+        L.orc_e5m2_encoders_disagree.restype = ctypes.c_int64
+        L.orc_e5m2_encoders_disagree.argtypes = [
+            ctypes.c_uint64, ctypes.c_uint64, ctypes.POINTER(ctypes.c_uint32)]
+        L.orc_e5m2_encode_array.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p]
+        L.orc_quantize_bf16_e5m2.restype = ctypes.c_int
+        L.orc_quantize_bf16_e5m2.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p,
+                                             ctypes.c_void_p]
         L.orc_round_bf16.restype = ctypes.c_uint16
         L.orc_round_bf16.argtypes = [ctypes.c_double]
         L.orc_round_bf16_array.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p]
@@ -142,6 +156,40 @@ def e4m3_encoders_disagree(begin: int, end: int):
     return int(n), int(first.value)
 
 
+def e5m2_decode_table() -> np.ndarray:
+    """float64 value of each of the 256 e5m2 codes (+-inf, NaN included)."""
+    t = np.empty(256, dtype=np.float64)
+    lib().orc_e5m2_decode_table(_ptr(t))
+    return t
+
+
+def e5m2_decode(codes: np.ndarray) -> np.ndarray:
+    return e5m2_decode_table()[np.asarray(codes, dtype=np.uint8)]
+
+
+def e5m2_encode(v) -> np.ndarray:
+    """Nearest e5m2 code of each fp32 value (arithmetic encoder)."""
+    v = np.ascontiguousarray(v, dtype=np.float32)
+    out = np.empty(v.shape, dtype=np.uint8)
+    lib().orc_e5m2_encode_array(_ptr(v), v.size, _ptr(out))
+    return out
+
+
+def e5m2_encode_search_scalar(v: float) -> int:
+    return int(lib().orc_e5m2_encode_search(ctypes.c_float(v)))
+
+
+def e5m2_encoders_disagree(begin: int, end: int):
+    """(count, first bad fp32 pattern) of the two e5m2 encoders over [begin, end)."""
+    first = ctypes.c_uint32(0)
+    n = lib().orc_e5m2_encoders_disagree(begin, end, ctypes.byref(first))
+    return int(n), int(first.value)
+
+
+def decode_table(fmt: str) -> np.ndarray:
+    return {"e4m3": e4m3_decode_table, "e5m2": e5m2_decode_table}[fmt]()
+
+
 def quantize_f32(v: np.ndarray):
     """Per-tensor e4m3 quantisation of fp32 values -> (codes, s, inv, rc)."""
     v = np.ascontiguousarray(v, dtype=np.float32)
@@ -151,12 +199,14 @@ def quantize_f32(v: np.ndarray):
     return codes, np.float32(sc[0]), np.float32(sc[1]), int(rc)
 
 
-def quantize_bf16(bits: np.ndarray):
-    """Per-tensor e4m3 quantisation of bf16 values given as uint16 patterns."""
+def quantize_bf16(bits: np.ndarray, fmt: str = "e4m3"):
+    """Per-tensor e4m3 (or e5m2) quantisation of bf16 values given as uint16
+    patterns -> (codes, s, inv, rc)."""
     bits = np.ascontiguousarray(bits, dtype=np.uint16)
     codes = np.empty(bits.shape, dtype=np.uint8)
     sc = np.empty(2, dtype=np.float32)
-    rc = lib().orc_quantize_bf16(_ptr(bits), bits.size, _ptr(codes), _ptr(sc))
+    fn = {"e4m3": lib().orc_quantize_bf16, "e5m2": lib().orc_quantize_bf16_e5m2}[fmt]
+    rc = fn(_ptr(bits), bits.size, _ptr(codes), _ptr(sc))
     return codes, np.float32(sc[0]), np.float32(sc[1]), int(rc)
 
 
@@ -215,12 +265,13 @@ def pack_quantize(D, H, d_qk, d_v, wq, wk, wv):
 
 # ------------------------------------------------------------------ GEMM
 
-def gemm_e4m3(a_codes: np.ndarray, b_codes: np.ndarray, s_a, s_b) -> np.ndarray:
+def gemm_e4m3(a_codes: np.ndarray, b_codes: np.ndarray, s_a, s_b, a_fmt: str = "e4m3",
+              b_fmt: str = "e4m3") -> np.ndarray:
     """C = s_a * s_b * dec(A) @ dec(B) in float64 ("96 is enough", "The
-    change": qkv = fp8_matmul(x, W_packed)).  A is [M][K], B is [K][N]."""
-    tab = e4m3_decode_table()
-    A = tab[a_codes]
-    B = tab[b_codes]
+    change": qkv = fp8_matmul(x, W_packed)).  A is [M][K], B is [K][N]; each
+    operand's codes are e4m3 unless its format says e5m2."""
+    A = decode_table(a_fmt)[a_codes]
+    B = decode_table(b_fmt)[b_codes]
     return (float(s_a) * float(s_b)) * (A @ B)
 
 
@@ -339,11 +390,13 @@ def qkv_forward(dims, n_seq: int, S: int, x_bits: np.ndarray,
 
 def qkv_backward(dims, n_seq: int, S: int, dq_bits, dk_bits, dv_bits,
                  x8: np.ndarray, s_x, qk_pre_bits: np.ndarray,
-                 w_packed: np.ndarray, s_w, dqkv_bits: np.ndarray | None = None):
+                 w_packed: np.ndarray, s_w, dqkv_bits: np.ndarray | None = None,
+                 grad_fmt: str = "e4m3"):
     """Backward chain.  dq/dk/dv: head-major bf16 patterns.  qk_pre_bits:
     [T][2*H*d_qk] bf16 pre-norm Q|K (saved by the forward).  If
     ``dqkv_bits`` is given, the GEMM stages are fed it instead of the
-    oracle's own packed gradient (stage-wise comparison)."""
+    oracle's own packed gradient (stage-wise comparison).  ``grad_fmt``
+    "e5m2" quantises the packed gradient to e5m2 instead of e4m3."""
     H, d_qk, d_v = dims["n_heads"], dims["d_qk"], dims["d_v"]
     eps, base = dims["eps"], dims["rope_base"]
     _, k0, v0, N = packed_columns(H, d_qk, d_v)
@@ -365,14 +418,14 @@ def qkv_backward(dims, n_seq: int, S: int, dq_bits, dk_bits, dv_bits,
         out["dqkv64"] = dqkv64
         dqkv_bits = round_bf16(dqkv64)
     out["dqkv_bits"] = dqkv_bits
-    g8, s_g, inv_g, rc_g = quantize_bf16(dqkv_bits)
+    g8, s_g, inv_g, rc_g = quantize_bf16(dqkv_bits, grad_fmt)
     out.update(g8=g8, s_g=s_g, inv_g=inv_g, rc_g=rc_g)
     # dX = dQKV @ W_packed^T, through the cached [D][N] codes
-    dx64 = gemm_e4m3(g8, np.ascontiguousarray(w_packed.T), s_g, s_w)
+    dx64 = gemm_e4m3(g8, np.ascontiguousarray(w_packed.T), s_g, s_w, a_fmt=grad_fmt)
     out["dx64"] = dx64
     out["dx_bits"] = round_bf16(dx64)
     # dW = x^T @ dQKV
-    dw64 = gemm_e4m3(np.ascontiguousarray(x8.T), g8, s_x, s_g)
+    dw64 = gemm_e4m3(np.ascontiguousarray(x8.T), g8, s_x, s_g, b_fmt=grad_fmt)
     out["dw64"] = dw64
     out["dw_f32"] = round_f32(dw64)
     return out

@@ -346,3 +346,171 @@ void orc_round_f32_array(const double* x, int64_t n, float* out)
     for (int64_t i = 0; i < n; ++i)
         out[i] = (float)x[i];
 }
+
+/* ================================================================ e5m2
+ *
+ * Optional gradient format (the attention-ready variants: FP8 gradients in
+ * OCP FP8 E5M2, whose wider exponent range suits gradients).  OCP E5M2:
+ * sign bit 7, exponent bits 6..2 (bias 15), mantissa bits 1..0; exponent 0
+ * is subnormal (2^-14 * m/4); exponent 31 holds infinity (m = 0) and NaN
+ * (m != 0); the largest finite value is 1.75 * 2^15 = 57344.
+ *
+ * Readings, as for e4m3: round to nearest, ties to even, saturating at
+ * +-57344 (never infinity), sign kept; per-tensor scale
+ * s = fl32(amax / 57344), inv = fl32(57344 / amax), codes enc(fl32(v * inv)).
+ */
+
+double orc_e5m2_decode(uint8_t code)
+{
+    int s = (code >> 7) & 1;
+    int e = (code >> 2) & 31;
+    int m = code & 3;
+    double mag;
+    if (e == 31)
+        mag = (m == 0) ? INFINITY : NAN;
+    else if (e == 0)
+        mag = ldexp((double)m / 4.0, -14);
+    else
+        mag = ldexp(1.0 + (double)m / 4.0, e - 15);
+    if (isnan(mag))
+        return NAN;
+    return s ? -mag : mag;
+}
+
+void orc_e5m2_decode_table(double out[256])
+{
+    for (int c = 0; c < 256; ++c)
+        out[c] = orc_e5m2_decode((uint8_t)c);
+}
+
+/* Nearest e5m2 code by exponent / mantissa arithmetic (see orc_e4m3_encode). */
+uint8_t orc_e5m2_encode(float v)
+{
+    uint8_t sign = signbit(v) ? 0x80 : 0x00;
+    double a = fabs((double)v);
+    if (isnan(v))
+        return (uint8_t)(sign | 0x7F);
+    if (a >= 57344.0)
+        return (uint8_t)(sign | 0x7B);
+    if (a < ldexp(1.0, -14)) {
+        /* subnormal grid: multiples of 2^-16; 4 is the smallest normal */
+        double r = nearbyint(a / ldexp(1.0, -16));
+        return (uint8_t)(sign | (uint8_t)r);
+    }
+    int ex;
+    (void)frexp(a, &ex);
+    int e = ex - 1;                          /* a = (2f) * 2^e, 2f in [1, 2) */
+    double r = nearbyint(ldexp(a, 2 - e));   /* significand in quarters: [4, 8] */
+    if (r == 8.0) {
+        r = 4.0;
+        e += 1;
+    }
+    int efield = e + 15;                     /* 1..30 below 57344 */
+    return (uint8_t)(sign | (efield << 2) | ((int)r - 4));
+}
+
+static double g_pos5[124];                   /* finite non-negative values, codes 0..0x7B */
+static int g_pos5_ready = 0;
+
+static void build_pos5(void)
+{
+    if (g_pos5_ready)
+        return;
+    for (int c = 0; c < 124; ++c)
+        g_pos5[c] = orc_e5m2_decode((uint8_t)c);
+    g_pos5_ready = 1;
+}
+
+/* Nearest e5m2 code by bisection over the sorted finite values. */
+uint8_t orc_e5m2_encode_search(float v)
+{
+    build_pos5();
+    uint8_t sign = signbit(v) ? 0x80 : 0x00;
+    double a = fabs((double)v);
+    if (isnan(v))
+        return (uint8_t)(sign | 0x7F);
+    if (a >= g_pos5[123])
+        return (uint8_t)(sign | 123);
+    int lo = 0, hi = 123;
+    while (hi - lo > 1) {
+        int mid = (lo + hi) / 2;
+        if (g_pos5[mid] <= a)
+            lo = mid;
+        else
+            hi = mid;
+    }
+    double dlo = a - g_pos5[lo];
+    double dhi = g_pos5[hi] - a;
+    int pick;
+    if (dlo < dhi)
+        pick = lo;
+    else if (dhi < dlo)
+        pick = hi;
+    else
+        pick = (lo % 2 == 0) ? lo : hi;
+    return (uint8_t)(sign | pick);
+}
+
+int64_t orc_e5m2_encoders_disagree(uint64_t begin, uint64_t end, uint32_t* first_bad)
+{
+    build_pos5();
+    int64_t bad = 0;
+    uint64_t first = UINT64_MAX;
+#pragma omp parallel for schedule(static) reduction(+ : bad) reduction(min : first)
+    for (int64_t i = (int64_t)begin; i < (int64_t)end; ++i) {
+        uint32_t bits = (uint32_t)i;
+        float v;
+        memcpy(&v, &bits, 4);
+        if (isnan(v))
+            continue;
+        if (orc_e5m2_encode(v) != orc_e5m2_encode_search(v)) {
+            bad += 1;
+            if ((uint64_t)i < first)
+                first = (uint64_t)i;
+        }
+    }
+    if (first_bad)
+        *first_bad = (first == UINT64_MAX) ? 0u : (uint32_t)first;
+    return bad;
+}
+
+void orc_e5m2_encode_array(const float* v, int64_t n, uint8_t* codes)
+{
+#pragma omp parallel for schedule(static)
+    for (int64_t i = 0; i < n; ++i)
+        codes[i] = orc_e5m2_encode(v[i]);
+}
+
+/* Per-tensor e5m2 quantisation of bf16 patterns; as orc_quantize_bf16 with
+ * 57344 in place of 448. */
+int orc_quantize_bf16_e5m2(const uint16_t* v, int64_t n, uint8_t* codes, float* scales_out)
+{
+    float amax = 0.0f;
+    int nan_seen = 0;
+    for (int64_t i = 0; i < n; ++i) {
+        float a = fabsf(bf16_bits_to_f32(v[i]));
+        if (isnan(a))
+            nan_seen = 1;
+        else if (a > amax)
+            amax = a;
+    }
+    if (nan_seen)
+        amax = NAN;
+    float s = 1.0f, inv = 1.0f;
+    int rc = 0;
+    if (!isfinite(amax)) {
+        rc = 1;
+    } else {
+        float i = 57344.0f / amax;
+        if (amax != 0.0f && isfinite(i)) {
+            s = amax / 57344.0f;
+            inv = i;
+        }
+    }
+#pragma omp parallel for schedule(static)
+    for (int64_t i = 0; i < n; ++i)
+        codes[i] = orc_e5m2_encode(bf16_bits_to_f32(v[i]) * inv);
+    scales_out[0] = s;
+    scales_out[1] = inv;
+    return rc;
+}
