@@ -202,6 +202,8 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="approximate CPU time of the oracle baseline sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--grad-format", choices=["e4m3", "e5m2"], default="e4m3",
+                    help="FP8 format of the QKV backward's packed gradient")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: this path runs on a single MI355X and has no "
@@ -231,7 +233,8 @@ def main():
         n_seq, S = w["n_seq"], w["seq_len"]
         D, H, dqk, dvw = w["d_model"], w["n_heads"], w["d_qk"], w["d_v"]
         N, nq = H * (2 * dqk + dvw), H * dqk
-        dims = B.make_dims(D, H, dqk, dvw, inputs.EPS, inputs.ROPE_BASE)
+        gfmt = B.FORMAT_E5M2 if args.grad_format == "e5m2" else B.FORMAT_E4M3
+        dims = B.make_dims(D, H, dqk, dvw, inputs.EPS, inputs.ROPE_BASE, grad_format=gfmt)
         x = bf16(inputs.make_x(w, args.seed))
         W = torch.from_numpy(inputs.make_w(w, args.seed + 1)).to(dev)
         dq, dk, dv = (bf16(a) for a in inputs.make_dy(w, args.seed + 2))
@@ -260,6 +263,8 @@ def main():
         gemm_flop += 3 * 2 * T * D * N
         config.update(n_seq=n_seq, seq_len=S, d_model=D, n_heads=H, d_qk=dqk, d_v=dvw,
                       packed_n=N)
+        if args.grad_format != "e4m3":
+            config["grad_format"] = args.grad_format
         oracle_steps.append(lambda seed, tokens: _oracle_step(w, seed, tokens))
     if wm is not None:
         Dm, F = wm["d_model"], wm["d_ff"]

@@ -18,6 +18,7 @@ HEADER = os.path.join(os.path.dirname(HERE), "include", "fpr.h")
 
 FPR_CALL_PACK, FPR_CALL_FORWARD, FPR_CALL_BACKWARD = 0, 1, 2
 STATUS_W_NONFINITE, STATUS_X_NONFINITE, STATUS_G_NONFINITE, STATUS_H_NONFINITE = 1, 2, 4, 8
+FORMAT_E4M3, FORMAT_E5M2 = 0, 1
 
 
 class FprError(RuntimeError):
@@ -30,7 +31,7 @@ class Dims(ctypes.Structure):
     _fields_ = [("d_model", ctypes.c_int32), ("n_heads", ctypes.c_int32),
                 ("d_qk", ctypes.c_int32), ("d_v", ctypes.c_int32),
                 ("eps", ctypes.c_float), ("rope_base", ctypes.c_float),
-                ("qk_stride", ctypes.c_int32)]
+                ("qk_stride", ctypes.c_int32), ("grad_format", ctypes.c_int32)]
 
     @property
     def n_packed(self) -> int:
@@ -125,6 +126,8 @@ def load():
     L.fpr_trace_set.argtypes = [ctypes.POINTER(_TraceC)]
     L.fpr_e4m3_encode.restype = ctypes.c_int
     L.fpr_e4m3_encode.argtypes = [_V, _I64, ctypes.c_float, _V, _V]
+    L.fpr_e5m2_encode.restype = ctypes.c_int
+    L.fpr_e5m2_encode.argtypes = [_V, _I64, ctypes.c_float, _V, _V]
     L.fpr_mlp_workspace_bytes.restype = _SZ
     L.fpr_mlp_workspace_bytes.argtypes = [P(MlpDims), _I64, ctypes.c_int]
     L.fpr_mlp_saved_bytes.restype = _SZ
@@ -154,9 +157,11 @@ def status_string(code: int) -> str:
 
 
 def make_dims(d_model: int, n_heads: int, d_qk: int = 96, d_v: int = 128,
-              eps: float = 1e-6, rope_base: float = 10000.0, qk_stride: int = 0) -> Dims:
-    """qk_stride > d_qk pads every q/k head row with zeros to that width."""
-    return Dims(d_model, n_heads, d_qk, d_v, eps, rope_base, qk_stride)
+              eps: float = 1e-6, rope_base: float = 10000.0, qk_stride: int = 0,
+              grad_format: int = FORMAT_E4M3) -> Dims:
+    """qk_stride > d_qk pads every q/k head row with zeros to that width;
+    grad_format FORMAT_E5M2 quantises the backward's packed gradient to e5m2."""
+    return Dims(d_model, n_heads, d_qk, d_v, eps, rope_base, qk_stride, grad_format)
 
 
 def workspace_bytes(dims: Dims, tokens: int, which: int) -> int:
@@ -294,15 +299,16 @@ def qkv_backward(dims: Dims, n_seq: int, seq_len: int, dq, dk, dv, saved, cache:
     return dx, dw
 
 
-def e4m3_encode(values: torch.Tensor, inv_scale: float = 1.0) -> torch.Tensor:
-    """Device encoder hook: e4m3(values * inv_scale), no amax."""
+def e4m3_encode(values: torch.Tensor, inv_scale: float = 1.0, e5m2: bool = False) -> torch.Tensor:
+    """Device encoder hook: e4m3(values * inv_scale) (or e5m2), no amax."""
     if values.dtype != torch.float32 or not values.is_cuda or not values.is_contiguous():
         raise ValueError("values must be a contiguous float32 GPU tensor")
     out = torch.empty(values.shape, dtype=torch.uint8, device=values.device)
-    rc = load().fpr_e4m3_encode(values.data_ptr(), values.numel(), inv_scale, out.data_ptr(),
-                                _stream(values.device))
+    fn, name = ((load().fpr_e5m2_encode, "fpr_e5m2_encode") if e5m2
+                else (load().fpr_e4m3_encode, "fpr_e4m3_encode"))
+    rc = fn(values.data_ptr(), values.numel(), inv_scale, out.data_ptr(), _stream(values.device))
     if rc:
-        raise FprError(rc, "fpr_e4m3_encode")
+        raise FprError(rc, name)
     return out
 
 

@@ -37,6 +37,7 @@ bool dims_ok(const fpr_dims* d) {
   if (d->d_model <= 0 || d->n_heads <= 0 || d->d_qk <= 0 || d->d_v <= 0) return false;
   if (!(d->eps >= 0.0f) || !(d->rope_base > 0.0f)) return false;
   if (d->qk_stride < 0) return false;
+  if (d->grad_format != FPR_FORMAT_E4M3 && d->grad_format != FPR_FORMAT_E5M2) return false;
   return true;
 }
 
@@ -361,15 +362,16 @@ int qkv_backward(const fpr_dims* dims, int32_t n_seq, int32_t seq_len, const uin
     fpr::launch_norm_rope_bwd(dq, dk, dv, qk, T, seq_len, p.H, p.dqk, p.qs, p.dv, dims->eps,
                               dims->rope_base, dqkv, parts, s);
   });
+  const bool e5 = dims->grad_format == FPR_FORMAT_E5M2;
   stage("quantize_g", s, [&] {
     fpr::launch_quantize_act_split(dqkv, p.nqk2, dv, p.dv, p.H, seq_len, T, p.N, parts,
                                    p.b_parts, gsc, cache->status, FPR_STATUS_G_NONFINITE, g8,
-                                   p.Tp, s);
+                                   p.Tp, s, e5);
   });
   stage("gemm_dx", s, [&] {
-    fpr::launch_gemm_dx(g8, cache->w_packed, (int)T, p.D, p.N, gsc, cache->scales, dx, s);
+    fpr::launch_gemm_dx(g8, cache->w_packed, (int)T, p.D, p.N, gsc, cache->scales, dx, s, e5);
   });
-  stage("gemm_dw", s, [&] { fpr::launch_gemm_dw(x8, g8, p.D, p.N, p.Tp, dwpart, s); });
+  stage("gemm_dw", s, [&] { fpr::launch_gemm_dw(x8, g8, p.D, p.N, p.Tp, dwpart, s, e5); });
   stage("dw_reduce", s, [&] {
     fpr::launch_dw_reduce(dwpart, p.D, p.N, p.Tp, xsc, gsc, dwq, ldq, dwk, ldk, dwv, ldv, p.nq, s);
   });
@@ -565,7 +567,15 @@ int fpr_e4m3_encode(const float* in, int64_t n, float inv_scale, uint8_t* out, v
   if (!in || !out || n <= 0) return FPR_ERR_ARG;
   if (!al16(in) || !al16(out) || n % 16) return FPR_ERR_ALIGN;
   (void)hipGetLastError();
-  fpr::launch_encode(in, n, inv_scale, out, static_cast<hipStream_t>(stream));
+  fpr::launch_encode(in, n, inv_scale, out, static_cast<hipStream_t>(stream), false);
+  return finish();
+}
+
+int fpr_e5m2_encode(const float* in, int64_t n, float inv_scale, uint8_t* out, void* stream) {
+  if (!in || !out || n <= 0) return FPR_ERR_ARG;
+  if (!al16(in) || !al16(out) || n % 16) return FPR_ERR_ALIGN;
+  (void)hipGetLastError();
+  fpr::launch_encode(in, n, inv_scale, out, static_cast<hipStream_t>(stream), true);
   return finish();
 }
 

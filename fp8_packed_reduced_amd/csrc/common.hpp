@@ -54,6 +54,25 @@ __device__ inline uint32_t e4m3x4(float a, float b, float c, float d) {
   return (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(sat448(c), sat448(d), lo, true);
 }
 
+// OCP E5M2 (the optional gradient format) through the gfx950 converter,
+// clamped to +-57344 first so that it saturates instead of overflowing.
+constexpr float kE4m3Max = 448.0f, kE5m2Max = 57344.0f;
+__device__ inline float sat57344(float v) { return __builtin_amdgcn_fmed3f(v, -kE5m2Max, kE5m2Max); }
+
+__device__ inline uint32_t e5m2x4(float a, float b, float c, float d) {
+  int lo = __builtin_amdgcn_cvt_pk_bf8_f32(sat57344(a), sat57344(b), 0, false);
+  return (uint32_t)__builtin_amdgcn_cvt_pk_bf8_f32(sat57344(c), sat57344(d), lo, true);
+}
+
+// Four fp32 values -> four codes of format E5 (e5m2) or e4m3.
+template <bool E5>
+__device__ inline uint32_t fp8x4(float a, float b, float c, float d) {
+  if constexpr (E5)
+    return e5m2x4(a, b, c, d);
+  else
+    return e4m3x4(a, b, c, d);
+}
+
 // ------------------------------------------------------------ reductions
 
 __device__ inline uint32_t wave_max_u32(uint32_t v) {

@@ -51,11 +51,16 @@ constexpr int kBK = 128;  // bytes (= e4m3 elements) of K per step
 constexpr int kCopyWaves = 4;
 constexpr int kStages = 3;
 
+// Operand formats of the matrix cores' f8f6f4 instructions (the codes of
+// their cbsz / blgp fields): OCP E4M3 and OCP E5M2.
+constexpr int kFmtE4M3 = 0, kFmtE5M2 = 1;
+
 // A BM x BN tile computed by MW x NW matrix waves (wave w: rows w / NW,
-// columns w % NW) and filled by kCopyWaves copy waves.
-template <int BM, int BN, int MW = 2, int NW = 2>
+// columns w % NW) and filled by kCopyWaves copy waves; A and B hold codes
+// of format FA and FB.
+template <int BM, int BN, int MW = 2, int NW = 2, int FA = kFmtE4M3, int FB = kFmtE4M3>
 struct TileCfg {
-  static constexpr int BM_ = BM, BN_ = BN;
+  static constexpr int BM_ = BM, BN_ = BN, FA_ = FA, FB_ = FB;
   static constexpr int MMA = MW * NW, NW_ = NW;
   static constexpr int THREADS = 64 * (MMA + kCopyWaves);
   static constexpr int WM = BM / MW, WN = BN / NW;     // one matrix wave's part
@@ -164,8 +169,11 @@ __device__ __forceinline__ v8i frag_b(const uint8_t* stage, int b0, int lane, in
   else return lds_frag(stage + C::BM_ * kBK, b0 + (lane & 31), lane >> 5, h);
 }
 
+// The instruction's first operand is B (format field cbsz), its second A
+// (blgp).
+template <class C>
 __device__ __forceinline__ v16f mfma32(v8i b, v8i a, v16f c) {
-  return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(b, a, c, 0, 0, 0, 127, 0, 127);
+  return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(b, a, c, C::FB_, C::FA_, 0, 127, 0, 127);
 }
 
 // ------------------------------------------------------------ schedule
@@ -390,7 +398,7 @@ __device__ __forceinline__ void mma_half(v16f (&acc)[C::FM][C::FN], Half<C>& f, 
 #pragma unroll
   for (int i = 0; i < C::FM; ++i) {
 #pragma unroll
-    for (int j = 0; j < C::FN; ++j) acc[i][j] = mfma32(f.b[j], f.a[i], FIRST ? v16f{} : acc[i][j]);
+    for (int j = 0; j < C::FN; ++j) acc[i][j] = mfma32<C>(f.b[j], f.a[i], FIRST ? v16f{} : acc[i][j]);
     f.a[i] = frag_a<C, TOK>(src, a0 + i * 32, lane, h);
 #pragma unroll
     for (int j = 0; j < C::FN; ++j) {
@@ -418,7 +426,7 @@ __device__ __forceinline__ void mma_half_barrier(v16f (&acc)[C::FM][C::FN], Half
 #pragma unroll
   for (int i = 0; i < ER; ++i)
 #pragma unroll
-    for (int j = 0; j < C::FN; ++j) acc[i][j] = mfma32(f.b[j], f.a[i], acc[i][j]);
+    for (int j = 0; j < C::FN; ++j) acc[i][j] = mfma32<C>(f.b[j], f.a[i], acc[i][j]);
   // scheduling fences: the barrier orders memory accesses only, and the
   // compiler would otherwise sink the early MFMAs below it
   __builtin_amdgcn_sched_barrier(0);
@@ -432,7 +440,7 @@ __device__ __forceinline__ void mma_half_barrier(v16f (&acc)[C::FM][C::FN], Half
 #pragma unroll
   for (int i = ER; i < C::FM; ++i) {
 #pragma unroll
-    for (int j = 0; j < C::FN; ++j) acc[i][j] = mfma32(f.b[j], f.a[i], acc[i][j]);
+    for (int j = 0; j < C::FN; ++j) acc[i][j] = mfma32<C>(f.b[j], f.a[i], acc[i][j]);
     f.a[i] = frag_a<C, TOK>(src, a0 + i * 32, lane, h);
 #pragma unroll
     for (int j = 0; j < C::FN; ++j) {
@@ -750,10 +758,10 @@ __device__ __forceinline__ void persistent_tiles(Sched& sc, int b, int G, int nt
   sc.steps = mine * sc.nk;
 }
 
-template <int BM, int BN, bool KTAIL, class Epi>
+template <int BM, int BN, bool KTAIL, class Epi, int FA = kFmtE4M3>
 __global__ __launch_bounds__((TileCfg<BM, BN>::THREADS), 1) void gemm_bf16out_kernel(
     Gemm gm, int ntiles, const float* __restrict__ sa, const float* __restrict__ sb, Epi epi) {
-  using C = TileCfg<BM, BN>;
+  using C = TileCfg<BM, BN, 2, 2, FA>;
   __shared__ __attribute__((aligned(16))) uint8_t lds[kStages * C::STAGE_BYTES];
   __shared__ __attribute__((aligned(16))) uint8_t slices[C::MMA * WaveSlice<C>::BYTES];
   const int lane = threadIdx.x & 63;
@@ -790,10 +798,10 @@ __global__ __launch_bounds__((TileCfg<BM, BN>::THREADS), 1) void gemm_bf16out_ke
 // so the blocks of one XCD share K ranges and rows of both operands in its
 // L2.  Unscaled fp32 partial sums go to part[split][m][n]; a split with no
 // K steps writes zeros.
-template <int BM, int BN, int MW, int NW>
+template <int BM, int BN, int MW, int NW, int FB = kFmtE4M3>
 __global__ __launch_bounds__((TileCfg<BM, BN, MW, NW>::THREADS), 1) void gemm_dw_part_kernel(
     Gemm gm, int splits, int ksteps_per_split, float* __restrict__ part) {
-  using C = TileCfg<BM, BN, MW, NW>;
+  using C = TileCfg<BM, BN, MW, NW, kFmtE4M3, FB>;
   __shared__ __attribute__((aligned(16))) uint8_t lds[kStages * C::STAGE_BYTES];
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -864,18 +872,17 @@ static int cu_count() {
 // fills are blocks * 4, at most kEpiAmaxBlocks * 4).
 constexpr int kEpiAmaxBlocks = 256;
 
-template <class Epi>
+template <class Epi, int FA = kFmtE4M3>
 static int launch_bf16out(const Gemm& gm, const float* sa, const float* sb, const Epi& epi,
                           hipStream_t s) {
   const int ntiles = (int)ceil_div(gm.M, kBMo) * gm.n_tiles;
   const int cus = Epi::kAmax ? std::min(cu_count(), kEpiAmaxBlocks) : cu_count();
   const int blocks = ntiles < cus ? ntiles : cus;
+  constexpr int kThr = TileCfg<kBMo, kBNo>::THREADS;
   if (gm.K % kBK)
-    gemm_bf16out_kernel<kBMo, kBNo, true, Epi><<<blocks, TileCfg<kBMo, kBNo>::THREADS, 0, s>>>(gm, ntiles, sa,
-                                                                              sb, epi);
+    gemm_bf16out_kernel<kBMo, kBNo, true, Epi, FA><<<blocks, kThr, 0, s>>>(gm, ntiles, sa, sb, epi);
   else
-    gemm_bf16out_kernel<kBMo, kBNo, false, Epi><<<blocks, TileCfg<kBMo, kBNo>::THREADS, 0, s>>>(gm, ntiles, sa,
-                                                                               sb, epi);
+    gemm_bf16out_kernel<kBMo, kBNo, false, Epi, FA><<<blocks, kThr, 0, s>>>(gm, ntiles, sa, sb, epi);
   return blocks;
 }
 
@@ -892,9 +899,13 @@ void launch_gemm_fwd(const uint8_t* x8, const uint8_t* w_packed_t, int T, int N,
 }
 
 void launch_gemm_dx(const uint8_t* g8, const uint8_t* w_packed, int T, int D, int Np,
-                    const float* g_scales, const float* w_scales, uint16_t* dx, hipStream_t s) {
+                    const float* g_scales, const float* w_scales, uint16_t* dx, hipStream_t s,
+                    bool g_e5m2) {
   const Gemm gm{g8, 0, w_packed, Np, T, D, Np, (int)ceil_div(D, kBNo), kActRows, 0, 0};
-  launch_bf16out(gm, g_scales, w_scales, EpiDx{dx, D}, s);
+  if (g_e5m2)
+    launch_bf16out<EpiDx, kFmtE5M2>(gm, g_scales, w_scales, EpiDx{dx, D}, s);
+  else
+    launch_bf16out(gm, g_scales, w_scales, EpiDx{dx, D}, s);
 }
 
 int launch_gemm_relu2(const uint8_t* x8, const uint8_t* w1_t, int T, int F, int D,
@@ -942,15 +953,19 @@ size_t dw_partial_bytes(int D, int Np, int64_t tokens_padded) {
 }
 
 void launch_gemm_dw(const uint8_t* x8, const uint8_t* g8, int D, int Np, int64_t Tp,
-                    float* part, hipStream_t s) {
+                    float* part, hipStream_t s, bool g_e5m2) {
   const int splits = dw_splits(D, Np, Tp);
   const int nk = (int)ceil_div(Tp, kBK);
   const int per = (int)ceil_div(nk, splits);
   const Gemm gm{x8, ceil_div(D, kKBlock), g8, ceil_div(Np, kKBlock), D, Np, (int)Tp,
                 (int)ceil_div(Np, kBNw), 0, 0, 1};
   const int blocks = (int)ceil_div(D, kBMw) * gm.n_tiles * splits;
-  gemm_dw_part_kernel<kBMw, kBNw, kMWw, kNWw>
-      <<<blocks, TileCfg<kBMw, kBNw, kMWw, kNWw>::THREADS, 0, s>>>(gm, splits, per, part);
+  constexpr int kThr = TileCfg<kBMw, kBNw, kMWw, kNWw>::THREADS;
+  if (g_e5m2)
+    gemm_dw_part_kernel<kBMw, kBNw, kMWw, kNWw, kFmtE5M2><<<blocks, kThr, 0, s>>>(gm, splits, per,
+                                                                                   part);
+  else
+    gemm_dw_part_kernel<kBMw, kBNw, kMWw, kNWw><<<blocks, kThr, 0, s>>>(gm, splits, per, part);
 }
 
 void launch_dw_reduce(const float* part, int D, int Np, int64_t Tp, const float* x_scales,

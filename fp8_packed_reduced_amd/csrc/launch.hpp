@@ -71,9 +71,12 @@ void launch_quantize_act(const uint16_t* src, int64_t rows, int cols, const uint
 void launch_quantize_act_split(const uint16_t* src, int split, const uint16_t* vsrc, int vw,
                                int vh, int vs, int64_t rows, int cols, const uint32_t* partials,
                                int parts, float* scales, int32_t* status, int status_bit,
-                               uint8_t* dst, int64_t tokens_padded, hipStream_t s);
+                               uint8_t* dst, int64_t tokens_padded, hipStream_t s,
+                               bool e5m2 = false);
 
-void launch_encode(const float* in, int64_t n, float inv, uint8_t* out, hipStream_t s);
+// e4m3 (or e5m2) codes of in[i] * inv, no amax: the encoder hooks.
+void launch_encode(const float* in, int64_t n, float inv, uint8_t* out, hipStream_t s,
+                   bool e5m2 = false);
 
 // ---- gemm.hip --------------------------------------------------------------
 
@@ -84,8 +87,10 @@ void launch_gemm_fwd(const uint8_t* x8, const uint8_t* w_packed_t, int T, int N,
                      uint16_t* v, int H, int d_v, int seq_len, hipStream_t s);
 
 // dX = s_g s_w g8 @ W_packed^T: M = T, N = D, K = N_packed; dx [T][D] bf16.
+// g_e5m2: g8 holds e5m2 codes (else e4m3); the weight codes are e4m3.
 void launch_gemm_dx(const uint8_t* g8, const uint8_t* w_packed, int T, int D, int Np,
-                    const float* g_scales, const float* w_scales, uint16_t* dx, hipStream_t s);
+                    const float* g_scales, const float* w_scales, uint16_t* dx, hipStream_t s,
+                    bool g_e5m2 = false);
 
 // FP8 ReLU^2 MLP (W1 [D][F], W2 [F][D]; activations in the blocked row
 // layout).  h = relu(s_x s_w1 x8 @ W1)^2 into h [T][F] bf16, through the
@@ -111,7 +116,8 @@ size_t dw_partial_bytes(int D, int Np, int64_t tokens_padded);
 // x8 [T][D], g8 [T][Np] in the blocked row layout, rows T .. Tp - 1 zero;
 // unscaled split-K partial sums go to `part` [dw_splits][D][Np] fp32 ...
 void launch_gemm_dw(const uint8_t* x8, const uint8_t* g8, int D, int Np, int64_t Tp,
-                    float* part, hipStream_t s);
+                    float* part, hipStream_t s,
+                    bool g_e5m2 = false);
 // ... and are summed in split order, scaled by s_x s_g and written into the
 // three column blocks dwq [D][nq] (ldq), dwk, dwv [D][N - 2nq] (ldv).
 void launch_dw_reduce(const float* part, int D, int Np, int64_t Tp, const float* x_scales,

@@ -85,14 +85,16 @@ __global__ __launch_bounds__(kThreads) void amax_bf16_kernel(const uint16_t* __r
 // ---------------------------------------------------------------- scales
 
 // The per-tensor scales from the amax partials (block-wide; every thread
-// gets them): s = fl(amax / 448), inv = fl(448 / amax) with IEEE-correct
-// fp32 divisions; (1, 1) for amax = 0, an inverse that overflows, or a
+// gets them): s = fl(amax / fmax), inv = fl(fmax / amax) with IEEE-correct
+// fp32 divisions, fmax the format's largest finite value (448 for e4m3,
+// 57344 for e5m2); (1, 1) for amax = 0, an inverse that overflows, or a
 // non-finite amax.  The block that `publishes` writes scales[0..1] and, for
 // a non-finite amax, sets `status_bit` in *status (overwriting *status
 // when `reset`).
 __device__ inline float2 tensor_scales(const uint32_t* __restrict__ partials, int parts,
                                        uint32_t* red, bool publish, float* __restrict__ scales,
-                                       int32_t* __restrict__ status, int status_bit, bool reset) {
+                                       int32_t* __restrict__ status, int status_bit, bool reset,
+                                       float fmax = kE4m3Max) {
   uint32_t m = 0;
 #pragma unroll 8
   for (int i = threadIdx.x; i < parts; i += kThreads) m = m > partials[i] ? m : partials[i];
@@ -101,9 +103,9 @@ __device__ inline float2 tensor_scales(const uint32_t* __restrict__ partials, in
   const bool finite = m < 0x7f800000u;
   if (finite) {
     const float amax = __uint_as_float(m);
-    const float i = 448.0f / amax;
+    const float i = fmax / amax;
     if (amax != 0.0f && i <= 3.40282347e38f) {
-      sc = amax / 448.0f;
+      sc = amax / fmax;
       inv = i;
     }
   }
@@ -183,6 +185,7 @@ struct ActSrc {
   int vw, vh, vs;
 };
 
+template <bool E5>
 __global__ __launch_bounds__(kThreads) void quantize_act_kernel(
     ActSrc as, int64_t rows, int cols, const uint32_t* __restrict__ partials, int parts,
     float* __restrict__ scales, int32_t* __restrict__ status, int status_bit,
@@ -213,17 +216,18 @@ __global__ __launch_bounds__(kThreads) void quantize_act_kernel(
     }
   }
   const float inv = tensor_scales(partials, parts, red, blockIdx.x == 0 && blockIdx.y == 0,
-                                  scales, status, status_bit, false).y;
+                                  scales, status, status_bit, false,
+                                  E5 ? kE5m2Max : kE4m3Max).y;
   // rows rows .. tokens_padded - 1 (zero input) are written as zero codes:
   // the dW GEMM reads them as its K tail
 #pragma unroll
   for (int i = 0; i < 8; ++i) {
     const int64_t t = t0 + 8 * rg + i;
     const uint4 v = in[i];
-    const uint32_t lo = e4m3x4(bf16_to_f32(v.x & 0xffffu) * inv, bf16_to_f32(v.x >> 16) * inv,
-                               bf16_to_f32(v.y & 0xffffu) * inv, bf16_to_f32(v.y >> 16) * inv);
-    const uint32_t hi = e4m3x4(bf16_to_f32(v.z & 0xffffu) * inv, bf16_to_f32(v.z >> 16) * inv,
-                               bf16_to_f32(v.w & 0xffffu) * inv, bf16_to_f32(v.w >> 16) * inv);
+    const uint32_t lo = fp8x4<E5>(bf16_to_f32(v.x & 0xffffu) * inv, bf16_to_f32(v.x >> 16) * inv,
+                                  bf16_to_f32(v.y & 0xffffu) * inv, bf16_to_f32(v.y >> 16) * inv);
+    const uint32_t hi = fp8x4<E5>(bf16_to_f32(v.z & 0xffffu) * inv, bf16_to_f32(v.z >> 16) * inv,
+                                  bf16_to_f32(v.w & 0xffffu) * inv, bf16_to_f32(v.w >> 16) * inv);
     if (t < tokens_padded) {
       const int64_t blk = (t / kActRows) * kblocks + kb;
       *reinterpret_cast<uint2*>(dst + (blk * kActRows + t % kActRows) * kKBlock + 8 * cc) =
@@ -232,6 +236,7 @@ __global__ __launch_bounds__(kThreads) void quantize_act_kernel(
   }
 }
 
+template <bool E5>
 __global__ __launch_bounds__(kThreads) void encode_kernel(const float* __restrict__ in, int64_t n,
                                                           float inv, uint8_t* __restrict__ out) {
   const int64_t i = (blockIdx.x * (int64_t)kThreads + threadIdx.x) * 16;
@@ -241,7 +246,7 @@ __global__ __launch_bounds__(kThreads) void encode_kernel(const float* __restric
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
     float4 f = p[j];
-    w[j] = e4m3x4(f.x * inv, f.y * inv, f.z * inv, f.w * inv);
+    w[j] = fp8x4<E5>(f.x * inv, f.y * inv, f.z * inv, f.w * inv);
   }
   *reinterpret_cast<uint4*>(out + i) = make_uint4(w[0], w[1], w[2], w[3]);
 }
@@ -274,22 +279,30 @@ void launch_quantize_act(const uint16_t* src, int64_t rows, int cols, const uint
                          int parts, float* scales, int32_t* status, int status_bit, uint8_t* dst,
                          int64_t tokens_padded, hipStream_t s) {
   launch_quantize_act_split(src, cols, nullptr, 1, 1, 1, rows, cols, partials, parts, scales,
-                            status, status_bit, dst, tokens_padded, s);
+                            status, status_bit, dst, tokens_padded, s, false);
 }
 
 void launch_quantize_act_split(const uint16_t* src, int split, const uint16_t* vsrc, int vw,
                                int vh, int vs, int64_t rows, int cols, const uint32_t* partials,
                                int parts, float* scales, int32_t* status, int status_bit,
-                               uint8_t* dst, int64_t tokens_padded, hipStream_t s) {
+                               uint8_t* dst, int64_t tokens_padded, hipStream_t s, bool e5m2) {
   dim3 grid((unsigned)(tokens_padded / kKBlock), (unsigned)ceil_div(cols, kKBlock));
-  quantize_act_kernel<<<grid, kThreads, 0, s>>>(ActSrc{src, split, vsrc, vw, vh, vs}, rows, cols,
-                                                partials, parts, scales, status, status_bit, dst,
-                                                tokens_padded);
+  const ActSrc as{src, split, vsrc, vw, vh, vs};
+  if (e5m2)
+    quantize_act_kernel<true><<<grid, kThreads, 0, s>>>(as, rows, cols, partials, parts, scales,
+                                                        status, status_bit, dst, tokens_padded);
+  else
+    quantize_act_kernel<false><<<grid, kThreads, 0, s>>>(as, rows, cols, partials, parts, scales,
+                                                         status, status_bit, dst, tokens_padded);
 }
 
-void launch_encode(const float* in, int64_t n, float inv, uint8_t* out, hipStream_t s) {
+void launch_encode(const float* in, int64_t n, float inv, uint8_t* out, hipStream_t s,
+                   bool e5m2) {
   const int64_t blocks = ceil_div(n / 16, kThreads);
-  encode_kernel<<<(unsigned)blocks, kThreads, 0, s>>>(in, n, inv, out);
+  if (e5m2)
+    encode_kernel<true><<<(unsigned)blocks, kThreads, 0, s>>>(in, n, inv, out);
+  else
+    encode_kernel<false><<<(unsigned)blocks, kThreads, 0, s>>>(in, n, inv, out);
 }
 
 }  // namespace fpr

@@ -93,7 +93,18 @@ typedef struct fpr_dims {
                           FlashAttention-3 is one of the steps fused into the
                           norm/RoPE kernel in "Reduced-width QK and packed FP8
                           attention", Changes. */
+    int32_t grad_format;  /* FPR_FORMAT_E4M3 (0, the default) or FPR_FORMAT_E5M2:
+                          the FP8 format of the packed gradient dQKV in the
+                          backward (its per-tensor scale then uses 57344, the
+                          largest finite e5m2, in place of 448).  The weight
+                          and x codes stay e4m3; dX and dW multiply e5m2 by
+                          e4m3 codes on the matrix cores.  An attention-ready
+                          variant: gradients keep e5m2's wider range. */
 } fpr_dims;
+
+/* FP8 formats (OCP): E4M3 (max 448, no inf) and E5M2 (max 57344, with inf;
+ * encoding saturates at +-57344). */
+enum { FPR_FORMAT_E4M3 = 0, FPR_FORMAT_E5M2 = 1 };
 
 /* The cached FP8 views of W_packed, rebuilt by pack_quantize_weights after
  * every update of the fp32 weights ("invalidate on update").  All four
@@ -327,6 +338,10 @@ FPR_API int fpr_mlp_get_layout(const fpr_mlp_dims* dims, int64_t tokens, fpr_mlp
  * encoder (no amax; the caller supplies the scale).  For exhaustive tests of
  * the encoder.  in/out are device pointers, 16-byte aligned, n % 16 == 0. */
 FPR_API int fpr_e4m3_encode(const float* in, int64_t n, float inv_scale, uint8_t* out,
+                    void* stream);
+
+/* The same for the device's e5m2 encoder (saturating at +-57344). */
+FPR_API int fpr_e5m2_encode(const float* in, int64_t n, float inv_scale, uint8_t* out,
                     void* stream);
 
 #ifdef __cplusplus

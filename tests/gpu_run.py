@@ -28,8 +28,9 @@ def dev_to_bits(t: torch.Tensor) -> np.ndarray:
     return t.contiguous().view(torch.int16).cpu().numpy().view(np.uint16)
 
 
-def dims_for(w: dict, qk_stride: int = 0):
-    return B.make_dims(w["d_model"], w["n_heads"], w["d_qk"], w["d_v"], EPS, BASE, qk_stride)
+def dims_for(w: dict, qk_stride: int = 0, grad_format: int = 0):
+    return B.make_dims(w["d_model"], w["n_heads"], w["d_qk"], w["d_v"], EPS, BASE, qk_stride,
+                       grad_format)
 
 
 def pad_rows(a: np.ndarray, width: int, fill: int) -> np.ndarray:
@@ -53,20 +54,22 @@ def unblock_rows(buf, off: int, rows: int, cols: int, lay) -> np.ndarray:
 
 
 def run(w: dict, seed: int = 42, x_bits=None, W=None, dy=None, backward: bool = True,
-        qk_stride: int = 0):
+        qk_stride: int = 0, grad_format: int = 0):
     """Pack, forward (and backward) on the GPU; returns a dict of numpy arrays.
 
     With qk_stride > d_qk, q and k come back with their padded rows (the
     output buffers start filled with NaN bits, so the padding seen is what
     the kernels wrote) and dq, dk (given or drawn at d_qk) go in padded with
-    NaN bits, which the backward must never read."""
+    NaN bits, which the backward must never read.  grad_format 1 quantises the
+    packed gradient to e5m2."""
     n_seq, S = w["n_seq"], w["seq_len"]
     T = n_seq * S
     D, H, dqk, dv = w["d_model"], w["n_heads"], w["d_qk"], w["d_v"]
     N = inputs.packed_width(w)
-    dims = dims_for(w, qk_stride)
+    dims = dims_for(w, qk_stride, grad_format)
     qs = qk_stride or dqk
-    say(f"[gpu] run n_seq={n_seq} S={S} D={D} H={H} d_qk={dqk} d_v={dv} stride={qs} seed={seed}")
+    say(f"[gpu] run n_seq={n_seq} S={S} D={D} H={H} d_qk={dqk} d_v={dv} stride={qs} "
+        f"grad_format={grad_format} seed={seed}")
     if x_bits is None:
         x_bits = inputs.make_x(w, seed)
     if W is None:

@@ -19,7 +19,8 @@ def test_library_exports_every_declared_call():
                           "qkv_forward", "qkv_backward", "fpr_status_string", "fpr_get_layout",
                           "fpr_e4m3_encode", "fpr_trace_set", "fpr_mlp_workspace_bytes",
                           "fpr_mlp_saved_bytes", "fpr_mlp_get_layout",
-                          "mlp_pack_quantize_weights", "mlp_forward", "mlp_backward"}
+                          "mlp_pack_quantize_weights", "mlp_forward", "mlp_backward",
+                          "fpr_e5m2_encode"}
     lib = B.load()
     for n in names:
         assert hasattr(lib, n), n
@@ -117,7 +118,17 @@ def test_qk_stride_leaves_buffers_alone():
     assert B.saved_bytes(a, 4096) == B.saved_bytes(b, 4096)
     for which in (B.FPR_CALL_FORWARD, B.FPR_CALL_BACKWARD):
         assert B.workspace_bytes(a, 4096, which) == B.workspace_bytes(b, 4096, which)
-    assert ctypes.sizeof(B.Dims) == 28 and B.Dims.qk_stride.offset == 24
+    assert ctypes.sizeof(B.Dims) == 32 and B.Dims.qk_stride.offset == 24
+    assert B.Dims.grad_format.offset == 28
+
+
+@pytest.mark.parametrize("fmt,ok", [(0, True), (1, True), (2, False), (-1, False)])
+def test_grad_format_support(fmt, ok):
+    d = B.make_dims(768, 6, grad_format=fmt)
+    assert (B.workspace_bytes(d, 256, B.FPR_CALL_BACKWARD) > 0) == ok
+    if ok:  # the format changes no buffer size
+        assert B.workspace_bytes(d, 4096, B.FPR_CALL_BACKWARD) == \
+            B.workspace_bytes(B.make_dims(768, 6), 4096, B.FPR_CALL_BACKWARD)
 
 
 def _cache_c(ptr=0x1000):

@@ -54,22 +54,25 @@ def _dims(w):
 
 # ------------------------------------------------------------------ encoder
 
-def test_encoder_matches_oracle_on_every_rounding_class():
+@pytest.mark.parametrize("fmt", ["e4m3", "e5m2"])
+def test_encoder_matches_oracle_on_every_rounding_class(fmt):
     from fp8_packed_reduced_amd import binding as B
+    e5 = fmt == "e5m2"
+    enc = oracle.e5m2_encode if e5 else oracle.e4m3_encode
     hi = np.arange(1 << 16, dtype=np.uint32) << 16
     tails = np.array([0x0000, 0x0001, 0x7FFF, 0x8000, 0x8001, 0xFFFF], dtype=np.uint32)
     v = (hi[:, None] | tails[None, :]).ravel().view(np.float32)
     v = v[np.isfinite(v)]
     v = v[: (v.size // 16) * 16]
-    say(f"[gpu] encoder sweep over {v.size} fp32 patterns")
-    got = B.e4m3_encode(torch.from_numpy(v).cuda(), 1.0).cpu().numpy()
-    assert np.array_equal(got, oracle.e4m3_encode(v))
+    say(f"[gpu] {fmt} encoder sweep over {v.size} fp32 patterns")
+    got = B.e4m3_encode(torch.from_numpy(v).cuda(), 1.0, e5m2=e5).cpu().numpy()
+    assert np.array_equal(got, enc(v))
     # with a scale: codes of fl32(v * inv)
     rng = np.random.default_rng(1)
     r = rng.standard_normal(1 << 20).astype(np.float32)
-    inv = np.float32(448.0) / np.float32(np.abs(r).max())
-    got = B.e4m3_encode(torch.from_numpy(r).cuda(), float(inv)).cpu().numpy()
-    assert np.array_equal(got, oracle.e4m3_encode(r * inv))
+    inv = np.float32(57344.0 if e5 else 448.0) / np.float32(np.abs(r).max())
+    got = B.e4m3_encode(torch.from_numpy(r).cuda(), float(inv), e5m2=e5).cpu().numpy()
+    assert np.array_equal(got, enc(r * inv))
 
 
 # ------------------------------------------------------------ weight quant
@@ -126,7 +129,7 @@ def _check_forward(w, r):
     assert np.array_equal(r["v"], o["v_bits"])  # v is a pure relayout of Y's V columns
 
 
-def _check_backward(w, r):
+def _check_backward(w, r, fmt="e4m3"):
     dims = _dims(w)
     n_seq, S = w["n_seq"], w["seq_len"]
     T, H, dqk = r["T"], w["n_heads"], w["d_qk"]
@@ -134,7 +137,7 @@ def _check_backward(w, r):
     dq, dk, dv = r["dy"]
     # a5: norm/RoPE backward fed the GPU's saved pre-norm rows
     ob = oracle.qkv_backward(dims, n_seq, S, dq, dk, dv, r["x8"], r["x_scales"][0], r["qk_pre"],
-                             r["w_packed"], r["w_scales"][0])
+                             r["w_packed"], r["w_scales"][0], grad_fmt=fmt)
     g = r["dqkv"]
     e_dqk = row_rel_err(bf16_to_f64(g[:, :nqk2]).reshape(T, 2 * H, dqk),
                         ob["dqkv64"][:, :nqk2].reshape(T, 2 * H, dqk))
@@ -142,16 +145,17 @@ def _check_backward(w, r):
     # head-major: its codes below are what checks that read
     assert np.array_equal(g[:, nqk2:], ob["dqkv_bits"][:, nqk2:])
     # a6: gradient quantiser, bit-exact on the GPU's own dQKV
-    g8, s_g, inv_g, _ = oracle.quantize_bf16(g)
+    g8, s_g, inv_g, _ = oracle.quantize_bf16(g, fmt)
     assert np.array_equal(r["g8"], g8) and not r["g8_kpad"].any()
     assert r["g_scales"][0] == s_g and r["g_scales"][1] == inv_g
     assert not r["g8_tail"].any()
     # a7, a8: GEMMs from the GPU's own codes
-    dx64 = oracle.gemm_e4m3(r["g8"], np.ascontiguousarray(r["w_packed"].T), s_g, r["w_scales"][0])
+    dx64 = oracle.gemm_e4m3(r["g8"], np.ascontiguousarray(r["w_packed"].T), s_g, r["w_scales"][0],
+                            a_fmt=fmt)
     e_dx = row_rel_err(bf16_to_f64(r["dx"]), bf16_to_f64(oracle.round_bf16(dx64)))
     x_dx, over_dx = bf16_gemm_excess(r["dx"], dx64, oracle.round_bf16)
     dw = oracle.round_f32(oracle.gemm_e4m3(np.ascontiguousarray(r["x8"].T), r["g8"],
-                                           r["x_scales"][0], s_g))
+                                           r["x_scales"][0], s_g, b_fmt=fmt))
     e_dw = row_rel_err(r["dw"], dw)
     say(f"[gpu] backward errors: dqkv {e_dqk:.2e} dx {e_dx:.2e} (excess {x_dx:.2e}) "
         f"dw {e_dw:.2e}")
@@ -270,6 +274,48 @@ def test_padded_qk_stride(name, w, stride):
     for key in ("v", "qk_pre", "dqkv", "g_scales", "g8", "dx", "dw"):
         assert np.array_equal(a[key], b[key]), key
     assert b["status"] == 0
+
+
+@pytest.mark.parametrize("name,w", [("tiny", inputs.WORKLOADS["tiny"]), ("tails", TAILS)])
+def test_e5m2_gradients_stagewise(name, w):
+    """The backward with the packed gradient in e5m2: its codes and scale
+    bit-exact, dX and dW (e5m2 x e4m3 on the matrix cores) to the GEMM bars;
+    the forward is unchanged."""
+    r = run(w, seed=21, grad_format=1)
+    _check_forward(w, r)
+    _check_backward(w, r, fmt="e5m2")
+    assert r["status"] == 0
+    # the e5m2 scale is amax / 57344
+    g = bf16_to_f64(r["dqkv"])
+    assert r["g_scales"][0] == np.float32(np.float32(np.abs(g).max()) / np.float32(57344.0))
+
+
+def test_e5m2_gradients_end_to_end():
+    """From the inputs alone: dX and dW with e5m2 gradients no further from
+    the unquantised float64 gradients than 1.1x the oracle's own e5m2 chain
+    + 1e-3, and e5m2 (2 fraction bits) measurably coarser than e4m3."""
+    w = inputs.WORKLOADS["tiny"]
+    r5 = run(w, seed=8, grad_format=1)
+    r4 = run(w, seed=8)
+    dims = _dims(w)
+    ref_dx, ref_dw = _unquantised(w, r5["x_bits"], r5["W"], r5["dy"])
+    wp, _, s_w, _, _ = oracle.pack_quantize_weights(dims, r5["W"])
+    of = oracle.qkv_forward(dims, w["n_seq"], w["seq_len"], r5["x_bits"], wp, s_w)
+    nqk2 = 2 * w["n_heads"] * w["d_qk"]
+    dq, dk, dv = r5["dy"]
+    ob = oracle.qkv_backward(dims, w["n_seq"], w["seq_len"], dq, dk, dv, of["x8"], of["s_x"],
+                             of["y_bits"][:, :nqk2], wp, s_w, grad_fmt="e5m2")
+
+    def err(a, b):
+        return float(np.linalg.norm(a - b) / np.linalg.norm(b))
+
+    e_dx, e_dw = err(bf16_to_f64(r5["dx"]), ref_dx), err(r5["dw"], ref_dw)
+    o_dx, o_dw = err(bf16_to_f64(ob["dx_bits"]), ref_dx), err(ob["dw64"], ref_dw)
+    e4_dw = err(r4["dw"], ref_dw)
+    say(f"[gpu] e5m2 e2e: dx gpu {e_dx:.3e} oracle {o_dx:.3e}; dw gpu {e_dw:.3e} oracle "
+        f"{o_dw:.3e}; e4m3 dw {e4_dw:.3e}")
+    assert e_dx <= 1.1 * o_dx + 1e-3 and e_dw <= 1.1 * o_dw + 1e-3
+    assert e_dw > e4_dw
 
 
 def test_zero_inputs_give_zero_outputs():
