@@ -72,7 +72,8 @@ class Layout(ctypes.Structure):
 
 
 class MlpDims(ctypes.Structure):
-    _fields_ = [("d_model", ctypes.c_int32), ("d_ff", ctypes.c_int32)]
+    _fields_ = [("d_model", ctypes.c_int32), ("d_ff", ctypes.c_int32),
+                ("grad_format", ctypes.c_int32)]
 
 
 class _MlpCacheC(ctypes.Structure):

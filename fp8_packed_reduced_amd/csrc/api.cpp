@@ -114,6 +114,7 @@ struct MlpPlan {
 
 int mlp_shape_check(const fpr_mlp_dims* d) {
   if (!d || d->d_model <= 0 || d->d_ff <= 0) return FPR_ERR_ARG;
+  if (d->grad_format != FPR_FORMAT_E4M3 && d->grad_format != FPR_FORMAT_E5M2) return FPR_ERR_ARG;
   if (d->d_model % 64 || d->d_ff % 64 || d->d_model > (1 << 16) || d->d_ff > (1 << 16))
     return FPR_ERR_SHAPE;
   return FPR_OK;
@@ -533,29 +534,34 @@ int mlp_backward(const fpr_mlp_dims* dims, int64_t tokens, const uint16_t* dy,
   uint8_t* dp8 = at<uint8_t>(workspace, p.b_dp8);
   float* dwpart = at<float>(workspace, p.b_dwpart);
   int np = 0;
+  const bool e5 = dims->grad_format == FPR_FORMAT_E5M2;
   stage("mlp_amax_dy", s, [&] { fpr::launch_amax_bf16(dy, T * p.D, dyparts, p.x_parts, s); });
   stage("mlp_quantize_dy", s, [&] {
-    fpr::launch_quantize_act(dy, T, p.D, dyparts, p.x_parts, dysc, cache->status,
-                             FPR_STATUS_G_NONFINITE, dy8, p.Tp, s);
+    fpr::launch_quantize_act_split(dy, p.D, nullptr, 1, 1, 1, T, p.D, dyparts, p.x_parts, dysc,
+                                   cache->status, FPR_STATUS_G_NONFINITE, dy8, p.Tp, s, e5);
   });
   stage("mlp_gemm_dh", s, [&] {
     np = fpr::launch_gemm_dpre(dy8, cache->w2, (int)T, p.F, p.D, dysc, cache->scales + 2, h8,
-                               hsc, dpre, dpparts, s);
+                               hsc, dpre, dpparts, s, e5);
   });
   stage("mlp_quantize_dpre", s, [&] {
-    fpr::launch_quantize_act(dpre, T, p.F, dpparts, np, dpsc, cache->status,
-                             FPR_STATUS_H_NONFINITE, dp8, p.Tp, s);
+    fpr::launch_quantize_act_split(dpre, p.F, nullptr, 1, 1, 1, T, p.F, dpparts, np, dpsc,
+                                   cache->status, FPR_STATUS_H_NONFINITE, dp8, p.Tp, s, e5);
   });
   stage("mlp_gemm_dx", s, [&] {
-    fpr::launch_gemm_dx(dp8, cache->w1, (int)T, p.D, p.F, dpsc, cache->scales, dx, s);
+    fpr::launch_gemm_dx(dp8, cache->w1, (int)T, p.D, p.F, dpsc, cache->scales, dx, s, e5);
   });
   // one column block covers the whole output (nq = its width)
-  stage("mlp_gemm_dw1", s, [&] { fpr::launch_gemm_dw(x8, dp8, p.D, p.F, p.Tp, dwpart, s); });
+  stage("mlp_gemm_dw1", s, [&] {
+    fpr::launch_gemm_dw(x8, dp8, p.D, p.F, p.Tp, dwpart, s, e5);
+  });
   stage("mlp_dw1_reduce", s, [&] {
     fpr::launch_dw_reduce(dwpart, p.D, p.F, p.Tp, xsc, dpsc, dw1, ld1, dw1, ld1, dw1, ld1, p.F,
                           s);
   });
-  stage("mlp_gemm_dw2", s, [&] { fpr::launch_gemm_dw(h8, dy8, p.F, p.D, p.Tp, dwpart, s); });
+  stage("mlp_gemm_dw2", s, [&] {
+    fpr::launch_gemm_dw(h8, dy8, p.F, p.D, p.Tp, dwpart, s, e5);
+  });
   stage("mlp_dw2_reduce", s, [&] {
     fpr::launch_dw_reduce(dwpart, p.F, p.D, p.Tp, hsc, dysc, dw2, ld2, dw2, ld2, dw2, ld2, p.D,
                           s);

@@ -921,7 +921,8 @@ int launch_gemm_relu2(const uint8_t* x8, const uint8_t* w1_t, int T, int F, int 
 
 int launch_gemm_dpre(const uint8_t* dy8, const uint8_t* w2, int T, int F, int D,
                      const float* dy_scales, const float* w_scales, const uint8_t* h8,
-                     const float* h_scales, uint16_t* dpre, uint32_t* partials, hipStream_t s) {
+                     const float* h_scales, uint16_t* dpre, uint32_t* partials, hipStream_t s,
+                     bool dy_e5m2) {
   const Gemm gm{dy8, 0, w2, D, T, F, D, (int)ceil_div(F, kBNo), kActRows, 0, 0};
   EpiDpre epi{};
   epi.dx = dpre;
@@ -930,7 +931,9 @@ int launch_gemm_dpre(const uint8_t* dy8, const uint8_t* w2, int T, int F, int D,
   epi.h8 = h8;
   epi.h_scales = h_scales;
   epi.kc = (int)ceil_div(F, kKBlock);
-  return launch_bf16out(gm, dy_scales, w_scales, epi, s) * TileCfg<kBMo, kBNo>::MMA;
+  const int blocks = dy_e5m2 ? launch_bf16out<EpiDpre, kFmtE5M2>(gm, dy_scales, w_scales, epi, s)
+                             : launch_bf16out(gm, dy_scales, w_scales, epi, s);
+  return blocks * TileCfg<kBMo, kBNo>::MMA;
 }
 
 // The split count s <= kMaxSplits (and <= the K steps) whose tiles x s

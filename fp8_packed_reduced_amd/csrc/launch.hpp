@@ -106,7 +106,8 @@ int launch_gemm_relu2(const uint8_t* x8, const uint8_t* w1_t, int T, int F, int 
                       uint32_t* partials, hipStream_t s);
 int launch_gemm_dpre(const uint8_t* dy8, const uint8_t* w2, int T, int F, int D,
                      const float* dy_scales, const float* w_scales, const uint8_t* h8,
-                     const float* h_scales, uint16_t* dpre, uint32_t* partials, hipStream_t s);
+                     const float* h_scales, uint16_t* dpre, uint32_t* partials, hipStream_t s,
+                     bool dy_e5m2 = false);
 
 // Number of K splits the dW GEMM uses, and its partial-buffer size.
 int dw_splits(int D, int Np, int64_t tokens_padded);

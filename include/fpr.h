@@ -263,8 +263,10 @@ FPR_API void fpr_trace_set(fpr_trace* trace);
  * 1 <= T <= 2^24.
  * ------------------------------------------------------------------- */
 typedef struct fpr_mlp_dims {
-    int32_t d_model;   /* D */
-    int32_t d_ff;      /* F, the hidden width (3072 for D = 768) */
+    int32_t d_model;      /* D */
+    int32_t d_ff;         /* F, the hidden width (3072 for D = 768) */
+    int32_t grad_format;  /* FPR_FORMAT_E4M3 (0) or FPR_FORMAT_E5M2: the format
+                             of the backward's gradient codes dy8 and dpre8 */
 } fpr_mlp_dims;
 
 /* The cached FP8 views of W1 and W2, rebuilt by mlp_pack_quantize_weights

@@ -485,7 +485,7 @@ def mlp_forward(x_bits: np.ndarray, wq: dict, h_bits: np.ndarray | None = None):
 
 
 def mlp_backward(dy_bits: np.ndarray, x8: np.ndarray, s_x, h8: np.ndarray, s_h, wq: dict,
-                 dpre_bits: np.ndarray | None = None):
+                 dpre_bits: np.ndarray | None = None, grad_fmt: str = "e4m3"):
     """Backward of the FP8 ReLU^2 MLP from the saved x8, h8 and their scales;
     quantisers treated as the identity.
 
@@ -494,22 +494,24 @@ def mlp_backward(dy_bits: np.ndarray, x8: np.ndarray, s_x, h8: np.ndarray, s_h, 
       dx   = dpre @ W1^T          (through the cached [D][F] codes of W1)
       dW1  = x^T dpre,  dW2 = h^T dy
 
-    If ``dpre_bits`` is given, the stages after it are fed those values."""
-    dy8, s_dy, inv_dy, rc_dy = quantize_bf16(dy_bits)
+    If ``dpre_bits`` is given, the stages after it are fed those values.
+    ``grad_fmt`` "e5m2" quantises the gradients dy and dpre to e5m2."""
+    g = grad_fmt
+    dy8, s_dy, inv_dy, rc_dy = quantize_bf16(dy_bits, g)
     out = dict(dy8=dy8, s_dy=s_dy, inv_dy=inv_dy, rc_dy=rc_dy)
     if dpre_bits is None:
-        dh64 = gemm_e4m3(dy8, np.ascontiguousarray(wq["w2"].T), s_dy, wq["s_w2"])
+        dh64 = gemm_e4m3(dy8, np.ascontiguousarray(wq["w2"].T), s_dy, wq["s_w2"], a_fmt=g)
         h = float(s_h) * e4m3_decode(h8)
         out["dh64"] = dh64
         out["dpre64"] = relu2_grad(dh64, h)
         dpre_bits = round_bf16(out["dpre64"])
     out["dpre_bits"] = dpre_bits
-    dp8, s_dp, inv_dp, rc_dp = quantize_bf16(dpre_bits)
+    dp8, s_dp, inv_dp, rc_dp = quantize_bf16(dpre_bits, g)
     out.update(dp8=dp8, s_dp=s_dp, inv_dp=inv_dp, rc_dp=rc_dp)
-    dx64 = gemm_e4m3(dp8, np.ascontiguousarray(wq["w1"].T), s_dp, wq["s_w1"])
+    dx64 = gemm_e4m3(dp8, np.ascontiguousarray(wq["w1"].T), s_dp, wq["s_w1"], a_fmt=g)
     out["dx64"] = dx64
     out["dx_bits"] = round_bf16(dx64)
-    dw1 = gemm_e4m3(np.ascontiguousarray(x8.T), dp8, s_x, s_dp)
-    dw2 = gemm_e4m3(np.ascontiguousarray(h8.T), dy8, s_h, s_dy)
+    dw1 = gemm_e4m3(np.ascontiguousarray(x8.T), dp8, s_x, s_dp, b_fmt=g)
+    dw2 = gemm_e4m3(np.ascontiguousarray(h8.T), dy8, s_h, s_dy, b_fmt=g)
     out.update(dw1_64=dw1, dw2_64=dw2, dw1_f32=round_f32(dw1), dw2_f32=round_f32(dw2))
     return out

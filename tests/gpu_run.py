@@ -163,17 +163,17 @@ def bf16_gemm_excess(gpu_bits: np.ndarray, exact: np.ndarray, round_bf16) -> tup
 # ------------------------------------------------------- FP8 ReLU^2 MLP
 
 def run_mlp(w: dict, seed: int = 42, x_bits=None, w12=None, dy_bits=None,
-            backward: bool = True):
+            backward: bool = True, grad_format: int = 0):
     """Pack, forward (and backward) of the FP8 ReLU^2 MLP on the GPU; every
     stage's output as numpy arrays (bf16 as uint16 patterns)."""
     T = w["n_seq"] * w["seq_len"]
     D, F = w["d_model"], w["d_ff"]
-    say(f"[gpu] mlp T={T} D={D} F={F} seed={seed}")
+    say(f"[gpu] mlp T={T} D={D} F={F} grad_format={grad_format} seed={seed}")
     if x_bits is None:
         x_bits = inputs.make_x(w, seed)
     if w12 is None:
         w12 = inputs.make_mlp_w(w, seed + 1)
-    dims = B.MlpDims(D, F)
+    dims = B.MlpDims(D, F, grad_format)
     cache = B.MlpCache(dims)
     w1d, w2d = (torch.from_numpy(np.ascontiguousarray(a)).cuda() for a in w12)
     B.mlp_pack_quantize_weights(dims, w1d, w2d, cache)

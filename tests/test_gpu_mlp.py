@@ -44,7 +44,7 @@ def _check_bf16_gemm(name, gpu_bits, exact):
     assert excess <= GEMM_TOL, name
 
 
-def _check_stages(w, r):
+def _check_stages(w, r, fmt="e4m3"):
     T, D, F = r["T"], w["d_model"], w["d_ff"]
     wq = oracle.mlp_quantize_weights(r["w1"], r["w2"])
     for k in ("w1", "w1_t", "w2", "w2_t"):
@@ -66,11 +66,12 @@ def _check_stages(w, r):
     _check_bf16_gemm("y", r["y"], fw2["y64"])
     # backward from the GPU's saved x8, h8
     s_x, s_h = np.float32(r["x_scales"][0]), np.float32(r["h_scales"][0])
-    bw = oracle.mlp_backward(r["dy"], r["x8"], s_x, r["h8"], s_h, wq)
+    bw = oracle.mlp_backward(r["dy"], r["x8"], s_x, r["h8"], s_h, wq, grad_fmt=fmt)
     assert np.array_equal(r["dy8"], bw["dy8"])
     assert r["dy_scales"][0] == bw["s_dy"] and r["dy_scales"][1] == bw["inv_dy"]
     _check_bf16_gemm("dpre", r["dpre"], bw["dpre64"])
-    bw2 = oracle.mlp_backward(r["dy"], r["x8"], s_x, r["h8"], s_h, wq, dpre_bits=r["dpre"])
+    bw2 = oracle.mlp_backward(r["dy"], r["x8"], s_x, r["h8"], s_h, wq, dpre_bits=r["dpre"],
+                              grad_fmt=fmt)
     assert np.array_equal(r["dp8"], bw2["dp8"])
     assert r["dp_scales"][0] == bw2["s_dp"] and r["dp_scales"][1] == bw2["inv_dp"]
     assert not r["dp8_tail"].any()
@@ -86,6 +87,14 @@ def _check_stages(w, r):
                                     ("tails", MLP_TAILS)])
 def test_mlp_stagewise(name, w):
     _check_stages(w, run_mlp(w, seed=42))
+
+
+@pytest.mark.parametrize("name,w", [("tiny", inputs.MLP_WORKLOADS["mlp_tiny"]),
+                                    ("tails", MLP_TAILS)])
+def test_mlp_e5m2_gradients_stagewise(name, w):
+    """dy8 and dpre8 in e5m2: codes and scales bit-exact, the GEMMs that read
+    them (dh, dX, dW1, dW2: e5m2 x e4m3 on the matrix cores) to the bars."""
+    _check_stages(w, run_mlp(w, seed=42, grad_format=1), fmt="e5m2")
 
 
 def test_mlp_end_to_end_against_oracle_chain():

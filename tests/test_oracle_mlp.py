@@ -109,7 +109,10 @@ def _expected(x, w1, w2, dy, perm_i, sig1, perm_f, sig2):
     return dict(h=h, y=y, dpre=dpre, dx=dx, dw1=dw1, dw2=dw2)
 
 
-def test_structured_mlp_is_exact():
+@pytest.mark.parametrize("fmt,s_dy", [("e4m3", 0.125), ("e5m2", 2.0 ** -10)])
+def test_structured_mlp_is_exact(fmt, s_dy):
+    """Both gradient formats: dy's scale is a power of two in each (56/448,
+    56/57344), and every dy and dpre value is exact in both."""
     x, w1, w2, dy, *perm = _structured()
     e = _expected(x, w1, w2, dy, *perm)
     wq = oracle.mlp_quantize_weights(w1, w2)
@@ -121,11 +124,13 @@ def test_structured_mlp_is_exact():
     assert np.array_equal(float(fw["s_h"]) * oracle.e4m3_decode(fw["h8"]), e["h"])
     assert np.array_equal(oracle.bf16_to_f64(fw["y_bits"]), e["y"])
     dy_bits = np.vectorize(_bf16_bits)(dy).astype(np.uint16)
-    bw = oracle.mlp_backward(dy_bits, fw["x8"], fw["s_x"], fw["h8"], fw["s_h"], wq)
-    assert bw["s_dy"] == 0.125
+    bw = oracle.mlp_backward(dy_bits, fw["x8"], fw["s_x"], fw["h8"], fw["s_h"], wq, grad_fmt=fmt)
+    assert bw["s_dy"] == s_dy
+    dec = oracle.e5m2_decode if fmt == "e5m2" else oracle.e4m3_decode
+    assert np.array_equal(float(bw["s_dy"]) * dec(bw["dy8"]), dy.astype(np.float64))
     assert np.array_equal(oracle.bf16_to_f64(bw["dpre_bits"]), e["dpre"])
     # dpre's scale is a power of two, so its codes are exact too
-    assert np.array_equal(float(bw["s_dp"]) * oracle.e4m3_decode(bw["dp8"]), e["dpre"])
+    assert np.array_equal(float(bw["s_dp"]) * dec(bw["dp8"]), e["dpre"])
     assert np.array_equal(oracle.bf16_to_f64(bw["dx_bits"]), e["dx"])
     assert np.array_equal(bw["dw1_f32"].astype(np.float64), e["dw1"])
     assert np.array_equal(bw["dw2_f32"].astype(np.float64), e["dw2"])
