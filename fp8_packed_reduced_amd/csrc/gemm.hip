@@ -664,26 +664,42 @@ __device__ __forceinline__ void store_bf16_tile(const v16f (&acc)[C::FM][C::FN],
   const int64_t step = epi.step8(col);
   // this lane's accumulator columns: nl + 32 j + 8 g + 0..3
   const int nl = n0 + wn * C::WN + 4 * (lane >> 5);
-  // auxiliary inputs of the rows of slice i + 1 are fetched while slice i
-  // is worked on (two slices in flight)
-  uint32_t aux[2][C::FN][4];
-  auto fetch_aux = [&](int i, uint32_t (&dst)[C::FN][4]) {
+  // Auxiliary bytes (one per output element, blocked like h8) of slice i
+  // are fetched as the output leaves: lane (rq, p) reads the 8 bytes of
+  // chunk p of rows rq + 8q, so 8 lanes cover one row's 64 bytes.  They
+  // pass through the wave's LDS slice (rows 72 bytes apart: 18 words, so
+  // the 32 rows x 2 words of one read below fall in 64 distinct banks) into
+  // the lanes that hold the matching accumulators.  Slice i + 1 is fetched
+  // while slice i is worked on.
+  static_assert(C::WN == 64, "64 auxiliary bytes per row");
+  uint2 raw[4];
+  auto fetch_aux = [&](int i, uint2 (&dst)[4]) {
     if constexpr (Epi::kAux) {
-      static_assert(C::WN <= kKBlock, "a lane's columns share one block of h8");
-      const uint8_t* ar = epi.aux_row(mp + i * 32 + (lane & 31), nl);
+      const uint8_t* ar = epi.aux_row(mp + i * 32 + rq, n0 + wn * C::WN + 8 * p);
+#pragma unroll
+      for (int q = 0; q < 4; ++q)  // rows rq + 8q lie in the same block of kActRows rows
+        dst[q] = *reinterpret_cast<const uint2*>(ar + q * 8 * kKBlock);
+    }
+  };
+  auto aux_word = [](int row, int w) { return row * 72 + 4 * w; };
+  if constexpr (Epi::kAux) fetch_aux(0, raw);
+#pragma unroll
+  for (int i = 0; i < C::FM; ++i) {
+    const int ml = mp + i * 32 + (lane & 31);  // this lane's accumulator row
+    uint32_t aux[C::FN][4];
+    if constexpr (Epi::kAux) {
+      // the wave's LDS operations complete in order: the reads below finish
+      // before the bf16 writes reuse the slice
+#pragma unroll
+      for (int q = 0; q < 4; ++q)
+        *reinterpret_cast<uint2*>(slice + aux_word(rq + 8 * q, 2 * p)) = raw[q];
+      if (i + 1 < C::FM) fetch_aux(i + 1, raw);
 #pragma unroll
       for (int j = 0; j < C::FN; ++j)
 #pragma unroll
         for (int g = 0; g < 4; ++g)
-          dst[j][g] = *reinterpret_cast<const uint32_t*>(ar + 32 * j + 8 * g);
-    }
-  };
-  if constexpr (Epi::kAux) fetch_aux(0, aux[0]);
-#pragma unroll
-  for (int i = 0; i < C::FM; ++i) {
-    const int ml = mp + i * 32 + (lane & 31);  // this lane's accumulator row
-    if constexpr (Epi::kAux) {
-      if (i + 1 < C::FM) fetch_aux(i + 1, aux[(i + 1) & 1]);
+          aux[j][g] = *reinterpret_cast<const uint32_t*>(
+              slice + aux_word(lane & 31, 8 * j + 2 * g + (lane >> 5)));
     }
 #pragma unroll
     for (int j = 0; j < C::FN; ++j)
@@ -692,7 +708,7 @@ __device__ __forceinline__ void store_bf16_tile(const v16f (&acc)[C::FM][C::FN],
         const v16f& a = acc[i][j];
         float v[4] = {a[4 * g] * alpha, a[4 * g + 1] * alpha, a[4 * g + 2] * alpha,
                       a[4 * g + 3] * alpha};
-        if constexpr (Epi::kMap) epi.map(v, Epi::kAux ? aux[i & 1][j][g] : 0u);
+        if constexpr (Epi::kMap) epi.map(v, Epi::kAux ? aux[j][g] : 0u);
         const uint32_t w0 = cvt_bf16x2_rn(v[0], v[1]), w1 = cvt_bf16x2_rn(v[2], v[3]);
         if constexpr (Epi::kAmax) {
           if (ml < M && nl + 32 * j + 8 * g < epi.N) {
