@@ -165,13 +165,14 @@ def _oracle_mlp_step(w: dict, seed: int, tokens: int) -> float:
     return time.perf_counter() - t0
 
 
-def cpu_baseline(T: int, oracle_step, seed: int, target_s: float) -> dict:
+def cpu_baseline(T: int, oracle_step, seed: int, target_s: float, c1_step=None) -> dict:
     """The oracle, untouched, timed on a bounded prefix of the workload whose
     length is chosen (in multiples of 4096 tokens, at most the whole
     workload) from a 4096-token probe so that it takes about target_s; when
     the whole workload takes less, it is run repeatedly for about target_s.
     oracle_step(seed, tokens) returns the seconds one step of that prefix
-    takes."""
+    takes.  c1_step(seed), if given, is timed once more on one thread (the
+    tiny configuration's step)."""
     probe = min(4096, T)
     t_probe = oracle_step(seed, probe)
     tokens = int(min(T, max(probe, probe * round(target_s / max(t_probe, 1e-3)))))
@@ -185,11 +186,55 @@ def cpu_baseline(T: int, oracle_step, seed: int, target_s: float) -> dict:
     except Exception:
         cores = os.cpu_count()
     runs = f", {reps} runs" if reps > 1 else ""
+    single = None
+    if c1_step is not None:
+        try:
+            from threadpoolctl import threadpool_limits
+            with threadpool_limits(limits=1):
+                single = round(c1_step(seed), 3)
+        except Exception:
+            single = None
     return {"value": round(reps * tokens / dt, 1), "unit": "tokens/s", "cores": cores,
+            "c1_single_thread_s": single,
             "kind": "oracle",
             "sample": f"pack + forward + backward of the first {tokens} tokens (one sequence, "
                       f"positions 0..{tokens - 1}) of the same workload and seed{runs}; "
                       f"{dt:.2f} s"}
+
+
+# A weight large enough for the weight quantiser to stream (4096 x 10240 fp32,
+# 168 MB: 32 heads of the pages' widths at D = 4096): at the benchmark's
+# 5.9 MB the two pack kernels are launch-latency bound.
+WIDE_PACK = dict(n_seq=1, seq_len=256, d_model=4096, n_heads=32, d_qk=96, d_v=128)
+
+
+def pack_streaming(B, inputs, dev, seed: int, reps: int = 20) -> dict:
+    import torch
+    w = WIDE_PACK
+    D, H, dqk, dv = w["d_model"], w["n_heads"], w["d_qk"], w["d_v"]
+    N, nq = H * (2 * dqk + dv), H * dqk
+    dims = B.make_dims(D, H, dqk, dv, inputs.EPS, inputs.ROPE_BASE)
+    W = torch.from_numpy(inputs.make_w(w, seed + 1)).to(dev)
+    cache = B.WeightCache(dims, dev)
+    ws = torch.empty(B.workspace_bytes(dims, 0, B.FPR_CALL_PACK), dtype=torch.uint8, device=dev)
+    args = (dims, W[:, :nq], W[:, nq:2 * nq], W[:, 2 * nq:], cache)
+    B.pack_quantize_weights(*args, workspace=ws)
+    torch.cuda.synchronize()
+    with B.KernelTrace(2 * reps, device=dev) as tr:
+        for _ in range(reps):
+            B.pack_quantize_weights(*args, workspace=ws)
+    torch.cuda.synchronize()
+    t = {}
+    for name, ms in tr.records():
+        t[name] = t.get(name, 0.0) + ms / reps
+    work = {"amax_w": 4 * D * N, "quantize_w": 6 * D * N}
+    out = {"workload": f"W [{D}][{N}] fp32 ({4 * D * N / 1e6:.0f} MB)"}
+    for name, b in work.items():
+        rate = b / (t[name] / 1e3)
+        out[name] = {"us": round(t[name] * 1e3, 2), "GB/s": round(rate / 1e9, 1),
+                     "frac": round(rate / PEAK_HBM_BYTES, 4)}
+    del W, cache, ws
+    return out
 
 
 def main():
@@ -391,10 +436,25 @@ def main():
                      "avg_us": round(dom_avg_s * 1e6, 2)},
         "kernels": kernels,
     }
+    # Per-step distribution: one event per step boundary over another K steps.
+    evs = [torch.cuda.Event(enable_timing=True) for _ in range(K + 1)]
+    torch.cuda.synchronize()
+    evs[0].record(stream)
+    for i in range(K):
+        step()
+        evs[i + 1].record(stream)
+    torch.cuda.synchronize()
+    per = sorted(evs[i].elapsed_time(evs[i + 1]) for i in range(K))
+    out["step_ms_p10_p50_p90"] = [round(per[int(0.1 * (K - 1))], 4), round(per[(K - 1) // 2], 4),
+                                  round(per[int(0.9 * (K - 1))], 4)]
+    if w is not None:
+        out["weight_quantiser_streaming"] = pack_streaming(B, inputs, dev, args.seed)
     if not args.no_cpu_baseline:
+        tiny = inputs.WORKLOADS["tiny"]
+        c1 = (lambda seed: _oracle_step(tiny, seed, tiny["seq_len"])) if w is not None else None
         out["cpu_baseline"] = cpu_baseline(
             T, lambda seed, tokens: sum(f(seed, tokens) for f in oracle_steps), args.seed,
-            args.cpu_seconds)
+            args.cpu_seconds, c1)
     print(json.dumps(out), flush=True)
 
 

@@ -603,12 +603,15 @@ constexpr int kFwdTT = 16, kBwdTT = 8;
 static bool quad_width(int d) { return d == 64 || d == 96 || d == 128; }
 
 
+// The quad-chunk kernels use static LDS only: 0 for their widths.
 size_t norm_rope_fwd_lds(int H, int d) {
+  if (quad_width(d)) return 0;
   const size_t items = (size_t)kFwdTT * 2 * H * (d / 16);
   return items * (32 + 4) + (size_t)kFwdTT * (d / 2) * 8;
 }
 
 size_t norm_rope_bwd_lds(int H, int d) {
+  if (quad_width(d)) return 0;
   const size_t items = (size_t)kBwdTT * 2 * H * (d / 16);
   return items * (64 + 8) + (size_t)kBwdTT * (d / 2) * 8;
 }

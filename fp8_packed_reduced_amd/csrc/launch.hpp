@@ -127,7 +127,8 @@ void launch_dw_reduce(const float* part, int D, int Np, int64_t Tp, const float*
 
 // ---- epilogue.hip ----------------------------------------------------------
 
-// Dynamic LDS bytes of the two epilogue kernels (callers keep them <= 64 KiB).
+// Dynamic LDS bytes of the two epilogue kernels (callers keep them <= 64 KiB);
+// 0 for d_qk = 64, 96, 128, whose kernels use only static LDS.
 size_t norm_rope_fwd_lds(int H, int d_qk);
 size_t norm_rope_bwd_lds(int H, int d_qk);
 

@@ -25,18 +25,17 @@ __device__ inline float4 load_w4(const float* wq, int64_t ldq, const float* wk, 
   return *reinterpret_cast<const float4*>(p);
 }
 
+// Block b takes rows b, b + grid, ... of the logical [D][N] matrix; its
+// threads stride over a row's float4s (no index division), four loads in
+// flight per thread where the row is long enough.
 __global__ __launch_bounds__(kThreads) void amax_w_kernel(
     const float* __restrict__ wq, int64_t ldq, const float* __restrict__ wk, int64_t ldk,
     const float* __restrict__ wv, int64_t ldv, int D, int nq, int N,
     uint32_t* __restrict__ partials) {
   __shared__ uint32_t red[4];
-  const int64_t quads = (int64_t)D * (N / 4);
+  const int quads = N / 4;
   uint32_t m = 0;
-  for (int64_t i = blockIdx.x * (int64_t)kThreads + threadIdx.x; i < quads;
-       i += (int64_t)gridDim.x * kThreads) {
-    const int d = (int)(i / (N / 4));
-    const int n = (int)(i % (N / 4)) * 4;
-    float4 w = load_w4(wq, ldq, wk, ldk, wv, ldv, nq, d, n);
+  auto fold = [&](float4 w) {
     uint32_t a = __float_as_uint(w.x) & 0x7fffffffu;
     uint32_t b = __float_as_uint(w.y) & 0x7fffffffu;
     uint32_t c = __float_as_uint(w.z) & 0x7fffffffu;
@@ -45,6 +44,20 @@ __global__ __launch_bounds__(kThreads) void amax_w_kernel(
     c = c > e ? c : e;
     a = a > c ? a : c;
     m = m > a ? m : a;
+  };
+  for (int d = blockIdx.x; d < D; d += gridDim.x) {
+    int q = threadIdx.x;
+    for (; q + 3 * kThreads < quads; q += 4 * kThreads) {
+      const float4 w0 = load_w4(wq, ldq, wk, ldk, wv, ldv, nq, d, 4 * q);
+      const float4 w1 = load_w4(wq, ldq, wk, ldk, wv, ldv, nq, d, 4 * (q + kThreads));
+      const float4 w2 = load_w4(wq, ldq, wk, ldk, wv, ldv, nq, d, 4 * (q + 2 * kThreads));
+      const float4 w3 = load_w4(wq, ldq, wk, ldk, wv, ldv, nq, d, 4 * (q + 3 * kThreads));
+      fold(w0);
+      fold(w1);
+      fold(w2);
+      fold(w3);
+    }
+    for (; q < quads; q += kThreads) fold(load_w4(wq, ldq, wk, ldk, wv, ldv, nq, d, 4 * q));
   }
   m = block_max_u32(m, red);
   if (threadIdx.x == 0) partials[blockIdx.x] = m;

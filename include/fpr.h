@@ -40,9 +40,10 @@
  *    caller synchronises.
  *
  * Supported shapes: d_model % 64 == 0, d_qk % 16 == 0, d_v % 16 == 0,
- * N % 64 == 0, and the norm/RoPE tiles of 16 tokens must fit 64 KiB of LDS
- * (36 * 2*n_heads*d_qk + 64*d_qk bytes; the pages' 6 heads of 96 use 47 KiB);
- * any 1 <= T <= 2^24 (ragged tails are masked).
+ * N % 64 == 0, n_heads <= 64; for d_qk other than 64, 96 and 128 the
+ * norm/RoPE tiles of 16 tokens must also fit 64 KiB of LDS
+ * (36 * 2*n_heads*d_qk + 64*d_qk bytes); any 1 <= T <= 2^24 (ragged tails
+ * are masked).
  * Alignment: every pointer 16-byte aligned; ldq/ldk/ldv multiples of 4.
  */
 #ifndef FPR_H

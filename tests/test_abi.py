@@ -95,7 +95,8 @@ def test_ragged_tokens_pad_to_whole_k_steps():
     ((768, 6, 96, 128), True), ((128, 1, 96, 128), True), ((768, 6, 64, 128), True),
     ((768, 6, 128, 128), True), ((100, 6, 96, 128), False), ((768, 6, 40, 128), False),
     ((768, 6, 96, 120), False), ((768, 1, 32, 32), False), ((768, 0, 96, 128), False),
-    ((768, 16, 96, 128), False)])
+    ((768, 16, 96, 128), True), ((4096, 32, 96, 128), True), ((768, 24, 48, 64), False),
+    ((768, 65, 96, 128), False)])
 def test_shape_support(dims, ok):
     d = B.make_dims(*dims)
     assert (B.saved_bytes(d, 256) > 0) == ok
