@@ -844,25 +844,28 @@ __global__ __launch_bounds__((TileCfg<BM, BN, MW, NW>::THREADS), 1) void gemm_dw
 }
 
 // Sum the split-K partials in split order (deterministic), scale, and write
-// the three column blocks of dW.
+// the three column blocks of dW.  Block (x, y) covers float4s
+// 256 x .. 256 x + 255 of rows y, y + gridDim.y, ...
 __global__ __launch_bounds__(kThreads) void dw_reduce_kernel(
     const float* __restrict__ part, int splits, int D, int N, const float* __restrict__ sx,
     const float* __restrict__ sg, int nq, float* __restrict__ dwq, int64_t ldq,
     float* __restrict__ dwk, int64_t ldk, float* __restrict__ dwv, int64_t ldv) {
-  const int64_t i = blockIdx.x * (int64_t)kThreads + threadIdx.x;  // float4 index
-  const int64_t quads = (int64_t)D * N / 4;
-  if (i >= quads) return;
-  const int d = (int)(i / (N / 4)), n = (int)(i % (N / 4)) * 4;
-  float4 s = make_float4(0.f, 0.f, 0.f, 0.f);
-  for (int k = 0; k < splits; ++k) {
-    const float4 p = reinterpret_cast<const float4*>(part + ((int64_t)k * D + d) * N)[n / 4];
-    s.x += p.x; s.y += p.y; s.z += p.z; s.w += p.w;
-  }
+  const int n = 4 * (blockIdx.x * kThreads + threadIdx.x);
+  if (n >= N) return;
+  const int64_t plane = (int64_t)D * N;
   const float alpha = sx[0] * sg[0];
-  s = make_float4(s.x * alpha, s.y * alpha, s.z * alpha, s.w * alpha);
-  float* dst = n < nq ? dwq + d * ldq + n : n < 2 * nq ? dwk + d * ldk + (n - nq)
-                                                       : dwv + d * ldv + (n - 2 * nq);
-  *reinterpret_cast<float4*>(dst) = s;
+  for (int d = blockIdx.y; d < D; d += gridDim.y) {
+    const float* src = part + (int64_t)d * N + n;
+    float4 s = make_float4(0.f, 0.f, 0.f, 0.f);
+    for (int k = 0; k < splits; ++k) {
+      const float4 p = *reinterpret_cast<const float4*>(src + k * plane);
+      s.x += p.x; s.y += p.y; s.z += p.z; s.w += p.w;
+    }
+    s = make_float4(s.x * alpha, s.y * alpha, s.z * alpha, s.w * alpha);
+    float* dst = n < nq ? dwq + d * ldq + n : n < 2 * nq ? dwk + d * ldk + (n - nq)
+                                                         : dwv + d * ldv + (n - 2 * nq);
+    *reinterpret_cast<float4*>(dst) = s;
+  }
 }
 
 // ------------------------------------------------------------- launchers
@@ -990,9 +993,9 @@ void launch_gemm_dw(const uint8_t* x8, const uint8_t* g8, int D, int Np, int64_t
 void launch_dw_reduce(const float* part, int D, int Np, int64_t Tp, const float* x_scales,
                       const float* g_scales, float* dwq, int64_t ldq, float* dwk, int64_t ldk,
                       float* dwv, int64_t ldv, int nq, hipStream_t s) {
-  const int64_t quads = (int64_t)D * Np / 4;
-  dw_reduce_kernel<<<(unsigned)ceil_div(quads, kThreads), kThreads, 0, s>>>(
-      part, dw_splits(D, Np, Tp), D, Np, x_scales, g_scales, nq, dwq, ldq, dwk, ldk, dwv, ldv);
+  const dim3 grid((unsigned)ceil_div(Np / 4, kThreads), (unsigned)std::min(D, 32768));
+  dw_reduce_kernel<<<grid, kThreads, 0, s>>>(part, dw_splits(D, Np, Tp), D, Np, x_scales,
+                                             g_scales, nq, dwq, ldq, dwk, ldk, dwv, ldv);
 }
 
 }  // namespace fpr
