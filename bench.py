@@ -247,6 +247,9 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="approximate CPU time of the oracle baseline sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-extras", action="store_true",
+                    help="skip the step-time percentiles and the large-weight quantiser "
+                         "measurement (profiling runs, whose dispatches must be whole steps)")
     ap.add_argument("--grad-format", choices=["e4m3", "e5m2"], default="e4m3",
                     help="FP8 format of the QKV backward's packed gradient")
     args = ap.parse_args()
@@ -436,19 +439,21 @@ def main():
                      "avg_us": round(dom_avg_s * 1e6, 2)},
         "kernels": kernels,
     }
-    # Per-step distribution: one event per step boundary over another K steps.
-    evs = [torch.cuda.Event(enable_timing=True) for _ in range(K + 1)]
-    torch.cuda.synchronize()
-    evs[0].record(stream)
-    for i in range(K):
-        step()
-        evs[i + 1].record(stream)
-    torch.cuda.synchronize()
-    per = sorted(evs[i].elapsed_time(evs[i + 1]) for i in range(K))
-    out["step_ms_p10_p50_p90"] = [round(per[int(0.1 * (K - 1))], 4), round(per[(K - 1) // 2], 4),
-                                  round(per[int(0.9 * (K - 1))], 4)]
-    if w is not None:
-        out["weight_quantiser_streaming"] = pack_streaming(B, inputs, dev, args.seed)
+    if not args.no_extras:
+        # Per-step distribution: one event per step boundary over another K steps.
+        evs = [torch.cuda.Event(enable_timing=True) for _ in range(K + 1)]
+        torch.cuda.synchronize()
+        evs[0].record(stream)
+        for i in range(K):
+            step()
+            evs[i + 1].record(stream)
+        torch.cuda.synchronize()
+        per = sorted(evs[i].elapsed_time(evs[i + 1]) for i in range(K))
+        out["step_ms_p10_p50_p90"] = [round(per[int(0.1 * (K - 1))], 4),
+                                      round(per[(K - 1) // 2], 4),
+                                      round(per[int(0.9 * (K - 1))], 4)]
+        if w is not None:
+            out["weight_quantiser_streaming"] = pack_streaming(B, inputs, dev, args.seed)
     if not args.no_cpu_baseline:
         tiny = inputs.WORKLOADS["tiny"]
         c1 = (lambda seed: _oracle_step(tiny, seed, tiny["seq_len"])) if w is not None else None
