@@ -464,3 +464,130 @@ def test_all_codes_through_the_forward_gemm():
     assert np.array_equal(gpu_y, y)
     # the identity columns reproduce the decode table (signed zeros add to +0)
     assert np.array_equal(oracle.bf16_to_f64(gpu_y[:, :D]), vals + 0.0)
+
+
+# ------------------------------------------------ the largest token count
+
+def _gather_blocked_rows(buf, off, rows, cols, lay):
+    """Rows of a blocked FP8 copy inside a device byte buffer, gathered on the
+    device: [len(rows)][ceil(cols / k_block) * k_block] uint8 on the host."""
+    R, KB = lay.act_block_rows, lay.k_block
+    kc = -(-cols // KB)
+    t = torch.as_tensor(rows, dtype=torch.int64, device=buf.device)
+    kb = torch.arange(kc, device=buf.device)
+    c = torch.arange(KB, device=buf.device)
+    idx = (off + (((t // R)[:, None] * kc + kb[None, :]) * R + (t % R)[:, None])[:, :, None] * KB
+           + c[None, None, :])
+    return buf[idx.reshape(-1)].reshape(len(rows), kc * KB).cpu().numpy()
+
+
+def _gather_blocked_column(buf, off, col, T, cols, lay):
+    """One column (all T rows) of a blocked FP8 copy, gathered on the device."""
+    R, KB = lay.act_block_rows, lay.k_block
+    kc = -(-cols // KB)
+    t = torch.arange(T, dtype=torch.int64, device=buf.device)
+    idx = off + (((t // R) * kc + col // KB) * R + t % R) * KB + col % KB
+    return buf[idx].cpu().numpy()
+
+
+def test_max_tokens_sampled():
+    """The largest supported token count, T = 2^24 (256 sequences of 65536
+    positions), at the tiny workload's widths (D = 128, one head), so that
+    every tensor fits: the offsets that this token cap is there to keep in
+    range are exercised at their limit.  Inputs come from torch's seeded
+    generator on the device (x ~ N(0,1), dq/dk/dv ~ N(0, 1e-2)); the oracle
+    gets the same values copied to the host.  Checked: both scales against
+    the oracle's quantiser of the whole tensor's amax; sampled token rows of
+    x8, q, k, v, the gradient codes and dX against the oracle; and dW
+    entries (sums over all 2^24 tokens) to 1e-3 of their natural scale
+    sqrt(sum of squared terms)."""
+    from fp8_packed_reduced_amd import binding as B
+    w = dict(inputs.WORKLOADS["tiny"], n_seq=256, seq_len=65536)
+    n_seq, S, D, H, dqk, dvw = (w[k] for k in ("n_seq", "seq_len", "d_model", "n_heads",
+                                                "d_qk", "d_v"))
+    T, nq = n_seq * S, H * dqk
+    assert T == 1 << 24
+    dims_o = _dims(w)
+    dims = B.make_dims(D, H, dqk, dvw, EPS, BASE)
+    dev = torch.device("cuda")
+    g = torch.Generator(device=dev)
+    g.manual_seed(2024)
+    say(f"[gpu] max tokens: T={T} D={D} H={H}")
+    x = torch.randn((T, D), generator=g, device=dev).to(torch.bfloat16)
+    dq = (torch.randn((n_seq, H, S, dqk), generator=g, device=dev) * 0.1).to(torch.bfloat16)
+    dk = (torch.randn((n_seq, H, S, dqk), generator=g, device=dev) * 0.1).to(torch.bfloat16)
+    dv = (torch.randn((n_seq, H, S, dvw), generator=g, device=dev) * 0.1).to(torch.bfloat16)
+    W = inputs.make_w(w, 43)
+    Wd = torch.from_numpy(W).to(dev)
+    cache = B.WeightCache(dims)
+    B.pack_quantize_weights(dims, Wd[:, :nq], Wd[:, nq:2 * nq], Wd[:, 2 * nq:], cache)
+    q, k, v, saved = B.qkv_forward(dims, n_seq, S, x, cache)
+    ws_b = torch.empty(B.workspace_bytes(dims, T, B.FPR_CALL_BACKWARD), dtype=torch.uint8,
+                       device=dev)
+    dx, dw = B.qkv_backward(dims, n_seq, S, dq, dk, dv, saved, cache, workspace=ws_b)
+    torch.cuda.synchronize()
+    say("[gpu] max tokens: run done")
+    lay = B.layout(dims, T)
+    assert int(cache.status.item()) == 0
+    wp, _, s_w, _, _ = oracle.pack_quantize_weights(dims_o, W)
+    assert np.array_equal(cache.w_packed.cpu().numpy(), wp)
+
+    def bits(t):
+        return t.contiguous().view(torch.int16).cpu().numpy().view(np.uint16)
+
+    def amax_scales(*arrays):
+        m = max(int((a & 0x7FFF).max()) for a in arrays)  # |bf16| bit patterns are ordered
+        _, s, inv, _ = oracle.quantize_bf16(np.array([m], np.uint16))
+        return s, inv
+
+    x_h = bits(x)
+    s_x, inv_x = amax_scales(x_h)
+    xsc = B.view_bytes(saved, lay.saved_x_scales, (2,), torch.float32).cpu().numpy()
+    assert xsc[0] == s_x and xsc[1] == inv_x
+    rng = np.random.default_rng(3)
+    rows = np.unique(np.concatenate([[0, 1, S - 1, S, T - S, T - 2, T - 1],
+                                     rng.choice(T, 57, replace=False)]))
+    pos = rows % S
+    x8r = _gather_blocked_rows(saved, lay.saved_x8, rows, D, lay)[:, :D]
+    assert np.array_equal(x8r, oracle.e4m3_encode(oracle.bf16_to_f64(x_h[rows]) * inv_x))
+    # forward rows: the oracle's GEMM and norm/RoPE of these tokens
+    y64 = oracle.gemm_e4m3(x8r, wp, s_x, s_w)
+    qk_pre = B.view_bytes(saved, lay.saved_qk_pre, (T, 2 * nq), torch.bfloat16)
+    qkr = bits(qk_pre[torch.as_tensor(rows, device=dev)])
+    _, over = bf16_gemm_excess(qkr, y64[:, :2 * nq], oracle.round_bf16)
+    a = bf16_to_f64(qkr)
+    qo = oracle.qk_norm_rope_fwd(a[:, :nq].reshape(-1, H, dqk), pos, EPS, BASE)
+    ko = oracle.qk_norm_rope_fwd(a[:, nq:].reshape(-1, H, dqk), pos, EPS, BASE)
+    b_idx, s_idx = torch.as_tensor(rows // S, device=dev), torch.as_tensor(pos, device=dev)
+    e_q = row_rel_err(bf16_to_f64(bits(q[b_idx, :, s_idx])), qo)
+    e_k = row_rel_err(bf16_to_f64(bits(k[b_idx, :, s_idx])), ko)
+    vr = bits(v[b_idx, :, s_idx]).reshape(len(rows), -1)
+    _, over_v = bf16_gemm_excess(vr, y64[:, 2 * nq:], oracle.round_bf16)
+    # gradient scale from the whole dQKV; gradient codes and dX on the rows
+    dqkv = B.view_bytes(ws_b, lay.bwd_dqkv, (T, 2 * nq), torch.bfloat16)
+    s_g, inv_g = amax_scales(bits(dqkv), bits(dv))
+    gsc = B.view_bytes(ws_b, lay.bwd_g_scales, (2,), torch.float32).cpu().numpy()
+    assert gsc[0] == s_g and gsc[1] == inv_g
+    N = 2 * nq + H * dvw
+    g8r = _gather_blocked_rows(ws_b, lay.bwd_g8, rows, N, lay)[:, :N]
+    gr = np.concatenate([bits(dqkv[torch.as_tensor(rows, device=dev)]),
+                         bits(dv[b_idx, :, s_idx]).reshape(len(rows), -1)], axis=1)
+    assert np.array_equal(g8r, oracle.e4m3_encode(oracle.bf16_to_f64(gr) * inv_g))
+    dx64 = oracle.gemm_e4m3(g8r, np.ascontiguousarray(wp.T), s_g, s_w)
+    _, over_dx = bf16_gemm_excess(bits(dx[torch.as_tensor(rows, device=dev)]), dx64,
+                                  oracle.round_bf16)
+    # dW entries over all tokens
+    tab = oracle.e4m3_decode_table()
+    dw_h = dw.cpu().numpy()
+    worst = 0.0
+    for j in (0, D - 1):
+        xc = tab[_gather_blocked_column(saved, lay.saved_x8, j, T, D, lay)]
+        for n in (0, nq, 2 * nq, N - 1):
+            terms = xc * tab[_gather_blocked_column(ws_b, lay.bwd_g8, n, T, N, lay)]
+            exact = float(s_x) * float(s_g) * terms.sum()
+            scale = float(s_x) * float(s_g) * np.sqrt(np.sum(terms * terms))
+            worst = max(worst, abs(float(dw_h[j, n]) - exact) / scale)
+    say(f"[gpu] max tokens: gemm excess {over:.2e} v {over_v:.2e} q {e_q:.2e} k {e_k:.2e} "
+        f"dx excess {over_dx:.2e} dw {worst:.2e}")
+    assert over <= GEMM_TOL and over_v <= GEMM_TOL and over_dx <= GEMM_TOL
+    assert max(e_q, e_k) <= NORM_TOL and worst <= GEMM_TOL
