@@ -128,8 +128,8 @@ def read_traffic(workload: str, stage: str):
     return None
 
 
-def _oracle_step(w: dict, seed: int, tokens: int) -> float:
-    """Seconds the oracle takes for pack + forward + backward of the first
+def _oracle_step(w: dict, seed: int, tokens: int, backward: bool = True) -> float:
+    """Seconds the oracle takes for pack + forward (+ backward) of the first
     `tokens` tokens of the workload (as one sequence)."""
     import oracle
     from fp8_packed_reduced_amd import inputs
@@ -143,8 +143,9 @@ def _oracle_step(w: dict, seed: int, tokens: int) -> float:
     t0 = time.perf_counter()
     wp, _, s_w, _, _ = oracle.pack_quantize_weights(dims, W)
     of = oracle.qkv_forward(dims, 1, tokens, x, wp, s_w)
-    oracle.qkv_backward(dims, 1, tokens, dq, dk, dv, of["x8"], of["s_x"],
-                        of["y_bits"][:, :nqk2], wp, s_w)
+    if backward:
+        oracle.qkv_backward(dims, 1, tokens, dq, dk, dv, of["x8"], of["s_x"],
+                            of["y_bits"][:, :nqk2], wp, s_w)
     return time.perf_counter() - t0
 
 
@@ -165,7 +166,8 @@ def _oracle_mlp_step(w: dict, seed: int, tokens: int) -> float:
     return time.perf_counter() - t0
 
 
-def cpu_baseline(T: int, oracle_step, seed: int, target_s: float, c1_step=None) -> dict:
+def cpu_baseline(T: int, oracle_step, seed: int, target_s: float, c1_step=None,
+                 what: str = "pack + forward + backward") -> dict:
     """The oracle, untouched, timed on a bounded prefix of the workload whose
     length is chosen (in multiples of 4096 tokens, at most the whole
     workload) from a 4096-token probe so that it takes about target_s; when
@@ -197,7 +199,7 @@ def cpu_baseline(T: int, oracle_step, seed: int, target_s: float, c1_step=None) 
     return {"value": round(reps * tokens / dt, 1), "unit": "tokens/s", "cores": cores,
             "c1_single_thread_s": single,
             "kind": "oracle",
-            "sample": f"pack + forward + backward of the first {tokens} tokens (one sequence, "
+            "sample": f"{what} of the first {tokens} tokens (one sequence, "
                       f"positions 0..{tokens - 1}) of the same workload and seed{runs}; "
                       f"{dt:.2f} s"}
 
@@ -247,6 +249,8 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="approximate CPU time of the oracle baseline sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--forward-only", action="store_true",
+                    help="time pack + forward only (the 16k-token forward configuration)")
     ap.add_argument("--no-extras", action="store_true",
                     help="skip the step-time percentiles and the large-weight quantiser "
                          "measurement (profiling runs, whose dispatches must be whole steps)")
@@ -304,16 +308,18 @@ def main():
         def qkv_step():
             B.pack_quantize_weights(dims, wq, wk, wv, cache, workspace=ws_p)
             B.qkv_forward(dims, n_seq, S, x, cache, q, k, v, saved, ws_f)
-            B.qkv_backward(dims, n_seq, S, dq, dk, dv, saved, cache, dx, dw, ws_b)
+            if not args.forward_only:
+                B.qkv_backward(dims, n_seq, S, dq, dk, dv, saved, cache, dx, dw, ws_b)
 
         steps.append(qkv_step)
         work.update(stage_work(w, B.layout(dims, T).dw_splits))
-        gemm_flop += 3 * 2 * T * D * N
+        gemm_flop += (1 if args.forward_only else 3) * 2 * T * D * N
         config.update(n_seq=n_seq, seq_len=S, d_model=D, n_heads=H, d_qk=dqk, d_v=dvw,
                       packed_n=N)
         if args.grad_format != "e4m3":
             config["grad_format"] = args.grad_format
-        oracle_steps.append(lambda seed, tokens: _oracle_step(w, seed, tokens))
+        oracle_steps.append(
+            lambda seed, tokens: _oracle_step(w, seed, tokens, not args.forward_only))
     if wm is not None:
         Dm, F = wm["d_model"], wm["d_ff"]
         mdims = B.MlpDims(Dm, F)
@@ -345,10 +351,18 @@ def main():
         config.update(d_model=Dm, d_ff=F)
         oracle_steps.append(lambda seed, tokens: _oracle_mlp_step(wm, seed, tokens))
     config["step"] = " + ".join(
-        (["pack_quantize_weights + qkv_forward + qkv_backward"] if w is not None else []) +
+        (["pack_quantize_weights + qkv_forward" + ("" if args.forward_only else " + qkv_backward")]
+         if w is not None else []) +
         (["mlp_pack_quantize_weights + mlp_forward + mlp_backward"] if wm is not None else []))
     config["seed"] = args.seed
     metric = METRIC if wm is None else METRIC_MLP if w is None else METRIC_BLOCK
+    if w is not None and (D, H, T, dqk) != (768, 6, 65536, 96):  # another QKV shape
+        metric = (f"packed FP8 QKV fwd+bwd tokens/s and TFLOP/s (% FP8 peak) at "
+                  f"D={D},H={H},d_qk={dqk},T={T}")
+    if args.forward_only:
+        if wm is not None:
+            raise SystemExit("--forward-only applies to the QKV workloads")
+        metric = metric.replace("fwd+bwd", "forward (pack + forward)")
 
     def step():
         for f in steps:
@@ -459,7 +473,8 @@ def main():
         c1 = (lambda seed: _oracle_step(tiny, seed, tiny["seq_len"])) if w is not None else None
         out["cpu_baseline"] = cpu_baseline(
             T, lambda seed, tokens: sum(f(seed, tokens) for f in oracle_steps), args.seed,
-            args.cpu_seconds, c1)
+            args.cpu_seconds, c1,
+            "pack + forward" if args.forward_only else "pack + forward + backward")
     print(json.dumps(out), flush=True)
 
 
