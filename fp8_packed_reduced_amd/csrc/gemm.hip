@@ -314,6 +314,11 @@ __device__ __forceinline__ void issue_next(CopyState<C>& st, uint8_t* lds, const
 #if defined(__HIP_DEVICE_COMPILE__)  // an AMDGPU builtin: the host pass never runs this
     __builtin_amdgcn_global_load_lds((t < C::A_PER_WAVE ? Ak : Bk) + off,
                                      stage + (cw + kCopyWaves * t) * 1024, 16, 0, 0);
+#else
+    (void)off;
+    (void)stage;
+    (void)Ak;
+    (void)Bk;
 #endif
   }
 }
