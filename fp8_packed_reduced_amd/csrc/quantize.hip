@@ -77,7 +77,7 @@ __device__ inline uint32_t absmax_bits8(uint4 v) {
   return m;
 }
 
-// Four independent 16-byte loads in flight per thread.
+// Eight independent 16-byte loads in flight per thread.
 __global__ __launch_bounds__(kThreads) void amax_bf16_kernel(const uint16_t* __restrict__ x,
                                                              int64_t n,
                                                              uint32_t* __restrict__ partials) {
@@ -86,9 +86,12 @@ __global__ __launch_bounds__(kThreads) void amax_bf16_kernel(const uint16_t* __r
   const uint4* v = reinterpret_cast<const uint4*>(x);
   uint32_t m = 0;
   int64_t i = blockIdx.x * (int64_t)kThreads + threadIdx.x;
-  for (; i + 3 * stride < vecs; i += 4 * stride) {
-    const uint4 a = v[i], b = v[i + stride], c = v[i + 2 * stride], d = v[i + 3 * stride];
-    m = max(m, max(max(absmax_bits8(a), absmax_bits8(b)), max(absmax_bits8(c), absmax_bits8(d))));
+  for (; i + 7 * stride < vecs; i += 8 * stride) {
+    uint4 a[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) a[j] = v[i + j * stride];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) m = max(m, absmax_bits8(a[j]));
   }
   for (; i < vecs; i += stride) m = max(m, absmax_bits8(v[i]));
   m = block_max_u32(m << 16, red);
