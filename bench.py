@@ -23,6 +23,7 @@ FP8 ReLU^2 MLP alone (``mlp_64k``: mlp_pack_quantize_weights + mlp_forward
 from __future__ import annotations
 
 import argparse
+import contextlib
 import hashlib
 import json
 import os
@@ -249,6 +250,8 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="approximate CPU time of the oracle baseline sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--graph", action="store_true",
+                    help="time the step replayed from a captured HIP graph")
     ap.add_argument("--forward-only", action="store_true",
                     help="time pack + forward only (the 16k-token forward configuration)")
     ap.add_argument("--no-extras", action="store_true",
@@ -364,9 +367,11 @@ def main():
             raise SystemExit("--forward-only applies to the QKV workloads")
         metric = metric.replace("fwd+bwd", "forward (pack + forward)")
 
-    def step():
+    def eager_step():
         for f in steps:
             f()
+
+    step = eager_step
 
     # A streaming kernel of known traffic (the e4m3 encoder: 256 MiB of fp32
     # read, 64 MiB of codes written), so that rocprofv3 byte counters taken on
@@ -380,11 +385,19 @@ def main():
     for _ in range(max(args.warmup, 1)):
         step()
     torch.cuda.synchronize()
+    if args.graph:  # the same kernels, launched by one graph replay per step
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            eager_step()
+        torch.cuda.synchronize()
+        step = graph.replay
+        step()
+        torch.cuda.synchronize()
     # Per-stage times: the mean over TRACE_STEPS traced steps (the sum of a
     # stage's launches in a step; a single step is too noisy to rank by).
     with B.KernelTrace(32 * TRACE_STEPS, device=dev) as tr:
         for _ in range(TRACE_STEPS):
-            step()
+            eager_step()
     torch.cuda.synchronize()
     per_stage, launches = {}, {}
     for name, ms in tr.records():
@@ -396,7 +409,10 @@ def main():
     stream = torch.cuda.current_stream(dev)
     e0 = torch.cuda.Event(enable_timing=True)
     e1 = torch.cuda.Event(enable_timing=True)
-    with B.KernelTrace(K * launches[dominant] // TRACE_STEPS, only=dominant, device=dev) as dom:
+    # The dominant kernel is timed inside the timed region; a graph replay
+    # makes no library calls, so in that mode it is timed over K eager steps.
+    dom = B.KernelTrace(K * launches[dominant] // TRACE_STEPS, only=dominant, device=dev)
+    with (contextlib.nullcontext() if args.graph else dom):
         torch.cuda.synchronize()
         t_wall = time.perf_counter()
         e0.record(stream)
@@ -405,6 +421,11 @@ def main():
         e1.record(stream)
         torch.cuda.synchronize()
         t_wall = time.perf_counter() - t_wall
+    if args.graph:
+        with dom:
+            for _ in range(K):
+                eager_step()
+        torch.cuda.synchronize()
     ms_total = e0.elapsed_time(e1)
     ms_step = ms_total / K
     dom_ms = [ms for _, ms in dom.records()]
@@ -447,6 +468,7 @@ def main():
         "tflops": round(tflops, 1),
         "pct_fp8_peak": round(100 * tflops * 1e12 / PEAK_FP8_FLOPS, 2),
         "wall_ms_per_step": round(t_wall * 1e3 / K, 4),
+        "launch": "hip graph replay" if args.graph else "eager",
         "roofline": {"kernel": dominant, "bound": kind, "achieved": round(achieved, 1),
                      "peak": peak, "unit": unit, "frac": round(achieved / peak, 4),
                      "traffic": traffic, "launches": len(dom_ms),
