@@ -488,6 +488,20 @@ def main():
         out["step_ms_p10_p50_p90"] = [round(per[int(0.1 * (K - 1))], 4),
                                       round(per[(K - 1) // 2], 4),
                                       round(per[int(0.9 * (K - 1))], 4)]
+        # Cold: 512 MB written between steps evicts the 256 MB last-level
+        # cache; each step is timed on its own, the flush outside the events.
+        flush = torch.empty(512 << 20, dtype=torch.uint8, device=dev)
+        cold = []
+        for i in range(min(K, 20)):
+            flush.fill_(i & 0xFF)
+            c0, c1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            c0.record(stream)
+            step()
+            c1.record(stream)
+            torch.cuda.synchronize()
+            cold.append(c0.elapsed_time(c1))
+        del flush
+        out["cold_ms_per_step"] = round(sum(cold) / len(cold), 4)
         if w is not None:
             out["weight_quantiser_streaming"] = pack_streaming(B, inputs, dev, args.seed)
     if not args.no_cpu_baseline:
