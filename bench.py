@@ -45,6 +45,7 @@ CALIB_FLOATS = 64 << 20   # counter calibration: encoder over 256 MiB of fp32
 STAGE_SOURCES = {
     "amax_w": "quantize.hip", "quantize_w": "quantize.hip",
     "amax_x": "quantize.hip", "quantize_x": "quantize.hip", "quantize_g": "quantize.hip",
+    "amax_dv": "quantize.hip",
     "gemm_fwd": "gemm.hip", "gemm_dx": "gemm.hip", "gemm_dw": "gemm.hip",
     "dw_reduce": "gemm.hip", "norm_rope_fwd": "epilogue.hip", "norm_rope_bwd": "epilogue.hip",
     "mlp_amax_w": "quantize.hip", "mlp_quantize_w": "quantize.hip",
@@ -74,7 +75,8 @@ def stage_work(w: dict, dw_splits: int) -> dict:
         "quantize_x": ("hbm", 2 * T * D + T * D),                # bf16 in, e4m3 out
         "gemm_fwd": ("mfma", gemm),
         "norm_rope_fwd": ("hbm", 2 * T * qk + 2 * T * qk),       # pre-norm Q|K in, q|k out
-        "norm_rope_bwd": ("hbm", 2 * T * qk * 2 + 2 * T * vv + 2 * T * qk),  # dq,dk,pre, dv in; dQK out
+        "norm_rope_bwd": ("hbm", 2 * T * qk * 2 + 2 * T * qk),  # dq, dk, pre-norm in; dQK out
+        "amax_dv": ("hbm", 2 * T * vv),
         "quantize_g": ("hbm", 2 * T * N + T * N),
         "gemm_dx": ("mfma", gemm),
         "gemm_dw": ("mfma", gemm),

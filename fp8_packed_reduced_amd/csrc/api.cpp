@@ -28,7 +28,7 @@ struct Plan {
   size_t f_part, fwd_total;
   int f_parts;
   size_t b_part, b_gsc, b_dqkv, b_g8, b_dwpart, bwd_total;
-  int b_parts;
+  int b_parts, b_nr_parts, b_dv_parts;  // all amax partials = norm/RoPE's, then dv's
   size_t p_part, pack_total;
 };
 
@@ -85,7 +85,10 @@ Plan make_plan(const fpr_dims* d, int64_t T) {
   p.f_part = take(c, (size_t)p.f_parts * 4);
   p.fwd_total = c;
   c = 0;
-  p.b_parts = fpr::norm_rope_bwd_blocks(T > 0 ? T : 1, p.H, p.dqk);
+  p.b_nr_parts = fpr::norm_rope_bwd_blocks(T > 0 ? T : 1, p.H, p.dqk);
+  p.b_dv_parts = (int)std::max<int64_t>(
+      1, std::min<int64_t>(kPartsAct, ceil_div(T * p.H * p.dv / 8, fpr::kThreads)));
+  p.b_parts = p.b_nr_parts + p.b_dv_parts;
   p.b_part = take(c, (size_t)p.b_parts * 4);
   p.b_gsc = take(c, 4 * sizeof(float));
   p.b_dqkv = take(c, (size_t)T * p.nqk2 * 2);
@@ -360,8 +363,11 @@ int qkv_backward(const fpr_dims* dims, int32_t n_seq, int32_t seq_len, const uin
   uint8_t* g8 = at<uint8_t>(workspace, p.b_g8);
   float* dwpart = at<float>(workspace, p.b_dwpart);
   stage("norm_rope_bwd", s, [&] {
-    fpr::launch_norm_rope_bwd(dq, dk, dv, qk, T, seq_len, p.H, p.dqk, p.qs, p.dv, dims->eps,
+    fpr::launch_norm_rope_bwd(dq, dk, qk, T, seq_len, p.H, p.dqk, p.qs, dims->eps,
                               dims->rope_base, dqkv, parts, s);
+  });
+  stage("amax_dv", s, [&] {
+    fpr::launch_amax_bf16(dv, T * p.H * p.dv, parts + p.b_nr_parts, p.b_dv_parts, s);
   });
   const bool e5 = dims->grad_format == FPR_FORMAT_E5M2;
   stage("quantize_g", s, [&] {

@@ -11,8 +11,8 @@
 // Backward ("Where the eight seconds were hiding", "The inventory": the norm,
 // RoPE and backward shuffles): du = R_{-p} dq; da = rho * (du - u <u,du>/d)
 // into the Q|K part of the packed gradient, dQK [T][2H d] bf16, with one
-// amax partial per block over dQK and dv together for the gradient
-// quantiser, which reads the V columns straight from dv.
+// amax partial per block over dQK for the gradient quantiser, which reads
+// the V columns straight from dv (whose amax a separate pass takes).
 //
 // Main kernels (d = 64, 96, 128): four consecutive lanes own one head row
 // and every access is a whole 16-byte chunk (below); the row sums take two
@@ -350,32 +350,21 @@ __device__ __forceinline__ uint32_t qc_bwd_finish(const QcBwdRow<D>& r, const fl
   return amax;
 }
 
-// Chunk i of the V gradient rows of tokens t0 .. t0 + nt - 1, head-major
-// (head, token, chunk of CV), so consecutive i are consecutive in memory.
-__device__ __forceinline__ uint4 dv_chunk(const uint16_t* __restrict__ dv, int i, int CV, int nt,
-                                          int H, int seq_len, int dvw, int64_t t0) {
-  const int cc = i % CV, rest = i / CV, tt = rest % nt, hh = rest / nt;
-  const int t = (int)t0 + tt, b = t / seq_len, sp = t - b * seq_len;
-  return *reinterpret_cast<const uint4*>(dv + (((int64_t)b * H + hh) * seq_len + sp) * dvw +
-                                         8 * cc);
-}
-
 // Per token group, every load is issued before anything waits on one: the
 // lane's bwd_rows<D>() head rows (for d = 96 and H = 6, the group's 192
-// rows are exactly 3 per quad) and its kBwdDv chunks of the V gradient
-// (only their amax is needed); the cos/sin table of the group is built
+// rows are exactly 3 per quad); the cos/sin table of the group is built
 // while they are in flight.  Three rows of d = 128 would not fit two waves
-// per SIMD in registers.
+// per SIMD in registers.  The V gradient's amax is a separate streaming
+// pass over dv (launch_amax_bf16): reading it here, head-major beside four
+// other streams, cost more than that pass.
 template <int D>
 constexpr int bwd_rows() { return D == 128 ? 2 : 3; }
-constexpr int kBwdDv = 6;
 
 template <int D>
 __global__ __launch_bounds__(kThreads) void norm_rope_bwd_qc(
     const uint16_t* __restrict__ dq, const uint16_t* __restrict__ dk,
-    const uint16_t* __restrict__ dv, const uint16_t* __restrict__ qk_pre, int64_t T,
-    int seq_len, int H, int qs, int dvw, float eps, float base, uint16_t* __restrict__ dqkv,
-    uint32_t* __restrict__ partials) {
+    const uint16_t* __restrict__ qk_pre, int64_t T, int seq_len, int H, int qs, float eps,
+    float base, uint16_t* __restrict__ dqkv, uint32_t* __restrict__ partials) {
   using Q = QuadChunks<D>;
   constexpr int h = Q::h, QUADS = kThreads / 4, RB = bwd_rows<D>();
   __shared__ double rev[h];
@@ -384,18 +373,12 @@ __global__ __launch_bounds__(kThreads) void norm_rope_bwd_qc(
   __shared__ int sp[kQuadTT];
   __shared__ uint32_t red[4];
   build_rev_table(rev, h, D, base);
-  const int R = 2 * H, qkw = R * D, CV = dvw / 8, l = threadIdx.x & 3, quad = threadIdx.x >> 2;
+  const int R = 2 * H, qkw = R * D, l = threadIdx.x & 3, quad = threadIdx.x >> 2;
   uint32_t amax = 0;
   const int64_t groups = ceil_div(T, kQuadTT);
   for (int64_t gi = blockIdx.x; gi < groups; gi += gridDim.x) {
     const int64_t t0 = gi * kQuadTT;
-    const int nt = (int)min<int64_t>(kQuadTT, T - t0), rows = nt * R, nv = nt * H * CV;
-    uint4 vv[kBwdDv];
-#pragma unroll
-    for (int j = 0; j < kBwdDv; ++j) {
-      const int i = threadIdx.x + j * kThreads;
-      vv[j] = i < nv ? dv_chunk(dv, i, CV, nt, H, seq_len, dvw, t0) : make_uint4(0, 0, 0, 0);
-    }
+    const int nt = (int)min<int64_t>(kQuadTT, T - t0), rows = nt * R;
     for (int rb = 0; rb < rows; rb += RB * QUADS) {
       QcBwdRow<D> r[RB];
 #pragma unroll
@@ -410,10 +393,6 @@ __global__ __launch_bounds__(kThreads) void norm_rope_bwd_qc(
       for (int j = 0; j < RB; ++j)
         amax = max(amax, qc_bwd_finish<D>(r[j], cs, t0, qkw, eps, dqkv, l));
     }
-#pragma unroll
-    for (int j = 0; j < kBwdDv; ++j) amax = max(amax, absmax8(vv[j]));
-    for (int i = threadIdx.x + kBwdDv * kThreads; i < nv; i += kThreads)
-      amax = max(amax, absmax8(dv_chunk(dv, i, CV, nt, H, seq_len, dvw, t0)));
     __syncthreads();
   }
   amax = block_max_u32(amax << 16, red);
@@ -497,9 +476,8 @@ __global__ __launch_bounds__(kThreads) void norm_rope_fwd_kernel(
 template <int TT>
 __global__ __launch_bounds__(kThreads) void norm_rope_bwd_kernel(
     const uint16_t* __restrict__ dq, const uint16_t* __restrict__ dk,
-    const uint16_t* __restrict__ dv, const uint16_t* __restrict__ qk_pre, int64_t T,
-    int seq_len, int H, int d, int qs, int dvw, float eps, float base,
-    uint16_t* __restrict__ dqkv, uint32_t* __restrict__ partials) {
+    const uint16_t* __restrict__ qk_pre, int64_t T, int seq_len, int H, int d, int qs,
+    float eps, float base, uint16_t* __restrict__ dqkv, uint32_t* __restrict__ partials) {
   extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
   __shared__ uint32_t red[4];
   const int h = d / 2, C = h / 8, R = 2 * H, qkw = R * d;
@@ -582,16 +560,6 @@ __global__ __launch_bounds__(kThreads) void norm_rope_bwd_kernel(
     *reinterpret_cast<uint4*>(dst + 8 * c) = plo;
     *reinterpret_cast<uint4*>(dst + h + 8 * c) = phi;
   }
-  // amax of the V gradient
-  const int cv = dvw / 8, vitems = TT * H * cv;
-  for (int it = threadIdx.x; it < vitems; it += kThreads) {
-    const int c = it % cv, hh = (it / cv) % H, tt = it / (cv * H);
-    const int64_t t = t0 + tt;
-    if (t >= T) continue;
-    const int64_t bseq = t / seq_len, s = t - bseq * seq_len;
-    amax = max(amax, absmax8(*reinterpret_cast<const uint4*>(
-                         dv + ((bseq * H + hh) * seq_len + s) * dvw + 8 * c)));
-  }
   amax = block_max_u32(amax << 16, red);
   if (threadIdx.x == 0) partials[blockIdx.x] = amax;
 }
@@ -646,30 +614,29 @@ int norm_rope_bwd_blocks(int64_t T, int H, int d) {
              : (int)ceil_div(T, kBwdTT);
 }
 
-void launch_norm_rope_bwd(const uint16_t* dq, const uint16_t* dk, const uint16_t* dv,
-                          const uint16_t* qk_pre, int64_t T, int seq_len, int H, int d, int qs,
-                          int d_v, float eps, float base, uint16_t* dqkv, uint32_t* partials,
-                          hipStream_t s) {
+void launch_norm_rope_bwd(const uint16_t* dq, const uint16_t* dk, const uint16_t* qk_pre,
+                          int64_t T, int seq_len, int H, int d, int qs, float eps, float base,
+                          uint16_t* dqkv, uint32_t* partials, hipStream_t s) {
   const unsigned grid = (unsigned)norm_rope_bwd_blocks(T, H, d);
   switch (d) {
     case 64:
-      norm_rope_bwd_qc<64><<<grid, kThreads, 0, s>>>(dq, dk, dv, qk_pre, T, seq_len, H, qs, d_v,
-                                                        eps, base, dqkv, partials);
+      norm_rope_bwd_qc<64><<<grid, kThreads, 0, s>>>(dq, dk, qk_pre, T, seq_len, H, qs, eps,
+                                                        base, dqkv, partials);
       return;
     case 96:
-      norm_rope_bwd_qc<96><<<grid, kThreads, 0, s>>>(dq, dk, dv, qk_pre, T, seq_len, H, qs, d_v,
-                                                        eps, base, dqkv, partials);
+      norm_rope_bwd_qc<96><<<grid, kThreads, 0, s>>>(dq, dk, qk_pre, T, seq_len, H, qs, eps,
+                                                        base, dqkv, partials);
       return;
     case 128:
-      norm_rope_bwd_qc<128><<<grid, kThreads, 0, s>>>(dq, dk, dv, qk_pre, T, seq_len, H, qs,
-                                                         d_v, eps, base, dqkv, partials);
+      norm_rope_bwd_qc<128><<<grid, kThreads, 0, s>>>(dq, dk, qk_pre, T, seq_len, H, qs, eps,
+                                                        base, dqkv, partials);
       return;
     default:
       break;
   }
   const size_t lds = norm_rope_bwd_lds(H, d);
-  norm_rope_bwd_kernel<kBwdTT><<<grid, kThreads, lds, s>>>(dq, dk, dv, qk_pre, T, seq_len, H, d,
-                                                          qs, d_v, eps, base, dqkv, partials);
+  norm_rope_bwd_kernel<kBwdTT><<<grid, kThreads, lds, s>>>(dq, dk, qk_pre, T, seq_len, H, d, qs,
+                                                          eps, base, dqkv, partials);
 }
 
 }  // namespace fpr

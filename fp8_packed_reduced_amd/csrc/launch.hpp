@@ -140,13 +140,13 @@ void launch_norm_rope_fwd(const uint16_t* qk_pre, int64_t T, int seq_len, int H,
                           hipStream_t s);
 
 // Backward epilogue: dq, dk (head-major, rows of qs elements of which the
-// first d_qk are read) + qk_pre -> the Q|K part of the
-// packed gradient, dQK [T][2 H d_qk] bf16, plus one amax partial per block
-// over dQK and dv; norm_rope_bwd_blocks() is that block count.
+// first d_qk are read) + qk_pre -> the Q|K part of the packed gradient,
+// dQK [T][2 H d_qk] bf16, plus one amax partial per block over dQK;
+// norm_rope_bwd_blocks() is that block count.  (dv's amax is taken by
+// launch_amax_bf16.)
 int norm_rope_bwd_blocks(int64_t T, int H, int d_qk);
-void launch_norm_rope_bwd(const uint16_t* dq, const uint16_t* dk, const uint16_t* dv,
-                          const uint16_t* qk_pre, int64_t T, int seq_len, int H, int d_qk,
-                          int qs, int d_v, float eps, float base, uint16_t* dqkv,
-                          uint32_t* partials, hipStream_t s);
+void launch_norm_rope_bwd(const uint16_t* dq, const uint16_t* dk, const uint16_t* qk_pre,
+                          int64_t T, int seq_len, int H, int d_qk, int qs, float eps, float base,
+                          uint16_t* dqkv, uint32_t* partials, hipStream_t s);
 
 }  // namespace fpr

@@ -22,7 +22,7 @@ import sys
 
 # Launch order of one step of each part (a stage may launch more than once)
 QKV_ORDER = ["amax_w", "quantize_w", "amax_x", "quantize_x", "gemm_fwd", "norm_rope_fwd",
-             "norm_rope_bwd", "quantize_g", "gemm_dx", "gemm_dw", "dw_reduce"]
+             "norm_rope_bwd", "amax_dv", "quantize_g", "gemm_dx", "gemm_dw", "dw_reduce"]
 MLP_ORDER = ["mlp_amax_w", "mlp_quantize_w", "mlp_amax_w", "mlp_quantize_w", "mlp_amax_x",
              "mlp_quantize_x", "mlp_gemm_up", "mlp_quantize_h", "mlp_gemm_down", "mlp_amax_dy",
              "mlp_quantize_dy", "mlp_gemm_dh", "mlp_quantize_dpre", "mlp_gemm_dx",
@@ -31,7 +31,8 @@ KERNEL_OF_STAGE = {
     "amax_w": "amax_w_kernel", "quantize_w": "quantize_w_kernel",
     "amax_x": "amax_bf16_kernel", "quantize_x": "quantize_act_kernel",
     "gemm_fwd": "gemm_bf16out_kernel", "norm_rope_fwd": "norm_rope_fwd",
-    "norm_rope_bwd": "norm_rope_bwd", "quantize_g": "quantize_act_kernel",
+    "norm_rope_bwd": "norm_rope_bwd", "amax_dv": "amax_bf16_kernel",
+    "quantize_g": "quantize_act_kernel",
     "gemm_dx": "gemm_bf16out_kernel", "gemm_dw": "gemm_dw_part_kernel",
     "dw_reduce": "dw_reduce_kernel",
     "mlp_amax_w": "amax_w_kernel", "mlp_quantize_w": "quantize_w_kernel",
