@@ -1,6 +1,7 @@
 /*
  * fpr.h -- C interface of libfpr.so: the packed FP8 QKV projection with
- * reduced-width Q/K heads, forward and backward, on one MI355X (gfx950).
+ * reduced-width Q/K heads, forward and backward, on one MI355X (gfx950);
+ * and the FP8 ReLU^2 MLP of the same block (the mlp_* calls below).
  *
  * The method ("96 is enough: shrinking attention's routing vectors",
  * section "The change"): Q and K heads are d_qk = 96 wide while V stays
