@@ -39,6 +39,7 @@
 // with transposing LDS reads; it splits K over blocks and writes fp32
 // partial sums that a second kernel adds in split order.
 #include <algorithm>
+#include <type_traits>
 
 #include "common.hpp"
 #include "launch.hpp"
@@ -676,68 +677,81 @@ __device__ __forceinline__ void store_bf16_tile(const v16f (&acc)[C::FM][C::FN],
   // the 32 rows x 2 words of one read below fall in 64 distinct banks) into
   // the lanes that hold the matching accumulators.  Slice i + 1 is fetched
   // while slice i is worked on.
-  static_assert(C::WN == 64, "64 auxiliary bytes per row");
-  uint2 raw[4];
-  auto fetch_aux = [&](int i, uint2 (&dst)[4]) {
-    if constexpr (Epi::kAux) {
-      const uint8_t* ar = epi.aux_row(mp + i * 32 + rq, n0 + wn * C::WN + 8 * p);
+  // The store path is chosen once per part (fast is uniform over the
+  // wave), so each variant is straight-line code; with an auxiliary input
+  // the two copies would no longer fit the registers, and the choice is
+  // made per store instead.  fast_c is std::true_type, std::false_type or
+  // the runtime flag.
+  auto body = [&](auto fast_c) {
+    static_assert(C::WN == 64, "64 auxiliary bytes per row");
+    uint2 raw[4];
+    auto fetch_aux = [&](int i, uint2 (&dst)[4]) {
+      if constexpr (Epi::kAux) {
+        const uint8_t* ar = epi.aux_row(mp + i * 32 + rq, n0 + wn * C::WN + 8 * p);
 #pragma unroll
-      for (int q = 0; q < 4; ++q)  // rows rq + 8q lie in the same block of kActRows rows
-        dst[q] = *reinterpret_cast<const uint2*>(ar + q * 8 * kKBlock);
-    }
-  };
-  auto aux_word = [](int row, int w) { return row * 72 + 4 * w; };
-  if constexpr (Epi::kAux) fetch_aux(0, raw);
+        for (int q = 0; q < 4; ++q)  // rows rq + 8q lie in the same block of kActRows rows
+          dst[q] = *reinterpret_cast<const uint2*>(ar + q * 8 * kKBlock);
+      }
+    };
+    auto aux_word = [](int row, int w) { return row * 72 + 4 * w; };
+    if constexpr (Epi::kAux) fetch_aux(0, raw);
 #pragma unroll
-  for (int i = 0; i < C::FM; ++i) {
-    const int ml = mp + i * 32 + (lane & 31);  // this lane's accumulator row
-    uint32_t aux[C::FN][4];
-    if constexpr (Epi::kAux) {
-      // the wave's LDS operations complete in order: the reads below finish
-      // before the bf16 writes reuse the slice
+    for (int i = 0; i < C::FM; ++i) {
+      const int ml = mp + i * 32 + (lane & 31);  // this lane's accumulator row
+      uint32_t aux[C::FN][4];
+      if constexpr (Epi::kAux) {
+        // the wave's LDS operations complete in order: the reads below finish
+        // before the bf16 writes reuse the slice
 #pragma unroll
-      for (int q = 0; q < 4; ++q)
-        *reinterpret_cast<uint2*>(slice + aux_word(rq + 8 * q, 2 * p)) = raw[q];
-      if (i + 1 < C::FM) fetch_aux(i + 1, raw);
+        for (int q = 0; q < 4; ++q)
+          *reinterpret_cast<uint2*>(slice + aux_word(rq + 8 * q, 2 * p)) = raw[q];
+        if (i + 1 < C::FM) fetch_aux(i + 1, raw);
+#pragma unroll
+        for (int j = 0; j < C::FN; ++j)
+#pragma unroll
+          for (int g = 0; g < 4; ++g)
+            aux[j][g] = *reinterpret_cast<const uint32_t*>(
+                slice + aux_word(lane & 31, 8 * j + 2 * g + (lane >> 5)));
+      }
 #pragma unroll
       for (int j = 0; j < C::FN; ++j)
 #pragma unroll
-        for (int g = 0; g < 4; ++g)
-          aux[j][g] = *reinterpret_cast<const uint32_t*>(
-              slice + aux_word(lane & 31, 8 * j + 2 * g + (lane >> 5)));
-    }
-#pragma unroll
-    for (int j = 0; j < C::FN; ++j)
-#pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        const v16f& a = acc[i][j];
-        float v[4] = {a[4 * g] * alpha, a[4 * g + 1] * alpha, a[4 * g + 2] * alpha,
-                      a[4 * g + 3] * alpha};
-        if constexpr (Epi::kMap) epi.map(v, Epi::kAux ? aux[j][g] : 0u);
-        const uint32_t w0 = cvt_bf16x2_rn(v[0], v[1]), w1 = cvt_bf16x2_rn(v[2], v[3]);
-        if constexpr (Epi::kAmax) {
-          if (ml < M && nl + 32 * j + 8 * g < epi.N) {
-            const uint32_t a01 = absmax_bf16x2(w0), a23 = absmax_bf16x2(w1);
-            amax = max(amax, max(a01, a23));
+        for (int g = 0; g < 4; ++g) {
+          const v16f& a = acc[i][j];
+          float v[4] = {a[4 * g] * alpha, a[4 * g + 1] * alpha, a[4 * g + 2] * alpha,
+                        a[4 * g + 3] * alpha};
+          if constexpr (Epi::kMap) epi.map(v, Epi::kAux ? aux[j][g] : 0u);
+          const uint32_t w0 = cvt_bf16x2_rn(v[0], v[1]), w1 = cvt_bf16x2_rn(v[2], v[3]);
+          if constexpr (Epi::kAmax) {
+            if (ml < M && nl + 32 * j + 8 * g < epi.N) {
+              const uint32_t a01 = absmax_bf16x2(w0), a23 = absmax_bf16x2(w1);
+              amax = max(amax, max(a01, a23));
+            }
           }
+          *reinterpret_cast<uint2*>(slice + W::at(lane & 31, 4 * j + g) + 8 * (lane >> 5)) =
+              make_uint2(w0, w1);
         }
-        *reinterpret_cast<uint2*>(slice + W::at(lane & 31, 4 * j + g) + 8 * (lane >> 5)) =
-            make_uint2(w0, w1);
-      }
-    uint4 val[4];
+      uint4 val[4];
 #pragma unroll
-    for (int q = 0; q < 4; ++q) val[q] = *reinterpret_cast<const uint4*>(slice + W::at(rq + 8 * q, p));
+      for (int q = 0; q < 4; ++q) val[q] = *reinterpret_cast<const uint4*>(slice + W::at(rq + 8 * q, p));
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      if (fast) {
-        if (col.live) store_stream(ptr, val[q]);
-        ptr += step;
-      } else {
-        if (row.m < M) epi.chunk(row, col, val[q]);
-        epi.advance(row, 8);
+      for (int q = 0; q < 4; ++q) {
+        if (static_cast<bool>(fast_c)) {
+          if (col.live) store_stream(ptr, val[q]);
+          ptr += step;
+        } else {
+          if (row.m < M) epi.chunk(row, col, val[q]);
+          epi.advance(row, 8);
+        }
       }
     }
-  }
+  };
+  if constexpr (Epi::kAux)
+    body(fast);
+  else if (fast)
+    body(std::true_type{});
+  else
+    body(std::false_type{});
 }
 
 // fp32 split-K partials: lane l holds four consecutive n of one m.
