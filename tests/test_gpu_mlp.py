@@ -84,7 +84,10 @@ def _check_stages(w, r, fmt="e4m3"):
 
 
 @pytest.mark.parametrize("name,w", [("tiny", inputs.MLP_WORKLOADS["mlp_tiny"]),
-                                    ("tails", MLP_TAILS)])
+                                    ("tails", MLP_TAILS),
+                                    ("one_token", dict(n_seq=1, seq_len=1, d_model=128, d_ff=128)),
+                                    ("block_plus_one",
+                                     dict(n_seq=1, seq_len=257, d_model=64, d_ff=64))])
 def test_mlp_stagewise(name, w):
     _check_stages(w, run_mlp(w, seed=42))
 

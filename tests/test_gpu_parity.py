@@ -164,7 +164,11 @@ def _check_backward(w, r, fmt="e4m3"):
 
 
 @pytest.mark.parametrize("name,w", [("tiny", inputs.WORKLOADS["tiny"]), ("ragged", RAGGED),
-                                    ("d768", SMALL_16K_DIMS), ("tails", TAILS)])
+                                    ("d768", SMALL_16K_DIMS), ("tails", TAILS),
+                                    ("one_token", dict(n_seq=1, seq_len=1, d_model=128,
+                                                       n_heads=1, d_qk=96, d_v=128)),
+                                    ("one_token_per_seq", dict(n_seq=5, seq_len=1, d_model=64,
+                                                               n_heads=1, d_qk=96, d_v=128))])
 def test_forward_backward_stagewise(name, w):
     r = run(w, seed=42)
     assert r["status"] == 0
