@@ -471,6 +471,7 @@ def main():
         "pct_fp8_peak": round(100 * tflops * 1e12 / PEAK_FP8_FLOPS, 2),
         "wall_ms_per_step": round(t_wall * 1e3 / K, 4),
         "launch": "hip graph replay" if args.graph else "eager",
+        "device": torch.cuda.get_device_name(dev),
         "roofline": {"kernel": dominant, "bound": kind, "achieved": round(achieved, 1),
                      "peak": peak, "unit": unit, "frac": round(achieved / peak, 4),
                      "traffic": traffic, "launches": len(dom_ms),
