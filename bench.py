@@ -260,7 +260,7 @@ def main():
                     help="skip the step-time percentiles and the large-weight quantiser "
                          "measurement (profiling runs, whose dispatches must be whole steps)")
     ap.add_argument("--grad-format", choices=["e4m3", "e5m2"], default="e4m3",
-                    help="FP8 format of the QKV backward's packed gradient")
+                    help="FP8 format of the backward's gradient codes (QKV and MLP)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: this path runs on a single MI355X and has no "
@@ -327,7 +327,7 @@ def main():
             lambda seed, tokens: _oracle_step(w, seed, tokens, not args.forward_only))
     if wm is not None:
         Dm, F = wm["d_model"], wm["d_ff"]
-        mdims = B.MlpDims(Dm, F)
+        mdims = B.MlpDims(Dm, F, B.FORMAT_E5M2 if args.grad_format == "e5m2" else B.FORMAT_E4M3)
         mx = bf16(inputs.make_x(wm, args.seed))
         w1, w2 = (torch.from_numpy(a).to(dev) for a in inputs.make_mlp_w(wm, args.seed + 1))
         mdy = bf16(inputs.make_mlp_dy(wm, args.seed + 2))
@@ -354,6 +354,8 @@ def main():
         work.update(mlp_stage_work(wm, (ml.dw1_splits, ml.dw2_splits)))
         gemm_flop += 6 * 2 * T * Dm * F
         config.update(d_model=Dm, d_ff=F)
+        if args.grad_format != "e4m3":
+            config["grad_format"] = args.grad_format
         oracle_steps.append(lambda seed, tokens: _oracle_mlp_step(wm, seed, tokens))
     config["step"] = " + ".join(
         (["pack_quantize_weights + qkv_forward" + ("" if args.forward_only else " + qkv_backward")]
@@ -471,7 +473,9 @@ def main():
         "pct_fp8_peak": round(100 * tflops * 1e12 / PEAK_FP8_FLOPS, 2),
         "wall_ms_per_step": round(t_wall * 1e3 / K, 4),
         "launch": "hip graph replay" if args.graph else "eager",
-        "device": torch.cuda.get_device_name(dev),
+        "device": f"{torch.cuda.get_device_name(dev)} "
+                  f"({getattr(torch.cuda.get_device_properties(dev), 'gcnArchName', '?')}, "
+                  f"{torch.cuda.get_device_properties(dev).multi_processor_count} CUs)",
         "roofline": {"kernel": dominant, "bound": kind, "achieved": round(achieved, 1),
                      "peak": peak, "unit": unit, "frac": round(achieved / peak, 4),
                      "traffic": traffic, "launches": len(dom_ms),
