@@ -362,12 +362,12 @@ int qkv_backward(const fpr_dims* dims, int32_t n_seq, int32_t seq_len, const uin
   uint16_t* dqkv = at<uint16_t>(workspace, p.b_dqkv);
   uint8_t* g8 = at<uint8_t>(workspace, p.b_g8);
   float* dwpart = at<float>(workspace, p.b_dwpart);
+  stage("amax_dv", s, [&] {
+    fpr::launch_amax_bf16(dv, T * p.H * p.dv, parts + p.b_nr_parts, p.b_dv_parts, s);
+  });
   stage("norm_rope_bwd", s, [&] {
     fpr::launch_norm_rope_bwd(dq, dk, qk, T, seq_len, p.H, p.dqk, p.qs, dims->eps,
                               dims->rope_base, dqkv, parts, s);
-  });
-  stage("amax_dv", s, [&] {
-    fpr::launch_amax_bf16(dv, T * p.H * p.dv, parts + p.b_nr_parts, p.b_dv_parts, s);
   });
   const bool e5 = dims->grad_format == FPR_FORMAT_E5M2;
   stage("quantize_g", s, [&] {

@@ -22,7 +22,7 @@ import sys
 
 # Launch order of one step of each part (a stage may launch more than once)
 QKV_ORDER = ["amax_w", "quantize_w", "amax_x", "quantize_x", "gemm_fwd", "norm_rope_fwd",
-             "norm_rope_bwd", "amax_dv", "quantize_g", "gemm_dx", "gemm_dw", "dw_reduce"]
+             "amax_dv", "norm_rope_bwd", "quantize_g", "gemm_dx", "gemm_dw", "dw_reduce"]
 MLP_ORDER = ["mlp_amax_w", "mlp_quantize_w", "mlp_amax_w", "mlp_quantize_w", "mlp_amax_x",
              "mlp_quantize_x", "mlp_gemm_up", "mlp_quantize_h", "mlp_gemm_down", "mlp_amax_dy",
              "mlp_quantize_dy", "mlp_gemm_dh", "mlp_quantize_dpre", "mlp_gemm_dx",

@@ -224,7 +224,7 @@ FPR_API int fpr_get_layout(const fpr_dims* dims, int64_t tokens, fpr_layout* out
  * stored in names[i], for i = count, count+1, ... while count < capacity
  * (and count < FPR_TRACE_MAX).  events are caller-created hipEvent_t handles.
  * Stage names: amax_w, quantize_w, amax_x, quantize_x, gemm_fwd,
- * norm_rope_fwd, norm_rope_bwd, amax_dv, quantize_g, gemm_dx, gemm_dw,
+ * norm_rope_fwd, amax_dv, norm_rope_bwd, quantize_g, gemm_dx, gemm_dw,
  * dw_reduce;
  * for the MLP: mlp_amax_w, mlp_quantize_w, mlp_amax_x, mlp_quantize_x,
  * mlp_gemm_up, mlp_quantize_h, mlp_gemm_down, mlp_amax_dy, mlp_quantize_dy,
