@@ -8,6 +8,10 @@ under ``profiles/``.
         -> per-launch HBM bytes of every stage of the step, from two ``--pmc``
            runs (FETCH_SIZE, then WRITE_SIZE, in KiB per dispatch)
 
+    python -m fp8_packed_reduced_amd.rocprof_summary mfma COUNTER_CSV AGENT_CSV WORKLOAD CMD...
+        -> matrix-core use of every GEMM stage, from one ``--pmc`` run of
+           SQ_INSTS_VALU_MFMA_F8, SQ_VALU_MFMA_BUSY_CYCLES and GRBM_GUI_ACTIVE
+
 Byte counters are calibrated against the encoder launches bench.py makes
 before its first step (known traffic: 4 bytes read and 1 byte written per
 element): factor = known bytes / counter reading, per counter.  A stage's
@@ -78,23 +82,32 @@ def _dispatches(path: str, counter: str):
             for r in rows]
 
 
+def _by_stage(path: str, ds, order: list[str]):
+    """Stage -> [(dispatch id, value)] of the step launches (calibration and
+    torch's own launches left out), refusing anything but whole steps in the
+    library's launch order."""
+    step_kernels = [(d, n, v) for d, n, v in ds if "fpr::" in n and CALIB_KERNEL not in n]
+    if len(step_kernels) % len(order):
+        raise SystemExit(f"{path}: {len(step_kernels)} library dispatches is not a whole "
+                         f"number of {len(order)}-kernel steps")
+    per = {s: [] for s in order}
+    for i, (d, n, v) in enumerate(step_kernels):
+        stage = order[i % len(order)]
+        if KERNEL_OF_STAGE[stage] not in n:
+            raise SystemExit(f"{path}: dispatch {i} is {n}, expected {stage}")
+        per[stage].append((d, v))
+    return per
+
+
 def _per_stage(path: str, counter: str, known_bytes: float, order: list[str]):
     ds = _dispatches(path, counter)
     calib = [v for _, n, v in ds if CALIB_KERNEL in n]
     if not calib:
         raise SystemExit(f"{path}: no calibration launch ({CALIB_KERNEL}) found")
     factor = known_bytes / (statistics.median(calib) * 1024.0)
-    step_kernels = [(n, v) for _, n, v in ds if "fpr::" in n and CALIB_KERNEL not in n]
-    if len(step_kernels) % len(order):
-        raise SystemExit(f"{path}: {len(step_kernels)} library dispatches is not a whole "
-                         f"number of {len(order)}-kernel steps")
-    per = {s: [] for s in order}
-    for i, (n, v) in enumerate(step_kernels):
-        stage = order[i % len(order)]
-        if KERNEL_OF_STAGE[stage] not in n:
-            raise SystemExit(f"{path}: dispatch {i} is {n}, expected {stage}")
-        per[stage].append(v * 1024.0 * factor)
-    return {s: statistics.mean(v) for s, v in per.items()}, factor
+    per = _by_stage(path, ds, order)
+    return {s: statistics.mean(v * 1024.0 * factor for _, v in dv)
+            for s, dv in per.items()}, factor
 
 
 def traffic(fetch_csv: str, write_csv: str, workload: str, cmd: str) -> str:
@@ -113,11 +126,77 @@ def traffic(fetch_csv: str, write_csv: str, workload: str, cmd: str) -> str:
     return "\n".join(out) + "\n"
 
 
+# FLOP of one v_mfma_scale_f32_32x32x64_f8f6f4 (every GEMM here uses only it)
+MFMA_FLOP = 2 * 32 * 32 * 64
+
+
+def gemm_flop(workload: str) -> dict:
+    """Algorithmic 2*M*N*K of each GEMM stage of the workload."""
+    import bench
+    from fp8_packed_reduced_amd import inputs
+    qkv, mlp = bench.BENCH_WORKLOADS.get(workload, (workload, None))
+    work = {}
+    if qkv:
+        work.update(bench.stage_work(inputs.WORKLOADS[qkv], 1))
+    if mlp:
+        work.update(bench.mlp_stage_work(inputs.MLP_WORKLOADS[mlp], (1, 1)))
+    return {s: v for s, (kind, v) in work.items() if kind == "mfma"}
+
+
+def mfma_rows(counter_csv: str, xcc: int, simds: int, workload: str) -> tuple[dict, float]:
+    """Per GEMM stage: mean MFMA F8 instructions, busy cycles, active cycles
+    per XCD and duration of a launch; and the shader clock fitted over every
+    step launch (active cycles per XCD against duration, least squares: the
+    slope is the clock, the intercept the counter window's fixed overhead)."""
+    order = step_order(workload)
+    flop = gemm_flop(workload)
+    ns = {int(r["Dispatch_Id"]): int(r["End_Timestamp"]) - int(r["Start_Timestamp"])
+          for r in csv.DictReader(open(counter_csv))}
+    per = {c: _by_stage(counter_csv, _dispatches(counter_csv, c), order)
+           for c in ("SQ_INSTS_VALU_MFMA_F8", "SQ_VALU_MFMA_BUSY_CYCLES", "GRBM_GUI_ACTIVE")}
+    gui = [(ns[d], v / xcc) for dv in per["GRBM_GUI_ACTIVE"].values() for d, v in dv]
+    clock_ghz = statistics.linear_regression([t for t, _ in gui], [c for _, c in gui]).slope
+    rows = {}
+    for s in dict.fromkeys(order):
+        if s not in flop:
+            continue
+        inst = statistics.mean(v for _, v in per["SQ_INSTS_VALU_MFMA_F8"][s])
+        busy = statistics.mean(v for _, v in per["SQ_VALU_MFMA_BUSY_CYCLES"][s])
+        act = statistics.mean(v / xcc for _, v in per["GRBM_GUI_ACTIVE"][s])
+        t = statistics.mean(ns[d] for d, _ in per["GRBM_GUI_ACTIVE"][s])
+        rows[s] = dict(launches=len(per["GRBM_GUI_ACTIVE"][s]), inst=inst,
+                       flop_ratio=inst * MFMA_FLOP / flop[s], busy_per_inst=busy / inst,
+                       us=t / 1e3, util=busy / (act * simds),
+                       busy_frac=busy / (simds * clock_ghz * t))
+    return rows, clock_ghz
+
+
+def mfma(counter_csv: str, agent_csv: str, workload: str, cmd: str) -> str:
+    gpu = [r for r in csv.DictReader(open(agent_csv)) if r["Agent_Type"] == "GPU"][0]
+    xcc, simds = int(gpu["Num_Xcc"]), int(gpu["Simd_Count"])
+    rows, clock = mfma_rows(counter_csv, xcc, simds, workload)
+    out = [f"# Matrix-core use of the GEMMs, {workload}\n",
+           "Command (run from /tmp with TMPDIR=/tmp, repository at $R):\n",
+           "```\n" + cmd + "\n```\n",
+           f"{xcc} XCDs, {simds} SIMDs. Shader clock fitted over every step launch "
+           f"(active cycles per XCD against duration): {clock:.2f} GHz.\n",
+           "| stage | launches | MFMA F8 instr / launch | instr x 131072 / 2MNK | busy cycles / instr "
+           "| µs | MfmaUtil | busy at fitted clock |",
+           "|---|---:|---:|---:|---:|---:|---:|---:|"]
+    for s, r in rows.items():
+        out.append(f"| `{s}` | {r['launches']} | {r['inst']:.0f} | {r['flop_ratio']:.4f} | "
+                   f"{r['busy_per_inst']:.2f} | {r['us']:.1f} | {100 * r['util']:.1f}% | "
+                   f"{100 * r['busy_frac']:.1f}% |")
+    return "\n".join(out) + "\n"
+
+
 if __name__ == "__main__":
     mode = sys.argv[1]
     if mode == "stats":
         sys.stdout.write(stats(sys.argv[2], sys.argv[3], sys.argv[4]))
     elif mode == "traffic":
         sys.stdout.write(traffic(sys.argv[2], sys.argv[3], sys.argv[4], " ".join(sys.argv[5:])))
+    elif mode == "mfma":
+        sys.stdout.write(mfma(sys.argv[2], sys.argv[3], sys.argv[4], " ".join(sys.argv[5:])))
     else:
         raise SystemExit(__doc__)

@@ -61,3 +61,39 @@ def test_step_orders_match_the_library_stage_names():
     for stage in set(rs.QKV_ORDER + rs.MLP_ORDER):
         assert stage in names, stage
         assert stage in bench.STAGE_SOURCES, stage
+
+
+def test_mfma_rows_count_flop_and_fit_the_clock(tmp_path):
+    """Three counters per dispatch with timestamps; the GEMM stages carry
+    exactly 2MNK / 131072 instructions and the active cycles follow a 2.0 GHz
+    clock plus a fixed window, which the fit must recover."""
+    order = rs.step_order("step_64k")
+    flop = rs.gemm_flop("step_64k")
+    xcc, simds = 8, 1024
+    f = tmp_path / "c.csv"
+    with open(f, "w", newline="") as fh:
+        w = csv.DictWriter(fh, fieldnames=["Dispatch_Id", "Kernel_Name", "Counter_Name",
+                                           "Counter_Value", "Start_Timestamp", "End_Timestamp"])
+        w.writeheader()
+        d, t0 = 0, 10**9
+        for step in range(2):
+            for k, stage in enumerate(order):
+                ns = 1000 * (k + 3) + 7 * step
+                inst = flop[stage] // rs.MFMA_FLOP if stage in flop else 0
+                vals = {"SQ_INSTS_VALU_MFMA_F8": inst, "SQ_VALU_MFMA_BUSY_CYCLES": 64 * inst,
+                        "GRBM_GUI_ACTIVE": xcc * (20000 + 2.0 * ns)}
+                for c, v in vals.items():
+                    w.writerow({"Dispatch_Id": d, "Kernel_Name": _kernel_name(stage),
+                                "Counter_Name": c, "Counter_Value": v,
+                                "Start_Timestamp": t0, "End_Timestamp": t0 + ns})
+                d, t0 = d + 1, t0 + ns + 500
+    rows, clock = rs.mfma_rows(str(f), xcc, simds, "step_64k")
+    assert clock == pytest.approx(2.0)
+    assert set(rows) == {"gemm_fwd", "gemm_dx", "gemm_dw"}
+    for s, r in rows.items():
+        assert r["flop_ratio"] == pytest.approx(1.0) and r["busy_per_inst"] == 64
+        assert r["launches"] == 2
+        k = order.index(s)
+        t = 1000 * (k + 3) + 3.5
+        assert r["busy_frac"] == pytest.approx(64 * r["inst"] / (simds * 2.0 * t))
+        assert r["util"] == pytest.approx(64 * r["inst"] / ((20000 + 2.0 * t) * simds))
