@@ -1,8 +1,11 @@
 """Turn rocprofv3 output of ``bench.py`` into the short text summaries kept
 under ``profiles/``.
 
-    python -m fp8_packed_reduced_amd.rocprof_summary stats KERNEL_STATS_CSV TITLE CMD
-        -> markdown table of per-kernel durations (``--kernel-trace --stats``)
+    python -m fp8_packed_reduced_amd.rocprof_summary stats KERNEL_STATS_CSV TITLE CMD [BENCH_OUT]
+        -> markdown table of per-kernel durations (``--kernel-trace --stats``);
+           with BENCH_OUT (what the profiled bench.py printed), also the
+           roofline kernel's HIP-event average that bench.py measured live in
+           the same run
 
     python -m fp8_packed_reduced_amd.rocprof_summary traffic FETCH_CSV WRITE_CSV WORKLOAD CMD...
         -> per-launch HBM bytes of every stage of the step, from two ``--pmc``
@@ -61,7 +64,16 @@ def short(name: str) -> str:
     return name.split("(")[0].replace("void ", "")
 
 
-def stats(path: str, title: str, cmd: str) -> str:
+def _bench_line(path: str) -> dict:
+    """The JSON line bench.py printed (its last line starting with '{')."""
+    import json
+    lines = [ln for ln in open(path) if ln.startswith("{")]
+    if not lines:
+        raise SystemExit(f"{path}: no bench.py JSON line")
+    return json.loads(lines[-1])
+
+
+def stats(path: str, title: str, cmd: str, bench_out: str | None = None) -> str:
     rows = list(csv.DictReader(open(path)))
     out = [f"# {title}\n", "Command (run from /tmp with TMPDIR=/tmp, repository at $R):\n",
            "```\n" + cmd + "\n```\n",
@@ -71,6 +83,13 @@ def stats(path: str, title: str, cmd: str) -> str:
         out.append(f"| `{short(r['Name'])}` | {r['Calls']} | {float(r['AverageNs']) / 1e3:.2f} | "
                    f"{float(r['MinNs']) / 1e3:.2f} | {float(r['MaxNs']) / 1e3:.2f} | "
                    f"{float(r['Percentage']):.2f} |")
+    if bench_out:
+        b = _bench_line(bench_out)
+        rf = b["roofline"]
+        out.append(f"\nbench.py in the same run: {b['ms_per_step']} ms per step; roofline kernel "
+                   f"`{rf['kernel']}` {rf['avg_us']} µs average over {rf['launches']} launches "
+                   f"(HIP events on its stream), {rf['achieved']} {rf['unit']} = "
+                   f"{rf['frac']} of {rf['peak']}.")
     return "\n".join(out) + "\n"
 
 
@@ -193,7 +212,8 @@ def mfma(counter_csv: str, agent_csv: str, workload: str, cmd: str) -> str:
 if __name__ == "__main__":
     mode = sys.argv[1]
     if mode == "stats":
-        sys.stdout.write(stats(sys.argv[2], sys.argv[3], sys.argv[4]))
+        sys.stdout.write(stats(sys.argv[2], sys.argv[3], sys.argv[4],
+                               sys.argv[5] if len(sys.argv) > 5 else None))
     elif mode == "traffic":
         sys.stdout.write(traffic(sys.argv[2], sys.argv[3], sys.argv[4], " ".join(sys.argv[5:])))
     elif mode == "mfma":

@@ -97,3 +97,23 @@ def test_mfma_rows_count_flop_and_fit_the_clock(tmp_path):
         t = 1000 * (k + 3) + 3.5
         assert r["busy_frac"] == pytest.approx(64 * r["inst"] / (simds * 2.0 * t))
         assert r["util"] == pytest.approx(64 * r["inst"] / ((20000 + 2.0 * t) * simds))
+
+
+def test_stats_carries_the_live_average_of_the_same_run(tmp_path):
+    f = tmp_path / "stats.csv"
+    with open(f, "w", newline="") as fh:
+        w = csv.DictWriter(fh, fieldnames=["Name", "Calls", "AverageNs", "MinNs", "MaxNs",
+                                           "Percentage"])
+        w.writeheader()
+        w.writerow({"Name": "void fpr::gemm_bf16out_kernel<x>(args)", "Calls": 3,
+                    "AverageNs": 97000, "MinNs": 96000, "MaxNs": 99000, "Percentage": 17.0})
+    log = tmp_path / "bench.log"
+    log.write_text('rocprofv3 noise\n{"ms_per_step": 0.59, "roofline": {"kernel": "gemm_fwd", '
+                   '"avg_us": 96.9, "launches": 30, "achieved": 1995.0, "unit": "TFLOP/s", '
+                   '"frac": 0.399, "peak": 5000.0}}\nmore noise\n')
+    out = rs.stats(str(f), "t", "cmd", str(log))
+    assert "| `fpr::gemm_bf16out_kernel<x>` | 3 | 97.00 |" in out
+    assert "`gemm_fwd` 96.9 µs average over 30 launches" in out and "0.399 of 5000.0" in out
+    log.write_text("no json here\n")
+    with pytest.raises(SystemExit, match="no bench.py JSON"):
+        rs.stats(str(f), "t", "cmd", str(log))
