@@ -73,9 +73,10 @@ def stage_work(w: dict, dw_splits: int) -> dict:
         "quantize_w": ("hbm", 4 * D * N + 2 * D * N),            # fp32 in, two e4m3 layouts out
         "amax_x": ("hbm", 2 * T * D),
         "quantize_x": ("hbm", 2 * T * D + T * D),                # bf16 in, e4m3 out
-        "gemm_fwd": ("mfma", gemm),
-        "norm_rope_fwd": ("hbm", 2 * T * qk + 2 * T * qk),       # pre-norm Q|K in, q|k out
-        "norm_rope_bwd": ("hbm", 2 * T * qk * 2 + 2 * T * qk),  # dq, dk, pre-norm in; dQK out
+        "gemm_fwd": ("mfma", gemm),   # with the norm/RoPE in its epilogue at d_qk 64/96/128
+        "norm_rope_fwd": ("hbm", 2 * T * qk + 2 * T * qk),       # other widths: pre-norm in, q|k out
+        # dq, dk, q, k and the 1/rms of each Q/K head row in; dQK out
+        "norm_rope_bwd": ("hbm", 2 * T * qk * 2 + 2 * T * qk + 4 * T * 2 * H),
         "amax_dv": ("hbm", 2 * T * vv),
         "quantize_g": ("hbm", 2 * T * N + T * N),
         "gemm_dx": ("mfma", gemm),
@@ -314,7 +315,7 @@ def main():
             B.pack_quantize_weights(dims, wq, wk, wv, cache, workspace=ws_p)
             B.qkv_forward(dims, n_seq, S, x, cache, q, k, v, saved, ws_f)
             if not args.forward_only:
-                B.qkv_backward(dims, n_seq, S, dq, dk, dv, saved, cache, dx, dw, ws_b)
+                B.qkv_backward(dims, n_seq, S, q, k, dq, dk, dv, saved, cache, dx, dw, ws_b)
 
         steps.append(qkv_step)
         work.update(stage_work(w, B.layout(dims, T).dw_splits))

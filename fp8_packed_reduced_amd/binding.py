@@ -19,6 +19,7 @@ HEADER = os.path.join(os.path.dirname(HERE), "include", "fpr.h")
 FPR_CALL_PACK, FPR_CALL_FORWARD, FPR_CALL_BACKWARD = 0, 1, 2
 STATUS_W_NONFINITE, STATUS_X_NONFINITE, STATUS_G_NONFINITE, STATUS_H_NONFINITE = 1, 2, 4, 8
 FORMAT_E4M3, FORMAT_E5M2 = 0, 1
+NOT_PRESENT = ctypes.c_size_t(-1).value  # a layout offset of "(size_t)-1"
 
 
 class FprError(RuntimeError):
@@ -63,12 +64,18 @@ class _TraceC(ctypes.Structure):
 
 class Layout(ctypes.Structure):
     _fields_ = [("tokens", ctypes.c_int64), ("tokens_padded", ctypes.c_int64),
-                ("saved_x8", ctypes.c_size_t), ("saved_qk_pre", ctypes.c_size_t),
-                ("saved_x_scales", ctypes.c_size_t),
+                ("saved_x8", ctypes.c_size_t), ("saved_rho", ctypes.c_size_t),
+                ("saved_x_scales", ctypes.c_size_t), ("fwd_qk_pre", ctypes.c_size_t),
                 ("bwd_dqkv", ctypes.c_size_t), ("bwd_g_scales", ctypes.c_size_t),
                 ("bwd_g8", ctypes.c_size_t),
                 ("bwd_dw_part", ctypes.c_size_t), ("dw_splits", ctypes.c_int32),
+                ("bwd_amax_partials", ctypes.c_int32),
                 ("k_block", ctypes.c_int32), ("act_block_rows", ctypes.c_int32)]
+
+    @property
+    def fused_forward(self) -> bool:
+        """Norm and RoPE run in the forward GEMM's epilogue (no pre-norm rows)."""
+        return self.fwd_qk_pre == NOT_PRESENT
 
 
 class MlpDims(ctypes.Structure):
@@ -121,8 +128,8 @@ def load():
     L.qkv_forward.argtypes = [P(Dims), _I32, _I32, _V, P(_CacheC), _V, _V, _V, _V, _SZ, _V,
                               _SZ, _V]
     L.qkv_backward.restype = ctypes.c_int
-    L.qkv_backward.argtypes = [P(Dims), _I32, _I32, _V, _V, _V, _V, _SZ, P(_CacheC), _V,
-                               _V, _I64, _V, _I64, _V, _I64, _V, _SZ, _V]
+    L.qkv_backward.argtypes = [P(Dims), _I32, _I32, _V, _V, _V, _V, _V, _V, _SZ, P(_CacheC),
+                               _V, _V, _I64, _V, _I64, _V, _I64, _V, _SZ, _V]
     L.fpr_trace_set.restype = None
     L.fpr_trace_set.argtypes = [ctypes.POINTER(_TraceC)]
     L.fpr_e4m3_encode.restype = ctypes.c_int
@@ -270,13 +277,16 @@ def qkv_forward(dims: Dims, n_seq: int, seq_len: int, x, cache: WeightCache, q=N
     return q, k, v, saved
 
 
-def qkv_backward(dims: Dims, n_seq: int, seq_len: int, dq, dk, dv, saved, cache: WeightCache,
-                 dx=None, dw=None, workspace=None):
-    """Returns (dx, dw) with dw the [D][N] packed fp32 gradient whose column
-    blocks [:nq], [nq:2nq], [2nq:] are dW_q, dW_k, dW_v."""
+def qkv_backward(dims: Dims, n_seq: int, seq_len: int, q, k, dq, dk, dv, saved,
+                 cache: WeightCache, dx=None, dw=None, workspace=None):
+    """q, k: the matching forward's outputs.  Returns (dx, dw) with dw the
+    [D][N] packed fp32 gradient whose column blocks [:nq], [nq:2nq], [2nq:]
+    are dW_q, dW_k, dW_v."""
     T = n_seq * seq_len
     H, dqk, dvw, D, N, nq = dims.n_heads, dims.qk_row, dims.d_v, dims.d_model, dims.n_packed, dims.n_q
     dev = dq.device
+    _need(q, torch.bfloat16, (n_seq, H, seq_len, dqk), "q")
+    _need(k, torch.bfloat16, (n_seq, H, seq_len, dqk), "k")
     _need(dq, torch.bfloat16, (n_seq, H, seq_len, dqk), "dq")
     _need(dk, torch.bfloat16, (n_seq, H, seq_len, dqk), "dk")
     _need(dv, torch.bfloat16, (n_seq, H, seq_len, dvw), "dv")
@@ -291,8 +301,9 @@ def qkv_backward(dims: Dims, n_seq: int, seq_len: int, dq, dk, dv, saved, cache:
                                 device=dev)
     dwq, dwk, dwv = dw[:, :nq], dw[:, nq:2 * nq], dw[:, 2 * nq:]
     cc = cache.c()
-    rc = load().qkv_backward(ctypes.byref(dims), n_seq, seq_len, dq.data_ptr(), dk.data_ptr(),
-                             dv.data_ptr(), saved.data_ptr(), saved.numel(), ctypes.byref(cc),
+    rc = load().qkv_backward(ctypes.byref(dims), n_seq, seq_len, q.data_ptr(), k.data_ptr(),
+                             dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), saved.data_ptr(),
+                             saved.numel(), ctypes.byref(cc),
                              dx.data_ptr(), dwq.data_ptr(), N, dwk.data_ptr(), N, dwv.data_ptr(),
                              N, workspace.data_ptr(), workspace.numel(), _stream(dev))
     if rc:

@@ -24,8 +24,9 @@ constexpr size_t kMaxDynLds = 64 * 1024;  // dynamic LDS of one epilogue block
 struct Plan {
   int D, H, dqk, dv, qs, nq, nqk2, N;
   int64_t T, Tp;
-  size_t s_x8, s_qk, s_xsc, saved_total;
-  size_t f_part, fwd_total;
+  bool fused;  // norm/RoPE in the forward GEMM's epilogue (else qk_pre in the workspace)
+  size_t s_x8, s_rho, s_xsc, saved_total;
+  size_t f_part, f_qk, fwd_total;
   int f_parts;
   size_t b_part, b_gsc, b_dqkv, b_g8, b_dwpart, bwd_total;
   int b_parts, b_nr_parts, b_dv_parts;  // all amax partials = norm/RoPE's, then dv's
@@ -74,21 +75,23 @@ Plan make_plan(const fpr_dims* d, int64_t T) {
   p.N = p.nqk2 + p.H * p.dv;
   p.T = T;
   p.Tp = round_up(T > 0 ? T : 1, 128);
+  p.fused = fpr::fused_forward_width(p.dqk);
   size_t c = 0;
   p.s_x8 = take(c, fpr::act_blocked_bytes(T, p.D));
-  p.s_qk = take(c, (size_t)T * p.nqk2 * 2);
+  p.s_rho = take(c, (size_t)T * 2 * p.H * sizeof(float));
   p.s_xsc = take(c, 4 * sizeof(float));
   p.saved_total = c;
   c = 0;
   // one amax block per 256 x 16-byte vectors of x, at most kPartsAct
   p.f_parts = (int)std::max<int64_t>(1, std::min<int64_t>(kPartsAct, ceil_div(T * p.D / 8, fpr::kThreads)));
   p.f_part = take(c, (size_t)p.f_parts * 4);
+  p.f_qk = p.fused ? (size_t)-1 : take(c, (size_t)T * p.nqk2 * 2);
   p.fwd_total = c;
   c = 0;
   p.b_nr_parts = fpr::norm_rope_bwd_blocks(T > 0 ? T : 1, p.H, p.dqk);
   p.b_dv_parts = (int)std::max<int64_t>(
       1, std::min<int64_t>(kPartsAct, ceil_div(T * p.H * p.dv / 8, fpr::kThreads)));
-  p.b_parts = p.b_nr_parts + p.b_dv_parts;
+  p.b_parts = p.b_nr_parts + p.b_dv_parts;  // <= kMaxPartials, checked by plan_ok()
   p.b_part = take(c, (size_t)p.b_parts * 4);
   p.b_gsc = take(c, 4 * sizeof(float));
   p.b_dqkv = take(c, (size_t)T * p.nqk2 * 2);
@@ -100,6 +103,10 @@ Plan make_plan(const fpr_dims* d, int64_t T) {
   p.pack_total = c;
   return p;
 }
+
+// Every quantiser block re-reduces all amax partials of its tensor, so their
+// number must stay bounded at any token count.
+bool plan_ok(const Plan& p) { return p.b_parts <= fpr::kMaxPartials && p.f_parts <= fpr::kMaxPartials; }
 
 // ---- FP8 ReLU^2 MLP: shapes and memory plan
 
@@ -242,6 +249,7 @@ size_t fpr_workspace_bytes(const fpr_dims* dims, int64_t tokens, int which) {
   if (which == FPR_CALL_PACK) return make_plan(dims, 1).pack_total;
   if (tokens <= 0 || tokens > kMaxTokens) return 0;
   const Plan p = make_plan(dims, tokens);
+  if (!plan_ok(p)) return 0;
   if (which == FPR_CALL_FORWARD) return p.fwd_total;
   if (which == FPR_CALL_BACKWARD) return p.bwd_total;
   return 0;
@@ -261,13 +269,15 @@ int fpr_get_layout(const fpr_dims* dims, int64_t tokens, fpr_layout* out) {
   out->tokens = p.T;
   out->tokens_padded = p.Tp;
   out->saved_x8 = p.s_x8;
-  out->saved_qk_pre = p.s_qk;
+  out->saved_rho = p.s_rho;
   out->saved_x_scales = p.s_xsc;
+  out->fwd_qk_pre = p.f_qk;
   out->bwd_dqkv = p.b_dqkv;
   out->bwd_g_scales = p.b_gsc;
   out->bwd_g8 = p.b_g8;
   out->bwd_dw_part = p.b_dwpart;
   out->dw_splits = fpr::dw_splits(p.D, p.N, p.Tp);
+  out->bwd_amax_partials = p.b_parts;
   out->k_block = fpr::kKBlock;
   out->act_block_rows = fpr::kActRows;
   return FPR_OK;
@@ -312,31 +322,41 @@ int qkv_forward(const fpr_dims* dims, int32_t n_seq, int32_t seq_len, const uint
   if (!al16(x) || !al16(q) || !al16(k) || !al16(v) || !al16(saved) || !al16(workspace))
     return FPR_ERR_ALIGN;
   const Plan p = make_plan(dims, T);
+  if (!plan_ok(p)) return FPR_ERR_SHAPE;
   if (saved_bytes < p.saved_total || workspace_bytes < p.fwd_total) return FPR_ERR_WORKSPACE;
   hipStream_t s = static_cast<hipStream_t>(stream);
   (void)hipGetLastError();
   uint32_t* parts = at<uint32_t>(workspace, p.f_part);
   float* xsc = at<float>(saved, p.s_xsc);
   uint8_t* x8 = at<uint8_t>(saved, p.s_x8);
-  uint16_t* qk = at<uint16_t>(saved, p.s_qk);
+  float* rho = at<float>(saved, p.s_rho);
   stage("amax_x", s, [&] { fpr::launch_amax_bf16(x, T * p.D, parts, p.f_parts, s); });
   stage("quantize_x", s, [&] {
     fpr::launch_quantize_act(x, T, p.D, parts, p.f_parts, xsc, cache->status,
                              FPR_STATUS_X_NONFINITE, x8, p.Tp, s);
   });
-  stage("gemm_fwd", s, [&] {
-    fpr::launch_gemm_fwd(x8, cache->w_packed_t, (int)T, p.N, p.D, xsc, cache->scales, qk,
-                         p.nqk2, v, p.H, p.dv, seq_len, s);
-  });
-  stage("norm_rope_fwd", s, [&] {
-    fpr::launch_norm_rope_fwd(qk, T, seq_len, p.H, p.dqk, p.qs, dims->eps, dims->rope_base, q, k,
-                              s);
-  });
+  if (p.fused) {
+    stage("gemm_fwd", s, [&] {
+      fpr::launch_gemm_qkv_fwd(x8, cache->w_packed_t, n_seq, seq_len, p.D, p.H, p.dqk, p.dv, p.qs,
+                               dims->eps, dims->rope_base, xsc, cache->scales, q, k, v, rho, s);
+    });
+  } else {
+    uint16_t* qk = at<uint16_t>(workspace, p.f_qk);
+    stage("gemm_fwd", s, [&] {
+      fpr::launch_gemm_fwd(x8, cache->w_packed_t, (int)T, p.N, p.D, xsc, cache->scales, qk,
+                           p.nqk2, v, p.H, p.dv, seq_len, s);
+    });
+    stage("norm_rope_fwd", s, [&] {
+      fpr::launch_norm_rope_fwd(qk, T, seq_len, p.H, p.dqk, p.qs, dims->eps, dims->rope_base, q,
+                                k, rho, s);
+    });
+  }
   return finish();
 }
 
-int qkv_backward(const fpr_dims* dims, int32_t n_seq, int32_t seq_len, const uint16_t* dq,
-                 const uint16_t* dk, const uint16_t* dv, const void* saved, size_t saved_bytes,
+int qkv_backward(const fpr_dims* dims, int32_t n_seq, int32_t seq_len, const uint16_t* q,
+                 const uint16_t* k, const uint16_t* dq, const uint16_t* dk, const uint16_t* dv,
+                 const void* saved, size_t saved_bytes,
                  const fpr_weight_cache* cache, uint16_t* dx, float* dwq, int64_t ldq,
                  float* dwk, int64_t ldk, float* dwv, int64_t ldv, void* workspace,
                  size_t workspace_bytes, void* stream) {
@@ -345,18 +365,20 @@ int qkv_backward(const fpr_dims* dims, int32_t n_seq, int32_t seq_len, const uin
   int64_t T;
   if ((rc = tokens_check(n_seq, seq_len, &T)) || (rc = cache_check(cache))) return rc;
   const Plan p = make_plan(dims, T);
+  if (!plan_ok(p)) return FPR_ERR_SHAPE;
   if ((rc = ld_check(ldq, p.nq, dwq)) || (rc = ld_check(ldk, p.nq, dwk)) ||
       (rc = ld_check(ldv, (int64_t)p.H * p.dv, dwv)))
     return rc;
-  if (!dq || !dk || !dv || !saved || !dx || !workspace) return FPR_ERR_ARG;
-  if (!al16(dq) || !al16(dk) || !al16(dv) || !al16(saved) || !al16(dx) || !al16(workspace))
+  if (!q || !k || !dq || !dk || !dv || !saved || !dx || !workspace) return FPR_ERR_ARG;
+  if (!al16(q) || !al16(k) || !al16(dq) || !al16(dk) || !al16(dv) || !al16(saved) || !al16(dx) ||
+      !al16(workspace))
     return FPR_ERR_ALIGN;
   if (saved_bytes < p.saved_total || workspace_bytes < p.bwd_total) return FPR_ERR_WORKSPACE;
   hipStream_t s = static_cast<hipStream_t>(stream);
   (void)hipGetLastError();
   const float* xsc = at<float>(saved, p.s_xsc);
   const uint8_t* x8 = at<uint8_t>(saved, p.s_x8);
-  const uint16_t* qk = at<uint16_t>(saved, p.s_qk);
+  const float* rho = at<float>(saved, p.s_rho);
   uint32_t* parts = at<uint32_t>(workspace, p.b_part);
   float* gsc = at<float>(workspace, p.b_gsc);
   uint16_t* dqkv = at<uint16_t>(workspace, p.b_dqkv);
@@ -366,8 +388,8 @@ int qkv_backward(const fpr_dims* dims, int32_t n_seq, int32_t seq_len, const uin
     fpr::launch_amax_bf16(dv, T * p.H * p.dv, parts + p.b_nr_parts, p.b_dv_parts, s);
   });
   stage("norm_rope_bwd", s, [&] {
-    fpr::launch_norm_rope_bwd(dq, dk, qk, T, seq_len, p.H, p.dqk, p.qs, dims->eps,
-                              dims->rope_base, dqkv, parts, s);
+    fpr::launch_norm_rope_bwd(dq, dk, q, k, rho, T, seq_len, p.H, p.dqk, p.qs, dims->rope_base,
+                              dqkv, parts, s);
   });
   const bool e5 = dims->grad_format == FPR_FORMAT_E5M2;
   stage("quantize_g", s, [&] {

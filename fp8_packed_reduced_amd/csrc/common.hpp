@@ -73,6 +73,27 @@ __device__ inline uint32_t fp8x4(float a, float b, float c, float d) {
     return e4m3x4(a, b, c, d);
 }
 
+// ------------------------------------------------------------------ RoPE
+//
+// "96 is enough", "The change": rope(q), rope(k).  Pair (i, i + d/2) of a
+// head row at position p turns by p * base^(-2i/d).  The angle is formed in
+// revolutions, p * theta_i / (2 pi) in double (positions reach 2^24 and the
+// angle 2^24 rad), reduced to its fractional part, and the hardware sin/cos
+// (v_sin_f32 / v_cos_f32 take revolutions) of that fraction in fp32.
+
+// theta_i / (2 pi) = base^(-2i/d) / (2 pi)
+__device__ inline double rope_rev(int i, int d, float base) {
+  return exp2(-(2.0 * i / d) * log2((double)base)) * 0.15915494309189533576888376337251;
+}
+
+__device__ inline void rope_cs(double rev_i, int64_t pos, float& c, float& s) {
+  double r = (double)pos * rev_i;
+  r -= rint(r);
+  const float f = (float)r;
+  s = __builtin_amdgcn_sinf(f);  // sin(2 pi f)
+  c = __builtin_amdgcn_cosf(f);
+}
+
 // ------------------------------------------------------------ reductions
 
 __device__ inline uint32_t wave_max_u32(uint32_t v) {

@@ -190,7 +190,7 @@ __device__ __forceinline__ v16f mfma32(v8i b, v8i a, v16f c) {
 // from memory once and are shared in that XCD's L2.
 // An operand is either row-major with leading dimension ld, or blocked
 // (blk > 0): blocks of blk rows x 128 bytes of K, as the activation
-// quantiser writes them (blk equals the tile's rows for that operand).
+// quantiser writes them (the tile's rows for that operand divide blk).
 // With tok, both operands are token-major instead (dW: K = tokens): the
 // row layouts of x8 and g8, blocks of kActRows tokens x kKBlock features,
 // lda / ldb = feature blocks per block row.
@@ -275,10 +275,12 @@ __device__ __forceinline__ void dma_plan(CopyState<C>& st, const Gemm& gm, int t
     else
       st.off[t] = (uint32_t)((min(n0 + row - C::BM_, gm.N - 1) - n0) * rb) + chunk;
   }
+  // a blocked operand's tile rows lie inside one block of blk rows (the
+  // tile's rows divide blk): block m0 / blk, from its row m0 % blk on
   const int64_t kblocks = (gm.K + kBK - 1) / kBK;
-  st.Atile = gm.a_blk ? gm.A + (int64_t)(m0 / C::BM_) * kblocks * C::BM_ * kBK
+  st.Atile = gm.a_blk ? gm.A + ((int64_t)(m0 / gm.a_blk) * kblocks * gm.a_blk + m0 % gm.a_blk) * kBK
                       : gm.A + (int64_t)m0 * gm.lda;
-  st.Btile = gm.b_blk ? gm.B + (int64_t)(n0 / C::BN_) * kblocks * C::BN_ * kBK
+  st.Btile = gm.b_blk ? gm.B + ((int64_t)(n0 / gm.b_blk) * kblocks * gm.b_blk + n0 % gm.b_blk) * kBK
                       : gm.B + (int64_t)n0 * gm.ldb;
   st.tile = tile;
 }
@@ -300,8 +302,8 @@ __device__ __forceinline__ void issue_next(CopyState<C>& st, uint8_t* lds, const
     Ak = st.Atile + (int64_t)(ks >> 1) * gm.lda * kActRows * kBK + half;
     Bk = st.Btile + (int64_t)(ks >> 1) * gm.ldb * kActRows * kBK + half;
   } else {
-    Ak = st.Atile + (gm.a_blk ? (int64_t)ks * C::BM_ * kBK : k0);
-    Bk = st.Btile + (gm.b_blk ? (int64_t)ks * C::BN_ * kBK : k0);
+    Ak = st.Atile + (gm.a_blk ? (int64_t)ks * gm.a_blk * kBK : k0);
+    Bk = st.Btile + (gm.b_blk ? (int64_t)ks * gm.b_blk * kBK : k0);
   }
   uint8_t* stage = lds + (g % kStages) * C::STAGE_BYTES;
 #pragma unroll
@@ -793,6 +795,229 @@ __device__ __forceinline__ void persistent_tiles(Sched& sc, int b, int G, int nt
   sc.steps = mine * sc.nk;
 }
 
+// --------------------------------- forward with RMSNorm and RoPE fused in
+//
+// "96 is enough", "The change": after the one packed matmul, q and k are
+// RMS-normalised and rotated; PR #344 page, "Changes": norm, RoPE and the
+// layout conversion are fused.  Here they run in the matmul's own epilogue,
+// so no pre-norm row ever reaches memory.  The tile is 128 rows x 2 d
+// columns (d = d_qk), so each matrix wave (64 rows x d) holds whole rows of
+// one packed head: the Q|K / V boundary 2 H d is a multiple of d.  For row
+// l % 32 (+ 32 i) a lane holds the head's columns 8 idx + 4 (l / 32) + e
+// (idx < d / 8, e < 4): the row's sum of squares is the lane's own values
+// plus one exchange with lane l ^ 32, and the rotation partner of column
+// c < d / 2, c + d / 2, sits in the same lane (group idx + d / 16, same e).
+// The product is rounded to bf16 first, exactly where an unfused path would
+// store it, then normalised (fp32) and rotated; 1 / rms of every Q and K
+// head row goes out with q, k and v, and the backward rebuilds the
+// normalised rows from q and k with it.
+
+struct QkvOut {
+  uint16_t* q;   // [n_seq][H][S][qs]
+  uint16_t* k;
+  uint16_t* v;   // [n_seq][H][S][dv]
+  float* rho;    // [2][n_seq][H][S]: 1 / rms of each q row, then of each k row
+  int H, S, dv, qs, N, nqk2, n_seq;
+  float eps;
+};
+
+// 64 bf16 columns x 32 rows of a wave's LDS slice: row pitch 128 bytes,
+// 16-byte chunks XOR-swizzled by row.
+__device__ __forceinline__ int slice64(int row, int chunk) {
+  return row * 128 + ((chunk ^ (row & 7)) << 4);
+}
+
+// The rotation frequencies of a lane's columns c = 8 idx + 4 (l / 32) + e,
+// in revolutions per position: theta_c / (2 pi) = rev0 * r^(c - c0) with
+// r = base^(-2/d), stepped by one multiplication per column (fp64, so the
+// angles stay exact to ~1e-14 revolutions per position).
+struct RopeRev {
+  double rev0;  // theta_c0 / (2 pi) of the lane's first column c0 = 4 (l / 32)
+  double r1, r5;  // r and r^5: one column on, and from e = 3 to the next group
+};
+
+// A pass of the epilogue puts 64 of the head's columns through the wave's
+// slice: the 8-column groups 4 ps + s of the lower half (slot s < 4) and
+// their rotation partners, the groups 4 ps + s + d/16 (slot s + 4).  Each
+// rotated pair is written as soon as it is formed; the readback stores
+// every 16-byte chunk at the column its slot stands for.
+template <int D>
+struct QkvPass {
+  static constexpr int G = D / 8, HG = G / 2, PASSES = (HG + 3) / 4;
+  // 8-column group held in slot sl of pass ps (or -1)
+  __device__ static constexpr int group(int ps, int sl) {
+    return sl < 4 ? (4 * ps + sl < HG ? 4 * ps + sl : -1)
+                  : (4 * ps + sl - 4 < HG ? 4 * ps + sl - 4 + HG : -1);
+  }
+  // slots in use in pass ps: 0 .. n/2 - 1 and 4 .. 4 + n/2 - 1
+  __device__ static constexpr int slots(int ps) {
+    return 2 * (HG - 4 * ps < 4 ? HG - 4 * ps : 4);
+  }
+};
+
+template <class C, int D>
+__device__ __forceinline__ void store_qkv_tile(const v16f (&acc)[C::FM][C::FN], float alpha,
+                                               uint8_t* slice, const RopeRev& rr,
+                                               const QkvOut& o, int M, int m0, int n0, int wm,
+                                               int wn, int lane) {
+  using P = QkvPass<D>;
+  constexpr int G = P::G, HG = P::HG;
+  static_assert(C::WN == D && C::FN * 4 == G && C::WM == 64, "one head per matrix wave");
+  const int nb = n0 + wn * D;  // the wave's first packed column
+  if (nb >= o.N) return;       // past the last column (ragged last tile)
+  const bool qk = nb < o.nqk2;
+  const int hq = nb / D;  // Q|K heads: 0 .. H-1 Q, H .. 2H-1 K
+  const bool isk = hq >= o.H;
+  const int hh = isk ? hq - o.H : hq;
+  const int r = lane & 31, hl = lane >> 5;
+  const int mp = m0 + wm * C::WM;
+  // the part's rows lie inside M and one sequence: rows follow each other
+  // in every output (else each row is placed on its own)
+  const int b0 = mp / o.S, s0 = mp - b0 * o.S;
+  const bool fast = mp + C::WM <= M && (mp + C::WM - 1) / o.S == b0;
+  uint16_t* qkout = isk ? o.k : o.q;
+  // element offset of column 0 of token m's row in its output (q/k, or v
+  // head hv)
+  auto row_off = [&](int m, int hv) -> int64_t {
+    int b = b0, s = s0 + (m - mp);
+    if (!fast) { b = m / o.S; s = m - b * o.S; }
+    return qk ? ((int64_t)b * o.H + hh) * o.S * o.qs + (int64_t)s * o.qs
+              : ((int64_t)b * o.H + hv) * o.S * o.dv + (int64_t)s * o.dv;
+  };
+#pragma unroll
+  for (int i = 0; i < C::FM; ++i) {
+    const int m = mp + 32 * i + r;  // this lane's row
+    // the product of columns 8 idx + 4 hl + 0..3, rounded to bf16 (packed)
+    auto prod = [&](int idx) {
+      const v16f& a = acc[i][idx / 4];
+      const int g = idx % 4;
+      return make_uint2(cvt_bf16x2_rn(a[4 * g] * alpha, a[4 * g + 1] * alpha),
+                        cvt_bf16x2_rn(a[4 * g + 2] * alpha, a[4 * g + 3] * alpha));
+    };
+    auto unpack4 = [](uint2 w, float (&f)[4]) {
+      f[0] = __uint_as_float(w.x << 16);
+      f[1] = __uint_as_float(w.x & 0xffff0000u);
+      f[2] = __uint_as_float(w.y << 16);
+      f[3] = __uint_as_float(w.y & 0xffff0000u);
+    };
+    auto put = [&](int sl, uint2 w) {  // this lane's 8 bytes of slot sl
+      *reinterpret_cast<uint2*>(slice + slice64(r, sl) + 8 * hl) = w;
+    };
+    float rho = 0.f;
+    int p = 0;
+    if (qk) {
+      float ss = 0.f;
+#pragma unroll
+      for (int idx = 0; idx < G; ++idx) {
+        float y[4];
+        unpack4(prod(idx), y);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) ss += y[e] * y[e];
+      }
+      ss += __shfl_xor(ss, 32);
+      rho = 1.0f / sqrtf(ss / (float)D + o.eps);
+      const int b = m / o.S;
+      p = m - b * o.S;
+      if (hl == 0 && m < M) o.rho[(((int64_t)isk * o.n_seq + b) * o.H + hh) * o.S + p] = rho;
+    }
+    double rev = rr.rev0;
+#pragma unroll
+    for (int ps = 0; ps < P::PASSES; ++ps) {
+      // fill the slots of this pass
+#pragma unroll
+      for (int sl = 0; sl < 4; ++sl) {
+        const int lo = P::group(ps, sl);
+        if (lo < 0) break;
+        if (qk) {
+          float y1[4], y2[4], o1[4], o2[4];
+          unpack4(prod(lo), y1);
+          unpack4(prod(lo + HG), y2);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            float cn, sn;
+            rope_cs(rev, p, cn, sn);
+            rev *= e < 3 ? rr.r1 : rr.r5;
+            const float u1 = y1[e] * rho, u2 = y2[e] * rho;
+            o1[e] = u1 * cn - u2 * sn;
+            o2[e] = u2 * cn + u1 * sn;
+          }
+          put(sl, make_uint2(cvt_bf16x2_rn(o1[0], o1[1]), cvt_bf16x2_rn(o1[2], o1[3])));
+          put(sl + 4, make_uint2(cvt_bf16x2_rn(o2[0], o2[1]), cvt_bf16x2_rn(o2[2], o2[3])));
+        } else {
+          put(sl, prod(lo));
+          put(sl + 4, prod(lo + HG));
+        }
+      }
+      // read back: CPR chunks per row in use, lane (rq, pc) takes chunk pc
+      // of rows rq + RPI q
+      const int CPR = P::slots(ps);
+      const int RPI = 64 / CPR, NI = CPR / 2;
+      const int rq = lane / CPR, pc = lane - rq * CPR;
+      const int sl = pc < CPR / 2 ? pc : pc - CPR / 2 + 4;  // slots 0.. and 4..
+      uint4 val[4];
+#pragma unroll
+      for (int qq = 0; qq < 4; ++qq)
+        if (qq < NI) val[qq] = *reinterpret_cast<const uint4*>(slice + slice64(rq + RPI * qq, sl));
+      const int col = 8 * (sl < 4 ? 4 * ps + sl : 4 * ps + sl - 4 + HG);  // column in the head
+      int hv = 0, jv = col;
+      bool live = true;
+      if (!qk) {  // a V part: columns of one or two V heads
+        const int vc = nb - o.nqk2 + col;
+        hv = vc / o.dv;
+        jv = vc - hv * o.dv;
+        live = nb + col < o.N;
+      }
+#pragma unroll
+      for (int qq = 0; qq < 4; ++qq) {
+        if (qq >= NI) break;
+        const int mt = mp + 32 * i + rq + RPI * qq;
+        if (live && mt < M) store_stream((qk ? qkout : o.v) + row_off(mt, hv) + jv, val[qq]);
+      }
+    }
+    // zero padding columns d .. qs - 1 of the fragment's q / k rows
+    if (qk && o.qs > D) {
+      const int pcs = (o.qs - D) / 8;
+      for (int it = lane; it < 32 * pcs; it += 64) {
+        const int rr2 = it / pcs, c = it - rr2 * pcs;
+        const int mt = mp + 32 * i + rr2;
+        if (mt < M) store_stream(qkout + row_off(mt, 0) + D + 8 * c, make_uint4(0, 0, 0, 0));
+      }
+    }
+  }
+}
+
+template <int D, bool KTAIL>
+__global__ __launch_bounds__((TileCfg<128, 2 * D>::THREADS), 1) void gemm_qkv_fwd_kernel(
+    Gemm gm, int ntiles, const float* __restrict__ sa, const float* __restrict__ sb, QkvOut o,
+    float base) {
+  using C = TileCfg<128, 2 * D>;
+  __shared__ __attribute__((aligned(16))) uint8_t lds[kStages * C::STAGE_BYTES];
+  __shared__ __attribute__((aligned(16))) uint8_t slices[C::MMA * 4096];
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  Sched sc;
+  sc.nk = (gm.K + kBK - 1) / kBK;
+  sc.ks0 = 0;
+  persistent_tiles(sc, blockIdx.x, gridDim.x, ntiles, gm.n_tiles);
+  if (wave >= C::MMA) {
+    copy_role<C, KTAIL>(lds, gm, sc, wave - C::MMA, lane);
+    return;
+  }
+  const int wm = wave / C::NW_, wn = wave % C::NW_;
+  const float alpha = sa[0] * sb[0];
+  uint8_t* slice = slices + wave * 4096;
+  const double r1 = rope_rev(1, D, base) / rope_rev(0, D, base);
+  const RopeRev rr{rope_rev(4 * (lane >> 5), D, base), r1, r1 * r1 * r1 * r1 * r1};
+  int ord = 0;
+  v16f acc[C::FM][C::FN];
+  auto done = [&](v16f (&a)[C::FM][C::FN]) {
+    const int tile = sc.tile_of(ord++);
+    store_qkv_tile<C, D>(a, alpha, slice, rr, o, gm.M, (tile / gm.n_tiles) * C::BM_,
+                         (tile % gm.n_tiles) * C::BN_, wm, wn, lane);
+  };
+  mma_role<C, false, true>(lds, sc, wm, wn, lane, acc, done);
+}
+
 template <int BM, int BN, bool KTAIL, class Epi, int FA = kFmtE4M3>
 __global__ __launch_bounds__((TileCfg<BM, BN>::THREADS), 1) void gemm_bf16out_kernel(
     Gemm gm, int ntiles, const float* __restrict__ sa, const float* __restrict__ sb, Epi epi) {
@@ -934,6 +1159,36 @@ void launch_gemm_fwd(const uint8_t* x8, const uint8_t* w_packed_t, int T, int N,
                      uint16_t* v, int H, int d_v, int seq_len, hipStream_t s) {
   const Gemm gm{x8, 0, w_packed_t, D, T, N, D, (int)ceil_div(N, kBNo), kActRows, 0, 0};
   launch_bf16out(gm, x_scales, w_scales, EpiFwd{qk_pre, v, N, nqk2, H, d_v, seq_len}, s);
+}
+
+bool fused_forward_width(int d_qk) { return d_qk == 64 || d_qk == 96 || d_qk == 128; }
+
+template <int DQK>
+static void launch_qkv_fwd_t(const Gemm& gm, int ntiles, const float* sa, const float* sb,
+                             const QkvOut& o, float base, hipStream_t s) {
+  constexpr int kThr = TileCfg<128, 2 * DQK>::THREADS;
+  const int blocks = std::min(ntiles, cu_count());
+  if (gm.K % kBK)
+    gemm_qkv_fwd_kernel<DQK, true><<<blocks, kThr, 0, s>>>(gm, ntiles, sa, sb, o, base);
+  else
+    gemm_qkv_fwd_kernel<DQK, false><<<blocks, kThr, 0, s>>>(gm, ntiles, sa, sb, o, base);
+}
+
+void launch_gemm_qkv_fwd(const uint8_t* x8, const uint8_t* w_packed_t, int n_seq, int seq_len,
+                         int D, int H, int d_qk, int d_v, int qs, float eps, float base,
+                         const float* x_scales, const float* w_scales, uint16_t* q, uint16_t* k,
+                         uint16_t* v, float* rho, hipStream_t s) {
+  const int T = n_seq * seq_len, nqk2 = 2 * H * d_qk, N = nqk2 + H * d_v;
+  const int bn = 2 * d_qk;  // the tile's columns: two heads
+  const Gemm gm{x8, 0, w_packed_t, D, T, N, D, (int)ceil_div(N, bn), kActRows, 0, 0};
+  const int ntiles = (int)ceil_div(T, 128) * gm.n_tiles;
+  const QkvOut o{q, k, v, rho, H, seq_len, d_v, qs, N, nqk2, n_seq, eps};
+  switch (d_qk) {
+    case 64: launch_qkv_fwd_t<64>(gm, ntiles, x_scales, w_scales, o, base, s); break;
+    case 96: launch_qkv_fwd_t<96>(gm, ntiles, x_scales, w_scales, o, base, s); break;
+    case 128: launch_qkv_fwd_t<128>(gm, ntiles, x_scales, w_scales, o, base, s); break;
+    default: break;
+  }
 }
 
 void launch_gemm_dx(const uint8_t* g8, const uint8_t* w_packed, int T, int D, int Np,

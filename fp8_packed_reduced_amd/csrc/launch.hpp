@@ -81,10 +81,24 @@ void launch_encode(const float* in, int64_t n, float inv, uint8_t* out, hipStrea
 // ---- gemm.hip --------------------------------------------------------------
 
 // Forward: Y = s_x s_w x8 @ W_packed, M = T rows, N packed columns, K = D.
-// Q|K columns go to qk_pre [T][nqk2] bf16; V columns to v head-major.
+// Q|K columns go to qk_pre [T][nqk2] bf16; V columns to v head-major.  (The
+// path for head widths without a fused forward, below.)
 void launch_gemm_fwd(const uint8_t* x8, const uint8_t* w_packed_t, int T, int N, int D,
                      const float* x_scales, const float* w_scales, uint16_t* qk_pre, int nqk2,
                      uint16_t* v, int H, int d_v, int seq_len, hipStream_t s);
+
+// Whether the forward GEMM carries the norm and RoPE in its epilogue at this
+// head width (64, 96, 128).
+bool fused_forward_width(int d_qk);
+
+// Forward with RMSNorm and RoPE in the GEMM's epilogue: q, k head-major rows
+// of qs >= d_qk elements (columns d_qk .. qs - 1 written as zero), v
+// head-major, and rho [2][n_seq][H][S] fp32 = 1 / rms of every q, then every
+// k head row (of the bf16-rounded product).
+void launch_gemm_qkv_fwd(const uint8_t* x8, const uint8_t* w_packed_t, int n_seq, int seq_len,
+                         int D, int H, int d_qk, int d_v, int qs, float eps, float base,
+                         const float* x_scales, const float* w_scales, uint16_t* q, uint16_t* k,
+                         uint16_t* v, float* rho, hipStream_t s);
 
 // dX = s_g s_w g8 @ W_packed^T: M = T, N = D, K = N_packed; dx [T][D] bf16.
 // g_e5m2: g8 holds e5m2 codes (else e4m3); the weight codes are e4m3.
@@ -132,21 +146,23 @@ void launch_dw_reduce(const float* part, int D, int Np, int64_t Tp, const float*
 size_t norm_rope_fwd_lds(int H, int d_qk);
 size_t norm_rope_bwd_lds(int H, int d_qk);
 
-// Forward epilogue: pre-norm Q|K rows (qk_pre [T][2*H*d_qk] bf16) ->
-// RMSNorm -> RoPE -> head-major q, k with rows of qs >= d_qk elements (a
-// multiple of 8), columns d_qk .. qs - 1 written as zero.
+// Forward norm/RoPE for head widths without a fused forward: pre-norm Q|K
+// rows (qk_pre [T][2*H*d_qk] bf16) -> RMSNorm -> RoPE -> head-major q, k
+// with rows of qs >= d_qk elements (a multiple of 8), columns d_qk .. qs - 1
+// written as zero, and rho [2][n_seq][H][S] = 1 / rms of each row.
 void launch_norm_rope_fwd(const uint16_t* qk_pre, int64_t T, int seq_len, int H, int d_qk,
-                          int qs, float eps, float base, uint16_t* q, uint16_t* k,
+                          int qs, float eps, float base, uint16_t* q, uint16_t* k, float* rho,
                           hipStream_t s);
 
-// Backward epilogue: dq, dk (head-major, rows of qs elements of which the
-// first d_qk are read) + qk_pre -> the Q|K part of the packed gradient,
-// dQK [T][2 H d_qk] bf16, plus one amax partial per block over dQK;
-// norm_rope_bwd_blocks() is that block count.  (dv's amax is taken by
-// launch_amax_bf16.)
+// Backward epilogue from the forward's outputs: dq, dk, q, k (head-major,
+// rows of qs elements of which the first d_qk are read) and rho -> the Q|K
+// part of the packed gradient, dQK [T][2 H d_qk] bf16, plus one amax partial
+// per block over dQK; norm_rope_bwd_blocks() is that block count (at most
+// 1024).  (dv's amax is taken by launch_amax_bf16.)
 int norm_rope_bwd_blocks(int64_t T, int H, int d_qk);
-void launch_norm_rope_bwd(const uint16_t* dq, const uint16_t* dk, const uint16_t* qk_pre,
-                          int64_t T, int seq_len, int H, int d_qk, int qs, float eps, float base,
-                          uint16_t* dqkv, uint32_t* partials, hipStream_t s);
+void launch_norm_rope_bwd(const uint16_t* dq, const uint16_t* dk, const uint16_t* q,
+                          const uint16_t* k, const float* rho, int64_t T, int seq_len, int H,
+                          int d_qk, int qs, float base, uint16_t* dqkv, uint32_t* partials,
+                          hipStream_t s);
 
 }  // namespace fpr

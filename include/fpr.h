@@ -6,9 +6,9 @@
  * The method ("96 is enough: shrinking attention's routing vectors",
  * section "The change"): Q and K heads are d_qk = 96 wide while V stays
  * d_v = 128 wide; the three projections are packed into one weight
- * W_packed = [W_q | W_k | W_v] (320 columns per head instead of 384) and
- * computed by a single FP8 matmul qkv = x @ W_packed; q, k, v are split off,
- * q and k are RMS-normalised and rotated with RoPE.  The PR #344 page,
+ * W_packed = [W_q | W_k | W_v] (320 columns per head instead of 384), and a
+ * single FP8 product of x with W_packed gives all three; q, k, v are split
+ * off, q and k are RMS-normalised and rotated with RoPE.  The PR #344 page,
  * section "Changes", adds: both FP8 layouts of W_packed (row-major and
  * transposed) are cached per optimizer update and come from one weight
  * read; the logical Q/K and V packs are quantised without materialising the
@@ -125,8 +125,11 @@ enum { FPR_CALL_PACK = 0, FPR_CALL_FORWARD = 1, FPR_CALL_BACKWARD = 2 };
 FPR_API size_t fpr_workspace_bytes(const fpr_dims* dims, int64_t tokens, int which);
 
 /* Bytes of the buffer qkv_forward fills for qkv_backward: the FP8 x (in the
- * layout the dW GEMM reads), its scales, and the pre-norm Q|K values in bf16.
- * It must stay alive and unmodified from forward to backward. */
+ * layout the dW GEMM reads), its scales, and one fp32 1/rms per Q and K head
+ * row.  It must stay alive and unmodified from forward to backward, and so
+ * must the forward's q and k outputs, which the backward reads too (no
+ * pre-norm row is kept: the backward rebuilds the normalised rows from q, k
+ * and the saved 1/rms). */
 FPR_API size_t fpr_saved_bytes(const fpr_dims* dims, int64_t tokens);
 
 /* Step 1 ("Changes": cache row-major and transposed FP8 weights once per
@@ -145,8 +148,12 @@ FPR_API int pack_quantize_weights(const fpr_dims* dims,
                           void* workspace, size_t workspace_bytes,
                           void* stream);
 
-/* Step 2 ("The change": qkv = fp8_matmul(x, W_packed); split; rms_norm and
- * rope on q and k).
+/* Step 2 ("96 is enough", "The change": one FP8 product of x with W_packed,
+ * split, rms_norm and rope on q and k; "Reduced-width QK and packed FP8
+ * attention", Changes: norm, RoPE and layout conversion fused).  For d_qk of
+ * 64, 96 and 128 the norm and RoPE run inside the GEMM's epilogue and no
+ * pre-norm value reaches memory; other widths pass the pre-norm Q|K rows
+ * through the forward workspace.
  *   x:  [T][D] bf16 input activations
  *   q:  [n_seq][H][seq_len][qk_stride] bf16 out (normalised, rotated; the
  *       columns past d_qk written as zero)
@@ -161,15 +168,23 @@ FPR_API int qkv_forward(const fpr_dims* dims, int32_t n_seq, int32_t seq_len,
                 void* workspace, size_t workspace_bytes,
                 void* stream);
 
-/* Step 3 (FP8 backward: norm/RoPE backward, then dX through the cached
- * W_packed codes and dW = x^T dQKV, quantisers treated as identity).
+/* Step 3, the backward of step 2 ("Reduced-width QK and packed FP8
+ * attention", Changes: the FP8 coverage extends to the backward GEMMs;
+ * "Where the eight seconds were hiding", The inventory: the backward reads
+ * the cached transposed weight view instead of rebuilding it).  The
+ * norm/RoPE backward gives the packed gradient dQKV from q, k, the saved
+ * 1/rms and dq, dk, dv (with u = R_{-p} q the normalised row, the pre-norm
+ * gradient is rho * R_{-p}(dq - q <q,dq> / d_qk)); then dX through the
+ * cached W_packed codes and dW = x^T dQKV, quantisers treated as identity.
+ *   q, k:   the matching qkv_forward's q and k outputs, unmodified
  *   dq, dk: [n_seq][H][seq_len][qk_stride] bf16 upstream gradients (only
- *           the first d_qk columns of each row are read)
+ *           the first d_qk columns of each row, of q and k too, are read)
  *   dv:     [n_seq][H][seq_len][d_v]  bf16
  *   saved:  the buffer filled by the matching qkv_forward
  *   dx:     [T][D] bf16 out
  *   dwq: [D][H*d_qk] fp32 out (row stride ldq), dwk likewise, dwv [D][H*d_v]. */
 FPR_API int qkv_backward(const fpr_dims* dims, int32_t n_seq, int32_t seq_len,
+                 const uint16_t* q, const uint16_t* k,
                  const uint16_t* dq, const uint16_t* dk, const uint16_t* dv,
                  const void* saved, size_t saved_bytes,
                  const fpr_weight_cache* cache,
@@ -202,15 +217,20 @@ typedef struct fpr_layout {
     int64_t tokens_padded;   /* T rounded up to k_block                     */
     /* in `saved` */
     size_t saved_x8;         /* [T][D] e4m3 blocked                         */
-    size_t saved_qk_pre;     /* [T][2*H*d_qk] bf16, pre-norm Q|K            */
+    size_t saved_rho;        /* [2][n_seq][H][S] fp32: 1/rms of each q head
+                                row, then of each k head row               */
     size_t saved_x_scales;   /* [2] fp32: s_x, inv_x                        */
-    /* in the backward workspace (the forward one holds only amax partials) */
+    /* in the forward workspace (besides the x amax partials) */
+    size_t fwd_qk_pre;       /* [T][2*H*d_qk] bf16 pre-norm Q|K, for head
+                                widths without the fused forward; -1 else  */
+    /* in the backward workspace */
     size_t bwd_dqkv;         /* [T][2*H*d_qk] bf16, Q|K part of the packed
                                 gradient (its V part is dv itself)           */
     size_t bwd_g_scales;     /* [2] fp32: s_g, inv_g                         */
     size_t bwd_g8;           /* [T][N] e4m3 blocked                          */
     size_t bwd_dw_part;      /* [dw_splits][D][N] fp32 split-K dW partials   */
     int32_t dw_splits;       /* K splits of the dW GEMM at this token count  */
+    int32_t bwd_amax_partials; /* amax partials the gradient quantiser folds */
     int32_t k_block;         /* bytes of K per block (128)                   */
     int32_t act_block_rows;  /* rows per block of x8 and g8 (256)            */
 } fpr_layout;
@@ -245,8 +265,8 @@ FPR_API void fpr_trace_set(fpr_trace* trace);
 /* ---------------------------------------------------------------------
  * FP8 ReLU^2 MLP ("Reduced-width QK and packed FP8 attention", Changes:
  * FP8 extended to the whole ReLU-squared MLP, forward and backward, both
- * projections and all four backward GEMMs; relu(pre) rebuilt from the
- * stored squared activation instead of keeping pre).
+ * projections and all four backward GEMMs; pre is not kept, and relu(pre)
+ * is recovered as sqrt(s_h * dec(h8)) from the squared activation's codes).
  *
  *   forward:  pre = x W1, h = relu(pre)^2, y = h W2
  *             (W1 [D][F], W2 [F][D] fp32; x, y [T][D] bf16)

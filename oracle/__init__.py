@@ -18,7 +18,7 @@ What is computed, and where the pages say so:
 * "Where the eight seconds were hiding", section "The inventory": the
   transposed weight view is cached and reused by the backward pass.
 * PR #344 page, section "Changes": the FP8 ReLU-squared MLP, forward and
-  backward, with relu(pre) rebuilt from the stored squared activation
+  backward, pre not kept and relu(pre) recovered as sqrt(s_h dec(h8))
   (``mlp_forward`` / ``mlp_backward``, readings at that section).
 
 Every floating-point step runs in float64.  FP8 codes, scales and bf16/fp32
@@ -268,7 +268,7 @@ def pack_quantize(D, H, d_qk, d_v, wq, wk, wv):
 def gemm_e4m3(a_codes: np.ndarray, b_codes: np.ndarray, s_a, s_b, a_fmt: str = "e4m3",
               b_fmt: str = "e4m3") -> np.ndarray:
     """C = s_a * s_b * dec(A) @ dec(B) in float64 ("96 is enough", "The
-    change": qkv = fp8_matmul(x, W_packed)).  A is [M][K], B is [K][N]; each
+    change": Y = x W_packed as one FP8 product).  A is [M][K], B is [K][N]; each
     operand's codes are e4m3 unless its format says e5m2."""
     A = decode_table(a_fmt)[a_codes]
     B = decode_table(b_fmt)[b_codes]
@@ -434,9 +434,9 @@ def qkv_backward(dims, n_seq: int, S: int, dq_bits, dk_bits, dv_bits,
 # ------------------------------------------------------ FP8 ReLU^2 MLP
 #
 # PR #344 page, "Changes": FP8 covers the whole ReLU-squared MLP, forward
-# and backward, both projections and all four backward GEMMs; the backward
-# rebuilds relu(pre) from the stored squared activation instead of keeping
-# pre.  Readings where the page is silent: W1 is [D][F] and W2 is [F][D]
+# and backward, both projections and all four backward GEMMs; pre is not
+# kept: the backward recovers relu(pre) from the squared activation.
+# Readings where the page is silent: W1 is [D][F] and W2 is [F][D]
 # (y = relu(x W1)^2 W2), one per-tensor e4m3 scale per tensor exactly as for
 # the QKV path, and the stored squared activation is its e4m3 copy h8 with
 # scale s_h, which the second projection and dW2 read anyway, so

@@ -98,7 +98,13 @@ def run(w: dict, seed: int = 42, x_bits=None, W=None, dy=None, backward: bool = 
     # x8_tail: the zero token rows T .. Tp - 1 that the dW GEMM reads as its K tail
     out["x8"], out["x8_kpad"], out["x8_tail"] = x8[:T, :D], x8[:T, D:], x8[T:Tp]
     out["x_scales"] = B.view_bytes(saved, lay.saved_x_scales, (2,), torch.float32).cpu().numpy()
-    out["qk_pre"] = dev_to_bits(B.view_bytes(saved, lay.saved_qk_pre, (T, 2 * nq), torch.bfloat16))
+    # 1/rms of every q, then every k head row: [2][n_seq][H][S]
+    out["rho"] = B.view_bytes(saved, lay.saved_rho, (2, n_seq, H, S), torch.float32).cpu().numpy()
+    # the pre-norm Q|K rows exist only where the norm/RoPE is not fused into
+    # the forward GEMM (then in the forward workspace)
+    out["fused"] = lay.fused_forward
+    out["qk_pre"] = None if lay.fused_forward else dev_to_bits(
+        B.view_bytes(ws_f, lay.fwd_qk_pre, (T, 2 * nq), torch.bfloat16))
     out["q"], out["k"], out["v"] = dev_to_bits(q), dev_to_bits(k), dev_to_bits(v)
     if backward:
         if dy is None:
@@ -107,7 +113,8 @@ def run(w: dict, seed: int = 42, x_bits=None, W=None, dy=None, backward: bool = 
                          for i, a in enumerate(dy))
         ws_b = torch.empty(B.workspace_bytes(dims, T, B.FPR_CALL_BACKWARD), dtype=torch.uint8,
                            device="cuda")
-        dx, dw = B.qkv_backward(dims, n_seq, S, dqd, dkd, dvd, saved, cache, workspace=ws_b)
+        dx, dw = B.qkv_backward(dims, n_seq, S, q, k, dqd, dkd, dvd, saved, cache,
+                                workspace=ws_b)
         torch.cuda.synchronize()
         out["dy"] = dy
         # the packed gradient: its Q|K part from the workspace, its V part is
@@ -123,6 +130,12 @@ def run(w: dict, seed: int = 42, x_bits=None, W=None, dy=None, backward: bool = 
     out["status"] = int(cache.status.cpu().item())
     say("[gpu] done")
     return out
+
+
+def rho_rows(rho: np.ndarray) -> np.ndarray:
+    """[2][n_seq][H][S] (q rows, then k rows) -> [T][2H] in packed head order."""
+    two, n_seq, H, S = rho.shape
+    return np.ascontiguousarray(rho.transpose(1, 3, 0, 2)).reshape(n_seq * S, 2 * H)
 
 
 def bf16_to_f64(bits: np.ndarray) -> np.ndarray:

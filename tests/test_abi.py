@@ -1,7 +1,9 @@
 """Host-side checks of the C interface (no GPU needed, nothing is launched):
 the library loads, exports every call the header declares, sizes and the
 private layout are consistent, and every argument error is reported before
-any kernel launch."""
+any kernel launch.  The argument-error tests pass made-up device addresses,
+so they run only where no GPU is visible: there a check that regressed
+could reach a launch on an unmapped address."""
 import ctypes
 
 import pytest
@@ -38,15 +40,17 @@ def test_sizes_and_layout_at_the_64k_step_shape():
     lay = B.layout(d, T)
     assert lay.tokens == T and lay.tokens_padded == T
     saved = B.saved_bytes(d, T)
-    # x8 [T][768] blocked + pre-norm Q|K [T][1152] bf16 + scales
-    assert saved >= 768 * T + T * 1152 * 2 + 8
-    assert lay.saved_x8 + 768 * T <= lay.saved_qk_pre
-    assert lay.saved_qk_pre + T * 1152 * 2 <= lay.saved_x_scales < saved
+    # x8 [T][768] blocked + 1/rms of 12 Q/K head rows per token + scales; no
+    # pre-norm rows (the norm/RoPE runs in the GEMM's epilogue at d_qk = 96)
+    assert lay.fused_forward
+    assert 768 * T + T * 12 * 4 + 8 <= saved < 768 * T + T * 12 * 4 + 4096
+    assert lay.saved_x8 + 768 * T <= lay.saved_rho
+    assert lay.saved_rho + T * 12 * 4 <= lay.saved_x_scales < saved
     # the forward workspace holds only the x amax partials
     assert B.workspace_bytes(d, T, B.FPR_CALL_FORWARD) <= 4096
     bw = B.workspace_bytes(d, T, B.FPR_CALL_BACKWARD)
     assert bw >= lay.bwd_g8 + 1920 * T
-    for off in (lay.saved_x8, lay.saved_qk_pre, lay.saved_x_scales,
+    for off in (lay.saved_x8, lay.saved_rho, lay.saved_x_scales,
                 lay.bwd_dqkv, lay.bwd_g8, lay.bwd_g_scales, lay.bwd_dw_part):
         assert off % 256 == 0
     # split-K partials of dW fit after the gradient codes
@@ -63,7 +67,7 @@ def test_blocked_fp8_layouts_cover_their_padding():
     assert (lay.k_block, lay.act_block_rows) == (128, 256)
     assert lay.tokens_padded == 256
     # x8: one block row of 256 tokens x 2 K blocks of 128 bytes
-    assert lay.saved_x8 + 256 * 256 <= lay.saved_qk_pre
+    assert lay.saved_x8 + 256 * 256 <= lay.saved_rho
     # g8: 256 tokens x 3 K blocks
     assert lay.bwd_g8 + 256 * 384 <= lay.bwd_dw_part
 
@@ -76,6 +80,29 @@ def test_dw_split_count_depends_only_on_shapes():
     assert B.layout(d, 16384).dw_splits == 5
     # never more splits than 128-token K steps
     assert B.layout(B.make_dims(128, 1), 100).dw_splits == 1
+
+
+def test_unfused_widths_keep_the_prenorm_rows_in_the_forward_workspace():
+    # d_qk = 48: no fused forward; its pre-norm Q|K rows [T][2 * 2 * 48] bf16
+    # pass through the forward workspace, never the saved buffer
+    d = B.make_dims(192, 2, 48, 64)
+    T = 1000
+    lay = B.layout(d, T)
+    assert not lay.fused_forward
+    assert lay.fwd_qk_pre % 256 == 0
+    assert lay.fwd_qk_pre + T * 192 * 2 <= B.workspace_bytes(d, T, B.FPR_CALL_FORWARD)
+    for dqk in (64, 96, 128):
+        assert B.layout(B.make_dims(768, 6, dqk, 128), T).fused_forward
+
+
+@pytest.mark.parametrize("dims", [(768, 6, 96, 128), (192, 2, 48, 64), (128, 1, 96, 128)])
+def test_amax_partials_stay_bounded(dims):
+    # every quantiser block folds all partials of its tensor: their number
+    # must not grow with the token count (at most 4096)
+    d = B.make_dims(*dims)
+    for T in (1, 1000, 65536, 1 << 24):
+        lay = B.layout(d, T)
+        assert 1 <= lay.bwd_amax_partials <= 1024 + 256
 
 
 def test_token_limit():
@@ -136,6 +163,11 @@ def _cache_c(ptr=0x1000):
     return B._CacheC(ptr, ptr, ptr, ptr)
 
 
+_NO_GPU = pytest.mark.skipif(torch.cuda.is_available(),
+                             reason="made-up device addresses: host-only")
+
+
+@_NO_GPU
 def test_argument_errors_are_reported_before_any_launch():
     L = B.load()
     d = B.make_dims(128, 1)
@@ -164,11 +196,16 @@ def test_argument_errors_are_reported_before_any_launch():
     # forward with an incomplete weight cache
     half = B._CacheC(ws, None, ws, ws)
     assert L.qkv_forward(by(d), 1, 256, ws, by(half), ws, ws, ws, ws, 1 << 30, ws, 1 << 30, None) == 1
-    # backward: ld errors on the dW outputs, small workspace
-    assert L.qkv_backward(by(d), 1, 256, ws, ws, ws, ws, 1 << 30, by(cc), ws, ws, 90, ws, 96, ws,
-                          128, ws, 1 << 30, None) == 1
-    assert L.qkv_backward(by(d), 1, 256, ws, ws, ws, ws, 1 << 30, by(cc), ws, ws, 96, ws, 96, ws,
-                          128, ws, 100, None) == 4
+    # backward: ld errors on the dW outputs, missing or misaligned forward
+    # outputs, small workspace
+    assert L.qkv_backward(by(d), 1, 256, ws, ws, ws, ws, ws, ws, 1 << 30, by(cc), ws, ws, 90, ws,
+                          96, ws, 128, ws, 1 << 30, None) == 1
+    assert L.qkv_backward(by(d), 1, 256, None, ws, ws, ws, ws, ws, 1 << 30, by(cc), ws, ws, 96,
+                          ws, 96, ws, 128, ws, 1 << 30, None) == 1
+    assert L.qkv_backward(by(d), 1, 256, ws, ws + 8, ws, ws, ws, ws, 1 << 30, by(cc), ws, ws, 96,
+                          ws, 96, ws, 128, ws, 1 << 30, None) == 3
+    assert L.qkv_backward(by(d), 1, 256, ws, ws, ws, ws, ws, ws, 1 << 30, by(cc), ws, ws, 96, ws,
+                          96, ws, 128, ws, 100, None) == 4
     # encoder hook
     assert L.fpr_e4m3_encode(ws, 15, 1.0, ws, None) == 3
     assert L.fpr_e4m3_encode(None, 16, 1.0, ws, None) == 1
@@ -204,6 +241,7 @@ def test_mlp_layout_is_disjoint_and_sized():
     assert lay.dw1_splits == lay.dw2_splits == 7
 
 
+@_NO_GPU
 def test_mlp_argument_errors_are_reported_before_any_launch():
     L = B.load()
     d = B.MlpDims(128, 512)

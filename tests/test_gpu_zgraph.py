@@ -70,7 +70,7 @@ def test_qkv_step_replays_from_a_graph():
         B.pack_quantize_weights(dims, W[:, :nq], W[:, nq:2 * nq], W[:, 2 * nq:], cache,
                                 workspace=ws_p)
         B.qkv_forward(dims, n_seq, S, x, cache, q, k, v, saved, ws_f)
-        B.qkv_backward(dims, n_seq, S, dq, dk, dvg, saved, cache, dx, dw, ws_b)
+        B.qkv_backward(dims, n_seq, S, q, k, dq, dk, dvg, saved, cache, dx, dw, ws_b)
 
     outs = [cache.w_packed, cache.w_packed_t, cache.scales, q, k, v, dx, dw]
     step()
