@@ -75,7 +75,7 @@ Plan make_plan(const fpr_dims* d, int64_t T) {
   p.N = p.nqk2 + p.H * p.dv;
   p.T = T;
   p.Tp = round_up(T > 0 ? T : 1, 128);
-  p.fused = fpr::fused_forward_width(p.dqk);
+  p.fused = fpr::fused_forward(p.dqk, p.N, p.D);
   size_t c = 0;
   p.s_x8 = take(c, fpr::act_blocked_bytes(T, p.D));
   p.s_rho = take(c, (size_t)T * 2 * p.H * sizeof(float));

@@ -87,9 +87,7 @@ __device__ inline double rope_rev(int i, int d, float base) {
 }
 
 __device__ inline void rope_cs(double rev_i, int64_t pos, float& c, float& s) {
-  double r = (double)pos * rev_i;
-  r -= rint(r);
-  const float f = (float)r;
+  const float f = (float)__builtin_amdgcn_fract((double)pos * rev_i);  // in [0, 1)
   s = __builtin_amdgcn_sinf(f);  // sin(2 pi f)
   c = __builtin_amdgcn_cosf(f);
 }

@@ -194,6 +194,32 @@ __device__ __forceinline__ v16f mfma32(v8i b, v8i a, v16f c) {
 // With tok, both operands are token-major instead (dW: K = tokens): the
 // row layouts of x8 and g8, blocks of kActRows tokens x kKBlock features,
 // lda / ldb = feature blocks per block row.
+// Head-aligned column tiles of the forward projection (d > 0; d = 0 means
+// tile column c of tile n is packed column 128 n + c).  128-column tile n
+// < n_mixed holds the hpt whole Q/K heads n hpt, n hpt + 1, ... (d columns
+// each) followed by `fill` columns of V (V columns n fill, ...); later tiles
+// hold 128 V columns each, from n_mixed fill on.  The copy waves fetch the
+// B rows of each tile in this order, so every matrix wave of a 256 x 128
+// tile (64 rows x all 128 columns) sees whole Q/K head rows.
+struct ColMap {
+  int d, hpt, fill, n_mixed, nqk2, nv;  // head width, heads per tile, V columns
+                                        // per mixed tile, mixed tiles, Q|K and V columns
+  // packed column of column c (< 128) of tile column n, or -1 (none)
+  __host__ __device__ int natural(int n, int c) const {
+    if (n < n_mixed) {
+      const int hd = hpt * d;
+      if (c < hd) {
+        const int col = (n * hpt + c / d) * d + c % d;
+        return col < nqk2 ? col : -1;
+      }
+      const int f = n * fill + (c - hd);
+      return f < nv ? nqk2 + f : -1;
+    }
+    const int v = n_mixed * fill + (n - n_mixed) * 128 + c;
+    return v < nv ? nqk2 + v : -1;
+  }
+};
+
 struct Gemm {
   const uint8_t* A;
   int64_t lda;
@@ -202,6 +228,7 @@ struct Gemm {
   int M, N, K, n_tiles;
   int a_blk, b_blk;  // 0: row-major; else block rows
   int tok;
+  ColMap cm;         // B row order (forward with the fused norm/RoPE)
 };
 
 struct Sched {
@@ -270,18 +297,23 @@ __device__ __forceinline__ void dma_plan(CopyState<C>& st, const Gemm& gm, int t
   for (int t = 0; t < C::PER_WAVE; ++t) {
     const int row = (cw + kCopyWaves * t) * 8 + rl;
     const uint32_t chunk = (uint32_t)((p ^ swz_key(row)) << 4);
-    if (t < C::A_PER_WAVE)
+    if (t < C::A_PER_WAVE) {
       st.off[t] = (uint32_t)((min(m0 + row, gm.M - 1) - m0) * ra) + chunk;
-    else
+    } else if (gm.cm.d) {  // mapped B rows, offsets from B itself (N * ldb < 2^31)
+      const int nc = gm.cm.natural(tile % gm.n_tiles, row - C::BM_);
+      st.off[t] = (uint32_t)((nc < 0 ? 0 : nc) * rb) + chunk;
+    } else {
       st.off[t] = (uint32_t)((min(n0 + row - C::BM_, gm.N - 1) - n0) * rb) + chunk;
+    }
   }
   // a blocked operand's tile rows lie inside one block of blk rows (the
   // tile's rows divide blk): block m0 / blk, from its row m0 % blk on
   const int64_t kblocks = (gm.K + kBK - 1) / kBK;
   st.Atile = gm.a_blk ? gm.A + ((int64_t)(m0 / gm.a_blk) * kblocks * gm.a_blk + m0 % gm.a_blk) * kBK
                       : gm.A + (int64_t)m0 * gm.lda;
-  st.Btile = gm.b_blk ? gm.B + ((int64_t)(n0 / gm.b_blk) * kblocks * gm.b_blk + n0 % gm.b_blk) * kBK
-                      : gm.B + (int64_t)n0 * gm.ldb;
+  st.Btile = gm.cm.d  ? gm.B
+             : gm.b_blk ? gm.B + ((int64_t)(n0 / gm.b_blk) * kblocks * gm.b_blk + n0 % gm.b_blk) * kBK
+                        : gm.B + (int64_t)n0 * gm.ldb;
   st.tile = tile;
 }
 
@@ -460,6 +492,64 @@ __device__ __forceinline__ void mma_half_barrier(v16f (&acc)[C::FM][C::FN], Half
   for (int j = 0; j < C::FN; ++j) f.b[j] = nb[j];
 }
 
+// The same two steps with the loops the other way round, for wave tiles
+// with more B than A fragments (FN > FM): the A fragments of the next
+// half-step stream in first and B fragment j is reloaded after its last
+// use, so that the fewer fragments are the ones held twice.
+template <class C, bool TOK, bool FIRST = false>
+__device__ __forceinline__ void mma_half_bo(v16f (&acc)[C::FM][C::FN], Half<C>& f,
+                                            const uint8_t* src, int a0, int b0, int lane, int h) {
+  v8i na[C::FM];
+#pragma unroll
+  for (int i = 0; i < C::FM; ++i) na[i] = frag_a<C, TOK>(src, a0 + i * 32, lane, h);
+#pragma unroll
+  for (int j = 0; j < C::FN; ++j) {
+#pragma unroll
+    for (int i = 0; i < C::FM; ++i) acc[i][j] = mfma32<C>(f.b[j], f.a[i], FIRST ? v16f{} : acc[i][j]);
+    f.b[j] = frag_b<C, TOK>(src, b0 + j * 32, lane, h);
+#pragma unroll
+    for (int i = 0; i < C::FM; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // 1 MFMA
+      __builtin_amdgcn_sched_group_barrier(0x100, TOK ? 4 : 2, 0);  // then LDS reads
+    }
+  }
+#pragma unroll
+  for (int i = 0; i < C::FM; ++i) f.a[i] = na[i];
+}
+
+template <class C, bool TOK>
+__device__ __forceinline__ void mma_half_barrier_bo(v16f (&acc)[C::FM][C::FN], Half<C>& f,
+                                                    const uint8_t* src, int a0, int b0,
+                                                    int lane, int h) {
+  constexpr int EJ = kEarlyRows < C::FN ? kEarlyRows : C::FN - 1;  // columns before the barrier
+  static_assert(EJ >= 1, "columns on both sides of the barrier");
+#pragma unroll
+  for (int j = 0; j < EJ; ++j)
+#pragma unroll
+    for (int i = 0; i < C::FM; ++i) acc[i][j] = mfma32<C>(f.b[j], f.a[i], acc[i][j]);
+  __builtin_amdgcn_sched_barrier(0);
+  barrier_lds();
+  __builtin_amdgcn_sched_barrier(0);
+  v8i na[C::FM];
+#pragma unroll
+  for (int i = 0; i < C::FM; ++i) na[i] = frag_a<C, TOK>(src, a0 + i * 32, lane, h);
+#pragma unroll
+  for (int j = 0; j < EJ; ++j) f.b[j] = frag_b<C, TOK>(src, b0 + j * 32, lane, h);
+#pragma unroll
+  for (int j = EJ; j < C::FN; ++j) {
+#pragma unroll
+    for (int i = 0; i < C::FM; ++i) acc[i][j] = mfma32<C>(f.b[j], f.a[i], acc[i][j]);
+    f.b[j] = frag_b<C, TOK>(src, b0 + j * 32, lane, h);
+#pragma unroll
+    for (int i = 0; i < C::FM; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // 1 MFMA
+      __builtin_amdgcn_sched_group_barrier(0x100, TOK ? 4 : 2, 0);  // then LDS reads
+    }
+  }
+#pragma unroll
+  for (int i = 0; i < C::FM; ++i) f.a[i] = na[i];
+}
+
 template <class C>
 __device__ __forceinline__ void zero_acc(v16f (&acc)[C::FM][C::FN]) {
 #pragma unroll
@@ -485,23 +575,35 @@ __device__ __forceinline__ void mma_role(const uint8_t* lds, const Sched& sc, in
                                          int lane, v16f (&acc)[C::FM][C::FN],
                                          const TileDone& tile_done) {
   const int a0 = wm * C::WM, b0 = wn * C::WN;
-  zero_acc<C>(acc);
+  if (!ZC) zero_acc<C>(acc);
   barrier_lds();
   Half<C> f;
   load_half<C, TOK>(lds, a0, b0, lane, 0, f);
-  int ks_in_tile = 0;
-  for (int g = 0; g < sc.steps; ++g) {
+  // one K step: half 1 of the step's stage, then half 0 of the next one
+  // around the step's barrier; FIRST starts the tile's accumulators from zero
+  auto step = [&](int g, auto first) {
+    constexpr bool FIRST = decltype(first)::value;
     const uint8_t* cur = lds + (g % kStages) * C::STAGE_BYTES;
     const uint8_t* nxt = lds + ((g + 1) % kStages) * C::STAGE_BYTES;
-    if (ZC && ks_in_tile == 0)
-      mma_half<C, TOK, true>(acc, f, cur, a0, b0, lane, 1);
-    else
-      mma_half<C, TOK>(acc, f, cur, a0, b0, lane, 1);
-    mma_half_barrier<C, TOK>(acc, f, nxt, a0, b0, lane, 0);
-    if (++ks_in_tile == sc.nk) {
-      tile_done(acc);
-      ks_in_tile = 0;
+    if constexpr (C::FN > C::FM) {
+      mma_half_bo<C, TOK, FIRST>(acc, f, cur, a0, b0, lane, 1);
+      mma_half_barrier_bo<C, TOK>(acc, f, nxt, a0, b0, lane, 0);
+    } else {
+      mma_half<C, TOK, FIRST>(acc, f, cur, a0, b0, lane, 1);
+      mma_half_barrier<C, TOK>(acc, f, nxt, a0, b0, lane, 0);
     }
+  };
+  // tile by tile, so that the accumulators are dead between a tile's
+  // tile_done and the next tile's first step (with ZC, which writes them
+  // from zero): the epilogue then has their registers
+  for (int g = 0; g < sc.steps;) {
+    if (ZC)
+      step(g, std::true_type{});
+    else
+      step(g, std::false_type{});
+    ++g;
+    for (int ks = 1; ks < sc.nk; ++ks, ++g) step(g, std::false_type{});
+    tile_done(acc);
   }
 }
 
@@ -800,197 +902,231 @@ __device__ __forceinline__ void persistent_tiles(Sched& sc, int b, int G, int nt
 // "96 is enough", "The change": after the one packed matmul, q and k are
 // RMS-normalised and rotated; PR #344 page, "Changes": norm, RoPE and the
 // layout conversion are fused.  Here they run in the matmul's own epilogue,
-// so no pre-norm row ever reaches memory.  The tile is 128 rows x 2 d
-// columns (d = d_qk), so each matrix wave (64 rows x d) holds whole rows of
-// one packed head: the Q|K / V boundary 2 H d is a multiple of d.  For row
-// l % 32 (+ 32 i) a lane holds the head's columns 8 idx + 4 (l / 32) + e
-// (idx < d / 8, e < 4): the row's sum of squares is the lane's own values
-// plus one exchange with lane l ^ 32, and the rotation partner of column
-// c < d / 2, c + d / 2, sits in the same lane (group idx + d / 16, same e).
-// The product is rounded to bf16 first, exactly where an unfused path would
-// store it, then normalised (fp32) and rotated; 1 / rms of every Q and K
-// head row goes out with q, k and v, and the backward rebuilds the
-// normalised rows from q and k with it.
+// so no pre-norm row ever reaches memory.  The tile is the bf16 GEMM's
+// 256 x 128, its B rows fetched in head-aligned order (ColMap), and its
+// four matrix waves each take 64 rows x all 128 columns: every Q/K head row
+// of a tile lies inside one wave.  For row l % 32 (+ 32 i) a lane holds the
+// tile's columns 8 g + 4 (l / 32) + e (g < 16, e < 4): a head row's sum of
+// squares is the lane's own values plus one exchange with lane l ^ 32, and
+// the rotation partner of head column c < d/2, c + d/2, sits in the same
+// lane (group g + d/16, same e).  The product is rounded to bf16 first,
+// exactly where an unfused path would store it, then normalised (fp32) and
+// rotated; 1 / rms of every Q and K head row goes out with q, k and v, and
+// the backward rebuilds the normalised rows from q and k with it.
 
 struct QkvOut {
   uint16_t* q;   // [n_seq][H][S][qs]
   uint16_t* k;
   uint16_t* v;   // [n_seq][H][S][dv]
   float* rho;    // [2][n_seq][H][S]: 1 / rms of each q row, then of each k row
-  int H, S, dv, qs, N, nqk2, n_seq;
+  int H, S, dv, qs, n_seq;
   float eps;
 };
 
-// 64 bf16 columns x 32 rows of a wave's LDS slice: row pitch 128 bytes,
+// The rotation frequencies of a lane's head columns c = 8 idx + 4 (l / 32) +
+// e, in revolutions per position: theta_c / (2 pi) = rev0 * r^(c - c0) with
+// r = base^(-2/d), stepped by one multiplication per column (fp64, so the
+// angles stay exact to ~1e-14 revolutions per position).
+struct RopeRev {
+  double rev0;    // theta_c0 / (2 pi) of the lane's first column c0 = 4 (l / 32)
+  double r1, r5;  // r and r^5: one column on, and from e = 3 to the next group
+};
+
+// 32 rows x 64 bf16 columns of a wave's LDS slice: row pitch 128 bytes,
 // 16-byte chunks XOR-swizzled by row.
 __device__ __forceinline__ int slice64(int row, int chunk) {
   return row * 128 + ((chunk ^ (row & 7)) << 4);
 }
 
-// The rotation frequencies of a lane's columns c = 8 idx + 4 (l / 32) + e,
-// in revolutions per position: theta_c / (2 pi) = rev0 * r^(c - c0) with
-// r = base^(-2/d), stepped by one multiplication per column (fp64, so the
-// angles stay exact to ~1e-14 revolutions per position).
-struct RopeRev {
-  double rev0;  // theta_c0 / (2 pi) of the lane's first column c0 = 4 (l / 32)
-  double r1, r5;  // r and r^5: one column on, and from e = 3 to the next group
-};
-
-// A pass of the epilogue puts 64 of the head's columns through the wave's
-// slice: the 8-column groups 4 ps + s of the lower half (slot s < 4) and
-// their rotation partners, the groups 4 ps + s + d/16 (slot s + 4).  Each
-// rotated pair is written as soon as it is formed; the readback stores
-// every 16-byte chunk at the column its slot stands for.
-template <int D>
-struct QkvPass {
-  static constexpr int G = D / 8, HG = G / 2, PASSES = (HG + 3) / 4;
-  // 8-column group held in slot sl of pass ps (or -1)
-  __device__ static constexpr int group(int ps, int sl) {
-    return sl < 4 ? (4 * ps + sl < HG ? 4 * ps + sl : -1)
-                  : (4 * ps + sl - 4 < HG ? 4 * ps + sl - 4 + HG : -1);
-  }
-  // slots in use in pass ps: 0 .. n/2 - 1 and 4 .. 4 + n/2 - 1
-  __device__ static constexpr int slots(int ps) {
-    return 2 * (HG - 4 * ps < 4 ? HG - 4 * ps : 4);
-  }
-};
-
 template <class C, int D>
 __device__ __forceinline__ void store_qkv_tile(const v16f (&acc)[C::FM][C::FN], float alpha,
                                                uint8_t* slice, const RopeRev& rr,
-                                               const QkvOut& o, int M, int m0, int n0, int wm,
-                                               int wn, int lane) {
-  using P = QkvPass<D>;
-  constexpr int G = P::G, HG = P::HG;
-  static_assert(C::WN == D && C::FN * 4 == G && C::WM == 64, "one head per matrix wave");
-  const int nb = n0 + wn * D;  // the wave's first packed column
-  if (nb >= o.N) return;       // past the last column (ragged last tile)
-  const bool qk = nb < o.nqk2;
-  const int hq = nb / D;  // Q|K heads: 0 .. H-1 Q, H .. 2H-1 K
-  const bool isk = hq >= o.H;
-  const int hh = isk ? hq - o.H : hq;
+                                               const QkvOut& o, const ColMap& cm, int M, int m0,
+                                               int nt, int wm, int lane) {
+  constexpr int HPT = 128 / D, G = D / 8, HG = G / 2, VG0 = HPT * G;  // V groups from VG0 on
+  static_assert(C::WN == 128 && C::FN == 4 && C::WM == 64, "whole tile rows per matrix wave");
+  const bool mixed = nt < cm.n_mixed;
   const int r = lane & 31, hl = lane >> 5;
   const int mp = m0 + wm * C::WM;
   // the part's rows lie inside M and one sequence: rows follow each other
   // in every output (else each row is placed on its own)
   const int b0 = mp / o.S, s0 = mp - b0 * o.S;
   const bool fast = mp + C::WM <= M && (mp + C::WM - 1) / o.S == b0;
-  uint16_t* qkout = isk ? o.k : o.q;
-  // element offset of column 0 of token m's row in its output (q/k, or v
-  // head hv)
-  auto row_off = [&](int m, int hv) -> int64_t {
-    int b = b0, s = s0 + (m - mp);
-    if (!fast) { b = m / o.S; s = m - b * o.S; }
-    return qk ? ((int64_t)b * o.H + hh) * o.S * o.qs + (int64_t)s * o.qs
-              : ((int64_t)b * o.H + hv) * o.S * o.dv + (int64_t)s * o.dv;
+  // element offset of token m's row in head hh of an [n_seq][H][S][w] output
+  auto row_off = [&](int m, int hh, int w) -> int64_t {
+    int b = b0, sp = s0 + (m - mp);
+    if (!fast) { b = m / o.S; sp = m - b * o.S; }
+    return (((int64_t)b * o.H + hh) * o.S + sp) * w;
   };
+  const int hq0 = nt * HPT;  // the tile's first packed head (Q heads, then K heads)
+  auto head_ok = [&](int hs) { return mixed && hq0 + hs < 2 * o.H; };
+  // the whole product of the part, rounded to bf16 (packed pairs), first:
+  // the fp32 accumulators die here, which leaves room for the norm and
+  // rotation (the opaque step keeps the compiler from sinking the
+  // conversions back to their uses)
+  uint2 P[C::FM][16];
+#pragma unroll
+  for (int i = 0; i < C::FM; ++i)
+#pragma unroll
+    for (int g = 0; g < 16; ++g) {
+      const v16f& a = acc[i][g / 4];
+      const int q4 = g % 4;
+      P[i][g] = make_uint2(cvt_bf16x2_rn(a[4 * q4] * alpha, a[4 * q4 + 1] * alpha),
+                           cvt_bf16x2_rn(a[4 * q4 + 2] * alpha, a[4 * q4 + 3] * alpha));
+      asm volatile("" : "+v"(P[i][g].x), "+v"(P[i][g].y));
+    }
 #pragma unroll
   for (int i = 0; i < C::FM; ++i) {
     const int m = mp + 32 * i + r;  // this lane's row
-    // the product of columns 8 idx + 4 hl + 0..3, rounded to bf16 (packed)
-    auto prod = [&](int idx) {
-      const v16f& a = acc[i][idx / 4];
-      const int g = idx % 4;
-      return make_uint2(cvt_bf16x2_rn(a[4 * g] * alpha, a[4 * g + 1] * alpha),
-                        cvt_bf16x2_rn(a[4 * g + 2] * alpha, a[4 * g + 3] * alpha));
-    };
+    // the product of tile columns 8 g + 4 hl + 0..3, rounded to bf16 (packed)
+    auto prod = [&](int g) { return P[i][g]; };
     auto unpack4 = [](uint2 w, float (&f)[4]) {
       f[0] = __uint_as_float(w.x << 16);
       f[1] = __uint_as_float(w.x & 0xffff0000u);
       f[2] = __uint_as_float(w.y << 16);
       f[3] = __uint_as_float(w.y & 0xffff0000u);
     };
-    auto put = [&](int sl, uint2 w) {  // this lane's 8 bytes of slot sl
-      *reinterpret_cast<uint2*>(slice + slice64(r, sl) + 8 * hl) = w;
+    // group g of the row goes to the slice now (first 64 columns) or is
+    // held for the second pass
+    uint2 hold[8];
+    auto emit = [&](int g, uint2 w) {
+      if (g < 8)
+        *reinterpret_cast<uint2*>(slice + slice64(r, g) + 8 * hl) = w;
+      else
+        hold[g - 8] = w;
     };
-    float rho = 0.f;
-    int p = 0;
-    if (qk) {
+#pragma unroll
+    for (int hs = 0; hs < HPT; ++hs) {
+      if (!head_ok(hs)) continue;  // uniform
       float ss = 0.f;
 #pragma unroll
-      for (int idx = 0; idx < G; ++idx) {
+      for (int g = 0; g < G; ++g) {
         float y[4];
-        unpack4(prod(idx), y);
+        unpack4(prod(hs * G + g), y);
 #pragma unroll
         for (int e = 0; e < 4; ++e) ss += y[e] * y[e];
       }
       ss += __shfl_xor(ss, 32);
-      rho = 1.0f / sqrtf(ss / (float)D + o.eps);
-      const int b = m / o.S;
-      p = m - b * o.S;
-      if (hl == 0 && m < M) o.rho[(((int64_t)isk * o.n_seq + b) * o.H + hh) * o.S + p] = rho;
-    }
-    double rev = rr.rev0;
-#pragma unroll
-    for (int ps = 0; ps < P::PASSES; ++ps) {
-      // fill the slots of this pass
-#pragma unroll
-      for (int sl = 0; sl < 4; ++sl) {
-        const int lo = P::group(ps, sl);
-        if (lo < 0) break;
-        if (qk) {
-          float y1[4], y2[4], o1[4], o2[4];
-          unpack4(prod(lo), y1);
-          unpack4(prod(lo + HG), y2);
-#pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            float cn, sn;
-            rope_cs(rev, p, cn, sn);
-            rev *= e < 3 ? rr.r1 : rr.r5;
-            const float u1 = y1[e] * rho, u2 = y2[e] * rho;
-            o1[e] = u1 * cn - u2 * sn;
-            o2[e] = u2 * cn + u1 * sn;
-          }
-          put(sl, make_uint2(cvt_bf16x2_rn(o1[0], o1[1]), cvt_bf16x2_rn(o1[2], o1[3])));
-          put(sl + 4, make_uint2(cvt_bf16x2_rn(o2[0], o2[1]), cvt_bf16x2_rn(o2[2], o2[3])));
-        } else {
-          put(sl, prod(lo));
-          put(sl + 4, prod(lo + HG));
-        }
+      const float rho = 1.0f / sqrtf(ss / (float)D + o.eps);
+      int b = b0, p = s0 + 32 * i + r;  // the row's sequence and position
+      if (!fast) {
+        b = m / o.S;
+        p = m - b * o.S;
       }
-      // read back: CPR chunks per row in use, lane (rq, pc) takes chunk pc
-      // of rows rq + RPI q
-      const int CPR = P::slots(ps);
-      const int RPI = 64 / CPR, NI = CPR / 2;
-      const int rq = lane / CPR, pc = lane - rq * CPR;
-      const int sl = pc < CPR / 2 ? pc : pc - CPR / 2 + 4;  // slots 0.. and 4..
+      // opaque to the compiler: the frequency chain is formed here, per
+      // tile, instead of being hoisted out of the tile loop, where its 24
+      // doubles would stay live through the matrix work
+      double rev = rr.rev0;
+      asm volatile("" : "+v"(rev));
+#pragma unroll
+      for (int idx = 0; idx < HG; ++idx) {
+        float y1[4], y2[4], o1[4], o2[4];
+        unpack4(prod(hs * G + idx), y1);
+        unpack4(prod(hs * G + idx + HG), y2);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          float cn, sn;
+          rope_cs(rev, p, cn, sn);
+          rev *= e < 3 ? rr.r1 : rr.r5;
+          const float u1 = y1[e] * rho, u2 = y2[e] * rho;
+          o1[e] = u1 * cn - u2 * sn;
+          o2[e] = u2 * cn + u1 * sn;
+        }
+        emit(hs * G + idx, make_uint2(cvt_bf16x2_rn(o1[0], o1[1]), cvt_bf16x2_rn(o1[2], o1[3])));
+        emit(hs * G + idx + HG,
+             make_uint2(cvt_bf16x2_rn(o2[0], o2[1]), cvt_bf16x2_rn(o2[2], o2[3])));
+      }
+      const bool isk = hq0 + hs >= o.H;
+      if (hl == 0 && m < M)
+        o.rho[(((int64_t)isk * o.n_seq + b) * o.H + (isk ? hq0 + hs - o.H : hq0 + hs)) * o.S + p] =
+            rho;
+    }
+    // two passes of 64 columns: lane (rq, pc) stores chunk pc of rows
+    // rq + 8 q, q < 4 (8 rows x 128 bytes per store instruction)
+    const int pc = lane & 7, rq = lane >> 3;
+#pragma unroll
+    for (int ps = 0; ps < 2; ++ps) {
+      if (ps == 1) {
+#pragma unroll
+        for (int g = 8; g < 16; ++g) {
+          const bool head = mixed && g < VG0;
+          if (head && !head_ok(g / G)) continue;
+          *reinterpret_cast<uint2*>(slice + slice64(r, g - 8) + 8 * hl) = head ? hold[g - 8] : prod(g);
+        }
+      } else {
+#pragma unroll
+        for (int g = 0; g < 8; ++g)
+          if (!(mixed && g < VG0))
+            *reinterpret_cast<uint2*>(slice + slice64(r, g) + 8 * hl) = prod(g);
+      }
       uint4 val[4];
 #pragma unroll
-      for (int qq = 0; qq < 4; ++qq)
-        if (qq < NI) val[qq] = *reinterpret_cast<const uint4*>(slice + slice64(rq + RPI * qq, sl));
-      const int col = 8 * (sl < 4 ? 4 * ps + sl : 4 * ps + sl - 4 + HG);  // column in the head
-      int hv = 0, jv = col;
-      bool live = true;
-      if (!qk) {  // a V part: columns of one or two V heads
-        const int vc = nb - o.nqk2 + col;
-        hv = vc / o.dv;
-        jv = vc - hv * o.dv;
-        live = nb + col < o.N;
+      for (int q = 0; q < 4; ++q)
+        val[q] = *reinterpret_cast<const uint4*>(slice + slice64(rq + 8 * q, pc));
+      const int g = 8 * ps + pc;  // the chunk's tile group
+      // the chunk's output: a Q/K head's row, or a V head's row
+      uint16_t* dst = nullptr;
+      int w = 0, hh = 0, col = 0;
+      if (mixed && g < VG0) {
+        const int hs = g / G;
+        if (head_ok(hs)) {
+          const int hq = hq0 + hs;
+          const bool isk = hq >= o.H;
+          dst = isk ? o.k : o.q;
+          hh = isk ? hq - o.H : hq;
+          w = o.qs;
+          col = 8 * (g - hs * G);
+        }
+      } else {  // the filler of a mixed tile, or a whole-V tile
+        const int f = mixed ? nt * cm.fill + 8 * (g - VG0)
+                            : cm.n_mixed * cm.fill + (nt - cm.n_mixed) * 128 + 8 * g;
+        if (f < cm.nv) {
+          hh = f / o.dv;
+          dst = o.v;
+          w = o.dv;
+          col = f - hh * o.dv;
+        }
       }
+      if (dst) {
+        const int mt0 = mp + 32 * i + rq;
+        if (fast) {  // rows rq + 8 q follow each other: one pointer, fixed stride
+          uint16_t* at = dst + row_off(mt0, hh, w) + col;
 #pragma unroll
-      for (int qq = 0; qq < 4; ++qq) {
-        if (qq >= NI) break;
-        const int mt = mp + 32 * i + rq + RPI * qq;
-        if (live && mt < M) store_stream((qk ? qkout : o.v) + row_off(mt, hv) + jv, val[qq]);
+          for (int q = 0; q < 4; ++q, at += 8 * w) store_stream(at, val[q]);
+        } else {
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            const int mt = mt0 + 8 * q;
+            if (mt < M) store_stream(dst + row_off(mt, hh, w) + col, val[q]);
+          }
+        }
       }
     }
     // zero padding columns d .. qs - 1 of the fragment's q / k rows
-    if (qk && o.qs > D) {
+    if (o.qs > D) {
       const int pcs = (o.qs - D) / 8;
-      for (int it = lane; it < 32 * pcs; it += 64) {
-        const int rr2 = it / pcs, c = it - rr2 * pcs;
-        const int mt = mp + 32 * i + rr2;
-        if (mt < M) store_stream(qkout + row_off(mt, 0) + D + 8 * c, make_uint4(0, 0, 0, 0));
+#pragma unroll
+      for (int hs = 0; hs < HPT; ++hs) {
+        if (!head_ok(hs)) continue;
+        const int hq = hq0 + hs;
+        const bool isk = hq >= o.H;
+        for (int it = lane; it < 32 * pcs; it += 64) {
+          const int rw = it / pcs, c = it - rw * pcs;
+          const int mt = mp + 32 * i + rw;
+          if (mt < M)
+            store_stream((isk ? o.k : o.q) + row_off(mt, isk ? hq - o.H : hq, o.qs) + D + 8 * c,
+                         make_uint4(0, 0, 0, 0));
+        }
       }
     }
   }
 }
 
 template <int D, bool KTAIL>
-__global__ __launch_bounds__((TileCfg<128, 2 * D>::THREADS), 1) void gemm_qkv_fwd_kernel(
+__global__ __launch_bounds__((TileCfg<256, 128, 4, 1>::THREADS), 1) void gemm_qkv_fwd_kernel(
     Gemm gm, int ntiles, const float* __restrict__ sa, const float* __restrict__ sb, QkvOut o,
     float base) {
-  using C = TileCfg<128, 2 * D>;
+  using C = TileCfg<256, 128, 4, 1>;
   __shared__ __attribute__((aligned(16))) uint8_t lds[kStages * C::STAGE_BYTES];
   __shared__ __attribute__((aligned(16))) uint8_t slices[C::MMA * 4096];
   const int lane = threadIdx.x & 63;
@@ -1003,7 +1139,6 @@ __global__ __launch_bounds__((TileCfg<128, 2 * D>::THREADS), 1) void gemm_qkv_fw
     copy_role<C, KTAIL>(lds, gm, sc, wave - C::MMA, lane);
     return;
   }
-  const int wm = wave / C::NW_, wn = wave % C::NW_;
   const float alpha = sa[0] * sb[0];
   uint8_t* slice = slices + wave * 4096;
   const double r1 = rope_rev(1, D, base) / rope_rev(0, D, base);
@@ -1012,10 +1147,10 @@ __global__ __launch_bounds__((TileCfg<128, 2 * D>::THREADS), 1) void gemm_qkv_fw
   v16f acc[C::FM][C::FN];
   auto done = [&](v16f (&a)[C::FM][C::FN]) {
     const int tile = sc.tile_of(ord++);
-    store_qkv_tile<C, D>(a, alpha, slice, rr, o, gm.M, (tile / gm.n_tiles) * C::BM_,
-                         (tile % gm.n_tiles) * C::BN_, wm, wn, lane);
+    store_qkv_tile<C, D>(a, alpha, slice, rr, o, gm.cm, gm.M, (tile / gm.n_tiles) * C::BM_,
+                         tile % gm.n_tiles, wave, lane);
   };
-  mma_role<C, false, true>(lds, sc, wm, wn, lane, acc, done);
+  mma_role<C, false, true>(lds, sc, wave, 0, lane, acc, done);
 }
 
 template <int BM, int BN, bool KTAIL, class Epi, int FA = kFmtE4M3>
@@ -1161,12 +1296,33 @@ void launch_gemm_fwd(const uint8_t* x8, const uint8_t* w_packed_t, int T, int N,
   launch_bf16out(gm, x_scales, w_scales, EpiFwd{qk_pre, v, N, nqk2, H, d_v, seq_len}, s);
 }
 
-bool fused_forward_width(int d_qk) { return d_qk == 64 || d_qk == 96 || d_qk == 128; }
+// The head-aligned tile order of the forward projection (ColMap).
+static ColMap fwd_colmap(int H, int d_qk, int d_v) {
+  ColMap cm{};
+  cm.d = d_qk;
+  cm.hpt = 128 / d_qk;
+  cm.fill = 128 - cm.hpt * d_qk;
+  cm.n_mixed = (int)ceil_div(2 * H, cm.hpt);
+  cm.nqk2 = 2 * H * d_qk;
+  cm.nv = H * d_v;
+  return cm;
+}
+
+static int fwd_col_tiles(const ColMap& cm) {
+  const int rest = cm.nv - cm.n_mixed * cm.fill;
+  return cm.n_mixed + (rest > 0 ? (int)ceil_div(rest, 128) : 0);
+}
+
+// Head widths with the fused forward; the B offsets of its mapped rows are
+// 32-bit, so the packed weight must stay under 2 GiB.
+bool fused_forward(int d_qk, int64_t N, int D) {
+  return (d_qk == 64 || d_qk == 96 || d_qk == 128) && N * D < ((int64_t)1 << 31);
+}
 
 template <int DQK>
 static void launch_qkv_fwd_t(const Gemm& gm, int ntiles, const float* sa, const float* sb,
                              const QkvOut& o, float base, hipStream_t s) {
-  constexpr int kThr = TileCfg<128, 2 * DQK>::THREADS;
+  constexpr int kThr = TileCfg<256, 128, 4, 1>::THREADS;
   const int blocks = std::min(ntiles, cu_count());
   if (gm.K % kBK)
     gemm_qkv_fwd_kernel<DQK, true><<<blocks, kThr, 0, s>>>(gm, ntiles, sa, sb, o, base);
@@ -1178,11 +1334,12 @@ void launch_gemm_qkv_fwd(const uint8_t* x8, const uint8_t* w_packed_t, int n_seq
                          int D, int H, int d_qk, int d_v, int qs, float eps, float base,
                          const float* x_scales, const float* w_scales, uint16_t* q, uint16_t* k,
                          uint16_t* v, float* rho, hipStream_t s) {
-  const int T = n_seq * seq_len, nqk2 = 2 * H * d_qk, N = nqk2 + H * d_v;
-  const int bn = 2 * d_qk;  // the tile's columns: two heads
-  const Gemm gm{x8, 0, w_packed_t, D, T, N, D, (int)ceil_div(N, bn), kActRows, 0, 0};
-  const int ntiles = (int)ceil_div(T, 128) * gm.n_tiles;
-  const QkvOut o{q, k, v, rho, H, seq_len, d_v, qs, N, nqk2, n_seq, eps};
+  const int T = n_seq * seq_len, N = 2 * H * d_qk + H * d_v;
+  const ColMap cm = fwd_colmap(H, d_qk, d_v);
+  Gemm gm{x8, 0, w_packed_t, D, T, N, D, fwd_col_tiles(cm), kActRows, 0, 0};
+  gm.cm = cm;
+  const int ntiles = (int)ceil_div(T, kBMo) * gm.n_tiles;
+  const QkvOut o{q, k, v, rho, H, seq_len, d_v, qs, n_seq, eps};
   switch (d_qk) {
     case 64: launch_qkv_fwd_t<64>(gm, ntiles, x_scales, w_scales, o, base, s); break;
     case 96: launch_qkv_fwd_t<96>(gm, ntiles, x_scales, w_scales, o, base, s); break;

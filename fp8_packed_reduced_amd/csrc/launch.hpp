@@ -87,9 +87,9 @@ void launch_gemm_fwd(const uint8_t* x8, const uint8_t* w_packed_t, int T, int N,
                      const float* x_scales, const float* w_scales, uint16_t* qk_pre, int nqk2,
                      uint16_t* v, int H, int d_v, int seq_len, hipStream_t s);
 
-// Whether the forward GEMM carries the norm and RoPE in its epilogue at this
-// head width (64, 96, 128).
-bool fused_forward_width(int d_qk);
+// Whether the forward GEMM carries the norm and RoPE in its epilogue: head
+// widths 64, 96 and 128, packed weight (N x D bytes) under 2 GiB.
+bool fused_forward(int d_qk, int64_t N, int D);
 
 // Forward with RMSNorm and RoPE in the GEMM's epilogue: q, k head-major rows
 // of qs >= d_qk elements (columns d_qk .. qs - 1 written as zero), v
