@@ -127,6 +127,11 @@ def load():
     L.qkv_forward.restype = ctypes.c_int
     L.qkv_forward.argtypes = [P(Dims), _I32, _I32, _V, P(_CacheC), _V, _V, _V, _V, _SZ, _V,
                               _SZ, _V]
+    L.qkv_forward_noalloc.restype = ctypes.c_int
+    L.qkv_forward_noalloc.argtypes = [P(Dims), _I32, _I32, _V, P(_CacheC), _V, _V, _V, _V, _SZ,
+                                      _V]
+    L.fpr_noalloc_scratch_bytes.restype = _SZ
+    L.fpr_noalloc_scratch_bytes.argtypes = []
     L.qkv_backward.restype = ctypes.c_int
     L.qkv_backward.argtypes = [P(Dims), _I32, _I32, _V, _V, _V, _V, _V, _V, _SZ, P(_CacheC),
                                _V, _V, _I64, _V, _I64, _V, _I64, _V, _SZ, _V]
@@ -275,6 +280,29 @@ def qkv_forward(dims: Dims, n_seq: int, seq_len: int, x, cache: WeightCache, q=N
     if rc:
         raise FprError(rc, "qkv_forward")
     return q, k, v, saved
+
+
+def qkv_forward_noalloc(dims: Dims, n_seq: int, seq_len: int, x, cache: WeightCache, q, k, v,
+                        saved):
+    """qkv_forward with its workspace in the library's fixed per-device
+    scratch: the caller passes only inputs and outputs (all preallocated)."""
+    T = n_seq * seq_len
+    H, dqk, dv = dims.n_heads, dims.qk_row, dims.d_v
+    _need(x, torch.bfloat16, (T, dims.d_model), "x")
+    _need(q, torch.bfloat16, (n_seq, H, seq_len, dqk), "q")
+    _need(k, torch.bfloat16, (n_seq, H, seq_len, dqk), "k")
+    _need(v, torch.bfloat16, (n_seq, H, seq_len, dv), "v")
+    cc = cache.c()
+    rc = load().qkv_forward_noalloc(ctypes.byref(dims), n_seq, seq_len, x.data_ptr(),
+                                    ctypes.byref(cc), q.data_ptr(), k.data_ptr(), v.data_ptr(),
+                                    saved.data_ptr(), saved.numel(), _stream(x.device))
+    if rc:
+        raise FprError(rc, "qkv_forward_noalloc")
+    return q, k, v, saved
+
+
+def noalloc_scratch_bytes() -> int:
+    return int(load().fpr_noalloc_scratch_bytes())
 
 
 def qkv_backward(dims: Dims, n_seq: int, seq_len: int, q, k, dq, dk, dv, saved,

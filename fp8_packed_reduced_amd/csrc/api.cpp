@@ -5,6 +5,7 @@
 
 #include <algorithm>
 #include <cstdint>
+#include <mutex>
 
 #include "../../include/fpr.h"
 #include "common.hpp"
@@ -240,6 +241,33 @@ int ld_check(int64_t ld, int64_t cols, const void* p) {
   return FPR_OK;
 }
 
+// ---- the fixed scratch of qkv_forward_noalloc
+//
+// For callers that cannot allocate: the forward's workspace (with the norm
+// and RoPE fused into the GEMM, only the x amax partials) lives in this
+// array, one copy per device, held until the process ends.  Host code never
+// uses the array's name as an address: each device's copy is looked up once
+// with hipGetSymbolAddress and that pointer is what the kernels get.
+constexpr size_t kNoAllocScratch = 64 * 1024;
+constexpr int kMaxDevices = 64;
+__device__ __attribute__((aligned(256))) uint8_t scratch[kNoAllocScratch];
+
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices];
+
+// This device's copy of the scratch array, or null on failure.
+void* device_scratch() {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return nullptr;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* ptr = nullptr;
+    if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess || !ptr) return nullptr;
+    g_scratch_ptr[dev] = ptr;
+  }
+  return g_scratch_ptr[dev];
+}
+
 }  // namespace
 
 extern "C" {
@@ -354,6 +382,22 @@ int qkv_forward(const fpr_dims* dims, int32_t n_seq, int32_t seq_len, const uint
   return finish();
 }
 
+int qkv_forward_noalloc(const fpr_dims* dims, int32_t n_seq, int32_t seq_len, const uint16_t* x,
+                        const fpr_weight_cache* cache, uint16_t* q, uint16_t* k, uint16_t* v,
+                        void* saved, size_t saved_bytes, void* stream) {
+  int rc = shape_check(dims);
+  if (rc) return rc;
+  int64_t T;
+  if ((rc = tokens_check(n_seq, seq_len, &T))) return rc;
+  if (make_plan(dims, T).fwd_total > kNoAllocScratch) return FPR_ERR_SCRATCH;
+  void* ws = device_scratch();
+  if (!ws) return FPR_ERR_LAUNCH;
+  return qkv_forward(dims, n_seq, seq_len, x, cache, q, k, v, saved, saved_bytes, ws,
+                     kNoAllocScratch, stream);
+}
+
+size_t fpr_noalloc_scratch_bytes(void) { return kNoAllocScratch; }
+
 int qkv_backward(const fpr_dims* dims, int32_t n_seq, int32_t seq_len, const uint16_t* q,
                  const uint16_t* k, const uint16_t* dq, const uint16_t* dk, const uint16_t* dv,
                  const void* saved, size_t saved_bytes,
@@ -417,6 +461,9 @@ const char* fpr_status_string(int code) {
     case FPR_ERR_ALIGN: return "misaligned pointer or leading dimension";
     case FPR_ERR_WORKSPACE: return "workspace or saved buffer too small";
     case FPR_ERR_LAUNCH: return "kernel launch failed";
+    case FPR_ERR_SCRATCH:
+      return "the call needs more workspace than the library's fixed scratch "
+             "(fpr_noalloc_scratch_bytes)";
     default: return "unknown status code";
   }
 }

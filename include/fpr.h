@@ -66,7 +66,9 @@ enum {
     FPR_ERR_SHAPE = 2,      /* dimensions outside the supported set */
     FPR_ERR_ALIGN = 3,      /* pointer or leading dimension misaligned */
     FPR_ERR_WORKSPACE = 4,  /* workspace or saved buffer too small */
-    FPR_ERR_LAUNCH = 5      /* a kernel launch failed */
+    FPR_ERR_LAUNCH = 5,     /* a kernel launch failed */
+    FPR_ERR_SCRATCH = 6     /* qkv_forward_noalloc: the workspace the call
+                               needs exceeds the fixed scratch */
 };
 
 /* Bits of *cache->status (device int32). */
@@ -167,6 +169,27 @@ FPR_API int qkv_forward(const fpr_dims* dims, int32_t n_seq, int32_t seq_len,
                 void* saved, size_t saved_bytes,
                 void* workspace, size_t workspace_bytes,
                 void* stream);
+
+/* For callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc): the same
+ * as qkv_forward, with the workspace taken from a fixed device array inside
+ * the library, fpr_noalloc_scratch_bytes() = 64 KiB per device, held until
+ * the process ends.  No allocation happens in the call.  With the norm and
+ * RoPE fused into the GEMM (d_qk 64, 96, 128) the forward needs only the x
+ * amax partials (at most 1 KiB); a call that would need more (other head
+ * widths, whose pre-norm rows pass through the workspace) returns
+ * FPR_ERR_SCRATCH before anything is launched.  Every call on one device
+ * shares that device's array, and nothing in it needs to start at zero:
+ * calls that overlap on one device (other streams, other threads) race on
+ * it and must be ordered by the caller.  The first call on a device looks
+ * up the array's address there (hipGetSymbolAddress). */
+FPR_API int qkv_forward_noalloc(const fpr_dims* dims, int32_t n_seq, int32_t seq_len,
+                const uint16_t* x, const fpr_weight_cache* cache,
+                uint16_t* q, uint16_t* k, uint16_t* v,
+                void* saved, size_t saved_bytes, void* stream);
+
+/* Bytes of the fixed scratch qkv_forward_noalloc uses. */
+FPR_API size_t fpr_noalloc_scratch_bytes(void);
 
 /* Step 3, the backward of step 2 ("Reduced-width QK and packed FP8
  * attention", Changes: the FP8 coverage extends to the backward GEMMs;

@@ -22,14 +22,14 @@ def test_library_exports_every_declared_call():
                           "fpr_e4m3_encode", "fpr_trace_set", "fpr_mlp_workspace_bytes",
                           "fpr_mlp_saved_bytes", "fpr_mlp_get_layout",
                           "mlp_pack_quantize_weights", "mlp_forward", "mlp_backward",
-                          "fpr_e5m2_encode"}
+                          "fpr_e5m2_encode", "qkv_forward_noalloc", "fpr_noalloc_scratch_bytes"}
     lib = B.load()
     for n in names:
         assert hasattr(lib, n), n
 
 
 def test_status_strings():
-    for code in range(6):
+    for code in range(7):
         assert B.status_string(code)
     assert "unknown" in B.status_string(99)
 
