@@ -41,6 +41,14 @@ __device__ inline uint32_t pack_bf16x2(float a, float b) {
   return f32_to_bf16(a) | (f32_to_bf16(b) << 16);
 }
 
+// Sum of the products of two packed bf16 pairs, added to c in fp32
+// (v_dot2_f32_bf16: each bf16 product is exact in fp32).
+typedef __bf16 v2bf16_t __attribute__((ext_vector_type(2)));
+__device__ inline float dot2_bf16(uint32_t a, uint32_t b, float c) {
+  return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(v2bf16_t, a),
+                                        __builtin_bit_cast(v2bf16_t, b), c, false);
+}
+
 // ------------------------------------------------------------------ e4m3
 //
 // OCP E4M3 through the gfx950 converter (round to nearest even).  The

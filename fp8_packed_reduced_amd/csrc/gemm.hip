@@ -998,13 +998,11 @@ __device__ __forceinline__ void store_qkv_tile(const v16f (&acc)[C::FM][C::FN], 
 #pragma unroll
     for (int hs = 0; hs < HPT; ++hs) {
       if (!head_ok(hs)) continue;  // uniform
-      float ss = 0.f;
+      float ss = 0.f;  // the row's sum of squares, bf16 pairs at a time
 #pragma unroll
       for (int g = 0; g < G; ++g) {
-        float y[4];
-        unpack4(prod(hs * G + g), y);
-#pragma unroll
-        for (int e = 0; e < 4; ++e) ss += y[e] * y[e];
+        const uint2 w = prod(hs * G + g);
+        ss = dot2_bf16(w.y, w.y, dot2_bf16(w.x, w.x, ss));
       }
       ss += __shfl_xor(ss, 32);
       const float rho = 1.0f / sqrtf(ss / (float)D + o.eps);
