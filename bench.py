@@ -110,6 +110,65 @@ def mlp_stage_work(w: dict, dw_splits: tuple[int, int]) -> dict:
     }
 
 
+def measured_ceilings(B, dev, reps: int = 5) -> dict:
+    """The device's practical ceilings, taken in this run with the library's
+    probe kernels and HIP events: a streaming copy and a streaming read of
+    1 GiB (four times the last-level cache), and the bare FP8 MFMA loop
+    (2 waves per SIMD, 4 independent accumulators each).  Medians of reps."""
+    import torch
+    stream = torch.cuda.current_stream(dev)
+
+    def timed(launch) -> float:
+        ts = []
+        for _ in range(reps + 1):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            launch()
+            e1.record(stream)
+            torch.cuda.synchronize(dev)
+            ts.append(e0.elapsed_time(e1) / 1e3)
+        return sorted(ts[1:])[reps // 2]
+
+    nbytes = 1 << 30
+    src = torch.ones(nbytes, dtype=torch.uint8, device=dev)
+    dst = torch.empty(nbytes, dtype=torch.uint8, device=dev)
+    words = torch.empty(8192, dtype=torch.int32, device=dev)
+    blocks = 8 * torch.cuda.get_device_properties(dev).multi_processor_count
+    t_copy = timed(lambda: B.probe_copy(src, dst, blocks))
+    t_read = timed(lambda: B.probe_read(src, words, blocks))
+    del src, dst
+    mb, iters = 4 * torch.cuda.get_device_properties(dev).multi_processor_count, 2000
+    sink = torch.empty(mb * 8, dtype=torch.float32, device=dev)
+    flop = B.probe_mfma(mb, iters, sink)
+    t_mfma = timed(lambda: B.probe_mfma(mb, iters, sink))
+    return {"copy_GBps": round(2 * nbytes / t_copy / 1e9, 1),
+            "read_GBps": round(nbytes / t_read / 1e9, 1),
+            "mfma_TFLOPs": round(flop / t_mfma / 1e12, 1),
+            "how": "library probe kernels in this run: streaming copy and read of 1 GiB, "
+                   "bare FP8 32x32x64 MFMA loop; HIP events, median of 5"}
+
+
+def ceiling_of(stage: str, kind: str, ceil: dict) -> float:
+    """The measured ceiling a stage is held to: the MFMA loop for the GEMMs,
+    the streaming read for the read-only amax passes, the copy otherwise."""
+    if kind == "mfma":
+        return ceil["mfma_TFLOPs"] * 1e12
+    if "amax" in stage:
+        return ceil["read_GBps"] * 1e9
+    return ceil["copy_GBps"] * 1e9
+
+
+def cpu_model() -> str:
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    import platform
+    return platform.processor() or "unknown"
+
+
 def source_hash(stage: str) -> str:
     path = os.path.join(ROOT, "fp8_packed_reduced_amd", "csrc", STAGE_SOURCES[stage])
     return hashlib.sha256(open(path, "rb").read()).hexdigest()[:12]
@@ -201,7 +260,7 @@ def cpu_baseline(T: int, oracle_step, seed: int, target_s: float, c1_step=None,
         except Exception:
             single = None
     return {"value": round(reps * tokens / dt, 1), "unit": "tokens/s", "cores": cores,
-            "c1_single_thread_s": single,
+            "cpu_model": cpu_model(), "c1_single_thread_s": single,
             "kind": "oracle",
             "sample": f"{what} of the first {tokens} tokens (one sequence, "
                       f"positions 0..{tokens - 1}) of the same workload and seed{runs}; "
@@ -387,6 +446,7 @@ def main():
     torch.cuda.synchronize()
     del calib
 
+    ceil = measured_ceilings(B, dev)
     for _ in range(max(args.warmup, 1)):
         step()
     torch.cuda.synchronize()
@@ -452,7 +512,8 @@ def main():
         kernels[name] = {"us": round(ms * 1e3, 2),
                          ("TFLOP/s" if kd == "mfma" else "GB/s"):
                              round(rate / (1e12 if kd == "mfma" else 1e9), 1),
-                         "frac": round(rate / (PEAK_FP8_FLOPS if kd == "mfma" else PEAK_HBM_BYTES), 4)}
+                         "frac": round(rate / (PEAK_FP8_FLOPS if kd == "mfma" else PEAK_HBM_BYTES), 4),
+                         "frac_measured": round(rate / ceiling_of(name, kd, ceil), 4)}
         if n_launch > 1:
             kernels[name]["launches"] = n_launch
 
@@ -480,7 +541,12 @@ def main():
         "roofline": {"kernel": dominant, "bound": kind, "achieved": round(achieved, 1),
                      "peak": peak, "unit": unit, "frac": round(achieved / peak, 4),
                      "traffic": traffic, "launches": len(dom_ms),
-                     "avg_us": round(dom_avg_s * 1e6, 2)},
+                     "avg_us": round(dom_avg_s * 1e6, 2),
+                     "measured_ceiling": round(ceiling_of(dominant, kind, ceil) /
+                                               (1e12 if kind == "mfma" else 1e9), 1),
+                     "frac_measured": round(amount / dom_avg_s / ceiling_of(dominant, kind, ceil),
+                                            4)},
+        "measured_ceilings": ceil,
         "kernels": kernels,
     }
     if not args.no_extras:

@@ -139,6 +139,12 @@ def load():
     L.fpr_trace_set.argtypes = [ctypes.POINTER(_TraceC)]
     L.fpr_e4m3_encode.restype = ctypes.c_int
     L.fpr_e4m3_encode.argtypes = [_V, _I64, ctypes.c_float, _V, _V]
+    L.fpr_probe_copy.restype = ctypes.c_int
+    L.fpr_probe_copy.argtypes = [_V, _V, _I64, ctypes.c_int, _V]
+    L.fpr_probe_read.restype = ctypes.c_int
+    L.fpr_probe_read.argtypes = [_V, _I64, _V, ctypes.c_int, _V]
+    L.fpr_probe_mfma.restype = _I64
+    L.fpr_probe_mfma.argtypes = [ctypes.c_int, ctypes.c_int, _V, _V]
     L.fpr_e5m2_encode.restype = ctypes.c_int
     L.fpr_e5m2_encode.argtypes = [_V, _I64, ctypes.c_float, _V, _V]
     L.fpr_mlp_workspace_bytes.restype = _SZ
@@ -350,6 +356,30 @@ def e4m3_encode(values: torch.Tensor, inv_scale: float = 1.0, e5m2: bool = False
     if rc:
         raise FprError(rc, name)
     return out
+
+
+def probe_copy(src: torch.Tensor, dst: torch.Tensor, blocks: int):
+    """Measurement hook: streaming copy of src's bytes into dst."""
+    rc = load().fpr_probe_copy(src.data_ptr(), dst.data_ptr(), src.numel() * src.element_size(),
+                               blocks, _stream(src.device))
+    if rc:
+        raise FprError(rc, "fpr_probe_copy")
+
+
+def probe_read(src: torch.Tensor, out: torch.Tensor, blocks: int):
+    """Measurement hook: streaming read of src's bytes (one word per block to out)."""
+    rc = load().fpr_probe_read(src.data_ptr(), src.numel() * src.element_size(), out.data_ptr(),
+                               blocks, _stream(src.device))
+    if rc:
+        raise FprError(rc, "fpr_probe_read")
+
+
+def probe_mfma(blocks: int, iters: int, out: torch.Tensor) -> int:
+    """Measurement hook: the bare FP8 MFMA loop; returns the FLOP it does."""
+    flop = load().fpr_probe_mfma(blocks, iters, out.data_ptr(), _stream(out.device))
+    if flop < 0:
+        raise FprError(-flop, "fpr_probe_mfma")
+    return int(flop)
 
 
 def view_bytes(buf: torch.Tensor, offset: int, shape, dtype) -> torch.Tensor:

@@ -18,7 +18,7 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 OUT = os.path.join(HERE, "libfpr.so")
 OBJ = os.path.join(ROOT, "_build", "fpr")
-SOURCES = ["quantize.hip", "gemm.hip", "epilogue.hip", "api.cpp"]
+SOURCES = ["quantize.hip", "gemm.hip", "epilogue.hip", "probe.hip", "api.cpp"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-Wall", "-fvisibility=hidden",
          "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",

@@ -652,6 +652,29 @@ int fpr_e4m3_encode(const float* in, int64_t n, float inv_scale, uint8_t* out, v
   return finish();
 }
 
+int fpr_probe_copy(const void* src, void* dst, int64_t bytes, int blocks, void* stream) {
+  if (!src || !dst || bytes <= 0 || blocks <= 0) return FPR_ERR_ARG;
+  if (!al16(src) || !al16(dst) || bytes % 16) return FPR_ERR_ALIGN;
+  (void)hipGetLastError();
+  fpr::launch_probe_copy(src, dst, bytes, blocks, static_cast<hipStream_t>(stream));
+  return finish();
+}
+
+int fpr_probe_read(const void* src, int64_t bytes, uint32_t* out, int blocks, void* stream) {
+  if (!src || !out || bytes <= 0 || blocks <= 0) return FPR_ERR_ARG;
+  if (!al16(src) || bytes % 16) return FPR_ERR_ALIGN;
+  (void)hipGetLastError();
+  fpr::launch_probe_read(src, bytes, out, blocks, static_cast<hipStream_t>(stream));
+  return finish();
+}
+
+int64_t fpr_probe_mfma(int blocks, int iters, float* out, void* stream) {
+  if (!out || blocks <= 0 || iters <= 0) return -FPR_ERR_ARG;
+  (void)hipGetLastError();
+  fpr::launch_probe_mfma(blocks, iters, out, static_cast<hipStream_t>(stream));
+  return finish() == FPR_OK ? fpr::probe_mfma_flop(blocks, iters) : -FPR_ERR_LAUNCH;
+}
+
 int fpr_e5m2_encode(const float* in, int64_t n, float inv_scale, uint8_t* out, void* stream) {
   if (!in || !out || n <= 0) return FPR_ERR_ARG;
   if (!al16(in) || !al16(out) || n % 16) return FPR_ERR_ALIGN;

@@ -928,8 +928,9 @@ struct QkvOut {
 // r = base^(-2/d), stepped by one multiplication per column (fp64, so the
 // angles stay exact to ~1e-14 revolutions per position).
 struct RopeRev {
-  double rev0;    // theta_c0 / (2 pi) of the lane's first column c0 = 4 (l / 32)
-  double r1, r5;  // r and r^5: one column on, and from e = 3 to the next group
+  double rev0;        // theta_c0 / (2 pi) of the lane's first column c0 = 4 (l / 32)
+  double r1, r5, r8;  // r, r^5 and r^8: one column on, from e = 3 to the next
+                      // group, and one group on
 };
 
 // 32 rows x 64 bf16 columns of a wave's LDS slice: row pitch 128 bytes,
@@ -986,17 +987,16 @@ __device__ __forceinline__ void store_qkv_tile(const v16f (&acc)[C::FM][C::FN], 
       f[2] = __uint_as_float(w.y << 16);
       f[3] = __uint_as_float(w.y & 0xffff0000u);
     };
-    // group g of the row goes to the slice now (first 64 columns) or is
-    // held for the second pass
-    uint2 hold[8];
-    auto emit = [&](int g, uint2 w) {
-      if (g < 8)
-        *reinterpret_cast<uint2*>(slice + slice64(r, g) + 8 * hl) = w;
-      else
-        hold[g - 8] = w;
-    };
+    // a head's 1 / rms and the row's position
+    float rho[HPT];
+    int b = b0, p = s0 + 32 * i + r;
+    if (!fast) {
+      b = m / o.S;
+      p = m - b * o.S;
+    }
 #pragma unroll
     for (int hs = 0; hs < HPT; ++hs) {
+      rho[hs] = 0.f;
       if (!head_ok(hs)) continue;  // uniform
       float ss = 0.f;  // the row's sum of squares, bf16 pairs at a time
 #pragma unroll
@@ -1005,57 +1005,76 @@ __device__ __forceinline__ void store_qkv_tile(const v16f (&acc)[C::FM][C::FN], 
         ss = dot2_bf16(w.y, w.y, dot2_bf16(w.x, w.x, ss));
       }
       ss += __shfl_xor(ss, 32);
-      const float rho = 1.0f / sqrtf(ss / (float)D + o.eps);
-      int b = b0, p = s0 + 32 * i + r;  // the row's sequence and position
-      if (!fast) {
-        b = m / o.S;
-        p = m - b * o.S;
-      }
-      // opaque to the compiler: the frequency chain is formed here, per
-      // tile, instead of being hoisted out of the tile loop, where its 24
-      // doubles would stay live through the matrix work
-      double rev = rr.rev0;
-      asm volatile("" : "+v"(rev));
-#pragma unroll
-      for (int idx = 0; idx < HG; ++idx) {
-        float y1[4], y2[4], o1[4], o2[4];
-        unpack4(prod(hs * G + idx), y1);
-        unpack4(prod(hs * G + idx + HG), y2);
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          float cn, sn;
-          rope_cs(rev, p, cn, sn);
-          rev *= e < 3 ? rr.r1 : rr.r5;
-          const float u1 = y1[e] * rho, u2 = y2[e] * rho;
-          o1[e] = u1 * cn - u2 * sn;
-          o2[e] = u2 * cn + u1 * sn;
-        }
-        emit(hs * G + idx, make_uint2(cvt_bf16x2_rn(o1[0], o1[1]), cvt_bf16x2_rn(o1[2], o1[3])));
-        emit(hs * G + idx + HG,
-             make_uint2(cvt_bf16x2_rn(o2[0], o2[1]), cvt_bf16x2_rn(o2[2], o2[3])));
-      }
+      rho[hs] = 1.0f / sqrtf(ss / (float)D + o.eps);
       const bool isk = hq0 + hs >= o.H;
       if (hl == 0 && m < M)
         o.rho[(((int64_t)isk * o.n_seq + b) * o.H + (isk ? hq0 + hs - o.H : hq0 + hs)) * o.S + p] =
-            rho;
+            rho[hs];
     }
+    // The rotated pairs (idx, idx + d/16) of head hs whose groups fall in
+    // pass ps (groups 8 ps .. 8 ps + 7) go into the slice.  A pair with a
+    // half in each pass is formed in the first and its upper half held in
+    // registers (d = 96: 4 groups), or, for d = 128, where every pair
+    // straddles the passes, formed again in the second.
+    constexpr bool kHold = D != 128;
+    uint2 hold[8];
+    auto put = [&](int g, uint2 w) {
+      *reinterpret_cast<uint2*>(slice + slice64(r, g & 7) + 8 * hl) = w;
+    };
+    auto rotate_pairs = [&](int ps) {
+#pragma unroll
+      for (int hs = 0; hs < HPT; ++hs) {
+        if (!head_ok(hs)) continue;  // uniform
+        // opaque to the compiler: the frequency chain is formed here, per
+        // tile, instead of being hoisted out of the tile loop, where its
+        // doubles would stay live through the matrix work
+        double rev = rr.rev0;
+        asm volatile("" : "+v"(rev));
+#pragma unroll
+        for (int idx = 0; idx < HG; ++idx) {
+          const int glo = hs * G + idx, ghi = glo + HG;
+          const bool straddle = glo / 8 != ghi / 8;
+          const bool want_lo = glo / 8 == ps, want_hi = ghi / 8 == ps && !(kHold && straddle);
+          const bool keep_hi = kHold && straddle && ps == 0;
+          if (!want_lo && !want_hi && !keep_hi) {
+            rev *= rr.r8;  // the next group's first column
+            continue;
+          }
+          float y1[4], y2[4], o1[4], o2[4];
+          unpack4(prod(glo), y1);
+          unpack4(prod(ghi), y2);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            float cn, sn;
+            rope_cs(rev, p, cn, sn);
+            rev *= e < 3 ? rr.r1 : rr.r5;
+            const float u1 = y1[e] * rho[hs], u2 = y2[e] * rho[hs];
+            o1[e] = u1 * cn - u2 * sn;
+            o2[e] = u2 * cn + u1 * sn;
+          }
+          const uint2 w1 = make_uint2(cvt_bf16x2_rn(o1[0], o1[1]), cvt_bf16x2_rn(o1[2], o1[3]));
+          const uint2 w2 = make_uint2(cvt_bf16x2_rn(o2[0], o2[1]), cvt_bf16x2_rn(o2[2], o2[3]));
+          if (want_lo) put(glo, w1);
+          if (want_hi) put(ghi, w2);
+          if (keep_hi) hold[ghi - 8] = w2;
+        }
+      }
+    };
     // two passes of 64 columns: lane (rq, pc) stores chunk pc of rows
     // rq + 8 q, q < 4 (8 rows x 128 bytes per store instruction)
     const int pc = lane & 7, rq = lane >> 3;
 #pragma unroll
     for (int ps = 0; ps < 2; ++ps) {
-      if (ps == 1) {
+      rotate_pairs(ps);
 #pragma unroll
-        for (int g = 8; g < 16; ++g) {
-          const bool head = mixed && g < VG0;
-          if (head && !head_ok(g / G)) continue;
-          *reinterpret_cast<uint2*>(slice + slice64(r, g - 8) + 8 * hl) = head ? hold[g - 8] : prod(g);
+      for (int g = 8 * ps; g < 8 * ps + 8; ++g) {
+        const bool head = mixed && g < VG0;
+        if (!head) {
+          put(g, prod(g));
+        } else if (kHold && ps == 1 && g % G >= HG && (g - HG) / 8 == 0) {
+          // the upper half of a pair formed (and held) in the first pass
+          if (head_ok(g / G)) put(g, hold[g - 8]);
         }
-      } else {
-#pragma unroll
-        for (int g = 0; g < 8; ++g)
-          if (!(mixed && g < VG0))
-            *reinterpret_cast<uint2*>(slice + slice64(r, g) + 8 * hl) = prod(g);
       }
       uint4 val[4];
 #pragma unroll
@@ -1140,7 +1159,8 @@ __global__ __launch_bounds__((TileCfg<256, 128, 4, 1>::THREADS), 1) void gemm_qk
   const float alpha = sa[0] * sb[0];
   uint8_t* slice = slices + wave * 4096;
   const double r1 = rope_rev(1, D, base) / rope_rev(0, D, base);
-  const RopeRev rr{rope_rev(4 * (lane >> 5), D, base), r1, r1 * r1 * r1 * r1 * r1};
+  const double r4 = r1 * r1 * r1 * r1;
+  const RopeRev rr{rope_rev(4 * (lane >> 5), D, base), r1, r4 * r1, r4 * r4};
   int ord = 0;
   v16f acc[C::FM][C::FN];
   auto done = [&](v16f (&a)[C::FM][C::FN]) {

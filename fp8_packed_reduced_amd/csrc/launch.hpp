@@ -165,4 +165,15 @@ void launch_norm_rope_bwd(const uint16_t* dq, const uint16_t* dk, const uint16_t
                           int d_qk, int qs, float base, uint16_t* dqkv, uint32_t* partials,
                           hipStream_t s);
 
+// ---- probe.hip: measured ceilings -------------------------------------------
+
+// Streaming copy of `bytes` (a multiple of 16) from src to dst.
+void launch_probe_copy(const void* src, void* dst, int64_t bytes, int blocks, hipStream_t s);
+// Streaming read of `bytes` (a multiple of 16); one word per block to out.
+void launch_probe_read(const void* src, int64_t bytes, uint32_t* out, int blocks, hipStream_t s);
+// `blocks` blocks of 8 waves, each `iters` rounds of 4 independent FP8 MFMAs;
+// one float per wave to out (blocks * 8).
+void launch_probe_mfma(int blocks, int iters, float* out, hipStream_t s);
+int64_t probe_mfma_flop(int blocks, int iters);
+
 }  // namespace fpr

@@ -27,9 +27,14 @@ import csv
 import statistics
 import sys
 
-# Launch order of one step of each part (a stage may launch more than once)
-QKV_ORDER = ["amax_w", "quantize_w", "amax_x", "quantize_x", "gemm_fwd", "norm_rope_fwd",
+# Launch order of one step of each part (a stage may launch more than once).
+# Head widths 64, 96 and 128 run the norm/RoPE inside the forward GEMM
+# (gemm_qkv_fwd_kernel); other widths launch norm_rope_fwd after it.
+QKV_ORDER = ["amax_w", "quantize_w", "amax_x", "quantize_x", "gemm_fwd",
              "amax_dv", "norm_rope_bwd", "quantize_g", "gemm_dx", "gemm_dw", "dw_reduce"]
+QKV_ORDER_UNFUSED = ["amax_w", "quantize_w", "amax_x", "quantize_x", "gemm_fwd", "norm_rope_fwd",
+                     "amax_dv", "norm_rope_bwd", "quantize_g", "gemm_dx", "gemm_dw", "dw_reduce"]
+FUSED_WIDTHS = (64, 96, 128)
 MLP_ORDER = ["mlp_amax_w", "mlp_quantize_w", "mlp_amax_w", "mlp_quantize_w", "mlp_amax_x",
              "mlp_quantize_x", "mlp_gemm_up", "mlp_quantize_h", "mlp_gemm_down", "mlp_amax_dy",
              "mlp_quantize_dy", "mlp_gemm_dh", "mlp_quantize_dpre", "mlp_gemm_dx",
@@ -37,7 +42,7 @@ MLP_ORDER = ["mlp_amax_w", "mlp_quantize_w", "mlp_amax_w", "mlp_quantize_w", "ml
 KERNEL_OF_STAGE = {
     "amax_w": "amax_w_kernel", "quantize_w": "quantize_w_kernel",
     "amax_x": "amax_bf16_kernel", "quantize_x": "quantize_act_kernel",
-    "gemm_fwd": "gemm_bf16out_kernel", "norm_rope_fwd": "norm_rope_fwd",
+    "gemm_fwd": "gemm_", "norm_rope_fwd": "norm_rope_fwd",
     "norm_rope_bwd": "norm_rope_bwd", "amax_dv": "amax_bf16_kernel",
     "quantize_g": "quantize_act_kernel",
     "gemm_dx": "gemm_bf16out_kernel", "gemm_dw": "gemm_dw_part_kernel",
@@ -55,8 +60,13 @@ KERNEL_OF_STAGE = {
 
 def step_order(workload: str) -> list[str]:
     import bench
+    from fp8_packed_reduced_amd import inputs
     qkv, mlp = bench.BENCH_WORKLOADS.get(workload, (workload, None))
-    return (QKV_ORDER if qkv else []) + (MLP_ORDER if mlp else [])
+    order = []
+    if qkv:
+        fused = inputs.WORKLOADS[qkv]["d_qk"] in FUSED_WIDTHS
+        order += QKV_ORDER if fused else QKV_ORDER_UNFUSED
+    return order + (MLP_ORDER if mlp else [])
 CALIB_KERNEL = "encode_kernel"
 
 
@@ -102,10 +112,11 @@ def _dispatches(path: str, counter: str):
 
 
 def _by_stage(path: str, ds, order: list[str]):
-    """Stage -> [(dispatch id, value)] of the step launches (calibration and
-    torch's own launches left out), refusing anything but whole steps in the
-    library's launch order."""
-    step_kernels = [(d, n, v) for d, n, v in ds if "fpr::" in n and CALIB_KERNEL not in n]
+    """Stage -> [(dispatch id, value)] of the step launches (calibration,
+    ceiling probes and torch's own launches left out), refusing anything but
+    whole steps in the library's launch order."""
+    step_kernels = [(d, n, v) for d, n, v in ds
+                    if "fpr::" in n and CALIB_KERNEL not in n and "probe_" not in n]
     if len(step_kernels) % len(order):
         raise SystemExit(f"{path}: {len(step_kernels)} library dispatches is not a whole "
                          f"number of {len(order)}-kernel steps")

@@ -392,6 +392,23 @@ FPR_API int fpr_e4m3_encode(const float* in, int64_t n, float inv_scale, uint8_t
 FPR_API int fpr_e5m2_encode(const float* in, int64_t n, float inv_scale, uint8_t* out,
                     void* stream);
 
+/* ---------------------------------------------------------------------
+ * Measurement hooks: the device's practical ceilings, for holding the
+ * kernels above against measured limits next to the published peaks.
+ * All pointers are device pointers, 16-byte aligned; `blocks` is the grid.
+ *   fpr_probe_copy: streaming copy of `bytes` (multiple of 16) src -> dst
+ *                   (counts 2 * bytes of HBM traffic);
+ *   fpr_probe_read: streaming read of `bytes`, one word per block to out;
+ *   fpr_probe_mfma: blocks of 8 waves, each `iters` rounds of 4 independent
+ *                   FP8 32x32x64 MFMAs on register operands, one float per
+ *                   wave to out[blocks * 8]; returns the FLOP it does (or
+ *                   -FPR_ERR_* on an error).
+ * ------------------------------------------------------------------- */
+FPR_API int fpr_probe_copy(const void* src, void* dst, int64_t bytes, int blocks, void* stream);
+FPR_API int fpr_probe_read(const void* src, int64_t bytes, uint32_t* out, int blocks,
+                           void* stream);
+FPR_API int64_t fpr_probe_mfma(int blocks, int iters, float* out, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -22,7 +22,8 @@ def test_library_exports_every_declared_call():
                           "fpr_e4m3_encode", "fpr_trace_set", "fpr_mlp_workspace_bytes",
                           "fpr_mlp_saved_bytes", "fpr_mlp_get_layout",
                           "mlp_pack_quantize_weights", "mlp_forward", "mlp_backward",
-                          "fpr_e5m2_encode", "qkv_forward_noalloc", "fpr_noalloc_scratch_bytes"}
+                          "fpr_e5m2_encode", "qkv_forward_noalloc", "fpr_noalloc_scratch_bytes",
+                          "fpr_probe_copy", "fpr_probe_read", "fpr_probe_mfma"}
     lib = B.load()
     for n in names:
         assert hasattr(lib, n), n
@@ -206,6 +207,11 @@ def test_argument_errors_are_reported_before_any_launch():
                           ws, 96, ws, 128, ws, 1 << 30, None) == 3
     assert L.qkv_backward(by(d), 1, 256, ws, ws, ws, ws, ws, ws, 1 << 30, by(cc), ws, ws, 96, ws,
                           96, ws, 128, ws, 100, None) == 4
+    # measurement hooks
+    assert L.fpr_probe_copy(ws, ws + 8, 1024, 4, None) == 3
+    assert L.fpr_probe_copy(ws, ws, 1000, 4, None) == 3
+    assert L.fpr_probe_read(None, 1024, ws, 4, None) == 1
+    assert L.fpr_probe_mfma(0, 10, ws, None) == -1
     # encoder hook
     assert L.fpr_e4m3_encode(ws, 15, 1.0, ws, None) == 3
     assert L.fpr_e4m3_encode(None, 16, 1.0, ws, None) == 1
