@@ -15,17 +15,23 @@ namespace fpr {
 
 typedef float v16f_p __attribute__((ext_vector_type(16)));
 
+typedef unsigned v4u_p __attribute__((ext_vector_type(4)));
+
+// Eight 16-byte loads in flight per thread, then eight streaming stores.
 __global__ __launch_bounds__(kThreads) void probe_copy_kernel(const uint4* __restrict__ src,
                                                               uint4* __restrict__ dst,
                                                               int64_t n) {
   const int64_t stride = (int64_t)gridDim.x * kThreads;
   int64_t i = (int64_t)blockIdx.x * kThreads + threadIdx.x;
-  for (; i + 3 * stride < n; i += 4 * stride) {
-    const uint4 a = src[i], b = src[i + stride], c = src[i + 2 * stride], d = src[i + 3 * stride];
-    dst[i] = a;
-    dst[i + stride] = b;
-    dst[i + 2 * stride] = c;
-    dst[i + 3 * stride] = d;
+  for (; i + 7 * stride < n; i += 8 * stride) {
+    uint4 a[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) a[j] = src[i + j * stride];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const v4u_p x = {a[j].x, a[j].y, a[j].z, a[j].w};
+      __builtin_nontemporal_store(x, reinterpret_cast<v4u_p*>(dst + i + j * stride));
+    }
   }
   for (; i < n; i += stride) dst[i] = src[i];
 }
