@@ -217,15 +217,14 @@ __device__ __forceinline__ uint32_t qc_bwd_finish(const QcBwdRow<D>& r, const fl
   using Q = QuadChunks<D>;
   constexpr int h = Q::h, M = Q::M, HC = Q::HC;
   if (!r.ok) return 0;
-  // <q, dq> over the row
+  // <q, dq> over the row, bf16 pairs at a time
   float sd = 0.f;
 #pragma unroll
   for (int m = 0; m < M; ++m) {
-    float x[8], gx[8];
-    unpack8(r.q[m], x);
-    unpack8(r.g[m], gx);
-#pragma unroll
-    for (int e = 0; e < 8; ++e) sd += x[e] * gx[e];
+    sd = dot2_bf16(r.q[m].x, r.g[m].x, sd);
+    sd = dot2_bf16(r.q[m].y, r.g[m].y, sd);
+    sd = dot2_bf16(r.q[m].z, r.g[m].z, sd);
+    sd = dot2_bf16(r.q[m].w, r.g[m].w, sd);
   }
   uint4 pq[M], pg[M];
   quad_partners<D>(r.q, pq, l);
@@ -270,11 +269,18 @@ __device__ __forceinline__ uint32_t qc_bwd_finish(const QcBwdRow<D>& r, const fl
 template <int D>
 constexpr int bwd_rows() { return D == 128 ? 2 : 3; }
 
+//
+// The grid is what fits on the device at once (at most `nparts` blocks),
+// and the blocks deal the groups of kQuadTT tokens round-robin, so that at
+// any moment they work on neighbouring tokens (ranges of tokens per block,
+// 768 streams of 12 head rows each far apart, ran ~10% slower).  Block b
+// writes amax partial b; block 0 zeroes the slots [gridDim.x, nparts) that
+// no block owns.
 template <int D>
 __global__ __launch_bounds__(kThreads) void norm_rope_bwd_qc(
     const uint16_t* __restrict__ dq, const uint16_t* __restrict__ dk, FwdRows f, int64_t T,
     int seq_len, int H, int qs, float base, uint16_t* __restrict__ dqkv,
-    uint32_t* __restrict__ partials) {
+    uint32_t* __restrict__ partials, int nparts) {
   using Q = QuadChunks<D>;
   constexpr int h = Q::h, QUADS = kThreads / 4, RB = bwd_rows<D>();
   __shared__ double rev[h];
@@ -303,6 +309,8 @@ __global__ __launch_bounds__(kThreads) void norm_rope_bwd_qc(
   }
   amax = block_max_u32(amax << 16, red);
   if (threadIdx.x == 0) partials[blockIdx.x] = amax;
+  if (blockIdx.x == 0)
+    for (int i = gridDim.x + threadIdx.x; i < nparts; i += kThreads) partials[i] = 0;
 }
 
 // ------------------------------------------------- forward (other widths)
@@ -505,31 +513,55 @@ int norm_rope_bwd_blocks(int64_t T, int H, int d) {
   return (int)std::min<int64_t>(kQuadTileBlocks, std::max<int64_t>(1, ceil_div(T, tt)));
 }
 
+// Blocks of the quad backward for width D that the current device holds at
+// once, over all its CUs (queried once per device).
+template <int D>
+static int quad_bwd_resident() {
+  constexpr int kDevs = 64;
+  static int cached[kDevs] = {};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kDevs) dev = -1;
+  if (dev >= 0 && cached[dev] > 0) return cached[dev];
+  int cus = 0, per_cu = 0;
+  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev < 0 ? 0 : dev) !=
+          hipSuccess || cus <= 0)
+    cus = 256;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, norm_rope_bwd_qc<D>, kThreads, 0) !=
+          hipSuccess || per_cu <= 0)
+    per_cu = 1;
+  const int n = cus * per_cu;
+  if (dev >= 0) cached[dev] = n;
+  return n;
+}
+
+template <int D>
+static void launch_bwd_qc(const uint16_t* dq, const uint16_t* dk, const FwdRows& f, int64_t T,
+                          int seq_len, int H, int qs, float base, uint16_t* dqkv,
+                          uint32_t* partials, int nparts, hipStream_t s) {
+  const unsigned grid = (unsigned)std::min(nparts, quad_bwd_resident<D>());
+  norm_rope_bwd_qc<D><<<grid, kThreads, 0, s>>>(dq, dk, f, T, seq_len, H, qs, base, dqkv,
+                                                 partials, nparts);
+}
+
 void launch_norm_rope_bwd(const uint16_t* dq, const uint16_t* dk, const uint16_t* q,
                           const uint16_t* k, const float* rho, int64_t T, int seq_len, int H,
                           int d, int qs, float base, uint16_t* dqkv, uint32_t* partials,
                           hipStream_t s) {
-  const unsigned grid = (unsigned)norm_rope_bwd_blocks(T, H, d);
+  const int nparts = norm_rope_bwd_blocks(T, H, d);
   const FwdRows f{q, k, rho, (int)(T / seq_len)};
   switch (d) {
     case 64:
-      norm_rope_bwd_qc<64><<<grid, kThreads, 0, s>>>(dq, dk, f, T, seq_len, H, qs, base, dqkv,
-                                                        partials);
-      return;
+      return launch_bwd_qc<64>(dq, dk, f, T, seq_len, H, qs, base, dqkv, partials, nparts, s);
     case 96:
-      norm_rope_bwd_qc<96><<<grid, kThreads, 0, s>>>(dq, dk, f, T, seq_len, H, qs, base, dqkv,
-                                                        partials);
-      return;
+      return launch_bwd_qc<96>(dq, dk, f, T, seq_len, H, qs, base, dqkv, partials, nparts, s);
     case 128:
-      norm_rope_bwd_qc<128><<<grid, kThreads, 0, s>>>(dq, dk, f, T, seq_len, H, qs, base, dqkv,
-                                                         partials);
-      return;
+      return launch_bwd_qc<128>(dq, dk, f, T, seq_len, H, qs, base, dqkv, partials, nparts, s);
     default:
       break;
   }
   const size_t lds = norm_rope_bwd_lds(H, d);
-  norm_rope_bwd_kernel<kBwdTT><<<grid, kThreads, lds, s>>>(dq, dk, f, T, seq_len, H, d, qs, base,
-                                                          dqkv, partials);
+  norm_rope_bwd_kernel<kBwdTT><<<(unsigned)nparts, kThreads, lds, s>>>(
+      dq, dk, f, T, seq_len, H, d, qs, base, dqkv, partials);
 }
 
 }  // namespace fpr

@@ -9,9 +9,10 @@ inputs to it, with the bars of the QKV path:
     result to bf16 costs by at most 1.1x + 1e-3;
   * dW1, dW2 (fp32): <= 1e-3 relative per row.
 End to end from x, W1, W2 and dy alone: y, dX, dW1 and dW2 no further
-from the unquantised float64 results than 1.1x the oracle's own distance +
-1e-3.  (A one-ulp bf16 difference in h can move an h8 code by one e4m3
-step, 12.5%, so y is not compared with the oracle's chain row by row.)
+from the unquantised float64 results, in their worst row, than 1.1x the
+oracle's own worst row + 1e-3.  (A one-ulp bf16 difference in h can move
+an h8 code by one e4m3 step, 12.5%, so y is not compared with the
+oracle's chain row by row.)
 """
 import numpy as np
 import pytest
@@ -117,10 +118,11 @@ def test_mlp_end_to_end_against_oracle_chain():
     gpu = dict(y=bf16_to_f64(r["y"]), dx=bf16_to_f64(r["dx"]), dw1=r["dw1"], dw2=r["dw2"])
     orc = dict(y=bf16_to_f64(fw["y_bits"]), dx=bf16_to_f64(bw["dx_bits"]), dw1=bw["dw1_64"],
                dw2=bw["dw2_64"])
+    # worst row of each (token rows of y and dX, rows of dW1 [D][F] and
+    # dW2 [F][D])
     for k in ref:
-        eg = float(np.linalg.norm(gpu[k] - ref[k]) / np.linalg.norm(ref[k]))
-        eo = float(np.linalg.norm(orc[k] - ref[k]) / np.linalg.norm(ref[k]))
-        say(f"[gpu] mlp e2e {k}: gpu {eg:.3e} oracle {eo:.3e}")
+        eg, eo = row_rel_err(gpu[k], ref[k]), row_rel_err(orc[k], ref[k])
+        say(f"[gpu] mlp e2e {k}: worst row gpu {eg:.3e} oracle {eo:.3e}")
         assert eg <= 1.1 * eo + 1e-3, k
 
 
