@@ -565,15 +565,15 @@ __device__ __forceinline__ void zero_acc(v16f (&acc)[C::FM][C::FN]) {
 // then (after the first rows of half 1's MFMAs) barrier g: all of this
 // wave's reads of step g are done and step g + 1 has landed; half 0 of
 // step g + 1 streams in during the rest of half 1's MFMAs.
-// `tile_done(acc)` runs after the last K step of each tile (every nk
-// steps).  With ZC the first half-step of every tile starts from zero
+// `tile_start()` runs before the first K step of each tile and
+// `tile_done(acc)` after its last one (every nk steps).  With ZC the first half-step of every tile starts from zero
 // accumulators and tile_done may leave acc as it is; without it tile_done
 // must zero acc.  After the block's last step the stream reads a stage
 // whose contents are not used.
-template <class C, bool TOK, bool ZC, class TileDone>
+template <class C, bool TOK, bool ZC, class TileDone, class TileStart>
 __device__ __forceinline__ void mma_role(const uint8_t* lds, const Sched& sc, int wm, int wn,
                                          int lane, v16f (&acc)[C::FM][C::FN],
-                                         const TileDone& tile_done) {
+                                         const TileDone& tile_done, const TileStart& tile_start) {
   const int a0 = wm * C::WM, b0 = wn * C::WN;
   if (!ZC) zero_acc<C>(acc);
   barrier_lds();
@@ -597,6 +597,7 @@ __device__ __forceinline__ void mma_role(const uint8_t* lds, const Sched& sc, in
   // tile_done and the next tile's first step (with ZC, which writes them
   // from zero): the epilogue then has their registers
   for (int g = 0; g < sc.steps;) {
+    tile_start();
     if (ZC)
       step(g, std::true_type{});
     else
@@ -756,11 +757,25 @@ __device__ __forceinline__ uint32_t absmax_bf16x2(uint32_t w) {
   return lo > hi ? lo : hi;
 }
 
+// Lane (rq, p) of a wave's part (rows mp.., columns np..): the 8 auxiliary
+// bytes of chunk p of rows mp + 32 i + rq + 8 q, q < 4, so that 8 lanes
+// cover one row's 64 bytes.
+template <class C, class Epi>
+__device__ __forceinline__ void aux_slice(const Epi& epi, int mp, int np, int i, int lane,
+                                          uint2 (&dst)[4]) {
+  if constexpr (Epi::kAux) {
+    const uint8_t* ar = epi.aux_row(mp + i * 32 + (lane >> 3), np + 8 * (lane & 7));
+#pragma unroll
+    for (int q = 0; q < 4; ++q)  // rows rq + 8q lie in the same block of kActRows rows
+      dst[q] = *reinterpret_cast<const uint2*>(ar + q * 8 * kKBlock);
+  }
+}
+
 template <class C, class Epi>
 __device__ __forceinline__ void store_bf16_tile(const v16f (&acc)[C::FM][C::FN], float alpha,
                                                 uint8_t* slice, const Epi& epi, int M, int m0,
                                                 int n0, int wm, int wn, int lane,
-                                                uint32_t& amax) {
+                                                uint32_t& amax, const uint2 (&aux0)[4]) {
   using W = WaveSlice<C>;
   const int p = lane & 7, rq = lane >> 3;
   const typename Epi::Col col = epi.column(n0 + wn * C::WN + 8 * p);
@@ -775,12 +790,11 @@ __device__ __forceinline__ void store_bf16_tile(const v16f (&acc)[C::FM][C::FN],
   // this lane's accumulator columns: nl + 32 j + 8 g + 0..3
   const int nl = n0 + wn * C::WN + 4 * (lane >> 5);
   // Auxiliary bytes (one per output element, blocked like h8) of slice i
-  // are fetched as the output leaves: lane (rq, p) reads the 8 bytes of
-  // chunk p of rows rq + 8q, so 8 lanes cover one row's 64 bytes.  They
-  // pass through the wave's LDS slice (rows 72 bytes apart: 18 words, so
-  // the 32 rows x 2 words of one read below fall in 64 distinct banks) into
-  // the lanes that hold the matching accumulators.  Slice i + 1 is fetched
-  // while slice i is worked on.
+  // (aux_slice) pass through the wave's LDS slice (rows 72 bytes apart: 18
+  // words, so the 32 rows x 2 words of one read below fall in 64 distinct
+  // banks) into the lanes that hold the matching accumulators.  Slice 0's
+  // were fetched when the tile started (aux0); slice i + 1 is fetched while
+  // slice i is worked on.
   // The store path is chosen once per part (fast is uniform over the
   // wave), so each variant is straight-line code; with an auxiliary input
   // the two copies would no longer fit the registers, and the choice is
@@ -789,16 +803,10 @@ __device__ __forceinline__ void store_bf16_tile(const v16f (&acc)[C::FM][C::FN],
   auto body = [&](auto fast_c) {
     static_assert(C::WN == 64, "64 auxiliary bytes per row");
     uint2 raw[4];
-    auto fetch_aux = [&](int i, uint2 (&dst)[4]) {
-      if constexpr (Epi::kAux) {
-        const uint8_t* ar = epi.aux_row(mp + i * 32 + rq, n0 + wn * C::WN + 8 * p);
+    if constexpr (Epi::kAux)
 #pragma unroll
-        for (int q = 0; q < 4; ++q)  // rows rq + 8q lie in the same block of kActRows rows
-          dst[q] = *reinterpret_cast<const uint2*>(ar + q * 8 * kKBlock);
-      }
-    };
+      for (int q = 0; q < 4; ++q) raw[q] = aux0[q];
     auto aux_word = [](int row, int w) { return row * 72 + 4 * w; };
-    if constexpr (Epi::kAux) fetch_aux(0, raw);
 #pragma unroll
     for (int i = 0; i < C::FM; ++i) {
       const int ml = mp + i * 32 + (lane & 31);  // this lane's accumulator row
@@ -809,7 +817,7 @@ __device__ __forceinline__ void store_bf16_tile(const v16f (&acc)[C::FM][C::FN],
 #pragma unroll
         for (int q = 0; q < 4; ++q)
           *reinterpret_cast<uint2*>(slice + aux_word(rq + 8 * q, 2 * p)) = raw[q];
-        if (i + 1 < C::FM) fetch_aux(i + 1, raw);
+        if (i + 1 < C::FM) aux_slice<C, Epi>(epi, mp, n0 + wn * C::WN, i + 1, lane, raw);
 #pragma unroll
         for (int j = 0; j < C::FN; ++j)
 #pragma unroll
@@ -1168,7 +1176,7 @@ __global__ __launch_bounds__((TileCfg<256, 128, 4, 1>::THREADS), 1) void gemm_qk
     store_qkv_tile<C, D>(a, alpha, slice, rr, o, gm.cm, gm.M, (tile / gm.n_tiles) * C::BM_,
                          tile % gm.n_tiles, wave, lane);
   };
-  mma_role<C, false, true>(lds, sc, wave, 0, lane, acc, done);
+  mma_role<C, false, true>(lds, sc, wave, 0, lane, acc, done, [] {});
 }
 
 template <int BM, int BN, bool KTAIL, class Epi, int FA = kFmtE4M3>
@@ -1196,11 +1204,24 @@ __global__ __launch_bounds__((TileCfg<BM, BN>::THREADS), 1) void gemm_bf16out_ke
   Epi e = epi;
   if constexpr (Epi::kMap) e.prepare();
   v16f acc[C::FM][C::FN];
-  mma_role<C, false, true>(lds, sc, wm, wn, lane, acc, [&](v16f (&a)[C::FM][C::FN]) {
-    const int tile = sc.tile_of(ord++);
-    store_bf16_tile<C, Epi>(a, alpha, slice, e, gm.M, (tile / gm.n_tiles) * BM,
-                            (tile % gm.n_tiles) * BN, wm, wn, lane, amax);
-  });
+  // an epilogue's auxiliary bytes for the tile's first 32-row slice are
+  // fetched when the tile starts, so that they arrive during its K steps
+  uint2 aux0[4];
+  auto start = [&] {
+    if constexpr (Epi::kAux) {
+      const int tile = sc.tile_of(ord);
+      aux_slice<C, Epi>(e, (tile / gm.n_tiles) * BM + wm * C::WM,
+                        (tile % gm.n_tiles) * BN + wn * C::WN, 0, lane, aux0);
+    }
+  };
+  mma_role<C, false, true>(
+      lds, sc, wm, wn, lane, acc,
+      [&](v16f (&a)[C::FM][C::FN]) {
+        const int tile = sc.tile_of(ord++);
+        store_bf16_tile<C, Epi>(a, alpha, slice, e, gm.M, (tile / gm.n_tiles) * BM,
+                                (tile % gm.n_tiles) * BN, wm, wn, lane, amax, aux0);
+      },
+      start);
   if constexpr (Epi::kAmax) e.finish(amax, blockIdx.x * C::MMA + wave, lane);
 }
 
@@ -1235,7 +1256,7 @@ __global__ __launch_bounds__((TileCfg<BM, BN, MW, NW>::THREADS), 1) void gemm_dw
   }
   const int wm = wave / C::NW_, wn = wave % C::NW_;
   v16f acc[C::FM][C::FN];
-  mma_role<C, true, false>(lds, sc, wm, wn, lane, acc, [](v16f (&)[C::FM][C::FN]) {});
+  mma_role<C, true, false>(lds, sc, wm, wn, lane, acc, [](v16f (&)[C::FM][C::FN]) {}, [] {});
   store_partial_tile<C>(acc, part + (int64_t)split * gm.M * gm.N, gm.M, gm.N,
                         (tile / gm.n_tiles) * BM, (tile % gm.n_tiles) * BN, wm, wn, lane);
 }
