@@ -775,7 +775,8 @@ template <class C, class Epi>
 __device__ __forceinline__ void store_bf16_tile(const v16f (&acc)[C::FM][C::FN], float alpha,
                                                 uint8_t* slice, const Epi& epi, int M, int m0,
                                                 int n0, int wm, int wn, int lane,
-                                                uint32_t& amax, const uint2 (&aux0)[4]) {
+                                                uint32_t& amax, const uint2 (&aux0)[4],
+                                                const uint2 (&aux1)[4]) {
   using W = WaveSlice<C>;
   const int p = lane & 7, rq = lane >> 3;
   const typename Epi::Col col = epi.column(n0 + wn * C::WN + 8 * p);
@@ -792,9 +793,9 @@ __device__ __forceinline__ void store_bf16_tile(const v16f (&acc)[C::FM][C::FN],
   // Auxiliary bytes (one per output element, blocked like h8) of slice i
   // (aux_slice) pass through the wave's LDS slice (rows 72 bytes apart: 18
   // words, so the 32 rows x 2 words of one read below fall in 64 distinct
-  // banks) into the lanes that hold the matching accumulators.  Slice 0's
-  // were fetched when the tile started (aux0); slice i + 1 is fetched while
-  // slice i is worked on.
+  // banks) into the lanes that hold the matching accumulators.  Those of
+  // slices 0 and 1 were fetched when the tile started (aux0, aux1); slice
+  // i + 2's are fetched while slice i is worked on.
   // The store path is chosen once per part (fast is uniform over the
   // wave), so each variant is straight-line code; with an auxiliary input
   // the two copies would no longer fit the registers, and the choice is
@@ -802,10 +803,13 @@ __device__ __forceinline__ void store_bf16_tile(const v16f (&acc)[C::FM][C::FN],
   // the runtime flag.
   auto body = [&](auto fast_c) {
     static_assert(C::WN == 64, "64 auxiliary bytes per row");
-    uint2 raw[4];
+    uint2 raw[4], nxt[4];
     if constexpr (Epi::kAux)
 #pragma unroll
-      for (int q = 0; q < 4; ++q) raw[q] = aux0[q];
+      for (int q = 0; q < 4; ++q) {
+        raw[q] = aux0[q];
+        nxt[q] = aux1[q];
+      }
     auto aux_word = [](int row, int w) { return row * 72 + 4 * w; };
 #pragma unroll
     for (int i = 0; i < C::FM; ++i) {
@@ -817,7 +821,9 @@ __device__ __forceinline__ void store_bf16_tile(const v16f (&acc)[C::FM][C::FN],
 #pragma unroll
         for (int q = 0; q < 4; ++q)
           *reinterpret_cast<uint2*>(slice + aux_word(rq + 8 * q, 2 * p)) = raw[q];
-        if (i + 1 < C::FM) aux_slice<C, Epi>(epi, mp, n0 + wn * C::WN, i + 1, lane, raw);
+#pragma unroll
+        for (int q = 0; q < 4; ++q) raw[q] = nxt[q];
+        if (i + 2 < C::FM) aux_slice<C, Epi>(epi, mp, n0 + wn * C::WN, i + 2, lane, nxt);
 #pragma unroll
         for (int j = 0; j < C::FN; ++j)
 #pragma unroll
@@ -1204,14 +1210,16 @@ __global__ __launch_bounds__((TileCfg<BM, BN>::THREADS), 1) void gemm_bf16out_ke
   Epi e = epi;
   if constexpr (Epi::kMap) e.prepare();
   v16f acc[C::FM][C::FN];
-  // an epilogue's auxiliary bytes for the tile's first 32-row slice are
-  // fetched when the tile starts, so that they arrive during its K steps
-  uint2 aux0[4];
+  // an epilogue's auxiliary bytes for the tile's first two 32-row slices
+  // are fetched when the tile starts, so that they arrive during its K steps
+  uint2 aux0[4], aux1[4];
   auto start = [&] {
     if constexpr (Epi::kAux) {
       const int tile = sc.tile_of(ord);
       aux_slice<C, Epi>(e, (tile / gm.n_tiles) * BM + wm * C::WM,
                         (tile % gm.n_tiles) * BN + wn * C::WN, 0, lane, aux0);
+      aux_slice<C, Epi>(e, (tile / gm.n_tiles) * BM + wm * C::WM,
+                        (tile % gm.n_tiles) * BN + wn * C::WN, 1, lane, aux1);
     }
   };
   mma_role<C, false, true>(
@@ -1219,7 +1227,7 @@ __global__ __launch_bounds__((TileCfg<BM, BN>::THREADS), 1) void gemm_bf16out_ke
       [&](v16f (&a)[C::FM][C::FN]) {
         const int tile = sc.tile_of(ord++);
         store_bf16_tile<C, Epi>(a, alpha, slice, e, gm.M, (tile / gm.n_tiles) * BM,
-                                (tile % gm.n_tiles) * BN, wm, wn, lane, amax, aux0);
+                                (tile % gm.n_tiles) * BN, wm, wn, lane, amax, aux0, aux1);
       },
       start);
   if constexpr (Epi::kAmax) e.finish(amax, blockIdx.x * C::MMA + wave, lane);
