@@ -939,8 +939,11 @@ struct QkvOut {
 
 // The rotation frequencies of a lane's head columns c = 8 idx + 4 (l / 32) +
 // e, in revolutions per position: theta_c / (2 pi) = rev0 * r^(c - c0) with
-// r = base^(-2/d), stepped by one multiplication per column (fp64, so the
-// angles stay exact to ~1e-14 revolutions per position).
+// r = base^(-2/d).  A row's angles p theta_c / (2 pi) are stepped by one
+// fp64 multiplication per column: with positions below 2^24 the angles
+// stay below 2^22 revolutions, and over the at most 32 steps of a head
+// their fractional parts keep an error below ~1e-8 revolutions before the
+// fp32 sine.
 struct RopeRev {
   double rev0;        // theta_c0 / (2 pi) of the lane's first column c0 = 4 (l / 32)
   double r1, r5, r8;  // r, r^5 and r^8: one column on, from e = 3 to the next
@@ -990,6 +993,47 @@ __device__ __forceinline__ void store_qkv_tile(const v16f (&acc)[C::FM][C::FN], 
                            cvt_bf16x2_rn(a[4 * q4 + 2] * alpha, a[4 * q4 + 3] * alpha));
       asm volatile("" : "+v"(P[i][g].x), "+v"(P[i][g].y));
     }
+  // The output of tile group g (8 columns): a Q/K head's row (array, head,
+  // row width, first column), or a V head's row, or none.  V column f's
+  // head f / d_v comes from a float product: f < H d_v <= 2^16, so
+  // (f + 0.5) / d_v is off by far less than 0.5 / d_v.
+  struct Dst {
+    uint16_t* arr;
+    int hh, w, col;
+  };
+  const float inv_dv = 1.0f / (float)o.dv;
+  auto chunk_dst = [&](int g) -> Dst {
+    Dst d{nullptr, 0, 0, 0};
+    if (mixed && g < VG0) {
+      const int hs = g / G;
+      if (head_ok(hs)) {
+        const int hq = hq0 + hs;
+        const bool isk = hq >= o.H;
+        d = Dst{isk ? o.k : o.q, isk ? hq - o.H : hq, o.qs, 8 * (g - hs * G)};
+      }
+    } else {  // the filler of a mixed tile, or a whole-V tile
+      const int f = mixed ? nt * cm.fill + 8 * (g - VG0)
+                          : cm.n_mixed * cm.fill + (nt - cm.n_mixed) * 128 + 8 * g;
+      if (f < cm.nv) {
+        const int hh = (int)(((float)f + 0.5f) * inv_dv);
+        d = Dst{o.v, hh, o.dv, f - hh * o.dv};
+      }
+    }
+    return d;
+  };
+  // fast path: where lane (rq, pc)'s chunk of pass ps goes for row mp + rq
+  // (fragment i adds 32 i rows), once per tile
+  const int pc = lane & 7, rq = lane >> 3;
+  uint16_t* fdst[2] = {nullptr, nullptr};
+  int fw[2] = {0, 0};
+  if (fast) {
+#pragma unroll
+    for (int ps = 0; ps < 2; ++ps) {
+      const Dst d = chunk_dst(8 * ps + pc);
+      if (d.arr) fdst[ps] = d.arr + (((int64_t)(b0 * o.H + d.hh) * o.S + s0 + rq) * d.w + d.col);
+      fw[ps] = d.w;
+    }
+  }
 #pragma unroll
   for (int i = 0; i < C::FM; ++i) {
     const int m = mp + 32 * i + r;  // this lane's row
@@ -1018,12 +1062,18 @@ __device__ __forceinline__ void store_qkv_tile(const v16f (&acc)[C::FM][C::FN], 
         const uint2 w = prod(hs * G + g);
         ss = dot2_bf16(w.y, w.y, dot2_bf16(w.x, w.x, ss));
       }
-      ss += __shfl_xor(ss, 32);
+      {  // plus the other half of the row, in lane l ^ 32 (same sum on both)
+        const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(ss),
+                                                         __float_as_uint(ss), false, false);
+        ss = __uint_as_float(sw[0]) + __uint_as_float(sw[1]);
+      }
       rho[hs] = 1.0f / sqrtf(ss / (float)D + o.eps);
-      const bool isk = hq0 + hs >= o.H;
-      if (hl == 0 && m < M)
-        o.rho[(((int64_t)isk * o.n_seq + b) * o.H + (isk ? hq0 + hs - o.H : hq0 + hs)) * o.S + p] =
-            rho[hs];
+      if (hl == 0 && m < M) {
+        const bool isk = hq0 + hs >= o.H;
+        const int hh = isk ? hq0 + hs - o.H : hq0 + hs;
+        // [2][n_seq][H][S]: row (isk, b, hh, p)
+        o.rho[((int64_t)(isk * o.n_seq + b) * o.H + hh) * o.S + p] = rho[hs];
+      }
     }
     // The rotated pairs (idx, idx + d/16) of head hs whose groups fall in
     // pass ps (groups 8 ps .. 8 ps + 7) go into the slice.  A pair with a
@@ -1039,11 +1089,14 @@ __device__ __forceinline__ void store_qkv_tile(const v16f (&acc)[C::FM][C::FN], 
 #pragma unroll
       for (int hs = 0; hs < HPT; ++hs) {
         if (!head_ok(hs)) continue;  // uniform
-        // opaque to the compiler: the frequency chain is formed here, per
-        // tile, instead of being hoisted out of the tile loop, where its
-        // doubles would stay live through the matrix work
-        double rev = rr.rev0;
-        asm volatile("" : "+v"(rev));
+        // the row's angle in revolutions, p theta_c / (2 pi), stepped from
+        // column to column like the frequency (opaque to the compiler: the
+        // chain is formed here, per tile, instead of being hoisted out of
+        // the tile loop, where its doubles would stay live through the
+        // matrix work)
+        double ang = rr.rev0;
+        asm volatile("" : "+v"(ang));
+        ang *= (double)p;
 #pragma unroll
         for (int idx = 0; idx < HG; ++idx) {
           const int glo = hs * G + idx, ghi = glo + HG;
@@ -1051,7 +1104,7 @@ __device__ __forceinline__ void store_qkv_tile(const v16f (&acc)[C::FM][C::FN], 
           const bool want_lo = glo / 8 == ps, want_hi = ghi / 8 == ps && !(kHold && straddle);
           const bool keep_hi = kHold && straddle && ps == 0;
           if (!want_lo && !want_hi && !keep_hi) {
-            rev *= rr.r8;  // the next group's first column
+            ang *= rr.r8;  // the next group's first column
             continue;
           }
           float y1[4], y2[4], o1[4], o2[4];
@@ -1060,8 +1113,10 @@ __device__ __forceinline__ void store_qkv_tile(const v16f (&acc)[C::FM][C::FN], 
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
             float cn, sn;
-            rope_cs(rev, p, cn, sn);
-            rev *= e < 3 ? rr.r1 : rr.r5;
+            const float f = (float)__builtin_amdgcn_fract(ang);  // in [0, 1)
+            sn = __builtin_amdgcn_sinf(f);                        // sin(2 pi f)
+            cn = __builtin_amdgcn_cosf(f);
+            ang *= e < 3 ? rr.r1 : rr.r5;
             const float u1 = y1[e] * rho[hs], u2 = y2[e] * rho[hs];
             o1[e] = u1 * cn - u2 * sn;
             o2[e] = u2 * cn + u1 * sn;
@@ -1076,7 +1131,6 @@ __device__ __forceinline__ void store_qkv_tile(const v16f (&acc)[C::FM][C::FN], 
     };
     // two passes of 64 columns: lane (rq, pc) stores chunk pc of rows
     // rq + 8 q, q < 4 (8 rows x 128 bytes per store instruction)
-    const int pc = lane & 7, rq = lane >> 3;
 #pragma unroll
     for (int ps = 0; ps < 2; ++ps) {
       rotate_pairs(ps);
@@ -1094,41 +1148,20 @@ __device__ __forceinline__ void store_qkv_tile(const v16f (&acc)[C::FM][C::FN], 
 #pragma unroll
       for (int q = 0; q < 4; ++q)
         val[q] = *reinterpret_cast<const uint4*>(slice + slice64(rq + 8 * q, pc));
-      const int g = 8 * ps + pc;  // the chunk's tile group
-      // the chunk's output: a Q/K head's row, or a V head's row
-      uint16_t* dst = nullptr;
-      int w = 0, hh = 0, col = 0;
-      if (mixed && g < VG0) {
-        const int hs = g / G;
-        if (head_ok(hs)) {
-          const int hq = hq0 + hs;
-          const bool isk = hq >= o.H;
-          dst = isk ? o.k : o.q;
-          hh = isk ? hq - o.H : hq;
-          w = o.qs;
-          col = 8 * (g - hs * G);
-        }
-      } else {  // the filler of a mixed tile, or a whole-V tile
-        const int f = mixed ? nt * cm.fill + 8 * (g - VG0)
-                            : cm.n_mixed * cm.fill + (nt - cm.n_mixed) * 128 + 8 * g;
-        if (f < cm.nv) {
-          hh = f / o.dv;
-          dst = o.v;
-          w = o.dv;
-          col = f - hh * o.dv;
-        }
-      }
-      if (dst) {
-        const int mt0 = mp + 32 * i + rq;
-        if (fast) {  // rows rq + 8 q follow each other: one pointer, fixed stride
-          uint16_t* at = dst + row_off(mt0, hh, w) + col;
+      if (fast) {  // rows rq + 8 q follow each other: one pointer, fixed stride
+        if (fdst[ps]) {
+          uint16_t* at = fdst[ps] + 32 * i * fw[ps];
 #pragma unroll
-          for (int q = 0; q < 4; ++q, at += 8 * w) store_stream(at, val[q]);
-        } else {
+          for (int q = 0; q < 4; ++q, at += 8 * fw[ps]) store_stream(at, val[q]);
+        }
+      } else {
+        const Dst d = chunk_dst(8 * ps + pc);
+        if (d.arr) {
+          const int mt0 = mp + 32 * i + rq;
 #pragma unroll
           for (int q = 0; q < 4; ++q) {
             const int mt = mt0 + 8 * q;
-            if (mt < M) store_stream(dst + row_off(mt, hh, w) + col, val[q]);
+            if (mt < M) store_stream(d.arr + row_off(mt, d.hh, d.w) + d.col, val[q]);
           }
         }
       }
