@@ -619,6 +619,12 @@ __device__ __forceinline__ void store_stream(uint16_t* p, uint4 v) {
   __builtin_nontemporal_store(x, reinterpret_cast<v4u*>(p));
 }
 
+// An ordinary 16-byte store, for outputs whose cache lines are filled by
+// several stores (from neighbouring rows or tiles) that the L2 must merge.
+__device__ __forceinline__ void store_plain(uint16_t* p, uint4 v) {
+  *reinterpret_cast<uint4*>(p) = v;
+}
+
 // bf16 tile store through the matrix wave's own LDS slice: 32 rows x WN
 // columns (WN * 2 bytes per row, 16-byte chunks XOR-swizzled by row).  Each
 // lane writes its 4-column groups, then reads back whole 16-byte chunks:
@@ -926,7 +932,12 @@ __device__ __forceinline__ void persistent_tiles(Sched& sc, int b, int G, int nt
 // lane (group g + d/16, same e).  The product is rounded to bf16 first,
 // exactly where an unfused path would store it, then normalised (fp32) and
 // rotated; 1 / rms of every Q and K head row goes out with q, k and v, and
-// the backward rebuilds the normalised rows from q and k with it.
+// the backward rebuilds the normalised rows from q and k with it.  The
+// stores are ordinary ones: a q / k row (d * 2 bytes) and the 64-byte V
+// pieces of the mixed tiles fill cache lines only together with their
+// neighbours (rows of the same store, tiles of the same row panel on the
+// same XCD), which the L2 merges; streaming stores wrote ~24% more bytes to
+// memory (partial lines written out one by one), at the same speed.
 
 struct QkvOut {
   uint16_t* q;   // [n_seq][H][S][qs]
@@ -1152,7 +1163,7 @@ __device__ __forceinline__ void store_qkv_tile(const v16f (&acc)[C::FM][C::FN], 
         if (fdst[ps]) {
           uint16_t* at = fdst[ps] + 32 * i * fw[ps];
 #pragma unroll
-          for (int q = 0; q < 4; ++q, at += 8 * fw[ps]) store_stream(at, val[q]);
+          for (int q = 0; q < 4; ++q, at += 8 * fw[ps]) store_plain(at, val[q]);
         }
       } else {
         const Dst d = chunk_dst(8 * ps + pc);
@@ -1161,7 +1172,7 @@ __device__ __forceinline__ void store_qkv_tile(const v16f (&acc)[C::FM][C::FN], 
 #pragma unroll
           for (int q = 0; q < 4; ++q) {
             const int mt = mt0 + 8 * q;
-            if (mt < M) store_stream(d.arr + row_off(mt, d.hh, d.w) + d.col, val[q]);
+            if (mt < M) store_plain(d.arr + row_off(mt, d.hh, d.w) + d.col, val[q]);
           }
         }
       }
@@ -1178,7 +1189,7 @@ __device__ __forceinline__ void store_qkv_tile(const v16f (&acc)[C::FM][C::FN], 
           const int rw = it / pcs, c = it - rw * pcs;
           const int mt = mp + 32 * i + rw;
           if (mt < M)
-            store_stream((isk ? o.k : o.q) + row_off(mt, isk ? hq - o.H : hq, o.qs) + D + 8 * c,
+            store_plain((isk ? o.k : o.q) + row_off(mt, isk ? hq - o.H : hq, o.qs) + D + 8 * c,
                          make_uint4(0, 0, 0, 0));
         }
       }
