@@ -932,12 +932,15 @@ __device__ __forceinline__ void persistent_tiles(Sched& sc, int b, int G, int nt
 // lane (group g + d/16, same e).  The product is rounded to bf16 first,
 // exactly where an unfused path would store it, then normalised (fp32) and
 // rotated; 1 / rms of every Q and K head row goes out with q, k and v, and
-// the backward rebuilds the normalised rows from q and k with it.  The
-// stores are ordinary ones: a q / k row (d * 2 bytes) and the 64-byte V
-// pieces of the mixed tiles fill cache lines only together with their
-// neighbours (rows of the same store, tiles of the same row panel on the
-// same XCD), which the L2 merges; streaming stores wrote ~24% more bytes to
-// memory (partial lines written out one by one), at the same speed.
+// the backward rebuilds the normalised rows from q and k with it.
+// Stores: the 64-byte V pieces of a mixed tile fill a V row's cache lines
+// only together with the neighbouring tiles' (same row panel, same XCD),
+// so they are ordinary stores, which the L2 merges; everything else is
+// streamed.  (Measured on the forward GEMM at 65536 tokens, fetched +
+// written: all streamed 63 + 315 MB, this 65 + 302 MB, all ordinary 130 +
+// 256 MB, the L2 then reading lines in before partial writes; the same
+// time each.  The q / k rows, d * 2 bytes, fill whole lines only across
+// the two 64-column passes.)
 
 struct QkvOut {
   uint16_t* q;   // [n_seq][H][S][qs]
@@ -1162,8 +1165,13 @@ __device__ __forceinline__ void store_qkv_tile(const v16f (&acc)[C::FM][C::FN], 
       if (fast) {  // rows rq + 8 q follow each other: one pointer, fixed stride
         if (fdst[ps]) {
           uint16_t* at = fdst[ps] + 32 * i * fw[ps];
+          if (mixed && 8 * ps + pc >= VG0) {  // a 64-byte piece of a V row
 #pragma unroll
-          for (int q = 0; q < 4; ++q, at += 8 * fw[ps]) store_plain(at, val[q]);
+            for (int q = 0; q < 4; ++q, at += 8 * fw[ps]) store_plain(at, val[q]);
+          } else {
+#pragma unroll
+            for (int q = 0; q < 4; ++q, at += 8 * fw[ps]) store_stream(at, val[q]);
+          }
         }
       } else {
         const Dst d = chunk_dst(8 * ps + pc);
@@ -1172,7 +1180,7 @@ __device__ __forceinline__ void store_qkv_tile(const v16f (&acc)[C::FM][C::FN], 
 #pragma unroll
           for (int q = 0; q < 4; ++q) {
             const int mt = mt0 + 8 * q;
-            if (mt < M) store_plain(d.arr + row_off(mt, d.hh, d.w) + d.col, val[q]);
+            if (mt < M) store_stream(d.arr + row_off(mt, d.hh, d.w) + d.col, val[q]);
           }
         }
       }
@@ -1189,7 +1197,7 @@ __device__ __forceinline__ void store_qkv_tile(const v16f (&acc)[C::FM][C::FN], 
           const int rw = it / pcs, c = it - rw * pcs;
           const int mt = mp + 32 * i + rw;
           if (mt < M)
-            store_plain((isk ? o.k : o.q) + row_off(mt, isk ? hq - o.H : hq, o.qs) + D + 8 * c,
+            store_stream((isk ? o.k : o.q) + row_off(mt, isk ? hq - o.H : hq, o.qs) + D + 8 * c,
                          make_uint4(0, 0, 0, 0));
         }
       }
