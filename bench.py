@@ -27,6 +27,7 @@ import contextlib
 import hashlib
 import json
 import os
+import re
 import sys
 import time
 
@@ -172,8 +173,14 @@ def cpu_model() -> str:
 
 
 def source_hash(stage: str) -> str:
+    """Hash of the code of a stage's kernel source: comments and blank space
+    dropped, so that a comment edit keeps its counter lines valid."""
     path = os.path.join(ROOT, "fp8_packed_reduced_amd", "csrc", STAGE_SOURCES[stage])
-    return hashlib.sha256(open(path, "rb").read()).hexdigest()[:12]
+    text = open(path, encoding="utf-8").read()
+    text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
+    text = re.sub(r"//[^\n]*", " ", text)
+    code = " ".join(text.split())
+    return hashlib.sha256(code.encode()).hexdigest()[:12]
 
 
 def read_traffic(workload: str, stage: str):

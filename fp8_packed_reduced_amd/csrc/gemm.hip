@@ -728,9 +728,10 @@ struct EpiRelu2 : EpiDx {
 };
 
 // The MLP's dh = dy W2^T turned into dpre = 2 dh relu(pre), with relu(pre)
-// rebuilt from the stored squared activation as sqrt(s_h dec(h8)) (PR #344
-// page, "Changes"), computed as dh sqrt(4 s_h dec(h8)) with the hardware
-// square root (1 ulp; the result is rounded to bf16).  h8 is in the blocked
+// recovered as sqrt(s_h dec(h8)) from the kept h^2 codes (PR #344 page,
+// "Changes": no pre-activation is kept), computed as dh sqrt(4 s_h
+// dec(h8)) with the hardware square root (1 ulp; the result is rounded to
+// bf16).  h8 is in the blocked
 // row layout (kc blocks of kKBlock columns per block row); aux_row() points
 // at the code of column n of row m, and the codes of a lane's columns n +
 // 32 j + 8 g, which share that 128-column block, follow at fixed offsets.

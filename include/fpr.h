@@ -298,7 +298,7 @@ FPR_API void fpr_trace_set(fpr_trace* trace);
  *
  * Every GEMM is FP8 e4m3 x e4m3 with fp32 accumulation and one per-tensor
  * scale per operand (the convention of the QKV path): x, W1, h, W2, dy and
- * dpre.  The stored squared activation is h's e4m3 copy h8 (and s_h),
+ * dpre.  The kept h^2 is h's e4m3 copy h8 (and s_h),
  * which the second projection and dW2 read anyway; the backward takes
  * relu(pre) = sqrt(s_h * dec(h8)).  The h and dpre that are quantised are
  * the fp32 results rounded once to bf16.  Quantisers are treated as the

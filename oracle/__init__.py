@@ -438,7 +438,7 @@ def qkv_backward(dims, n_seq: int, S: int, dq_bits, dk_bits, dv_bits,
 # kept: the backward recovers relu(pre) from the squared activation.
 # Readings where the page is silent: W1 is [D][F] and W2 is [F][D]
 # (y = relu(x W1)^2 W2), one per-tensor e4m3 scale per tensor exactly as for
-# the QKV path, and the stored squared activation is its e4m3 copy h8 with
+# the QKV path, and the kept h^2 is its e4m3 copy h8 with
 # scale s_h, which the second projection and dW2 read anyway, so
 # relu(pre) = sqrt(s_h dec(h8)).  The bf16 h that the quantiser reads is
 # relu(pre)^2 rounded once.
