@@ -639,8 +639,9 @@ struct WaveSlice {
   }
 };
 
-// Forward: Q|K columns to the saved pre-norm rows, V columns straight into
-// the head-major v output.  A chunk of 8 columns never straddles a V head
+// Forward for head widths without the fused epilogue: Q|K columns to the
+// pre-norm rows in the forward workspace (the norm/RoPE kernel reads them
+// next), V columns straight into the head-major v output.  A chunk of 8 columns never straddles a V head
 // (d_v % 16 == 0) nor the Q|K / V boundary.
 struct EpiFwd {
   static constexpr bool kMap = false, kAux = false, kAmax = false;
