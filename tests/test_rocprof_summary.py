@@ -117,3 +117,24 @@ def test_stats_carries_the_live_average_of_the_same_run(tmp_path):
     log.write_text("no json here\n")
     with pytest.raises(SystemExit, match="no bench.py JSON"):
         rs.stats(str(f), "t", "cmd", str(log))
+
+
+def test_counter_lines_are_keyed_to_kernel_code_not_comments(tmp_path, monkeypatch):
+    """A stage's counter line stays valid across comment edits of its kernel
+    source and is dropped once a line of code changes."""
+    src = tmp_path / "fp8_packed_reduced_amd" / "csrc"
+    src.mkdir(parents=True)
+    (tmp_path / "profiles").mkdir()
+    f = src / bench.STAGE_SOURCES["gemm_fwd"]
+    f.write_text("// a kernel\nint f(int x) { return x + 1; }  /* done */\n")
+    monkeypatch.setattr(bench, "ROOT", str(tmp_path))
+    h = bench.source_hash("gemm_fwd")
+    (tmp_path / "profiles" / "traffic_w.txt").write_text(
+        "# header\n" f"gemm_fwd 1000 24 {h}\n")
+    assert bench.read_traffic("w", "gemm_fwd") == 1024
+    f.write_text("/* the kernel,\n   reworded */\nint f(int x) {\n  return x + 1;\n}\n")
+    assert bench.source_hash("gemm_fwd") == h
+    assert bench.read_traffic("w", "gemm_fwd") == 1024
+    f.write_text("int f(int x) { return x + 2; }\n")
+    assert bench.source_hash("gemm_fwd") != h
+    assert bench.read_traffic("w", "gemm_fwd") is None
