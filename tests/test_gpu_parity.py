@@ -300,13 +300,16 @@ def test_scores_depend_only_on_position_difference():
 
 
 @pytest.mark.parametrize("name,w,stride", [("tiny", inputs.WORKLOADS["tiny"], 128),
-                                           ("ragged", RAGGED, 104), ("tails", TAILS, 64)])
+                                           ("ragged", RAGGED, 104), ("tails", TAILS, 64),
+                                           ("d64", dict(RAGGED, d_qk=64), 128),
+                                           ("d128", dict(RAGGED, d_qk=128), 136)])
 def test_padded_qk_stride(name, w, stride):
     """q/k rows padded to `stride` (the 96 -> 128 case an attention kernel with
-    equal head widths needs; 48 -> 64 goes through the other norm/RoPE
-    kernels): the first d_qk columns and every backward output are bit-equal
-    to the unpadded run's, the padding is written as zeros, and the NaN bits
-    in the padding of dq/dk are never read."""
+    equal head widths needs; 64 and 128 wide heads through the fused forward
+    too; 48 -> 64 goes through the other norm/RoPE kernels): the first d_qk
+    columns and every backward output are bit-equal to the unpadded run's,
+    the padding is written as zeros, and the NaN bits in the padding of
+    dq/dk are never read."""
     d = w["d_qk"]
     a = run(w, seed=13)
     b = run(w, seed=13, dy=a["dy"], qk_stride=stride)
