@@ -7,12 +7,12 @@
 //
 // All three are C[m][n] = sum_k A[m][k] * B[n][k] with both operands
 // K-contiguous in memory, built from v_mfma_scale_f32_32x32x64_f8f6f4 with
-// neutral E8M0 scales (it sustains ~4.3 PFLOP/s here, against ~3.2-3.9 for
-// the 16x16x128 form).
+// neutral E8M0 scales (a bare loop of it sustains 4.6-4.8 PFLOP/s here,
+// against ~3.2-3.9 for the 16x16x128 form).
 //
 // A block is 8 waves with two roles.  Waves 0-3 (one per SIMD) are the
-// matrix waves: 2 x 2 of them compute a BM x BN tile and never load from
-// global memory.  Waves 4-7 are the copy waves: they fill a ring of three
+// matrix waves: 2 x 2 of them (4 x 1 in the fused forward) compute a
+// BM x BN tile and never load from global memory.  Waves 4-7 are the copy waves: they fill a ring of three
 // LDS stages, K advancing 128 bytes per stage, with direct global-to-LDS
 // loads and wait only on their own vector-memory counter.  As that counter
 // is per wave, the matrix waves' output stores never hold up the operand
@@ -31,10 +31,12 @@
 // of one m (l % 32).  Which k each byte of a lane's 32-byte operand stands
 // for does not matter, as both operands use the same assignment.
 //
-// bf16 outputs (forward, dX) come from a persistent kernel, one block per
-// CU walking its tiles; a finished 32-row slice of a matrix wave's tile is
-// transposed through that wave's own 4 KiB of LDS so that every lane
-// stores a 16-byte run of one row.  dW (K = tokens) reads x8 and g8 as the
+// bf16 outputs (forward, dX, the MLP's) come from persistent kernels, one
+// block per CU walking its tiles; a finished 32-row slice of a matrix
+// wave's tile is transposed through that wave's own 4 KiB of LDS so that
+// every lane stores a 16-byte run of one row.  The forward for head widths
+// 64, 96 and 128 also normalises and rotates q and k in that epilogue
+// (gemm_qkv_fwd_kernel, below).  dW (K = tokens) reads x8 and g8 as the
 // quantiser stores them, token by token, and turns them into MFMA operands
 // with transposing LDS reads; it splits K over blocks and writes fp32
 // partial sums that a second kernel adds in split order.
