@@ -1096,9 +1096,7 @@ __device__ __forceinline__ void store_qkv_tile(const v16f (&acc)[C::FM][C::FN], 
     // The rotated pairs (idx, idx + d/16) of head hs whose groups fall in
     // pass ps (groups 8 ps .. 8 ps + 7) go into the slice.  A pair with a
     // half in each pass is formed in the first and its upper half held in
-    // registers (d = 96: 4 groups), or, for d = 128, where every pair
-    // straddles the passes, formed again in the second.
-    constexpr bool kHold = D != 128;
+    // registers until the second (d = 96: 4 groups; d = 128: all 8).
     uint2 hold[8];
     auto put = [&](int g, uint2 w) {
       *reinterpret_cast<uint2*>(slice + slice64(r, g & 7) + 8 * hl) = w;
@@ -1119,8 +1117,8 @@ __device__ __forceinline__ void store_qkv_tile(const v16f (&acc)[C::FM][C::FN], 
         for (int idx = 0; idx < HG; ++idx) {
           const int glo = hs * G + idx, ghi = glo + HG;
           const bool straddle = glo / 8 != ghi / 8;
-          const bool want_lo = glo / 8 == ps, want_hi = ghi / 8 == ps && !(kHold && straddle);
-          const bool keep_hi = kHold && straddle && ps == 0;
+          const bool want_lo = glo / 8 == ps, want_hi = ghi / 8 == ps && !straddle;
+          const bool keep_hi = straddle && ps == 0;
           if (!want_lo && !want_hi && !keep_hi) {
             ang *= rr.r8;  // the next group's first column
             continue;
@@ -1157,7 +1155,7 @@ __device__ __forceinline__ void store_qkv_tile(const v16f (&acc)[C::FM][C::FN], 
         const bool head = mixed && g < VG0;
         if (!head) {
           put(g, prod(g));
-        } else if (kHold && ps == 1 && g % G >= HG && (g - HG) / 8 == 0) {
+        } else if (ps == 1 && g % G >= HG && (g - HG) / 8 == 0) {
           // the upper half of a pair formed (and held) in the first pass
           if (head_ok(g / G)) put(g, hold[g - 8]);
         }
