@@ -31,6 +31,7 @@
 // rotation partners; row sums go through per-item partials in LDS, summed
 // in a fixed order.
 #include <algorithm>
+#include <atomic>
 
 #include "common.hpp"
 #include "launch.hpp"
@@ -518,10 +519,13 @@ int norm_rope_bwd_blocks(int64_t T, int H, int d) {
 template <int D>
 static int quad_bwd_resident() {
   constexpr int kDevs = 64;
-  static int cached[kDevs] = {};
+  static std::atomic<int> cached[kDevs] = {};  // 0: not yet queried
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kDevs) dev = -1;
-  if (dev >= 0 && cached[dev] > 0) return cached[dev];
+  if (dev >= 0) {
+    const int c = cached[dev].load(std::memory_order_relaxed);
+    if (c > 0) return c;
+  }
   int cus = 0, per_cu = 0;
   if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev < 0 ? 0 : dev) !=
           hipSuccess || cus <= 0)
@@ -530,7 +534,7 @@ static int quad_bwd_resident() {
           hipSuccess || per_cu <= 0)
     per_cu = 1;
   const int n = cus * per_cu;
-  if (dev >= 0) cached[dev] = n;
+  if (dev >= 0) cached[dev].store(n, std::memory_order_relaxed);  // same value from any thread
   return n;
 }
 
