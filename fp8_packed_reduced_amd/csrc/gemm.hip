@@ -963,9 +963,8 @@ struct QkvOut {
 // their fractional parts keep an error below ~1e-8 revolutions before the
 // fp32 sine.
 struct RopeRev {
-  double rev0;        // theta_c0 / (2 pi) of the lane's first column c0 = 4 (l / 32)
-  double r1, r5, r8;  // r, r^5 and r^8: one column on, from e = 3 to the next
-                      // group, and one group on
+  double rev0;    // theta_c0 / (2 pi) of the lane's first column c0 = 4 (l / 32)
+  double r1, r5;  // r and r^5: one column on, and from e = 3 to the next group
 };
 
 // 32 rows x 64 bf16 columns of a wave's LDS slice: row pitch 128 bytes,
@@ -1052,32 +1051,31 @@ __device__ __forceinline__ void store_qkv_tile(const v16f (&acc)[C::FM][C::FN], 
       fw[ps] = d.w;
     }
   }
+  auto unpack4 = [](uint2 w, float (&f)[4]) {
+    f[0] = __uint_as_float(w.x << 16);
+    f[1] = __uint_as_float(w.x & 0xffff0000u);
+    f[2] = __uint_as_float(w.y << 16);
+    f[3] = __uint_as_float(w.y & 0xffff0000u);
+  };
+  // Norm and rotation of both fragments first, in place in P (the two
+  // fragments' chains are independent, which gives the scheduler work to
+  // overlap); then the stores.
 #pragma unroll
   for (int i = 0; i < C::FM; ++i) {
+    if (!mixed) break;  // uniform: a tile of V columns only
     const int m = mp + 32 * i + r;  // this lane's row
-    // the product of tile columns 8 g + 4 hl + 0..3, rounded to bf16 (packed)
-    auto prod = [&](int g) { return P[i][g]; };
-    auto unpack4 = [](uint2 w, float (&f)[4]) {
-      f[0] = __uint_as_float(w.x << 16);
-      f[1] = __uint_as_float(w.x & 0xffff0000u);
-      f[2] = __uint_as_float(w.y << 16);
-      f[3] = __uint_as_float(w.y & 0xffff0000u);
-    };
-    // a head's 1 / rms and the row's position
-    float rho[HPT];
-    int b = b0, p = s0 + 32 * i + r;
+    int b = b0, p = s0 + 32 * i + r;  // its sequence and position
     if (!fast) {
       b = m / o.S;
       p = m - b * o.S;
     }
 #pragma unroll
     for (int hs = 0; hs < HPT; ++hs) {
-      rho[hs] = 0.f;
       if (!head_ok(hs)) continue;  // uniform
       float ss = 0.f;  // the row's sum of squares, bf16 pairs at a time
 #pragma unroll
       for (int g = 0; g < G; ++g) {
-        const uint2 w = prod(hs * G + g);
+        const uint2 w = P[i][hs * G + g];
         ss = dot2_bf16(w.y, w.y, dot2_bf16(w.x, w.x, ss));
       }
       {  // plus the other half of the row, in lane l ^ 32 (same sum on both)
@@ -1085,81 +1083,51 @@ __device__ __forceinline__ void store_qkv_tile(const v16f (&acc)[C::FM][C::FN], 
                                                          __float_as_uint(ss), false, false);
         ss = __uint_as_float(sw[0]) + __uint_as_float(sw[1]);
       }
-      rho[hs] = 1.0f / sqrtf(ss / (float)D + o.eps);
+      const float rho = 1.0f / sqrtf(ss / (float)D + o.eps);
       if (hl == 0 && m < M) {
         const bool isk = hq0 + hs >= o.H;
         const int hh = isk ? hq0 + hs - o.H : hq0 + hs;
         // [2][n_seq][H][S]: row (isk, b, hh, p)
-        o.rho[((int64_t)(isk * o.n_seq + b) * o.H + hh) * o.S + p] = rho[hs];
+        o.rho[((int64_t)(isk * o.n_seq + b) * o.H + hh) * o.S + p] = rho;
+      }
+      // the pairs (idx, idx + d/16), rotated in place; the row's angle in
+      // revolutions, p theta_c / (2 pi), is stepped from column to column
+      // like the frequency (opaque to the compiler: the chain is formed here,
+      // per tile, instead of being hoisted out of the tile loop, where its
+      // doubles would stay live through the matrix work)
+      double ang = rr.rev0;
+      asm volatile("" : "+v"(ang));
+      ang *= (double)p;
+#pragma unroll
+      for (int idx = 0; idx < HG; ++idx) {
+        const int glo = hs * G + idx, ghi = glo + HG;
+        float y1[4], y2[4], o1[4], o2[4];
+        unpack4(P[i][glo], y1);
+        unpack4(P[i][ghi], y2);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const float f = (float)__builtin_amdgcn_fract(ang);  // in [0, 1)
+          const float sn = __builtin_amdgcn_sinf(f);          // sin(2 pi f)
+          const float cn = __builtin_amdgcn_cosf(f);
+          ang *= e < 3 ? rr.r1 : rr.r5;
+          const float u1 = y1[e] * rho, u2 = y2[e] * rho;
+          o1[e] = u1 * cn - u2 * sn;
+          o2[e] = u2 * cn + u1 * sn;
+        }
+        P[i][glo] = make_uint2(cvt_bf16x2_rn(o1[0], o1[1]), cvt_bf16x2_rn(o1[2], o1[3]));
+        P[i][ghi] = make_uint2(cvt_bf16x2_rn(o2[0], o2[1]), cvt_bf16x2_rn(o2[2], o2[3]));
       }
     }
-    // The rotated pairs (idx, idx + d/16) of head hs whose groups fall in
-    // pass ps (groups 8 ps .. 8 ps + 7) go into the slice.  A pair with a
-    // half in each pass is formed in the first and its upper half held in
-    // registers until the second (d = 96: 4 groups; d = 128: all 8).
-    uint2 hold[8];
-    auto put = [&](int g, uint2 w) {
-      *reinterpret_cast<uint2*>(slice + slice64(r, g & 7) + 8 * hl) = w;
-    };
-    auto rotate_pairs = [&](int ps) {
+  }
 #pragma unroll
-      for (int hs = 0; hs < HPT; ++hs) {
-        if (!head_ok(hs)) continue;  // uniform
-        // the row's angle in revolutions, p theta_c / (2 pi), stepped from
-        // column to column like the frequency (opaque to the compiler: the
-        // chain is formed here, per tile, instead of being hoisted out of
-        // the tile loop, where its doubles would stay live through the
-        // matrix work)
-        double ang = rr.rev0;
-        asm volatile("" : "+v"(ang));
-        ang *= (double)p;
-#pragma unroll
-        for (int idx = 0; idx < HG; ++idx) {
-          const int glo = hs * G + idx, ghi = glo + HG;
-          const bool straddle = glo / 8 != ghi / 8;
-          const bool want_lo = glo / 8 == ps, want_hi = ghi / 8 == ps && !straddle;
-          const bool keep_hi = straddle && ps == 0;
-          if (!want_lo && !want_hi && !keep_hi) {
-            ang *= rr.r8;  // the next group's first column
-            continue;
-          }
-          float y1[4], y2[4], o1[4], o2[4];
-          unpack4(prod(glo), y1);
-          unpack4(prod(ghi), y2);
-#pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            float cn, sn;
-            const float f = (float)__builtin_amdgcn_fract(ang);  // in [0, 1)
-            sn = __builtin_amdgcn_sinf(f);                        // sin(2 pi f)
-            cn = __builtin_amdgcn_cosf(f);
-            ang *= e < 3 ? rr.r1 : rr.r5;
-            const float u1 = y1[e] * rho[hs], u2 = y2[e] * rho[hs];
-            o1[e] = u1 * cn - u2 * sn;
-            o2[e] = u2 * cn + u1 * sn;
-          }
-          const uint2 w1 = make_uint2(cvt_bf16x2_rn(o1[0], o1[1]), cvt_bf16x2_rn(o1[2], o1[3]));
-          const uint2 w2 = make_uint2(cvt_bf16x2_rn(o2[0], o2[1]), cvt_bf16x2_rn(o2[2], o2[3]));
-          if (want_lo) put(glo, w1);
-          if (want_hi) put(ghi, w2);
-          if (keep_hi) hold[ghi - 8] = w2;
-        }
-      }
-    };
+  for (int i = 0; i < C::FM; ++i) {
     // two passes of 64 columns: lane (rq, pc) stores chunk pc of rows
     // rq + 8 q, q < 4 (8 rows x 128 bytes per store instruction)
 #pragma unroll
     for (int ps = 0; ps < 2; ++ps) {
-      rotate_pairs(ps);
 #pragma unroll
-      for (int g = 8 * ps; g < 8 * ps + 8; ++g) {
-        const bool head = mixed && g < VG0;
-        if (!head) {
-          put(g, prod(g));
-        } else if (ps == 1 && g % G >= HG && (g - HG) / 8 == 0) {
-          // the upper half of a pair formed (and held) in the first pass
-          if (head_ok(g / G)) put(g, hold[g - 8]);
-        }
-      }
+      for (int g = 8 * ps; g < 8 * ps + 8; ++g)
+        *reinterpret_cast<uint2*>(slice + slice64(r, g & 7) + 8 * hl) = P[i][g];
       uint4 val[4];
 #pragma unroll
       for (int q = 0; q < 4; ++q)
@@ -1227,8 +1195,7 @@ __global__ __launch_bounds__((TileCfg<256, 128, 4, 1>::THREADS), 1) void gemm_qk
   const float alpha = sa[0] * sb[0];
   uint8_t* slice = slices + wave * 4096;
   const double r1 = rope_rev(1, D, base) / rope_rev(0, D, base);
-  const double r4 = r1 * r1 * r1 * r1;
-  const RopeRev rr{rope_rev(4 * (lane >> 5), D, base), r1, r4 * r1, r4 * r4};
+  const RopeRev rr{rope_rev(4 * (lane >> 5), D, base), r1, r1 * r1 * r1 * r1 * r1};
   int ord = 0;
   v16f acc[C::FM][C::FN];
   auto done = [&](v16f (&a)[C::FM][C::FN]) {
