@@ -17,7 +17,7 @@ using fpr::ceil_div;
 using fpr::round_up;
 
 constexpr size_t kAlign = 256;
-constexpr int kPartsW = 256;     // amax blocks for W_packed
+constexpr int kPartsW = 768;     // amax blocks for W_packed (one row each at D = 768)
 constexpr int kPartsAct = 256;   // amax blocks for x
 using fpr::kMaxTokens;
 constexpr size_t kMaxDynLds = 64 * 1024;  // dynamic LDS of one epilogue block
