@@ -62,13 +62,19 @@ STAGE_SOURCES = {
 TRACE_STEPS = 10
 
 
-def stage_work(w: dict, dw_splits: int) -> dict:
-    """Algorithmic work per launch: ("mfma", FLOP) or ("hbm", bytes)."""
+def stage_work(w: dict, dw_splits: int, two_pass: bool = False) -> dict:
+    """Algorithmic work per launch: ("mfma", FLOP) or ("hbm", bytes).  With
+    the two-pass backward, norm_rope_bwd is its amax pass (the forward's rows
+    in, nothing out) and quantize_g its second pass (the same rows and dv in,
+    the gradient codes out)."""
     T = w["n_seq"] * w["seq_len"]
     D, H, dqk, dv = w["d_model"], w["n_heads"], w["d_qk"], w["d_v"]
     N = H * (2 * dqk + dv)
     qk, vv = 2 * H * dqk, H * dv
     gemm = 2 * T * D * N
+    fwd_rows = 2 * T * qk * 2 + 4 * T * 2 * H  # dq, dk, q, k and the 1/rms of each row
+    two = {"norm_rope_bwd": ("hbm", fwd_rows),
+           "quantize_g": ("hbm", fwd_rows + 2 * T * vv + T * N)} if two_pass else {}
     return {
         "amax_w": ("hbm", 4 * D * N),
         "quantize_w": ("hbm", 4 * D * N + 2 * D * N),            # fp32 in, two e4m3 layouts out
@@ -83,6 +89,7 @@ def stage_work(w: dict, dw_splits: int) -> dict:
         "gemm_dx": ("mfma", gemm),
         "gemm_dw": ("mfma", gemm),
         "dw_reduce": ("hbm", dw_splits * 4 * D * N + 4 * D * N),
+        **two,
     }
 
 
@@ -328,6 +335,8 @@ def main():
     ap.add_argument("--no-extras", action="store_true",
                     help="skip the step-time percentiles and the large-weight quantiser "
                          "measurement (profiling runs, whose dispatches must be whole steps)")
+    ap.add_argument("--bwd-passes", type=int, choices=[1, 2], default=1,
+                    help="2: the backward in two passes that never write dQK")
     ap.add_argument("--grad-format", choices=["e4m3", "e5m2"], default="e4m3",
                     help="FP8 format of the backward's gradient codes (QKV and MLP)")
     args = ap.parse_args()
@@ -360,7 +369,8 @@ def main():
         D, H, dqk, dvw = w["d_model"], w["n_heads"], w["d_qk"], w["d_v"]
         N, nq = H * (2 * dqk + dvw), H * dqk
         gfmt = B.FORMAT_E5M2 if args.grad_format == "e5m2" else B.FORMAT_E4M3
-        dims = B.make_dims(D, H, dqk, dvw, inputs.EPS, inputs.ROPE_BASE, grad_format=gfmt)
+        dims = B.make_dims(D, H, dqk, dvw, inputs.EPS, inputs.ROPE_BASE, grad_format=gfmt,
+                           bwd_passes=args.bwd_passes)
         x = bf16(inputs.make_x(w, args.seed))
         W = torch.from_numpy(inputs.make_w(w, args.seed + 1)).to(dev)
         dq, dk, dv = (bf16(a) for a in inputs.make_dy(w, args.seed + 2))
@@ -386,12 +396,14 @@ def main():
                 B.qkv_backward(dims, n_seq, S, q, k, dq, dk, dv, saved, cache, dx, dw, ws_b)
 
         steps.append(qkv_step)
-        work.update(stage_work(w, B.layout(dims, T).dw_splits))
+        work.update(stage_work(w, B.layout(dims, T).dw_splits, args.bwd_passes == 2))
         gemm_flop += (1 if args.forward_only else 3) * 2 * T * D * N
         config.update(n_seq=n_seq, seq_len=S, d_model=D, n_heads=H, d_qk=dqk, d_v=dvw,
                       packed_n=N)
         if args.grad_format != "e4m3":
             config["grad_format"] = args.grad_format
+        if args.bwd_passes == 2:
+            config["bwd_passes"] = 2
         oracle_steps.append(
             lambda seed, tokens: _oracle_step(w, seed, tokens, not args.forward_only))
     if wm is not None:
@@ -425,6 +437,8 @@ def main():
         config.update(d_model=Dm, d_ff=F)
         if args.grad_format != "e4m3":
             config["grad_format"] = args.grad_format
+        if args.bwd_passes == 2:
+            config["bwd_passes"] = 2
         oracle_steps.append(lambda seed, tokens: _oracle_mlp_step(wm, seed, tokens))
     config["step"] = " + ".join(
         (["pack_quantize_weights + qkv_forward" + ("" if args.forward_only else " + qkv_backward")]

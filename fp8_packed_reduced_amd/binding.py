@@ -32,7 +32,8 @@ class Dims(ctypes.Structure):
     _fields_ = [("d_model", ctypes.c_int32), ("n_heads", ctypes.c_int32),
                 ("d_qk", ctypes.c_int32), ("d_v", ctypes.c_int32),
                 ("eps", ctypes.c_float), ("rope_base", ctypes.c_float),
-                ("qk_stride", ctypes.c_int32), ("grad_format", ctypes.c_int32)]
+                ("qk_stride", ctypes.c_int32), ("grad_format", ctypes.c_int32),
+                ("bwd_passes", ctypes.c_int32)]
 
     @property
     def n_packed(self) -> int:
@@ -177,10 +178,11 @@ def status_string(code: int) -> str:
 
 def make_dims(d_model: int, n_heads: int, d_qk: int = 96, d_v: int = 128,
               eps: float = 1e-6, rope_base: float = 10000.0, qk_stride: int = 0,
-              grad_format: int = FORMAT_E4M3) -> Dims:
+              grad_format: int = FORMAT_E4M3, bwd_passes: int = 0) -> Dims:
     """qk_stride > d_qk pads every q/k head row with zeros to that width;
-    grad_format FORMAT_E5M2 quantises the backward's packed gradient to e5m2."""
-    return Dims(d_model, n_heads, d_qk, d_v, eps, rope_base, qk_stride, grad_format)
+    grad_format FORMAT_E5M2 quantises the backward's packed gradient to e5m2;
+    bwd_passes 2 runs the backward in two passes that never write dQK."""
+    return Dims(d_model, n_heads, d_qk, d_v, eps, rope_base, qk_stride, grad_format, bwd_passes)
 
 
 def workspace_bytes(dims: Dims, tokens: int, which: int) -> int:

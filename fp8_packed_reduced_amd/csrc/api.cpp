@@ -26,6 +26,7 @@ struct Plan {
   int D, H, dqk, dv, qs, nq, nqk2, N;
   int64_t T, Tp;
   bool fused;  // norm/RoPE in the forward GEMM's epilogue (else qk_pre in the workspace)
+  bool two_pass;  // backward without dQK (fpr_dims.bwd_passes = 2)
   size_t s_x8, s_rho, s_xsc, saved_total;
   size_t f_part, f_qk, fwd_total;
   int f_parts;
@@ -40,6 +41,7 @@ bool dims_ok(const fpr_dims* d) {
   if (!(d->eps >= 0.0f) || !(d->rope_base > 0.0f)) return false;
   if (d->qk_stride < 0) return false;
   if (d->grad_format != FPR_FORMAT_E4M3 && d->grad_format != FPR_FORMAT_E5M2) return false;
+  if (d->bwd_passes < 0 || d->bwd_passes > 2) return false;
   return true;
 }
 
@@ -52,6 +54,7 @@ int shape_check(const fpr_dims* d) {
     return FPR_ERR_SHAPE;
   if (d->qk_stride && (d->qk_stride < d->d_qk || d->qk_stride % 8 || d->qk_stride > 1024))
     return FPR_ERR_SHAPE;
+  if (d->bwd_passes == 2 && !fpr::norm_rope_bwd_two_pass(d->d_qk)) return FPR_ERR_SHAPE;
   if (fpr::norm_rope_fwd_lds(d->n_heads, d->d_qk) > kMaxDynLds ||
       fpr::norm_rope_bwd_lds(d->n_heads, d->d_qk) > kMaxDynLds)
     return FPR_ERR_SHAPE;
@@ -77,6 +80,7 @@ Plan make_plan(const fpr_dims* d, int64_t T) {
   p.T = T;
   p.Tp = round_up(T > 0 ? T : 1, 128);
   p.fused = fpr::fused_forward(p.dqk, p.N, p.D);
+  p.two_pass = d->bwd_passes == 2;
   size_t c = 0;
   p.s_x8 = take(c, fpr::act_blocked_bytes(T, p.D));
   p.s_rho = take(c, (size_t)T * 2 * p.H * sizeof(float));
@@ -95,7 +99,7 @@ Plan make_plan(const fpr_dims* d, int64_t T) {
   p.b_parts = p.b_nr_parts + p.b_dv_parts;  // <= kMaxPartials, checked by plan_ok()
   p.b_part = take(c, (size_t)p.b_parts * 4);
   p.b_gsc = take(c, 4 * sizeof(float));
-  p.b_dqkv = take(c, (size_t)T * p.nqk2 * 2);
+  p.b_dqkv = p.two_pass ? (size_t)-1 : take(c, (size_t)T * p.nqk2 * 2);
   p.b_g8 = take(c, fpr::act_blocked_bytes(T, p.N));
   p.b_dwpart = take(c, fpr::dw_partial_bytes(p.D, p.N, p.Tp));
   p.bwd_total = c;
@@ -425,22 +429,36 @@ int qkv_backward(const fpr_dims* dims, int32_t n_seq, int32_t seq_len, const uin
   const float* rho = at<float>(saved, p.s_rho);
   uint32_t* parts = at<uint32_t>(workspace, p.b_part);
   float* gsc = at<float>(workspace, p.b_gsc);
-  uint16_t* dqkv = at<uint16_t>(workspace, p.b_dqkv);
   uint8_t* g8 = at<uint8_t>(workspace, p.b_g8);
   float* dwpart = at<float>(workspace, p.b_dwpart);
   stage("amax_dv", s, [&] {
     fpr::launch_amax_bf16(dv, T * p.H * p.dv, parts + p.b_nr_parts, p.b_dv_parts, s);
   });
-  stage("norm_rope_bwd", s, [&] {
-    fpr::launch_norm_rope_bwd(dq, dk, q, k, rho, T, seq_len, p.H, p.dqk, p.qs, dims->rope_base,
-                              dqkv, parts, s);
-  });
   const bool e5 = dims->grad_format == FPR_FORMAT_E5M2;
-  stage("quantize_g", s, [&] {
-    fpr::launch_quantize_act_split(dqkv, p.nqk2, dv, p.dv, p.H, seq_len, T, p.N, parts,
-                                   p.b_parts, gsc, cache->status, FPR_STATUS_G_NONFINITE, g8,
-                                   p.Tp, s, e5);
-  });
+  if (p.two_pass) {  // "Eight seconds", What generalizes: dQK never reaches memory
+    stage("norm_rope_bwd", s, [&] {
+      fpr::launch_norm_rope_bwd_amax(dq, dk, q, k, rho, T, seq_len, p.H, p.dqk, p.qs,
+                                     dims->rope_base, parts, s);
+    });
+    stage("quantize_g", s, [&] {
+      fpr::launch_norm_rope_bwd_codes(dq, dk, q, k, rho, T, seq_len, p.H, p.dqk, p.qs,
+                                      dims->rope_base, parts, p.b_parts, g8, p.N, s, e5);
+      fpr::launch_quantize_act_split(nullptr, p.nqk2, dv, p.dv, p.H, seq_len, T, p.N, parts,
+                                     p.b_parts, gsc, cache->status, FPR_STATUS_G_NONFINITE, g8,
+                                     p.Tp, s, e5);
+    });
+  } else {
+    uint16_t* dqkv = at<uint16_t>(workspace, p.b_dqkv);
+    stage("norm_rope_bwd", s, [&] {
+      fpr::launch_norm_rope_bwd(dq, dk, q, k, rho, T, seq_len, p.H, p.dqk, p.qs,
+                                dims->rope_base, dqkv, parts, s);
+    });
+    stage("quantize_g", s, [&] {
+      fpr::launch_quantize_act_split(dqkv, p.nqk2, dv, p.dv, p.H, seq_len, T, p.N, parts,
+                                     p.b_parts, gsc, cache->status, FPR_STATUS_G_NONFINITE, g8,
+                                     p.Tp, s, e5);
+    });
+  }
   stage("gemm_dx", s, [&] {
     fpr::launch_gemm_dx(g8, cache->w_packed, (int)T, p.D, p.N, gsc, cache->scales, dx, s, e5);
   });

@@ -122,4 +122,42 @@ __device__ inline uint32_t block_max_u32(uint32_t v, uint32_t* lds4) {
   return r;
 }
 
+// ---------------------------------------------------------------- scales
+
+// The per-tensor scales from the amax partials (block-wide; every thread
+// gets them): s = fl(amax / fmax), inv = fl(fmax / amax) with IEEE-correct
+// fp32 divisions, fmax the format's largest finite value (448 for e4m3,
+// 57344 for e5m2); (1, 1) for amax = 0, an inverse that overflows, or a
+// non-finite amax.  The block that `publishes` writes scales[0..1] and, for
+// a non-finite amax, sets `status_bit` in *status (overwriting *status
+// when `reset`).
+__device__ inline float2 tensor_scales(const uint32_t* __restrict__ partials, int parts,
+                                       uint32_t* red, bool publish, float* __restrict__ scales,
+                                       int32_t* __restrict__ status, int status_bit, bool reset,
+                                       float fmax = kE4m3Max) {
+  uint32_t m = 0;
+#pragma unroll 8
+  for (int i = threadIdx.x; i < parts; i += kThreads) m = m > partials[i] ? m : partials[i];
+  m = block_max_u32(m, red);
+  float sc = 1.0f, inv = 1.0f;
+  const bool finite = m < 0x7f800000u;
+  if (finite) {
+    const float amax = __uint_as_float(m);
+    const float i = fmax / amax;
+    if (amax != 0.0f && i <= 3.40282347e38f) {
+      sc = amax / fmax;
+      inv = i;
+    }
+  }
+  if (publish && threadIdx.x == 0) {
+    scales[0] = sc;
+    scales[1] = inv;
+    if (reset)
+      *status = finite ? 0 : status_bit;
+    else if (!finite)
+      atomicOr(status, status_bit);
+  }
+  return make_float2(sc, inv);
+}
+
 }  // namespace fpr

@@ -209,12 +209,24 @@ __device__ __forceinline__ void qc_bwd_load(QcBwdRow<D>& r, int row, int rows, i
   r.rho = f.rho[(isq ? 0 : (int64_t)f.n_seq * H * seq_len) + row_i];
 }
 
-// Finishes the row into dQK (rows of N elements) and returns the largest
-// |bf16| bit pattern.
-template <int D>
+// What the quad-chunk backward does with a finished row: write it to dQK
+// (rows of N bf16), only fold it into the amax, or encode it into the
+// gradient codes (the blocked row layout the GEMMs read, as the gradient
+// quantiser writes it, from the same bf16 values and scale).
+enum { kBwdWrite = 0, kBwdAmax = 1, kBwdCodes = 2 };
+
+struct GradCodes {
+  uint8_t* g8;               // [Tp / kActRows][kblocks][kActRows][kKBlock]
+  int kblocks;
+  const uint32_t* partials;  // every amax partial of dQKV, for the scale
+  int parts;
+};
+
+// Finishes the row and returns the largest |bf16| bit pattern of it.
+template <int D, int MODE, bool E5>
 __device__ __forceinline__ uint32_t qc_bwd_finish(const QcBwdRow<D>& r, const float2* cs,
                                                   int64_t t0, int N, uint16_t* __restrict__ dqkv,
-                                                  int l) {
+                                                  int l, const GradCodes& gc, float inv) {
   using Q = QuadChunks<D>;
   constexpr int h = Q::h, M = Q::M, HC = Q::HC;
   if (!r.ok) return 0;
@@ -232,7 +244,7 @@ __device__ __forceinline__ uint32_t qc_bwd_finish(const QcBwdRow<D>& r, const fl
   quad_partners<D>(r.g, pg, l);
   sd = quad_sum(sd);
   const float c = sd / (float)D;
-  uint16_t* dst = dqkv + (t0 + r.tt) * N + r.rr * D;
+  const int64_t t = t0 + r.tt;
   uint32_t amax = 0;
 #pragma unroll
   for (int m = 0; m < M; ++m) {
@@ -255,7 +267,18 @@ __device__ __forceinline__ uint32_t qc_bwd_finish(const QcBwdRow<D>& r, const fl
     }
     const uint4 pk = pack8_rn(o);
     amax = max(amax, absmax8(pk));
-    *reinterpret_cast<uint4*>(dst + 8 * ch) = pk;
+    if constexpr (MODE == kBwdWrite) {
+      *reinterpret_cast<uint4*>(dqkv + t * N + r.rr * D + 8 * ch) = pk;
+    } else if constexpr (MODE == kBwdCodes) {
+      const uint32_t lo = fp8x4<E5>(bf16_to_f32(pk.x & 0xffffu) * inv, bf16_to_f32(pk.x >> 16) * inv,
+                                    bf16_to_f32(pk.y & 0xffffu) * inv, bf16_to_f32(pk.y >> 16) * inv);
+      const uint32_t hi = fp8x4<E5>(bf16_to_f32(pk.z & 0xffffu) * inv, bf16_to_f32(pk.z >> 16) * inv,
+                                    bf16_to_f32(pk.w & 0xffffu) * inv, bf16_to_f32(pk.w >> 16) * inv);
+      const int col = r.rr * D + 8 * ch;  // < 2^16
+      const int64_t blk = (t / kActRows) * gc.kblocks + col / kKBlock;
+      *reinterpret_cast<uint2*>(gc.g8 + (blk * kActRows + t % kActRows) * kKBlock +
+                                col % kKBlock) = make_uint2(lo, hi);
+    }
   }
   return amax;
 }
@@ -277,16 +300,22 @@ constexpr int bwd_rows() { return D == 128 ? 2 : 3; }
 // 768 streams of 12 head rows each far apart, ran ~10% slower).  Block b
 // writes amax partial b; block 0 zeroes the slots [gridDim.x, nparts) that
 // no block owns.
-template <int D>
+// With MODE = kBwdCodes the block first folds every partial into the
+// gradient scale and writes no partial itself.
+template <int D, int MODE, bool E5>
 __global__ __launch_bounds__(kThreads) void norm_rope_bwd_qc(
     const uint16_t* __restrict__ dq, const uint16_t* __restrict__ dk, FwdRows f, int64_t T,
     int seq_len, int H, int qs, float base, uint16_t* __restrict__ dqkv,
-    uint32_t* __restrict__ partials, int nparts) {
+    uint32_t* __restrict__ partials, int nparts, GradCodes gc) {
   using Q = QuadChunks<D>;
   constexpr int h = Q::h, QUADS = kThreads / 4, RB = bwd_rows<D>();
   __shared__ double rev[h];
   __shared__ float2 cs[kQuadTT * h];
   __shared__ uint32_t red[4];
+  float inv = 1.0f;
+  if constexpr (MODE == kBwdCodes)
+    inv = tensor_scales(gc.partials, gc.parts, red, false, nullptr, nullptr, 0, false,
+                        E5 ? kE5m2Max : kE4m3Max).y;
   build_rev_table(rev, h, D, base);
   const int R = 2 * H, qkw = R * D, l = threadIdx.x & 3, quad = threadIdx.x >> 2;
   uint32_t amax = 0;
@@ -304,14 +333,17 @@ __global__ __launch_bounds__(kThreads) void norm_rope_bwd_qc(
         __syncthreads();
       }
 #pragma unroll
-      for (int j = 0; j < RB; ++j) amax = max(amax, qc_bwd_finish<D>(r[j], cs, t0, qkw, dqkv, l));
+      for (int j = 0; j < RB; ++j)
+        amax = max(amax, qc_bwd_finish<D, MODE, E5>(r[j], cs, t0, qkw, dqkv, l, gc, inv));
     }
     __syncthreads();
   }
-  amax = block_max_u32(amax << 16, red);
-  if (threadIdx.x == 0) partials[blockIdx.x] = amax;
-  if (blockIdx.x == 0)
-    for (int i = gridDim.x + threadIdx.x; i < nparts; i += kThreads) partials[i] = 0;
+  if constexpr (MODE != kBwdCodes) {
+    amax = block_max_u32(amax << 16, red);
+    if (threadIdx.x == 0) partials[blockIdx.x] = amax;
+    if (blockIdx.x == 0)
+      for (int i = gridDim.x + threadIdx.x; i < nparts; i += kThreads) partials[i] = 0;
+  }
 }
 
 // ------------------------------------------------- forward (other widths)
@@ -516,7 +548,7 @@ int norm_rope_bwd_blocks(int64_t T, int H, int d) {
 
 // Blocks of the quad backward for width D that the current device holds at
 // once, over all its CUs (queried once per device).
-template <int D>
+template <int D, int MODE, bool E5>
 static int quad_bwd_resident() {
   constexpr int kDevs = 64;
   static std::atomic<int> cached[kDevs] = {};  // 0: not yet queried
@@ -530,7 +562,8 @@ static int quad_bwd_resident() {
   if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev < 0 ? 0 : dev) !=
           hipSuccess || cus <= 0)
     cus = 256;
-  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, norm_rope_bwd_qc<D>, kThreads, 0) !=
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, norm_rope_bwd_qc<D, MODE, E5>,
+                                                   kThreads, 0) !=
           hipSuccess || per_cu <= 0)
     per_cu = 1;
   const int n = cus * per_cu;
@@ -538,13 +571,32 @@ static int quad_bwd_resident() {
   return n;
 }
 
+template <int D, int MODE, bool E5>
+static void launch_bwd_qc_as(const uint16_t* dq, const uint16_t* dk, const FwdRows& f, int64_t T,
+                             int seq_len, int H, int qs, float base, uint16_t* dqkv,
+                             uint32_t* partials, int nparts, const GradCodes& gc, hipStream_t s) {
+  const unsigned grid = (unsigned)std::min(nparts, quad_bwd_resident<D, MODE, E5>());
+  norm_rope_bwd_qc<D, MODE, E5><<<grid, kThreads, 0, s>>>(dq, dk, f, T, seq_len, H, qs, base,
+                                                          dqkv, partials, nparts, gc);
+}
+
 template <int D>
 static void launch_bwd_qc(const uint16_t* dq, const uint16_t* dk, const FwdRows& f, int64_t T,
                           int seq_len, int H, int qs, float base, uint16_t* dqkv,
-                          uint32_t* partials, int nparts, hipStream_t s) {
-  const unsigned grid = (unsigned)std::min(nparts, quad_bwd_resident<D>());
-  norm_rope_bwd_qc<D><<<grid, kThreads, 0, s>>>(dq, dk, f, T, seq_len, H, qs, base, dqkv,
-                                                 partials, nparts);
+                          uint32_t* partials, int nparts, int mode, const GradCodes& gc,
+                          bool e5, hipStream_t s) {
+  if (mode == kBwdWrite)
+    launch_bwd_qc_as<D, kBwdWrite, false>(dq, dk, f, T, seq_len, H, qs, base, dqkv, partials,
+                                          nparts, gc, s);
+  else if (mode == kBwdAmax)
+    launch_bwd_qc_as<D, kBwdAmax, false>(dq, dk, f, T, seq_len, H, qs, base, dqkv, partials,
+                                         nparts, gc, s);
+  else if (e5)
+    launch_bwd_qc_as<D, kBwdCodes, true>(dq, dk, f, T, seq_len, H, qs, base, dqkv, partials,
+                                         nparts, gc, s);
+  else
+    launch_bwd_qc_as<D, kBwdCodes, false>(dq, dk, f, T, seq_len, H, qs, base, dqkv, partials,
+                                          nparts, gc, s);
 }
 
 void launch_norm_rope_bwd(const uint16_t* dq, const uint16_t* dk, const uint16_t* q,
@@ -553,19 +605,60 @@ void launch_norm_rope_bwd(const uint16_t* dq, const uint16_t* dk, const uint16_t
                           hipStream_t s) {
   const int nparts = norm_rope_bwd_blocks(T, H, d);
   const FwdRows f{q, k, rho, (int)(T / seq_len)};
+  const GradCodes none{nullptr, 0, nullptr, 0};
   switch (d) {
     case 64:
-      return launch_bwd_qc<64>(dq, dk, f, T, seq_len, H, qs, base, dqkv, partials, nparts, s);
+      return launch_bwd_qc<64>(dq, dk, f, T, seq_len, H, qs, base, dqkv, partials, nparts,
+                               kBwdWrite, none, false, s);
     case 96:
-      return launch_bwd_qc<96>(dq, dk, f, T, seq_len, H, qs, base, dqkv, partials, nparts, s);
+      return launch_bwd_qc<96>(dq, dk, f, T, seq_len, H, qs, base, dqkv, partials, nparts,
+                               kBwdWrite, none, false, s);
     case 128:
-      return launch_bwd_qc<128>(dq, dk, f, T, seq_len, H, qs, base, dqkv, partials, nparts, s);
+      return launch_bwd_qc<128>(dq, dk, f, T, seq_len, H, qs, base, dqkv, partials, nparts,
+                                kBwdWrite, none, false, s);
     default:
       break;
   }
   const size_t lds = norm_rope_bwd_lds(H, d);
   norm_rope_bwd_kernel<kBwdTT><<<(unsigned)nparts, kThreads, lds, s>>>(
       dq, dk, f, T, seq_len, H, d, qs, base, dqkv, partials);
+}
+
+bool norm_rope_bwd_two_pass(int d) { return d == 64 || d == 96 || d == 128; }
+
+void launch_norm_rope_bwd_amax(const uint16_t* dq, const uint16_t* dk, const uint16_t* q,
+                               const uint16_t* k, const float* rho, int64_t T, int seq_len, int H,
+                               int d, int qs, float base, uint32_t* partials, hipStream_t s) {
+  const int nparts = norm_rope_bwd_blocks(T, H, d);
+  const FwdRows f{q, k, rho, (int)(T / seq_len)};
+  const GradCodes none{nullptr, 0, nullptr, 0};
+  if (d == 64)
+    launch_bwd_qc<64>(dq, dk, f, T, seq_len, H, qs, base, nullptr, partials, nparts, kBwdAmax,
+                      none, false, s);
+  else if (d == 96)
+    launch_bwd_qc<96>(dq, dk, f, T, seq_len, H, qs, base, nullptr, partials, nparts, kBwdAmax,
+                      none, false, s);
+  else if (d == 128)
+    launch_bwd_qc<128>(dq, dk, f, T, seq_len, H, qs, base, nullptr, partials, nparts, kBwdAmax,
+                       none, false, s);
+}
+
+void launch_norm_rope_bwd_codes(const uint16_t* dq, const uint16_t* dk, const uint16_t* q,
+                                const uint16_t* k, const float* rho, int64_t T, int seq_len,
+                                int H, int d, int qs, float base, const uint32_t* partials,
+                                int parts, uint8_t* g8, int N, hipStream_t s, bool e5m2) {
+  const int nparts = norm_rope_bwd_blocks(T, H, d);
+  const FwdRows f{q, k, rho, (int)(T / seq_len)};
+  const GradCodes gc{g8, (int)ceil_div(N, kKBlock), partials, parts};
+  if (d == 64)
+    launch_bwd_qc<64>(dq, dk, f, T, seq_len, H, qs, base, nullptr, nullptr, nparts, kBwdCodes,
+                      gc, e5m2, s);
+  else if (d == 96)
+    launch_bwd_qc<96>(dq, dk, f, T, seq_len, H, qs, base, nullptr, nullptr, nparts, kBwdCodes,
+                      gc, e5m2, s);
+  else if (d == 128)
+    launch_bwd_qc<128>(dq, dk, f, T, seq_len, H, qs, base, nullptr, nullptr, nparts, kBwdCodes,
+                       gc, e5m2, s);
 }
 
 }  // namespace fpr

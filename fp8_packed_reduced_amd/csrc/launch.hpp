@@ -68,6 +68,8 @@ void launch_quantize_act(const uint16_t* src, int64_t rows, int cols, const uint
 // and the rest from head-major rows: column split + h * vw + j of token t is
 // element j of row (t / vs * vh + h) * vs + t % vs of vsrc (the packed
 // gradient: dQK, then dv [n_seq][H][S][d_v]).  split % 16 == 0, vw % 16 == 0.
+// With src null, columns below split of the rows < rows are neither read nor
+// written (another kernel writes their codes); their padding rows still are.
 void launch_quantize_act_split(const uint16_t* src, int split, const uint16_t* vsrc, int vw,
                                int vh, int vs, int64_t rows, int cols, const uint32_t* partials,
                                int parts, float* scales, int32_t* status, int status_bit,
@@ -164,6 +166,21 @@ void launch_norm_rope_bwd(const uint16_t* dq, const uint16_t* dk, const uint16_t
                           const uint16_t* k, const float* rho, int64_t T, int seq_len, int H,
                           int d_qk, int qs, float base, uint16_t* dqkv, uint32_t* partials,
                           hipStream_t s);
+
+// The same backward in two passes that never write dQK (d_qk 64, 96, 128
+// only, norm_rope_bwd_two_pass()): the first leaves only the amax partials;
+// the second, after dv's partials are in too, recomputes every row and
+// encodes it with the gradient scale straight into the Q|K columns of the
+// gradient codes g8 (blocked row layout, N columns), the same codes the
+// quantiser would write from dQK.  Rows T .. of g8 are not written.
+bool norm_rope_bwd_two_pass(int d_qk);
+void launch_norm_rope_bwd_amax(const uint16_t* dq, const uint16_t* dk, const uint16_t* q,
+                               const uint16_t* k, const float* rho, int64_t T, int seq_len, int H,
+                               int d_qk, int qs, float base, uint32_t* partials, hipStream_t s);
+void launch_norm_rope_bwd_codes(const uint16_t* dq, const uint16_t* dk, const uint16_t* q,
+                                const uint16_t* k, const float* rho, int64_t T, int seq_len,
+                                int H, int d_qk, int qs, float base, const uint32_t* partials,
+                                int parts, uint8_t* g8, int N, hipStream_t s, bool e5m2);
 
 // ---- probe.hip: measured ceilings -------------------------------------------
 

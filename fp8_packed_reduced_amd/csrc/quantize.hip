@@ -98,44 +98,6 @@ __global__ __launch_bounds__(kThreads) void amax_bf16_kernel(const uint16_t* __r
   if (threadIdx.x == 0) partials[blockIdx.x] = m;
 }
 
-// ---------------------------------------------------------------- scales
-
-// The per-tensor scales from the amax partials (block-wide; every thread
-// gets them): s = fl(amax / fmax), inv = fl(fmax / amax) with IEEE-correct
-// fp32 divisions, fmax the format's largest finite value (448 for e4m3,
-// 57344 for e5m2); (1, 1) for amax = 0, an inverse that overflows, or a
-// non-finite amax.  The block that `publishes` writes scales[0..1] and, for
-// a non-finite amax, sets `status_bit` in *status (overwriting *status
-// when `reset`).
-__device__ inline float2 tensor_scales(const uint32_t* __restrict__ partials, int parts,
-                                       uint32_t* red, bool publish, float* __restrict__ scales,
-                                       int32_t* __restrict__ status, int status_bit, bool reset,
-                                       float fmax = kE4m3Max) {
-  uint32_t m = 0;
-#pragma unroll 8
-  for (int i = threadIdx.x; i < parts; i += kThreads) m = m > partials[i] ? m : partials[i];
-  m = block_max_u32(m, red);
-  float sc = 1.0f, inv = 1.0f;
-  const bool finite = m < 0x7f800000u;
-  if (finite) {
-    const float amax = __uint_as_float(m);
-    const float i = fmax / amax;
-    if (amax != 0.0f && i <= 3.40282347e38f) {
-      sc = amax / fmax;
-      inv = i;
-    }
-  }
-  if (publish && threadIdx.x == 0) {
-    scales[0] = sc;
-    scales[1] = inv;
-    if (reset)
-      *status = finite ? 0 : status_bit;
-    else if (!finite)
-      atomicOr(status, status_bit);
-  }
-  return make_float2(sc, inv);
-}
-
 // ----------------------------------------------- W_packed, both layouts
 
 // One 64 (d) x 64 (n) tile per block.  Each fp32 weight is read once; its
@@ -195,8 +157,8 @@ __global__ __launch_bounds__(kThreads) void quantize_w_kernel(
 // columns 8cc..8cc+7: it reads 8 x 16 bytes of bf16 and writes 8 x 8 bytes
 // of codes (16 threads cover a block row's 128 bytes).
 struct ActSrc {
-  const uint16_t* src;   // [rows][split]
-  int split;
+  const uint16_t* src;   // [rows][split], or null: those columns of rows < rows are
+  int split;             // written by another kernel (neither read nor written here)
   const uint16_t* vsrc;  // head-major rows of the remaining columns
   int vw, vh, vs;
 };
@@ -212,15 +174,18 @@ __global__ __launch_bounds__(kThreads) void quantize_act_kernel(
   const int cc = threadIdx.x & 15, rg = threadIdx.x >> 4;
   const int kblocks = (int)ceil_div(cols, kKBlock);
   const int c = c0 + 8 * cc;
+  // a block with only columns left to another kernel and no padding rows
+  if (!as.src && c0 + kKBlock <= as.split && t0 + kKBlock <= rows) return;
   uint4 in[8];  // the tile's loads go out before the scale reduction
   const bool head_major = c >= as.split;
+  const bool skip = !as.src && !head_major;  // real rows of these columns are not ours
   const int hv = head_major ? (c - as.split) / as.vw : 0;
   const int jv = head_major ? c - as.split - hv * as.vw : 0;
 #pragma unroll
   for (int i = 0; i < 8; ++i) {
     const int64_t t = t0 + 8 * rg + i;
     in[i] = make_uint4(0, 0, 0, 0);
-    if (t < rows && c < cols) {
+    if (t < rows && c < cols && !skip) {
       const uint16_t* p;
       if (head_major) {  // tokens < 2^24: 32-bit division
         const int b = (int)t / as.vs;
@@ -231,9 +196,9 @@ __global__ __launch_bounds__(kThreads) void quantize_act_kernel(
       in[i] = *reinterpret_cast<const uint4*>(p);
     }
   }
-  const float inv = tensor_scales(partials, parts, red, blockIdx.x == 0 && blockIdx.y == 0,
-                                  scales, status, status_bit, false,
-                                  E5 ? kE5m2Max : kE4m3Max).y;
+  const float inv = tensor_scales(partials, parts, red,
+                                  blockIdx.x == 0 && blockIdx.y == gridDim.y - 1, scales, status,
+                                  status_bit, false, E5 ? kE5m2Max : kE4m3Max).y;
   // rows rows .. tokens_padded - 1 (zero input) are written as zero codes:
   // the dW GEMM reads them as its K tail
 #pragma unroll
@@ -244,7 +209,7 @@ __global__ __launch_bounds__(kThreads) void quantize_act_kernel(
                                   bf16_to_f32(v.y & 0xffffu) * inv, bf16_to_f32(v.y >> 16) * inv);
     const uint32_t hi = fp8x4<E5>(bf16_to_f32(v.z & 0xffffu) * inv, bf16_to_f32(v.z >> 16) * inv,
                                   bf16_to_f32(v.w & 0xffffu) * inv, bf16_to_f32(v.w >> 16) * inv);
-    if (t < tokens_padded) {
+    if (t < tokens_padded && !(skip && t < rows)) {
       const int64_t blk = (t / kActRows) * kblocks + kb;
       *reinterpret_cast<uint2*>(dst + (blk * kActRows + t % kActRows) * kKBlock + 8 * cc) =
           make_uint2(lo, hi);

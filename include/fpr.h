@@ -104,6 +104,15 @@ typedef struct fpr_dims {
                           and x codes stay e4m3; dX and dW multiply e5m2 by
                           e4m3 codes on the matrix cores.  An attention-ready
                           variant: gradients keep e5m2's wider range. */
+    int32_t bwd_passes;   /* 0 or 1 (the default): the backward writes dQK in bf16
+                          to its workspace and quantises dQK and dv from there.
+                          2: two passes over the forward's rows that never
+                          write dQK, the fusion of the norm/RoPE backward into
+                          the gradient quantiser with a two-pass amax: the
+                          first pass takes dQK's amax, the second re-derives
+                          every row and encodes it with the gradient scale.
+                          The same codes, dX and dW bit for bit, and no dQK
+                          buffer in the workspace; d_qk 64, 96 or 128 only. */
 } fpr_dims;
 
 /* FP8 formats (OCP): E4M3 (max 448, no inf) and E5M2 (max 57344, with inf;
@@ -248,7 +257,8 @@ typedef struct fpr_layout {
                                 widths without the fused forward; -1 else  */
     /* in the backward workspace */
     size_t bwd_dqkv;         /* [T][2*H*d_qk] bf16, Q|K part of the packed
-                                gradient (its V part is dv itself)           */
+                                gradient (its V part is dv itself); -1 with
+                                bwd_passes = 2, which never writes it        */
     size_t bwd_g_scales;     /* [2] fp32: s_g, inv_g                         */
     size_t bwd_g8;           /* [T][N] e4m3 blocked                          */
     size_t bwd_dw_part;      /* [dw_splits][D][N] fp32 split-K dW partials   */

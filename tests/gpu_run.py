@@ -28,9 +28,9 @@ def dev_to_bits(t: torch.Tensor) -> np.ndarray:
     return t.contiguous().view(torch.int16).cpu().numpy().view(np.uint16)
 
 
-def dims_for(w: dict, qk_stride: int = 0, grad_format: int = 0):
+def dims_for(w: dict, qk_stride: int = 0, grad_format: int = 0, bwd_passes: int = 0):
     return B.make_dims(w["d_model"], w["n_heads"], w["d_qk"], w["d_v"], EPS, BASE, qk_stride,
-                       grad_format)
+                       grad_format, bwd_passes)
 
 
 def pad_rows(a: np.ndarray, width: int, fill: int) -> np.ndarray:
@@ -54,22 +54,23 @@ def unblock_rows(buf, off: int, rows: int, cols: int, lay) -> np.ndarray:
 
 
 def run(w: dict, seed: int = 42, x_bits=None, W=None, dy=None, backward: bool = True,
-        qk_stride: int = 0, grad_format: int = 0):
+        qk_stride: int = 0, grad_format: int = 0, bwd_passes: int = 0):
     """Pack, forward (and backward) on the GPU; returns a dict of numpy arrays.
 
     With qk_stride > d_qk, q and k come back with their padded rows (the
     output buffers start filled with NaN bits, so the padding seen is what
     the kernels wrote) and dq, dk (given or drawn at d_qk) go in padded with
     NaN bits, which the backward must never read.  grad_format 1 quantises the
-    packed gradient to e5m2."""
+    packed gradient to e5m2.  bwd_passes 2 runs the two-pass backward, which
+    never writes dQK (then "dqkv" is None)."""
     n_seq, S = w["n_seq"], w["seq_len"]
     T = n_seq * S
     D, H, dqk, dv = w["d_model"], w["n_heads"], w["d_qk"], w["d_v"]
     N = inputs.packed_width(w)
-    dims = dims_for(w, qk_stride, grad_format)
+    dims = dims_for(w, qk_stride, grad_format, bwd_passes)
     qs = qk_stride or dqk
     say(f"[gpu] run n_seq={n_seq} S={S} D={D} H={H} d_qk={dqk} d_v={dv} stride={qs} "
-        f"grad_format={grad_format} seed={seed}")
+        f"grad_format={grad_format} bwd_passes={bwd_passes} seed={seed}")
     if x_bits is None:
         x_bits = inputs.make_x(w, seed)
     if W is None:
@@ -119,9 +120,11 @@ def run(w: dict, seed: int = 42, x_bits=None, W=None, dy=None, backward: bool = 
         out["dy"] = dy
         # the packed gradient: its Q|K part from the workspace, its V part is
         # dv itself (the gradient quantiser reads it head-major)
-        gqk = dev_to_bits(B.view_bytes(ws_b, lay.bwd_dqkv, (T, 2 * nq), torch.bfloat16))
-        dvt = np.ascontiguousarray(np.asarray(dy[2]).transpose(0, 2, 1, 3)).reshape(T, H * dv)
-        out["dqkv"] = np.concatenate([gqk, dvt], axis=1)
+        out["dqkv"] = None
+        if lay.bwd_dqkv != B.NOT_PRESENT:
+            gqk = dev_to_bits(B.view_bytes(ws_b, lay.bwd_dqkv, (T, 2 * nq), torch.bfloat16))
+            dvt = np.ascontiguousarray(np.asarray(dy[2]).transpose(0, 2, 1, 3)).reshape(T, H * dv)
+            out["dqkv"] = np.concatenate([gqk, dvt], axis=1)
         out["g_scales"] = B.view_bytes(ws_b, lay.bwd_g_scales, (2,), torch.float32).cpu().numpy()
         g8 = unblock_rows(ws_b, lay.bwd_g8, T, N, lay)
         out["g8"], out["g8_kpad"], out["g8_tail"] = g8[:T, :N], g8[:T, N:], g8[T:Tp]

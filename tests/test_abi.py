@@ -147,8 +147,8 @@ def test_qk_stride_leaves_buffers_alone():
     assert B.saved_bytes(a, 4096) == B.saved_bytes(b, 4096)
     for which in (B.FPR_CALL_FORWARD, B.FPR_CALL_BACKWARD):
         assert B.workspace_bytes(a, 4096, which) == B.workspace_bytes(b, 4096, which)
-    assert ctypes.sizeof(B.Dims) == 32 and B.Dims.qk_stride.offset == 24
-    assert B.Dims.grad_format.offset == 28
+    assert ctypes.sizeof(B.Dims) == 36 and B.Dims.qk_stride.offset == 24
+    assert B.Dims.grad_format.offset == 28 and B.Dims.bwd_passes.offset == 32
 
 
 @pytest.mark.parametrize("fmt,ok", [(0, True), (1, True), (2, False), (-1, False)])
@@ -271,3 +271,29 @@ def test_mlp_argument_errors_are_reported_before_any_launch():
                           None) == 1
     assert L.mlp_backward(by(d), 256, p, p, 1 << 30, by(cc), p, p, 512, p, 128, p, 64,
                           None) == 4
+
+
+@pytest.mark.parametrize("passes,dqk,ok", [(0, 96, True), (1, 96, True), (2, 96, True),
+                                           (2, 64, True), (2, 128, True), (2, 48, False),
+                                           (2, 112, False), (1, 48, True), (3, 96, False),
+                                           (-1, 96, False)])
+def test_bwd_passes_support(passes, dqk, ok):
+    """The two-pass backward exists for the quad-lane widths only."""
+    d = B.make_dims(768, 6, d_qk=dqk, bwd_passes=passes)
+    assert (B.workspace_bytes(d, 256, B.FPR_CALL_BACKWARD) > 0) == ok
+
+
+def test_two_pass_backward_needs_no_dqk_buffer():
+    """Without dQK in memory the backward workspace is dQK's bytes smaller,
+    the layout reports no dQK, and nothing else moves in size."""
+    T = 4096
+    one, two = B.make_dims(768, 6), B.make_dims(768, 6, bwd_passes=2)
+    nq2 = 2 * 6 * 96
+    wb1 = B.workspace_bytes(one, T, B.FPR_CALL_BACKWARD)
+    wb2 = B.workspace_bytes(two, T, B.FPR_CALL_BACKWARD)
+    assert wb1 - wb2 >= T * nq2 * 2 and wb1 - wb2 < T * nq2 * 2 + 4096
+    assert B.layout(two, T).bwd_dqkv == B.NOT_PRESENT
+    assert B.layout(one, T).bwd_dqkv != B.NOT_PRESENT
+    assert B.saved_bytes(one, T) == B.saved_bytes(two, T)
+    for which in (B.FPR_CALL_PACK, B.FPR_CALL_FORWARD):
+        assert B.workspace_bytes(one, T, which) == B.workspace_bytes(two, T, which)
