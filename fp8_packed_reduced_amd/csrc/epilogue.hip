@@ -24,7 +24,12 @@
 // Main backward kernel (d = 64, 96, 128): four consecutive lanes own one
 // head row and every access is a whole 16-byte chunk (below); the row sum
 // takes two cross-lane steps (DPP quad permutes).  Rotation angles come
-// once per token and pair into an LDS table that all heads share.
+// once per token and pair into an LDS table that all heads share.  The
+// same kernel also runs the two-pass form that keeps dQK out of memory
+// ("Where the eight seconds were hiding", "What generalizes": bytes that
+// carry nothing new): a pass that only takes the amax, then one that
+// re-derives every row and writes its gradient codes with the scale of the
+// whole of dQKV, which that amax (and dv's) decides.
 //
 // Fallback kernels (other head widths): work item = (token, head row,
 // chunk c), a thread owns the 8 elements [8c, 8c+8) of a row and their

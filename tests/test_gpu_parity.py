@@ -396,17 +396,19 @@ def _direct_rel(gpu_bits, exact):
     return row_rel_err(bf16_to_f64(gpu_bits), bf16_to_f64(oracle.round_bf16(exact)))
 
 
-@pytest.mark.parametrize("name,wl,fmt", [
-    ("tiny", inputs.WORKLOADS["tiny"], 0), ("ragged", RAGGED, 0),
-    ("d64", dict(RAGGED, d_qk=64), 0), ("d128", dict(RAGGED, d_qk=128), 0),
-    ("e5m2", RAGGED, 1), ("step_64k", inputs.WORKLOADS["step_64k"], 0)])
-def test_two_pass_backward_matches_one_pass(name, wl, fmt):
+@pytest.mark.parametrize("name,wl,fmt,qs", [
+    ("tiny", inputs.WORKLOADS["tiny"], 0, 0), ("ragged", RAGGED, 0, 0),
+    ("d64", dict(RAGGED, d_qk=64), 0, 0), ("d128", dict(RAGGED, d_qk=128), 0, 0),
+    ("e5m2", RAGGED, 1, 0), ("padded", RAGGED, 0, 136),
+    ("step_64k", inputs.WORKLOADS["step_64k"], 0, 0)])
+def test_two_pass_backward_matches_one_pass(name, wl, fmt, qs):
     """The backward with the norm/RoPE backward fused into the gradient
     quantiser (two passes, no dQK in memory) writes the codes the one-pass
     form quantises from dQK, bit for bit, including the zero rows of the dW
-    K tail, and so the same scale, dX and dW."""
-    one = run(wl, seed=17, grad_format=fmt)
-    two = run(wl, seed=17, grad_format=fmt, bwd_passes=2)
+    K tail, and so the same scale, dX and dW (also with padded q/k rows,
+    whose NaN padding neither form may read)."""
+    one = run(wl, seed=17, grad_format=fmt, qk_stride=qs)
+    two = run(wl, seed=17, grad_format=fmt, qk_stride=qs, bwd_passes=2)
     assert two["dqkv"] is None
     for key in ("g8", "g8_kpad", "g8_tail", "g_scales", "dx", "q", "k", "v"):
         assert np.array_equal(one[key], two[key]), key
