@@ -6,7 +6,7 @@
 // The scale needs the whole tensor's amax before any code can be written,
 // so each quantiser is two kernels: per-block partial amax, then quantize,
 // whose every block first reduces the (few KB of, L2-resident) partials to
-// the scales itself; its first block also publishes them.  Partials are
+// the scales itself; one of its blocks also publishes them.  Partials are
 // fp32 bit patterns of |v| held as uint32: for non-negative floats the
 // integer order is the float order, and any NaN or Inf pattern compares
 // above every finite value.
