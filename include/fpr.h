@@ -214,7 +214,10 @@ FPR_API size_t fpr_noalloc_scratch_bytes(void);
  *   dv:     [n_seq][H][seq_len][d_v]  bf16
  *   saved:  the buffer filled by the matching qkv_forward
  *   dx:     [T][D] bf16 out
- *   dwq: [D][H*d_qk] fp32 out (row stride ldq), dwk likewise, dwv [D][H*d_v]. */
+ *   dwq: [D][H*d_qk] fp32 out (row stride ldq), dwk likewise, dwv [D][H*d_v].
+ * With dims->bwd_passes = 2 the norm/RoPE backward runs twice instead of
+ * writing dQK (its amax first, then straight into the gradient codes), and
+ * the workspace holds no dQK; the outputs are the same bit for bit. */
 FPR_API int qkv_backward(const fpr_dims* dims, int32_t n_seq, int32_t seq_len,
                  const uint16_t* q, const uint16_t* k,
                  const uint16_t* dq, const uint16_t* dk, const uint16_t* dv,
