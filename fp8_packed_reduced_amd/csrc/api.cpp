@@ -432,7 +432,8 @@ int qkv_backward(const fpr_dims* dims, int32_t n_seq, int32_t seq_len, const uin
   uint8_t* g8 = at<uint8_t>(workspace, p.b_g8);
   float* dwpart = at<float>(workspace, p.b_dwpart);
   stage("amax_dv", s, [&] {
-    fpr::launch_amax_bf16(dv, T * p.H * p.dv, parts + p.b_nr_parts, p.b_dv_parts, s);
+    // dv is read again only after the norm/RoPE backward's 450 MB
+    fpr::launch_amax_bf16(dv, T * p.H * p.dv, parts + p.b_nr_parts, p.b_dv_parts, s, true);
   });
   const bool e5 = dims->grad_format == FPR_FORMAT_E5M2;
   if (p.two_pass) {  // "Eight seconds", What generalizes: dQK never reaches memory

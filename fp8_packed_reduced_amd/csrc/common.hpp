@@ -111,6 +111,14 @@ __device__ inline uint32_t wave_max_u32(uint32_t v) {
 }
 
 // Max over the 256 threads of a block; every thread gets the result.
+// A 16-byte load marked non-temporal: data read once and streamed past the
+// caches, which then keep what the next kernels reuse.
+__device__ inline uint4 load_stream(const void* p) {
+  typedef unsigned v4u_l __attribute__((ext_vector_type(4)));
+  const v4u_l v = __builtin_nontemporal_load(reinterpret_cast<const v4u_l*>(p));
+  return make_uint4(v.x, v.y, v.z, v.w);
+}
+
 __device__ inline uint32_t block_max_u32(uint32_t v, uint32_t* lds4) {
   v = wave_max_u32(v);
   const int wave = threadIdx.x >> 6;

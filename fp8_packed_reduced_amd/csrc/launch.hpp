@@ -23,9 +23,10 @@ void launch_amax_w(const float* wq, int64_t ldq, const float* wk, int64_t ldk,
                    const float* wv, int64_t ldv, int D, int nq, int N,
                    uint32_t* partials, int parts, hipStream_t s);
 
-// Per-block max |x| of n bf16 values (n % 8 == 0).
+// Per-block max |x| of n bf16 values (n % 8 == 0).  stream: non-temporal
+// loads, for a tensor whose quantiser does not follow at once.
 void launch_amax_bf16(const uint16_t* x, int64_t n, uint32_t* partials, int parts,
-                      hipStream_t s);
+                      hipStream_t s, bool stream = false);
 
 // The quantisers below take the `parts` amax partials of their tensor and
 // reduce them to the scales (scales[0] = s, scales[1] = inv, which they also

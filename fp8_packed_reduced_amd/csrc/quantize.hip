@@ -77,7 +77,10 @@ __device__ inline uint32_t absmax_bits8(uint4 v) {
   return m;
 }
 
-// Eight independent 16-byte loads in flight per thread.
+// Eight independent 16-byte loads in flight per thread.  NT streams the
+// tensor past the caches (for a tensor that nothing reads again soon);
+// otherwise the last-level cache keeps part of it for the quantiser's read.
+template <bool NT>
 __global__ __launch_bounds__(kThreads) void amax_bf16_kernel(const uint16_t* __restrict__ x,
                                                              int64_t n,
                                                              uint32_t* __restrict__ partials) {
@@ -89,7 +92,7 @@ __global__ __launch_bounds__(kThreads) void amax_bf16_kernel(const uint16_t* __r
   for (; i + 7 * stride < vecs; i += 8 * stride) {
     uint4 a[8];
 #pragma unroll
-    for (int j = 0; j < 8; ++j) a[j] = v[i + j * stride];
+    for (int j = 0; j < 8; ++j) a[j] = NT ? load_stream(v + i + j * stride) : v[i + j * stride];
 #pragma unroll
     for (int j = 0; j < 8; ++j) m = max(m, absmax_bits8(a[j]));
   }
@@ -241,8 +244,11 @@ void launch_amax_w(const float* wq, int64_t ldq, const float* wk, int64_t ldk, c
 }
 
 void launch_amax_bf16(const uint16_t* x, int64_t n, uint32_t* partials, int parts,
-                      hipStream_t s) {
-  amax_bf16_kernel<<<parts, kThreads, 0, s>>>(x, n, partials);
+                      hipStream_t s, bool stream) {
+  if (stream)
+    amax_bf16_kernel<true><<<parts, kThreads, 0, s>>>(x, n, partials);
+  else
+    amax_bf16_kernel<false><<<parts, kThreads, 0, s>>>(x, n, partials);
 }
 
 void launch_quantize_w(const float* wq, int64_t ldq, const float* wk, int64_t ldk,
