@@ -153,6 +153,7 @@ def measured_ceilings(B, dev, reps: int = 5) -> dict:
             "read_GBps": round(nbytes / t_read / 1e9, 1),
             "mfma_TFLOPs": round(flop / t_mfma / 1e12, 1),
             "how": "library probe kernels in this run: streaming copy and read of 1 GiB "
+                   "(non-temporal 16-byte loads, four in flight per thread, 64 blocks per CU) "
                    "(cold: 4x the last-level cache; a kernel whose inputs partly hit that "
                    "cache can exceed them), bare FP8 32x32x64 MFMA loop; HIP events, "
                    "median of 5"}

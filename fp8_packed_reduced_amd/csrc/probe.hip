@@ -1,10 +1,14 @@
 // Measurement probes for gfx950: the ceilings the path's kernels are held
 // against next to the published peaks, measured on the same device in the
 // same run.
-//  - copy: a streaming copy (16-byte loads and stores, grid-stride), the
-//    practical HBM ceiling of the read-and-write kernels;
-//  - read: a streaming read (16-byte loads folded into one word per block),
-//    that of the read-only (amax) kernels;
+//  - copy: a streaming copy (16-byte non-temporal loads and stores, four in
+//    flight per thread, grid-stride), the practical HBM ceiling of the
+//    read-and-write kernels;
+//  - read: a streaming read (16-byte non-temporal loads, four in flight,
+//    folded into one word per block), that of the read-only (amax) kernels.
+//    Of the forms tried (plain or non-temporal, four to sixteen loads in
+//    flight, 4 to 64 blocks per CU, grid-stride or one contiguous chunk per
+//    block) these were the fastest, by up to 20% over plain loads;
 //  - mfma: back-to-back v_mfma_scale_f32_32x32x64_f8f6f4 on register
 //    operands, four independent accumulators per wave and two waves per
 //    SIMD, the practical FP8 matrix-core ceiling (no loads, no LDS).
@@ -17,18 +21,19 @@ typedef float v16f_p __attribute__((ext_vector_type(16)));
 
 typedef unsigned v4u_p __attribute__((ext_vector_type(4)));
 
-// Eight 16-byte loads in flight per thread, then eight streaming stores.
+// Four 16-byte non-temporal loads in flight per thread, then four
+// streaming stores.
 __global__ __launch_bounds__(kThreads) void probe_copy_kernel(const uint4* __restrict__ src,
                                                               uint4* __restrict__ dst,
                                                               int64_t n) {
   const int64_t stride = (int64_t)gridDim.x * kThreads;
   int64_t i = (int64_t)blockIdx.x * kThreads + threadIdx.x;
-  for (; i + 7 * stride < n; i += 8 * stride) {
-    uint4 a[8];
+  for (; i + 3 * stride < n; i += 4 * stride) {
+    uint4 a[4];
 #pragma unroll
-    for (int j = 0; j < 8; ++j) a[j] = src[i + j * stride];
+    for (int j = 0; j < 4; ++j) a[j] = load_stream(src + i + j * stride);
 #pragma unroll
-    for (int j = 0; j < 8; ++j) {
+    for (int j = 0; j < 4; ++j) {
       const v4u_p x = {a[j].x, a[j].y, a[j].z, a[j].w};
       __builtin_nontemporal_store(x, reinterpret_cast<v4u_p*>(dst + i + j * stride));
     }
@@ -43,12 +48,12 @@ __global__ __launch_bounds__(kThreads) void probe_read_kernel(const uint4* __res
   const int64_t stride = (int64_t)gridDim.x * kThreads;
   int64_t i = (int64_t)blockIdx.x * kThreads + threadIdx.x;
   uint32_t x = 0;
-  for (; i + 7 * stride < n; i += 8 * stride) {
-    uint4 a[8];
+  for (; i + 3 * stride < n; i += 4 * stride) {
+    uint4 a[4];
 #pragma unroll
-    for (int j = 0; j < 8; ++j) a[j] = src[i + j * stride];
+    for (int j = 0; j < 4; ++j) a[j] = load_stream(src + i + j * stride);
 #pragma unroll
-    for (int j = 0; j < 8; ++j) x ^= a[j].x ^ a[j].y ^ a[j].z ^ a[j].w;
+    for (int j = 0; j < 4; ++j) x ^= a[j].x ^ a[j].y ^ a[j].z ^ a[j].w;
   }
   for (; i < n; i += stride) {
     const uint4 a = src[i];
