@@ -196,7 +196,7 @@ __global__ __launch_bounds__(kThreads) void quantize_act_kernel(
       } else {
         p = as.src + t * as.split + c;
       }
-      in[i] = *reinterpret_cast<const uint4*>(p);
+      in[i] = load_stream(p);  // read once: streamed past the caches
     }
   }
   const float inv = tensor_scales(partials, parts, red,
