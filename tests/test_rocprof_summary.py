@@ -138,3 +138,19 @@ def test_counter_lines_are_keyed_to_kernel_code_not_comments(tmp_path, monkeypat
     f.write_text("int f(int x) { return x + 2; }\n")
     assert bench.source_hash("gemm_fwd") != h
     assert bench.read_traffic("w", "gemm_fwd") is None
+
+
+def test_two_pass_backward_work_accounting():
+    """With two backward passes the norm/RoPE stage reads the forward's rows
+    and writes nothing, and the gradient-code stage reads them again with dv
+    and writes the codes; every other stage keeps its work."""
+    w = dict(n_seq=1, seq_len=65536, d_model=768, n_heads=6, d_qk=96, d_v=128)
+    T, H, dqk, dv = 65536, 6, 96, 128
+    N, qk = H * (2 * dqk + dv), 2 * H * dqk
+    one, two = bench.stage_work(w, 5), bench.stage_work(w, 5, two_pass=True)
+    rows = 2 * T * qk * 2 + 4 * T * 2 * H
+    assert one["norm_rope_bwd"] == ("hbm", rows + 2 * T * qk)
+    assert two["norm_rope_bwd"] == ("hbm", rows)
+    assert two["quantize_g"] == ("hbm", rows + 2 * T * H * dv + T * N)
+    assert {k: v for k, v in one.items() if k not in ("norm_rope_bwd", "quantize_g")} == \
+        {k: v for k, v in two.items() if k not in ("norm_rope_bwd", "quantize_g")}
