@@ -46,7 +46,7 @@ CALIB_FLOATS = 64 << 20   # counter calibration: encoder over 256 MiB of fp32
 STAGE_SOURCES = {
     "amax_w": "quantize.hip", "quantize_w": "quantize.hip",
     "amax_x": "quantize.hip", "quantize_x": "quantize.hip", "quantize_g": "quantize.hip",
-    "amax_dv": "quantize.hip",
+    "amax_dv": "quantize.hip", "amax_wx": "quantize.hip", "quantize_wx": "quantize.hip",
     "gemm_fwd": "gemm.hip", "gemm_dx": "gemm.hip", "gemm_dw": "gemm.hip",
     "dw_reduce": "gemm.hip", "norm_rope_fwd": "epilogue.hip", "norm_rope_bwd": "epilogue.hip",
     "mlp_amax_w": "quantize.hip", "mlp_quantize_w": "quantize.hip",
@@ -80,6 +80,9 @@ def stage_work(w: dict, dw_splits: int, two_pass: bool = False) -> dict:
         "quantize_w": ("hbm", 4 * D * N + 2 * D * N),            # fp32 in, two e4m3 layouts out
         "amax_x": ("hbm", 2 * T * D),
         "quantize_x": ("hbm", 2 * T * D + T * D),                # bf16 in, e4m3 out
+        # qkv_pack_forward: the two above pairs, each in one launch
+        "amax_wx": ("hbm", 4 * D * N + 2 * T * D),
+        "quantize_wx": ("hbm", 6 * D * N + 3 * T * D),
         "gemm_fwd": ("mfma", gemm),   # with the norm/RoPE in its epilogue at d_qk 64/96/128
         "norm_rope_fwd": ("hbm", 2 * T * qk + 2 * T * qk),       # other widths: pre-norm in, q|k out
         # dq, dk, q, k and the 1/rms of each Q/K head row in; dQK out
@@ -338,6 +341,10 @@ def main():
                          "measurement (profiling runs, whose dispatches must be whole steps)")
     ap.add_argument("--bwd-passes", type=int, choices=[1, 2], default=1,
                     help="2: the backward in two passes that never write dQK")
+    ap.add_argument("--pack-forward", choices=["combined", "separate"], default="combined",
+                    help="combined: the weight pack and the forward in one qkv_pack_forward "
+                         "call, whose quantiser launches serve W and x together; separate: "
+                         "pack_quantize_weights, then qkv_forward")
     ap.add_argument("--grad-format", choices=["e4m3", "e5m2"], default="e4m3",
                     help="FP8 format of the backward's gradient codes (QKV and MLP)")
     args = ap.parse_args()
@@ -390,9 +397,17 @@ def main():
         dx = torch.empty((T, D), dtype=torch.bfloat16, device=dev)
         dw = torch.empty((D, N), dtype=torch.float32, device=dev)
 
+        combined = args.pack_forward == "combined"
+        if combined:
+            ws_f = torch.empty(B.workspace_bytes(dims, T, B.FPR_CALL_PACK_FORWARD),
+                               dtype=torch.uint8, device=dev)
+
         def qkv_step():
-            B.pack_quantize_weights(dims, wq, wk, wv, cache, workspace=ws_p)
-            B.qkv_forward(dims, n_seq, S, x, cache, q, k, v, saved, ws_f)
+            if combined:
+                B.qkv_pack_forward(dims, wq, wk, wv, cache, n_seq, S, x, q, k, v, saved, ws_f)
+            else:
+                B.pack_quantize_weights(dims, wq, wk, wv, cache, workspace=ws_p)
+                B.qkv_forward(dims, n_seq, S, x, cache, q, k, v, saved, ws_f)
             if not args.forward_only:
                 B.qkv_backward(dims, n_seq, S, q, k, dq, dk, dv, saved, cache, dx, dw, ws_b)
 
@@ -405,6 +420,8 @@ def main():
             config["grad_format"] = args.grad_format
         if args.bwd_passes == 2:
             config["bwd_passes"] = 2
+        if not combined:
+            config["pack_forward"] = "separate"
         oracle_steps.append(
             lambda seed, tokens: _oracle_step(w, seed, tokens, not args.forward_only))
     if wm is not None:
@@ -441,8 +458,10 @@ def main():
         if args.bwd_passes == 2:
             config["bwd_passes"] = 2
         oracle_steps.append(lambda seed, tokens: _oracle_mlp_step(wm, seed, tokens))
+    qkv_calls = ("qkv_pack_forward" if args.pack_forward == "combined" else
+                 "pack_quantize_weights + qkv_forward")
     config["step"] = " + ".join(
-        (["pack_quantize_weights + qkv_forward" + ("" if args.forward_only else " + qkv_backward")]
+        ([qkv_calls + ("" if args.forward_only else " + qkv_backward")]
          if w is not None else []) +
         (["mlp_pack_quantize_weights + mlp_forward + mlp_backward"] if wm is not None else []))
     config["seed"] = args.seed

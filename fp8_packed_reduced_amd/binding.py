@@ -16,7 +16,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(HERE, "libfpr.so")
 HEADER = os.path.join(os.path.dirname(HERE), "include", "fpr.h")
 
-FPR_CALL_PACK, FPR_CALL_FORWARD, FPR_CALL_BACKWARD = 0, 1, 2
+FPR_CALL_PACK, FPR_CALL_FORWARD, FPR_CALL_BACKWARD, FPR_CALL_PACK_FORWARD = 0, 1, 2, 3
 STATUS_W_NONFINITE, STATUS_X_NONFINITE, STATUS_G_NONFINITE, STATUS_H_NONFINITE = 1, 2, 4, 8
 FORMAT_E4M3, FORMAT_E5M2 = 0, 1
 NOT_PRESENT = ctypes.c_size_t(-1).value  # a layout offset of "(size_t)-1"
@@ -128,6 +128,9 @@ def load():
     L.qkv_forward.restype = ctypes.c_int
     L.qkv_forward.argtypes = [P(Dims), _I32, _I32, _V, P(_CacheC), _V, _V, _V, _V, _SZ, _V,
                               _SZ, _V]
+    L.qkv_pack_forward.restype = ctypes.c_int
+    L.qkv_pack_forward.argtypes = [P(Dims), _V, _I64, _V, _I64, _V, _I64, P(_CacheC), _I32, _I32,
+                                   _V, _V, _V, _V, _V, _SZ, _V, _SZ, _V]
     L.qkv_forward_noalloc.restype = ctypes.c_int
     L.qkv_forward_noalloc.argtypes = [P(Dims), _I32, _I32, _V, P(_CacheC), _V, _V, _V, _V, _SZ,
                                       _V]
@@ -287,6 +290,43 @@ def qkv_forward(dims: Dims, n_seq: int, seq_len: int, x, cache: WeightCache, q=N
                             saved.numel(), workspace.data_ptr(), workspace.numel(), _stream(dev))
     if rc:
         raise FprError(rc, "qkv_forward")
+    return q, k, v, saved
+
+
+def qkv_pack_forward(dims: Dims, wq, wk, wv, cache: WeightCache, n_seq: int, seq_len: int, x,
+                     q=None, k=None, v=None, saved=None, workspace=None):
+    """pack_quantize_weights then qkv_forward in one call (shared launches).
+    Returns (q, k, v, saved)."""
+    T = n_seq * seq_len
+    D, nq, nv = dims.d_model, dims.n_q, dims.n_heads * dims.d_v
+    H, dqk, dv = dims.n_heads, dims.qk_row, dims.d_v
+    ldq = _need_rows(wq, D, nq, "wq")
+    ldk = _need_rows(wk, D, nq, "wk")
+    ldv = _need_rows(wv, D, nv, "wv")
+    dev = x.device
+    _need(x, torch.bfloat16, (T, D), "x")
+    if q is None:
+        q = torch.empty((n_seq, H, seq_len, dqk), dtype=torch.bfloat16, device=dev)
+    if k is None:
+        k = torch.empty((n_seq, H, seq_len, dqk), dtype=torch.bfloat16, device=dev)
+    if v is None:
+        v = torch.empty((n_seq, H, seq_len, dv), dtype=torch.bfloat16, device=dev)
+    _need(q, torch.bfloat16, (n_seq, H, seq_len, dqk), "q")
+    _need(k, torch.bfloat16, (n_seq, H, seq_len, dqk), "k")
+    _need(v, torch.bfloat16, (n_seq, H, seq_len, dv), "v")
+    if saved is None:
+        saved = torch.empty(saved_bytes(dims, T), dtype=torch.uint8, device=dev)
+    if workspace is None:
+        workspace = torch.empty(workspace_bytes(dims, T, FPR_CALL_PACK_FORWARD),
+                                dtype=torch.uint8, device=dev)
+    cc = cache.c()
+    rc = load().qkv_pack_forward(ctypes.byref(dims), wq.data_ptr(), ldq, wk.data_ptr(), ldk,
+                                 wv.data_ptr(), ldv, ctypes.byref(cc), n_seq, seq_len,
+                                 x.data_ptr(), q.data_ptr(), k.data_ptr(), v.data_ptr(),
+                                 saved.data_ptr(), saved.numel(), workspace.data_ptr(),
+                                 workspace.numel(), _stream(dev))
+    if rc:
+        raise FprError(rc, "qkv_pack_forward")
     return q, k, v, saved
 
 

@@ -272,6 +272,38 @@ void* device_scratch() {
   return g_scratch_ptr[dev];
 }
 
+// qkv_pack_forward's workspace: the weight pack's, then the forward's.
+size_t pack_forward_off(const Plan& p) { return (size_t)round_up((int64_t)p.pack_total, kAlign); }
+size_t pack_forward_bytes(const Plan& p) { return pack_forward_off(p) + p.fwd_total; }
+
+// The forward after x8 and its scales exist: the packed GEMM with the norm,
+// RoPE and head-major stores in its epilogue, or, for other head widths,
+// the GEMM and then the norm/RoPE kernel.
+void forward_gemm(const fpr_dims* dims, const Plan& p, int32_t n_seq, int32_t seq_len,
+                  const fpr_weight_cache* cache, uint16_t* q, uint16_t* k, uint16_t* v,
+                  void* saved, void* workspace, hipStream_t s) {
+  const int64_t T = p.T;
+  float* xsc = at<float>(saved, p.s_xsc);
+  uint8_t* x8 = at<uint8_t>(saved, p.s_x8);
+  float* rho = at<float>(saved, p.s_rho);
+  if (p.fused) {
+    stage("gemm_fwd", s, [&] {
+      fpr::launch_gemm_qkv_fwd(x8, cache->w_packed_t, n_seq, seq_len, p.D, p.H, p.dqk, p.dv, p.qs,
+                               dims->eps, dims->rope_base, xsc, cache->scales, q, k, v, rho, s);
+    });
+  } else {
+    uint16_t* qk = at<uint16_t>(workspace, p.f_qk);
+    stage("gemm_fwd", s, [&] {
+      fpr::launch_gemm_fwd(x8, cache->w_packed_t, (int)T, p.N, p.D, xsc, cache->scales, qk,
+                           p.nqk2, v, p.H, p.dv, seq_len, s);
+    });
+    stage("norm_rope_fwd", s, [&] {
+      fpr::launch_norm_rope_fwd(qk, T, seq_len, p.H, p.dqk, p.qs, dims->eps, dims->rope_base, q,
+                                k, rho, s);
+    });
+  }
+}
+
 }  // namespace
 
 extern "C" {
@@ -284,6 +316,7 @@ size_t fpr_workspace_bytes(const fpr_dims* dims, int64_t tokens, int which) {
   if (!plan_ok(p)) return 0;
   if (which == FPR_CALL_FORWARD) return p.fwd_total;
   if (which == FPR_CALL_BACKWARD) return p.bwd_total;
+  if (which == FPR_CALL_PACK_FORWARD) return pack_forward_bytes(p);
   return 0;
 }
 
@@ -361,28 +394,52 @@ int qkv_forward(const fpr_dims* dims, int32_t n_seq, int32_t seq_len, const uint
   uint32_t* parts = at<uint32_t>(workspace, p.f_part);
   float* xsc = at<float>(saved, p.s_xsc);
   uint8_t* x8 = at<uint8_t>(saved, p.s_x8);
-  float* rho = at<float>(saved, p.s_rho);
   stage("amax_x", s, [&] { fpr::launch_amax_bf16(x, T * p.D, parts, p.f_parts, s); });
   stage("quantize_x", s, [&] {
     fpr::launch_quantize_act(x, T, p.D, parts, p.f_parts, xsc, cache->status,
                              FPR_STATUS_X_NONFINITE, x8, p.Tp, s);
   });
-  if (p.fused) {
-    stage("gemm_fwd", s, [&] {
-      fpr::launch_gemm_qkv_fwd(x8, cache->w_packed_t, n_seq, seq_len, p.D, p.H, p.dqk, p.dv, p.qs,
-                               dims->eps, dims->rope_base, xsc, cache->scales, q, k, v, rho, s);
-    });
-  } else {
-    uint16_t* qk = at<uint16_t>(workspace, p.f_qk);
-    stage("gemm_fwd", s, [&] {
-      fpr::launch_gemm_fwd(x8, cache->w_packed_t, (int)T, p.N, p.D, xsc, cache->scales, qk,
-                           p.nqk2, v, p.H, p.dv, seq_len, s);
-    });
-    stage("norm_rope_fwd", s, [&] {
-      fpr::launch_norm_rope_fwd(qk, T, seq_len, p.H, p.dqk, p.qs, dims->eps, dims->rope_base, q,
-                                k, rho, s);
-    });
-  }
+  forward_gemm(dims, p, n_seq, seq_len, cache, q, k, v, saved, workspace, s);
+  return finish();
+}
+
+int qkv_pack_forward(const fpr_dims* dims, const float* wq, int64_t ldq, const float* wk,
+                     int64_t ldk, const float* wv, int64_t ldv, const fpr_weight_cache* cache,
+                     int32_t n_seq, int32_t seq_len, const uint16_t* x, uint16_t* q, uint16_t* k,
+                     uint16_t* v, void* saved, size_t saved_bytes, void* workspace,
+                     size_t workspace_bytes, void* stream) {
+  int rc = shape_check(dims);
+  if (rc) return rc;
+  int64_t T;
+  if ((rc = tokens_check(n_seq, seq_len, &T)) || (rc = cache_check(cache))) return rc;
+  const Plan p = make_plan(dims, T);
+  if ((rc = ld_check(ldq, p.nq, wq)) || (rc = ld_check(ldk, p.nq, wk)) ||
+      (rc = ld_check(ldv, (int64_t)p.H * p.dv, wv)))
+    return rc;
+  if (!x || !q || !k || !v || !saved || !workspace) return FPR_ERR_ARG;
+  if (!al16(x) || !al16(q) || !al16(k) || !al16(v) || !al16(saved) || !al16(workspace))
+    return FPR_ERR_ALIGN;
+  if (!plan_ok(p)) return FPR_ERR_SHAPE;
+  if (saved_bytes < p.saved_total || workspace_bytes < pack_forward_bytes(p))
+    return FPR_ERR_WORKSPACE;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  (void)hipGetLastError();
+  uint32_t* pw = at<uint32_t>(workspace, p.p_part);
+  void* fws = static_cast<uint8_t*>(workspace) + pack_forward_off(p);
+  uint32_t* px = at<uint32_t>(fws, p.f_part);
+  float* xsc = at<float>(saved, p.s_xsc);
+  uint8_t* x8 = at<uint8_t>(saved, p.s_x8);
+  stage("amax_wx", s, [&] {
+    fpr::launch_amax_wx(wq, ldq, wk, ldk, wv, ldv, p.D, p.nq, p.N, pw, kPartsW, x, T * p.D, px,
+                        p.f_parts, cache->status, s);
+  });
+  stage("quantize_wx", s, [&] {
+    fpr::launch_quantize_wx(wq, ldq, wk, ldk, wv, ldv, p.D, p.nq, p.N, pw, kPartsW,
+                            cache->scales, cache->w_packed, cache->w_packed_t,
+                            FPR_STATUS_W_NONFINITE, x, T, p.D, px, p.f_parts, xsc,
+                            FPR_STATUS_X_NONFINITE, x8, p.Tp, cache->status, s);
+  });
+  forward_gemm(dims, p, n_seq, seq_len, cache, q, k, v, saved, fws, s);
   return finish();
 }
 

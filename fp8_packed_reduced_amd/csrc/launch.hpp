@@ -43,6 +43,21 @@ void launch_quantize_w(const float* wq, int64_t ldq, const float* wk, int64_t ld
                        int status_bit, uint8_t* w_packed, uint8_t* w_packed_t, hipStream_t s,
                        bool reset_status = true);
 
+// The weight pack and x's quantiser sharing launches: one launch takes both
+// amaxes (parts_w W blocks, then parts_x x blocks; block 0 clears *status),
+// the next writes both codes (W's both layouts and scales with bit w_bit,
+// x8 and its scales with x_bit, as the separate launchers do).
+void launch_amax_wx(const float* wq, int64_t ldq, const float* wk, int64_t ldk, const float* wv,
+                    int64_t ldv, int D, int nq, int N, uint32_t* pw, int parts_w,
+                    const uint16_t* x, int64_t n, uint32_t* px, int parts_x, int32_t* status,
+                    hipStream_t s);
+void launch_quantize_wx(const float* wq, int64_t ldq, const float* wk, int64_t ldk,
+                        const float* wv, int64_t ldv, int D, int nq, int N, const uint32_t* pw,
+                        int parts_w, float* w_scales, uint8_t* w_packed, uint8_t* w_packed_t,
+                        int w_bit, const uint16_t* x, int64_t rows, int cols, const uint32_t* px,
+                        int parts_x, float* x_scales, int x_bit, uint8_t* x8,
+                        int64_t tokens_padded, int32_t* status, hipStream_t s);
+
 // Blocked layout of the FP8 activation copies x8 and g8, which only the
 // GEMMs read.  A matrix of R rows (tokens) and K columns (K contiguous) is
 // stored as blocks of kActRows rows x kKBlock bytes: block

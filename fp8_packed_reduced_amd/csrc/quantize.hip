@@ -25,42 +25,57 @@ __device__ inline float4 load_w4(const float* wq, int64_t ldq, const float* wk, 
   return *reinterpret_cast<const float4*>(p);
 }
 
-// Block b takes rows b, b + grid, ... of the logical [D][N] matrix; its
+// The three pieces of the logical W_packed [D][N]: columns [0, nq) from wq,
+// [nq, 2 nq) from wk, the rest from wv, each with its own row stride.
+struct WSrc {
+  const float* wq;
+  int64_t ldq;
+  const float* wk;
+  int64_t ldk;
+  const float* wv;
+  int64_t ldv;
+  int D, nq, N;
+};
+
+// Block b of nb takes rows b, b + nb, ... of the logical [D][N] matrix; its
 // threads stride over a row's float4s (no index division), four loads in
 // flight per thread where the row is long enough.
-__global__ __launch_bounds__(kThreads) void amax_w_kernel(
-    const float* __restrict__ wq, int64_t ldq, const float* __restrict__ wk, int64_t ldk,
-    const float* __restrict__ wv, int64_t ldv, int D, int nq, int N,
-    uint32_t* __restrict__ partials) {
-  __shared__ uint32_t red[4];
-  const int quads = N / 4;
+__device__ __forceinline__ void amax_w_block(const WSrc& w, int b, int nb,
+                                             uint32_t* __restrict__ partials, uint32_t* red) {
+  const int quads = w.N / 4;
   uint32_t m = 0;
-  auto fold = [&](float4 w) {
-    uint32_t a = __float_as_uint(w.x) & 0x7fffffffu;
-    uint32_t b = __float_as_uint(w.y) & 0x7fffffffu;
-    uint32_t c = __float_as_uint(w.z) & 0x7fffffffu;
-    uint32_t e = __float_as_uint(w.w) & 0x7fffffffu;
-    a = a > b ? a : b;
-    c = c > e ? c : e;
+  auto fold = [&](float4 v) {
+    uint32_t a = __float_as_uint(v.x) & 0x7fffffffu;
+    uint32_t c = __float_as_uint(v.y) & 0x7fffffffu;
+    uint32_t e = __float_as_uint(v.z) & 0x7fffffffu;
+    uint32_t f = __float_as_uint(v.w) & 0x7fffffffu;
     a = a > c ? a : c;
+    e = e > f ? e : f;
+    a = a > e ? a : e;
     m = m > a ? m : a;
   };
-  for (int d = blockIdx.x; d < D; d += gridDim.x) {
+  auto ld = [&](int d, int n) { return load_w4(w.wq, w.ldq, w.wk, w.ldk, w.wv, w.ldv, w.nq, d, n); };
+  for (int d = b; d < w.D; d += nb) {
     int q = threadIdx.x;
     for (; q + 3 * kThreads < quads; q += 4 * kThreads) {
-      const float4 w0 = load_w4(wq, ldq, wk, ldk, wv, ldv, nq, d, 4 * q);
-      const float4 w1 = load_w4(wq, ldq, wk, ldk, wv, ldv, nq, d, 4 * (q + kThreads));
-      const float4 w2 = load_w4(wq, ldq, wk, ldk, wv, ldv, nq, d, 4 * (q + 2 * kThreads));
-      const float4 w3 = load_w4(wq, ldq, wk, ldk, wv, ldv, nq, d, 4 * (q + 3 * kThreads));
+      const float4 w0 = ld(d, 4 * q);
+      const float4 w1 = ld(d, 4 * (q + kThreads));
+      const float4 w2 = ld(d, 4 * (q + 2 * kThreads));
+      const float4 w3 = ld(d, 4 * (q + 3 * kThreads));
       fold(w0);
       fold(w1);
       fold(w2);
       fold(w3);
     }
-    for (; q < quads; q += kThreads) fold(load_w4(wq, ldq, wk, ldk, wv, ldv, nq, d, 4 * q));
+    for (; q < quads; q += kThreads) fold(ld(d, 4 * q));
   }
   m = block_max_u32(m, red);
-  if (threadIdx.x == 0) partials[blockIdx.x] = m;
+  if (threadIdx.x == 0) partials[b] = m;
+}
+
+__global__ __launch_bounds__(kThreads) void amax_w_kernel(WSrc w, uint32_t* __restrict__ partials) {
+  __shared__ uint32_t red[4];
+  amax_w_block(w, blockIdx.x, gridDim.x, partials, red);
 }
 
 // --------------------------------------------------------- amax of bf16
@@ -77,18 +92,17 @@ __device__ inline uint32_t absmax_bits8(uint4 v) {
   return m;
 }
 
-// Eight independent 16-byte loads in flight per thread.  NT streams the
-// tensor past the caches (for a tensor that nothing reads again soon);
-// otherwise the last-level cache keeps part of it for the quantiser's read.
+// Block b of nb: eight independent 16-byte loads in flight per thread.  NT
+// streams the tensor past the caches (for a tensor that nothing reads again
+// soon); otherwise the last-level cache keeps part of it for the quantiser.
 template <bool NT>
-__global__ __launch_bounds__(kThreads) void amax_bf16_kernel(const uint16_t* __restrict__ x,
-                                                             int64_t n,
-                                                             uint32_t* __restrict__ partials) {
-  __shared__ uint32_t red[4];
-  const int64_t vecs = n / 8, stride = (int64_t)gridDim.x * kThreads;
+__device__ __forceinline__ void amax_bf16_block(const uint16_t* __restrict__ x, int64_t n, int b,
+                                                int nb, uint32_t* __restrict__ partials,
+                                                uint32_t* red) {
+  const int64_t vecs = n / 8, stride = (int64_t)nb * kThreads;
   const uint4* v = reinterpret_cast<const uint4*>(x);
   uint32_t m = 0;
-  int64_t i = blockIdx.x * (int64_t)kThreads + threadIdx.x;
+  int64_t i = b * (int64_t)kThreads + threadIdx.x;
   for (; i + 7 * stride < vecs; i += 8 * stride) {
     uint4 a[8];
 #pragma unroll
@@ -98,25 +112,31 @@ __global__ __launch_bounds__(kThreads) void amax_bf16_kernel(const uint16_t* __r
   }
   for (; i < vecs; i += stride) m = max(m, absmax_bits8(v[i]));
   m = block_max_u32(m << 16, red);
-  if (threadIdx.x == 0) partials[blockIdx.x] = m;
+  if (threadIdx.x == 0) partials[b] = m;
+}
+
+template <bool NT>
+__global__ __launch_bounds__(kThreads) void amax_bf16_kernel(const uint16_t* __restrict__ x,
+                                                             int64_t n,
+                                                             uint32_t* __restrict__ partials) {
+  __shared__ uint32_t red[4];
+  amax_bf16_block<NT>(x, n, blockIdx.x, gridDim.x, partials, red);
 }
 
 // ----------------------------------------------- W_packed, both layouts
 
-// One 64 (d) x 64 (n) tile per block.  Each fp32 weight is read once; its
-// code goes straight to w_packed[d][n] and, through an LDS transpose, to
-// w_packed_t[n][d].
-__global__ __launch_bounds__(kThreads) void quantize_w_kernel(
-    const float* __restrict__ wq, int64_t ldq, const float* __restrict__ wk, int64_t ldk,
-    const float* __restrict__ wv, int64_t ldv, int D, int nq, int N,
-    const uint32_t* __restrict__ partials, int parts, float* __restrict__ scales,
-    int32_t* __restrict__ status, int status_bit, uint8_t* __restrict__ w_packed,
-    uint8_t* __restrict__ w_packed_t, bool reset) {
-  __shared__ uint8_t tile_t[64][64 + 4];
-  __shared__ uint32_t red[4];
-  const int n0 = blockIdx.x * 64, d0 = blockIdx.y * 64;
-  const float inv = tensor_scales(partials, parts, red, blockIdx.x == 0 && blockIdx.y == 0,
-                                  scales, status, status_bit, reset).y;
+// One 64 (d) x 64 (n) tile per block, (bx, by) = (n / 64, d / 64).  Each
+// fp32 weight is read once; its code goes straight to w_packed[d][n] and,
+// through an LDS transpose, to w_packed_t[n][d].
+__device__ __forceinline__ void quantize_w_block(
+    const WSrc& w, int bx, int by, const uint32_t* __restrict__ partials, int parts,
+    float* __restrict__ scales, int32_t* __restrict__ status, int status_bit,
+    uint8_t* __restrict__ w_packed, uint8_t* __restrict__ w_packed_t, bool publish, bool reset,
+    uint8_t (*tile_t)[64 + 4], uint32_t* red) {
+  const int D = w.D, N = w.N;
+  const int n0 = bx * 64, d0 = by * 64;
+  const float inv = tensor_scales(partials, parts, red, publish, scales, status, status_bit,
+                                  reset).y;
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     const int idx = threadIdx.x + kThreads * i;
@@ -124,8 +144,8 @@ __global__ __launch_bounds__(kThreads) void quantize_w_kernel(
     const int d = d0 + r, n = n0 + c;
     uint32_t code = 0;
     if (d < D && n < N) {
-      float4 w = load_w4(wq, ldq, wk, ldk, wv, ldv, nq, d, n);
-      code = e4m3x4(w.x * inv, w.y * inv, w.z * inv, w.w * inv);
+      float4 v = load_w4(w.wq, w.ldq, w.wk, w.ldk, w.wv, w.ldv, w.nq, d, n);
+      code = e4m3x4(v.x * inv, v.y * inv, v.z * inv, v.w * inv);
       *reinterpret_cast<uint32_t*>(w_packed + (int64_t)d * N + n) = code;
     }
     tile_t[c + 0][r] = (uint8_t)(code);
@@ -138,15 +158,25 @@ __global__ __launch_bounds__(kThreads) void quantize_w_kernel(
     const int r = threadIdx.x >> 2, c = (threadIdx.x & 3) * 16;  // r: n_local, c: d_local
     const int n = n0 + r, d = d0 + c;
     if (n < N && d < D) {
-      uint32_t w[4];
+      uint32_t q[4];
 #pragma unroll
       for (int j = 0; j < 4; ++j)
-        w[j] = (uint32_t)tile_t[r][c + 4 * j] | ((uint32_t)tile_t[r][c + 4 * j + 1] << 8) |
+        q[j] = (uint32_t)tile_t[r][c + 4 * j] | ((uint32_t)tile_t[r][c + 4 * j + 1] << 8) |
                ((uint32_t)tile_t[r][c + 4 * j + 2] << 16) |
                ((uint32_t)tile_t[r][c + 4 * j + 3] << 24);
-      *reinterpret_cast<uint4*>(w_packed_t + (int64_t)n * D + d) = make_uint4(w[0], w[1], w[2], w[3]);
+      *reinterpret_cast<uint4*>(w_packed_t + (int64_t)n * D + d) = make_uint4(q[0], q[1], q[2], q[3]);
     }
   }
+}
+
+__global__ __launch_bounds__(kThreads) void quantize_w_kernel(
+    WSrc w, const uint32_t* __restrict__ partials, int parts, float* __restrict__ scales,
+    int32_t* __restrict__ status, int status_bit, uint8_t* __restrict__ w_packed,
+    uint8_t* __restrict__ w_packed_t, bool reset) {
+  __shared__ uint8_t tile_t[64][64 + 4];
+  __shared__ uint32_t red[4];
+  quantize_w_block(w, blockIdx.x, blockIdx.y, partials, parts, scales, status, status_bit,
+                   w_packed, w_packed_t, blockIdx.x == 0 && blockIdx.y == 0, reset, tile_t, red);
 }
 
 // ------------------------------ bf16 rows -> e4m3, blocked row layout
@@ -166,14 +196,17 @@ struct ActSrc {
   int vw, vh, vs;
 };
 
+// Block (bx, by) of a (., gy) grid: tokens 128 bx .. and K block by; block
+// (0, gy - 1) publishes the scale (the last K block holds columns it
+// writes, also when src is null).
 template <bool E5>
-__global__ __launch_bounds__(kThreads) void quantize_act_kernel(
-    ActSrc as, int64_t rows, int cols, const uint32_t* __restrict__ partials, int parts,
-    float* __restrict__ scales, int32_t* __restrict__ status, int status_bit,
-    uint8_t* __restrict__ dst, int64_t tokens_padded) {
-  __shared__ uint32_t red[4];
-  const int64_t t0 = (int64_t)blockIdx.x * kKBlock;        // first token
-  const int kb = blockIdx.y, c0 = kb * kKBlock;            // K block of the row layout
+__device__ __forceinline__ void quantize_act_block(
+    const ActSrc& as, int64_t rows, int cols, int bx, int by, int gy,
+    const uint32_t* __restrict__ partials, int parts, float* __restrict__ scales,
+    int32_t* __restrict__ status, int status_bit, uint8_t* __restrict__ dst,
+    int64_t tokens_padded, uint32_t* red) {
+  const int64_t t0 = (int64_t)bx * kKBlock;                // first token
+  const int kb = by, c0 = kb * kKBlock;                    // K block of the row layout
   const int cc = threadIdx.x & 15, rg = threadIdx.x >> 4;
   const int kblocks = (int)ceil_div(cols, kKBlock);
   const int c = c0 + 8 * cc;
@@ -199,8 +232,7 @@ __global__ __launch_bounds__(kThreads) void quantize_act_kernel(
       in[i] = load_stream(p);  // read once: streamed past the caches
     }
   }
-  const float inv = tensor_scales(partials, parts, red,
-                                  blockIdx.x == 0 && blockIdx.y == gridDim.y - 1, scales, status,
+  const float inv = tensor_scales(partials, parts, red, bx == 0 && by == gy - 1, scales, status,
                                   status_bit, false, E5 ? kE5m2Max : kE4m3Max).y;
   // rows rows .. tokens_padded - 1 (zero input) are written as zero codes:
   // the dW GEMM reads them as its K tail
@@ -217,6 +249,60 @@ __global__ __launch_bounds__(kThreads) void quantize_act_kernel(
       *reinterpret_cast<uint2*>(dst + (blk * kActRows + t % kActRows) * kKBlock + 8 * cc) =
           make_uint2(lo, hi);
     }
+  }
+}
+
+template <bool E5>
+__global__ __launch_bounds__(kThreads) void quantize_act_kernel(
+    ActSrc as, int64_t rows, int cols, const uint32_t* __restrict__ partials, int parts,
+    float* __restrict__ scales, int32_t* __restrict__ status, int status_bit,
+    uint8_t* __restrict__ dst, int64_t tokens_padded) {
+  __shared__ uint32_t red[4];
+  quantize_act_block<E5>(as, rows, cols, blockIdx.x, blockIdx.y, gridDim.y, partials, parts,
+                         scales, status, status_bit, dst, tokens_padded, red);
+}
+
+// ------------------------------------- the weight pack and x in one launch
+//
+// For a step that packs fresh weights and then runs the forward: W's amax
+// blocks and x's run in one launch, then W's quantiser blocks and x's, so
+// the small, latency-bound weight work overlaps the activation streams
+// instead of running before them.  Each tensor keeps its own partials,
+// scales and status bit; block 0 of the amax launch clears the status word
+// (the weight pack's reset) before either quantiser can set a bit.
+
+__global__ __launch_bounds__(kThreads) void amax_wx_kernel(WSrc w, int parts_w,
+                                                           uint32_t* __restrict__ pw,
+                                                           const uint16_t* __restrict__ x,
+                                                           int64_t n, int parts_x,
+                                                           uint32_t* __restrict__ px,
+                                                           int32_t* __restrict__ status) {
+  __shared__ uint32_t red[4];
+  if (blockIdx.x == 0 && threadIdx.x == 0) *status = 0;
+  if ((int)blockIdx.x < parts_w)
+    amax_w_block(w, blockIdx.x, parts_w, pw, red);
+  else
+    amax_bf16_block<false>(x, n, blockIdx.x - parts_w, parts_x, px, red);
+}
+
+// Blocks [0, wgx * wgy) quantise W (tile (b % wgx, b / wgx)); the rest x,
+// gy_x consecutive blocks per 128 tokens.
+__global__ __launch_bounds__(kThreads) void quantize_wx_kernel(
+    WSrc w, int wgx, int wgy, const uint32_t* __restrict__ pw, int parts_w,
+    float* __restrict__ w_scales, uint8_t* __restrict__ w_packed,
+    uint8_t* __restrict__ w_packed_t, int w_bit, ActSrc as, int64_t rows, int cols, int gy_x,
+    const uint32_t* __restrict__ px, int parts_x, float* __restrict__ x_scales, int x_bit,
+    uint8_t* __restrict__ x8, int64_t tokens_padded, int32_t* __restrict__ status) {
+  __shared__ uint8_t tile_t[64][64 + 4];
+  __shared__ uint32_t red[4];
+  const int nw = wgx * wgy, b = blockIdx.x;
+  if (b < nw) {
+    quantize_w_block(w, b % wgx, b / wgx, pw, parts_w, w_scales, status, w_bit, w_packed,
+                     w_packed_t, b == 0, false, tile_t, red);
+  } else {
+    const int bb = b - nw;
+    quantize_act_block<false>(as, rows, cols, bb / gy_x, bb % gy_x, gy_x, px, parts_x, x_scales,
+                              status, x_bit, x8, tokens_padded, red);
   }
 }
 
@@ -240,7 +326,7 @@ __global__ __launch_bounds__(kThreads) void encode_kernel(const float* __restric
 void launch_amax_w(const float* wq, int64_t ldq, const float* wk, int64_t ldk, const float* wv,
                    int64_t ldv, int D, int nq, int N, uint32_t* partials, int parts,
                    hipStream_t s) {
-  amax_w_kernel<<<parts, kThreads, 0, s>>>(wq, ldq, wk, ldk, wv, ldv, D, nq, N, partials);
+  amax_w_kernel<<<parts, kThreads, 0, s>>>(WSrc{wq, ldq, wk, ldk, wv, ldv, D, nq, N}, partials);
 }
 
 void launch_amax_bf16(const uint16_t* x, int64_t n, uint32_t* partials, int parts,
@@ -257,9 +343,33 @@ void launch_quantize_w(const float* wq, int64_t ldq, const float* wk, int64_t ld
                        int status_bit, uint8_t* w_packed, uint8_t* w_packed_t, hipStream_t s,
                        bool reset_status) {
   dim3 grid((unsigned)ceil_div(N, 64), (unsigned)ceil_div(D, 64));
-  quantize_w_kernel<<<grid, kThreads, 0, s>>>(wq, ldq, wk, ldk, wv, ldv, D, nq, N, partials,
+  quantize_w_kernel<<<grid, kThreads, 0, s>>>(WSrc{wq, ldq, wk, ldk, wv, ldv, D, nq, N}, partials,
                                               parts, scales, status, status_bit, w_packed,
                                               w_packed_t, reset_status);
+}
+
+void launch_amax_wx(const float* wq, int64_t ldq, const float* wk, int64_t ldk, const float* wv,
+                    int64_t ldv, int D, int nq, int N, uint32_t* pw, int parts_w,
+                    const uint16_t* x, int64_t n, uint32_t* px, int parts_x, int32_t* status,
+                    hipStream_t s) {
+  amax_wx_kernel<<<parts_w + parts_x, kThreads, 0, s>>>(WSrc{wq, ldq, wk, ldk, wv, ldv, D, nq, N},
+                                                        parts_w, pw, x, n, parts_x, px, status);
+}
+
+void launch_quantize_wx(const float* wq, int64_t ldq, const float* wk, int64_t ldk,
+                        const float* wv, int64_t ldv, int D, int nq, int N, const uint32_t* pw,
+                        int parts_w, float* w_scales, uint8_t* w_packed, uint8_t* w_packed_t,
+                        int w_bit, const uint16_t* x, int64_t rows, int cols, const uint32_t* px,
+                        int parts_x, float* x_scales, int x_bit, uint8_t* x8,
+                        int64_t tokens_padded, int32_t* status, hipStream_t s) {
+  const int wgx = (int)ceil_div(N, 64), wgy = (int)ceil_div(D, 64);
+  const int gy_x = (int)ceil_div(cols, kKBlock);
+  const int64_t blocks = (int64_t)wgx * wgy + (tokens_padded / kKBlock) * gy_x;
+  const ActSrc as{x, cols, nullptr, 1, 1, 1};
+  quantize_wx_kernel<<<(unsigned)blocks, kThreads, 0, s>>>(
+      WSrc{wq, ldq, wk, ldk, wv, ldv, D, nq, N}, wgx, wgy, pw, parts_w, w_scales, w_packed,
+      w_packed_t, w_bit, as, rows, cols, gy_x, px, parts_x, x_scales, x_bit, x8, tokens_padded,
+      status);
 }
 
 void launch_quantize_act(const uint16_t* src, int64_t rows, int cols, const uint32_t* partials,

@@ -28,13 +28,18 @@ import statistics
 import sys
 
 # Launch order of one step of each part (a stage may launch more than once).
-# Head widths 64, 96 and 128 run the norm/RoPE inside the forward GEMM
+# The QKV step packs the weights and runs the forward in one qkv_pack_forward
+# call (two shared quantiser launches), or, with bench.py --pack-forward
+# separate, in pack_quantize_weights and qkv_forward (four launches).  Head
+# widths 64, 96 and 128 run the norm/RoPE inside the forward GEMM
 # (gemm_qkv_fwd_kernel); other widths launch norm_rope_fwd after it.
-QKV_ORDER = ["amax_w", "quantize_w", "amax_x", "quantize_x", "gemm_fwd",
-             "amax_dv", "norm_rope_bwd", "quantize_g", "gemm_dx", "gemm_dw", "dw_reduce"]
-QKV_ORDER_UNFUSED = ["amax_w", "quantize_w", "amax_x", "quantize_x", "gemm_fwd", "norm_rope_fwd",
-                     "amax_dv", "norm_rope_bwd", "quantize_g", "gemm_dx", "gemm_dw", "dw_reduce"]
+QKV_PACK_COMBINED = ["amax_wx", "quantize_wx"]
+QKV_PACK_SEPARATE = ["amax_w", "quantize_w", "amax_x", "quantize_x"]
+QKV_BWD = ["amax_dv", "norm_rope_bwd", "quantize_g", "gemm_dx", "gemm_dw", "dw_reduce"]
+QKV_ORDER = QKV_PACK_COMBINED + ["gemm_fwd"] + QKV_BWD
+QKV_ORDER_UNFUSED = QKV_PACK_COMBINED + ["gemm_fwd", "norm_rope_fwd"] + QKV_BWD
 FUSED_WIDTHS = (64, 96, 128)
+SEPARATE_FLAG = "--pack-forward separate"
 MLP_ORDER = ["mlp_amax_w", "mlp_quantize_w", "mlp_amax_w", "mlp_quantize_w", "mlp_amax_x",
              "mlp_quantize_x", "mlp_gemm_up", "mlp_quantize_h", "mlp_gemm_down", "mlp_amax_dy",
              "mlp_quantize_dy", "mlp_gemm_dh", "mlp_quantize_dpre", "mlp_gemm_dx",
@@ -42,6 +47,7 @@ MLP_ORDER = ["mlp_amax_w", "mlp_quantize_w", "mlp_amax_w", "mlp_quantize_w", "ml
 KERNEL_OF_STAGE = {
     "amax_w": "amax_w_kernel", "quantize_w": "quantize_w_kernel",
     "amax_x": "amax_bf16_kernel", "quantize_x": "quantize_act_kernel",
+    "amax_wx": "amax_wx_kernel", "quantize_wx": "quantize_wx_kernel",
     "gemm_fwd": "gemm_", "norm_rope_fwd": "norm_rope_fwd",
     "norm_rope_bwd": "norm_rope_bwd", "amax_dv": "amax_bf16_kernel",
     "quantize_g": "quantize_act_kernel",
@@ -58,7 +64,7 @@ KERNEL_OF_STAGE = {
 }
 
 
-def step_order(workload: str) -> list[str]:
+def step_order(workload: str, separate_pack: bool = False) -> list[str]:
     import bench
     from fp8_packed_reduced_amd import inputs
     qkv, mlp = bench.BENCH_WORKLOADS.get(workload, (workload, None))
@@ -66,6 +72,8 @@ def step_order(workload: str) -> list[str]:
     if qkv:
         fused = inputs.WORKLOADS[qkv]["d_qk"] in FUSED_WIDTHS
         order += QKV_ORDER if fused else QKV_ORDER_UNFUSED
+        if separate_pack:
+            order = QKV_PACK_SEPARATE + order[len(QKV_PACK_COMBINED):]
     return order + (MLP_ORDER if mlp else [])
 CALIB_KERNEL = "encode_kernel"
 
@@ -144,7 +152,7 @@ def traffic(fetch_csv: str, write_csv: str, workload: str, cmd: str) -> str:
     sys.path.insert(0, ".")
     import bench  # the stage -> source mapping and the calibration size
     n = bench.CALIB_FLOATS
-    order = step_order(workload)
+    order = step_order(workload, SEPARATE_FLAG in cmd)
     fetch, ff = _per_stage(fetch_csv, "FETCH_SIZE", 4.0 * n, order)
     write, wf = _per_stage(write_csv, "WRITE_SIZE", 1.0 * n, order)
     out = [f"# HBM traffic per launch, {workload}: stage fetch_bytes write_bytes source_sha12",
@@ -173,12 +181,13 @@ def gemm_flop(workload: str) -> dict:
     return {s: v for s, (kind, v) in work.items() if kind == "mfma"}
 
 
-def mfma_rows(counter_csv: str, xcc: int, simds: int, workload: str) -> tuple[dict, float]:
+def mfma_rows(counter_csv: str, xcc: int, simds: int, workload: str,
+              separate_pack: bool = False) -> tuple[dict, float]:
     """Per GEMM stage: mean MFMA F8 instructions, busy cycles, active cycles
     per XCD and duration of a launch; and the shader clock fitted over every
     step launch (active cycles per XCD against duration, least squares: the
     slope is the clock, the intercept the counter window's fixed overhead)."""
-    order = step_order(workload)
+    order = step_order(workload, separate_pack)
     flop = gemm_flop(workload)
     ns = {int(r["Dispatch_Id"]): int(r["End_Timestamp"]) - int(r["Start_Timestamp"])
           for r in csv.DictReader(open(counter_csv))}
@@ -204,7 +213,7 @@ def mfma_rows(counter_csv: str, xcc: int, simds: int, workload: str) -> tuple[di
 def mfma(counter_csv: str, agent_csv: str, workload: str, cmd: str) -> str:
     gpu = [r for r in csv.DictReader(open(agent_csv)) if r["Agent_Type"] == "GPU"][0]
     xcc, simds = int(gpu["Num_Xcc"]), int(gpu["Simd_Count"])
-    rows, clock = mfma_rows(counter_csv, xcc, simds, workload)
+    rows, clock = mfma_rows(counter_csv, xcc, simds, workload, SEPARATE_FLAG in cmd)
     out = [f"# Matrix-core use of the GEMMs, {workload}\n",
            "Command (run from /tmp with TMPDIR=/tmp, repository at $R):\n",
            "```\n" + cmd + "\n```\n",

@@ -129,10 +129,12 @@ typedef struct fpr_weight_cache {
     int32_t* status;      /* [1] FPR_STATUS_* bits; pack resets it             */
 } fpr_weight_cache;
 
-enum { FPR_CALL_PACK = 0, FPR_CALL_FORWARD = 1, FPR_CALL_BACKWARD = 2 };
+enum { FPR_CALL_PACK = 0, FPR_CALL_FORWARD = 1, FPR_CALL_BACKWARD = 2,
+       FPR_CALL_PACK_FORWARD = 3 };
 
 /* Bytes of workspace each call needs for `tokens` = T tokens (ignored for
- * FPR_CALL_PACK).  0 for invalid dims. */
+ * FPR_CALL_PACK; FPR_CALL_PACK_FORWARD is qkv_pack_forward's).  0 for
+ * invalid dims. */
 FPR_API size_t fpr_workspace_bytes(const fpr_dims* dims, int64_t tokens, int which);
 
 /* Bytes of the buffer qkv_forward fills for qkv_backward: the FP8 x (in the
@@ -178,6 +180,23 @@ FPR_API int qkv_forward(const fpr_dims* dims, int32_t n_seq, int32_t seq_len,
                 void* saved, size_t saved_bytes,
                 void* workspace, size_t workspace_bytes,
                 void* stream);
+
+/* pack_quantize_weights then qkv_forward, for a step that packs fresh
+ * weights before its forward (the weights change every optimizer step,
+ * "Reduced-width QK and packed FP8 attention", Changes): the same results
+ * bit for bit (the cache with its status word, saved, q, k, v), with the
+ * weight's amax and x's in one launch and both quantisers in the next, so
+ * that the small weight work runs beside the activation streams instead of
+ * before them.  Arguments, ownership and errors as in the two calls (every
+ * check of both is made before the first launch); the workspace is
+ * fpr_workspace_bytes(dims, T, FPR_CALL_PACK_FORWARD) bytes. */
+FPR_API int qkv_pack_forward(const fpr_dims* dims,
+                const float* wq, int64_t ldq, const float* wk, int64_t ldk,
+                const float* wv, int64_t ldv, const fpr_weight_cache* cache,
+                int32_t n_seq, int32_t seq_len, const uint16_t* x,
+                uint16_t* q, uint16_t* k, uint16_t* v,
+                void* saved, size_t saved_bytes,
+                void* workspace, size_t workspace_bytes, void* stream);
 
 /* For callers that cannot allocate device memory (code under HIP graph
  * capture, tight serving loops, harnesses that forbid hipMalloc): the same
@@ -279,9 +298,9 @@ FPR_API int fpr_get_layout(const fpr_dims* dims, int64_t tokens, fpr_layout* out
  * hipEventRecord(events[2i+1]) on the call's stream, and its stage name is
  * stored in names[i], for i = count, count+1, ... while count < capacity
  * (and count < FPR_TRACE_MAX).  events are caller-created hipEvent_t handles.
- * Stage names: amax_w, quantize_w, amax_x, quantize_x, gemm_fwd,
- * norm_rope_fwd, amax_dv, norm_rope_bwd, quantize_g, gemm_dx, gemm_dw,
- * dw_reduce;
+ * Stage names: amax_w, quantize_w, amax_x, quantize_x, amax_wx and
+ * quantize_wx (qkv_pack_forward's shared launches), gemm_fwd, norm_rope_fwd,
+ * amax_dv, norm_rope_bwd, quantize_g, gemm_dx, gemm_dw, dw_reduce;
  * for the MLP: mlp_amax_w, mlp_quantize_w, mlp_amax_x, mlp_quantize_x,
  * mlp_gemm_up, mlp_quantize_h, mlp_gemm_down, mlp_amax_dy, mlp_quantize_dy,
  * mlp_gemm_dh, mlp_quantize_dpre, mlp_gemm_dx, mlp_gemm_dw1,

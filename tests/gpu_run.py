@@ -54,7 +54,8 @@ def unblock_rows(buf, off: int, rows: int, cols: int, lay) -> np.ndarray:
 
 
 def run(w: dict, seed: int = 42, x_bits=None, W=None, dy=None, backward: bool = True,
-        qk_stride: int = 0, grad_format: int = 0, bwd_passes: int = 0):
+        qk_stride: int = 0, grad_format: int = 0, bwd_passes: int = 0,
+        pack_forward: bool = False):
     """Pack, forward (and backward) on the GPU; returns a dict of numpy arrays.
 
     With qk_stride > d_qk, q and k come back with their padded rows (the
@@ -62,7 +63,10 @@ def run(w: dict, seed: int = 42, x_bits=None, W=None, dy=None, backward: bool = 
     the kernels wrote) and dq, dk (given or drawn at d_qk) go in padded with
     NaN bits, which the backward must never read.  grad_format 1 quantises the
     packed gradient to e5m2.  bwd_passes 2 runs the two-pass backward, which
-    never writes dQK (then "dqkv" is None)."""
+    never writes dQK (then "dqkv" is None).  pack_forward packs the weights
+    and runs the forward in one qkv_pack_forward call, on a cache whose
+    status word starts with every bit set (the call must clear it); its
+    pre-norm rows are not returned ("qk_pre" is None)."""
     n_seq, S = w["n_seq"], w["seq_len"]
     T = n_seq * S
     D, H, dqk, dv = w["d_model"], w["n_heads"], w["d_qk"], w["d_v"]
@@ -70,7 +74,8 @@ def run(w: dict, seed: int = 42, x_bits=None, W=None, dy=None, backward: bool = 
     dims = dims_for(w, qk_stride, grad_format, bwd_passes)
     qs = qk_stride or dqk
     say(f"[gpu] run n_seq={n_seq} S={S} D={D} H={H} d_qk={dqk} d_v={dv} stride={qs} "
-        f"grad_format={grad_format} bwd_passes={bwd_passes} seed={seed}")
+        f"grad_format={grad_format} bwd_passes={bwd_passes} pack_forward={pack_forward} "
+        f"seed={seed}")
     if x_bits is None:
         x_bits = inputs.make_x(w, seed)
     if W is None:
@@ -79,15 +84,22 @@ def run(w: dict, seed: int = 42, x_bits=None, W=None, dy=None, backward: bool = 
     nq = H * dqk
     wq, wk, wv = Wd[:, :nq], Wd[:, nq:2 * nq], Wd[:, 2 * nq:]
     cache = B.WeightCache(dims)
-    B.pack_quantize_weights(dims, wq, wk, wv, cache)
     x = bits_to_dev(x_bits)
-    ws_f = torch.empty(B.workspace_bytes(dims, T, B.FPR_CALL_FORWARD), dtype=torch.uint8,
-                       device="cuda")
     qo = ko = None
     if qs != dqk:
         qo, ko = (torch.full((n_seq, H, S, qs), -1, dtype=torch.int16, device="cuda")
                   .view(torch.bfloat16) for _ in range(2))
-    q, k, v, saved = B.qkv_forward(dims, n_seq, S, x, cache, q=qo, k=ko, workspace=ws_f)
+    if pack_forward:
+        cache.status.fill_(-1)
+        ws_f = torch.empty(B.workspace_bytes(dims, T, B.FPR_CALL_PACK_FORWARD),
+                           dtype=torch.uint8, device="cuda")
+        q, k, v, saved = B.qkv_pack_forward(dims, wq, wk, wv, cache, n_seq, S, x, q=qo, k=ko,
+                                            workspace=ws_f)
+    else:
+        B.pack_quantize_weights(dims, wq, wk, wv, cache)
+        ws_f = torch.empty(B.workspace_bytes(dims, T, B.FPR_CALL_FORWARD), dtype=torch.uint8,
+                           device="cuda")
+        q, k, v, saved = B.qkv_forward(dims, n_seq, S, x, cache, q=qo, k=ko, workspace=ws_f)
     lay = B.layout(dims, T)
     Tp = lay.tokens_padded
     out = dict(T=T, N=N, Tp=Tp, x_bits=x_bits, W=W)
@@ -104,7 +116,7 @@ def run(w: dict, seed: int = 42, x_bits=None, W=None, dy=None, backward: bool = 
     # the pre-norm Q|K rows exist only where the norm/RoPE is not fused into
     # the forward GEMM (then in the forward workspace)
     out["fused"] = lay.fused_forward
-    out["qk_pre"] = None if lay.fused_forward else dev_to_bits(
+    out["qk_pre"] = None if lay.fused_forward or pack_forward else dev_to_bits(
         B.view_bytes(ws_f, lay.fwd_qk_pre, (T, 2 * nq), torch.bfloat16))
     out["q"], out["k"], out["v"] = dev_to_bits(q), dev_to_bits(k), dev_to_bits(v)
     if backward:

@@ -23,7 +23,8 @@ def test_library_exports_every_declared_call():
                           "fpr_mlp_saved_bytes", "fpr_mlp_get_layout",
                           "mlp_pack_quantize_weights", "mlp_forward", "mlp_backward",
                           "fpr_e5m2_encode", "qkv_forward_noalloc", "fpr_noalloc_scratch_bytes",
-                          "fpr_probe_copy", "fpr_probe_read", "fpr_probe_mfma"}
+                          "fpr_probe_copy", "fpr_probe_read", "fpr_probe_mfma",
+                          "qkv_pack_forward"}
     lib = B.load()
     for n in names:
         assert hasattr(lib, n), n
@@ -58,6 +59,10 @@ def test_sizes_and_layout_at_the_64k_step_shape():
     assert 1 <= lay.dw_splits <= 8
     assert lay.bwd_dw_part >= lay.bwd_g8 + 1920 * T
     assert lay.bwd_dw_part + lay.dw_splits * 768 * 1920 * 4 <= bw
+    # the pack + forward call's workspace: the pack's, aligned, then the forward's
+    pk = B.workspace_bytes(d, 0, B.FPR_CALL_PACK)
+    fw = B.workspace_bytes(d, T, B.FPR_CALL_FORWARD)
+    assert pk + fw <= B.workspace_bytes(d, T, B.FPR_CALL_PACK_FORWARD) < pk + fw + 256
 
 
 def test_blocked_fp8_layouts_cover_their_padding():
@@ -207,6 +212,29 @@ def test_argument_errors_are_reported_before_any_launch():
                           ws, 96, ws, 128, ws, 1 << 30, None) == 3
     assert L.qkv_backward(by(d), 1, 256, ws, ws, ws, ws, ws, ws, 1 << 30, by(cc), ws, ws, 96, ws,
                           96, ws, 128, ws, 100, None) == 4
+    # pack + forward in one call: the pack's and the forward's checks, and
+    # a workspace that must hold both parts
+    pf = B.workspace_bytes(d, 256, B.FPR_CALL_PACK_FORWARD)
+    sv = B.saved_bytes(d, 256)
+    args = [by(d), ws, 96, ws, 96, ws, 128, by(cc), 1, 256, ws, ws, ws, ws, ws, sv, ws, pf, None]
+
+    def pack_fwd(**change):
+        a = list(args)
+        for i, val in change.items():
+            a[int(i[1:])] = val
+        return L.qkv_pack_forward(*a)
+
+    assert pack_fwd(a1=None) == 1
+    assert pack_fwd(a2=95) == 1
+    assert pack_fwd(a8=0) == 1
+    assert pack_fwd(a11=None) == 1
+    assert pack_fwd(a10=ws + 2) == 3
+    assert pack_fwd(a3=ws + 4) == 3
+    assert pack_fwd(a15=sv - 1) == 4
+    assert pack_fwd(a17=pf - 1) == 4
+    assert pack_fwd(a17=B.workspace_bytes(d, 256, B.FPR_CALL_FORWARD)) == 4
+    assert pack_fwd(a7=by(half)) == 1
+    assert L.qkv_pack_forward(by(bad), *args[1:]) == 2
     # measurement hooks
     assert L.fpr_probe_copy(ws, ws + 8, 1024, 4, None) == 3
     assert L.fpr_probe_copy(ws, ws, 1000, 4, None) == 3

@@ -416,6 +416,39 @@ def test_two_pass_backward_matches_one_pass(name, wl, fmt, qs):
     assert one["status"] == two["status"] == 0
 
 
+@pytest.mark.parametrize("name,wl,qs", [
+    ("tiny", inputs.WORKLOADS["tiny"], 0), ("ragged", RAGGED, 0),
+    ("d48", dict(RAGGED, d_qk=48), 0), ("d128", dict(RAGGED, d_qk=128), 0),
+    ("padded", RAGGED, 136), ("step_64k", inputs.WORKLOADS["step_64k"], 0)])
+def test_pack_forward_matches_separate_calls(name, wl, qs):
+    """qkv_pack_forward (the weight pack and the forward with their
+    quantiser launches shared) writes what pack_quantize_weights followed by
+    qkv_forward writes, bit for bit: both weight views and their scales, x8
+    with its zero K and token tails and its scales, 1/rms, q, k, v; the
+    backward from its cache and saved buffer then matches too; and it
+    clears the status word it was handed with every bit set."""
+    sep = run(wl, seed=23, qk_stride=qs)
+    one = run(wl, seed=23, qk_stride=qs, pack_forward=True)
+    for key in ("w_packed", "w_packed_t", "w_scales", "x8", "x8_kpad", "x8_tail", "x_scales",
+                "rho", "q", "k", "v", "g8", "g_scales", "dx"):
+        assert np.array_equal(sep[key], one[key]), key
+    assert np.array_equal(sep["dw"].view(np.uint32), one["dw"].view(np.uint32))
+    assert sep["status"] == one["status"] == 0
+
+
+def test_pack_forward_status_bits():
+    """A NaN in W and one in x set the weight and the activation bits in
+    the combined call as they do in the separate calls."""
+    w = RAGGED
+    x_bits = inputs.make_x(w, 4)
+    x_bits[5, 7] = 0x7FC0
+    W = inputs.make_w(w, 5)
+    W[3, 11] = np.nan
+    sep = run(w, seed=4, x_bits=x_bits, W=W, backward=False)
+    one = run(w, seed=4, x_bits=x_bits, W=W, backward=False, pack_forward=True)
+    assert sep["status"] == one["status"] == 3
+
+
 @pytest.mark.parametrize("wl,fmt", [("step_64k", "e4m3"), ("sweep_64", "e4m3"),
                                     ("sweep_128", "e4m3"), ("step_64k", "e5m2")])
 def test_step_64k_sampled_rows(wl, fmt):

@@ -57,8 +57,12 @@ def test_step_orders_match_the_library_stage_names():
     assert rs.step_order("step_64k") == rs.QKV_ORDER
     assert rs.step_order("mlp_64k") == rs.MLP_ORDER
     assert rs.step_order("block_64k") == rs.QKV_ORDER + rs.MLP_ORDER
+    sep = rs.step_order("step_64k", separate_pack=True)
+    assert sep[:5] == ["amax_w", "quantize_w", "amax_x", "quantize_x", "gemm_fwd"]
+    assert sep[5:] == rs.QKV_ORDER[3:]
+    assert rs.QKV_ORDER_UNFUSED == rs.QKV_ORDER[:3] + ["norm_rope_fwd"] + rs.QKV_ORDER[3:]
     names = open("include/fpr.h").read()
-    for stage in set(rs.QKV_ORDER + rs.MLP_ORDER):
+    for stage in set(rs.QKV_ORDER + sep + rs.MLP_ORDER):
         assert stage in names, stage
         assert stage in bench.STAGE_SOURCES, stage
 
@@ -154,3 +158,12 @@ def test_two_pass_backward_work_accounting():
     assert two["quantize_g"] == ("hbm", rows + 2 * T * H * dv + T * N)
     assert {k: v for k, v in one.items() if k not in ("norm_rope_bwd", "quantize_g")} == \
         {k: v for k, v in two.items() if k not in ("norm_rope_bwd", "quantize_g")}
+
+
+def test_combined_pack_forward_work_accounting():
+    """qkv_pack_forward's two launches carry exactly the work of the four
+    separate quantiser launches: W's and x's amax, then both quantisers."""
+    w = dict(n_seq=1, seq_len=65536, d_model=768, n_heads=6, d_qk=96, d_v=128)
+    work = bench.stage_work(w, 5)
+    assert work["amax_wx"] == ("hbm", work["amax_w"][1] + work["amax_x"][1])
+    assert work["quantize_wx"] == ("hbm", work["quantize_w"][1] + work["quantize_x"][1])
