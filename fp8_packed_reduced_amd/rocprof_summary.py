@@ -1,11 +1,13 @@
 """Turn rocprofv3 output of ``bench.py`` into the short text summaries kept
 under ``profiles/``.
 
-    python -m fp8_packed_reduced_amd.rocprof_summary stats KERNEL_STATS_CSV TITLE CMD [BENCH_OUT]
+    python -m fp8_packed_reduced_amd.rocprof_summary stats KERNEL_STATS_CSV TITLE CMD [BENCH_OUT [WORKLOAD]]
         -> markdown table of per-kernel durations (``--kernel-trace --stats``);
            with BENCH_OUT (what the profiled bench.py printed), also the
            roofline kernel's HIP-event average that bench.py measured live in
-           the same run
+           the same run; with WORKLOAD, also every stage's mean duration from
+           the kernel trace beside the statistics (run_kernel_trace.csv), the
+           launches attributed to stages by launch order
 
     python -m fp8_packed_reduced_amd.rocprof_summary traffic FETCH_CSV WRITE_CSV WORKLOAD CMD...
         -> per-launch HBM bytes of every stage of the step, from two ``--pmc``
@@ -64,7 +66,8 @@ KERNEL_OF_STAGE = {
 }
 
 
-def step_order(workload: str, separate_pack: bool = False) -> list[str]:
+def step_order(workload: str, separate_pack: bool = False,
+               forward_only: bool = False) -> list[str]:
     import bench
     from fp8_packed_reduced_amd import inputs
     qkv, mlp = bench.BENCH_WORKLOADS.get(workload, (workload, None))
@@ -74,6 +77,8 @@ def step_order(workload: str, separate_pack: bool = False) -> list[str]:
         order += QKV_ORDER if fused else QKV_ORDER_UNFUSED
         if separate_pack:
             order = QKV_PACK_SEPARATE + order[len(QKV_PACK_COMBINED):]
+        if forward_only:  # bench.py --forward-only: pack and forward
+            order = order[:order.index("amax_dv")]
     return order + (MLP_ORDER if mlp else [])
 CALIB_KERNEL = "encode_kernel"
 
@@ -91,7 +96,19 @@ def _bench_line(path: str) -> dict:
     return json.loads(lines[-1])
 
 
-def stats(path: str, title: str, cmd: str, bench_out: str | None = None) -> str:
+def stage_times(trace_csv: str, workload: str, separate_pack: bool = False,
+                forward_only: bool = False) -> dict:
+    """Stage -> (launches, mean µs) from a kernel trace of whole steps."""
+    rows = list(csv.DictReader(open(trace_csv)))
+    rows.sort(key=lambda r: int(r["Start_Timestamp"]))
+    ds = [(i, short(r["Kernel_Name"]), (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3)
+          for i, r in enumerate(rows)]
+    per = _by_stage(trace_csv, ds, step_order(workload, separate_pack, forward_only))
+    return {s: (len(v), statistics.mean(us for _, us in v)) for s, v in per.items()}
+
+
+def stats(path: str, title: str, cmd: str, bench_out: str | None = None,
+          workload: str | None = None) -> str:
     rows = list(csv.DictReader(open(path)))
     out = [f"# {title}\n", "Command (run from /tmp with TMPDIR=/tmp, repository at $R):\n",
            "```\n" + cmd + "\n```\n",
@@ -101,6 +118,14 @@ def stats(path: str, title: str, cmd: str, bench_out: str | None = None) -> str:
         out.append(f"| `{short(r['Name'])}` | {r['Calls']} | {float(r['AverageNs']) / 1e3:.2f} | "
                    f"{float(r['MinNs']) / 1e3:.2f} | {float(r['MaxNs']) / 1e3:.2f} | "
                    f"{float(r['Percentage']):.2f} |")
+    if workload:
+        import os
+        trace = os.path.join(os.path.dirname(path), "run_kernel_trace.csv")
+        out += ["\nPer stage, from the kernel trace of the same run (launches attributed by "
+                "launch order):\n", "| stage | launches | avg µs |", "|---|---:|---:|"]
+        for st, (n, us) in stage_times(trace, workload, SEPARATE_FLAG in cmd,
+                                       "--forward-only" in cmd).items():
+            out.append(f"| `{st}` | {n} | {us:.2f} |")
     if bench_out:
         b = _bench_line(bench_out)
         rf = b["roofline"]
@@ -233,7 +258,8 @@ if __name__ == "__main__":
     mode = sys.argv[1]
     if mode == "stats":
         sys.stdout.write(stats(sys.argv[2], sys.argv[3], sys.argv[4],
-                               sys.argv[5] if len(sys.argv) > 5 else None))
+                               sys.argv[5] if len(sys.argv) > 5 else None,
+                               sys.argv[6] if len(sys.argv) > 6 else None))
     elif mode == "traffic":
         sys.stdout.write(traffic(sys.argv[2], sys.argv[3], sys.argv[4], " ".join(sys.argv[5:])))
     elif mode == "mfma":

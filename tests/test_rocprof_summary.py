@@ -167,3 +167,36 @@ def test_combined_pack_forward_work_accounting():
     work = bench.stage_work(w, 5)
     assert work["amax_wx"] == ("hbm", work["amax_w"][1] + work["amax_x"][1])
     assert work["quantize_wx"] == ("hbm", work["quantize_w"][1] + work["quantize_x"][1])
+
+
+def test_stage_times_split_a_trace_by_launch_order(tmp_path):
+    """Per-stage means from a kernel trace: torch's and the probes' launches
+    are skipped, stages that launch twice per step average both, and a
+    forward-only trace follows the forward's order."""
+    def write(order, steps):
+        f = tmp_path / "run_kernel_trace.csv"
+        with open(f, "w", newline="") as fh:
+            w = csv.DictWriter(fh, fieldnames=["Kernel_Name", "Start_Timestamp", "End_Timestamp"])
+            w.writeheader()
+            t = 1000
+            w.writerow({"Kernel_Name": "void fpr::probe_copy_kernel(args)",
+                        "Start_Timestamp": t, "End_Timestamp": t + 5000})
+            for step in range(steps):
+                for k, stage in enumerate(order):
+                    t += 10000
+                    w.writerow({"Kernel_Name": _kernel_name(stage), "Start_Timestamp": t,
+                                "End_Timestamp": t + 1000 * (k + 1) + 100 * step})
+            w.writerow({"Kernel_Name": "at::native::fill(args)", "Start_Timestamp": t + 20000,
+                        "End_Timestamp": t + 90000})
+        return str(f)
+
+    order = rs.step_order("mlp_64k")
+    got = rs.stage_times(write(order, 2), "mlp_64k")
+    assert got["mlp_gemm_up"] == (2, pytest.approx(order.index("mlp_gemm_up") + 1.05))
+    k1, k2 = 1, 3  # mlp_quantize_w launches once per weight
+    assert order[k1] == order[k2] == "mlp_quantize_w"
+    assert got["mlp_quantize_w"] == (4, pytest.approx((k1 + 1 + k2 + 1) / 2 + 0.05))
+    fwd = rs.step_order("fwd_16k", forward_only=True)
+    assert fwd == ["amax_wx", "quantize_wx", "gemm_fwd"]
+    got = rs.stage_times(write(fwd, 3), "fwd_16k", forward_only=True)
+    assert got["gemm_fwd"] == (3, pytest.approx(3.1))
