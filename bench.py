@@ -51,6 +51,7 @@ STAGE_SOURCES = {
     "dw_reduce": "gemm.hip", "norm_rope_fwd": "epilogue.hip", "norm_rope_bwd": "epilogue.hip",
     "mlp_amax_w": "quantize.hip", "mlp_quantize_w": "quantize.hip",
     "mlp_amax_x": "quantize.hip", "mlp_quantize_x": "quantize.hip",
+    "mlp_amax_wx": "quantize.hip", "mlp_quantize_wx": "quantize.hip",
     "mlp_quantize_h": "quantize.hip", "mlp_amax_dy": "quantize.hip",
     "mlp_quantize_dy": "quantize.hip", "mlp_quantize_dpre": "quantize.hip",
     "mlp_gemm_up": "gemm.hip", "mlp_gemm_down": "gemm.hip", "mlp_gemm_dh": "gemm.hip",
@@ -106,6 +107,9 @@ def mlp_stage_work(w: dict, dw_splits: tuple[int, int]) -> dict:
         "mlp_quantize_w": ("hbm", 4 * D * F + 2 * D * F),
         "mlp_amax_x": ("hbm", 2 * T * D),
         "mlp_quantize_x": ("hbm", 3 * T * D),
+        # mlp_pack_forward: both weights' pairs and x's, each kind in one launch
+        "mlp_amax_wx": ("hbm", 2 * 4 * D * F + 2 * T * D),
+        "mlp_quantize_wx": ("hbm", 2 * (4 * D * F + 2 * D * F) + 3 * T * D),
         "mlp_gemm_up": gemm,
         "mlp_quantize_h": ("hbm", 3 * T * F),
         "mlp_gemm_down": gemm,
@@ -342,9 +346,10 @@ def main():
     ap.add_argument("--bwd-passes", type=int, choices=[1, 2], default=1,
                     help="2: the backward in two passes that never write dQK")
     ap.add_argument("--pack-forward", choices=["combined", "separate"], default="combined",
-                    help="combined: the weight pack and the forward in one qkv_pack_forward "
-                         "call, whose quantiser launches serve W and x together; separate: "
-                         "pack_quantize_weights, then qkv_forward")
+                    help="combined: the weight pack and the forward in one call "
+                         "(qkv_pack_forward, mlp_pack_forward), whose quantiser launches serve "
+                         "the weights and x together; separate: the pack call, then the "
+                         "forward call")
     ap.add_argument("--grad-format", choices=["e4m3", "e5m2"], default="e4m3",
                     help="FP8 format of the backward's gradient codes (QKV and MLP)")
     args = ap.parse_args()
@@ -433,7 +438,9 @@ def main():
         mcache = B.MlpCache(mdims, dev)
         mws_p = torch.empty(B.mlp_workspace_bytes(mdims, 0, B.FPR_CALL_PACK), dtype=torch.uint8,
                             device=dev)
-        mws_f = torch.empty(B.mlp_workspace_bytes(mdims, T, B.FPR_CALL_FORWARD),
+        mcombined = args.pack_forward == "combined"
+        mws_f = torch.empty(B.mlp_workspace_bytes(mdims, T, B.FPR_CALL_PACK_FORWARD if mcombined
+                                                  else B.FPR_CALL_FORWARD),
                             dtype=torch.uint8, device=dev)
         mws_b = torch.empty(B.mlp_workspace_bytes(mdims, T, B.FPR_CALL_BACKWARD),
                             dtype=torch.uint8, device=dev)
@@ -444,8 +451,11 @@ def main():
         dw2 = torch.empty((F, Dm), dtype=torch.float32, device=dev)
 
         def mlp_step():
-            B.mlp_pack_quantize_weights(mdims, w1, w2, mcache, workspace=mws_p)
-            B.mlp_forward(mdims, mx, mcache, my, msaved, mws_f)
+            if mcombined:
+                B.mlp_pack_forward(mdims, w1, w2, mcache, mx, my, msaved, mws_f)
+            else:
+                B.mlp_pack_quantize_weights(mdims, w1, w2, mcache, workspace=mws_p)
+                B.mlp_forward(mdims, mx, mcache, my, msaved, mws_f)
             B.mlp_backward(mdims, mdy, msaved, mcache, mdx, dw1, dw2, mws_b)
 
         steps.append(mlp_step)
@@ -457,13 +467,17 @@ def main():
             config["grad_format"] = args.grad_format
         if args.bwd_passes == 2:
             config["bwd_passes"] = 2
+        if not mcombined:
+            config["pack_forward"] = "separate"
         oracle_steps.append(lambda seed, tokens: _oracle_mlp_step(wm, seed, tokens))
     qkv_calls = ("qkv_pack_forward" if args.pack_forward == "combined" else
                  "pack_quantize_weights + qkv_forward")
     config["step"] = " + ".join(
         ([qkv_calls + ("" if args.forward_only else " + qkv_backward")]
          if w is not None else []) +
-        (["mlp_pack_quantize_weights + mlp_forward + mlp_backward"] if wm is not None else []))
+        ([("mlp_pack_forward" if args.pack_forward == "combined" else
+           "mlp_pack_quantize_weights + mlp_forward") + " + mlp_backward"]
+         if wm is not None else []))
     config["seed"] = args.seed
     metric = METRIC if wm is None else METRIC_MLP if w is None else METRIC_BLOCK
     if w is not None and (D, H, T, dqk) != (768, 6, 65536, 96):  # another QKV shape

@@ -162,6 +162,9 @@ def load():
                                             _SZ, _V]
     L.mlp_forward.restype = ctypes.c_int
     L.mlp_forward.argtypes = [P(MlpDims), _I64, _V, P(_MlpCacheC), _V, _V, _SZ, _V, _SZ, _V]
+    L.mlp_pack_forward.restype = ctypes.c_int
+    L.mlp_pack_forward.argtypes = [P(MlpDims), _V, _I64, _V, _I64, P(_MlpCacheC), _I64, _V, _V,
+                                   _V, _SZ, _V, _SZ, _V]
     L.mlp_backward.restype = ctypes.c_int
     L.mlp_backward.argtypes = [P(MlpDims), _I64, _V, _V, _SZ, P(_MlpCacheC), _V, _V, _I64, _V,
                                _I64, _V, _SZ, _V]
@@ -538,6 +541,33 @@ def mlp_forward(dims: MlpDims, x, cache: MlpCache, y=None, saved=None, workspace
                             workspace.numel(), _stream(dev))
     if rc:
         raise FprError(rc, "mlp_forward")
+    return y, saved
+
+
+def mlp_pack_forward(dims: MlpDims, w1, w2, cache: MlpCache, x, y=None, saved=None,
+                     workspace=None):
+    """mlp_pack_quantize_weights then mlp_forward in one call (shared
+    launches).  Returns (y, saved)."""
+    T, D, F = x.shape[0], dims.d_model, dims.d_ff
+    ld1 = _need_rows(w1, D, F, "w1")
+    ld2 = _need_rows(w2, F, D, "w2")
+    dev = x.device
+    _need(x, torch.bfloat16, (T, D), "x")
+    if y is None:
+        y = torch.empty((T, D), dtype=torch.bfloat16, device=dev)
+    _need(y, torch.bfloat16, (T, D), "y")
+    if saved is None:
+        saved = torch.empty(mlp_saved_bytes(dims, T), dtype=torch.uint8, device=dev)
+    if workspace is None:
+        workspace = torch.empty(mlp_workspace_bytes(dims, T, FPR_CALL_PACK_FORWARD),
+                                dtype=torch.uint8, device=dev)
+    cc = cache.c()
+    rc = load().mlp_pack_forward(ctypes.byref(dims), w1.data_ptr(), ld1, w2.data_ptr(), ld2,
+                                 ctypes.byref(cc), T, x.data_ptr(), y.data_ptr(),
+                                 saved.data_ptr(), saved.numel(), workspace.data_ptr(),
+                                 workspace.numel(), _stream(dev))
+    if rc:
+        raise FprError(rc, "mlp_pack_forward")
     return y, saved
 
 

@@ -173,6 +173,11 @@ MlpPlan make_mlp_plan(const fpr_mlp_dims* d, int64_t T) {
   return p;
 }
 
+// mlp_pack_forward's workspace: W1's and W2's amax partials, then the
+// forward's.
+size_t mlp_pack_forward_off() { return (size_t)round_up(2 * (int64_t)kPartsW * 4, kAlign); }
+size_t mlp_pack_forward_bytes(const MlpPlan& p) { return mlp_pack_forward_off() + p.fwd_total; }
+
 int mlp_cache_check(const fpr_mlp_cache* c) {
   if (!c || !c->w1 || !c->w1_t || !c->w2 || !c->w2_t || !c->scales || !c->status)
     return FPR_ERR_ARG;
@@ -304,6 +309,31 @@ void forward_gemm(const fpr_dims* dims, const Plan& p, int32_t n_seq, int32_t se
   }
 }
 
+// The MLP forward after x8 and its scales exist: the up-projection with
+// relu^2 and the amax of h in its epilogue, h's quantiser, the down-projection.
+void mlp_forward_gemms(const MlpPlan& p, const fpr_mlp_cache* cache, uint16_t* y, void* saved,
+                       void* workspace, hipStream_t s) {
+  const int64_t T = p.T;
+  uint32_t* hparts = at<uint32_t>(workspace, p.f_hpart);
+  uint16_t* h = at<uint16_t>(workspace, p.f_h);
+  uint8_t* x8 = at<uint8_t>(saved, p.s_x8);
+  uint8_t* h8 = at<uint8_t>(saved, p.s_h8);
+  float* xsc = at<float>(saved, p.s_xsc);
+  float* hsc = at<float>(saved, p.s_hsc);
+  int nh = 0;
+  stage("mlp_gemm_up", s, [&] {
+    nh = fpr::launch_gemm_relu2(x8, cache->w1_t, (int)T, p.F, p.D, xsc, cache->scales, h,
+                                hparts, s);
+  });
+  stage("mlp_quantize_h", s, [&] {
+    fpr::launch_quantize_act(h, T, p.F, hparts, nh, hsc, cache->status, FPR_STATUS_H_NONFINITE,
+                             h8, p.Tp, s);
+  });
+  stage("mlp_gemm_down", s, [&] {
+    fpr::launch_gemm_dx(h8, cache->w2_t, (int)T, p.D, p.F, hsc, cache->scales + 2, y, s);
+  });
+}
+
 }  // namespace
 
 extern "C" {
@@ -424,20 +454,19 @@ int qkv_pack_forward(const fpr_dims* dims, const float* wq, int64_t ldq, const f
     return FPR_ERR_WORKSPACE;
   hipStream_t s = static_cast<hipStream_t>(stream);
   (void)hipGetLastError();
-  uint32_t* pw = at<uint32_t>(workspace, p.p_part);
   void* fws = static_cast<uint8_t*>(workspace) + pack_forward_off(p);
   uint32_t* px = at<uint32_t>(fws, p.f_part);
   float* xsc = at<float>(saved, p.s_xsc);
   uint8_t* x8 = at<uint8_t>(saved, p.s_x8);
+  const fpr::WeightJob job{wq, ldq, wk, ldk, wv, ldv, p.D, p.nq, p.N,
+                           at<uint32_t>(workspace, p.p_part), cache->scales, cache->w_packed,
+                           cache->w_packed_t};
   stage("amax_wx", s, [&] {
-    fpr::launch_amax_wx(wq, ldq, wk, ldk, wv, ldv, p.D, p.nq, p.N, pw, kPartsW, x, T * p.D, px,
-                        p.f_parts, cache->status, s);
+    fpr::launch_amax_wx(&job, 1, kPartsW, x, T * p.D, px, p.f_parts, cache->status, s);
   });
   stage("quantize_wx", s, [&] {
-    fpr::launch_quantize_wx(wq, ldq, wk, ldk, wv, ldv, p.D, p.nq, p.N, pw, kPartsW,
-                            cache->scales, cache->w_packed, cache->w_packed_t,
-                            FPR_STATUS_W_NONFINITE, x, T, p.D, px, p.f_parts, xsc,
-                            FPR_STATUS_X_NONFINITE, x8, p.Tp, cache->status, s);
+    fpr::launch_quantize_wx(&job, 1, kPartsW, FPR_STATUS_W_NONFINITE, x, T, p.D, px, p.f_parts,
+                            xsc, FPR_STATUS_X_NONFINITE, x8, p.Tp, cache->status, s);
   });
   forward_gemm(dims, p, n_seq, seq_len, cache, q, k, v, saved, fws, s);
   return finish();
@@ -553,6 +582,7 @@ size_t fpr_mlp_workspace_bytes(const fpr_mlp_dims* dims, int64_t tokens, int whi
   const MlpPlan p = make_mlp_plan(dims, tokens);
   if (which == FPR_CALL_FORWARD) return p.fwd_total;
   if (which == FPR_CALL_BACKWARD) return p.bwd_total;
+  if (which == FPR_CALL_PACK_FORWARD) return mlp_pack_forward_bytes(p);
   return 0;
 }
 
@@ -632,29 +662,50 @@ int mlp_forward(const fpr_mlp_dims* dims, int64_t tokens, const uint16_t* x,
   (void)hipGetLastError();
   const int64_t T = p.T;
   uint32_t* xparts = at<uint32_t>(workspace, p.f_xpart);
-  uint32_t* hparts = at<uint32_t>(workspace, p.f_hpart);
-  uint16_t* h = at<uint16_t>(workspace, p.f_h);
   uint8_t* x8 = at<uint8_t>(saved, p.s_x8);
-  uint8_t* h8 = at<uint8_t>(saved, p.s_h8);
   float* xsc = at<float>(saved, p.s_xsc);
-  float* hsc = at<float>(saved, p.s_hsc);
-  int nh = 0;
   stage("mlp_amax_x", s, [&] { fpr::launch_amax_bf16(x, T * p.D, xparts, p.x_parts, s); });
   stage("mlp_quantize_x", s, [&] {
     fpr::launch_quantize_act(x, T, p.D, xparts, p.x_parts, xsc, cache->status,
                              FPR_STATUS_X_NONFINITE, x8, p.Tp, s);
   });
-  stage("mlp_gemm_up", s, [&] {
-    nh = fpr::launch_gemm_relu2(x8, cache->w1_t, (int)T, p.F, p.D, xsc, cache->scales, h,
-                                hparts, s);
+  mlp_forward_gemms(p, cache, y, saved, workspace, s);
+  return finish();
+}
+
+int mlp_pack_forward(const fpr_mlp_dims* dims, const float* w1, int64_t ld1, const float* w2,
+                     int64_t ld2, const fpr_mlp_cache* cache, int64_t tokens, const uint16_t* x,
+                     uint16_t* y, void* saved, size_t saved_bytes, void* workspace,
+                     size_t workspace_bytes, void* stream) {
+  int rc = mlp_shape_check(dims);
+  if (rc || (rc = mlp_tokens_check(tokens)) || (rc = mlp_cache_check(cache))) return rc;
+  const MlpPlan p = make_mlp_plan(dims, tokens);
+  if ((rc = ld_check(ld1, p.F, w1)) || (rc = ld_check(ld2, p.D, w2))) return rc;
+  if (!x || !y || !saved || !workspace) return FPR_ERR_ARG;
+  if (!al16(x) || !al16(y) || !al16(saved) || !al16(workspace)) return FPR_ERR_ALIGN;
+  if (saved_bytes < p.saved_total || workspace_bytes < mlp_pack_forward_bytes(p))
+    return FPR_ERR_WORKSPACE;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  (void)hipGetLastError();
+  const int64_t T = p.T;
+  void* fws = static_cast<uint8_t*>(workspace) + mlp_pack_forward_off();
+  uint32_t* xparts = at<uint32_t>(fws, p.f_xpart);
+  uint8_t* x8 = at<uint8_t>(saved, p.s_x8);
+  float* xsc = at<float>(saved, p.s_xsc);
+  uint32_t* wparts = at<uint32_t>(workspace, 0);
+  // each matrix is the packed-weight case with all columns in one piece
+  const fpr::WeightJob jobs[2] = {
+      {w1, ld1, w1, ld1, w1, ld1, p.D, p.F, p.F, wparts, cache->scales, cache->w1, cache->w1_t},
+      {w2, ld2, w2, ld2, w2, ld2, p.F, p.D, p.D, wparts + kPartsW, cache->scales + 2, cache->w2,
+       cache->w2_t}};
+  stage("mlp_amax_wx", s, [&] {
+    fpr::launch_amax_wx(jobs, 2, kPartsW, x, T * p.D, xparts, p.x_parts, cache->status, s);
   });
-  stage("mlp_quantize_h", s, [&] {
-    fpr::launch_quantize_act(h, T, p.F, hparts, nh, hsc, cache->status, FPR_STATUS_H_NONFINITE,
-                             h8, p.Tp, s);
+  stage("mlp_quantize_wx", s, [&] {
+    fpr::launch_quantize_wx(jobs, 2, kPartsW, FPR_STATUS_W_NONFINITE, x, T, p.D, xparts,
+                            p.x_parts, xsc, FPR_STATUS_X_NONFINITE, x8, p.Tp, cache->status, s);
   });
-  stage("mlp_gemm_down", s, [&] {
-    fpr::launch_gemm_dx(h8, cache->w2_t, (int)T, p.D, p.F, hsc, cache->scales + 2, y, s);
-  });
+  mlp_forward_gemms(p, cache, y, saved, fws, s);
   return finish();
 }
 

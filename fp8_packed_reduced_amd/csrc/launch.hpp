@@ -47,14 +47,27 @@ void launch_quantize_w(const float* wq, int64_t ldq, const float* wk, int64_t ld
 // amaxes (parts_w W blocks, then parts_x x blocks; block 0 clears *status),
 // the next writes both codes (W's both layouts and scales with bit w_bit,
 // x8 and its scales with x_bit, as the separate launchers do).
-void launch_amax_wx(const float* wq, int64_t ldq, const float* wk, int64_t ldk, const float* wv,
-                    int64_t ldv, int D, int nq, int N, uint32_t* pw, int parts_w,
-                    const uint16_t* x, int64_t n, uint32_t* px, int parts_x, int32_t* status,
-                    hipStream_t s);
-void launch_quantize_wx(const float* wq, int64_t ldq, const float* wk, int64_t ldk,
-                        const float* wv, int64_t ldv, int D, int nq, int N, const uint32_t* pw,
-                        int parts_w, float* w_scales, uint8_t* w_packed, uint8_t* w_packed_t,
-                        int w_bit, const uint16_t* x, int64_t rows, int cols, const uint32_t* px,
+// The weight pack and x's quantiser in two shared launches, for one weight
+// (the packed QKV weight) or two (the MLP's W1 and W2; njobs <= 2).  A job
+// names a weight as launch_amax_w does, its parts_w amax partials, its
+// scales and both code layouts.  The amax launch clears *status first.
+struct WeightJob {
+  const float* wq;
+  int64_t ldq;
+  const float* wk;
+  int64_t ldk;
+  const float* wv;
+  int64_t ldv;
+  int D, nq, N;
+  uint32_t* partials;
+  float* scales;
+  uint8_t* packed;
+  uint8_t* packed_t;
+};
+void launch_amax_wx(const WeightJob* jobs, int njobs, int parts_w, const uint16_t* x, int64_t n,
+                    uint32_t* px, int parts_x, int32_t* status, hipStream_t s);
+void launch_quantize_wx(const WeightJob* jobs, int njobs, int parts_w, int w_bit,
+                        const uint16_t* x, int64_t rows, int cols, const uint32_t* px,
                         int parts_x, float* x_scales, int x_bit, uint8_t* x8,
                         int64_t tokens_padded, int32_t* status, hipStream_t s);
 

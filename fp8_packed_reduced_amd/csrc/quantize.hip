@@ -262,45 +262,67 @@ __global__ __launch_bounds__(kThreads) void quantize_act_kernel(
                          scales, status, status_bit, dst, tokens_padded, red);
 }
 
-// ------------------------------------- the weight pack and x in one launch
+// ------------------------------- the weight pack and x in shared launches
 //
-// For a step that packs fresh weights and then runs the forward: W's amax
-// blocks and x's run in one launch, then W's quantiser blocks and x's, so
-// the small, latency-bound weight work overlaps the activation streams
-// instead of running before them.  Each tensor keeps its own partials,
-// scales and status bit; block 0 of the amax launch clears the status word
-// (the weight pack's reset) before either quantiser can set a bit.
+// For a step that packs fresh weights and then runs the forward: the amax
+// blocks of one or two weights and of x run in one launch, then the
+// weights' quantiser tiles and x's quantiser blocks in the next, so the
+// small, latency-bound weight work overlaps the activation streams instead
+// of running before them.  Each tensor keeps its own partials, scales and
+// status bit; block 0 of the amax launch clears the status word (the
+// weight pack's reset) before either quantiser can set a bit.
 
-__global__ __launch_bounds__(kThreads) void amax_wx_kernel(WSrc w, int parts_w,
-                                                           uint32_t* __restrict__ pw,
+// One weight: its pieces, parts_w amax partials, scales and both layouts.
+struct WJob {
+  WSrc w;
+  uint32_t* partials;
+  float* scales;
+  uint8_t* packed;
+  uint8_t* packed_t;
+};
+
+__device__ __forceinline__ int w_tiles_x(const WSrc& w) { return (int)ceil_div(w.N, 64); }
+__device__ __forceinline__ int w_tiles(const WSrc& w) {
+  return w_tiles_x(w) * (int)ceil_div(w.D, 64);
+}
+
+// Blocks [0, nw parts_w): weight b / parts_w, its block b % parts_w; the
+// rest x, parts_x blocks.
+__global__ __launch_bounds__(kThreads) void amax_wx_kernel(WJob a, WJob b, int nw, int parts_w,
                                                            const uint16_t* __restrict__ x,
                                                            int64_t n, int parts_x,
                                                            uint32_t* __restrict__ px,
                                                            int32_t* __restrict__ status) {
   __shared__ uint32_t red[4];
-  if (blockIdx.x == 0 && threadIdx.x == 0) *status = 0;
-  if ((int)blockIdx.x < parts_w)
-    amax_w_block(w, blockIdx.x, parts_w, pw, red);
-  else
-    amax_bf16_block<false>(x, n, blockIdx.x - parts_w, parts_x, px, red);
+  const int blk = blockIdx.x;
+  if (blk == 0 && threadIdx.x == 0) *status = 0;
+  if (blk < nw * parts_w) {
+    const WJob& j = blk < parts_w ? a : b;
+    amax_w_block(j.w, blk % parts_w, parts_w, j.partials, red);
+  } else {
+    amax_bf16_block<false>(x, n, blk - nw * parts_w, parts_x, px, red);
+  }
 }
 
-// Blocks [0, wgx * wgy) quantise W (tile (b % wgx, b / wgx)); the rest x,
-// gy_x consecutive blocks per 128 tokens.
+// Blocks [0, tiles of a): a's 64 x 64 tiles in row order, then b's (nw =
+// 2), then x's, gy_x consecutive blocks per 128 tokens.  Each weight's
+// first tile publishes its scale.
 __global__ __launch_bounds__(kThreads) void quantize_wx_kernel(
-    WSrc w, int wgx, int wgy, const uint32_t* __restrict__ pw, int parts_w,
-    float* __restrict__ w_scales, uint8_t* __restrict__ w_packed,
-    uint8_t* __restrict__ w_packed_t, int w_bit, ActSrc as, int64_t rows, int cols, int gy_x,
+    WJob a, WJob b, int nw, int parts_w, int w_bit, ActSrc as, int64_t rows, int cols, int gy_x,
     const uint32_t* __restrict__ px, int parts_x, float* __restrict__ x_scales, int x_bit,
     uint8_t* __restrict__ x8, int64_t tokens_padded, int32_t* __restrict__ status) {
   __shared__ uint8_t tile_t[64][64 + 4];
   __shared__ uint32_t red[4];
-  const int nw = wgx * wgy, b = blockIdx.x;
-  if (b < nw) {
-    quantize_w_block(w, b % wgx, b / wgx, pw, parts_w, w_scales, status, w_bit, w_packed,
-                     w_packed_t, b == 0, false, tile_t, red);
+  const int na = w_tiles(a.w), nb = nw > 1 ? w_tiles(b.w) : 0;
+  const int blk = blockIdx.x;
+  if (blk < na + nb) {
+    const bool first = blk < na;
+    const WJob& j = first ? a : b;
+    const int t = first ? blk : blk - na, gx = w_tiles_x(j.w);
+    quantize_w_block(j.w, t % gx, t / gx, j.partials, parts_w, j.scales, status, w_bit, j.packed,
+                     j.packed_t, t == 0, false, tile_t, red);
   } else {
-    const int bb = b - nw;
+    const int bb = blk - na - nb;
     quantize_act_block<false>(as, rows, cols, bb / gy_x, bb % gy_x, gy_x, px, parts_x, x_scales,
                               status, x_bit, x8, tokens_padded, red);
   }
@@ -348,28 +370,34 @@ void launch_quantize_w(const float* wq, int64_t ldq, const float* wk, int64_t ld
                                               w_packed_t, reset_status);
 }
 
-void launch_amax_wx(const float* wq, int64_t ldq, const float* wk, int64_t ldk, const float* wv,
-                    int64_t ldv, int D, int nq, int N, uint32_t* pw, int parts_w,
-                    const uint16_t* x, int64_t n, uint32_t* px, int parts_x, int32_t* status,
-                    hipStream_t s) {
-  amax_wx_kernel<<<parts_w + parts_x, kThreads, 0, s>>>(WSrc{wq, ldq, wk, ldk, wv, ldv, D, nq, N},
-                                                        parts_w, pw, x, n, parts_x, px, status);
+namespace {
+WJob to_job(const WeightJob& j) {
+  return WJob{WSrc{j.wq, j.ldq, j.wk, j.ldk, j.wv, j.ldv, j.D, j.nq, j.N}, j.partials, j.scales,
+              j.packed, j.packed_t};
+}
+}  // namespace
+
+void launch_amax_wx(const WeightJob* jobs, int njobs, int parts_w, const uint16_t* x, int64_t n,
+                    uint32_t* px, int parts_x, int32_t* status, hipStream_t s) {
+  const WJob a = to_job(jobs[0]), b = to_job(jobs[njobs > 1 ? 1 : 0]);
+  amax_wx_kernel<<<njobs * parts_w + parts_x, kThreads, 0, s>>>(a, b, njobs, parts_w, x, n,
+                                                                parts_x, px, status);
 }
 
-void launch_quantize_wx(const float* wq, int64_t ldq, const float* wk, int64_t ldk,
-                        const float* wv, int64_t ldv, int D, int nq, int N, const uint32_t* pw,
-                        int parts_w, float* w_scales, uint8_t* w_packed, uint8_t* w_packed_t,
-                        int w_bit, const uint16_t* x, int64_t rows, int cols, const uint32_t* px,
+void launch_quantize_wx(const WeightJob* jobs, int njobs, int parts_w, int w_bit,
+                        const uint16_t* x, int64_t rows, int cols, const uint32_t* px,
                         int parts_x, float* x_scales, int x_bit, uint8_t* x8,
                         int64_t tokens_padded, int32_t* status, hipStream_t s) {
-  const int wgx = (int)ceil_div(N, 64), wgy = (int)ceil_div(D, 64);
+  const WJob a = to_job(jobs[0]), b = to_job(jobs[njobs > 1 ? 1 : 0]);
+  int64_t blocks = 0;
+  for (int i = 0; i < njobs; ++i)
+    blocks += ceil_div(jobs[i].N, 64) * ceil_div(jobs[i].D, 64);
   const int gy_x = (int)ceil_div(cols, kKBlock);
-  const int64_t blocks = (int64_t)wgx * wgy + (tokens_padded / kKBlock) * gy_x;
+  blocks += (tokens_padded / kKBlock) * gy_x;
   const ActSrc as{x, cols, nullptr, 1, 1, 1};
-  quantize_wx_kernel<<<(unsigned)blocks, kThreads, 0, s>>>(
-      WSrc{wq, ldq, wk, ldk, wv, ldv, D, nq, N}, wgx, wgy, pw, parts_w, w_scales, w_packed,
-      w_packed_t, w_bit, as, rows, cols, gy_x, px, parts_x, x_scales, x_bit, x8, tokens_padded,
-      status);
+  quantize_wx_kernel<<<(unsigned)blocks, kThreads, 0, s>>>(a, b, njobs, parts_w, w_bit, as, rows,
+                                                           cols, gy_x, px, parts_x, x_scales,
+                                                           x_bit, x8, tokens_padded, status);
 }
 
 void launch_quantize_act(const uint16_t* src, int64_t rows, int cols, const uint32_t* partials,

@@ -32,7 +32,8 @@ import sys
 # Launch order of one step of each part (a stage may launch more than once).
 # The QKV step packs the weights and runs the forward in one qkv_pack_forward
 # call (two shared quantiser launches), or, with bench.py --pack-forward
-# separate, in pack_quantize_weights and qkv_forward (four launches).  Head
+# separate, in pack_quantize_weights and qkv_forward (four launches); the
+# MLP step likewise in mlp_pack_forward (two) or in its two calls (six).  Head
 # widths 64, 96 and 128 run the norm/RoPE inside the forward GEMM
 # (gemm_qkv_fwd_kernel); other widths launch norm_rope_fwd after it.
 QKV_PACK_COMBINED = ["amax_wx", "quantize_wx"]
@@ -42,10 +43,13 @@ QKV_ORDER = QKV_PACK_COMBINED + ["gemm_fwd"] + QKV_BWD
 QKV_ORDER_UNFUSED = QKV_PACK_COMBINED + ["gemm_fwd", "norm_rope_fwd"] + QKV_BWD
 FUSED_WIDTHS = (64, 96, 128)
 SEPARATE_FLAG = "--pack-forward separate"
-MLP_ORDER = ["mlp_amax_w", "mlp_quantize_w", "mlp_amax_w", "mlp_quantize_w", "mlp_amax_x",
-             "mlp_quantize_x", "mlp_gemm_up", "mlp_quantize_h", "mlp_gemm_down", "mlp_amax_dy",
-             "mlp_quantize_dy", "mlp_gemm_dh", "mlp_quantize_dpre", "mlp_gemm_dx",
-             "mlp_gemm_dw1", "mlp_dw1_reduce", "mlp_gemm_dw2", "mlp_dw2_reduce"]
+MLP_PACK_COMBINED = ["mlp_amax_wx", "mlp_quantize_wx"]
+MLP_PACK_SEPARATE = ["mlp_amax_w", "mlp_quantize_w", "mlp_amax_w", "mlp_quantize_w",
+                     "mlp_amax_x", "mlp_quantize_x"]
+MLP_REST = ["mlp_gemm_up", "mlp_quantize_h", "mlp_gemm_down", "mlp_amax_dy",
+            "mlp_quantize_dy", "mlp_gemm_dh", "mlp_quantize_dpre", "mlp_gemm_dx",
+            "mlp_gemm_dw1", "mlp_dw1_reduce", "mlp_gemm_dw2", "mlp_dw2_reduce"]
+MLP_ORDER = MLP_PACK_COMBINED + MLP_REST
 KERNEL_OF_STAGE = {
     "amax_w": "amax_w_kernel", "quantize_w": "quantize_w_kernel",
     "amax_x": "amax_bf16_kernel", "quantize_x": "quantize_act_kernel",
@@ -57,6 +61,7 @@ KERNEL_OF_STAGE = {
     "dw_reduce": "dw_reduce_kernel",
     "mlp_amax_w": "amax_w_kernel", "mlp_quantize_w": "quantize_w_kernel",
     "mlp_amax_x": "amax_bf16_kernel", "mlp_quantize_x": "quantize_act_kernel",
+    "mlp_amax_wx": "amax_wx_kernel", "mlp_quantize_wx": "quantize_wx_kernel",
     "mlp_gemm_up": "EpiRelu2", "mlp_quantize_h": "quantize_act_kernel",
     "mlp_gemm_down": "EpiDx", "mlp_amax_dy": "amax_bf16_kernel",
     "mlp_quantize_dy": "quantize_act_kernel", "mlp_gemm_dh": "EpiDpre",
@@ -79,7 +84,9 @@ def step_order(workload: str, separate_pack: bool = False,
             order = QKV_PACK_SEPARATE + order[len(QKV_PACK_COMBINED):]
         if forward_only:  # bench.py --forward-only: pack and forward
             order = order[:order.index("amax_dv")]
-    return order + (MLP_ORDER if mlp else [])
+    if mlp:
+        order += (MLP_PACK_SEPARATE if separate_pack else MLP_PACK_COMBINED) + MLP_REST
+    return order
 CALIB_KERNEL = "encode_kernel"
 
 

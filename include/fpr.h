@@ -302,6 +302,7 @@ FPR_API int fpr_get_layout(const fpr_dims* dims, int64_t tokens, fpr_layout* out
  * quantize_wx (qkv_pack_forward's shared launches), gemm_fwd, norm_rope_fwd,
  * amax_dv, norm_rope_bwd, quantize_g, gemm_dx, gemm_dw, dw_reduce;
  * for the MLP: mlp_amax_w, mlp_quantize_w, mlp_amax_x, mlp_quantize_x,
+ * mlp_amax_wx and mlp_quantize_wx (mlp_pack_forward's shared launches),
  * mlp_gemm_up, mlp_quantize_h, mlp_gemm_down, mlp_amax_dy, mlp_quantize_dy,
  * mlp_gemm_dh, mlp_quantize_dpre, mlp_gemm_dx, mlp_gemm_dw1,
  * mlp_dw1_reduce, mlp_gemm_dw2, mlp_dw2_reduce.  fpr_trace_set(NULL) stops
@@ -358,7 +359,8 @@ typedef struct fpr_mlp_cache {
     int32_t* status;   /* [1] FPR_STATUS_* bits; pack resets it           */
 } fpr_mlp_cache;
 
-/* Bytes of workspace (FPR_CALL_PACK / _FORWARD / _BACKWARD) and of the
+/* Bytes of workspace (FPR_CALL_PACK / _FORWARD / _BACKWARD, and
+ * FPR_CALL_PACK_FORWARD for mlp_pack_forward) and of the
  * saved buffer (x8, h8 and their scales, which must stay alive and
  * unmodified from mlp_forward to mlp_backward) for T = tokens; 0 for
  * invalid dims or token counts. */
@@ -383,6 +385,22 @@ FPR_API int mlp_forward(const fpr_mlp_dims* dims, int64_t tokens,
                 void* saved, size_t saved_bytes,
                 void* workspace, size_t workspace_bytes,
                 void* stream);
+
+/* mlp_pack_quantize_weights then mlp_forward, for a step that packs fresh
+ * weights before its forward ("Reduced-width QK and packed FP8 attention",
+ * Changes: the MLP's forward and backward in FP8, its weights changing
+ * every step): the same results bit for bit (the cache with its status
+ * word, saved, y), with the amax of W1, W2 and x in one launch and their
+ * three quantisers in the next.  Arguments, ownership and errors as in the
+ * two calls (every check of both is made before the first launch); the
+ * workspace is fpr_mlp_workspace_bytes(dims, T, FPR_CALL_PACK_FORWARD)
+ * bytes. */
+FPR_API int mlp_pack_forward(const fpr_mlp_dims* dims,
+                const float* w1, int64_t ld1, const float* w2, int64_t ld2,
+                const fpr_mlp_cache* cache, int64_t tokens,
+                const uint16_t* x, uint16_t* y,
+                void* saved, size_t saved_bytes,
+                void* workspace, size_t workspace_bytes, void* stream);
 
 /* dy [T][D] bf16 -> dx [T][D] bf16, dW1 [D][F] fp32 (row stride ld1),
  * dW2 [F][D] fp32 (ld2).  Sets FPR_STATUS_G_NONFINITE for a NaN/Inf in dy,

@@ -191,12 +191,15 @@ def bf16_gemm_excess(gpu_bits: np.ndarray, exact: np.ndarray, round_bf16) -> tup
 # ------------------------------------------------------- FP8 ReLU^2 MLP
 
 def run_mlp(w: dict, seed: int = 42, x_bits=None, w12=None, dy_bits=None,
-            backward: bool = True, grad_format: int = 0):
+            backward: bool = True, grad_format: int = 0, pack_forward: bool = False):
     """Pack, forward (and backward) of the FP8 ReLU^2 MLP on the GPU; every
-    stage's output as numpy arrays (bf16 as uint16 patterns)."""
+    stage's output as numpy arrays (bf16 as uint16 patterns).  pack_forward
+    packs and runs the forward in one mlp_pack_forward call, on a cache
+    whose status word starts with every bit set; h is then not returned."""
     T = w["n_seq"] * w["seq_len"]
     D, F = w["d_model"], w["d_ff"]
-    say(f"[gpu] mlp T={T} D={D} F={F} grad_format={grad_format} seed={seed}")
+    say(f"[gpu] mlp T={T} D={D} F={F} grad_format={grad_format} pack_forward={pack_forward} "
+        f"seed={seed}")
     if x_bits is None:
         x_bits = inputs.make_x(w, seed)
     if w12 is None:
@@ -204,10 +207,16 @@ def run_mlp(w: dict, seed: int = 42, x_bits=None, w12=None, dy_bits=None,
     dims = B.MlpDims(D, F, grad_format)
     cache = B.MlpCache(dims)
     w1d, w2d = (torch.from_numpy(np.ascontiguousarray(a)).cuda() for a in w12)
-    B.mlp_pack_quantize_weights(dims, w1d, w2d, cache)
-    ws_f = torch.empty(B.mlp_workspace_bytes(dims, T, B.FPR_CALL_FORWARD), dtype=torch.uint8,
-                       device="cuda")
-    y, saved = B.mlp_forward(dims, bits_to_dev(x_bits), cache, workspace=ws_f)
+    if pack_forward:
+        cache.status.fill_(-1)
+        ws_f = torch.empty(B.mlp_workspace_bytes(dims, T, B.FPR_CALL_PACK_FORWARD),
+                           dtype=torch.uint8, device="cuda")
+        y, saved = B.mlp_pack_forward(dims, w1d, w2d, cache, bits_to_dev(x_bits), workspace=ws_f)
+    else:
+        B.mlp_pack_quantize_weights(dims, w1d, w2d, cache)
+        ws_f = torch.empty(B.mlp_workspace_bytes(dims, T, B.FPR_CALL_FORWARD),
+                           dtype=torch.uint8, device="cuda")
+        y, saved = B.mlp_forward(dims, bits_to_dev(x_bits), cache, workspace=ws_f)
     torch.cuda.synchronize()
     lay = B.mlp_layout(dims, T)
     qlay = B.layout(B.make_dims(128, 1), 1)  # the blocked layout's parameters
@@ -226,7 +235,8 @@ def run_mlp(w: dict, seed: int = 42, x_bits=None, w12=None, dy_bits=None,
     out["h8"], out["h8_tail"] = h8[:T, :F], h8[T:Tp]
     out["x_scales"] = B.view_bytes(saved, lay.saved_x_scales, (2,), torch.float32).cpu().numpy()
     out["h_scales"] = B.view_bytes(saved, lay.saved_h_scales, (2,), torch.float32).cpu().numpy()
-    out["h"] = dev_to_bits(B.view_bytes(ws_f, lay.fwd_h, (T, F), torch.bfloat16))
+    out["h"] = None if pack_forward else dev_to_bits(
+        B.view_bytes(ws_f, lay.fwd_h, (T, F), torch.bfloat16))
     out["y"] = dev_to_bits(y)
     if backward:
         if dy_bits is None:

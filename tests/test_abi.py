@@ -24,7 +24,7 @@ def test_library_exports_every_declared_call():
                           "mlp_pack_quantize_weights", "mlp_forward", "mlp_backward",
                           "fpr_e5m2_encode", "qkv_forward_noalloc", "fpr_noalloc_scratch_bytes",
                           "fpr_probe_copy", "fpr_probe_read", "fpr_probe_mfma",
-                          "qkv_pack_forward"}
+                          "qkv_pack_forward", "mlp_pack_forward"}
     lib = B.load()
     for n in names:
         assert hasattr(lib, n), n
@@ -273,6 +273,12 @@ def test_mlp_layout_is_disjoint_and_sized():
         assert regions[-1][0] + regions[-1][1] <= total
     assert lay.fwd_h + 2 * T * 3072 <= B.mlp_workspace_bytes(d, T, B.FPR_CALL_FORWARD)
     assert lay.dw1_splits == lay.dw2_splits == 7
+    # mlp_pack_forward's workspace: the two weights' amax partials, aligned,
+    # then the forward's
+    fw = B.mlp_workspace_bytes(d, T, B.FPR_CALL_FORWARD)
+    pk = B.mlp_workspace_bytes(d, 0, B.FPR_CALL_PACK)
+    pf = B.mlp_workspace_bytes(d, T, B.FPR_CALL_PACK_FORWARD)
+    assert fw + 2 * pk <= pf < fw + 2 * pk + 256
 
 
 @_NO_GPU
@@ -295,6 +301,28 @@ def test_mlp_argument_errors_are_reported_before_any_launch():
     assert L.mlp_forward(by(d), 256, p, by(cc), p, p, 16, p, 1 << 30, None) == 4
     half = B._MlpCacheC(p, p, None, p, p, p)
     assert L.mlp_forward(by(d), 256, p, by(half), p, p, 1 << 30, p, 1 << 30, None) == 1
+    # pack + forward in one call: the checks of both, a workspace for both
+    pf = B.mlp_workspace_bytes(d, 256, B.FPR_CALL_PACK_FORWARD)
+    sv = B.mlp_saved_bytes(d, 256)
+    args = [by(d), p, 512, p, 128, by(cc), 256, p, p, p, sv, p, pf, None]
+
+    def pack_fwd(**change):
+        a = list(args)
+        for i, val in change.items():
+            a[int(i[1:])] = val
+        return L.mlp_pack_forward(*a)
+
+    assert pack_fwd(a1=None) == 1
+    assert pack_fwd(a4=127) == 1
+    assert pack_fwd(a2=514) == 3
+    assert pack_fwd(a6=0) == 1
+    assert pack_fwd(a8=None) == 1
+    assert pack_fwd(a7=p + 2) == 3
+    assert pack_fwd(a10=sv - 1) == 4
+    assert pack_fwd(a12=pf - 1) == 4
+    assert pack_fwd(a12=B.mlp_workspace_bytes(d, 256, B.FPR_CALL_FORWARD)) == 4
+    assert pack_fwd(a5=by(half)) == 1
+    assert L.mlp_pack_forward(by(bad), *args[1:]) == 2
     assert L.mlp_backward(by(d), 256, p, p, 1 << 30, by(cc), p, p, 500, p, 128, p, 1 << 30,
                           None) == 1
     assert L.mlp_backward(by(d), 256, p, p, 1 << 30, by(cc), p, p, 512, p, 128, p, 64,

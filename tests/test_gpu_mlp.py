@@ -149,6 +149,41 @@ def test_mlp_nonfinite_input_sets_status():
     assert r["status"] & 2
 
 
+@pytest.mark.parametrize("name,w", [("tiny", inputs.MLP_WORKLOADS["mlp_tiny"]),
+                                    ("tails", MLP_TAILS),
+                                    ("one_token", dict(n_seq=1, seq_len=1, d_model=128, d_ff=128)),
+                                    ("mlp_64k", inputs.MLP_WORKLOADS["mlp_64k"])])
+def test_mlp_pack_forward_matches_separate_calls(name, w):
+    """mlp_pack_forward (the weight pack and the forward with their
+    quantiser launches shared) writes what mlp_pack_quantize_weights and
+    mlp_forward write, bit for bit: both layouts of W1 and W2 and their
+    scales, x8 and h8 with their zero tails and scales, y; the backward
+    from its cache and saved buffer then matches; and it clears the status
+    word it was handed with every bit set."""
+    sep = run_mlp(w, seed=29)
+    one = run_mlp(w, seed=29, pack_forward=True)
+    for k in ("c_w1", "c_w1_t", "c_w2", "c_w2_t", "w_scales", "x8", "x8_tail", "h8", "h8_tail",
+              "x_scales", "h_scales", "y", "dp8", "dx"):
+        assert np.array_equal(sep[k], one[k]), k
+    for k in ("dw1", "dw2"):
+        assert np.array_equal(sep[k].view(np.uint32), one[k].view(np.uint32)), k
+    assert sep["status"] == one["status"] == 0
+
+
+def test_mlp_pack_forward_status_bits():
+    """NaNs in W2 and in x set the weight and the activation bits in the
+    combined call as in the separate calls."""
+    w = MLP_TAILS
+    x = inputs.make_x(w, 6)
+    x[3, 1] = 0x7FC0
+    w1, w2 = inputs.make_mlp_w(w, 7)
+    w2[2, 5] = np.nan
+    sep = run_mlp(w, seed=6, x_bits=x, w12=(w1, w2), backward=False)
+    one = run_mlp(w, seed=6, x_bits=x, w12=(w1, w2), backward=False, pack_forward=True)
+    assert sep["status"] & 3 == 3
+    assert sep["status"] == one["status"]
+
+
 def test_mlp_64k_sampled():
     """The benchmark's MLP workload (T = 65536, D = 768, d_ff = 3072) in its
     launch configuration: every e4m3 code of x8, h8, dy8 and dpre8 bit-exact

@@ -61,8 +61,11 @@ def test_step_orders_match_the_library_stage_names():
     assert sep[:5] == ["amax_w", "quantize_w", "amax_x", "quantize_x", "gemm_fwd"]
     assert sep[5:] == rs.QKV_ORDER[3:]
     assert rs.QKV_ORDER_UNFUSED == rs.QKV_ORDER[:3] + ["norm_rope_fwd"] + rs.QKV_ORDER[3:]
+    msep = rs.step_order("mlp_64k", separate_pack=True)
+    assert msep[:7] == rs.MLP_PACK_SEPARATE + ["mlp_gemm_up"] and msep[6:] == rs.MLP_ORDER[2:]
+    assert rs.step_order("block_64k", separate_pack=True) == sep + msep
     names = open("include/fpr.h").read()
-    for stage in set(rs.QKV_ORDER + sep + rs.MLP_ORDER):
+    for stage in set(rs.QKV_ORDER + sep + rs.MLP_ORDER + msep):
         assert stage in names, stage
         assert stage in bench.STAGE_SOURCES, stage
 
@@ -162,11 +165,15 @@ def test_two_pass_backward_work_accounting():
 
 def test_combined_pack_forward_work_accounting():
     """qkv_pack_forward's two launches carry exactly the work of the four
-    separate quantiser launches: W's and x's amax, then both quantisers."""
+    separate quantiser launches: W's and x's amax, then both quantisers;
+    mlp_pack_forward's that of its six (two per weight, two for x)."""
     w = dict(n_seq=1, seq_len=65536, d_model=768, n_heads=6, d_qk=96, d_v=128)
     work = bench.stage_work(w, 5)
     assert work["amax_wx"] == ("hbm", work["amax_w"][1] + work["amax_x"][1])
     assert work["quantize_wx"] == ("hbm", work["quantize_w"][1] + work["quantize_x"][1])
+    m = bench.mlp_stage_work(dict(n_seq=1, seq_len=65536, d_model=768, d_ff=3072), (7, 7))
+    assert m["mlp_amax_wx"] == ("hbm", 2 * m["mlp_amax_w"][1] + m["mlp_amax_x"][1])
+    assert m["mlp_quantize_wx"] == ("hbm", 2 * m["mlp_quantize_w"][1] + m["mlp_quantize_x"][1])
 
 
 def test_stage_times_split_a_trace_by_launch_order(tmp_path):
@@ -190,8 +197,8 @@ def test_stage_times_split_a_trace_by_launch_order(tmp_path):
                         "End_Timestamp": t + 90000})
         return str(f)
 
-    order = rs.step_order("mlp_64k")
-    got = rs.stage_times(write(order, 2), "mlp_64k")
+    order = rs.step_order("mlp_64k", separate_pack=True)
+    got = rs.stage_times(write(order, 2), "mlp_64k", separate_pack=True)
     assert got["mlp_gemm_up"] == (2, pytest.approx(order.index("mlp_gemm_up") + 1.05))
     k1, k2 = 1, 3  # mlp_quantize_w launches once per weight
     assert order[k1] == order[k2] == "mlp_quantize_w"
