@@ -1,10 +1,11 @@
 #!/usr/bin/env python3
 """Benchmark of the packed FP8 QKV projection (reduced-width Q/K) on one MI355X.
 
-One step = pack_quantize_weights (the weight cache is rebuilt every step) +
-qkv_forward + qkv_backward at D=768, 6 heads, d_qk=96, d_v=128 (packed
-N=1920), T=65536 tokens in one sequence, all through the C interface of
-libfpr.so.  Inputs are synthetic (seeded normals of the shapes the pages
+One step = the weight pack (the weight cache is rebuilt every step) and
+the forward, in one qkv_pack_forward call, + qkv_backward at D=768, 6 heads,
+d_qk=96, d_v=128 (packed N=1920), T=65536 tokens in one sequence, all
+through the C interface of libfpr.so (--pack-forward separate: the pack and
+the forward as pack_quantize_weights + qkv_forward).  Inputs are synthetic (seeded normals of the shapes the pages
 train on) and resident in HBM before timing starts.
 
 Prints one JSON line: whole-step tokens/s, TFLOP/s of the FP8 GEMMs
@@ -13,8 +14,8 @@ with HIP events on its launch stream inside the timed region), and the CPU
 oracle timed on a bounded sample on this host.
 
 Other workloads (--workload): the QKV shapes of ``inputs.WORKLOADS``; the
-FP8 ReLU^2 MLP alone (``mlp_64k``: mlp_pack_quantize_weights + mlp_forward
-+ mlp_backward at D=768, d_ff=3072, T=65536); and the block's projection set
+FP8 ReLU^2 MLP alone (``mlp_64k``: mlp_pack_forward + mlp_backward at
+D=768, d_ff=3072, T=65536); and the block's projection set
 (``block_64k``: the QKV step of ``step_64k`` followed by the MLP step of
 ``mlp_64k``).
 

@@ -20,8 +20,10 @@
  * --------------------------------
  *  - All tensor pointers are DEVICE pointers owned by the caller.  The
  *    library never allocates, frees or synchronises, and keeps no mutable
- *    global state (apart from the optional per-thread profiling trace).  Every call only enqueues kernels on `stream` (a
- *    hipStream_t; NULL means the default stream) and returns.
+ *    global state apart from the optional per-thread profiling trace and
+ *    qkv_forward_noalloc's fixed per-device scratch.  Every call only
+ *    enqueues kernels on `stream` (a hipStream_t; NULL means the default
+ *    stream) and returns.
  *  - Inputs are read-only.  Outputs are fully overwritten (dW is written,
  *    not accumulated).
  *  - bf16 tensors are passed as uint16_t bit patterns.  FP8 is OCP E4M3
