@@ -630,9 +630,10 @@ def test_max_tokens_sampled():
     generator on the device (x ~ N(0,1), dq/dk/dv ~ N(0, 1e-2)); the oracle
     gets the same values copied to the host.  Checked: both scales against
     the oracle's quantiser of the whole tensor's amax; sampled token rows of
-    x8, q, k, v, the gradient codes and dX against the oracle; and dW
-    entries (sums over all 2^24 tokens) to 1e-3 of their natural scale
-    sqrt(sum of squared terms)."""
+    x8, q, k, v, the gradient codes and dX against the oracle; dW entries
+    (sums over all 2^24 tokens) to 1e-3 of their natural scale sqrt(sum of
+    squared terms); and qkv_pack_forward's outputs equal to those of the two
+    separate calls, byte for byte."""
     from fp8_packed_reduced_amd import binding as B
     w = dict(inputs.WORKLOADS["tiny"], n_seq=256, seq_len=65536)
     n_seq, S, D, H, dqk, dvw = (w[k] for k in ("n_seq", "seq_len", "d_model", "n_heads",
@@ -653,7 +654,23 @@ def test_max_tokens_sampled():
     Wd = torch.from_numpy(W).to(dev)
     cache = B.WeightCache(dims)
     B.pack_quantize_weights(dims, Wd[:, :nq], Wd[:, nq:2 * nq], Wd[:, 2 * nq:], cache)
-    q, k, v, saved = B.qkv_forward(dims, n_seq, S, x, cache)
+    saved = torch.zeros(B.saved_bytes(dims, T), dtype=torch.uint8, device=dev)
+    q, k, v, saved = B.qkv_forward(dims, n_seq, S, x, cache, saved=saved)
+    # the weight pack and the forward in one call, into fresh buffers: the
+    # same bytes (its launches' grids are largest at this token count)
+    cache2 = B.WeightCache(dims)
+    saved2 = torch.zeros_like(saved)
+    q2, k2, v2, _ = B.qkv_pack_forward(dims, Wd[:, :nq], Wd[:, nq:2 * nq], Wd[:, 2 * nq:], cache2,
+                                       n_seq, S, x, saved=saved2)
+    torch.cuda.synchronize()
+    for a, b_, name in ((q, q2, "q"), (k, k2, "k"), (v, v2, "v"), (saved, saved2, "saved"),
+                        (cache.w_packed, cache2.w_packed, "w_packed"),
+                        (cache.w_packed_t, cache2.w_packed_t, "w_packed_t"),
+                        (cache.scales, cache2.scales, "w_scales"),
+                        (cache.status, cache2.status, "status")):
+        assert torch.equal(a.view(torch.uint8) if a.dtype == torch.bfloat16 else a,
+                           b_.view(torch.uint8) if b_.dtype == torch.bfloat16 else b_), name
+    del q2, k2, v2, saved2, cache2
     ws_b = torch.empty(B.workspace_bytes(dims, T, B.FPR_CALL_BACKWARD), dtype=torch.uint8,
                        device=dev)
     dx, dw = B.qkv_backward(dims, n_seq, S, q, k, dq, dk, dv, saved, cache, workspace=ws_b)
