@@ -416,19 +416,21 @@ def test_two_pass_backward_matches_one_pass(name, wl, fmt, qs):
     assert one["status"] == two["status"] == 0
 
 
-@pytest.mark.parametrize("name,wl,qs", [
-    ("tiny", inputs.WORKLOADS["tiny"], 0), ("ragged", RAGGED, 0),
-    ("d48", dict(RAGGED, d_qk=48), 0), ("d128", dict(RAGGED, d_qk=128), 0),
-    ("padded", RAGGED, 136), ("step_64k", inputs.WORKLOADS["step_64k"], 0)])
-def test_pack_forward_matches_separate_calls(name, wl, qs):
+@pytest.mark.parametrize("name,wl,qs,fmt,passes", [
+    ("tiny", inputs.WORKLOADS["tiny"], 0, 0, 0), ("ragged", RAGGED, 0, 0, 0),
+    ("d48", dict(RAGGED, d_qk=48), 0, 0, 0), ("d128", dict(RAGGED, d_qk=128), 0, 0, 0),
+    ("padded", RAGGED, 136, 0, 0), ("e5m2", RAGGED, 0, 1, 0), ("two_pass", RAGGED, 0, 0, 2),
+    ("step_64k", inputs.WORKLOADS["step_64k"], 0, 0, 0)])
+def test_pack_forward_matches_separate_calls(name, wl, qs, fmt, passes):
     """qkv_pack_forward (the weight pack and the forward with their
     quantiser launches shared) writes what pack_quantize_weights followed by
     qkv_forward writes, bit for bit: both weight views and their scales, x8
     with its zero K and token tails and its scales, 1/rms, q, k, v; the
     backward from its cache and saved buffer then matches too; and it
-    clears the status word it was handed with every bit set."""
-    sep = run(wl, seed=23, qk_stride=qs)
-    one = run(wl, seed=23, qk_stride=qs, pack_forward=True)
+    clears the status word it was handed with every bit set (also with e5m2
+    gradients and the two-pass backward after it)."""
+    sep = run(wl, seed=23, qk_stride=qs, grad_format=fmt, bwd_passes=passes)
+    one = run(wl, seed=23, qk_stride=qs, grad_format=fmt, bwd_passes=passes, pack_forward=True)
     for key in ("w_packed", "w_packed_t", "w_scales", "x8", "x8_kpad", "x8_tail", "x_scales",
                 "rho", "q", "k", "v", "g8", "g_scales", "dx"):
         assert np.array_equal(sep[key], one[key]), key
